@@ -1,0 +1,231 @@
+/*
+ * infv2.h -- C ABI of the InfLLM v2 sparse-attention hot path for AMD MI355X (gfx950).
+ *
+ * InfLLM v2 (MiniCPM4 summary page, section "InfLLM v2: Trainable Sparse
+ * Attention for Both Prefilling and Decoding") splits attention into two
+ * stages: (1) score every KV block against the query's group through
+ * mean-pooled "semantic kernels" and pick the top-k blocks, and (2) run exact
+ * softmax attention over the chosen blocks only (paragraph "Complexity
+ * analysis").  The library exposes each step as one call:
+ *
+ *   infv2_compress_keys        step 1a: compressed keys  kbar_j = Mean(K[j s : j s + p])
+ *   infv2_select_blocks        step 1b: kernel softmax, group mean, block max, top-k
+ *   infv2_sparse_attn_decode   step 2 for one new token per sequence
+ *   infv2_sparse_attn_prefill  step 2 for a chunk of consecutive query rows
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or keeps them after the call returns.  Scratch
+ *    memory comes only from the caller's workspace (see infv2_workspace_bytes).
+ *  - Every call enqueues work on `stream` (a hipStream_t; NULL = the default
+ *    stream) and returns without synchronising.  Results are valid once the
+ *    caller has synchronised that stream.  No host<->device copies are made.
+ *  - Arguments are validated on the host BEFORE any HIP call: an invalid call
+ *    returns an error status and enqueues nothing.  Values that live in device
+ *    memory (offsets, lengths, indices) cannot be checked on the host; if they
+ *    are inconsistent with the buffers the result is undefined.
+ *  - Launch failures are reported as INFV2_ERR_DEVICE.
+ *  - The library holds no mutable global state.  Concurrent calls on
+ *    different streams need distinct workspaces.
+ *
+ * Layouts (row-major, contiguous; element type given by the config):
+ *  - Query heads h = g*G + r (r < G) belong to KV head g, G = Hq / Hkv.
+ *  - K / V of sequence b: tokens [kv_offsets[b], kv_offsets[b+1]) of a packed
+ *    buffer; inside, layout [Hkv][cap_b][d] with cap_b = kv_offsets[b+1] -
+ *    kv_offsets[b] (each KV head's keys contiguous).  The valid length is
+ *    kv_lens[b] <= cap_b (kv_lens == NULL: the length is cap_b).
+ *  - Compressed keys of sequence b: kernels [ck_offsets[b], ck_offsets[b+1])
+ *    of a packed buffer, layout [Hkv][ccap_b][d], element type ck_dtype, with
+ *    ccap_b >= n_c(kv_lens[b]).
+ *  - block_idx: int32 [rows][Hkv][topk], ascending, padded with -1.
+ *
+ * Readings of the pages that fix the arithmetic:
+ *  - kernels: only complete ones, n_c(n) = floor((n - p) / s) + 1 (0 if n < p);
+ *  - a query at absolute position i sees kernel j only if j*s + p <= i + 1;
+ *  - logits z = score_scale * q.kbar; LogSumExp per query head; group score
+ *    = mean over the group's heads of the per-head softmax; block score = max
+ *    over the visible kernels that share a token with the block;
+ *  - forced blocks F = {0..init-1} U {c-local+1..c}, c = floor(i/m); k counts
+ *    F; if c + 1 <= k every block 0..c is taken (dense); score ties go to the
+ *    lower block index;
+ *  - attention: softmax(attn_scale * q.k) over the tokens t <= i (and t < n)
+ *    of the selected blocks.
+ *
+ * Supported on the GPU: head_dim = 128, group size Hq/Hkv = 16 (one token's
+ * group forms the 16-row side of a 16x16 MFMA tile), block_size a multiple of
+ * 16 in [16, 256], 1 <= kernel_stride <= kernel_size <= 256, topk <= 1024,
+ * at most 16384 blocks per sequence.  Other values return INFV2_ERR_UNSUPPORTED.
+ */
+#ifndef INFV2_H
+#define INFV2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define INFV2_ABI_VERSION 1
+
+typedef enum infv2_status {
+    INFV2_OK = 0,
+    INFV2_ERR_NULL = 1,         /* a required pointer is NULL */
+    INFV2_ERR_SHAPE = 2,        /* sizes inconsistent (e.g. Hq % Hkv != 0, k < |F|) */
+    INFV2_ERR_UNSUPPORTED = 3,  /* valid but not implemented on this device path */
+    INFV2_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than infv2_workspace_bytes */
+    INFV2_ERR_DEVICE = 5        /* a HIP launch failed */
+} infv2_status;
+
+typedef enum infv2_dtype {
+    INFV2_FP32 = 0,
+    INFV2_BF16 = 1
+} infv2_dtype;
+
+typedef enum infv2_mode {
+    INFV2_MODE_DECODE = 0,      /* one query row per sequence, at position kv_lens[b] - 1 */
+    INFV2_MODE_PREFILL = 1      /* one sequence, rows at positions q_start .. q_start + rows - 1 */
+} infv2_mode;
+
+typedef enum infv2_op {         /* operation ids for infv2_workspace_bytes */
+    INFV2_OP_COMPRESS = 0,
+    INFV2_OP_SELECT_DECODE = 1,
+    INFV2_OP_SELECT_PREFILL = 2,
+    INFV2_OP_ATTN_DECODE = 3,
+    INFV2_OP_ATTN_PREFILL = 4
+} infv2_op;
+
+/* Method hyper-parameters (names follow the pages' notation). */
+typedef struct infv2_config {
+    int32_t head_dim;       /* d */
+    int32_t num_q_heads;    /* Hq */
+    int32_t num_kv_heads;   /* Hkv; group size G = Hq / Hkv */
+    int32_t block_size;     /* m: tokens per KV block ("Block-level key-value partitioning") */
+    int32_t kernel_size;    /* p: tokens per semantic kernel ("Semantic kernels"), 32 recommended */
+    int32_t kernel_stride;  /* s: stride between kernel starts, 16 recommended */
+    int32_t topk;           /* k: blocks attended per query token, forced blocks included */
+    int32_t init_blocks;    /* leading blocks always selected ("Initial and local tokens") */
+    int32_t local_blocks;   /* blocks of the local window ending at the query's block */
+    int32_t io_dtype;       /* infv2_dtype of q, k, v and out */
+    int32_t ck_dtype;       /* infv2_dtype of the compressed keys (FP32 default) */
+    float   score_scale;    /* selection logit scale (the pages print none: 1.0) */
+    float   attn_scale;     /* attention logit scale, usually 1/sqrt(d) */
+} infv2_config;
+
+/*
+ * infv2_compress_keys -- step 1a, "Semantic kernels" paragraph: the kernel
+ * j of sequence b covers tokens [j*s, j*s + p) and its compressed key is the
+ * mean of those keys ("What this computes" / "Why mean pooling").
+ *
+ * Computes, for every sequence b and KV head, the kernels
+ * j in [ck_begin[b], n_c(kv_lens[b])) and stores them at their index j in the
+ * sequence's compressed-key region (incremental update: earlier kernels are
+ * left untouched).  The mean is formed exactly (float64 sum) and rounded once
+ * to ck_dtype.
+ *
+ *   k            device, io_dtype, packed K (see Layouts)
+ *   kv_offsets   device int64 [batch+1], token offsets (capacities) of the K buffer
+ *   kv_lens      device int64 [batch] valid lengths, or NULL (= capacities)
+ *   ck_offsets   device int64 [batch+1], kernel offsets (capacities) of the CK buffer
+ *   ck_begin     device int64 [batch] first kernel to compute, or NULL (= 0)
+ *   batch        number of sequences, >= 1
+ *   max_len      host upper bound of every kv_lens[b] (sizes the grid)
+ *   max_new      host upper bound of n_c(kv_lens[b]) - ck_begin[b] over b;
+ *                < 0 means n_c(max_len)
+ *   ck           device, ck_dtype, packed compressed keys (written)
+ */
+int32_t infv2_compress_keys(const infv2_config* cfg, const void* k, const int64_t* kv_offsets,
+                            const int64_t* kv_lens, const int64_t* ck_offsets,
+                            const int64_t* ck_begin, int32_t batch, int64_t max_len,
+                            int64_t max_new, void* ck, void* stream);
+
+/*
+ * infv2_select_blocks -- step 1b, paragraphs "Semantic kernels" (eqs.
+ * r_kernel, r_block), "Query group sharing" (eq. r_group), "Top-K
+ * implementation and the LSE bottleneck" (two passes: LogSumExp, then
+ * normalised scores) and "Initial and local tokens always selected".
+ *
+ * For every query row and KV head g: logits of the group's G heads against
+ * every kernel visible to the row, per-head LogSumExp, group score per kernel
+ * (mean of the per-head softmax), block score (max over the kernels meeting
+ * the block), and the forced blocks plus the top (k - |F|) other blocks.
+ *
+ *   mode         INFV2_MODE_DECODE: rows == batch, q [batch][Hq][d], row b at
+ *                position kv_lens[b] - 1 of sequence b.
+ *                INFV2_MODE_PREFILL: batch == 1, q [rows][Hq][d], row r at
+ *                position q_start + r; compressed keys up to n_c(q_start + rows)
+ *                must be present.
+ *   q            device, io_dtype
+ *   ck, ck_offsets, kv_offsets, kv_lens, batch, max_len   as above
+ *                (prefill: max_len >= q_start + rows)
+ *   block_idx    device int32 [rows][Hkv][topk] (written)
+ *   block_score  device float [rows][Hkv][topk] or NULL: the block score of
+ *                each selected block (-inf if no kernel is visible in it,
+ *                NaN in padding slots)
+ *   ws           device workspace of ws_bytes >= infv2_workspace_bytes(op =
+ *                SELECT_DECODE or SELECT_PREFILL).  It must be zero-filled
+ *                before its first use; every call leaves it ready for the
+ *                next one.
+ */
+int32_t infv2_select_blocks(const infv2_config* cfg, int32_t mode, const void* q, int32_t rows,
+                            int64_t q_start, const void* ck, const int64_t* ck_offsets,
+                            const int64_t* kv_offsets, const int64_t* kv_lens, int32_t batch,
+                            int64_t max_len, int32_t* block_idx, float* block_score, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/*
+ * infv2_sparse_attn_decode -- step 2 for decoding ("Complexity analysis",
+ * Stage 2: each query token attends the k*m tokens of its selected blocks;
+ * "Query group sharing": the group's heads read the same blocks once).
+ *
+ *   q            device, io_dtype [batch][Hq][d]; row b at position kv_lens[b] - 1
+ *   k, v         device, io_dtype, packed K/V (see Layouts)
+ *   kv_offsets, kv_lens, batch, max_len   as above
+ *   block_idx    device int32 [batch][Hkv][topk] from infv2_select_blocks
+ *                (entries -1 are skipped)
+ *   out          device, io_dtype [batch][Hq][d] (written)
+ *   ws           workspace (infv2_workspace_bytes op = ATTN_DECODE), zero-filled
+ *                before first use, left ready for the next call
+ */
+int32_t infv2_sparse_attn_decode(const infv2_config* cfg, const void* q, const void* k,
+                                 const void* v, const int64_t* kv_offsets, const int64_t* kv_lens,
+                                 int32_t batch, int64_t max_len, const int32_t* block_idx,
+                                 void* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * infv2_sparse_attn_prefill -- step 2 for a chunk of consecutive query rows
+ * of one sequence ("Design principles summary": every query token selects its
+ * own blocks; rows are causal, t <= i).
+ *
+ *   q            device, io_dtype [rows][Hq][d]; row r at position q_start + r
+ *   k, v         device, io_dtype, one sequence [Hkv][cap][d] with
+ *                cap = kv_offsets[1] - kv_offsets[0] >= q_start + rows
+ *   kv_offsets   device int64 [2]
+ *   block_idx    device int32 [rows][Hkv][topk]
+ *   out          device, io_dtype [rows][Hq][d] (written)
+ *   ws           workspace (op = ATTN_PREFILL; may be 0 bytes)
+ */
+int32_t infv2_sparse_attn_prefill(const infv2_config* cfg, const void* q, int32_t rows,
+                                  int64_t q_start, const void* k, const void* v,
+                                  const int64_t* kv_offsets, const int32_t* block_idx, void* out,
+                                  void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace size in bytes for operation `op` (infv2_op) at the given sizes. */
+int32_t infv2_workspace_bytes(const infv2_config* cfg, int32_t op, int32_t rows, int32_t batch,
+                              int64_t max_len, size_t* bytes);
+
+/* Number of complete kernels over n keys: floor((n - p) / s) + 1, or 0 if n < p. */
+int64_t infv2_num_kernels(const infv2_config* cfg, int64_t n);
+
+/* Human-readable name of a status code (static string). */
+const char* infv2_status_str(int32_t status);
+
+/* INFV2_ABI_VERSION of the loaded library. */
+int32_t infv2_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INFV2_H */

@@ -1,0 +1,150 @@
+"""Device-side plumbing for the GPU parity tests and the bench.
+
+Uploads a synthetic workload with torch (memory only) and drives the HIP path
+through the Python binding of the C ABI.  bf16 tensors travel as their 16-bit
+patterns (torch.int16), so no torch bf16 arithmetic is involved anywhere.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+import trainable_block_sparse_amd as tbs
+from synth import Workload, bf16_bits_to_f32
+
+
+def cfg_of(wl: Workload, ck_dtype: str = "fp32", **over) -> tbs.Config:
+    kw = dict(head_dim=wl.head_dim, num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
+              block_size=wl.block_size, kernel_size=wl.kernel_size,
+              kernel_stride=wl.kernel_stride, topk=wl.topk, init_blocks=wl.init_blocks,
+              local_blocks=wl.local_blocks, io_dtype=wl.io_dtype, ck_dtype=ck_dtype,
+              score_scale=wl.score_scale, attn_scale=wl.attn_scale)
+    kw.update(over)
+    return tbs.Config(**kw)
+
+
+def num_kernels(n: int, p: int, s: int) -> int:
+    return 0 if n < p else (n - p) // s + 1
+
+
+def to_device(arr: np.ndarray, device="cuda") -> torch.Tensor:
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device)
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+
+
+def from_device(t: torch.Tensor, io_dtype: str) -> np.ndarray:
+    a = t.detach().cpu().numpy()
+    if io_dtype == "bf16":
+        return bf16_bits_to_f32(a.view(np.uint16)).astype(np.float64)
+    return a.astype(np.float64)
+
+
+class DeviceWorkload:
+    """A workload resident in GPU memory plus the calls of the hot path."""
+
+    def __init__(self, wl: Workload, ck_dtype: str = "fp32", device: str = "cuda", **cfg_over):
+        self.wl = wl
+        self.device = device
+        self.cfg = cfg_of(wl, ck_dtype, **cfg_over)
+        self.ck_dtype = ck_dtype
+        self.k = to_device(wl.k, device)
+        self.v = to_device(wl.v, device)
+        self.q = to_device(wl.q, device)
+        self.kv_offsets = torch.tensor(wl.kv_offsets, dtype=torch.int64, device=device)
+        self.kv_lens = torch.tensor(wl.lens, dtype=torch.int64, device=device)
+        self.max_len = int(wl.lens.max())
+        ncs = [num_kernels(int(n), wl.kernel_size, wl.kernel_stride) for n in wl.lens]
+        self.nc = ncs
+        off = np.zeros(len(ncs) + 1, dtype=np.int64)
+        off[1:] = np.cumsum(ncs)
+        self.ck_offsets = torch.tensor(off, dtype=torch.int64, device=device)
+        total = int(off[-1]) * wl.num_kv_heads * wl.head_dim
+        tdt = torch.int16 if ck_dtype == "bf16" else torch.float32
+        self.ck = torch.zeros(max(total, 1), dtype=tdt, device=device)
+        self._ws = {}
+
+    # ---------------------------------------------------------------- workspaces
+    def ws(self, op: int, rows: int, batch: int, max_len: int) -> torch.Tensor:
+        need = max(256, tbs.infv2_workspace_bytes(self.cfg, op, rows, batch, max_len))
+        key = op
+        t = self._ws.get(key)
+        if t is None or t.numel() < need:
+            t = torch.zeros(need, dtype=torch.uint8, device=self.device)
+            self._ws[key] = t
+        return t
+
+    # ---------------------------------------------------------------- step 1a
+    def compress(self, kv_lens: Optional[torch.Tensor] = None, ck_begin: Optional[torch.Tensor] = None,
+                 max_len: Optional[int] = None, max_new: int = -1) -> None:
+        tbs.infv2_compress_keys(self.cfg, self.k, self.kv_offsets,
+                                self.kv_lens if kv_lens is None else kv_lens, self.ck_offsets,
+                                ck_begin, self.wl.batch, self.max_len if max_len is None else max_len,
+                                max_new, self.ck)
+
+    def ck_host(self) -> List[np.ndarray]:
+        """Compressed keys per sequence as float64 [Hkv][n_c][d]."""
+        raw = self.ck.detach().cpu().numpy()
+        if self.ck_dtype == "bf16":
+            vals = bf16_bits_to_f32(raw.view(np.uint16)).astype(np.float64)
+        else:
+            vals = raw.astype(np.float64)
+        out, base = [], 0
+        hkv, d = self.wl.num_kv_heads, self.wl.head_dim
+        for nc in self.nc:
+            out.append(vals[base:base + nc * hkv * d].reshape(hkv, nc, d))
+            base += nc * hkv * d
+        return out
+
+    # ---------------------------------------------------------------- decode
+    def select_decode(self, q: Optional[torch.Tensor] = None):
+        B, hkv, k = self.wl.batch, self.wl.num_kv_heads, self.cfg.topk
+        idx = torch.empty((B, hkv, k), dtype=torch.int32, device=self.device)
+        score = torch.empty((B, hkv, k), dtype=torch.float32, device=self.device)
+        ws = self.ws(tbs.OP_SELECT_DECODE, B, B, self.max_len)
+        tbs.infv2_select_blocks(self.cfg, tbs.INFV2_MODE_DECODE, self.q if q is None else q, B, 0,
+                                self.ck, self.ck_offsets, self.kv_offsets, self.kv_lens, B,
+                                self.max_len, idx, score, ws)
+        return idx, score
+
+    def attn_decode(self, idx: torch.Tensor, q: Optional[torch.Tensor] = None) -> torch.Tensor:
+        B = self.wl.batch
+        out = torch.empty_like(self.q if q is None else q)
+        ws = self.ws(tbs.OP_ATTN_DECODE, B, B, self.max_len)
+        tbs.infv2_sparse_attn_decode(self.cfg, self.q if q is None else q, self.k, self.v,
+                                     self.kv_offsets, self.kv_lens, B, self.max_len, idx, out, ws)
+        return out
+
+    # ---------------------------------------------------------------- prefill
+    def prefill_chunk(self, q0: int, q1: int):
+        """Compress the kernels completed by rows [q0, q1), then select and attend them."""
+        wl = self.wl
+        p, s = wl.kernel_size, wl.kernel_stride
+        lens = torch.tensor([q1], dtype=torch.int64, device=self.device)
+        begin = torch.tensor([num_kernels(q0, p, s)], dtype=torch.int64, device=self.device)
+        new = num_kernels(q1, p, s) - num_kernels(q0, p, s)
+        self.compress(kv_lens=lens, ck_begin=begin, max_len=q1, max_new=new)
+        rows = q1 - q0
+        hkv, k = wl.num_kv_heads, self.cfg.topk
+        q = self.q[q0:q1]
+        idx = torch.empty((rows, hkv, k), dtype=torch.int32, device=self.device)
+        score = torch.empty((rows, hkv, k), dtype=torch.float32, device=self.device)
+        ws = self.ws(tbs.OP_SELECT_PREFILL, rows, 1, q1)
+        tbs.infv2_select_blocks(self.cfg, tbs.INFV2_MODE_PREFILL, q, rows, q0, self.ck,
+                                self.ck_offsets, self.kv_offsets, None, 1, q1, idx, score, ws)
+        out = torch.empty_like(q)
+        tbs.infv2_sparse_attn_prefill(self.cfg, q, rows, q0, self.k, self.v, self.kv_offsets, idx,
+                                      out)
+        return idx, score, out
+
+    def prefill(self, chunk: int):
+        L = int(self.wl.lens[0])
+        idxs, scores, outs = [], [], []
+        for q0 in range(0, L, chunk):
+            i, s, o = self.prefill_chunk(q0, min(L, q0 + chunk))
+            idxs.append(i)
+            scores.append(s)
+            outs.append(o)
+        return torch.cat(idxs), torch.cat(scores), torch.cat(outs)

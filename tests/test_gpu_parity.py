@@ -1,0 +1,254 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Selections must match bit-exactly except across near-ties inside the relative
+1e-4 band (tests/parity.py); outputs must be allclose with (2e-2, 1e-2) for
+bf16 inputs and (1e-5, 1e-5) for fp32 inputs, the oracle evaluated on the
+GPU's selection.  Compressed keys must match bit-exactly (both sides round the
+exact mean once).  Every test prints what it runs before touching the GPU.
+"""
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import infv2_ref as ref  # noqa: E402
+from synth import make_config, make_workload  # noqa: E402
+from tests.parity import accept_selection, assert_close  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import trainable_block_sparse_amd as tbs
+    tbs.load_library()
+    yield
+
+
+def _harness():
+    from tests import gpu_harness
+    return gpu_harness
+
+
+def params_of(wl, ck_dtype="fp32", **over):
+    kw = dict(head_dim=wl.head_dim, num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
+              block_size=wl.block_size, kernel_size=wl.kernel_size, kernel_stride=wl.kernel_stride,
+              topk=wl.topk, init_blocks=wl.init_blocks, local_blocks=wl.local_blocks,
+              score_scale=wl.score_scale, attn_scale=wl.attn_scale, ck_dtype=ck_dtype)
+    kw.update(over)
+    return ref.Params(**kw)
+
+
+def _check_rows(gpu_idx, gpu_score, rowsels, label):
+    """Selection acceptance over rows; returns (#exact, #band)."""
+    exact = band = 0
+    worst_rel = 0.0
+    for r, rs in enumerate(rowsels):
+        verdict = accept_selection(gpu_idx[r], rs)
+        assert not verdict.startswith("fail"), f"{label} row {r}: {verdict}"
+        exact += verdict == "exact"
+        band += verdict == "band"
+        sel = gpu_idx[r][gpu_idx[r] >= 0]
+        want = rs.S[sel]
+        got = gpu_score[r][:sel.shape[0]]
+        fin = np.isfinite(want)
+        assert np.array_equal(np.isfinite(got), fin), f"{label} row {r}: -inf pattern"
+        if fin.any():
+            rel = np.max(np.abs(got[fin] - want[fin]) / np.maximum(np.abs(want[fin]), 1e-30))
+            worst_rel = max(worst_rel, float(rel))
+    assert worst_rel < 1e-4, f"{label}: block-score relative error {worst_rel:.2e}"
+    _say(f"{label}: {exact} exact, {band} within the near-tie band, score rel err {worst_rel:.1e}")
+    return exact, band
+
+
+# ---------------------------------------------------------------------------- decode
+def _run_decode(wl, ck_dtype="fp32", label="decode"):
+    h = _harness()
+    _say(f"{label}: lens={wl.lens.tolist()[:4]}{'...' if wl.batch > 4 else ''} B={wl.batch} "
+         f"io={wl.io_dtype} ck={ck_dtype} k={wl.topk} local={wl.local_blocks}")
+    dev = h.DeviceWorkload(wl, ck_dtype)
+    dev.compress()
+    idx_t, score_t = dev.select_decode()
+    out_t = dev.attn_decode(idx_t)
+    torch.cuda.synchronize()
+    idx = idx_t.cpu().numpy().astype(np.int64)
+    score = score_t.cpu().numpy().astype(np.float64)
+    out = h.from_device(out_t, wl.io_dtype)
+    prm = params_of(wl, ck_dtype)
+    # compressed keys bit-exact
+    cks = dev.ck_host()
+    q = wl.q_f64()
+    for b in range(wl.batch):
+        K = wl.k_f64(b)
+        want_ck = ref.compress_keys(K, wl.kernel_size, wl.kernel_stride, ck_dtype)
+        assert np.array_equal(cks[b], want_ck), f"{label}: compressed keys differ (seq {b})"
+    rows, idx_rows, score_rows = [], [], []
+    for b in range(wl.batch):
+        K = wl.k_f64(b)
+        n = K.shape[1]
+        G = prm.group
+        for g in range(wl.num_kv_heads):
+            rs = ref.select_row(q[b, g * G:(g + 1) * G], cks[b][g], n - 1, prm)
+            rows.append(rs)
+            idx_rows.append(idx[b, g])
+            score_rows.append(score[b, g])
+    _check_rows(np.array(idx_rows), np.array(score_rows), rows, label)
+    want = np.zeros_like(out)
+    for b in range(wl.batch):
+        n = int(wl.lens[b])
+        want[b] = ref.attend_with_selection(q[b:b + 1], wl.k_f64(b), wl.v_f64(b), [n - 1],
+                                            idx[b:b + 1], prm)[0]
+    err = assert_close(out, want, wl.io_dtype, label)
+    _say(f"{label}: output max abs err {err:.2e}")
+    return dev, idx, out
+
+
+def _small(mode="decode", lens=(300,), io="bf16", hkv=2, topk=8, local=2, init=1, seed=0, **kw):
+    return make_workload(mode=mode, io_dtype=io, lens=list(lens), num_q_heads=16 * hkv,
+                         num_kv_heads=hkv, topk=topk, init_blocks=init, local_blocks=local,
+                         n_planted=kw.pop("n_planted", 3), seed=seed, **kw)
+
+
+def test_decode_ragged_small_batch():
+    wl = _small(lens=[1, 31, 32, 33, 63, 64, 65, 100, 513, 1000, 4097], topk=8, local=2, seed=21)
+    _run_decode(wl, label="decode ragged bf16")
+
+
+def test_decode_fp32_ragged_and_bf16_ck():
+    wl = _small(lens=[700, 1024, 2049], io="fp32", topk=6, local=1, seed=22)
+    _run_decode(wl, label="decode fp32")
+    wl2 = _small(lens=[700, 1024, 2049], io="bf16", topk=6, local=1, seed=23)
+    _run_decode(wl2, ck_dtype="bf16", label="decode bf16 ck-bf16")
+
+
+def test_decode_scaled_logits_and_no_init():
+    wl = _small(lens=[3000, 5000], topk=10, local=3, init=0, seed=24, score_scale=1 / math.sqrt(128))
+    _run_decode(wl, label="decode score_scale=1/sqrt(d) init=0")
+
+
+def test_decode_forced_only_and_dense():
+    wl = _small(lens=[2000, 130], topk=3, local=2, init=1, seed=25)    # k == |F|
+    _run_decode(wl, label="decode forced-only")
+    wl = _small(lens=[500, 511, 512], topk=8, local=2, seed=26)        # c + 1 <= k: dense
+    _run_decode(wl, label="decode dense")
+
+
+def test_decode_first_token_attends_itself():
+    h = _harness()
+    wl = _small(lens=[1], topk=4, local=1, seed=27)
+    _say("decode n=1")
+    dev = h.DeviceWorkload(wl)
+    dev.compress()
+    idx, _ = dev.select_decode()
+    out = h.from_device(dev.attn_decode(idx), "bf16")
+    assert idx.cpu().numpy()[0, 0].tolist() == [0, -1, -1, -1]
+    v0 = wl.v_f64(0)[:, 0, :]                                   # [Hkv][d]
+    want = np.repeat(v0, 16, axis=0)
+    assert np.array_equal(out[0], want)
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 4])
+def test_decode_configs(cfg):
+    wl = make_config(cfg)
+    if cfg == 0:
+        # the decode row of the tiny config: query row 1023 at position 1023
+        wl = make_workload(mode="decode", io_dtype="fp32", lens=[1024], num_q_heads=16,
+                           num_kv_heads=1, topk=8, init_blocks=1, local_blocks=2, n_planted=4, seed=0)
+    _run_decode(wl, label=f"config {cfg} decode")
+
+
+def test_decode_max_blocks_per_sequence():
+    wl = _small(lens=[16384 * 64], hkv=1, topk=64, local=4, seed=28, n_planted=8)
+    _run_decode(wl, label="decode 16384 blocks")
+
+
+# ---------------------------------------------------------------------------- prefill
+def _run_prefill(wl, chunk, ck_dtype="fp32", positions=None, label="prefill"):
+    h = _harness()
+    L = int(wl.lens[0])
+    _say(f"{label}: L={L} chunk={chunk} io={wl.io_dtype} ck={ck_dtype} k={wl.topk}")
+    dev = h.DeviceWorkload(wl, ck_dtype)
+    idx_t, score_t, out_t = dev.prefill(chunk)
+    torch.cuda.synchronize()
+    idx = idx_t.cpu().numpy().astype(np.int64)
+    score = score_t.cpu().numpy().astype(np.float64)
+    out = h.from_device(out_t, wl.io_dtype)
+    prm = params_of(wl, ck_dtype)
+    K, V = wl.k_f64(0), wl.v_f64(0)
+    ck = dev.ck_host()[0]
+    assert np.array_equal(ck, ref.compress_keys(K, wl.kernel_size, wl.kernel_stride, ck_dtype)), \
+        f"{label}: compressed keys differ"
+    pos = list(range(L)) if positions is None else list(positions)
+    q = wl.q_f64()
+    G = prm.group
+    rows, idx_rows, score_rows = [], [], []
+    for i in pos:
+        for g in range(wl.num_kv_heads):
+            rows.append(ref.select_row(q[i, g * G:(g + 1) * G], ck[g], i, prm))
+            idx_rows.append(idx[i, g])
+            score_rows.append(score[i, g])
+    _check_rows(np.array(idx_rows), np.array(score_rows), rows, label)
+    want = ref.attend_with_selection(q[pos], K, V, pos, idx[pos], prm)
+    err = assert_close(out[pos], want, wl.io_dtype, label)
+    _say(f"{label}: output max abs err {err:.2e} over {len(pos)} rows")
+    return dev, idx, out
+
+
+def test_prefill_config0_all_rows_and_chunking():
+    wl = make_config(0)
+    _, idx_a, out_a = _run_prefill(wl, 1024, label="config 0 prefill")
+    h = _harness()
+    _say("config 0 prefill, 4 chunks of 256 vs one chunk")
+    dev = h.DeviceWorkload(wl)
+    idx_t, _, out_t = dev.prefill(256)
+    assert np.array_equal(idx_t.cpu().numpy(), idx_a)
+    assert np.array_equal(h.from_device(out_t, "fp32"), out_a)
+
+
+def test_prefill_small_bf16_ragged_chunks():
+    wl = _small(mode="prefill", lens=[1000], topk=6, local=1, init=1, seed=31,
+                score_scale=1 / math.sqrt(128))
+    _run_prefill(wl, 300, label="prefill bf16 ragged chunks")
+
+
+def test_prefill_bf16_ck_and_forced_only():
+    wl = _small(mode="prefill", lens=[777], topk=8, local=2, seed=32)
+    _run_prefill(wl, 777, ck_dtype="bf16", label="prefill ck-bf16")
+    wl = _small(mode="prefill", lens=[600], topk=3, local=2, seed=33)
+    _run_prefill(wl, 250, label="prefill forced-only")
+
+
+def test_prefill_config3_sampled_rows():
+    wl = make_config(3)
+    rng = np.random.default_rng(303)
+    L = int(wl.lens[0])
+    pos = sorted(set(rng.integers(0, L, 48).tolist()) | set(range(L - 160, L))
+                 | {0, 63, 64, 4095, 4096, 4097, 8191})
+    _run_prefill(wl, wl.chunk, positions=pos, label="config 3 prefill")
+
+
+def test_decode_equals_last_prefill_row():
+    h = _harness()
+    wl = _small(mode="prefill", lens=[1500], topk=8, local=2, seed=34)
+    _say("decode vs prefill last row")
+    dev = h.DeviceWorkload(wl)
+    idx_p, _, out_p = dev.prefill(512)
+    wd = _small(mode="decode", lens=[1500], topk=8, local=2, seed=34)
+    # same K/V; query of the decode row = last prefill row
+    wd.k, wd.v = wl.k, wl.v
+    wd.q = wl.q[-1:].copy()
+    devd = h.DeviceWorkload(wd)
+    devd.compress()
+    idx_d, _ = devd.select_decode()
+    out_d = devd.attn_decode(idx_d)
+    assert np.array_equal(idx_d.cpu().numpy()[0], idx_p.cpu().numpy()[-1])
+    assert_close(h.from_device(out_d, "bf16")[0], h.from_device(out_p, "bf16")[-1], "bf16",
+                 "decode vs prefill")

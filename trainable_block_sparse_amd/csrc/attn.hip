@@ -1,0 +1,238 @@
+// Exact softmax attention over the selected blocks.  MiniCPM4 summary page,
+// "InfLLM v2" section, "Complexity analysis" (Stage 2: each query token attends
+// the k*m tokens of its selected blocks) and "Query group sharing" (the 16 heads
+// of a group read the same blocks, so K/V of a block is loaded once per group).
+//
+// Both kernels stage 64-token K/V tiles of a selected block in LDS and keep an
+// online softmax (running max, running sum, unnormalised output) per head.
+//   attn_decode_kernel   grid (split, KV head, sequence): each block handles
+//                        kBlocksPerSplit of the selected blocks; the last
+//                        block of a (sequence, KV head) merges the partial
+//                        (max, sum, output) triples by their LogSumExp.
+//   attn_prefill_kernel  grid (row, KV head): all selected blocks of one row,
+//                        causal within the query's own block (t <= i).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace infv2 {
+
+constexpr int kBlocksPerSplit = 4;
+constexpr int kTok = 64;             // tokens per LDS tile
+
+AttnDecodeWs attn_decode_ws(const Shape& sh, int batch) {
+    AttnDecodeWs w{};
+    w.nsplit = (sh.topk + kBlocksPerSplit - 1) / kBlocksPerSplit;
+    const size_t bg = static_cast<size_t>(batch) * sh.hkv;
+    size_t off = 0;
+    w.part_o = off;   off += align256(bg * w.nsplit * kGroup * kHeadDim * sizeof(float));
+    w.part_ml = off;  off += align256(bg * w.nsplit * kGroup * sizeof(float2));
+    w.counters = off; off += align256(bg * sizeof(uint32_t));
+    w.total = off;
+    return w;
+}
+
+struct AttnSmem {
+    float qs[kGroup][kHeadDim];
+    float ks[kTok][kHeadDim + 1];
+    float vs[kTok][kHeadDim];
+    float ps[kGroup][kTok];
+};
+
+// Online-softmax accumulation of selected blocks idx[jb..je) for the group's
+// 16 heads at query position i over keys [0, n).  Thread t owns head t/16 and
+// output columns (t%16)*8 .. +8.
+template <typename T>
+__device__ void attend_blocks(AttnSmem& sm, const T* __restrict__ kh, const T* __restrict__ vh,
+                              const int32_t* __restrict__ sel, int jb, int je, int64_t i,
+                              int64_t n, int m, float scale, float (&o)[8], float& mrun,
+                              float& lrun) {
+    const int t = threadIdx.x;
+    const int h = t >> 4, c0 = (t & 15) * 8;
+    const int w = t >> 6, lane = t & 63;
+    const int64_t lim = (i + 1 < n) ? i + 1 : n;   // keys t < min(i+1, n)
+    for (int e = jb; e < je; ++e) {
+        const int32_t blk = sel[e];
+        if (blk < 0) continue;
+        for (int sub = 0; sub < m; sub += kTok) {
+            const int64_t t0 = static_cast<int64_t>(blk) * m + sub;
+            int64_t cnt = lim - t0;
+            const int64_t in_blk = m - sub;
+            cnt = cnt < in_blk ? cnt : in_blk;
+            cnt = cnt < kTok ? cnt : kTok;
+            if (cnt <= 0) continue;
+            __syncthreads();
+            for (int x = t * 4; x < kTok * kHeadDim; x += 256 * 4) {
+                const int r = x / kHeadDim, col = x % kHeadDim;
+                float kv[4] = {0.f, 0.f, 0.f, 0.f}, vv[4] = {0.f, 0.f, 0.f, 0.f};
+                if (r < cnt) {
+                    load4(kh + (t0 + r) * kHeadDim + col, kv);
+                    load4(vh + (t0 + r) * kHeadDim + col, vv);
+                }
+                sm.ks[r][col] = kv[0]; sm.ks[r][col + 1] = kv[1];
+                sm.ks[r][col + 2] = kv[2]; sm.ks[r][col + 3] = kv[3];
+                *reinterpret_cast<float4*>(&sm.vs[r][col]) = make_float4(vv[0], vv[1], vv[2], vv[3]);
+            }
+            __syncthreads();
+            // scores: thread -> key `lane`, heads w, w+4, w+8, w+12
+            {
+                float acc[4] = {0.f, 0.f, 0.f, 0.f};
+                for (int d = 0; d < kHeadDim; ++d) {
+                    const float kd = sm.ks[lane][d];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acc[u] = fmaf(sm.qs[w + 4 * u][d], kd, acc[u]);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) sm.ps[w + 4 * u][lane] = lane < cnt ? scale * acc[u] : -INFINITY;
+            }
+            __syncthreads();
+            // softmax update for head h (16 threads per head, 4 keys each)
+            float sv[4];
+            float mt = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) { sv[u] = sm.ps[h][(t & 15) * 4 + u]; mt = fmaxf(mt, sv[u]); }
+            mt = max16(mt);
+            const float mnew = fmaxf(mrun, mt);
+            const float alpha = (mrun == -INFINITY) ? 0.f : expf(mrun - mnew);
+            float ls = 0.f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float pe = (sv[u] == -INFINITY) ? 0.f : expf(sv[u] - mnew);
+                ls += pe;
+                sv[u] = pe;
+            }
+            ls = sum16(ls);
+            lrun = lrun * alpha + ls;
+            mrun = mnew;
+#pragma unroll
+            for (int x = 0; x < 8; ++x) o[x] *= alpha;
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sm.ps[h][(t & 15) * 4 + u] = sv[u];
+            __syncthreads();
+            for (int r = 0; r < cnt; ++r) {
+                const float pr = sm.ps[h][r];
+                const float4 v0 = *reinterpret_cast<const float4*>(&sm.vs[r][c0]);
+                const float4 v1 = *reinterpret_cast<const float4*>(&sm.vs[r][c0 + 4]);
+                o[0] = fmaf(pr, v0.x, o[0]); o[1] = fmaf(pr, v0.y, o[1]);
+                o[2] = fmaf(pr, v0.z, o[2]); o[3] = fmaf(pr, v0.w, o[3]);
+                o[4] = fmaf(pr, v1.x, o[4]); o[5] = fmaf(pr, v1.y, o[5]);
+                o[6] = fmaf(pr, v1.z, o[6]); o[7] = fmaf(pr, v1.w, o[7]);
+            }
+        }
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void load_q_group(AttnSmem& sm, const T* qg) {
+    for (int e = threadIdx.x; e < kGroup * kHeadDim; e += 256) sm.qs[e / kHeadDim][e % kHeadDim] = io<T>::load(qg + e);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void attn_decode_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int64_t* __restrict__ kv_off, const int64_t* __restrict__ kv_lens,
+    const int32_t* __restrict__ idx, T* __restrict__ out, float* __restrict__ part_o,
+    float2* __restrict__ part_ml, uint32_t* __restrict__ counters, int hq, int hkv, int m,
+    int topk, int nsplit, float scale) {
+    __shared__ AttnSmem sm;
+    __shared__ uint32_t s_last;
+    const int b = blockIdx.z, g = blockIdx.y, sp = blockIdx.x, t = threadIdx.x;
+    const int64_t o0 = kv_off[b], cap = kv_off[b + 1] - o0;
+    int64_t n = kv_lens ? kv_lens[b] : cap;
+    n = n < cap ? n : cap;
+    const size_t bg = static_cast<size_t>(b) * hkv + g;
+    const T* kh = k + (o0 * hkv + static_cast<int64_t>(g) * cap) * kHeadDim;
+    const T* vh = v + (o0 * hkv + static_cast<int64_t>(g) * cap) * kHeadDim;
+    load_q_group(sm, q + (static_cast<size_t>(b) * hq + static_cast<size_t>(g) * kGroup) * kHeadDim);
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float mrun = -INFINITY, lrun = 0.f;
+    const int jb = sp * kBlocksPerSplit;
+    const int je = (jb + kBlocksPerSplit < topk) ? jb + kBlocksPerSplit : topk;
+    attend_blocks<T>(sm, kh, vh, idx + bg * topk, jb, je, n - 1, n, m, scale, o, mrun, lrun);
+
+    const int h = t >> 4, c0 = (t & 15) * 8;
+    float* po = part_o + ((bg * nsplit + sp) * kGroup + h) * kHeadDim + c0;
+    *reinterpret_cast<float4*>(po) = make_float4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<float4*>(po + 4) = make_float4(o[4], o[5], o[6], o[7]);
+    if ((t & 15) == 0) part_ml[(bg * nsplit + sp) * kGroup + h] = make_float2(mrun, lrun);
+
+    __threadfence();
+    __syncthreads();
+    if (t == 0) s_last = (atomicAdd(&counters[bg], 1u) == static_cast<uint32_t>(nsplit - 1));
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    float mx = -INFINITY;
+    for (int x = 0; x < nsplit; ++x) mx = fmaxf(mx, part_ml[(bg * nsplit + x) * kGroup + h].x);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+    if (mx != -INFINITY) {
+        for (int x = 0; x < nsplit; ++x) {
+            const float2 ml = part_ml[(bg * nsplit + x) * kGroup + h];
+            if (ml.x == -INFINITY) continue;
+            const float wgt = expf(ml.x - mx);
+            den += wgt * ml.y;
+            const float* src = part_o + ((bg * nsplit + x) * kGroup + h) * kHeadDim + c0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = fmaf(wgt, src[e], acc[e]);
+        }
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    T* dst = out + (static_cast<size_t>(b) * hq + static_cast<size_t>(g) * kGroup + h) * kHeadDim + c0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) io<T>::store(dst + e, acc[e] * inv);
+    if (t == 0) counters[bg] = 0u;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void attn_prefill_kernel(
+    const T* __restrict__ q, int64_t q_start, const T* __restrict__ k, const T* __restrict__ v,
+    const int64_t* __restrict__ kv_off, const int32_t* __restrict__ idx, T* __restrict__ out,
+    int hq, int hkv, int m, int topk, float scale) {
+    __shared__ AttnSmem sm;
+    const int row = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
+    const int64_t o0 = kv_off[0], cap = kv_off[1] - o0;
+    const T* kh = k + (o0 * hkv + static_cast<int64_t>(g) * cap) * kHeadDim;
+    const T* vh = v + (o0 * hkv + static_cast<int64_t>(g) * cap) * kHeadDim;
+    load_q_group(sm, q + (static_cast<size_t>(row) * hq + static_cast<size_t>(g) * kGroup) * kHeadDim);
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float mrun = -INFINITY, lrun = 0.f;
+    const size_t rg = static_cast<size_t>(row) * hkv + g;
+    attend_blocks<T>(sm, kh, vh, idx + rg * topk, 0, topk, q_start + row, cap, m, scale, o, mrun, lrun);
+    const int h = t >> 4, c0 = (t & 15) * 8;
+    const float inv = lrun > 0.f ? 1.f / lrun : 0.f;
+    T* dst = out + (static_cast<size_t>(row) * hq + static_cast<size_t>(g) * kGroup + h) * kHeadDim + c0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) io<T>::store(dst + e, o[e] * inv);
+}
+
+hipError_t launch_attn_decode(const Shape& sh, const void* q, const void* k, const void* v,
+                              const int64_t* kv_off, const int64_t* kv_lens, int batch,
+                              const int32_t* idx, void* out, void* ws, hipStream_t st) {
+    const AttnDecodeWs w = attn_decode_ws(sh, batch);
+    char* base = static_cast<char*>(ws);
+    dim3 grid(w.nsplit, sh.hkv, batch);
+    float* po = reinterpret_cast<float*>(base + w.part_o);
+    float2* pml = reinterpret_cast<float2*>(base + w.part_ml);
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(base + w.counters);
+    if (sh.io_bf16)
+        attn_decode_kernel<bf16_t><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), kv_off, kv_lens, idx, static_cast<bf16_t*>(out), po, pml, cnt, sh.hq, sh.hkv, sh.m, sh.topk, w.nsplit, sh.attn_scale);
+    else
+        attn_decode_kernel<float><<<grid, 256, 0, st>>>(static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), kv_off, kv_lens, idx, static_cast<float*>(out), po, pml, cnt, sh.hq, sh.hkv, sh.m, sh.topk, w.nsplit, sh.attn_scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_prefill(const Shape& sh, const void* q, int rows, int64_t q_start,
+                               const void* k, const void* v, const int64_t* kv_off,
+                               const int32_t* idx, void* out, void* ws, hipStream_t st) {
+    (void)ws;
+    if (rows <= 0) return hipSuccess;
+    dim3 grid(rows, sh.hkv);
+    if (sh.io_bf16)
+        attn_prefill_kernel<bf16_t><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(q), q_start, static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), kv_off, idx, static_cast<bf16_t*>(out), sh.hq, sh.hkv, sh.m, sh.topk, sh.attn_scale);
+    else
+        attn_prefill_kernel<float><<<grid, 256, 0, st>>>(static_cast<const float*>(q), q_start, static_cast<const float*>(k), static_cast<const float*>(v), kv_off, idx, static_cast<float*>(out), sh.hq, sh.hkv, sh.m, sh.topk, sh.attn_scale);
+    return hipGetLastError();
+}
+
+}  // namespace infv2

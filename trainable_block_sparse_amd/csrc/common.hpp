@@ -1,0 +1,104 @@
+// Device helpers shared by the InfLLM v2 HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kernels.hpp"
+
+namespace infv2 {
+
+constexpr int kWave = 64;
+
+typedef uint16_t bf16_t;          // bf16 carried as its bit pattern
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// round to nearest even (gfx950 has a hardware conversion for this)
+__device__ __forceinline__ bf16_t f32_to_bf16(float x) {
+    __bf16 h = static_cast<__bf16>(x);
+    return __builtin_bit_cast(bf16_t, h);
+}
+
+template <typename T> struct io;
+template <> struct io<float> {
+    __device__ static __forceinline__ float load(const float* p) { return *p; }
+    __device__ static __forceinline__ void store(float* p, float v) { *p = v; }
+};
+template <> struct io<bf16_t> {
+    __device__ static __forceinline__ float load(const bf16_t* p) { return bf16_to_f32(*p); }
+    __device__ static __forceinline__ void store(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+// load 4 consecutive elements as floats (16-byte aligned for float, 8-byte for bf16)
+__device__ __forceinline__ void load4(const float* p, float* o) {
+    float4 v = *reinterpret_cast<const float4*>(p);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+}
+__device__ __forceinline__ void load4(const bf16_t* p, float* o) {
+    uint2 v = *reinterpret_cast<const uint2*>(p);
+    o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
+    o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+
+// ---------------------------------------------------------------- scores as sortable keys
+// Block scores are >= 0 or -inf ("no visible kernel").  key = bits + 1 keeps the
+// order of non-negative floats and maps -inf to 0, the smallest key.
+__device__ __forceinline__ uint32_t score_to_key(float s) {
+    return (s == -INFINITY) ? 0u : (__float_as_uint(s) + 1u);
+}
+__device__ __forceinline__ float key_to_score(uint32_t k) {
+    return k == 0u ? -INFINITY : __uint_as_float(k - 1u);
+}
+
+// ---------------------------------------------------------------- method arithmetic helpers
+__device__ __forceinline__ int64_t num_kernels(int64_t n, int p, int s) {
+    return n < p ? 0 : (n - p) / s + 1;
+}
+
+// ---------------------------------------------------------------- wave reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+// reductions over aligned groups of 16 lanes
+__device__ __forceinline__ float max16(float v) {
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float sum16(float v) {
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// inclusive prefix sum over the 256 threads of a block (4 waves); `tmp` holds 4 words
+__device__ __forceinline__ uint32_t block_incl_scan256(uint32_t v, uint32_t* tmp) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        uint32_t u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
+    }
+    if (lane == 63) tmp[wid] = v;
+    __syncthreads();
+    uint32_t add = 0;
+    for (int w = 0; w < wid; ++w) add += tmp[w];
+    __syncthreads();
+    return v + add;
+}
+
+}  // namespace infv2

@@ -1,0 +1,89 @@
+// Compressed keys: kbar_j = Mean(K[j*s : j*s + p]) for every complete kernel j.
+// MiniCPM4 summary page, "InfLLM v2" section, paragraph "Semantic kernels for
+// block relevance scoring" (eq. S, "What this computes", "Why mean pooling").
+//
+// HBM-streaming kernel: each 256-thread block owns 16 consecutive kernels of one
+// (sequence, KV head); 32 threads cover one 128-wide key row with 4 lanes of
+// d each.  The p keys of a kernel are summed in float64 (exact for bf16 keys and
+// for p up to 2^21), divided by p, and rounded once to the storage type.  The
+// overlapping tokens (p > s) are re-read from L1/L2, so HBM sees each key once.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace infv2 {
+
+constexpr int kCompressKpb = 16;   // kernels per thread block
+
+// float64 -> bf16, one rounding to nearest even (including the subnormal range)
+__device__ __forceinline__ bf16_t f64_to_bf16(double x) {
+    if (x == 0.0 || !isfinite(x)) return f32_to_bf16(static_cast<float>(x));
+    int e;
+    frexp(x, &e);                         // |x| in [2^(e-1), 2^e)
+    const int ulp_exp = max(e - 1, -126) - 7;
+    const double y = ldexp(rint(ldexp(x, -ulp_exp)), ulp_exp);
+    const float f = static_cast<float>(y);   // exact (8 significant bits), or inf on overflow
+    return static_cast<bf16_t>(__float_as_uint(f) >> 16);
+}
+
+template <typename Tin, bool kCkBf16>
+__global__ __launch_bounds__(256) void compress_kernel(
+    const Tin* __restrict__ k, const int64_t* __restrict__ kv_off,
+    const int64_t* __restrict__ kv_lens, const int64_t* __restrict__ ck_off,
+    const int64_t* __restrict__ ck_begin, void* __restrict__ ck_out, int hkv, int p, int s) {
+    const int b = blockIdx.z, h = blockIdx.y;
+    const int64_t o0 = kv_off[b], cap = kv_off[b + 1] - o0;
+    int64_t n = kv_lens ? kv_lens[b] : cap;
+    n = n < cap ? n : cap;
+    const int64_t nc = num_kernels(n, p, s);
+    const int64_t c0 = ck_off[b], ccap = ck_off[b + 1] - c0;
+    const int64_t jb = ck_begin ? ck_begin[b] : 0;
+    const int col = (threadIdx.x & 31) * 4;
+    const Tin* kh = k + (o0 * hkv + static_cast<int64_t>(h) * cap) * kHeadDim + col;
+
+    for (int r = threadIdx.x >> 5; r < kCompressKpb; r += 8) {
+        const int64_t j = jb + static_cast<int64_t>(blockIdx.x) * kCompressKpb + r;
+        if (j < 0 || j >= nc || j >= ccap) continue;
+        double acc0 = 0.0, acc1 = 0.0, acc2 = 0.0, acc3 = 0.0;
+        const Tin* src = kh + j * s * kHeadDim;
+        for (int t = 0; t < p; ++t) {
+            float v[4];
+            load4(src + static_cast<int64_t>(t) * kHeadDim, v);
+            acc0 += v[0]; acc1 += v[1]; acc2 += v[2]; acc3 += v[3];
+        }
+        const double pd = static_cast<double>(p);
+        const double m0 = acc0 / pd, m1 = acc1 / pd, m2 = acc2 / pd, m3 = acc3 / pd;
+        const int64_t dst = ((c0 * hkv + static_cast<int64_t>(h) * ccap) + j) * kHeadDim + col;
+        if (kCkBf16) {
+            bf16_t* o = static_cast<bf16_t*>(ck_out) + dst;
+            uint2 w;
+            w.x = static_cast<uint32_t>(f64_to_bf16(m0)) | (static_cast<uint32_t>(f64_to_bf16(m1)) << 16);
+            w.y = static_cast<uint32_t>(f64_to_bf16(m2)) | (static_cast<uint32_t>(f64_to_bf16(m3)) << 16);
+            *reinterpret_cast<uint2*>(o) = w;
+        } else {
+            float* o = static_cast<float*>(ck_out) + dst;
+            *reinterpret_cast<float4*>(o) = make_float4(static_cast<float>(m0), static_cast<float>(m1),
+                                                        static_cast<float>(m2), static_cast<float>(m3));
+        }
+    }
+}
+
+hipError_t launch_compress(const Shape& sh, const void* k, const int64_t* kv_off,
+                           const int64_t* kv_lens, const int64_t* ck_off, const int64_t* ck_begin,
+                           int batch, int64_t max_new, void* ck, hipStream_t st) {
+    if (max_new <= 0) return hipSuccess;
+    dim3 grid(static_cast<unsigned>((max_new + kCompressKpb - 1) / kCompressKpb), sh.hkv, batch);
+    if (sh.io_bf16) {
+        if (sh.ck_bf16)
+            compress_kernel<bf16_t, true><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(k), kv_off, kv_lens, ck_off, ck_begin, ck, sh.hkv, sh.p, sh.s);
+        else
+            compress_kernel<bf16_t, false><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(k), kv_off, kv_lens, ck_off, ck_begin, ck, sh.hkv, sh.p, sh.s);
+    } else {
+        if (sh.ck_bf16)
+            compress_kernel<float, true><<<grid, 256, 0, st>>>(static_cast<const float*>(k), kv_off, kv_lens, ck_off, ck_begin, ck, sh.hkv, sh.p, sh.s);
+        else
+            compress_kernel<float, false><<<grid, 256, 0, st>>>(static_cast<const float*>(k), kv_off, kv_lens, ck_off, ck_begin, ck, sh.hkv, sh.p, sh.s);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace infv2

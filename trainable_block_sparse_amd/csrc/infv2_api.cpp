@@ -1,0 +1,181 @@
+// extern "C" entry points of libinfv2: host-side validation, workspace sizing
+// and dispatch to the HIP launchers.  Every check runs before the first HIP
+// call, so an invalid call enqueues nothing.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "../../include/infv2.h"
+#include "kernels.hpp"
+
+using infv2::Shape;
+
+namespace {
+
+constexpr int64_t kMaxBlocks = 16384;   // per sequence (top-k keys per row)
+constexpr int kMaxTopk = 1024;
+
+bool dtype_ok(int32_t d) { return d == INFV2_FP32 || d == INFV2_BF16; }
+
+int32_t check_config(const infv2_config* c) {
+    if (!c) return INFV2_ERR_NULL;
+    if (c->head_dim <= 0 || c->num_q_heads <= 0 || c->num_kv_heads <= 0 || c->block_size <= 0 ||
+        c->kernel_size <= 0 || c->kernel_stride <= 0 || c->topk <= 0 || c->init_blocks < 0 ||
+        c->local_blocks < 0)
+        return INFV2_ERR_SHAPE;
+    if (c->num_q_heads % c->num_kv_heads != 0) return INFV2_ERR_SHAPE;
+    if (c->kernel_size < c->kernel_stride) return INFV2_ERR_SHAPE;
+    if (c->topk < static_cast<int64_t>(c->init_blocks) + c->local_blocks) return INFV2_ERR_SHAPE;
+    if (!dtype_ok(c->io_dtype) || !dtype_ok(c->ck_dtype)) return INFV2_ERR_SHAPE;
+    if (!isfinite(c->score_scale) || !isfinite(c->attn_scale)) return INFV2_ERR_SHAPE;
+    // implemented subset
+    if (c->head_dim != infv2::kHeadDim) return INFV2_ERR_UNSUPPORTED;
+    if (c->num_q_heads / c->num_kv_heads != infv2::kGroup) return INFV2_ERR_UNSUPPORTED;
+    if (c->block_size % 16 != 0 || c->block_size > 256) return INFV2_ERR_UNSUPPORTED;
+    if (c->kernel_size > 256) return INFV2_ERR_UNSUPPORTED;
+    if (c->topk > kMaxTopk) return INFV2_ERR_UNSUPPORTED;
+    return INFV2_OK;
+}
+
+int32_t check_len(const infv2_config* c, int64_t max_len) {
+    if (max_len < 0) return INFV2_ERR_SHAPE;
+    if ((max_len + c->block_size - 1) / c->block_size > kMaxBlocks) return INFV2_ERR_UNSUPPORTED;
+    return INFV2_OK;
+}
+
+Shape make_shape(const infv2_config* c) {
+    Shape s;
+    s.hq = c->num_q_heads; s.hkv = c->num_kv_heads; s.d = c->head_dim;
+    s.m = c->block_size; s.p = c->kernel_size; s.s = c->kernel_stride;
+    s.topk = c->topk; s.init = c->init_blocks; s.local = c->local_blocks;
+    s.io_bf16 = c->io_dtype == INFV2_BF16; s.ck_bf16 = c->ck_dtype == INFV2_BF16;
+    s.score_scale = c->score_scale; s.attn_scale = c->attn_scale;
+    return s;
+}
+
+int32_t status_of(hipError_t e) { return e == hipSuccess ? INFV2_OK : INFV2_ERR_DEVICE; }
+
+size_t ws_bytes_for(const infv2_config* c, int32_t op, int32_t rows, int32_t batch, int64_t max_len) {
+    const Shape sh = make_shape(c);
+    switch (op) {
+        case INFV2_OP_SELECT_DECODE: return infv2::select_decode_ws(sh, batch, max_len).total;
+        case INFV2_OP_SELECT_PREFILL: return infv2::select_prefill_ws(sh, rows, max_len).total;
+        case INFV2_OP_ATTN_DECODE: return infv2::attn_decode_ws(sh, batch).total;
+        default: return 0;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t infv2_abi_version(void) { return INFV2_ABI_VERSION; }
+
+const char* infv2_status_str(int32_t s) {
+    switch (s) {
+        case INFV2_OK: return "INFV2_OK";
+        case INFV2_ERR_NULL: return "INFV2_ERR_NULL: a required pointer is NULL";
+        case INFV2_ERR_SHAPE: return "INFV2_ERR_SHAPE: inconsistent sizes or parameters";
+        case INFV2_ERR_UNSUPPORTED: return "INFV2_ERR_UNSUPPORTED: valid but not implemented on this path";
+        case INFV2_ERR_WORKSPACE: return "INFV2_ERR_WORKSPACE: workspace missing or too small";
+        case INFV2_ERR_DEVICE: return "INFV2_ERR_DEVICE: a HIP launch failed";
+        default: return "INFV2: unknown status";
+    }
+}
+
+int64_t infv2_num_kernels(const infv2_config* c, int64_t n) {
+    if (!c || c->kernel_size <= 0 || c->kernel_stride <= 0 || n < c->kernel_size) return 0;
+    return (n - c->kernel_size) / c->kernel_stride + 1;
+}
+
+int32_t infv2_workspace_bytes(const infv2_config* c, int32_t op, int32_t rows, int32_t batch,
+                              int64_t max_len, size_t* bytes) {
+    if (!bytes) return INFV2_ERR_NULL;
+    int32_t st = check_config(c);
+    if (st != INFV2_OK) return st;
+    if ((st = check_len(c, max_len)) != INFV2_OK) return st;
+    if (op < INFV2_OP_COMPRESS || op > INFV2_OP_ATTN_PREFILL || rows < 0 || batch < 0) return INFV2_ERR_SHAPE;
+    *bytes = ws_bytes_for(c, op, rows, batch, max_len);
+    return INFV2_OK;
+}
+
+int32_t infv2_compress_keys(const infv2_config* c, const void* k, const int64_t* kv_offsets,
+                            const int64_t* kv_lens, const int64_t* ck_offsets,
+                            const int64_t* ck_begin, int32_t batch, int64_t max_len,
+                            int64_t max_new, void* ck, void* stream) {
+    int32_t st = check_config(c);
+    if (st != INFV2_OK) return st;
+    if (!k || !kv_offsets || !ck_offsets || !ck) return INFV2_ERR_NULL;
+    if (batch < 1) return INFV2_ERR_SHAPE;
+    if ((st = check_len(c, max_len)) != INFV2_OK) return st;
+    const int64_t nc = infv2_num_kernels(c, max_len);
+    if (max_new < 0 || max_new > nc) max_new = nc;
+    return status_of(infv2::launch_compress(make_shape(c), k, kv_offsets, kv_lens, ck_offsets,
+                                            ck_begin, batch, max_new, ck,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int32_t infv2_select_blocks(const infv2_config* c, int32_t mode, const void* q, int32_t rows,
+                            int64_t q_start, const void* ck, const int64_t* ck_offsets,
+                            const int64_t* kv_offsets, const int64_t* kv_lens, int32_t batch,
+                            int64_t max_len, int32_t* block_idx, float* block_score, void* ws,
+                            size_t ws_bytes, void* stream) {
+    int32_t st = check_config(c);
+    if (st != INFV2_OK) return st;
+    if (!q || !ck || !ck_offsets || !block_idx) return INFV2_ERR_NULL;
+    if ((st = check_len(c, max_len)) != INFV2_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (mode == INFV2_MODE_DECODE) {
+        if (!kv_offsets) return INFV2_ERR_NULL;
+        if (batch < 1 || rows != batch) return INFV2_ERR_SHAPE;
+        const size_t need = ws_bytes_for(c, INFV2_OP_SELECT_DECODE, rows, batch, max_len);
+        if (!ws || ws_bytes < need) return INFV2_ERR_WORKSPACE;
+        return status_of(infv2::launch_select_decode(make_shape(c), q, ck, ck_offsets, kv_offsets,
+                                                     kv_lens, batch, max_len, block_idx,
+                                                     block_score, ws, s));
+    }
+    if (mode == INFV2_MODE_PREFILL) {
+        if (batch != 1 || rows < 0 || q_start < 0) return INFV2_ERR_SHAPE;
+        if (q_start + rows > max_len) return INFV2_ERR_SHAPE;
+        if (rows == 0) return INFV2_OK;
+        const size_t need = ws_bytes_for(c, INFV2_OP_SELECT_PREFILL, rows, batch, max_len);
+        if (!ws || ws_bytes < need) return INFV2_ERR_WORKSPACE;
+        return status_of(infv2::launch_select_prefill(make_shape(c), q, rows, q_start, ck,
+                                                      ck_offsets, max_len, block_idx, block_score,
+                                                      ws, s));
+    }
+    return INFV2_ERR_SHAPE;
+}
+
+int32_t infv2_sparse_attn_decode(const infv2_config* c, const void* q, const void* k,
+                                 const void* v, const int64_t* kv_offsets, const int64_t* kv_lens,
+                                 int32_t batch, int64_t max_len, const int32_t* block_idx,
+                                 void* out, void* ws, size_t ws_bytes, void* stream) {
+    int32_t st = check_config(c);
+    if (st != INFV2_OK) return st;
+    if (!q || !k || !v || !kv_offsets || !block_idx || !out) return INFV2_ERR_NULL;
+    if (batch < 1) return INFV2_ERR_SHAPE;
+    if ((st = check_len(c, max_len)) != INFV2_OK) return st;
+    const size_t need = ws_bytes_for(c, INFV2_OP_ATTN_DECODE, batch, batch, max_len);
+    if (!ws || ws_bytes < need) return INFV2_ERR_WORKSPACE;
+    return status_of(infv2::launch_attn_decode(make_shape(c), q, k, v, kv_offsets, kv_lens, batch,
+                                               block_idx, out, ws,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int32_t infv2_sparse_attn_prefill(const infv2_config* c, const void* q, int32_t rows,
+                                  int64_t q_start, const void* k, const void* v,
+                                  const int64_t* kv_offsets, const int32_t* block_idx, void* out,
+                                  void* ws, size_t ws_bytes, void* stream) {
+    int32_t st = check_config(c);
+    if (st != INFV2_OK) return st;
+    if (!q || !k || !v || !kv_offsets || !block_idx || !out) return INFV2_ERR_NULL;
+    if (rows < 0 || q_start < 0) return INFV2_ERR_SHAPE;
+    if ((st = check_len(c, q_start + rows)) != INFV2_OK) return st;
+    (void)ws_bytes;
+    if (rows == 0) return INFV2_OK;
+    return status_of(infv2::launch_attn_prefill(make_shape(c), q, rows, q_start, k, v, kv_offsets,
+                                                block_idx, out, ws,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

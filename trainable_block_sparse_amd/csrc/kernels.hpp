@@ -1,0 +1,63 @@
+// Host-side launchers of the HIP kernels (defined in the .hip files).
+// Arguments are already validated by the entry points in infv2_api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace infv2 {
+
+constexpr int kHeadDim = 128;     // d supported by the kernels
+constexpr int kGroup = 16;        // query heads per KV head supported by the kernels
+
+struct Shape {
+    int hq, hkv, d, m, p, s, topk, init, local;
+    int io_bf16, ck_bf16;
+    float score_scale, attn_scale;
+};
+
+// workspace carving (all offsets 256-byte aligned)
+struct SelectDecodeWs {
+    size_t logits, partial, lse, keys, counters, total;
+    int nchunk_a, nchunk_b;
+    int64_t nc_max, nblk_max;
+};
+SelectDecodeWs select_decode_ws(const Shape& sh, int batch, int64_t max_len);
+
+struct SelectPrefillWs {
+    size_t lse, keys, total;
+    int64_t nblk_max;
+};
+SelectPrefillWs select_prefill_ws(const Shape& sh, int rows, int64_t max_len);
+
+struct AttnDecodeWs {
+    size_t part_o, part_ml, counters, total;
+    int nsplit;
+};
+AttnDecodeWs attn_decode_ws(const Shape& sh, int batch);
+
+hipError_t launch_compress(const Shape& sh, const void* k, const int64_t* kv_off,
+                           const int64_t* kv_lens, const int64_t* ck_off, const int64_t* ck_begin,
+                           int batch, int64_t max_new, void* ck, hipStream_t st);
+
+hipError_t launch_select_decode(const Shape& sh, const void* q, const void* ck,
+                                const int64_t* ck_off, const int64_t* kv_off,
+                                const int64_t* kv_lens, int batch, int64_t max_len,
+                                int32_t* idx, float* score, void* ws, hipStream_t st);
+
+hipError_t launch_select_prefill(const Shape& sh, const void* q, int rows, int64_t q_start,
+                                 const void* ck, const int64_t* ck_off, int64_t max_len,
+                                 int32_t* idx, float* score, void* ws, hipStream_t st);
+
+hipError_t launch_attn_decode(const Shape& sh, const void* q, const void* k, const void* v,
+                              const int64_t* kv_off, const int64_t* kv_lens, int batch,
+                              const int32_t* idx, void* out, void* ws, hipStream_t st);
+
+hipError_t launch_attn_prefill(const Shape& sh, const void* q, int rows, int64_t q_start,
+                               const void* k, const void* v, const int64_t* kv_off,
+                               const int32_t* idx, void* out, void* ws, hipStream_t st);
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace infv2

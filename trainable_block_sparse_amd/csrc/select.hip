@@ -1,0 +1,470 @@
+// Block selection: kernel logits, per-head LogSumExp, group score, block max,
+// top-k with forced blocks.  MiniCPM4 summary page, "InfLLM v2" section:
+// "Semantic kernels" (eqs. r_kernel, r_block), "Query group sharing" (eq.
+// r_group), "Top-K implementation and the LSE bottleneck" (pass 1: LogSumExp
+// over all kernels; pass 2: normalised scores), "Initial and local tokens".
+//
+// Decode (one row per sequence, thousands of kernels per row):
+//   sel_dec_logits  grid (kernel chunk, KV head, sequence).  Each block scores
+//                   64 kernels against the group's 16 heads, stores the logits
+//                   (fp32 scratch, 16 x n_c floats per KV head: an eighth of a
+//                   fp32 compressed-key re-read) and a partial (max, sum-exp)
+//                   per head; the last block of each (sequence, head) to finish
+//                   folds the partials into the per-head LogSumExp.
+//   sel_dec_scores  grid (256-kernel chunk, KV head, sequence).  Group score
+//                   R_j = mean_h exp(z_hj - LSE_h), block max by atomicMax on
+//                   sortable keys; the last block runs the top-k.
+// Prefill (rows of one sequence, causal visibility per row):
+//   sel_pre_lse     4 rows per block: online (max, sum-exp) over visible kernels.
+//   sel_pre_scores  4 rows per block: logits again, group score, block max.
+//   sel_pre_topk    one block per (row, KV head).
+#include "common.hpp"
+#include "kernels.hpp"
+#include "topk.hpp"
+
+namespace infv2 {
+
+constexpr int kChunkA = 64;      // kernels per block in sel_dec_logits
+constexpr int kChunkB = 256;     // kernels per block in sel_dec_scores
+constexpr int kRowsPre = 4;      // query rows per block in the prefill passes
+constexpr int kTilePre = 64;     // kernels per LDS tile in the prefill passes
+
+__device__ __forceinline__ int64_t floor_div(int64_t a, int64_t b) {
+    return a >= 0 ? a / b : -((-a + b - 1) / b);
+}
+
+// first / last kernel meeting block `blk`: [j s, j s + p) and [blk m, (blk+1) m) share a token
+__device__ __forceinline__ int64_t first_kernel_of_block(int64_t blk, int m, int p, int s) {
+    const int64_t v = floor_div(blk * m - p, s) + 1;
+    return v > 0 ? v : 0;
+}
+__device__ __forceinline__ int64_t last_kernel_of_block(int64_t blk, int m, int s) {
+    return ((blk + 1) * m - 1) / s;
+}
+
+SelectDecodeWs select_decode_ws(const Shape& sh, int batch, int64_t max_len) {
+    SelectDecodeWs w{};
+    w.nc_max = max_len < sh.p ? 0 : (max_len - sh.p) / sh.s + 1;
+    w.nblk_max = (max_len + sh.m - 1) / sh.m;
+    if (w.nblk_max < 1) w.nblk_max = 1;
+    const int64_t ncm = w.nc_max > 0 ? w.nc_max : 1;
+    w.nchunk_a = static_cast<int>((ncm + kChunkA - 1) / kChunkA);
+    w.nchunk_b = static_cast<int>((ncm + kChunkB - 1) / kChunkB);
+    const size_t bg = static_cast<size_t>(batch) * sh.hkv;
+    size_t off = 0;
+    w.logits = off;   off += align256(bg * ncm * kGroup * sizeof(float));
+    w.partial = off;  off += align256(bg * w.nchunk_a * kGroup * sizeof(float2));
+    w.lse = off;      off += align256(bg * kGroup * sizeof(float));
+    w.keys = off;     off += align256(bg * w.nblk_max * sizeof(uint32_t));
+    w.counters = off; off += align256(bg * 2 * sizeof(uint32_t));
+    w.total = off;
+    return w;
+}
+
+SelectPrefillWs select_prefill_ws(const Shape& sh, int rows, int64_t max_len) {
+    SelectPrefillWs w{};
+    w.nblk_max = (max_len + sh.m - 1) / sh.m;
+    if (w.nblk_max < 1) w.nblk_max = 1;
+    size_t off = 0;
+    w.lse = off;  off += align256(static_cast<size_t>(rows) * sh.hq * sizeof(float));
+    w.keys = off; off += align256(static_cast<size_t>(rows) * sh.hkv * w.nblk_max * sizeof(uint32_t));
+    w.total = off;
+    return w;
+}
+
+// ------------------------------------------------------------------ decode, pass 1
+template <typename Tq, typename Tck>
+__global__ __launch_bounds__(256) void sel_dec_logits(
+    const Tq* __restrict__ q, const Tck* __restrict__ ck, const int64_t* __restrict__ ck_off,
+    const int64_t* __restrict__ kv_off, const int64_t* __restrict__ kv_lens, int hq, int hkv,
+    int p, int s, float score_scale, int64_t nc_max, int nchunk, int64_t nblk_max,
+    float* __restrict__ logits, float2* __restrict__ partial, float* __restrict__ lse,
+    uint32_t* __restrict__ keys, uint32_t* __restrict__ counters) {
+    __shared__ float qs[kGroup][kHeadDim];
+    __shared__ uint32_t s_last;
+    const int b = blockIdx.z, g = blockIdx.y, ch = blockIdx.x, t = threadIdx.x;
+    const int64_t cap = kv_off[b + 1] - kv_off[b];
+    int64_t n = kv_lens ? kv_lens[b] : cap;
+    n = n < cap ? n : cap;
+    const int64_t ccap = ck_off[b + 1] - ck_off[b];
+    int64_t nvis = num_kernels(n, p, s);          // row n-1 sees every complete kernel
+    nvis = nvis < ccap ? nvis : ccap;
+    nvis = nvis < nc_max ? nvis : nc_max;
+    const size_t bg = static_cast<size_t>(b) * hkv + g;
+
+    // clear this block's share of the block-score keys (filled by pass 2)
+    {
+        uint32_t* kb = keys + bg * nblk_max;
+        const int64_t per = (nblk_max + nchunk - 1) / nchunk;
+        const int64_t e = (ch + 1) * per < nblk_max ? (ch + 1) * per : nblk_max;
+        for (int64_t j = ch * per + t; j < e; j += 256) kb[j] = 0u;
+    }
+    const Tq* qg = q + (static_cast<size_t>(b) * hq + static_cast<size_t>(g) * kGroup) * kHeadDim;
+    for (int e = t; e < kGroup * kHeadDim; e += 256) qs[e / kHeadDim][e % kHeadDim] = io<Tq>::load(qg + e);
+    __syncthreads();
+
+    const int w = t >> 6, lane = t & 63;
+    const int64_t j = static_cast<int64_t>(ch) * kChunkA + lane;
+    float z[4];
+    if (j < nvis) {
+        const Tck* row = ck + ((ck_off[b] * hkv + static_cast<int64_t>(g) * ccap) + j) * kHeadDim;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int d = 0; d < kHeadDim; d += 4) {
+            float kv[4];
+            load4(row + d, kv);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float* qh = qs[w + 4 * u];
+                acc[u] = fmaf(qh[d], kv[0], acc[u]);
+                acc[u] = fmaf(qh[d + 1], kv[1], acc[u]);
+                acc[u] = fmaf(qh[d + 2], kv[2], acc[u]);
+                acc[u] = fmaf(qh[d + 3], kv[3], acc[u]);
+            }
+        }
+        float* dst = logits + (bg * nc_max + j) * kGroup;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            z[u] = score_scale * acc[u];
+            dst[w + 4 * u] = z[u];
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) z[u] = -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const float mx = wave_max(z[u]);
+        const float e = (j < nvis) ? expf(z[u] - mx) : 0.f;
+        const float sm = wave_sum(e);
+        if (lane == 0) partial[(bg * nchunk + ch) * kGroup + w + 4 * u] = make_float2(mx, sm);
+    }
+
+    // the last block of this (sequence, KV head) folds the partials into LSE
+    __threadfence();
+    __syncthreads();
+    if (t == 0) s_last = (atomicAdd(&counters[bg * 2], 1u) == static_cast<uint32_t>(nchunk - 1));
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    const int h = t >> 4, r = t & 15;
+    float mx = -INFINITY;
+    for (int c = r; c < nchunk; c += 16) mx = fmaxf(mx, partial[(bg * nchunk + c) * kGroup + h].x);
+    mx = max16(mx);
+    float sm = 0.f;
+    if (mx != -INFINITY)
+        for (int c = r; c < nchunk; c += 16) {
+            const float2 pm = partial[(bg * nchunk + c) * kGroup + h];
+            if (pm.x != -INFINITY) sm += pm.y * expf(pm.x - mx);
+        }
+    sm = sum16(sm);
+    if (r == 0) lse[bg * kGroup + h] = (mx == -INFINITY) ? -INFINITY : mx + logf(sm);
+    if (t == 0) counters[bg * 2] = 0u;
+}
+
+// ------------------------------------------------------------------ decode, pass 2 + top-k
+__global__ __launch_bounds__(256) void sel_dec_scores(
+    const int64_t* __restrict__ kv_off, const int64_t* __restrict__ kv_lens,
+    const int64_t* __restrict__ ck_off, int hkv, int m, int p, int s, int topk, int init,
+    int local, int64_t nc_max, int nchunk, int64_t nblk_max, const float* __restrict__ logits,
+    const float* __restrict__ lse, uint32_t* __restrict__ keys, uint32_t* __restrict__ counters,
+    int32_t* __restrict__ idx, float* __restrict__ score) {
+    __shared__ float ls[kGroup];
+    __shared__ float rs[kChunkB];
+    __shared__ uint32_t s_last;
+    __shared__ TopkSmem sm;
+    const int b = blockIdx.z, g = blockIdx.y, ch = blockIdx.x, t = threadIdx.x;
+    const int64_t cap = kv_off[b + 1] - kv_off[b];
+    int64_t n = kv_lens ? kv_lens[b] : cap;
+    n = n < cap ? n : cap;
+    const int64_t ccap = ck_off[b + 1] - ck_off[b];
+    int64_t nvis = num_kernels(n, p, s);
+    nvis = nvis < ccap ? nvis : ccap;
+    nvis = nvis < nc_max ? nvis : nc_max;
+    const size_t bg = static_cast<size_t>(b) * hkv + g;
+    uint32_t* kb = keys + bg * nblk_max;
+
+    if (t < kGroup) ls[t] = lse[bg * kGroup + t];
+    __syncthreads();
+    const int64_t j0 = static_cast<int64_t>(ch) * kChunkB;
+    const int64_t j = j0 + t;
+    float R = -INFINITY;
+    if (j < nvis) {
+        const float* z = logits + (bg * nc_max + j) * kGroup;
+        float acc = 0.f;
+#pragma unroll
+        for (int h = 0; h < kGroup; ++h) acc += expf(z[h] - ls[h]);
+        R = acc * (1.0f / kGroup);
+    }
+    rs[t] = R;
+    __syncthreads();
+    const int64_t jhi = (j0 + kChunkB < nvis ? j0 + kChunkB : nvis) - 1;
+    if (j0 <= jhi) {
+        const int64_t blo = (j0 * s) / m, bhi = (jhi * s + p - 1) / m;
+        for (int64_t blk = blo + t; blk <= bhi; blk += 256) {
+            int64_t k0 = first_kernel_of_block(blk, m, p, s), k1 = last_kernel_of_block(blk, m, s);
+            k0 = k0 > j0 ? k0 : j0;
+            k1 = k1 < jhi ? k1 : jhi;
+            if (k0 > k1) continue;
+            float mx = rs[k0 - j0];
+            for (int64_t kk = k0 + 1; kk <= k1; ++kk) mx = fmaxf(mx, rs[kk - j0]);
+            atomicMax(&kb[blk], score_to_key(mx));
+        }
+    }
+
+    __threadfence();
+    __syncthreads();
+    if (t == 0) s_last = (atomicAdd(&counters[bg * 2 + 1], 1u) == static_cast<uint32_t>(nchunk - 1));
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    int64_t c = n > 0 ? (n - 1) / m : -1;
+    c = c < nblk_max - 1 ? c : nblk_max - 1;
+    block_topk(kb, c, topk, init, local, idx + bg * topk, score ? score + bg * topk : nullptr, sm);
+    if (t == 0) counters[bg * 2 + 1] = 0u;
+}
+
+// ------------------------------------------------------------------ prefill, pass 1
+template <typename Tq, typename Tck>
+__device__ __forceinline__ void load_ck_tile(float (*cks)[kHeadDim + 1], const Tck* base,
+                                             int64_t j0, int64_t jn) {
+    // rows j0 .. j0+63 (those < jn) of a [.][128] compressed-key array into LDS
+    for (int e = threadIdx.x * 4; e < kTilePre * kHeadDim; e += 256 * 4) {
+        const int r = e / kHeadDim, c = e % kHeadDim;
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        if (j0 + r < jn) load4(base + (j0 + r) * kHeadDim + c, v);
+        cks[r][c] = v[0]; cks[r][c + 1] = v[1]; cks[r][c + 2] = v[2]; cks[r][c + 3] = v[3];
+    }
+}
+
+template <typename Tq, typename Tck>
+__global__ __launch_bounds__(256) void sel_pre_lse(
+    const Tq* __restrict__ q, int rows, int64_t q_start, const Tck* __restrict__ ck,
+    const int64_t* __restrict__ ck_off, int hq, int hkv, int p, int s, float score_scale,
+    int64_t nblk_max, float* __restrict__ lse, uint32_t* __restrict__ keys) {
+    __shared__ float qs[kRowsPre][kGroup][kHeadDim];
+    __shared__ float cks[kTilePre][kHeadDim + 1];
+    const int g = blockIdx.y, t = threadIdx.x;
+    const int r0 = blockIdx.x * kRowsPre;
+    const int64_t ccap = ck_off[1] - ck_off[0];
+    const Tck* ckh = ck + (ck_off[0] * hkv + static_cast<int64_t>(g) * ccap) * kHeadDim;
+    int64_t vis[kRowsPre];
+    int64_t vmax = 0;
+#pragma unroll
+    for (int rr = 0; rr < kRowsPre; ++rr) {
+        const int row = r0 + rr;
+        int64_t v = row < rows ? num_kernels(q_start + row + 1, p, s) : 0;
+        v = v < ccap ? v : ccap;
+        vis[rr] = v;
+        vmax = v > vmax ? v : vmax;
+        if (row < rows) {
+            uint32_t* kb = keys + (static_cast<size_t>(row) * hkv + g) * nblk_max;
+            for (int64_t jb = t; jb < nblk_max; jb += 256) kb[jb] = 0u;
+        }
+    }
+    for (int e = t; e < kRowsPre * kGroup * kHeadDim; e += 256) {
+        const int rr = e / (kGroup * kHeadDim), rem = e % (kGroup * kHeadDim);
+        const int row = r0 + rr;
+        qs[rr][rem / kHeadDim][rem % kHeadDim] =
+            row < rows ? io<Tq>::load(q + (static_cast<size_t>(row) * hq + static_cast<size_t>(g) * kGroup) * kHeadDim + rem) : 0.f;
+    }
+    const int w = t >> 6, lane = t & 63;
+    // this thread's 16 (row, head) pairs: pair u -> row u/4, head w + 4*(u%4)
+    float mrun[16], lrun[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) { mrun[u] = -INFINITY; lrun[u] = 0.f; }
+    for (int64_t j0 = 0; j0 < vmax; j0 += kTilePre) {
+        __syncthreads();
+        load_ck_tile<Tq, Tck>(cks, ckh, j0, vmax);
+        __syncthreads();
+        const int64_t j = j0 + lane;
+        float acc[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc[u] = 0.f;
+        for (int d = 0; d < kHeadDim; ++d) {
+            const float kd = cks[lane][d];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) acc[u] = fmaf(qs[u >> 2][w + 4 * (u & 3)][d], kd, acc[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            if (j < vis[u >> 2]) {
+                const float z = score_scale * acc[u];
+                if (z > mrun[u]) {
+                    lrun[u] = lrun[u] * expf(mrun[u] - z) + 1.f;
+                    mrun[u] = z;
+                } else {
+                    lrun[u] += expf(z - mrun[u]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const float mx = wave_max(mrun[u]);
+        const float part = (mrun[u] == -INFINITY) ? 0.f : lrun[u] * expf(mrun[u] - mx);
+        const float sm = wave_sum(part);
+        const int row = r0 + (u >> 2);
+        if (lane == 0 && row < rows)
+            lse[static_cast<size_t>(row) * hq + g * kGroup + w + 4 * (u & 3)] =
+                (mx == -INFINITY) ? -INFINITY : mx + logf(sm);
+    }
+}
+
+// ------------------------------------------------------------------ prefill, pass 2
+template <typename Tq, typename Tck>
+__global__ __launch_bounds__(256) void sel_pre_scores(
+    const Tq* __restrict__ q, int rows, int64_t q_start, const Tck* __restrict__ ck,
+    const int64_t* __restrict__ ck_off, int hq, int hkv, int m, int p, int s, float score_scale,
+    int64_t nblk_max, const float* __restrict__ lse, uint32_t* __restrict__ keys) {
+    __shared__ float qs[kRowsPre][kGroup][kHeadDim];
+    __shared__ float cks[kTilePre][kHeadDim + 1];
+    __shared__ float rs[kRowsPre][kTilePre];
+    __shared__ float ls[kRowsPre][kGroup];
+    const int g = blockIdx.y, t = threadIdx.x;
+    const int r0 = blockIdx.x * kRowsPre;
+    const int64_t ccap = ck_off[1] - ck_off[0];
+    const Tck* ckh = ck + (ck_off[0] * hkv + static_cast<int64_t>(g) * ccap) * kHeadDim;
+    const int w = t >> 6, lane = t & 63;       // wave w owns row r0 + w
+    const int row = r0 + w;
+    int64_t vmax = 0;
+    for (int rr = 0; rr < kRowsPre; ++rr) {
+        int64_t v = (r0 + rr) < rows ? num_kernels(q_start + r0 + rr + 1, p, s) : 0;
+        v = v < ccap ? v : ccap;
+        vmax = v > vmax ? v : vmax;
+    }
+    int64_t vis = row < rows ? num_kernels(q_start + row + 1, p, s) : 0;
+    vis = vis < ccap ? vis : ccap;
+    for (int e = t; e < kRowsPre * kGroup * kHeadDim; e += 256) {
+        const int rr = e / (kGroup * kHeadDim), rem = e % (kGroup * kHeadDim);
+        const int rw = r0 + rr;
+        qs[rr][rem / kHeadDim][rem % kHeadDim] =
+            rw < rows ? io<Tq>::load(q + (static_cast<size_t>(rw) * hq + static_cast<size_t>(g) * kGroup) * kHeadDim + rem) : 0.f;
+    }
+    if (t < kRowsPre * kGroup) {
+        const int rw = r0 + t / kGroup;
+        ls[t / kGroup][t % kGroup] = rw < rows ? lse[static_cast<size_t>(rw) * hq + g * kGroup + t % kGroup] : 0.f;
+    }
+    uint32_t* kb = keys + (static_cast<size_t>(row < rows ? row : 0) * hkv + g) * nblk_max;
+    for (int64_t j0 = 0; j0 < vmax; j0 += kTilePre) {
+        __syncthreads();
+        load_ck_tile<Tq, Tck>(cks, ckh, j0, vmax);
+        __syncthreads();
+        const int64_t j = j0 + lane;
+        float acc[kGroup];
+#pragma unroll
+        for (int h = 0; h < kGroup; ++h) acc[h] = 0.f;
+        for (int d = 0; d < kHeadDim; ++d) {
+            const float kd = cks[lane][d];
+#pragma unroll
+            for (int h = 0; h < kGroup; ++h) acc[h] = fmaf(qs[w][h][d], kd, acc[h]);
+        }
+        float R = -INFINITY;
+        if (j < vis) {
+            float sum = 0.f;
+#pragma unroll
+            for (int h = 0; h < kGroup; ++h) sum += expf(score_scale * acc[h] - ls[w][h]);
+            R = sum * (1.0f / kGroup);
+        }
+        rs[w][lane] = R;
+        __syncthreads();
+        const int64_t jhi = (j0 + kTilePre < vis ? j0 + kTilePre : vis) - 1;
+        if (row < rows && j0 <= jhi) {
+            const int64_t blo = (j0 * s) / m, bhi = (jhi * s + p - 1) / m;
+            for (int64_t blk = blo + lane; blk <= bhi; blk += 64) {
+                int64_t k0 = first_kernel_of_block(blk, m, p, s), k1 = last_kernel_of_block(blk, m, s);
+                k0 = k0 > j0 ? k0 : j0;
+                k1 = k1 < jhi ? k1 : jhi;
+                if (k0 > k1) continue;
+                float mx = rs[w][k0 - j0];
+                for (int64_t kk = k0 + 1; kk <= k1; ++kk) mx = fmaxf(mx, rs[w][kk - j0]);
+                atomicMax(&kb[blk], score_to_key(mx));
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ prefill, top-k
+__global__ __launch_bounds__(256) void sel_pre_topk(int64_t q_start, int hkv, int m, int topk,
+                                                    int init, int local, int64_t nblk_max,
+                                                    const uint32_t* __restrict__ keys,
+                                                    int32_t* __restrict__ idx,
+                                                    float* __restrict__ score) {
+    __shared__ TopkSmem sm;
+    const int row = blockIdx.x, g = blockIdx.y;
+    const size_t rg = static_cast<size_t>(row) * hkv + g;
+    const int64_t c = (q_start + row) / m;
+    block_topk(keys + rg * nblk_max, c, topk, init, local, idx + rg * topk,
+               score ? score + rg * topk : nullptr, sm);
+}
+
+// ------------------------------------------------------------------ launchers
+template <typename Tq, typename Tck>
+static void dec_launch(const Shape& sh, const void* q, const void* ck, const int64_t* ck_off,
+                       const int64_t* kv_off, const int64_t* kv_lens, int batch,
+                       const SelectDecodeWs& w, char* ws, int32_t* idx, float* score,
+                       hipStream_t st) {
+    dim3 ga(w.nchunk_a, sh.hkv, batch), gb(w.nchunk_b, sh.hkv, batch);
+    const int64_t ncm = w.nc_max > 0 ? w.nc_max : 1;
+    sel_dec_logits<Tq, Tck><<<ga, 256, 0, st>>>(
+        static_cast<const Tq*>(q), static_cast<const Tck*>(ck), ck_off, kv_off, kv_lens, sh.hq,
+        sh.hkv, sh.p, sh.s, sh.score_scale, ncm, w.nchunk_a, w.nblk_max,
+        reinterpret_cast<float*>(ws + w.logits), reinterpret_cast<float2*>(ws + w.partial),
+        reinterpret_cast<float*>(ws + w.lse), reinterpret_cast<uint32_t*>(ws + w.keys),
+        reinterpret_cast<uint32_t*>(ws + w.counters));
+    sel_dec_scores<<<gb, 256, 0, st>>>(
+        kv_off, kv_lens, ck_off, sh.hkv, sh.m, sh.p, sh.s, sh.topk, sh.init, sh.local, ncm,
+        w.nchunk_b, w.nblk_max, reinterpret_cast<const float*>(ws + w.logits),
+        reinterpret_cast<const float*>(ws + w.lse), reinterpret_cast<uint32_t*>(ws + w.keys),
+        reinterpret_cast<uint32_t*>(ws + w.counters), idx, score);
+}
+
+hipError_t launch_select_decode(const Shape& sh, const void* q, const void* ck,
+                                const int64_t* ck_off, const int64_t* kv_off,
+                                const int64_t* kv_lens, int batch, int64_t max_len,
+                                int32_t* idx, float* score, void* ws, hipStream_t st) {
+    const SelectDecodeWs w = select_decode_ws(sh, batch, max_len);
+    char* base = static_cast<char*>(ws);
+    if (sh.io_bf16) {
+        if (sh.ck_bf16) dec_launch<bf16_t, bf16_t>(sh, q, ck, ck_off, kv_off, kv_lens, batch, w, base, idx, score, st);
+        else dec_launch<bf16_t, float>(sh, q, ck, ck_off, kv_off, kv_lens, batch, w, base, idx, score, st);
+    } else {
+        if (sh.ck_bf16) dec_launch<float, bf16_t>(sh, q, ck, ck_off, kv_off, kv_lens, batch, w, base, idx, score, st);
+        else dec_launch<float, float>(sh, q, ck, ck_off, kv_off, kv_lens, batch, w, base, idx, score, st);
+    }
+    return hipGetLastError();
+}
+
+template <typename Tq, typename Tck>
+static void pre_launch(const Shape& sh, const void* q, int rows, int64_t q_start, const void* ck,
+                       const int64_t* ck_off, const SelectPrefillWs& w, char* ws, int32_t* idx,
+                       float* score, hipStream_t st) {
+    dim3 g1((rows + kRowsPre - 1) / kRowsPre, sh.hkv);
+    float* lse = reinterpret_cast<float*>(ws + w.lse);
+    uint32_t* keys = reinterpret_cast<uint32_t*>(ws + w.keys);
+    sel_pre_lse<Tq, Tck><<<g1, 256, 0, st>>>(static_cast<const Tq*>(q), rows, q_start,
+                                            static_cast<const Tck*>(ck), ck_off, sh.hq, sh.hkv,
+                                            sh.p, sh.s, sh.score_scale, w.nblk_max, lse, keys);
+    sel_pre_scores<Tq, Tck><<<g1, 256, 0, st>>>(static_cast<const Tq*>(q), rows, q_start,
+                                               static_cast<const Tck*>(ck), ck_off, sh.hq, sh.hkv,
+                                               sh.m, sh.p, sh.s, sh.score_scale, w.nblk_max, lse,
+                                               keys);
+    sel_pre_topk<<<dim3(rows, sh.hkv), 256, 0, st>>>(q_start, sh.hkv, sh.m, sh.topk, sh.init,
+                                                     sh.local, w.nblk_max, keys, idx, score);
+}
+
+hipError_t launch_select_prefill(const Shape& sh, const void* q, int rows, int64_t q_start,
+                                 const void* ck, const int64_t* ck_off, int64_t max_len,
+                                 int32_t* idx, float* score, void* ws, hipStream_t st) {
+    const SelectPrefillWs w = select_prefill_ws(sh, rows, max_len);
+    char* base = static_cast<char*>(ws);
+    if (sh.io_bf16) {
+        if (sh.ck_bf16) pre_launch<bf16_t, bf16_t>(sh, q, rows, q_start, ck, ck_off, w, base, idx, score, st);
+        else pre_launch<bf16_t, float>(sh, q, rows, q_start, ck, ck_off, w, base, idx, score, st);
+    } else {
+        if (sh.ck_bf16) pre_launch<float, bf16_t>(sh, q, rows, q_start, ck, ck_off, w, base, idx, score, st);
+        else pre_launch<float, float>(sh, q, rows, q_start, ck, ck_off, w, base, idx, score, st);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace infv2
