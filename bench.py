@@ -1,0 +1,450 @@
+#!/usr/bin/env python3
+"""Throughput of the InfLLM v2 hot path on one MI355X.
+
+Main line: single-step decode at 128K context (batch 1, 32 query heads over 2
+KV heads, head size 128, KV block 64, semantic kernels 32/16, top-k 64 with the
+initial block and 4 local blocks forced).  One step = the whole path for one new
+token: compressed key of the kernel the token completes, block selection
+(logits, LogSumExp, group score, block max, top-k) and sparse attention.  The
+step rotates through independent cache replicas ("layers") so that every step
+reads its compressed keys and selected K/V from HBM rather than from the 256 MiB
+Infinity Cache.  Inputs are resident in HBM before timing starts.
+
+Also reported on the same line: 32K chunked prefill (TFLOPS of useful
+selected-block attention FLOPs), batched decode of 16 sequences of 64K-128K,
+the roofline fraction of the dominant kernel, and the float64 CPU oracle timed
+on this host on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "128K sparse-attn decode tok/s + HBM GB/s; 32K prefill TFLOPS; % of roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- helpers
+def num_kernels(n: int, p: int, s: int) -> int:
+    return 0 if n < p else (n - p) // s + 1
+
+
+def attended_tokens(idx: np.ndarray, positions: np.ndarray, n: np.ndarray, m: int) -> np.ndarray:
+    """|T_i| per (row, KV head): tokens t <= i, t < n of the selected blocks."""
+    blk = idx.astype(np.int64)
+    start = blk * m
+    end = np.minimum(np.minimum(start + m, (positions + 1)[:, None, None]), n[:, None, None])
+    cnt = np.where(blk >= 0, np.maximum(end - start, 0), 0)
+    return cnt.sum(axis=2)
+
+
+class Timer:
+    """Elapsed GPU time between events recorded on the current (library) stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def event(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+
+# ----------------------------------------------------------------------------- decode
+def decode_bytes(wl, ck_bytes: int, n_list) -> dict:
+    """Algorithmic HBM bytes of one decode step (per call of each entry point)."""
+    d, hq, hkv, m, k = wl.head_dim, wl.num_q_heads, wl.num_kv_heads, wl.block_size, wl.topk
+    esz = 2 if wl.io_dtype == "bf16" else 4
+    q_b = hq * d * esz
+    sel_kv = sum(hkv * min(k * m, n) * d * esz * 2 for n in n_list)
+    ck = sum(hkv * num_kernels(n, wl.kernel_size, wl.kernel_stride) * d * ck_bytes for n in n_list)
+    B = len(n_list)
+    return {
+        "compress": B * hkv * (wl.kernel_size * d * esz + d * ck_bytes),
+        "select": ck + B * (q_b + hkv * k * 4),
+        "attn": sel_kv + B * (2 * q_b + hkv * k * 4),
+    }
+
+
+def bench_decode(cfg_index: int, args, torch, tbs, gh, replicas: int) -> dict:
+    from synth import make_config, extra_decode_queries
+    wl = make_config(cfg_index)
+    ck_dtype = args.ck_dtype
+    dev = gh.DeviceWorkload(wl, ck_dtype)
+    dev.compress()
+    cfg = dev.cfg
+    B, n_max = wl.batch, dev.max_len
+    R = replicas
+    log(f"config {cfg_index}: {wl.name}, B={B}, replicas={R}")
+    qs = gh.to_device(extra_decode_queries(wl, R))                # [R][B][Hq][d]
+    Ks = [dev.k] + [dev.k.clone() for _ in range(R - 1)]
+    Vs = [dev.v] + [dev.v.clone() for _ in range(R - 1)]
+    CKs = [dev.ck] + [dev.ck.clone() for _ in range(R - 1)]
+    outs = torch.empty((R,) + tuple(dev.q.shape), dtype=dev.q.dtype, device="cuda")
+    idx = torch.empty((B, wl.num_kv_heads, cfg.topk), dtype=torch.int32, device="cuda")
+    ws_sel = dev.ws(tbs.OP_SELECT_DECODE, B, B, n_max)
+    ws_att = dev.ws(tbs.OP_ATTN_DECODE, B, B, n_max)
+    # the step's new token completes (at most) the last kernel of each sequence
+    begin = torch.tensor([max(0, num_kernels(int(n), wl.kernel_size, wl.kernel_stride) - 1)
+                          for n in wl.lens], dtype=torch.int64, device="cuda")
+
+    def compress(r):
+        tbs.infv2_compress_keys(cfg, Ks[r], dev.kv_offsets, dev.kv_lens, dev.ck_offsets, begin, B,
+                                n_max, 1, CKs[r])
+
+    def select(r):
+        tbs.infv2_select_blocks(cfg, tbs.INFV2_MODE_DECODE, qs[r], B, 0, CKs[r], dev.ck_offsets,
+                                dev.kv_offsets, dev.kv_lens, B, n_max, idx, None, ws_sel)
+
+    def attn(r):
+        tbs.infv2_sparse_attn_decode(cfg, qs[r], Ks[r], Vs[r], dev.kv_offsets, dev.kv_lens, B, n_max,
+                                     idx, outs[r], ws_att)
+
+    def step(r):
+        compress(r)
+        select(r)
+        attn(r)
+
+    T = Timer(torch)
+    for t in range(args.warmup):
+        step(t % R)
+    torch.cuda.synchronize()
+    # per-entry-point times, eager launches with events between the calls
+    ev = []
+    for t in range(args.steps):
+        r = t % R
+        e0 = T.event(); compress(r); e1 = T.event(); select(r); e2 = T.event(); attn(r); e3 = T.event()
+        ev.append((e0, e1, e2, e3))
+    torch.cuda.synchronize()
+    per = np.array([[a.elapsed_time(b) for a, b in zip(x[:-1], x[1:])] for x in ev]) * 1e3  # us
+    per_us = dict(zip(["compress", "select", "attn"], per.mean(axis=0).tolist()))
+    # whole steps, eager
+    torch.cuda.synchronize()
+    s0 = T.event()
+    for t in range(args.steps):
+        step(t % R)
+    s1 = T.event()
+    torch.cuda.synchronize()
+    eager_ms = s0.elapsed_time(s1) / args.steps
+    # whole steps, HIP-graph replay (one graph per replica)
+    graph_ms = None
+    if args.graph:
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for r in range(R):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    step(r)
+                graphs.append(g)
+        torch.cuda.current_stream().wait_stream(side)
+        for t in range(args.warmup):
+            graphs[t % R].replay()
+        torch.cuda.synchronize()
+        g0 = T.event()
+        for t in range(args.steps):
+            graphs[t % R].replay()
+        g1 = T.event()
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / args.steps
+    ms = graph_ms if graph_ms is not None else eager_ms
+    ckb = 2 if ck_dtype == "bf16" else 4
+    nb = decode_bytes(wl, ckb, [int(n) for n in wl.lens])
+    step_bytes = sum(nb.values())
+    res = {
+        "workload": wl.name, "batch": B, "lens_min": int(wl.lens.min()), "lens_max": n_max,
+        "ms_per_step": ms, "ms_per_step_eager": eager_ms, "ms_per_step_graph": graph_ms,
+        "tok_per_s": B / (ms * 1e-3), "per_call_us": per_us, "bytes_per_step": step_bytes,
+        "bytes_per_call": nb, "hbm_gbps_step": step_bytes / (ms * 1e-3) / 1e9,
+        "replicas": R,
+    }
+    # spot parity of the timed path: replica 0, oracle selection on the same query
+    res["parity"] = decode_spot_parity(wl, dev, qs, outs, idx, select, attn, ck_dtype, torch, gh)
+    del Ks, Vs, CKs
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_spot_parity(wl, dev, qs, outs, idx, select, attn, ck_dtype, torch, gh) -> str:
+    from oracle import infv2_ref as ref
+    from tests.parity import accept_selection, assert_close
+    select(0)
+    attn(0)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy().astype(np.int64)
+    go = gh.from_device(outs[0], wl.io_dtype)
+    q = gh.from_device(qs[0], wl.io_dtype)
+    prm = ref.Params(head_dim=wl.head_dim, num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
+                     block_size=wl.block_size, kernel_size=wl.kernel_size,
+                     kernel_stride=wl.kernel_stride, topk=wl.topk, init_blocks=wl.init_blocks,
+                     local_blocks=wl.local_blocks, ck_dtype=ck_dtype)
+    cks = dev.ck_host()
+    verdicts = []
+    for b in range(min(wl.batch, 2)):
+        K = wl.k_f64(b)
+        n = K.shape[1]
+        for g in range(wl.num_kv_heads):
+            rs = ref.select_row(q[b, 16 * g:16 * g + 16], cks[b][g], n - 1, prm)
+            verdicts.append(accept_selection(gi[b, g], rs))
+        want = ref.attend_with_selection(q[b:b + 1], K, wl.v_f64(b), [n - 1], gi[b:b + 1], prm)
+        assert_close(go[b], want[0], wl.io_dtype, "bench decode spot check")
+    bad = [v for v in verdicts if v.startswith("fail")]
+    if bad:
+        raise AssertionError(f"bench parity: {bad[0]}")
+    return "ok (" + ", ".join(verdicts) + ")"
+
+
+# ----------------------------------------------------------------------------- prefill
+def bench_prefill(args, torch, tbs, gh) -> dict:
+    from synth import make_config
+    wl = make_config(3)
+    dev = gh.DeviceWorkload(wl, args.ck_dtype)
+    L, C = int(wl.lens[0]), wl.chunk
+    cfg = dev.cfg
+    log(f"config 3: {wl.name}, L={L}, chunk={C}")
+    T = Timer(torch)
+    hkv, k, hq, d = wl.num_kv_heads, cfg.topk, wl.num_q_heads, wl.head_dim
+    idx = torch.empty((L, hkv, k), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(dev.q)
+    ws = dev.ws(tbs.OP_SELECT_PREFILL, C, 1, L)
+    p, s = wl.kernel_size, wl.kernel_stride
+
+    def run(record):
+        evs = []
+        for q0 in range(0, L, C):
+            q1 = min(L, q0 + C)
+            lens = dev.kv_lens.new_tensor([q1])
+            begin = dev.kv_lens.new_tensor([num_kernels(q0, p, s)])
+            e0 = T.event() if record else None
+            tbs.infv2_compress_keys(cfg, dev.k, dev.kv_offsets, lens, dev.ck_offsets, begin, 1, q1,
+                                    num_kernels(q1, p, s) - num_kernels(q0, p, s), dev.ck)
+            e1 = T.event() if record else None
+            tbs.infv2_select_blocks(cfg, tbs.INFV2_MODE_PREFILL, dev.q[q0:q1], q1 - q0, q0, dev.ck,
+                                    dev.ck_offsets, dev.kv_offsets, None, 1, q1, idx[q0:q1], None,
+                                    ws)
+            e2 = T.event() if record else None
+            tbs.infv2_sparse_attn_prefill(cfg, dev.q[q0:q1], q1 - q0, q0, dev.k, dev.v,
+                                          dev.kv_offsets, idx[q0:q1], out[q0:q1])
+            e3 = T.event() if record else None
+            evs.append((e0, e1, e2, e3))
+        return evs
+
+    run(False)
+    torch.cuda.synchronize()
+    reps = []
+    for _ in range(args.prefill_reps):
+        evs = run(True)
+        torch.cuda.synchronize()
+        ph = np.array([[a.elapsed_time(b) for a, b in zip(x[:-1], x[1:])] for x in evs])  # ms
+        reps.append(ph)
+    ph = np.median(np.stack(reps), axis=0)          # [chunks][3]
+    gi = idx.cpu().numpy()
+    pos = np.arange(L)
+    tok = attended_tokens(gi, pos, np.full(L, L), wl.block_size)       # [L][Hkv]
+    useful = float(4 * d * (hq // hkv) * tok.sum())
+    attn_ms = float(ph[:, 2].sum())
+    total_ms = float(ph.sum())
+    sel_ms = float(ph[:, 1].sum())
+    # scoring GEMM work of one pass: Hq * d * 2 * sum_i n_vis(i)
+    nvis = np.array([num_kernels(i + 1, p, s) for i in range(L)], dtype=np.int64)
+    score_flops_pass = float(2 * d * hq * nvis.sum())
+    res = {
+        "workload": wl.name, "rows": L, "chunk": C, "useful_attn_flops": useful,
+        "attn_ms": attn_ms, "select_ms": sel_ms, "compress_ms": float(ph[:, 0].sum()),
+        "total_ms": total_ms, "tflops_attn": useful / (attn_ms * 1e-3) / 1e12,
+        "tflops_path": useful / (total_ms * 1e-3) / 1e12,
+        "score_gemm_flops_per_pass": score_flops_pass,
+        "last_chunk_attn_ms": float(ph[-1, 2]),
+        "last_chunk_useful_flops": float(4 * d * (hq // hkv) * tok[L - C:].sum()),
+        "mean_attended_tokens": float(tok.mean()),
+    }
+    res["roofline"] = {"bound": "mfma", "kernel": "attn_prefill_kernel",
+                       "achieved": res["tflops_attn"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                       "frac": res["tflops_attn"] / BF16_PEAK_TFLOPS, "traffic": None}
+    res["_idx"] = gi
+    res["_wl"] = wl
+    return res
+
+
+def bench_batched(args, torch, tbs, gh) -> dict:
+    # one step reads ~160 MiB, so three replicas already keep the MALL cold
+    return bench_decode(4, args, torch, tbs, gh, replicas=min(args.replicas, 4))
+
+
+# ----------------------------------------------------------------------------- CPU oracle
+def blas_threads() -> int:
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        return int(max([x.get("num_threads", 1) for x in info] + [1]))
+    except Exception:  # pragma: no cover - reporting only
+        return 1
+
+
+def cpu_baseline_decode(seconds: float) -> dict:
+    """Oracle decode steps at 128K (precomputed compressed keys as the cache state)."""
+    from oracle import infv2_ref as ref
+    from synth import make_config, extra_decode_queries, bf16_bits_to_f32
+    wl = make_config(2)
+    prm = ref.Params(head_dim=128, num_q_heads=32, num_kv_heads=2, block_size=64, kernel_size=32,
+                     kernel_stride=16, topk=64, init_blocks=1, local_blocks=4)
+    K, V = wl.k_f64(0), wl.v_f64(0)
+    n = K.shape[1]
+    ck = ref.compress_keys(K, 32, 16, "fp32")
+    qs = bf16_bits_to_f32(extra_decode_queries(wl, 64)).astype(np.float64)
+    t0 = time.perf_counter()
+    steps = 0
+    while True:
+        q = qs[steps % qs.shape[0], 0]
+        ref.compress_keys(K[:, n - 32:n], 32, 16, "fp32")           # the kernel the token completes
+        for g in range(2):
+            rs = ref.select_row(q[16 * g:16 * g + 16], ck[g], n - 1, prm)
+            ref.attend_row(q[16 * g:16 * g + 16], K[g], V[g], n - 1, rs.sel, prm)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds and steps >= 3:
+            break
+    return {"value": steps / el, "unit": "tok/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{steps} decode steps of the 128K config (B=1), float64 NumPy, "
+                      f"{el:.1f} s, cache state (compressed keys) precomputed"}
+
+
+def cpu_baseline_prefill(seconds: float, pre: dict) -> dict:
+    """Oracle prefill rows of the last 4096-row chunk of the 32K config."""
+    from oracle import infv2_ref as ref
+    wl = pre["_wl"]
+    prm = ref.Params(head_dim=128, num_q_heads=32, num_kv_heads=2, block_size=64, kernel_size=32,
+                     kernel_stride=16, topk=64, init_blocks=1, local_blocks=4)
+    K, V = wl.k_f64(0), wl.v_f64(0)
+    ck = ref.compress_keys(K, 32, 16, "fp32")
+    q = wl.q_f64()
+    L = q.shape[0]
+    rng = np.random.default_rng(5)
+    rows = rng.integers(L - wl.chunk, L, 4096)
+    t0 = time.perf_counter()
+    done = []
+    for i in rows.tolist():
+        for g in range(2):
+            rs = ref.select_row(q[i, 16 * g:16 * g + 16], ck[g], i, prm)
+            ref.attend_row(q[i, 16 * g:16 * g + 16], K[g], V[g], i, rs.sel, prm)
+        done.append(i)
+        if time.perf_counter() - t0 >= seconds and len(done) >= 4:
+            break
+    el = time.perf_counter() - t0
+    gi = pre["_idx"][done]
+    tok = attended_tokens(gi, np.array(done), np.full(len(done), L), 64)
+    flops = float(4 * 128 * 16 * tok.sum())
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{len(done)} random rows of the last 4096-row chunk of the 32K prefill "
+                      f"(selection + attention), {el:.1f} s; useful attention FLOPs / time"}
+
+
+# ----------------------------------------------------------------------------- main
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=32,
+                    help="independent cache copies rotated per step (defeats the 256 MiB MALL)")
+    ap.add_argument("--prefill-reps", type=int, default=3)
+    ap.add_argument("--ck-dtype", default="fp32", choices=["fp32", "bf16"])
+    ap.add_argument("--graph", type=int, default=1)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-batched", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--only", choices=["decode", "prefill", "batched"], default=None,
+                    help="run one workload only and print its record (for profiling)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the design note "
+              "on sharding is in DESIGN.md); run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import trainable_block_sparse_amd as tbs
+    from tests import gpu_harness as gh
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    tbs.load_library()
+    torch.cuda.set_device(0)
+
+    if args.only:
+        if args.only == "decode":
+            rec = bench_decode(2, args, torch, tbs, gh, replicas=args.replicas)
+        elif args.only == "prefill":
+            rec = {k: v for k, v in bench_prefill(args, torch, tbs, gh).items() if not k.startswith("_")}
+        else:
+            rec = bench_batched(args, torch, tbs, gh)
+        print(json.dumps({"only": args.only, "record": rec}))
+        return 0
+
+    main_res = bench_decode(2, args, torch, tbs, gh, replicas=args.replicas)
+    log(f"decode 128K: {main_res['ms_per_step'] * 1e3:.1f} us/step, per call {main_res['per_call_us']}")
+    pre = None if args.no_prefill else bench_prefill(args, torch, tbs, gh)
+    if pre:
+        log(f"prefill 32K: attn {pre['attn_ms']:.2f} ms, total {pre['total_ms']:.2f} ms, "
+            f"{pre['tflops_attn']:.1f} TFLOPS")
+    bat = None if args.no_batched else bench_batched(args, torch, tbs, gh)
+    if bat:
+        log(f"batched decode: {bat['ms_per_step'] * 1e3:.1f} us/step, per call {bat['per_call_us']}")
+
+    # dominant kernel of the main step: the decode attention kernel (one kernel per call)
+    att_us = main_res["per_call_us"]["attn"]
+    att_bytes = main_res["bytes_per_call"]["attn"]
+    roof = {"bound": "hbm", "kernel": "attn_decode_kernel", "achieved": att_bytes / (att_us * 1e-6) / 1e9,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+
+    out = {
+        "metric": METRIC,
+        "value": main_res["tok_per_s"],
+        "unit": "tok/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode_bf16_128k", "batch": 1, "context": 131072, "num_q_heads": 32,
+                   "num_kv_heads": 2, "head_dim": 128, "block_size": 64, "kernel_size": 32,
+                   "kernel_stride": 16, "topk": 64, "init_blocks": 1, "local_blocks": 4,
+                   "ck_dtype": args.ck_dtype, "cache_replicas": args.replicas,
+                   "graph_replay": bool(args.graph)},
+        "hbm_gbps": main_res["hbm_gbps_step"],
+        "roofline": roof,
+        "decode_128k": {k: v for k, v in main_res.items()},
+    }
+    if pre:
+        out["prefill_32k"] = {k: v for k, v in pre.items() if not k.startswith("_")}
+    if bat:
+        out["batched_decode_16x"] = bat
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline_decode(args.cpu_seconds)
+        if pre:
+            out["prefill_32k"]["cpu_baseline"] = cpu_baseline_prefill(args.cpu_seconds, pre)
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

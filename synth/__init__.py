@@ -8,6 +8,7 @@ it produces.
 from .gen import (  # noqa: F401
     Workload,
     bf16_bits_to_f32,
+    extra_decode_queries,
     f32_to_bf16_bits,
     make_config,
     make_workload,

@@ -1,0 +1,137 @@
+"""Host-only checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/infv2.h declares, and
+reject invalid arguments with the documented status before any HIP call (so
+these calls are safe without a device: nothing is ever launched).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import trainable_block_sparse_amd as tbs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "infv2.h")
+OK, ENULL, ESHAPE, EUNSUP, EWS = 0, 1, 2, 3, 4
+FAKE = 0x10000          # a non-NULL pointer that is never dereferenced on these paths
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tbs.LIB_PATH):
+        from trainable_block_sparse_amd.build import build
+        build()
+    return tbs.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(infv2_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ["infv2_compress_keys", "infv2_select_blocks", "infv2_sparse_attn_prefill",
+              "infv2_sparse_attn_decode"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(tbs.EXPORTED)
+
+
+def test_abi_version_and_status_strings(lib):
+    ver = int(re.search(r"#define INFV2_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert tbs.infv2_abi_version() == ver
+    for st in range(6):
+        assert tbs.infv2_status_str(st).startswith("INFV2_")
+
+
+def test_num_kernels_formula(lib):
+    cfg = tbs.Config()
+    for n in [0, 1, 31, 32, 33, 47, 48, 131072]:
+        want = 0 if n < 32 else (n - 32) // 16 + 1
+        assert tbs.infv2_num_kernels(cfg, n) == want
+
+
+def test_workspace_sizes_grow_with_the_problem(lib):
+    cfg = tbs.Config()
+    a = tbs.infv2_workspace_bytes(cfg, tbs.OP_SELECT_DECODE, 1, 1, 32768)
+    b = tbs.infv2_workspace_bytes(cfg, tbs.OP_SELECT_DECODE, 1, 1, 131072)
+    c = tbs.infv2_workspace_bytes(cfg, tbs.OP_SELECT_DECODE, 16, 16, 131072)
+    assert 0 < a < b < c
+    assert tbs.infv2_workspace_bytes(cfg, tbs.OP_ATTN_DECODE, 16, 16, 131072) > 0
+    assert tbs.infv2_workspace_bytes(cfg, tbs.OP_SELECT_PREFILL, 4096, 1, 32768) >= 4096 * 2 * 512 * 4
+
+
+def _c(cfg):
+    return ctypes.byref(cfg.to_c())
+
+
+def _compress(lib, cfg, k=FAKE, off=FAKE, ckoff=FAKE, ck=FAKE, batch=1, max_len=100):
+    return lib.infv2_compress_keys(_c(cfg) if cfg is not None else None, k, off, None, ckoff, None,
+                                   batch, max_len, -1, ck, None)
+
+
+@pytest.mark.parametrize("cfg,want", [
+    (tbs.Config(num_q_heads=30, num_kv_heads=4), ESHAPE),          # Hq % Hkv
+    (tbs.Config(topk=4, init_blocks=1, local_blocks=4), ESHAPE),   # k < |F|
+    (tbs.Config(kernel_size=8, kernel_stride=16), ESHAPE),         # p < s
+    (tbs.Config(block_size=0), ESHAPE),
+    (tbs.Config(head_dim=64), EUNSUP),
+    (tbs.Config(num_q_heads=16, num_kv_heads=2), EUNSUP),          # group of 8
+    (tbs.Config(block_size=48 + 1), EUNSUP),
+    (tbs.Config(topk=2048), EUNSUP),
+    (tbs.Config(kernel_size=512, kernel_stride=16), EUNSUP),
+])
+def test_invalid_configs_rejected(lib, cfg, want):
+    assert _compress(lib, cfg) == want
+
+
+def test_null_pointers_and_sizes_rejected(lib):
+    cfg = tbs.Config()
+    assert _compress(lib, None) == ENULL
+    assert _compress(lib, cfg, k=None) == ENULL
+    assert _compress(lib, cfg, ck=None) == ENULL
+    assert _compress(lib, cfg, batch=0) == ESHAPE
+    assert _compress(lib, cfg, max_len=-1) == ESHAPE
+    assert _compress(lib, cfg, max_len=16385 * 64) == EUNSUP      # more than 16384 blocks
+
+
+def test_select_and_attention_validation(lib):
+    cfg = tbs.Config()
+    c = _c(cfg)
+    ws_need = tbs.infv2_workspace_bytes(cfg, tbs.OP_SELECT_DECODE, 2, 2, 5000)
+    # decode: rows must equal batch; workspace must be large enough
+    assert lib.infv2_select_blocks(c, 0, FAKE, 3, 0, FAKE, FAKE, FAKE, None, 2, 5000, FAKE, None,
+                                   FAKE, ws_need, None) == ESHAPE
+    assert lib.infv2_select_blocks(c, 0, FAKE, 2, 0, FAKE, FAKE, FAKE, None, 2, 5000, FAKE, None,
+                                   FAKE, ws_need - 1, None) == EWS
+    assert lib.infv2_select_blocks(c, 0, FAKE, 2, 0, FAKE, FAKE, FAKE, None, 2, 5000, FAKE, None,
+                                   None, ws_need, None) == EWS
+    assert lib.infv2_select_blocks(c, 0, FAKE, 2, 0, FAKE, FAKE, None, None, 2, 5000, FAKE, None,
+                                   FAKE, ws_need, None) == ENULL
+    # prefill: one sequence, rows inside max_len, known mode
+    assert lib.infv2_select_blocks(c, 1, FAKE, 10, 0, FAKE, FAKE, FAKE, None, 2, 5000, FAKE, None,
+                                   FAKE, 1 << 30, None) == ESHAPE
+    assert lib.infv2_select_blocks(c, 1, FAKE, 10, 4995, FAKE, FAKE, FAKE, None, 1, 5000, FAKE,
+                                   None, FAKE, 1 << 30, None) == ESHAPE
+    assert lib.infv2_select_blocks(c, 7, FAKE, 10, 0, FAKE, FAKE, FAKE, None, 1, 5000, FAKE, None,
+                                   FAKE, 1 << 30, None) == ESHAPE
+    assert lib.infv2_select_blocks(c, 1, FAKE, 0, 0, FAKE, FAKE, FAKE, None, 1, 5000, FAKE, None,
+                                   FAKE, 1 << 30, None) == OK       # empty chunk: nothing to do
+    need_a = tbs.infv2_workspace_bytes(cfg, tbs.OP_ATTN_DECODE, 2, 2, 5000)
+    assert lib.infv2_sparse_attn_decode(c, FAKE, FAKE, FAKE, FAKE, None, 2, 5000, FAKE, FAKE, FAKE,
+                                        need_a - 1, None) == EWS
+    assert lib.infv2_sparse_attn_decode(c, FAKE, None, FAKE, FAKE, None, 2, 5000, FAKE, FAKE, FAKE,
+                                        need_a, None) == ENULL
+    assert lib.infv2_sparse_attn_prefill(c, FAKE, -1, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                                         None) == ESHAPE
+    assert lib.infv2_sparse_attn_prefill(c, FAKE, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                                         None) == OK

@@ -252,3 +252,53 @@ def test_decode_equals_last_prefill_row():
     assert np.array_equal(idx_d.cpu().numpy()[0], idx_p.cpu().numpy()[-1])
     assert_close(h.from_device(out_d, "bf16")[0], h.from_device(out_p, "bf16")[-1], "bf16",
                  "decode vs prefill")
+
+
+def test_decode_step_graph_replays_match_eager():
+    """A captured decode step (compress + select + attend) replayed several times,
+    with eager work and synchronisations in between, equals the eager result."""
+    h = _harness()
+    from synth import extra_decode_queries
+    import trainable_block_sparse_amd as tbs
+    wl = _small(lens=[9000, 20000], topk=16, local=4, seed=41)
+    _say("graph replay of a decode step")
+    dev = h.DeviceWorkload(wl)
+    dev.compress()
+    qs = h.to_device(extra_decode_queries(wl, 3))
+    B = wl.batch
+    idx = torch.empty((B, 2, 16), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(dev.q)
+    ws_s = dev.ws(tbs.OP_SELECT_DECODE, B, B, dev.max_len)
+    ws_a = dev.ws(tbs.OP_ATTN_DECODE, B, B, dev.max_len)
+    qbuf = qs[0].clone()
+
+    def step():
+        dev.compress()
+        tbs.infv2_select_blocks(dev.cfg, tbs.INFV2_MODE_DECODE, qbuf, B, 0, dev.ck, dev.ck_offsets,
+                                dev.kv_offsets, dev.kv_lens, B, dev.max_len, idx, None, ws_s)
+        tbs.infv2_sparse_attn_decode(dev.cfg, qbuf, dev.k, dev.v, dev.kv_offsets, dev.kv_lens, B,
+                                     dev.max_len, idx, out, ws_a)
+
+    eager = []
+    for r in range(3):
+        qbuf.copy_(qs[r])
+        step()
+        torch.cuda.synchronize()
+        eager.append((idx.clone(), out.clone()))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(6):
+        r = rep % 3
+        qbuf.copy_(qs[r])
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, eager[r][0]), f"replay {rep}: selection differs"
+        assert torch.equal(out, eager[r][1]), f"replay {rep}: output differs"
+        step()                     # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager[r][1])

@@ -3,12 +3,14 @@
 // the k*m tokens of its selected blocks) and "Query group sharing" (the 16 heads
 // of a group read the same blocks, so K/V of a block is loaded once per group).
 //
-// Both kernels stage 64-token K/V tiles of a selected block in LDS and keep an
-// online softmax (running max, running sum, unnormalised output) per head.
+// These vector-ALU kernels serve fp32 inputs (and bf16 prefill until its matrix
+// core kernel takes over); bf16 decode runs on the matrix cores (attn_decode.hip).
+// Both stage 64-token K/V tiles of a selected block in LDS and keep an online
+// softmax (running max, running sum, unnormalised output) per head.
 //   attn_decode_kernel   grid (split, KV head, sequence): each block handles
-//                        kBlocksPerSplit of the selected blocks; the last
-//                        block of a (sequence, KV head) merges the partial
-//                        (max, sum, output) triples by their LogSumExp.
+//                        kBlocksPerSplit of the selected blocks and writes a
+//                        partial (max, sum, output); attn_decode_merge
+//                        combines them by their LogSumExp.
 //   attn_prefill_kernel  grid (row, KV head): all selected blocks of one row,
 //                        causal within the query's own block (t <= i).
 #include "common.hpp"
@@ -26,7 +28,6 @@ AttnDecodeWs attn_decode_ws(const Shape& sh, int batch) {
     size_t off = 0;
     w.part_o = off;   off += align256(bg * w.nsplit * kGroup * kHeadDim * sizeof(float));
     w.part_ml = off;  off += align256(bg * w.nsplit * kGroup * sizeof(float2));
-    w.counters = off; off += align256(bg * sizeof(uint32_t));
     w.total = off;
     return w;
 }
@@ -131,11 +132,9 @@ template <typename T>
 __global__ __launch_bounds__(256) void attn_decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int64_t* __restrict__ kv_off, const int64_t* __restrict__ kv_lens,
-    const int32_t* __restrict__ idx, T* __restrict__ out, float* __restrict__ part_o,
-    float2* __restrict__ part_ml, uint32_t* __restrict__ counters, int hq, int hkv, int m,
-    int topk, int nsplit, float scale) {
+    const int32_t* __restrict__ idx, float* __restrict__ part_o, float2* __restrict__ part_ml,
+    int hq, int hkv, int m, int topk, int nsplit, float scale) {
     __shared__ AttnSmem sm;
-    __shared__ uint32_t s_last;
     const int b = blockIdx.z, g = blockIdx.y, sp = blockIdx.x, t = threadIdx.x;
     const int64_t o0 = kv_off[b], cap = kv_off[b + 1] - o0;
     int64_t n = kv_lens ? kv_lens[b] : cap;
@@ -154,34 +153,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     float* po = part_o + ((bg * nsplit + sp) * kGroup + h) * kHeadDim + c0;
     *reinterpret_cast<float4*>(po) = make_float4(o[0], o[1], o[2], o[3]);
     *reinterpret_cast<float4*>(po + 4) = make_float4(o[4], o[5], o[6], o[7]);
-    if ((t & 15) == 0) part_ml[(bg * nsplit + sp) * kGroup + h] = make_float2(mrun, lrun);
+    // max in log2 units, as the shared merge kernel expects
+    if ((t & 15) == 0)
+        part_ml[(bg * nsplit + sp) * kGroup + h] = make_float2(mrun * 1.4426950408889634f, lrun);
 
-    __threadfence();
-    __syncthreads();
-    if (t == 0) s_last = (atomicAdd(&counters[bg], 1u) == static_cast<uint32_t>(nsplit - 1));
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    float mx = -INFINITY;
-    for (int x = 0; x < nsplit; ++x) mx = fmaxf(mx, part_ml[(bg * nsplit + x) * kGroup + h].x);
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
-    if (mx != -INFINITY) {
-        for (int x = 0; x < nsplit; ++x) {
-            const float2 ml = part_ml[(bg * nsplit + x) * kGroup + h];
-            if (ml.x == -INFINITY) continue;
-            const float wgt = expf(ml.x - mx);
-            den += wgt * ml.y;
-            const float* src = part_o + ((bg * nsplit + x) * kGroup + h) * kHeadDim + c0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = fmaf(wgt, src[e], acc[e]);
-        }
-    }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    T* dst = out + (static_cast<size_t>(b) * hq + static_cast<size_t>(g) * kGroup + h) * kHeadDim + c0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) io<T>::store(dst + e, acc[e] * inv);
-    if (t == 0) counters[bg] = 0u;
 }
 
 template <typename T>
@@ -214,12 +189,15 @@ hipError_t launch_attn_decode(const Shape& sh, const void* q, const void* k, con
     dim3 grid(w.nsplit, sh.hkv, batch);
     float* po = reinterpret_cast<float*>(base + w.part_o);
     float2* pml = reinterpret_cast<float2*>(base + w.part_ml);
-    uint32_t* cnt = reinterpret_cast<uint32_t*>(base + w.counters);
-    if (sh.io_bf16)
-        attn_decode_kernel<bf16_t><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), kv_off, kv_lens, idx, static_cast<bf16_t*>(out), po, pml, cnt, sh.hq, sh.hkv, sh.m, sh.topk, w.nsplit, sh.attn_scale);
-    else
-        attn_decode_kernel<float><<<grid, 256, 0, st>>>(static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), kv_off, kv_lens, idx, static_cast<float*>(out), po, pml, cnt, sh.hq, sh.hkv, sh.m, sh.topk, w.nsplit, sh.attn_scale);
-    return hipGetLastError();
+    hipError_t e;
+    if (sh.io_bf16) {
+        e = launch_attn_decode_mfma(sh, q, k, v, kv_off, kv_lens, batch, idx, po, pml, w.nsplit, st);
+    } else {
+        attn_decode_kernel<float><<<grid, 256, 0, st>>>(static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), kv_off, kv_lens, idx, po, pml, sh.hq, sh.hkv, sh.m, sh.topk, w.nsplit, sh.attn_scale);
+        e = hipGetLastError();
+    }
+    if (e != hipSuccess) return e;
+    return launch_attn_decode_merge(sh, po, pml, out, batch, w.nsplit, st);
 }
 
 hipError_t launch_attn_prefill(const Shape& sh, const void* q, int rows, int64_t q_start,

@@ -102,3 +102,31 @@ __device__ __forceinline__ uint32_t block_incl_scan256(uint32_t v, uint32_t* tmp
 }
 
 }  // namespace infv2
+
+namespace infv2 {
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
+
+// D = A(16x32) * B(32x16) + C; lane l holds A[l%16][8(l/16)+e], B[8(l/16)+e][l%16],
+// C/D[4(l/16)+r][l%16]  (layout checked on gfx950)
+__device__ __forceinline__ f32x4_t mfma32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// D = A(16x16) * B(16x16) + C; lane l holds A[l%16][4(l/16)+e], B[4(l/16)+e][l%16]
+__device__ __forceinline__ f32x4_t mfma16(s16x4_t a, s16x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// two floats that hold bf16 values exactly -> packed bf16 pair (no rounding needed)
+__device__ __forceinline__ uint32_t pack_exact(float lo, float hi) {
+    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+// two floats -> packed bf16 pair, round to nearest even
+__device__ __forceinline__ uint32_t pack_rne(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+}  // namespace infv2

@@ -45,7 +45,17 @@ __global__ __launch_bounds__(256) void compress_kernel(
         if (j < 0 || j >= nc || j >= ccap) continue;
         double acc0 = 0.0, acc1 = 0.0, acc2 = 0.0, acc3 = 0.0;
         const Tin* src = kh + j * s * kHeadDim;
-        for (int t = 0; t < p; ++t) {
+        // batches of 8 independent loads keep the memory pipeline full; the sum
+        // itself still runs over t in order
+        int t = 0;
+        for (; t + 8 <= p; t += 8) {
+            float v[8][4];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) load4(src + static_cast<int64_t>(t + u) * kHeadDim, v[u]);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) { acc0 += v[u][0]; acc1 += v[u][1]; acc2 += v[u][2]; acc3 += v[u][3]; }
+        }
+        for (; t < p; ++t) {
             float v[4];
             load4(src + static_cast<int64_t>(t) * kHeadDim, v);
             acc0 += v[0]; acc1 += v[1]; acc2 += v[2]; acc3 += v[3];

@@ -19,9 +19,9 @@ struct Shape {
 
 // workspace carving (all offsets 256-byte aligned)
 struct SelectDecodeWs {
-    size_t logits, partial, lse, keys, counters, total;
+    size_t logits, partial, keys, total;
     int nchunk_a, nchunk_b;
-    int64_t nc_max, nblk_max;
+    int64_t nc_max, nc_ld, nblk_max;   // nc_ld: logits row stride (multiple of 4)
 };
 SelectDecodeWs select_decode_ws(const Shape& sh, int batch, int64_t max_len);
 
@@ -32,7 +32,7 @@ struct SelectPrefillWs {
 SelectPrefillWs select_prefill_ws(const Shape& sh, int rows, int64_t max_len);
 
 struct AttnDecodeWs {
-    size_t part_o, part_ml, counters, total;
+    size_t part_o, part_ml, total;
     int nsplit;
 };
 AttnDecodeWs attn_decode_ws(const Shape& sh, int batch);
@@ -53,6 +53,13 @@ hipError_t launch_select_prefill(const Shape& sh, const void* q, int rows, int64
 hipError_t launch_attn_decode(const Shape& sh, const void* q, const void* k, const void* v,
                               const int64_t* kv_off, const int64_t* kv_lens, int batch,
                               const int32_t* idx, void* out, void* ws, hipStream_t st);
+
+hipError_t launch_attn_decode_mfma(const Shape& sh, const void* q, const void* k, const void* v,
+                                   const int64_t* kv_off, const int64_t* kv_lens, int batch,
+                                   const int32_t* idx, float* part_o, float2* part_ml, int nsplit,
+                                   hipStream_t st);
+hipError_t launch_attn_decode_merge(const Shape& sh, const float* part_o, const float2* part_ml,
+                                    void* out, int batch, int nsplit, hipStream_t st);
 
 hipError_t launch_attn_prefill(const Shape& sh, const void* q, int rows, int64_t q_start,
                                const void* k, const void* v, const int64_t* kv_off,

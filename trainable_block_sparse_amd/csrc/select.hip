@@ -6,14 +6,18 @@
 //
 // Decode (one row per sequence, thousands of kernels per row):
 //   sel_dec_logits  grid (kernel chunk, KV head, sequence).  Each block scores
-//                   64 kernels against the group's 16 heads, stores the logits
-//                   (fp32 scratch, 16 x n_c floats per KV head: an eighth of a
-//                   fp32 compressed-key re-read) and a partial (max, sum-exp)
-//                   per head; the last block of each (sequence, head) to finish
-//                   folds the partials into the per-head LogSumExp.
-//   sel_dec_scores  grid (256-kernel chunk, KV head, sequence).  Group score
-//                   R_j = mean_h exp(z_hj - LSE_h), block max by atomicMax on
-//                   sortable keys; the last block runs the top-k.
+//                   64 kernels against the group's 16 heads (matrix cores for
+//                   bf16 queries), stores the logits (fp32 scratch, 16 x n_c
+//                   floats per KV head: an eighth of a fp32 compressed-key
+//                   re-read) and a partial (max, sum-exp) per head.
+//   sel_dec_scores  grid (256-kernel chunk, KV head, sequence).  Each block folds
+//                   the partials into the per-head LogSumExp, forms the group
+//                   score R_j = mean_h exp(z_hj - LSE_h) and the block max by
+//                   atomicMax on sortable keys.
+//   sel_dec_topk    one block per (sequence, KV head).
+// Cross-block results are handed over at kernel boundaries only: a device-scope
+// fence inside a kernel costs a write-back and invalidation of the whole L2 of
+// the XCD on gfx950, once per block.
 // Prefill (rows of one sequence, causal visibility per row):
 //   sel_pre_lse     4 rows per block: online (max, sum-exp) over visible kernels.
 //   sel_pre_scores  4 rows per block: logits again, group score, block max.
@@ -48,15 +52,14 @@ SelectDecodeWs select_decode_ws(const Shape& sh, int batch, int64_t max_len) {
     w.nblk_max = (max_len + sh.m - 1) / sh.m;
     if (w.nblk_max < 1) w.nblk_max = 1;
     const int64_t ncm = w.nc_max > 0 ? w.nc_max : 1;
+    w.nc_ld = (ncm + 3) & ~int64_t(3);
     w.nchunk_a = static_cast<int>((ncm + kChunkA - 1) / kChunkA);
     w.nchunk_b = static_cast<int>((ncm + kChunkB - 1) / kChunkB);
     const size_t bg = static_cast<size_t>(batch) * sh.hkv;
     size_t off = 0;
-    w.logits = off;   off += align256(bg * ncm * kGroup * sizeof(float));
+    w.logits = off;   off += align256(bg * w.nc_ld * kGroup * sizeof(float));
     w.partial = off;  off += align256(bg * w.nchunk_a * kGroup * sizeof(float2));
-    w.lse = off;      off += align256(bg * kGroup * sizeof(float));
     w.keys = off;     off += align256(bg * w.nblk_max * sizeof(uint32_t));
-    w.counters = off; off += align256(bg * 2 * sizeof(uint32_t));
     w.total = off;
     return w;
 }
@@ -77,11 +80,9 @@ template <typename Tq, typename Tck>
 __global__ __launch_bounds__(256) void sel_dec_logits(
     const Tq* __restrict__ q, const Tck* __restrict__ ck, const int64_t* __restrict__ ck_off,
     const int64_t* __restrict__ kv_off, const int64_t* __restrict__ kv_lens, int hq, int hkv,
-    int p, int s, float score_scale, int64_t nc_max, int nchunk, int64_t nblk_max,
-    float* __restrict__ logits, float2* __restrict__ partial, float* __restrict__ lse,
-    uint32_t* __restrict__ keys, uint32_t* __restrict__ counters) {
+    int p, int s, float score_scale, int64_t nc_max, int64_t nc_ld, int nchunk, int64_t nblk_max,
+    float* __restrict__ logits, float2* __restrict__ partial, uint32_t* __restrict__ keys) {
     __shared__ float qs[kGroup][kHeadDim];
-    __shared__ uint32_t s_last;
     const int b = blockIdx.z, g = blockIdx.y, ch = blockIdx.x, t = threadIdx.x;
     const int64_t cap = kv_off[b + 1] - kv_off[b];
     int64_t n = kv_lens ? kv_lens[b] : cap;
@@ -121,11 +122,10 @@ __global__ __launch_bounds__(256) void sel_dec_logits(
                 acc[u] = fmaf(qh[d + 3], kv[3], acc[u]);
             }
         }
-        float* dst = logits + (bg * nc_max + j) * kGroup;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             z[u] = score_scale * acc[u];
-            dst[w + 4 * u] = z[u];
+            logits[(bg * kGroup + w + 4 * u) * nc_ld + j] = z[u];
         }
     } else {
 #pragma unroll
@@ -139,39 +139,121 @@ __global__ __launch_bounds__(256) void sel_dec_logits(
         if (lane == 0) partial[(bg * nchunk + ch) * kGroup + w + 4 * u] = make_float2(mx, sm);
     }
 
-    // the last block of this (sequence, KV head) folds the partials into LSE
-    __threadfence();
-    __syncthreads();
-    if (t == 0) s_last = (atomicAdd(&counters[bg * 2], 1u) == static_cast<uint32_t>(nchunk - 1));
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    const int h = t >> 4, r = t & 15;
-    float mx = -INFINITY;
-    for (int c = r; c < nchunk; c += 16) mx = fmaxf(mx, partial[(bg * nchunk + c) * kGroup + h].x);
-    mx = max16(mx);
-    float sm = 0.f;
-    if (mx != -INFINITY)
-        for (int c = r; c < nchunk; c += 16) {
-            const float2 pm = partial[(bg * nchunk + c) * kGroup + h];
-            if (pm.x != -INFINITY) sm += pm.y * expf(pm.x - mx);
-        }
-    sm = sum16(sm);
-    if (r == 0) lse[bg * kGroup + h] = (mx == -INFINITY) ? -INFINITY : mx + logf(sm);
-    if (t == 0) counters[bg * 2] = 0u;
 }
 
-// ------------------------------------------------------------------ decode, pass 2 + top-k
+// ------------------------------------------------------------------ decode, pass 1 on the matrix cores
+// One wave per block scores 64 kernels.  Z^T[kernel][head] = CK (64x128) . Q^T:
+// the compressed keys are the A operand as stored (lane: 8 consecutive d of one
+// kernel); fp32 keys are split into bf16 hi + lo (x = hi + lo + O(2^-17 |x|)),
+// two MFMAs per tile, products exact in fp32.  Z^T puts one head per lane column.
+template <bool kCkBf16>
+__global__ __launch_bounds__(64) void sel_dec_logits_mfma(
+    const bf16_t* __restrict__ q, const void* __restrict__ ck, const int64_t* __restrict__ ck_off,
+    const int64_t* __restrict__ kv_off, const int64_t* __restrict__ kv_lens, int hq, int hkv,
+    int p, int s, float score_scale, int64_t nc_max, int64_t nc_ld, int nchunk, int64_t nblk_max,
+    float* __restrict__ logits, float2* __restrict__ partial, uint32_t* __restrict__ keys) {
+    const int b = blockIdx.z, g = blockIdx.y, ch = blockIdx.x, l = threadIdx.x;
+    const int lg = l >> 4, lc = l & 15;
+    const int64_t cap = kv_off[b + 1] - kv_off[b];
+    int64_t n = kv_lens ? kv_lens[b] : cap;
+    n = n < cap ? n : cap;
+    const int64_t ccap = ck_off[b + 1] - ck_off[b];
+    int64_t nvis = num_kernels(n, p, s);
+    nvis = nvis < ccap ? nvis : ccap;
+    nvis = nvis < nc_max ? nvis : nc_max;
+    const size_t bg = static_cast<size_t>(b) * hkv + g;
+    {
+        uint32_t* kb = keys + bg * nblk_max;
+        const int64_t per = (nblk_max + nchunk - 1) / nchunk;
+        const int64_t e = (ch + 1) * per < nblk_max ? (ch + 1) * per : nblk_max;
+        for (int64_t j = ch * per + l; j < e; j += 64) kb[j] = 0u;
+    }
+    const bf16_t* qrow = q + (static_cast<size_t>(b) * hq + static_cast<size_t>(g) * kGroup + lc) * kHeadDim;
+    bf16x8_t qf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(ldg16(qrow + 32 * ks + 8 * lg));
+    const int64_t j0 = static_cast<int64_t>(ch) * kChunkA;
+    const int64_t cbase = (ck_off[b] * hkv + static_cast<int64_t>(g) * ccap);
+    f32x4_t z[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        z[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        int64_t j = j0 + 16 * mt + lc;
+        if (j0 + 16 * mt >= nvis) continue;            // whole tile past the end (wave-uniform)
+        j = j < nvis ? j : nvis - 1;
+        if (kCkBf16) {
+            const bf16_t* row = static_cast<const bf16_t*>(ck) + (cbase + j) * kHeadDim + 8 * lg;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) z[mt] = mfma32(as_bf16x8(ldg16(row + 32 * ks)), qf[ks], z[mt]);
+        } else {
+            const float* row = static_cast<const float*>(ck) + (cbase + j) * kHeadDim + 8 * lg;
+            float4 xa[4], xb[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                xa[ks] = *reinterpret_cast<const float4*>(row + 32 * ks);
+                xb[ks] = *reinterpret_cast<const float4*>(row + 32 * ks + 4);
+            }
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const float x[8] = {xa[ks].x, xa[ks].y, xa[ks].z, xa[ks].w, xb[ks].x, xb[ks].y, xb[ks].z, xb[ks].w};
+                float hi[8], lo[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    hi[e] = bf16_to_f32(f32_to_bf16(x[e]));
+                    lo[e] = x[e] - hi[e];
+                }
+                uint4 uh, ul;
+                uh.x = pack_exact(hi[0], hi[1]); uh.y = pack_exact(hi[2], hi[3]);
+                uh.z = pack_exact(hi[4], hi[5]); uh.w = pack_exact(hi[6], hi[7]);
+                ul.x = pack_rne(lo[0], lo[1]); ul.y = pack_rne(lo[2], lo[3]);
+                ul.z = pack_rne(lo[4], lo[5]); ul.w = pack_rne(lo[6], lo[7]);
+                z[mt] = mfma32(as_bf16x8(uh), qf[ks], z[mt]);
+                z[mt] = mfma32(as_bf16x8(ul), qf[ks], z[mt]);
+            }
+        }
+    }
+    // lane holds Z[head lc][kernel j0 + 16 mt + 4 lg + r]
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const int64_t jb = j0 + 16 * mt + 4 * lg;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float v = (jb + r < nvis) ? score_scale * z[mt][r] : -INFINITY;
+            z[mt][r] = v;
+            mx = fmaxf(mx, v);
+        }
+        float* dst = logits + (bg * kGroup + lc) * nc_ld + jb;
+        if (jb + 3 < nvis) {
+            *reinterpret_cast<float4*>(dst) = make_float4(z[mt][0], z[mt][1], z[mt][2], z[mt][3]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) if (jb + r < nvis) dst[r] = z[mt][r];
+        }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float sm = 0.f;
+    if (mx != -INFINITY) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm += (z[mt][r] == -INFINITY) ? 0.f : expf(z[mt][r] - mx);
+    }
+    sm += __shfl_xor(sm, 16, 64);
+    sm += __shfl_xor(sm, 32, 64);
+    if (lg == 0) partial[(bg * nchunk + ch) * kGroup + lc] = make_float2(mx, sm);
+
+}
+
+// ------------------------------------------------------------------ decode, pass 2
 __global__ __launch_bounds__(256) void sel_dec_scores(
     const int64_t* __restrict__ kv_off, const int64_t* __restrict__ kv_lens,
-    const int64_t* __restrict__ ck_off, int hkv, int m, int p, int s, int topk, int init,
-    int local, int64_t nc_max, int nchunk, int64_t nblk_max, const float* __restrict__ logits,
-    const float* __restrict__ lse, uint32_t* __restrict__ keys, uint32_t* __restrict__ counters,
-    int32_t* __restrict__ idx, float* __restrict__ score) {
+    const int64_t* __restrict__ ck_off, int hkv, int m, int p, int s, int64_t nc_max,
+    int64_t nc_ld, int nchunk_a, int64_t nblk_max, const float* __restrict__ logits,
+    const float2* __restrict__ partial, uint32_t* __restrict__ keys) {
     __shared__ float ls[kGroup];
     __shared__ float rs[kChunkB];
-    __shared__ uint32_t s_last;
-    __shared__ TopkSmem sm;
     const int b = blockIdx.z, g = blockIdx.y, ch = blockIdx.x, t = threadIdx.x;
     const int64_t cap = kv_off[b + 1] - kv_off[b];
     int64_t n = kv_lens ? kv_lens[b] : cap;
@@ -183,16 +265,37 @@ __global__ __launch_bounds__(256) void sel_dec_scores(
     const size_t bg = static_cast<size_t>(b) * hkv + g;
     uint32_t* kb = keys + bg * nblk_max;
 
-    if (t < kGroup) ls[t] = lse[bg * kGroup + t];
+    // per-head LogSumExp from the (max, sum-exp) partials of pass 1 (16 threads per head)
+    {
+        const int h = t >> 4, r = t & 15;
+        const float2* pp = partial + bg * nchunk_a * kGroup + h;
+        float mx = -INFINITY;
+#pragma unroll 8
+        for (int c = r; c < nchunk_a; c += 16) mx = fmaxf(mx, pp[static_cast<size_t>(c) * kGroup].x);
+        mx = max16(mx);
+        float sm = 0.f;
+        if (mx != -INFINITY) {
+#pragma unroll 8
+            for (int c = r; c < nchunk_a; c += 16) {
+                const float2 pm = pp[static_cast<size_t>(c) * kGroup];
+                sm += (pm.x == -INFINITY) ? 0.f : pm.y * expf(pm.x - mx);
+            }
+        }
+        sm = sum16(sm);
+        if (r == 0) ls[h] = (mx == -INFINITY) ? -INFINITY : mx + logf(sm);
+    }
     __syncthreads();
     const int64_t j0 = static_cast<int64_t>(ch) * kChunkB;
     const int64_t j = j0 + t;
     float R = -INFINITY;
     if (j < nvis) {
-        const float* z = logits + (bg * nc_max + j) * kGroup;
+        const float* z = logits + bg * kGroup * nc_ld + j;
+        float zz[kGroup];
+#pragma unroll
+        for (int h = 0; h < kGroup; ++h) zz[h] = z[h * nc_ld];
         float acc = 0.f;
 #pragma unroll
-        for (int h = 0; h < kGroup; ++h) acc += expf(z[h] - ls[h]);
+        for (int h = 0; h < kGroup; ++h) acc += expf(zz[h] - ls[h]);
         R = acc * (1.0f / kGroup);
     }
     rs[t] = R;
@@ -210,17 +313,27 @@ __global__ __launch_bounds__(256) void sel_dec_scores(
             atomicMax(&kb[blk], score_to_key(mx));
         }
     }
+}
 
-    __threadfence();
-    __syncthreads();
-    if (t == 0) s_last = (atomicAdd(&counters[bg * 2 + 1], 1u) == static_cast<uint32_t>(nchunk - 1));
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+// ------------------------------------------------------------------ decode, top-k
+__global__ __launch_bounds__(256) void sel_dec_topk(const int64_t* __restrict__ kv_off,
+                                                    const int64_t* __restrict__ kv_lens, int hkv,
+                                                    int m, int topk, int init, int local,
+                                                    int64_t nblk_max,
+                                                    const uint32_t* __restrict__ keys,
+                                                    int32_t* __restrict__ idx,
+                                                    float* __restrict__ score) {
+    __shared__ TopkSmem sm;
+    extern __shared__ uint32_t lkeys[];
+    const int b = blockIdx.y, g = blockIdx.x;
+    const int64_t cap = kv_off[b + 1] - kv_off[b];
+    int64_t n = kv_lens ? kv_lens[b] : cap;
+    n = n < cap ? n : cap;
     int64_t c = n > 0 ? (n - 1) / m : -1;
     c = c < nblk_max - 1 ? c : nblk_max - 1;
-    block_topk(kb, c, topk, init, local, idx + bg * topk, score ? score + bg * topk : nullptr, sm);
-    if (t == 0) counters[bg * 2 + 1] = 0u;
+    const size_t bg = static_cast<size_t>(b) * hkv + g;
+    block_topk(keys + bg * nblk_max, c, topk, init, local, idx + bg * topk,
+               score ? score + bg * topk : nullptr, sm, lkeys);
 }
 
 // ------------------------------------------------------------------ prefill, pass 1
@@ -392,9 +505,11 @@ __global__ __launch_bounds__(256) void sel_pre_topk(int64_t q_start, int hkv, in
     __shared__ TopkSmem sm;
     const int row = blockIdx.x, g = blockIdx.y;
     const size_t rg = static_cast<size_t>(row) * hkv + g;
-    const int64_t c = (q_start + row) / m;
+    int64_t c = (q_start + row) / m;
+    c = c < nblk_max - 1 ? c : nblk_max - 1;
+    extern __shared__ uint32_t lkeys[];
     block_topk(keys + rg * nblk_max, c, topk, init, local, idx + rg * topk,
-               score ? score + rg * topk : nullptr, sm);
+               score ? score + rg * topk : nullptr, sm, lkeys);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -405,17 +520,22 @@ static void dec_launch(const Shape& sh, const void* q, const void* ck, const int
                        hipStream_t st) {
     dim3 ga(w.nchunk_a, sh.hkv, batch), gb(w.nchunk_b, sh.hkv, batch);
     const int64_t ncm = w.nc_max > 0 ? w.nc_max : 1;
-    sel_dec_logits<Tq, Tck><<<ga, 256, 0, st>>>(
-        static_cast<const Tq*>(q), static_cast<const Tck*>(ck), ck_off, kv_off, kv_lens, sh.hq,
-        sh.hkv, sh.p, sh.s, sh.score_scale, ncm, w.nchunk_a, w.nblk_max,
-        reinterpret_cast<float*>(ws + w.logits), reinterpret_cast<float2*>(ws + w.partial),
-        reinterpret_cast<float*>(ws + w.lse), reinterpret_cast<uint32_t*>(ws + w.keys),
-        reinterpret_cast<uint32_t*>(ws + w.counters));
-    sel_dec_scores<<<gb, 256, 0, st>>>(
-        kv_off, kv_lens, ck_off, sh.hkv, sh.m, sh.p, sh.s, sh.topk, sh.init, sh.local, ncm,
-        w.nchunk_b, w.nblk_max, reinterpret_cast<const float*>(ws + w.logits),
-        reinterpret_cast<const float*>(ws + w.lse), reinterpret_cast<uint32_t*>(ws + w.keys),
-        reinterpret_cast<uint32_t*>(ws + w.counters), idx, score);
+    float* logits = reinterpret_cast<float*>(ws + w.logits);
+    float2* partial = reinterpret_cast<float2*>(ws + w.partial);
+    uint32_t* keys = reinterpret_cast<uint32_t*>(ws + w.keys);
+    if (sizeof(Tq) == 2)
+        sel_dec_logits_mfma<sizeof(Tck) == 2><<<ga, 64, 0, st>>>(
+            static_cast<const bf16_t*>(q), ck, ck_off, kv_off, kv_lens, sh.hq, sh.hkv, sh.p, sh.s,
+            sh.score_scale, ncm, w.nc_ld, w.nchunk_a, w.nblk_max, logits, partial, keys);
+    else
+        sel_dec_logits<Tq, Tck><<<ga, 256, 0, st>>>(
+            static_cast<const Tq*>(q), static_cast<const Tck*>(ck), ck_off, kv_off, kv_lens, sh.hq,
+            sh.hkv, sh.p, sh.s, sh.score_scale, ncm, w.nc_ld, w.nchunk_a, w.nblk_max, logits,
+            partial, keys);
+    sel_dec_scores<<<gb, 256, 0, st>>>(kv_off, kv_lens, ck_off, sh.hkv, sh.m, sh.p, sh.s, ncm,
+                                       w.nc_ld, w.nchunk_a, w.nblk_max, logits, partial, keys);
+    sel_dec_topk<<<dim3(sh.hkv, batch), 256, w.nblk_max * sizeof(uint32_t), st>>>(
+        kv_off, kv_lens, sh.hkv, sh.m, sh.topk, sh.init, sh.local, w.nblk_max, keys, idx, score);
 }
 
 hipError_t launch_select_decode(const Shape& sh, const void* q, const void* ck,
@@ -448,7 +568,7 @@ static void pre_launch(const Shape& sh, const void* q, int rows, int64_t q_start
                                                static_cast<const Tck*>(ck), ck_off, sh.hq, sh.hkv,
                                                sh.m, sh.p, sh.s, sh.score_scale, w.nblk_max, lse,
                                                keys);
-    sel_pre_topk<<<dim3(rows, sh.hkv), 256, 0, st>>>(q_start, sh.hkv, sh.m, sh.topk, sh.init,
+    sel_pre_topk<<<dim3(rows, sh.hkv), 256, w.nblk_max * sizeof(uint32_t), st>>>(q_start, sh.hkv, sh.m, sh.topk, sh.init,
                                                      sh.local, w.nblk_max, keys, idx, score);
 }
 
