@@ -224,6 +224,7 @@ def bench_prefill(args, torch, tbs, gh) -> dict:
     idx = torch.empty((L, hkv, k), dtype=torch.int32, device="cuda")
     out = torch.empty_like(dev.q)
     ws = dev.ws(tbs.OP_SELECT_PREFILL, C, 1, L)
+    wsa = dev.ws(tbs.OP_ATTN_PREFILL, C, 1, L)
     p, s = wl.kernel_size, wl.kernel_stride
 
     def run(record):
@@ -241,7 +242,7 @@ def bench_prefill(args, torch, tbs, gh) -> dict:
                                     ws)
             e2 = T.event() if record else None
             tbs.infv2_sparse_attn_prefill(cfg, dev.q[q0:q1], q1 - q0, q0, dev.k, dev.v,
-                                          dev.kv_offsets, idx[q0:q1], out[q0:q1])
+                                          dev.kv_offsets, idx[q0:q1], out[q0:q1], wsa)
             e3 = T.event() if record else None
             evs.append((e0, e1, e2, e3))
         return evs
@@ -275,7 +276,7 @@ def bench_prefill(args, torch, tbs, gh) -> dict:
         "last_chunk_useful_flops": float(4 * d * (hq // hkv) * tok[L - C:].sum()),
         "mean_attended_tokens": float(tok.mean()),
     }
-    res["roofline"] = {"bound": "mfma", "kernel": "attn_prefill_kernel",
+    res["roofline"] = {"bound": "mfma", "kernel": "attn_prefill_mfma",
                        "achieved": res["tflops_attn"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                        "frac": res["tflops_attn"] / BF16_PEAK_TFLOPS, "traffic": None}
     res["_idx"] = gi

@@ -135,8 +135,9 @@ class DeviceWorkload:
         tbs.infv2_select_blocks(self.cfg, tbs.INFV2_MODE_PREFILL, q, rows, q0, self.ck,
                                 self.ck_offsets, self.kv_offsets, None, 1, q1, idx, score, ws)
         out = torch.empty_like(q)
+        wsa = self.ws(tbs.OP_ATTN_PREFILL, rows, 1, q1)
         tbs.infv2_sparse_attn_prefill(self.cfg, q, rows, q0, self.k, self.v, self.kv_offsets, idx,
-                                      out)
+                                      out, wsa)
         return idx, score, out
 
     def prefill(self, chunk: int):

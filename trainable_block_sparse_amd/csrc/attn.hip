@@ -3,8 +3,8 @@
 // the k*m tokens of its selected blocks) and "Query group sharing" (the 16 heads
 // of a group read the same blocks, so K/V of a block is loaded once per group).
 //
-// These vector-ALU kernels serve fp32 inputs (and bf16 prefill until its matrix
-// core kernel takes over); bf16 decode runs on the matrix cores (attn_decode.hip).
+// These vector-ALU kernels serve fp32 inputs and the shapes the matrix-core
+// kernels do not take (attn_decode.hip, attn_prefill.hip).
 // Both stage 64-token K/V tiles of a selected block in LDS and keep an online
 // softmax (running max, running sum, unnormalised output) per head.
 //   attn_decode_kernel   grid (split, KV head, sequence): each block handles
@@ -203,8 +203,9 @@ hipError_t launch_attn_decode(const Shape& sh, const void* q, const void* k, con
 hipError_t launch_attn_prefill(const Shape& sh, const void* q, int rows, int64_t q_start,
                                const void* k, const void* v, const int64_t* kv_off,
                                const int32_t* idx, void* out, void* ws, hipStream_t st) {
-    (void)ws;
     if (rows <= 0) return hipSuccess;
+    if (attn_prefill_mfma_ok(sh))
+        return launch_attn_prefill_mfma(sh, q, rows, q_start, k, v, kv_off, idx, out, ws, st);
     dim3 grid(rows, sh.hkv);
     if (sh.io_bf16)
         attn_prefill_kernel<bf16_t><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(q), q_start, static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), kv_off, idx, static_cast<bf16_t*>(out), sh.hq, sh.hkv, sh.m, sh.topk, sh.attn_scale);

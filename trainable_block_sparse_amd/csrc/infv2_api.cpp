@@ -60,6 +60,7 @@ size_t ws_bytes_for(const infv2_config* c, int32_t op, int32_t rows, int32_t bat
         case INFV2_OP_SELECT_DECODE: return infv2::select_decode_ws(sh, batch, max_len).total;
         case INFV2_OP_SELECT_PREFILL: return infv2::select_prefill_ws(sh, rows, max_len).total;
         case INFV2_OP_ATTN_DECODE: return infv2::attn_decode_ws(sh, batch).total;
+        case INFV2_OP_ATTN_PREFILL: return infv2::attn_prefill_ws_bytes(sh, max_len);
         default: return 0;
     }
 }
@@ -171,8 +172,9 @@ int32_t infv2_sparse_attn_prefill(const infv2_config* c, const void* q, int32_t 
     if (!q || !k || !v || !kv_offsets || !block_idx || !out) return INFV2_ERR_NULL;
     if (rows < 0 || q_start < 0) return INFV2_ERR_SHAPE;
     if ((st = check_len(c, q_start + rows)) != INFV2_OK) return st;
-    (void)ws_bytes;
     if (rows == 0) return INFV2_OK;
+    const size_t need = ws_bytes_for(c, INFV2_OP_ATTN_PREFILL, rows, 1, q_start + rows);
+    if (need > 0 && (!ws || ws_bytes < need)) return INFV2_ERR_WORKSPACE;
     return status_of(infv2::launch_attn_prefill(make_shape(c), q, rows, q_start, k, v, kv_offsets,
                                                 block_idx, out, ws,
                                                 static_cast<hipStream_t>(stream)));

@@ -61,6 +61,12 @@ hipError_t launch_attn_decode_mfma(const Shape& sh, const void* q, const void* k
 hipError_t launch_attn_decode_merge(const Shape& sh, const float* part_o, const float2* part_ml,
                                     void* out, int batch, int nsplit, hipStream_t st);
 
+bool attn_prefill_mfma_ok(const Shape& sh);
+size_t attn_prefill_ws_bytes(const Shape& sh, int64_t max_len);
+hipError_t launch_attn_prefill_mfma(const Shape& sh, const void* q, int rows, int64_t q_start,
+                                    const void* k, const void* v, const int64_t* kv_off,
+                                    const int32_t* idx, void* out, void* ws, hipStream_t st);
+
 hipError_t launch_attn_prefill(const Shape& sh, const void* q, int rows, int64_t q_start,
                                const void* k, const void* v, const int64_t* kv_off,
                                const int32_t* idx, void* out, void* ws, hipStream_t st);
