@@ -5,16 +5,20 @@
 // group sharing" (the group's 16 heads form the 16-wide matrix tile of a token).
 //
 // Every query row picks its own 64 blocks, so the matrix tile of a (row, block)
-// pair is 16 heads x 64 keys.  A thread block owns 16 consecutive rows (4 per
-// wave) of one KV head and streams the union of their selected blocks through
-// LDS once: K as stored, V as V^T tiles built by vt_build.  For each block a
-// wave runs each of its rows that selected the block, reading the V^T
-// fragments from LDS once for all of them:
+// pair is 16 heads x 64 keys.  A thread block owns 16 consecutive rows of one
+// KV head; wave w (of 8) takes rows w and w+8.  The block builds the union of
+// the rows' selected blocks and streams it through LDS with direct
+// global->LDS loads (K as stored, V as V^T tiles built by vt_build), two stages
+// of two blocks, so the next two blocks load while the current two compute.
+// For each block a wave runs each of its rows that selected it:
 //   S^T[key][head] = K_blk . Q_row^T          16 MFMA 16x16x32
 //   O^T[d][head]  += V^T_blk . P_row^T        16 MFMA 16x16x32
-// with the online softmax kept per (row, head) in registers (one head per lane
-// column, so rescaling is a per-lane scalar).  Keys after the row (t > i) are
-// masked in the row's own block.
+// One head sits in each lane column, so softmax state is per lane.  The
+// reference max of a row is only raised when a block exceeds it by more than
+// 2^8 (then the output is rescaled); otherwise probabilities are taken against
+// the old reference (p <= 256, exact in fp32 and bf16), which skips the
+// cross-lane max and the rescale on almost every block.  Row sums stay per lane
+// until the end.  Keys after the row (t > i) are masked in the row's own block.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -22,11 +26,13 @@ namespace infv2 {
 
 constexpr int kPB = 64;          // KV block size served here
 constexpr int kPRows = 16;       // query rows per thread block
-constexpr int kPRowsW = 4;       // query rows per wave
-constexpr int kKPad = 136;       // LDS row length of K tiles (128 + 8 bf16: 16-byte pad)
-constexpr int kVPad = 72;        // LDS row length of V^T tiles (64 + 8 bf16)
+constexpr int kPWaves = 8;
+constexpr int kPRowsW = 2;       // query rows per wave
+constexpr int kPThreads = kPWaves * 64;
 constexpr int kMaxWords = 512;   // bitmap words: up to 16384 blocks
 constexpr int kUnionCap = 2048;  // union entries: 16 rows x top-k, top-k <= 128
+constexpr int kGroup2 = 2;       // union blocks per LDS stage (two stages)
+constexpr float kRescaleSlack = 8.f;   // log2 units
 
 // V^T tiles store the 64 keys of a block in the order the P^T operand of the
 // PV product uses: position 32 kk + 8 g + 4 a + r holds key 32 kk + 16 a + 4 g + r.
@@ -65,23 +71,35 @@ __global__ __launch_bounds__(256) void vt_build(const bf16_t* __restrict__ v,
     }
 }
 
-struct PreSmem {
-    bf16_t k[2][kPB][kKPad];
-    bf16_t vt[2][kHeadDim][kVPad];
+// K tile: 64 keys x 16 chunks of 16 B; chunk c of key r sits at c ^ (r & 15).
+// V^T tile: 128 d x 8 chunks of 16 B; chunk c of row d sits at c ^ ((d >> 1) & 7).
+// Both swizzles make the 16-lane 16-byte column reads below conflict-free.
+struct UnionSmem {
     int32_t list[kUnionCap];          // union of the rows' blocks, ascending (<= 16 * topk)
     uint32_t mask[kUnionCap];         // which of the 16 rows selected each union block
     uint32_t bits[kMaxWords];
     uint32_t wbase[kMaxWords];
-    uint32_t scan_tmp[8];
+    uint32_t scan_tmp[16];
 };
+typedef bf16_t StageTiles[kGroup2][kPB * kHeadDim];   // 2 x 16 KB (K) or 2 x 16 KB (V^T)
 
-__global__ __launch_bounds__(256, 1) void attn_prefill_mfma(
+__device__ __forceinline__ uint4 k_frag(const StageTiles& t, int slot, int key, int chunk) {
+    return *reinterpret_cast<const uint4*>(&t[slot][key * kHeadDim + 8 * (chunk ^ (key & 15))]);
+}
+__device__ __forceinline__ uint4 vt_frag(const StageTiles& t, int slot, int d, int chunk) {
+    return *reinterpret_cast<const uint4*>(&t[slot][d * kPB + 8 * (chunk ^ ((d >> 1) & 7))]);
+}
+
+__global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
     const bf16_t* __restrict__ q, int rows, int64_t q_start, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ vt, const int64_t* __restrict__ kv_off,
     const int32_t* __restrict__ idx, bf16_t* __restrict__ out, int hq, int hkv, int topk,
     int64_t nblk, float scale_log2) {
-    extern __shared__ unsigned char smem_raw[];
-    PreSmem& sm = *reinterpret_cast<PreSmem*>(smem_raw);
+    // The two stages are distinct LDS objects and every access below names its
+    // stage, so the compiler can see that reading one stage does not depend on
+    // the direct global->LDS loads still filling the other one.
+    __shared__ __attribute__((aligned(16))) StageTiles k_a, v_a, k_b, v_b;
+    __shared__ UnionSmem sm;
     const int g = blockIdx.y, t = threadIdx.x;
     const int w = t >> 6, l = t & 63, lg = l >> 4, lc = l & 15;
     const int r0 = blockIdx.x * kPRows;
@@ -92,37 +110,34 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_mfma(
 
     // ---- union of the 16 rows' selected blocks (bitmap -> ascending list + row masks)
     const int nwords = static_cast<int>((nblk + 31) / 32);
-    for (int x = t; x < nwords; x += 256) sm.bits[x] = 0u;
+    for (int x = t; x < nwords; x += kPThreads) sm.bits[x] = 0u;
     __syncthreads();
     const int nent = kPRows * topk;
-    for (int e = t; e < nent; e += 256) {
+    for (int e = t; e < nent; e += kPThreads) {
         const int row = r0 + e / topk;
         if (row >= rows) continue;
         const int32_t blk = idx[(static_cast<size_t>(row) * hkv + g) * topk + e % topk];
         if (blk >= 0 && blk < nblk) atomicOr(&sm.bits[blk >> 5], 1u << (blk & 31));
     }
     __syncthreads();
-    uint32_t cnt_t = 0;
-    for (int x = 2 * t; x < 2 * t + 2 && x < nwords; ++x) cnt_t += __popc(sm.bits[x]);
-    const uint32_t base_t = block_incl_scan256(cnt_t, sm.scan_tmp) - cnt_t;
-    {
-        uint32_t pos = base_t;
-        for (int x = 2 * t; x < 2 * t + 2 && x < nwords; ++x) {
-            sm.wbase[x] = pos;
-            uint32_t bw = sm.bits[x];
-            while (bw) {
-                const int bit = __ffs(bw) - 1;
-                bw &= bw - 1;
-                sm.list[pos] = x * 32 + bit;
-                sm.mask[pos] = 0u;
-                ++pos;
-            }
+    const uint32_t word_t = t < nwords ? sm.bits[t] : 0u;      // one bitmap word per thread
+    const uint32_t cnt_t = __popc(word_t);
+    const uint32_t base_t = block_incl_scan<kPWaves>(cnt_t, sm.scan_tmp) - cnt_t;
+    if (t < nwords) {
+        sm.wbase[t] = base_t;
+        uint32_t bw = word_t, pos = base_t;
+        while (bw) {
+            const int bit = __ffs(bw) - 1;
+            bw &= bw - 1;
+            sm.list[pos] = t * 32 + bit;
+            sm.mask[pos] = 0u;
+            ++pos;
         }
-        if (t == 255) sm.scan_tmp[4] = pos;
     }
+    if (t == kPThreads - 1) sm.scan_tmp[kPWaves] = base_t + cnt_t;
     __syncthreads();
-    const int n_u = static_cast<int>(sm.scan_tmp[4]);
-    for (int e = t; e < nent; e += 256) {
+    const int n_u = static_cast<int>(sm.scan_tmp[kPWaves]);
+    for (int e = t; e < nent; e += kPThreads) {
         const int tok = e / topk, row = r0 + tok;
         if (row >= rows) continue;
         const int32_t blk = idx[(static_cast<size_t>(row) * hkv + g) * topk + e % topk];
@@ -132,14 +147,14 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_mfma(
         atomicOr(&sm.mask[pos], 1u << tok);
     }
 
-    // ---- per-wave row state
+    // ---- per-wave row state: wave w owns rows r0 + 8 i + w (i < 2)
     bf16x8_t qf[kPRowsW][4];
     f32x4_t o[kPRowsW][8];
-    float mrun[kPRowsW], lrun[kPRowsW];
+    float mref[kPRowsW], lsum[kPRowsW];       // per lane: reference max of head lc, partial row sum
     int64_t qpos[kPRowsW];
 #pragma unroll
     for (int i = 0; i < kPRowsW; ++i) {
-        const int row = r0 + kPRowsW * w + i;
+        const int row = r0 + kPWaves * i + w;
         const int rr = row < rows ? row : rows - 1;
         qpos[i] = q_start + row;
         const bf16_t* qrow = q + (static_cast<size_t>(rr) * hq + static_cast<size_t>(g) * kGroup + lc) * kHeadDim;
@@ -147,43 +162,37 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_mfma(
         for (int ks = 0; ks < 4; ++ks) qf[i][ks] = as_bf16x8(ldg16(qrow + 32 * ks + 8 * lg));
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) o[i][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        mrun[i] = -INFINITY;
-        lrun[i] = 0.f;
+        mref[i] = -INFINITY;
+        lsum[i] = 0.f;
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // only the tile loads stay in flight below
 
-    // ---- stream the union: registers -> LDS, double buffered
-    uint4 kreg[4], vreg[4];
-    auto fetch = [&](int u) {
+    // ---- stream the union through LDS with direct global->LDS loads.
+    // Each wave issues 2 K and 2 V^T instructions per block (1 KB of LDS each).
+    auto issue = [&](StageTiles& kt, StageTiles& vtt, int u) {
+        const int slot = u % kGroup2;
         const int32_t blk = sm.list[u];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = t + 256 * i;
-            const int row = e >> 4, c = e & 15;                // K: 64 rows x 16 chunks
-            const int64_t key = static_cast<int64_t>(blk) * kPB + row;
-            kreg[i] = key < nlim ? ldg16(kh + key * kHeadDim + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
-            const int d = e >> 3, p0 = (e & 7) * 8;            // V^T: 128 rows x 8 chunks
-            vreg[i] = ldg16(vth + (static_cast<int64_t>(blk) * kHeadDim + d) * kPB + p0);
+        for (int j = 0; j < 2; ++j) {
+            const int sg = 2 * w + j;
+            {   // K: bytes [1 KB sg, +1 KB) of the tile = keys 4 sg .. 4 sg + 3
+                const int key = 4 * sg + (l >> 4), phys = l & 15;
+                int64_t gk = static_cast<int64_t>(blk) * kPB + key;
+                gk = gk < nlim ? gk : nlim - 1;             // keys past the chunk are masked anyway
+                const bf16_t* src = kh + gk * kHeadDim + 8 * (phys ^ (key & 15));
+                __builtin_amdgcn_global_load_lds(src, &kt[slot][sg * 512], 16, 0, 0);
+            }
+            {   // V^T: bytes [1 KB sg, +1 KB) of the tile = d rows 8 sg .. 8 sg + 7
+                const int d = 8 * sg + (l >> 3), phys = l & 7;
+                const bf16_t* src = vth + (static_cast<int64_t>(blk) * kHeadDim + d) * kPB + 8 * (phys ^ ((d >> 1) & 7));
+                __builtin_amdgcn_global_load_lds(src, &vtt[slot][sg * 512], 16, 0, 0);
+            }
         }
     };
-    auto stash = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = t + 256 * i;
-            *reinterpret_cast<uint4*>(&sm.k[buf][e >> 4][8 * (e & 15)]) = kreg[i];
-            *reinterpret_cast<uint4*>(&sm.vt[buf][e >> 3][8 * (e & 7)]) = vreg[i];
-        }
-    };
-    __syncthreads();
-    if (n_u > 0) {
-        fetch(0);
-        stash(0);
-    }
-    __syncthreads();
-    for (int u = 0; u < n_u; ++u) {
-        const int buf = u & 1;
-        if (u + 1 < n_u) fetch(u + 1);
+    auto compute = [&](const StageTiles& kt, const StageTiles& vtt, int u) {
+        const int slot = u % kGroup2;
         const int32_t blk = sm.list[u];
-        const uint32_t act_all = (sm.mask[u] >> (kPRowsW * w)) & 0xFu;
+        const uint32_t msk = sm.mask[u];
         uint32_t act = 0;
         int cntr[kPRowsW];
 #pragma unroll
@@ -191,86 +200,113 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_mfma(
             int64_t c = qpos[i] + 1 - static_cast<int64_t>(blk) * kPB;
             c = c < kPB ? c : kPB;
             cntr[i] = static_cast<int>(c);
-            if (((act_all >> i) & 1u) && c > 0) act |= 1u << i;
+            if (((msk >> (kPWaves * i + w)) & 1u) && c > 0) act |= 1u << i;
         }
-        if (act) {
-            bf16x8_t pf[kPRowsW][2];
+        act = __builtin_amdgcn_readfirstlane(act);          // wave-uniform by construction
+        if (!act) return;
+        bf16x8_t pf[kPRowsW][2];
 #pragma unroll
-            for (int i = 0; i < kPRowsW; ++i) {
-                if (!((act >> i) & 1u)) continue;
-                // S^T for row i: lane holds S[head lc][key 16 mt + 4 lg + r]
-                f32x4_t s[4];
+        for (int i = 0; i < kPRowsW; ++i) {
+            if (!((act >> i) & 1u)) continue;
+            // S^T for row i: lane holds S[head lc][key 16 mt + 4 lg + r]
+            f32x4_t s[4];
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    f32x4_t a = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int mt = 0; mt < 4; ++mt) s[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks)
-                        a = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(&sm.k[buf][16 * mt + lc][32 * ks + 8 * lg])),
-                                   qf[i][ks], a);
-                    s[mt] = a;
-                }
-                float mx = -INFINITY;
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+                    s[mt] = mfma32(as_bf16x8(k_frag(kt, slot, 16 * mt + lc, 4 * ks + lg)), qf[i][ks], s[mt]);
+            float lm = -INFINITY;
+            if (__builtin_amdgcn_readfirstlane(cntr[i]) >= kPB) {
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        s[mt][r] *= scale_log2;
+                        lm = fmaxf(lm, s[mt][r]);
+                    }
+            } else {
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const float x = (16 * mt + 4 * lg + r) < cntr[i] ? s[mt][r] * scale_log2 : -INFINITY;
                         s[mt][r] = x;
-                        mx = fmaxf(mx, x);
+                        lm = fmaxf(lm, x);
                     }
-                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            }
+            // raise the reference only when some head of the row overshoots it
+            if (__any(lm > mref[i] + kRescaleSlack)) {
+                float mx = fmaxf(lm, __shfl_xor(lm, 16, 64));
                 mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-                const float mnew = fmaxf(mrun[i], mx);
-                const float alpha = (mrun[i] == -INFINITY) ? 0.f : exp2f(mrun[i] - mnew);
-                float ls = 0.f;
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float p = (s[mt][r] == -INFINITY) ? 0.f : exp2f(s[mt][r] - mnew);
-                        s[mt][r] = p;
-                        ls += p;
-                    }
-                ls += __shfl_xor(ls, 16, 64);
-                ls += __shfl_xor(ls, 32, 64);
-                lrun[i] = lrun[i] * alpha + ls;
-                mrun[i] = mnew;
+                const float mnew = fmaxf(mref[i], mx);
+                const float alpha = (mref[i] == -INFINITY) ? 0.f : fast_exp2(mref[i] - mnew);
+                lsum[i] *= alpha;
 #pragma unroll
                 for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) o[i][mt][r] *= alpha;
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    uint4 pu;
-                    pu.x = pack_rne(s[2 * kk][0], s[2 * kk][1]);
-                    pu.y = pack_rne(s[2 * kk][2], s[2 * kk][3]);
-                    pu.z = pack_rne(s[2 * kk + 1][0], s[2 * kk + 1][1]);
-                    pu.w = pack_rne(s[2 * kk + 1][2], s[2 * kk + 1][3]);
-                    pf[i][kk] = as_bf16x8(pu);
-                }
+                mref[i] = mnew;
             }
+            float ls = 0.f;
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-                const bf16x8_t v0 = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.vt[buf][16 * mt + lc][8 * lg]));
-                const bf16x8_t v1 = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.vt[buf][16 * mt + lc][32 + 8 * lg]));
+            for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int i = 0; i < kPRowsW; ++i) {
-                    if (!((act >> i) & 1u)) continue;
-                    o[i][mt] = mfma32(v0, pf[i][0], o[i][mt]);
-                    o[i][mt] = mfma32(v1, pf[i][1], o[i][mt]);
+                for (int r = 0; r < 4; ++r) {
+                    const float p = fast_exp2(s[mt][r] - mref[i]);   // masked keys: 2^-inf = 0
+                    s[mt][r] = p;
+                    ls += p;
                 }
+            lsum[i] += ls;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                uint4 pu;
+                pu.x = pack_rne(s[2 * kk][0], s[2 * kk][1]);
+                pu.y = pack_rne(s[2 * kk][2], s[2 * kk][3]);
+                pu.z = pack_rne(s[2 * kk + 1][0], s[2 * kk + 1][1]);
+                pu.w = pack_rne(s[2 * kk + 1][2], s[2 * kk + 1][3]);
+                pf[i][kk] = as_bf16x8(pu);
             }
         }
-        if (u + 1 < n_u) stash(buf ^ 1);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            const bf16x8_t v0 = as_bf16x8(vt_frag(vtt, slot, 16 * mt + lc, lg));
+            const bf16x8_t v1 = as_bf16x8(vt_frag(vtt, slot, 16 * mt + lc, 4 + lg));
+#pragma unroll
+            for (int i = 0; i < kPRowsW; ++i) {
+                if (!((act >> i) & 1u)) continue;
+                o[i][mt] = mfma32(v0, pf[i][0], o[i][mt]);
+                o[i][mt] = mfma32(v1, pf[i][1], o[i][mt]);
+            }
+        }
+    };
+    // one group of kGroup2 blocks per stage: wait for this stage (every wave's
+    // loads, then the barrier), start the next group into the other stage, then
+    // compute this one while those loads are in flight.  The loads are waited
+    // for with vmcnt(0) only: they are not relied on to retire in issue order.
+    auto run_group = [&](StageTiles& kc, StageTiles& vc, StageTiles& kn, StageTiles& vn, int u0) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        for (int x = u0 + kGroup2; x < u0 + 2 * kGroup2 && x < n_u; ++x) issue(kn, vn, x);
+        for (int u = u0; u < u0 + kGroup2 && u < n_u; ++u) compute(kc, vc, u);
+    };
+    __syncthreads();
+    for (int x = 0; x < kGroup2 && x < n_u; ++x) issue(k_a, v_a, x);
+    for (int u0 = 0; u0 < n_u; u0 += 2 * kGroup2) {
+        run_group(k_a, v_a, k_b, v_b, u0);
+        if (u0 + kGroup2 < n_u) run_group(k_b, v_b, k_a, v_a, u0 + kGroup2);
     }
 
-    // ---- epilogue: lane holds O[head lc][d = 16 mt + 4 lg + r]
+    // ---- epilogue: row sum over the four lanes of each head; lane holds
+    // O[head lc][d = 16 mt + 4 lg + r]
 #pragma unroll
     for (int i = 0; i < kPRowsW; ++i) {
-        const int row = r0 + kPRowsW * w + i;
+        float lt = lsum[i] + __shfl_xor(lsum[i], 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
+        const int row = r0 + kPWaves * i + w;
         if (row >= rows) continue;
-        const float inv = lrun[i] > 0.f ? 1.f / lrun[i] : 0.f;
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
         bf16_t* dst = out + (static_cast<size_t>(row) * hq + static_cast<size_t>(g) * kGroup + lc) * kHeadDim + 4 * lg;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
@@ -302,9 +338,8 @@ hipError_t launch_attn_prefill_mfma(const Shape& sh, const void* q, int rows, in
         static_cast<const bf16_t*>(v), kv_off, sh.hkv, n, nblk, vt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t smem = sizeof(PreSmem);
     const float scale_log2 = sh.attn_scale * 1.4426950408889634f;
-    attn_prefill_mfma<<<dim3((rows + kPRows - 1) / kPRows, sh.hkv), 256, smem, st>>>(
+    attn_prefill_mfma<<<dim3((rows + kPRows - 1) / kPRows, sh.hkv), kPThreads, 0, st>>>(
         static_cast<const bf16_t*>(q), rows, q_start, static_cast<const bf16_t*>(k), vt, kv_off,
         idx, static_cast<bf16_t*>(out), sh.hq, sh.hkv, sh.topk, nblk, scale_log2);
     return hipGetLastError();

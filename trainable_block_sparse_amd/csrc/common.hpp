@@ -130,3 +130,27 @@ __device__ __forceinline__ uint32_t pack_rne(float lo, float hi) {
 }
 
 }  // namespace infv2
+
+namespace infv2 {
+
+// inclusive prefix sum over the threads of a block of kWaves waves; `tmp` holds kWaves words
+template <int kWaves>
+__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* tmp) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        uint32_t u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
+    }
+    if (lane == 63) tmp[wid] = v;
+    __syncthreads();
+    uint32_t add = 0;
+    for (int w = 0; w < wid; ++w) add += tmp[w];
+    __syncthreads();
+    return v + add;
+}
+
+// 2^x on the transcendental unit (no denormal range handling: exp2(-inf) = 0)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace infv2
