@@ -19,8 +19,9 @@
 // fence inside a kernel costs a write-back and invalidation of the whole L2 of
 // the XCD on gfx950, once per block.
 // Prefill (rows of one sequence, causal visibility per row):
-//   sel_pre_lse     4 rows per block: online (max, sum-exp) over visible kernels.
-//   sel_pre_scores  4 rows per block: logits again, group score, block max.
+//   sel_pre_mfma<1> 16 rows per block on the matrix cores: per-head LogSumExp.
+//   sel_pre_mfma<2> the same logits again: group score, block max.
+//   (sel_pre_lse / sel_pre_scores: the vector-ALU versions for fp32 queries)
 //   sel_pre_topk    one block per (row, KV head).
 #include "common.hpp"
 #include "kernels.hpp"
@@ -496,6 +497,205 @@ __global__ __launch_bounds__(256) void sel_pre_scores(
     }
 }
 
+// ------------------------------------------------------------------ prefill passes on the matrix cores
+// Thread block = 16 query rows of one KV head (wave w: rows w, w+4, w+8, w+12),
+// streaming the compressed keys in tiles of 64 kernels through LDS (bf16; fp32
+// keys split into hi + lo tiles at staging).  Z[head][kernel] = Q . CK^T with Q
+// as the A operand (lane: head lc, 8 consecutive d) and the CK tile as B, so
+// each lane holds 4 heads (4 lg + r) of one kernel column (lc) per 16x16 tile.
+//   pass 1: per-lane online (max, sum) of 2^(log2e z) per head, folded over
+//           the 16 kernel columns at the end -> LSE[row][head]
+//   pass 2: R = mean_h 2^(log2e z - LSE2_h): 4 heads in-lane + two cross-lane
+//           adds; block max of R over the tile, atomicMax into the row's keys
+constexpr int kPreRowsG = 16;
+constexpr int kPreTileK = 64;
+
+template <int kPass, bool kCkBf16>
+__global__ __launch_bounds__(256) void sel_pre_mfma(
+    const bf16_t* __restrict__ q, int rows, int64_t q_start, const void* __restrict__ ck,
+    const int64_t* __restrict__ ck_off, int hq, int hkv, int m, int p, int s, float score_scale,
+    int64_t nblk_max, float* __restrict__ lse, uint32_t* __restrict__ keys) {
+    __shared__ __attribute__((aligned(16))) bf16_t ck_hi[kPreTileK * kHeadDim];
+    __shared__ __attribute__((aligned(16))) bf16_t ck_lo[kCkBf16 ? 8 : kPreTileK * kHeadDim];
+    __shared__ float rs[kPreRowsG][kPreTileK];
+    const int g = blockIdx.y, t = threadIdx.x;
+    const int w = t >> 6, l = t & 63, lg = l >> 4, lc = l & 15;
+    const int r0 = blockIdx.x * kPreRowsG;
+    const int64_t ccap = ck_off[1] - ck_off[0];
+    const int64_t cbase = (ck_off[0] * hkv + static_cast<int64_t>(g) * ccap) * kHeadDim;
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float zscale = score_scale * kLog2e;
+
+    int64_t vis[4];
+    bf16x8_t qf[4][4];
+    int64_t vmax = 0;
+    for (int rr = 0; rr < kPreRowsG; ++rr) {
+        const int row = r0 + rr;
+        int64_t v = row < rows ? num_kernels(q_start + row + 1, p, s) : 0;
+        v = v < ccap ? v : ccap;
+        vmax = v > vmax ? v : vmax;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = r0 + w + 4 * i;
+        int64_t v = row < rows ? num_kernels(q_start + row + 1, p, s) : 0;
+        vis[i] = v < ccap ? v : ccap;
+        const int rr = row < rows ? row : rows - 1;
+        const bf16_t* qrow = q + (static_cast<size_t>(rr) * hq + static_cast<size_t>(g) * kGroup + lc) * kHeadDim;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qf[i][ks] = as_bf16x8(ldg16(qrow + 32 * ks + 8 * lg));
+    }
+    if (kPass == 1) {
+        // pass 1 owns clearing the block-score keys of its rows
+        for (int rr = 0; rr < kPreRowsG; ++rr) {
+            const int row = r0 + rr;
+            if (row >= rows) break;
+            uint32_t* kb = keys + (static_cast<size_t>(row) * hkv + g) * nblk_max;
+            for (int64_t jb = t; jb < nblk_max; jb += 256) kb[jb] = 0u;
+        }
+    }
+    // pass 1 state: running (max, sum) for heads 4 lg + r; pass 2: LSE2 of those heads
+    float mr[4][4], lr[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { mr[i][r] = -INFINITY; lr[i][r] = 0.f; }
+    if (kPass == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = r0 + w + 4 * i;
+            const int rr = row < rows ? row : rows - 1;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                mr[i][r] = lse[static_cast<size_t>(rr) * hq + g * kGroup + 4 * lg + r] * kLog2e;
+        }
+    }
+
+    for (int64_t j0 = 0; j0 < vmax; j0 += kPreTileK) {
+        __syncthreads();
+        // stage 64 kernels; chunk c of kernel r at c ^ (r & 15)
+        if (kCkBf16) {
+            const bf16_t* src = static_cast<const bf16_t*>(ck) + cbase;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int e = t + 256 * x, r = e >> 4, c = e & 15;
+                uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                if (j0 + r < vmax) v = ldg16(src + (j0 + r) * kHeadDim + 8 * c);
+                *reinterpret_cast<uint4*>(&ck_hi[r * kHeadDim + 8 * (c ^ (r & 15))]) = v;
+            }
+        } else {
+            const float* src = static_cast<const float*>(ck) + cbase;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int e = t + 256 * x, r = e >> 4, c = e & 15;
+                float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+                if (j0 + r < vmax) {
+                    a = *reinterpret_cast<const float4*>(src + (j0 + r) * kHeadDim + 8 * c);
+                    b = *reinterpret_cast<const float4*>(src + (j0 + r) * kHeadDim + 8 * c + 4);
+                }
+                const float xv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                float hi[8], lo[8];
+#pragma unroll
+                for (int e8 = 0; e8 < 8; ++e8) {
+                    hi[e8] = bf16_to_f32(f32_to_bf16(xv[e8]));
+                    lo[e8] = xv[e8] - hi[e8];
+                }
+                const int off = r * kHeadDim + 8 * (c ^ (r & 15));
+                *reinterpret_cast<uint4*>(&ck_hi[off]) =
+                    make_uint4(pack_exact(hi[0], hi[1]), pack_exact(hi[2], hi[3]), pack_exact(hi[4], hi[5]), pack_exact(hi[6], hi[7]));
+                *reinterpret_cast<uint4*>(&ck_lo[off]) =
+                    make_uint4(pack_rne(lo[0], lo[1]), pack_rne(lo[2], lo[3]), pack_rne(lo[4], lo[5]), pack_rne(lo[6], lo[7]));
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            f32x4_t z[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) z[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            const int kr = 16 * nt + lc;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int off = kr * kHeadDim + 8 * ((4 * ks + lg) ^ (kr & 15));
+                const bf16x8_t bh = as_bf16x8(*reinterpret_cast<const uint4*>(&ck_hi[off]));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) z[i] = mfma32(qf[i][ks], bh, z[i]);
+                if (!kCkBf16) {
+                    const bf16x8_t bl = as_bf16x8(*reinterpret_cast<const uint4*>(&ck_lo[off]));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) z[i] = mfma32(qf[i][ks], bl, z[i]);
+                }
+            }
+            const int64_t jk = j0 + kr;          // this lane's kernel column
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = jk < vis[i];
+                if (kPass == 1) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (!ok) continue;
+                        const float x = z[i][r] * zscale;
+                        if (x > mr[i][r]) {
+                            lr[i][r] = lr[i][r] * fast_exp2(mr[i][r] - x) + 1.f;
+                            mr[i][r] = x;
+                        } else {
+                            lr[i][r] += fast_exp2(x - mr[i][r]);
+                        }
+                    }
+                } else {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc += fast_exp2(z[i][r] * zscale - mr[i][r]);
+                    acc += __shfl_xor(acc, 16, 64);
+                    acc += __shfl_xor(acc, 32, 64);
+                    if (lg == 0) rs[w + 4 * i][kr] = ok ? acc * (1.0f / kGroup) : -INFINITY;
+                }
+            }
+        }
+        if (kPass == 2) {
+            __syncthreads();
+            // block max over this tile's kernels, one (row, block) per thread
+            const int64_t jhi_t = (j0 + kPreTileK < vmax ? j0 + kPreTileK : vmax) - 1;
+            const int64_t blo = (j0 * s) / m, bhi = (jhi_t * s + p - 1) / m;
+            const int nbt = static_cast<int>(bhi - blo + 1);
+            for (int e = t; e < kPreRowsG * nbt; e += 256) {
+                const int rr = e / nbt, row = r0 + rr;
+                if (row >= rows) continue;
+                const int64_t blk = blo + e % nbt;
+                int64_t v = num_kernels(q_start + row + 1, p, s);
+                v = v < ccap ? v : ccap;
+                int64_t k0 = first_kernel_of_block(blk, m, p, s), k1 = last_kernel_of_block(blk, m, s);
+                k0 = k0 > j0 ? k0 : j0;
+                const int64_t jhi = (jhi_t < v - 1) ? jhi_t : v - 1;
+                k1 = k1 < jhi ? k1 : jhi;
+                if (k0 > k1) continue;
+                float mx = rs[rr][k0 - j0];
+                for (int64_t kk = k0 + 1; kk <= k1; ++kk) mx = fmaxf(mx, rs[rr][kk - j0]);
+                atomicMax(&keys[(static_cast<size_t>(row) * hkv + g) * nblk_max + blk], score_to_key(mx));
+            }
+        }
+    }
+    if (kPass == 1) {
+        // fold the 16 kernel columns: lanes with equal lg hold the same heads
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = r0 + w + 4 * i;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float mx = mr[i][r];
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+                float sm = (mr[i][r] == -INFINITY) ? 0.f : lr[i][r] * fast_exp2(mr[i][r] - mx);
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) sm += __shfl_xor(sm, o, 64);
+                if (lc == 0 && row < rows)
+                    lse[static_cast<size_t>(row) * hq + g * kGroup + 4 * lg + r] =
+                        (mx == -INFINITY) ? -INFINITY : (mx + __log2f(sm)) * 0.6931471805599453f;
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------ prefill, top-k
 __global__ __launch_bounds__(256) void sel_pre_topk(int64_t q_start, int hkv, int m, int topk,
                                                     int init, int local, int64_t nblk_max,
@@ -561,6 +761,18 @@ static void pre_launch(const Shape& sh, const void* q, int rows, int64_t q_start
     dim3 g1((rows + kRowsPre - 1) / kRowsPre, sh.hkv);
     float* lse = reinterpret_cast<float*>(ws + w.lse);
     uint32_t* keys = reinterpret_cast<uint32_t*>(ws + w.keys);
+    if (sizeof(Tq) == 2) {
+        constexpr bool kB = sizeof(Tck) == 2;
+        dim3 gm((rows + kPreRowsG - 1) / kPreRowsG, sh.hkv);
+        const bf16_t* qq = static_cast<const bf16_t*>(q);
+        sel_pre_mfma<1, kB><<<gm, 256, 0, st>>>(qq, rows, q_start, ck, ck_off, sh.hq, sh.hkv, sh.m,
+                                                sh.p, sh.s, sh.score_scale, w.nblk_max, lse, keys);
+        sel_pre_mfma<2, kB><<<gm, 256, 0, st>>>(qq, rows, q_start, ck, ck_off, sh.hq, sh.hkv, sh.m,
+                                                sh.p, sh.s, sh.score_scale, w.nblk_max, lse, keys);
+        sel_pre_topk<<<dim3(rows, sh.hkv), 256, w.nblk_max * sizeof(uint32_t), st>>>(
+            q_start, sh.hkv, sh.m, sh.topk, sh.init, sh.local, w.nblk_max, keys, idx, score);
+        return;
+    }
     sel_pre_lse<Tq, Tck><<<g1, 256, 0, st>>>(static_cast<const Tq*>(q), rows, q_start,
                                             static_cast<const Tck*>(ck), ck_off, sh.hq, sh.hkv,
                                             sh.p, sh.s, sh.score_scale, w.nblk_max, lse, keys);
