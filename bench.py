@@ -66,9 +66,54 @@ class Timer:
         return e
 
 
+def kernel_times(tbs, torch, run, steps: int, families) -> dict:
+    """Live per-kernel times: the library brackets every launch of one kernel
+    family with HIP events on its launch stream while a session is open; one
+    eager pass of `steps` steps per family."""
+    out = {}
+    for fam in families:
+        torch.cuda.synchronize()
+        tbs.infv2_timing_start(fam)
+        try:
+            for t in range(steps):
+                run(t)
+        finally:
+            ms, n = tbs.infv2_timing_stop()
+        out[fam] = {"launches_per_step": n / steps,
+                    "us_per_launch": ms * 1e3 / n if n else None,
+                    "us_per_step": ms * 1e3 / steps}
+    return out
+
+
+def roofline_of(times: dict, work: dict, bound: str, peak: float, unit: str, scale: float) -> dict:
+    """Roofline line of the dominant kernel: the largest time per step among the
+    kernels that carry the step's algorithmic traffic or FLOPs (the others only
+    pass intermediates between kernels and are reported in "kernels")."""
+    cand = [f for f in work if times.get(f, {}).get("us_per_launch")]
+    dom = max(cand, key=lambda f: times[f]["us_per_step"])
+    us = times[dom]["us_per_launch"]
+    achieved = work[dom] / (us * 1e-6) / scale
+    return {"bound": bound, "kernel": dom, "achieved": achieved, "peak": peak, "unit": unit,
+            "frac": achieved / peak, "traffic": None, "us_per_launch": us,
+            "work_per_launch": work[dom]}
+
+
 # ----------------------------------------------------------------------------- decode
+DECODE_FAMILIES = ("compress", "select_logits", "select_scores", "select_topk", "attn_decode",
+                   "attn_merge")
+
+
 def decode_bytes(wl, ck_bytes: int, n_list) -> dict:
-    """Algorithmic HBM bytes of one decode step (per call of each entry point)."""
+    """Algorithmic HBM bytes of one decode step, per call of each entry point."""
+    kb = decode_kernel_bytes(wl, ck_bytes, n_list)
+    return {"compress": kb["compress"], "select": kb["select_logits"] + kb["select_topk"],
+            "attn": kb["attn_decode"] + kb["attn_merge"]}
+
+
+def decode_kernel_bytes(wl, ck_bytes: int, n_list) -> dict:
+    """Algorithmic HBM bytes per launch of each decode kernel: what the step must
+    move, attributed to the kernel that moves it (intermediates between kernels
+    are not counted)."""
     d, hq, hkv, m, k = wl.head_dim, wl.num_q_heads, wl.num_kv_heads, wl.block_size, wl.topk
     esz = 2 if wl.io_dtype == "bf16" else 4
     q_b = hq * d * esz
@@ -76,9 +121,11 @@ def decode_bytes(wl, ck_bytes: int, n_list) -> dict:
     ck = sum(hkv * num_kernels(n, wl.kernel_size, wl.kernel_stride) * d * ck_bytes for n in n_list)
     B = len(n_list)
     return {
-        "compress": B * hkv * (wl.kernel_size * d * esz + d * ck_bytes),
-        "select": ck + B * (q_b + hkv * k * 4),
-        "attn": sel_kv + B * (2 * q_b + hkv * k * 4),
+        "compress": B * hkv * (wl.kernel_size * d * esz + d * ck_bytes),   # p keys in, one CK out
+        "select_logits": ck + B * q_b,                                    # every visible CK, q
+        "select_topk": B * hkv * k * 4,                                   # block ids out
+        "attn_decode": sel_kv + B * (q_b + hkv * k * 4),                  # selected K/V, q, ids
+        "attn_merge": B * q_b,                                            # output rows
     }
 
 
@@ -134,6 +181,7 @@ def bench_decode(cfg_index: int, args, torch, tbs, gh, replicas: int) -> dict:
     torch.cuda.synchronize()
     per = np.array([[a.elapsed_time(b) for a, b in zip(x[:-1], x[1:])] for x in ev]) * 1e3  # us
     per_us = dict(zip(["compress", "select", "attn"], per.mean(axis=0).tolist()))
+    kt = kernel_times(tbs, torch, lambda t: step(t % R), args.steps, DECODE_FAMILIES)
     # whole steps, eager
     torch.cuda.synchronize()
     s0 = T.event()
@@ -167,13 +215,22 @@ def bench_decode(cfg_index: int, args, torch, tbs, gh, replicas: int) -> dict:
     ms = graph_ms if graph_ms is not None else eager_ms
     ckb = 2 if ck_dtype == "bf16" else 4
     nb = decode_bytes(wl, ckb, [int(n) for n in wl.lens])
+    kb = decode_kernel_bytes(wl, ckb, [int(n) for n in wl.lens])
     step_bytes = sum(nb.values())
+    for f, v in kt.items():
+        if f in kb and v["us_per_launch"]:
+            v["bytes_per_launch"] = kb[f]
+            v["gbps"] = kb[f] / (v["us_per_launch"] * 1e-6) / 1e9
     res = {
         "workload": wl.name, "batch": B, "lens_min": int(wl.lens.min()), "lens_max": n_max,
         "ms_per_step": ms, "ms_per_step_eager": eager_ms, "ms_per_step_graph": graph_ms,
-        "tok_per_s": B / (ms * 1e-3), "per_call_us": per_us, "bytes_per_step": step_bytes,
+        "tok_per_s": B / (ms * 1e-3), "per_call_us": per_us, "kernels": kt,
+        "bytes_per_step": step_bytes,
         "bytes_per_call": nb, "hbm_gbps_step": step_bytes / (ms * 1e-3) / 1e9,
         "replicas": R,
+        "roofline": roofline_of(kt, {"select_logits": kb["select_logits"],
+                                     "attn_decode": kb["attn_decode"]},
+                                "hbm", HBM_PEAK_GBS, "GB/s", 1e9),
     }
     # spot parity of the timed path: replica 0, oracle selection on the same query
     res["parity"] = decode_spot_parity(wl, dev, qs, outs, idx, select, attn, ck_dtype, torch, gh)
@@ -212,6 +269,9 @@ def decode_spot_parity(wl, dev, qs, outs, idx, select, attn, ck_dtype, torch, gh
 
 
 # ----------------------------------------------------------------------------- prefill
+PREFILL_FAMILIES = ("compress", "select_prefill", "select_topk", "vt_build", "attn_prefill")
+
+
 def bench_prefill(args, torch, tbs, gh) -> dict:
     from synth import make_config
     wl = make_config(3)
@@ -276,9 +336,13 @@ def bench_prefill(args, torch, tbs, gh) -> dict:
         "last_chunk_useful_flops": float(4 * d * (hq // hkv) * tok[L - C:].sum()),
         "mean_attended_tokens": float(tok.mean()),
     }
-    res["roofline"] = {"bound": "mfma", "kernel": "attn_prefill_mfma",
-                       "achieved": res["tflops_attn"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                       "frac": res["tflops_attn"] / BF16_PEAK_TFLOPS, "traffic": None}
+    reps_k = max(1, args.prefill_reps)
+    kt = kernel_times(tbs, torch, lambda t: run(False), reps_k, PREFILL_FAMILIES)
+    res["kernels"] = kt
+    n_attn = kt["attn_prefill"]["launches_per_step"]
+    res["tflops_attn_kernel"] = useful / (kt["attn_prefill"]["us_per_step"] * 1e-6) / 1e12
+    res["roofline"] = roofline_of(kt, {"attn_prefill": useful / n_attn}, "mfma", BF16_PEAK_TFLOPS,
+                                  "TFLOP/s", 1e12)
     res["_idx"] = gi
     res["_wl"] = wl
     return res
@@ -410,13 +474,7 @@ def main() -> int:
     if bat:
         log(f"batched decode: {bat['ms_per_step'] * 1e3:.1f} us/step, per call {bat['per_call_us']}")
 
-    # dominant kernel of the main step: the decode attention kernel (one kernel per call)
-    att_us = main_res["per_call_us"]["attn"]
-    att_bytes = main_res["bytes_per_call"]["attn"]
-    roof = {"bound": "hbm", "kernel": "attn_decode_kernel", "achieved": att_bytes / (att_us * 1e-6) / 1e9,
-            "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-
+    roof = main_res["roofline"]
     out = {
         "metric": METRIC,
         "value": main_res["tok_per_s"],

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define INFV2_ABI_VERSION 1
+#define INFV2_ABI_VERSION 2
 
 typedef enum infv2_status {
     INFV2_OK = 0,
@@ -223,6 +223,39 @@ const char* infv2_status_str(int32_t status);
 
 /* INFV2_ABI_VERSION of the loaded library. */
 int32_t infv2_abi_version(void);
+
+/*
+ * Kernel timing, for benchmarks and profiling only (not part of the method).
+ * While a timing session is open, every launch of the chosen kernel family is
+ * bracketed by a pair of HIP events recorded on the stream it is launched on,
+ * so one kernel can be timed on its own although an entry point launches
+ * several.  Launches on a stream that is being captured into a graph are not
+ * bracketed.  This is the only global state of the library: one session at a
+ * time per process, guarded by a mutex.
+ *
+ * infv2_timing_start  opens a session for `kernel` (an infv2_kernel id);
+ *                     INFV2_ERR_SHAPE for an unknown id or a session already
+ *                     open.
+ * infv2_timing_stop   closes it, waits for the recorded events and returns
+ *                     the summed duration in milliseconds and the number of
+ *                     bracketed launches; INFV2_ERR_SHAPE if no session is
+ *                     open, INFV2_ERR_DEVICE if an event failed.
+ */
+typedef enum infv2_kernel {
+    INFV2_KERNEL_COMPRESS = 0,          /* compressed keys */
+    INFV2_KERNEL_SELECT_LOGITS = 1,     /* decode: kernel logits + per-chunk (max, sum exp) */
+    INFV2_KERNEL_SELECT_SCORES = 2,     /* decode: LSE, group scores, block max */
+    INFV2_KERNEL_SELECT_PREFILL = 3,    /* prefill: the two scoring passes */
+    INFV2_KERNEL_SELECT_TOPK = 4,       /* top-k kernels that read keys from memory */
+    INFV2_KERNEL_ATTN_DECODE = 5,       /* decode: attention over the selected blocks (partials) */
+    INFV2_KERNEL_ATTN_MERGE = 6,        /* decode: merge of the partials */
+    INFV2_KERNEL_ATTN_PREFILL = 7,      /* prefill: attention over the selected blocks */
+    INFV2_KERNEL_VT_BUILD = 8,          /* prefill: transposed V tiles */
+    INFV2_KERNEL_COUNT = 9
+} infv2_kernel;
+
+int32_t infv2_timing_start(int32_t kernel);
+int32_t infv2_timing_stop(double* total_ms, int32_t* launches);
 
 #ifdef __cplusplus
 }

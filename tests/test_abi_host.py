@@ -135,3 +135,17 @@ def test_select_and_attention_validation(lib):
                                          None) == ESHAPE
     assert lib.infv2_sparse_attn_prefill(c, FAKE, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
                                          None) == OK
+
+
+def test_timing_session_state_machine(lib):
+    # no GPU work: only the session bookkeeping, which never touches a device
+    with pytest.raises(tbs.Infv2Error):
+        tbs.infv2_timing_stop()                        # nothing open
+    with pytest.raises(tbs.Infv2Error):
+        tbs.infv2_timing_start(len(tbs.KERNELS))       # unknown family
+    tbs.infv2_timing_start("attn_decode")
+    with pytest.raises(tbs.Infv2Error):
+        tbs.infv2_timing_start("compress")             # one session at a time
+    assert tbs.infv2_timing_stop() == (0.0, 0)
+    hdr = open(HEADER).read()
+    assert int(re.search(r"INFV2_KERNEL_COUNT = (\d+)", hdr).group(1)) == len(tbs.KERNELS)

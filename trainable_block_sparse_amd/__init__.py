@@ -21,6 +21,10 @@ LIB_PATH = os.path.join(_HERE, "libinfv2.so")
 INFV2_FP32, INFV2_BF16 = 0, 1
 INFV2_MODE_DECODE, INFV2_MODE_PREFILL = 0, 1
 OP_COMPRESS, OP_SELECT_DECODE, OP_SELECT_PREFILL, OP_ATTN_DECODE, OP_ATTN_PREFILL = range(5)
+# kernel families for infv2_timing_start (infv2_kernel in infv2.h)
+KERNELS = ("compress", "select_logits", "select_scores", "select_prefill", "select_topk",
+           "attn_decode", "attn_merge", "attn_prefill", "vt_build")
+KERNEL_ID = {name: i for i, name in enumerate(KERNELS)}
 STATUS = {0: "INFV2_OK", 1: "INFV2_ERR_NULL", 2: "INFV2_ERR_SHAPE", 3: "INFV2_ERR_UNSUPPORTED",
           4: "INFV2_ERR_WORKSPACE", 5: "INFV2_ERR_DEVICE"}
 
@@ -92,6 +96,8 @@ def load_library(path: str = LIB_PATH):
         "infv2_num_kernels": (i64, [cfgp, i64]),
         "infv2_status_str": (ctypes.c_char_p, [i32]),
         "infv2_abi_version": (i32, []),
+        "infv2_timing_start": (i32, [i32]),
+        "infv2_timing_stop": (i32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -102,7 +108,7 @@ def load_library(path: str = LIB_PATH):
 
 EXPORTED = ("infv2_compress_keys", "infv2_select_blocks", "infv2_sparse_attn_decode",
             "infv2_sparse_attn_prefill", "infv2_workspace_bytes", "infv2_num_kernels",
-            "infv2_status_str", "infv2_abi_version")
+            "infv2_status_str", "infv2_abi_version", "infv2_timing_start", "infv2_timing_stop")
 
 
 # ---------------------------------------------------------------- marshalling helpers
@@ -140,6 +146,19 @@ def infv2_abi_version() -> int:
 
 def infv2_status_str(status: int) -> str:
     return load_library().infv2_status_str(status).decode()
+
+
+def infv2_timing_start(kernel) -> None:
+    """Open a timing session for one kernel family (name from KERNELS or its id)."""
+    kid = KERNEL_ID[kernel] if isinstance(kernel, str) else int(kernel)
+    _check(load_library().infv2_timing_start(kid), "infv2_timing_start")
+
+
+def infv2_timing_stop():
+    """Close the session: (summed milliseconds, number of bracketed launches)."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int32(0)
+    _check(load_library().infv2_timing_stop(ctypes.byref(ms), ctypes.byref(n)), "infv2_timing_stop")
+    return ms.value, n.value
 
 
 def infv2_num_kernels(cfg: Config, n: int) -> int:

@@ -334,11 +334,15 @@ hipError_t launch_attn_prefill_mfma(const Shape& sh, const void* q, int rows, in
     const int64_t n = q_start + rows;
     const int64_t nblk = (n + kPB - 1) / kPB;
     bf16_t* vt = static_cast<bf16_t*>(ws);
-    vt_build<<<dim3(static_cast<unsigned>(nblk), sh.hkv), 256, 0, st>>>(
-        static_cast<const bf16_t*>(v), kv_off, sh.hkv, n, nblk, vt);
+    {
+        KernelTimer kt(INFV2_KERNEL_VT_BUILD, st);
+        vt_build<<<dim3(static_cast<unsigned>(nblk), sh.hkv), 256, 0, st>>>(
+            static_cast<const bf16_t*>(v), kv_off, sh.hkv, n, nblk, vt);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const float scale_log2 = sh.attn_scale * 1.4426950408889634f;
+    KernelTimer kt(INFV2_KERNEL_ATTN_PREFILL, st);
     attn_prefill_mfma<<<dim3((rows + kPRows - 1) / kPRows, sh.hkv), kPThreads, 0, st>>>(
         static_cast<const bf16_t*>(q), rows, q_start, static_cast<const bf16_t*>(k), vt, kv_off,
         idx, static_cast<bf16_t*>(out), sh.hq, sh.hkv, sh.topk, nblk, scale_log2);

@@ -82,6 +82,7 @@ hipError_t launch_compress(const Shape& sh, const void* k, const int64_t* kv_off
                            int batch, int64_t max_new, void* ck, hipStream_t st) {
     if (max_new <= 0) return hipSuccess;
     dim3 grid(static_cast<unsigned>((max_new + kCompressKpb - 1) / kCompressKpb), sh.hkv, batch);
+    KernelTimer kt(INFV2_KERNEL_COMPRESS, st);
     if (sh.io_bf16) {
         if (sh.ck_bf16)
             compress_kernel<bf16_t, true><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(k), kv_off, kv_lens, ck_off, ck_begin, ck, sh.hkv, sh.p, sh.s);

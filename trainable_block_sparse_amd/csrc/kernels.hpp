@@ -6,10 +6,26 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/infv2.h"
+
 namespace infv2 {
 
 constexpr int kHeadDim = 128;     // d supported by the kernels
 constexpr int kGroup = 16;        // query heads per KV head supported by the kernels
+
+// Brackets one kernel launch with HIP events while a timing session for its
+// family (an infv2_kernel id) is open; does nothing otherwise (timing.cpp).
+class KernelTimer {
+  public:
+    KernelTimer(int kernel, hipStream_t st);
+    ~KernelTimer();
+    KernelTimer(const KernelTimer&) = delete;
+    KernelTimer& operator=(const KernelTimer&) = delete;
+
+  private:
+    hipStream_t st_;
+    void* stop_ = nullptr;
+};
 
 struct Shape {
     int hq, hkv, d, m, p, s, topk, init, local;

@@ -333,8 +333,8 @@ __global__ __launch_bounds__(256) void sel_dec_topk(const int64_t* __restrict__ 
     int64_t c = n > 0 ? (n - 1) / m : -1;
     c = c < nblk_max - 1 ? c : nblk_max - 1;
     const size_t bg = static_cast<size_t>(b) * hkv + g;
-    block_topk(keys + bg * nblk_max, c, topk, init, local, idx + bg * topk,
-               score ? score + bg * topk : nullptr, sm, lkeys);
+    block_topk<256>(keys + bg * nblk_max, c, topk, init, local, idx + bg * topk,
+                    score ? score + bg * topk : nullptr, sm, lkeys);
 }
 
 // ------------------------------------------------------------------ prefill, pass 1
@@ -708,8 +708,8 @@ __global__ __launch_bounds__(256) void sel_pre_topk(int64_t q_start, int hkv, in
     int64_t c = (q_start + row) / m;
     c = c < nblk_max - 1 ? c : nblk_max - 1;
     extern __shared__ uint32_t lkeys[];
-    block_topk(keys + rg * nblk_max, c, topk, init, local, idx + rg * topk,
-               score ? score + rg * topk : nullptr, sm, lkeys);
+    block_topk<256>(keys + rg * nblk_max, c, topk, init, local, idx + rg * topk,
+                    score ? score + rg * topk : nullptr, sm, lkeys);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -723,17 +723,24 @@ static void dec_launch(const Shape& sh, const void* q, const void* ck, const int
     float* logits = reinterpret_cast<float*>(ws + w.logits);
     float2* partial = reinterpret_cast<float2*>(ws + w.partial);
     uint32_t* keys = reinterpret_cast<uint32_t*>(ws + w.keys);
-    if (sizeof(Tq) == 2)
-        sel_dec_logits_mfma<sizeof(Tck) == 2><<<ga, 64, 0, st>>>(
-            static_cast<const bf16_t*>(q), ck, ck_off, kv_off, kv_lens, sh.hq, sh.hkv, sh.p, sh.s,
-            sh.score_scale, ncm, w.nc_ld, w.nchunk_a, w.nblk_max, logits, partial, keys);
-    else
-        sel_dec_logits<Tq, Tck><<<ga, 256, 0, st>>>(
-            static_cast<const Tq*>(q), static_cast<const Tck*>(ck), ck_off, kv_off, kv_lens, sh.hq,
-            sh.hkv, sh.p, sh.s, sh.score_scale, ncm, w.nc_ld, w.nchunk_a, w.nblk_max, logits,
-            partial, keys);
-    sel_dec_scores<<<gb, 256, 0, st>>>(kv_off, kv_lens, ck_off, sh.hkv, sh.m, sh.p, sh.s, ncm,
-                                       w.nc_ld, w.nchunk_a, w.nblk_max, logits, partial, keys);
+    {
+        KernelTimer kt(INFV2_KERNEL_SELECT_LOGITS, st);
+        if (sizeof(Tq) == 2)
+            sel_dec_logits_mfma<sizeof(Tck) == 2><<<ga, 64, 0, st>>>(
+                static_cast<const bf16_t*>(q), ck, ck_off, kv_off, kv_lens, sh.hq, sh.hkv, sh.p,
+                sh.s, sh.score_scale, ncm, w.nc_ld, w.nchunk_a, w.nblk_max, logits, partial, keys);
+        else
+            sel_dec_logits<Tq, Tck><<<ga, 256, 0, st>>>(
+                static_cast<const Tq*>(q), static_cast<const Tck*>(ck), ck_off, kv_off, kv_lens,
+                sh.hq, sh.hkv, sh.p, sh.s, sh.score_scale, ncm, w.nc_ld, w.nchunk_a, w.nblk_max,
+                logits, partial, keys);
+    }
+    {
+        KernelTimer kt(INFV2_KERNEL_SELECT_SCORES, st);
+        sel_dec_scores<<<gb, 256, 0, st>>>(kv_off, kv_lens, ck_off, sh.hkv, sh.m, sh.p, sh.s, ncm,
+                                           w.nc_ld, w.nchunk_a, w.nblk_max, logits, partial, keys);
+    }
+    KernelTimer kt(INFV2_KERNEL_SELECT_TOPK, st);
     sel_dec_topk<<<dim3(sh.hkv, batch), 256, w.nblk_max * sizeof(uint32_t), st>>>(
         kv_off, kv_lens, sh.hkv, sh.m, sh.topk, sh.init, sh.local, w.nblk_max, keys, idx, score);
 }
@@ -765,21 +772,37 @@ static void pre_launch(const Shape& sh, const void* q, int rows, int64_t q_start
         constexpr bool kB = sizeof(Tck) == 2;
         dim3 gm((rows + kPreRowsG - 1) / kPreRowsG, sh.hkv);
         const bf16_t* qq = static_cast<const bf16_t*>(q);
-        sel_pre_mfma<1, kB><<<gm, 256, 0, st>>>(qq, rows, q_start, ck, ck_off, sh.hq, sh.hkv, sh.m,
-                                                sh.p, sh.s, sh.score_scale, w.nblk_max, lse, keys);
-        sel_pre_mfma<2, kB><<<gm, 256, 0, st>>>(qq, rows, q_start, ck, ck_off, sh.hq, sh.hkv, sh.m,
-                                                sh.p, sh.s, sh.score_scale, w.nblk_max, lse, keys);
+        {
+            KernelTimer kt(INFV2_KERNEL_SELECT_PREFILL, st);
+            sel_pre_mfma<1, kB><<<gm, 256, 0, st>>>(qq, rows, q_start, ck, ck_off, sh.hq, sh.hkv,
+                                                    sh.m, sh.p, sh.s, sh.score_scale, w.nblk_max,
+                                                    lse, keys);
+        }
+        {
+            KernelTimer kt(INFV2_KERNEL_SELECT_PREFILL, st);
+            sel_pre_mfma<2, kB><<<gm, 256, 0, st>>>(qq, rows, q_start, ck, ck_off, sh.hq, sh.hkv,
+                                                    sh.m, sh.p, sh.s, sh.score_scale, w.nblk_max,
+                                                    lse, keys);
+        }
+        KernelTimer kt(INFV2_KERNEL_SELECT_TOPK, st);
         sel_pre_topk<<<dim3(rows, sh.hkv), 256, w.nblk_max * sizeof(uint32_t), st>>>(
             q_start, sh.hkv, sh.m, sh.topk, sh.init, sh.local, w.nblk_max, keys, idx, score);
         return;
     }
-    sel_pre_lse<Tq, Tck><<<g1, 256, 0, st>>>(static_cast<const Tq*>(q), rows, q_start,
-                                            static_cast<const Tck*>(ck), ck_off, sh.hq, sh.hkv,
-                                            sh.p, sh.s, sh.score_scale, w.nblk_max, lse, keys);
-    sel_pre_scores<Tq, Tck><<<g1, 256, 0, st>>>(static_cast<const Tq*>(q), rows, q_start,
-                                               static_cast<const Tck*>(ck), ck_off, sh.hq, sh.hkv,
-                                               sh.m, sh.p, sh.s, sh.score_scale, w.nblk_max, lse,
-                                               keys);
+    {
+        KernelTimer kt(INFV2_KERNEL_SELECT_PREFILL, st);
+        sel_pre_lse<Tq, Tck><<<g1, 256, 0, st>>>(static_cast<const Tq*>(q), rows, q_start,
+                                                static_cast<const Tck*>(ck), ck_off, sh.hq, sh.hkv,
+                                                sh.p, sh.s, sh.score_scale, w.nblk_max, lse, keys);
+    }
+    {
+        KernelTimer kt(INFV2_KERNEL_SELECT_PREFILL, st);
+        sel_pre_scores<Tq, Tck><<<g1, 256, 0, st>>>(static_cast<const Tq*>(q), rows, q_start,
+                                                   static_cast<const Tck*>(ck), ck_off, sh.hq,
+                                                   sh.hkv, sh.m, sh.p, sh.s, sh.score_scale,
+                                                   w.nblk_max, lse, keys);
+    }
+    KernelTimer kt(INFV2_KERNEL_SELECT_TOPK, st);
     sel_pre_topk<<<dim3(rows, sh.hkv), 256, w.nblk_max * sizeof(uint32_t), st>>>(q_start, sh.hkv, sh.m, sh.topk, sh.init,
                                                      sh.local, w.nblk_max, keys, idx, score);
 }
