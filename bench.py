@@ -441,8 +441,8 @@ def main() -> int:
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (the design note "
-              "on sharding is in DESIGN.md); run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path; "
+              "run with --gpus 1.", file=sys.stderr)
         return 2
 
     import torch

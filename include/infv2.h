@@ -26,8 +26,9 @@
  *    memory (offsets, lengths, indices) cannot be checked on the host; if they
  *    are inconsistent with the buffers the result is undefined.
  *  - Launch failures are reported as INFV2_ERR_DEVICE.
- *  - The library holds no mutable global state.  Concurrent calls on
- *    different streams need distinct workspaces.
+ *  - The method's calls hold no mutable global state (the benchmark timing
+ *    session at the end of this header is the only global state).
+ *    Concurrent calls on different streams need distinct workspaces.
  *
  * Layouts (row-major, contiguous; element type given by the config):
  *  - Query heads h = g*G + r (r < G) belong to KV head g, G = Hq / Hkv.

@@ -11,8 +11,7 @@ cited below as [IV2 <paragraph>]; the block-score formula is also restated
 cleanly in the Korean review page (dimensionstp), section "3-2. Module
 breakdown, 1) InfLLM v2", cited as [Review 3-2].
 
-Readings taken where the pages are silent or garbled (each also listed in
-DESIGN.md):
+Readings taken where the pages are silent or garbled:
   * only complete kernels exist: n_c(n) = floor((n - p)/s) + 1 for n >= p;
   * row i (absolute position) sees kernel j^ only if it lies wholly in
     [0, i]: j^*s + p <= i + 1 (causality of the pooled keys);
