@@ -141,6 +141,32 @@ def test_decode_forced_only_and_dense():
     _run_decode(wl, label="decode dense")
 
 
+@pytest.mark.parametrize("ck_dtype", ["fp32", "bf16"])
+def test_compress_incremental_token_by_token(ck_dtype):
+    """Decode-style cache growth: the compressed keys of a prefix, then one call
+    per appended token for the kernel it completes (few-kernel path), equal the
+    oracle's compressed keys of the whole sequence bit for bit."""
+    h = _harness()
+    wl = _small(lens=[3001, 700, 4500], topk=8, local=2, seed=29)
+    _say(f"incremental compress ck={ck_dtype}")
+    dev = h.DeviceWorkload(wl, ck_dtype)
+    p, s = wl.kernel_size, wl.kernel_stride
+    lens = wl.lens.astype(np.int64)
+    start = lens - 60
+    dev.compress(kv_lens=torch.tensor(start, device="cuda"))
+    for step in range(1, 61):
+        cur = start + step
+        begin = np.array([max(0, h.num_kernels(int(n) - 1, p, s)) for n in cur], dtype=np.int64)
+        new = max(h.num_kernels(int(n), p, s) - int(b0) for n, b0 in zip(cur, begin))
+        dev.compress(kv_lens=torch.tensor(cur, device="cuda"),
+                     ck_begin=torch.tensor(begin, device="cuda"), max_new=max(new, 1))
+    torch.cuda.synchronize()
+    cks = dev.ck_host()
+    for b in range(wl.batch):
+        want = ref.compress_keys(wl.k_f64(b), p, s, ck_dtype)
+        assert np.array_equal(cks[b], want), f"sequence {b}"
+
+
 def test_decode_first_token_attends_itself():
     h = _harness()
     wl = _small(lens=[1], topk=4, local=1, seed=27)
@@ -233,6 +259,49 @@ def test_prefill_config3_sampled_rows():
     pos = sorted(set(rng.integers(0, L, 48).tolist()) | set(range(L - 160, L))
                  | {0, 63, 64, 4095, 4096, 4097, 8191})
     _run_prefill(wl, wl.chunk, positions=pos, label="config 3 prefill")
+
+
+def _with_keys(wl, keys_of_seq):
+    """Replace the keys of every sequence of a workload by keys_of_seq(b, [Hkv][n][d])."""
+    from synth import f32_to_bf16_bits
+    parts = []
+    for b in range(wl.batch):
+        n = int(wl.lens[b])
+        kf = np.asarray(keys_of_seq(b, (wl.num_kv_heads, n, wl.head_dim)), dtype=np.float32)
+        parts.append((f32_to_bf16_bits(kf) if wl.io_dtype == "bf16" else kf).reshape(-1))
+    wl.k = np.concatenate(parts)
+    return wl
+
+
+def _levels(n_levels, seed):
+    """Keys constant inside each 64-token block, one of n_levels multiples of a
+    direction: many exactly equal block scores, so the top-k boundary falls
+    inside a run of ties."""
+    rng = np.random.default_rng(seed)
+
+    def keys(b, shape):
+        hkv, n, d = shape
+        u = rng.standard_normal(d)
+        u /= np.linalg.norm(u)
+        lvl = rng.integers(0, n_levels, size=(hkv, -(-n // 64)))
+        return np.repeat(lvl, 64, axis=1)[:, :n, None] * 0.5 * u[None, None, :]
+    return keys
+
+
+def test_selection_with_massive_ties():
+    """All scores equal (the lowest blocks win) and a few distinct score levels
+    (the boundary falls inside long runs of equal scores)."""
+    zero = lambda b, shape: np.zeros(shape)
+    wl = _with_keys(_small(lens=[7000, 20000], topk=16, local=2, seed=51), zero)
+    _run_decode(wl, label="decode all-equal scores")
+    wl = _with_keys(_small(lens=[9000, 33000], topk=24, local=3, seed=52), _levels(3, 52))
+    _run_decode(wl, label="decode 3 score levels")
+    wl = _with_keys(_small(lens=[5000], topk=20, local=2, seed=53), _levels(6, 53))
+    _run_decode(wl, label="decode 6 score levels")
+    wl = _with_keys(_small(mode="prefill", lens=[2000], topk=8, local=2, seed=54), _levels(2, 54))
+    _run_prefill(wl, 700, label="prefill 2 score levels")
+    wl = _with_keys(_small(mode="prefill", lens=[1500], topk=6, local=1, seed=55), zero)
+    _run_prefill(wl, 1500, label="prefill all-equal scores")
 
 
 def test_decode_equals_last_prefill_row():

@@ -13,6 +13,7 @@
 namespace infv2 {
 
 constexpr int kCompressKpb = 16;   // kernels per thread block
+constexpr int kCompressFew = 4;    // up to this many new kernels: one block per kernel
 
 // float64 -> bf16, one rounding to nearest even (including the subnormal range)
 __device__ __forceinline__ bf16_t f64_to_bf16(double x) {
@@ -77,12 +78,65 @@ __global__ __launch_bounds__(256) void compress_kernel(
     }
 }
 
+// Few new kernels per sequence (a decode step completes at most one): one block
+// per kernel, the p rows split over 8 groups of 32 lanes so that every row is
+// loaded in the same memory round trip, then the 8 float64 partial sums are
+// added in LDS.
+template <typename Tin, bool kCkBf16>
+__global__ __launch_bounds__(256) void compress_few_kernel(
+    const Tin* __restrict__ k, const int64_t* __restrict__ kv_off,
+    const int64_t* __restrict__ kv_lens, const int64_t* __restrict__ ck_off,
+    const int64_t* __restrict__ ck_begin, void* __restrict__ ck_out, int hkv, int p, int s) {
+    __shared__ double part[8][kHeadDim];
+    const int b = blockIdx.z, h = blockIdx.y;
+    const int64_t o0 = kv_off[b], cap = kv_off[b + 1] - o0;
+    int64_t n = kv_lens ? kv_lens[b] : cap;
+    n = n < cap ? n : cap;
+    const int64_t nc = num_kernels(n, p, s);
+    const int64_t c0 = ck_off[b], ccap = ck_off[b + 1] - c0;
+    const int64_t j = (ck_begin ? ck_begin[b] : 0) + blockIdx.x;
+    if (j < 0 || j >= nc || j >= ccap) return;          // uniform over the block
+    const int grp = threadIdx.x >> 5, col = (threadIdx.x & 31) * 4;
+    const Tin* src = k + (o0 * hkv + static_cast<int64_t>(h) * cap + j * s) * kHeadDim + col;
+    double acc0 = 0.0, acc1 = 0.0, acc2 = 0.0, acc3 = 0.0;
+    for (int t0 = grp; t0 < p; t0 += 64) {               // up to 8 rows per batch
+        float v[8][4];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int t = t0 + 8 * u;
+            if (t < p) load4(src + static_cast<int64_t>(t) * kHeadDim, v[u]);
+            else v[u][0] = v[u][1] = v[u][2] = v[u][3] = 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) { acc0 += v[u][0]; acc1 += v[u][1]; acc2 += v[u][2]; acc3 += v[u][3]; }
+    }
+    part[grp][col] = acc0; part[grp][col + 1] = acc1; part[grp][col + 2] = acc2; part[grp][col + 3] = acc3;
+    __syncthreads();
+    if (threadIdx.x >= kHeadDim) return;
+    const int d = threadIdx.x;
+    double sum = 0.0;
+#pragma unroll
+    for (int g2 = 0; g2 < 8; ++g2) sum += part[g2][d];
+    const double mean = sum / static_cast<double>(p);
+    const int64_t dst = ((c0 * hkv + static_cast<int64_t>(h) * ccap) + j) * kHeadDim + d;
+    if (kCkBf16) static_cast<bf16_t*>(ck_out)[dst] = f64_to_bf16(mean);
+    else static_cast<float*>(ck_out)[dst] = static_cast<float>(mean);
+}
+
 hipError_t launch_compress(const Shape& sh, const void* k, const int64_t* kv_off,
                            const int64_t* kv_lens, const int64_t* ck_off, const int64_t* ck_begin,
                            int batch, int64_t max_new, void* ck, hipStream_t st) {
     if (max_new <= 0) return hipSuccess;
-    dim3 grid(static_cast<unsigned>((max_new + kCompressKpb - 1) / kCompressKpb), sh.hkv, batch);
     KernelTimer kt(INFV2_KERNEL_COMPRESS, st);
+    if (max_new <= kCompressFew) {
+        const dim3 g1(static_cast<unsigned>(max_new), sh.hkv, batch);
+#define INFV2_FEW(TIN, CKB) compress_few_kernel<TIN, CKB><<<g1, 256, 0, st>>>(static_cast<const TIN*>(k), kv_off, kv_lens, ck_off, ck_begin, ck, sh.hkv, sh.p, sh.s)
+        if (sh.io_bf16) { if (sh.ck_bf16) INFV2_FEW(bf16_t, true); else INFV2_FEW(bf16_t, false); }
+        else { if (sh.ck_bf16) INFV2_FEW(float, true); else INFV2_FEW(float, false); }
+#undef INFV2_FEW
+        return hipGetLastError();
+    }
+    dim3 grid(static_cast<unsigned>((max_new + kCompressKpb - 1) / kCompressKpb), sh.hkv, batch);
     if (sh.io_bf16) {
         if (sh.ck_bf16)
             compress_kernel<bf16_t, true><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(k), kv_off, kv_lens, ck_off, ck_begin, ck, sh.hkv, sh.p, sh.s);

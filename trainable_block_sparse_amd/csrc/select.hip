@@ -265,35 +265,48 @@ __global__ __launch_bounds__(256) void sel_dec_scores(
     nvis = nvis < nc_max ? nvis : nc_max;
     const size_t bg = static_cast<size_t>(b) * hkv + g;
     uint32_t* kb = keys + bg * nblk_max;
+    const int64_t j0 = static_cast<int64_t>(ch) * kChunkB;
+    const int64_t j = j0 + t;
 
-    // per-head LogSumExp from the (max, sum-exp) partials of pass 1 (16 threads per head)
+    // this thread's 16 logits and the (max, sum-exp) partials are independent
+    // loads: issue them together (one memory round trip)
+    float zz[kGroup];
+    {
+        const float* z = logits + bg * kGroup * nc_ld + (j < nvis ? j : 0);
+#pragma unroll
+        for (int h = 0; h < kGroup; ++h) zz[h] = z[h * nc_ld];
+    }
+    // per-head LogSumExp from the partials of pass 1 (16 threads per head)
     {
         const int h = t >> 4, r = t & 15;
         const float2* pp = partial + bg * nchunk_a * kGroup + h;
+        constexpr int kMaxPer = 16;          // partials per thread held in registers
+        float2 pm[kMaxPer];
+#pragma unroll
+        for (int u = 0; u < kMaxPer; ++u) {
+            const int c = r + 16 * u;
+            pm[u] = c < nchunk_a ? pp[static_cast<size_t>(c) * kGroup] : make_float2(-INFINITY, 0.f);
+        }
         float mx = -INFINITY;
-#pragma unroll 8
-        for (int c = r; c < nchunk_a; c += 16) mx = fmaxf(mx, pp[static_cast<size_t>(c) * kGroup].x);
+#pragma unroll
+        for (int u = 0; u < kMaxPer; ++u) mx = fmaxf(mx, pm[u].x);
+        for (int c = r + 16 * kMaxPer; c < nchunk_a; c += 16) mx = fmaxf(mx, pp[static_cast<size_t>(c) * kGroup].x);
         mx = max16(mx);
         float sm = 0.f;
         if (mx != -INFINITY) {
-#pragma unroll 8
-            for (int c = r; c < nchunk_a; c += 16) {
-                const float2 pm = pp[static_cast<size_t>(c) * kGroup];
-                sm += (pm.x == -INFINITY) ? 0.f : pm.y * expf(pm.x - mx);
+#pragma unroll
+            for (int u = 0; u < kMaxPer; ++u) sm += (pm[u].x == -INFINITY) ? 0.f : pm[u].y * expf(pm[u].x - mx);
+            for (int c = r + 16 * kMaxPer; c < nchunk_a; c += 16) {
+                const float2 q2 = pp[static_cast<size_t>(c) * kGroup];
+                sm += (q2.x == -INFINITY) ? 0.f : q2.y * expf(q2.x - mx);
             }
         }
         sm = sum16(sm);
         if (r == 0) ls[h] = (mx == -INFINITY) ? -INFINITY : mx + logf(sm);
     }
     __syncthreads();
-    const int64_t j0 = static_cast<int64_t>(ch) * kChunkB;
-    const int64_t j = j0 + t;
     float R = -INFINITY;
     if (j < nvis) {
-        const float* z = logits + bg * kGroup * nc_ld + j;
-        float zz[kGroup];
-#pragma unroll
-        for (int h = 0; h < kGroup; ++h) zz[h] = z[h * nc_ld];
         float acc = 0.f;
 #pragma unroll
         for (int h = 0; h < kGroup; ++h) acc += expf(zz[h] - ls[h]);
@@ -317,24 +330,33 @@ __global__ __launch_bounds__(256) void sel_dec_scores(
 }
 
 // ------------------------------------------------------------------ decode, top-k
+// Keys of the thread's blocks are loaded straight into registers, in the same
+// memory round trip as the sequence length.
+template <int kPer>
 __global__ __launch_bounds__(256) void sel_dec_topk(const int64_t* __restrict__ kv_off,
                                                     const int64_t* __restrict__ kv_lens, int hkv,
                                                     int m, int topk, int init, int local,
-                                                    int64_t nblk_max,
+                                                    int64_t nblk_max, int per,
                                                     const uint32_t* __restrict__ keys,
                                                     int32_t* __restrict__ idx,
                                                     float* __restrict__ score) {
-    __shared__ TopkSmem sm;
-    extern __shared__ uint32_t lkeys[];
+    __shared__ TopkSmem<256> sm;
     const int b = blockIdx.y, g = blockIdx.x;
+    const size_t bg = static_cast<size_t>(b) * hkv + g;
+    const int jb = static_cast<int>(threadIdx.x) * per;
+    const uint32_t* gk = keys + bg * nblk_max;
+    uint32_t key[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) key[u] = (u < per && jb + u < nblk_max) ? gk[jb + u] : 0u;
     const int64_t cap = kv_off[b + 1] - kv_off[b];
     int64_t n = kv_lens ? kv_lens[b] : cap;
     n = n < cap ? n : cap;
     int64_t c = n > 0 ? (n - 1) / m : -1;
     c = c < nblk_max - 1 ? c : nblk_max - 1;
-    const size_t bg = static_cast<size_t>(b) * hkv + g;
-    block_topk<256>(keys + bg * nblk_max, c, topk, init, local, idx + bg * topk,
-                    score ? score + bg * topk : nullptr, sm, lkeys);
+    int cnt = static_cast<int>(c + 1) - jb;
+    cnt = cnt < 0 ? 0 : (cnt > per ? per : cnt);
+    block_topk_regs<256>(key, jb, cnt, static_cast<int>(c), topk, init, local, idx + bg * topk,
+                         score ? score + bg * topk : nullptr, sm);
 }
 
 // ------------------------------------------------------------------ prefill, pass 1
@@ -697,22 +719,57 @@ __global__ __launch_bounds__(256) void sel_pre_mfma(
 }
 
 // ------------------------------------------------------------------ prefill, top-k
+template <int kPer>
 __global__ __launch_bounds__(256) void sel_pre_topk(int64_t q_start, int hkv, int m, int topk,
-                                                    int init, int local, int64_t nblk_max,
+                                                    int init, int local, int64_t nblk_max, int per,
                                                     const uint32_t* __restrict__ keys,
                                                     int32_t* __restrict__ idx,
                                                     float* __restrict__ score) {
-    __shared__ TopkSmem sm;
+    __shared__ TopkSmem<256> sm;
     const int row = blockIdx.x, g = blockIdx.y;
     const size_t rg = static_cast<size_t>(row) * hkv + g;
     int64_t c = (q_start + row) / m;
     c = c < nblk_max - 1 ? c : nblk_max - 1;
-    extern __shared__ uint32_t lkeys[];
-    block_topk<256>(keys + rg * nblk_max, c, topk, init, local, idx + rg * topk,
-                    score ? score + rg * topk : nullptr, sm, lkeys);
+    const int jb = static_cast<int>(threadIdx.x) * per;
+    int cnt = static_cast<int>(c + 1) - jb;
+    cnt = cnt < 0 ? 0 : (cnt > per ? per : cnt);
+    const uint32_t* gk = keys + rg * nblk_max;
+    uint32_t key[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) key[u] = u < cnt ? gk[jb + u] : 0u;
+    block_topk_regs<256>(key, jb, cnt, static_cast<int>(c), topk, init, local, idx + rg * topk,
+                         score ? score + rg * topk : nullptr, sm);
 }
 
 // ------------------------------------------------------------------ launchers
+// keys per thread: the smallest register-array size that covers nblk_max / 256
+#define INFV2_TOPK_DISPATCH(per, LAUNCH) \
+    do {                                  \
+        if ((per) <= 2) LAUNCH(2);        \
+        else if ((per) <= 8) LAUNCH(8);   \
+        else if ((per) <= 16) LAUNCH(16); \
+        else LAUNCH(64);                  \
+    } while (0)
+
+static void launch_topk_dec(const Shape& sh, int batch, int64_t nblk_max, const int64_t* kv_off,
+                            const int64_t* kv_lens, const uint32_t* keys, int32_t* idx,
+                            float* score, hipStream_t st) {
+    const int per = topk_per(nblk_max, 256);
+#define INFV2_L(P) sel_dec_topk<P><<<dim3(sh.hkv, batch), 256, 0, st>>>( \
+        kv_off, kv_lens, sh.hkv, sh.m, sh.topk, sh.init, sh.local, nblk_max, per, keys, idx, score)
+    INFV2_TOPK_DISPATCH(per, INFV2_L);
+#undef INFV2_L
+}
+
+static void launch_topk_pre(const Shape& sh, int rows, int64_t q_start, int64_t nblk_max,
+                            const uint32_t* keys, int32_t* idx, float* score, hipStream_t st) {
+    const int per = topk_per(nblk_max, 256);
+#define INFV2_L(P) sel_pre_topk<P><<<dim3(rows, sh.hkv), 256, 0, st>>>( \
+        q_start, sh.hkv, sh.m, sh.topk, sh.init, sh.local, nblk_max, per, keys, idx, score)
+    INFV2_TOPK_DISPATCH(per, INFV2_L);
+#undef INFV2_L
+}
+
 template <typename Tq, typename Tck>
 static void dec_launch(const Shape& sh, const void* q, const void* ck, const int64_t* ck_off,
                        const int64_t* kv_off, const int64_t* kv_lens, int batch,
@@ -741,9 +798,9 @@ static void dec_launch(const Shape& sh, const void* q, const void* ck, const int
                                            w.nc_ld, w.nchunk_a, w.nblk_max, logits, partial, keys);
     }
     KernelTimer kt(INFV2_KERNEL_SELECT_TOPK, st);
-    sel_dec_topk<<<dim3(sh.hkv, batch), 256, w.nblk_max * sizeof(uint32_t), st>>>(
-        kv_off, kv_lens, sh.hkv, sh.m, sh.topk, sh.init, sh.local, w.nblk_max, keys, idx, score);
+    launch_topk_dec(sh, batch, w.nblk_max, kv_off, kv_lens, keys, idx, score, st);
 }
+
 
 hipError_t launch_select_decode(const Shape& sh, const void* q, const void* ck,
                                 const int64_t* ck_off, const int64_t* kv_off,
@@ -785,8 +842,7 @@ static void pre_launch(const Shape& sh, const void* q, int rows, int64_t q_start
                                                     lse, keys);
         }
         KernelTimer kt(INFV2_KERNEL_SELECT_TOPK, st);
-        sel_pre_topk<<<dim3(rows, sh.hkv), 256, w.nblk_max * sizeof(uint32_t), st>>>(
-            q_start, sh.hkv, sh.m, sh.topk, sh.init, sh.local, w.nblk_max, keys, idx, score);
+        launch_topk_pre(sh, rows, q_start, w.nblk_max, keys, idx, score, st);
         return;
     }
     {
@@ -803,8 +859,7 @@ static void pre_launch(const Shape& sh, const void* q, int rows, int64_t q_start
                                                    w.nblk_max, lse, keys);
     }
     KernelTimer kt(INFV2_KERNEL_SELECT_TOPK, st);
-    sel_pre_topk<<<dim3(rows, sh.hkv), 256, w.nblk_max * sizeof(uint32_t), st>>>(q_start, sh.hkv, sh.m, sh.topk, sh.init,
-                                                     sh.local, w.nblk_max, keys, idx, score);
+    launch_topk_pre(sh, rows, q_start, w.nblk_max, keys, idx, score, st);
 }
 
 hipError_t launch_select_prefill(const Shape& sh, const void* q, int rows, int64_t q_start,

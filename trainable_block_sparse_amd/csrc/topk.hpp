@@ -5,147 +5,244 @@
 // local window are always kept; shorter than k*m degenerates to dense).
 //
 // Candidates are the blocks 0..c that are not forced.  Scores arrive as sortable
-// 32-bit keys (score_to_key) in LDS.  The k' = k - |F| largest keys are found
-// by an MSB-first radix select (four 8-bit digits, histogram in LDS), which
-// yields the exact k'-th largest key T and how many candidates equal to T are
-// still needed; those are taken in increasing block order, so ties go to the
-// lower block.  Each thread owns a contiguous range of block indices, so the
-// ascending output needs only two block-wide scans.  Must be called by all
-// kThreads threads of the block (kThreads a multiple of 256).
+// 32-bit keys (score_to_key).  Thread t owns the contiguous blocks
+// [t*per, t*per + per) and holds their keys in registers for the whole
+// selection.  The k' = k - |F| largest keys, ties to the lower block, are
+// found by narrowing a key window [lo, hi]:
+//   1. lo, hi = min and max candidate key;
+//   2. histogram of the candidates in the window over at most 1024 bins of
+//      2^sh consecutive key values (sh chosen so the window fits), which
+//      adapts to the data: the bins spread even when every score shares its
+//      exponent;
+//   3. the bin holding the k'-th largest key becomes the new window; every key
+//      above it is taken.
+// The loop stops when the window's keys are all needed, when the window holds
+// at most kThreads keys (each is then ranked against the others by (key desc,
+// block asc)), or when the window is a single key value (the lowest blocks are
+// taken).  Each step shrinks the window by 2^10 (a 32-bit key range needs at
+// most four steps; typical inputs need one).  The ascending output needs one
+// block scan because ownership is contiguous.
 #pragma once
+
+#include <type_traits>
 
 #include "common.hpp"
 
 namespace infv2 {
 
+constexpr int kTopkBins = 1024;
+
+template <int kThreads>
 struct TopkSmem {
-    uint32_t hist[256];
-    uint32_t scan_tmp[24];
-    uint32_t prefix, need;
+    uint32_t hist[kTopkBins];
+    uint32_t scan_tmp[kThreads / 64 + 1];
+    uint32_t rmin[kThreads / 64], rmax[kThreads / 64];
+    uint32_t ckey[kThreads];        // the window's keys (rank step), then keep flags
+    int32_t cidx[kThreads];         // and their blocks
+    uint32_t bstar, above, ncol, total;
 };
 
-__device__ __forceinline__ bool is_forced(int64_t j, int64_t c, int init, int local) {
-    return j < init || j > c - local;
+// keys per thread held in registers for a block of kThreads and nblk blocks
+__host__ __device__ constexpr int topk_per(int64_t nblk, int threads) {
+    return static_cast<int>((nblk + threads - 1) / threads);
 }
 
-// lk: [c+1] sortable scores in LDS.  Writes idx[k] (and score[k] if non-null).
-template <int kThreads>
-__device__ inline void block_topk_lds(const uint32_t* lk, int64_t c, int k, int init, int local,
-                                      int32_t* __restrict__ idx, float* __restrict__ score,
-                                      TopkSmem& sm) {
+// key[u] is the key of block jb + u for u < cnt (cnt = valid blocks of this
+// thread, 0 if none).  Must be called by all kThreads threads of the block.
+// Writes idx[k] ascending, padded with -1 (and score[k] if non-null).
+template <int kThreads, int kPer, typename Smem>
+__device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int cnt, int c, int k,
+                                       int init, int local, int32_t* __restrict__ idx,
+                                       float* __restrict__ score, Smem& sm) {
+    static_assert(kThreads % 64 == 0 && kThreads <= kTopkBins && kTopkBins % kThreads == 0,
+                  "block size");
+    static_assert(kPer <= 64, "at most 64 keys per thread");
+    using Mask = typename std::conditional<(kPer > 32), uint64_t, uint32_t>::type;
     constexpr int kWaves = kThreads / 64;
-    const int t = threadIdx.x;
-    const int nb = static_cast<int>(c + 1);
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int nb = c + 1;
     const float kNaN = __uint_as_float(0x7fc00000u);
     if (nb <= k) {                      // dense: every block, then -1 padding
-        for (int r = t; r < k; r += kThreads) {
-            idx[r] = r < nb ? r : -1;
-            if (score) score[r] = r < nb ? key_to_score(lk[r]) : kNaN;
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            if (u < cnt) {
+                idx[jb + u] = jb + u;
+                if (score) score[jb + u] = key_to_score(key[u]);
+            }
+        }
+        for (int r = nb + t; r < k; r += kThreads) {
+            idx[r] = -1;
+            if (score) score[r] = kNaN;
         }
         return;
     }
     const int a = init < nb ? init : nb;
-    const int lo = c - local + 1 > 0 ? static_cast<int>(c - local + 1) : 0;
-    const int nforced = a + (nb - (lo > a ? lo : a));
+    const int lo_loc = c - local + 1 > 0 ? c - local + 1 : 0;
+    const int nforced = a + (nb - (lo_loc > a ? lo_loc : a));
     const uint32_t kp = static_cast<uint32_t>(k - nforced);
-    const int per = (nb + kThreads - 1) / kThreads;
-    const int jb = t * per;
-    const int je = jb + per < nb ? jb + per : nb;
+    // candidate mask of this thread's blocks
+    Mask cmask = 0;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int j = jb + u;
+        if (u < cnt && j >= init && j <= c - local) cmask |= Mask(1) << u;
+    }
+    auto cand = [&](int u) { return ((cmask >> u) & 1u) != 0; };
 
-    uint32_t prefix = 0, mask = 0, need = kp;
+    // window [lo, hi] of undecided keys; keys above hi are taken.
+    // mode: 0 = take every candidate in the window, 1 = rank the window,
+    //       2 = single key value: the lowest `need` blocks, 3 = none.
+    uint32_t lo = 0, hi = 0, need = kp;
+    int mode = 3;
     if (kp > 0) {
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            if (t < 256) sm.hist[t] = 0;
-            __syncthreads();
-            for (int j = jb; j < je; ++j) {
-                if (is_forced(j, c, init, local)) continue;
-                const uint32_t key = lk[j];
-                if ((key & mask) == prefix) atomicAdd(&sm.hist[(key >> shift) & 255u], 1u);
-            }
-            __syncthreads();
-            // thread t < 256 looks at digit 255 - t; incl = #candidates with digit >= it
-            const uint32_t v = t < 256 ? sm.hist[255 - t] : 0u;
-            const uint32_t incl = block_incl_scan<kWaves>(v, sm.scan_tmp);
-            const uint32_t excl = incl - v;
-            if (t < 256 && excl < need && need <= incl) {
-                sm.prefix = prefix | (static_cast<uint32_t>(255 - t) << shift);
-                sm.need = need - excl;
-            }
-            __syncthreads();
-            prefix = sm.prefix;
-            need = sm.need;
-            mask |= 255u << shift;
-            __syncthreads();
-        }
-    }
-    // selected = forced, strictly above T, and the first `need` candidates equal to T
-    uint32_t n_eq = 0;
-    if (kp > 0)
-        for (int j = jb; j < je; ++j)
-            n_eq += (!is_forced(j, c, init, local) && lk[j] == prefix) ? 1u : 0u;
-    const uint32_t eq_base = block_incl_scan<kWaves>(n_eq, sm.scan_tmp) - n_eq;
-    uint32_t n_sel = 0;
-    {
-        uint32_t r = eq_base;
-        for (int j = jb; j < je; ++j) {
-            const bool f = is_forced(j, c, init, local);
-            const uint32_t key = lk[j];
-            const bool eq = !f && kp > 0 && key == prefix;
-            const bool sel = f || (!f && kp > 0 && key > prefix) || (eq && r < need);
-            r += eq ? 1u : 0u;
-            n_sel += sel ? 1u : 0u;
-        }
-    }
-    uint32_t pos = block_incl_scan<kWaves>(n_sel, sm.scan_tmp) - n_sel;
-    {
-        uint32_t r = eq_base;
-        for (int j = jb; j < je; ++j) {
-            const bool f = is_forced(j, c, init, local);
-            const uint32_t key = lk[j];
-            const bool eq = !f && kp > 0 && key == prefix;
-            const bool sel = f || (!f && kp > 0 && key > prefix) || (eq && r < need);
-            r += eq ? 1u : 0u;
-            if (sel && pos < static_cast<uint32_t>(k)) {
-                idx[pos] = j;
-                if (score) score[pos] = key_to_score(key);
-            }
-            pos += sel ? 1u : 0u;
-        }
-    }
-    // every selected block is written above; slots past the total stay padding
-    if (t == kThreads - 1) sm.scan_tmp[kWaves] = pos;
-    __syncthreads();
-    for (int r = static_cast<int>(sm.scan_tmp[kWaves]) + t; r < k; r += kThreads) {
-        idx[r] = -1;
-        if (score) score[r] = kNaN;
-    }
-}
-
-// keys in global memory: staged into the LDS scratch `lk` (>= c+1 words) first
-template <int kThreads>
-__device__ inline void block_topk(const uint32_t* gkeys, int64_t c, int k, int init, int local,
-                                  int32_t* __restrict__ idx, float* __restrict__ score,
-                                  TopkSmem& sm, uint32_t* lk) {
-    const int nb = static_cast<int>(c + 1);
-    if (nb > k) {
-        // batches of independent loads, then the LDS stores
-        for (int j0 = threadIdx.x; j0 < nb; j0 += 8 * kThreads) {
-            uint32_t r[8];
+        uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int j = j0 + u * kThreads;
-                r[u] = j < nb ? gkeys[j] : 0u;
+        for (int u = 0; u < kPer; ++u) {
+            if (cand(u)) {
+                mn = key[u] < mn ? key[u] : mn;
+                mx = key[u] > mx ? key[u] : mx;
             }
+        }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int j = j0 + u * kThreads;
-                if (j < nb) lk[j] = r[u];
+        for (int o = 32; o >= 1; o >>= 1) {
+            const uint32_t a0 = __shfl_xor(mn, o, 64), a1 = __shfl_xor(mx, o, 64);
+            mn = a0 < mn ? a0 : mn;
+            mx = a1 > mx ? a1 : mx;
+        }
+        if (lane == 0) { sm.rmin[w] = mn; sm.rmax[w] = mx; }
+        __syncthreads();
+        lo = 0xffffffffu; hi = 0u;
+#pragma unroll
+        for (int x = 0; x < kWaves; ++x) {
+            lo = sm.rmin[x] < lo ? sm.rmin[x] : lo;
+            hi = sm.rmax[x] > hi ? sm.rmax[x] : hi;
+        }
+        for (;;) {
+            const uint32_t span = hi - lo;
+            if (span == 0) { mode = 2; break; }
+            const int bits = 32 - __clz(span);
+            const int sh = bits > 10 ? bits - 10 : 0;
+#pragma unroll
+            for (int x = t; x < kTopkBins; x += kThreads) sm.hist[x] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < kPer; ++u)
+                if (cand(u) && key[u] >= lo && key[u] <= hi) atomicAdd(&sm.hist[(key[u] - lo) >> sh], 1u);
+            __syncthreads();
+            // descending bins: thread t owns bins [1024 - kB (t+1), 1024 - kB t)
+            constexpr int kB = kTopkBins / kThreads;
+            uint32_t cntb[kB];
+            uint32_t sum = 0;
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                cntb[u] = sm.hist[kTopkBins - 1 - (t * kB + u)];
+                sum += cntb[u];
+            }
+            const uint32_t incl = block_incl_scan<kWaves>(sum, sm.scan_tmp);
+            uint32_t run = incl - sum;            // candidates in higher bins
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                if (run < need && need <= run + cntb[u]) {
+                    sm.bstar = static_cast<uint32_t>(kTopkBins - 1 - (t * kB + u));
+                    sm.above = run;
+                }
+                run += cntb[u];
+            }
+            __syncthreads();
+            const uint32_t bstar = sm.bstar;
+            need -= sm.above;
+            const uint32_t e = sm.hist[bstar];
+            __syncthreads();                      // bstar / above / hist read by all
+            const uint32_t nlo = lo + (bstar << sh);
+            const uint32_t width = (sh >= 32) ? 0xffffffffu : ((1u << sh) - 1u);
+            hi = (hi - nlo > width) ? nlo + width : hi;
+            lo = nlo;
+            if (e == need) { mode = 0; break; }
+            if (e <= static_cast<uint32_t>(kThreads)) { mode = 1; break; }
+        }
+    }
+    auto in_window = [&](int u) { return cand(u) && key[u] >= lo && key[u] <= hi; };
+    uint32_t ncol = 0;
+    if (mode == 1) {                      // collect the window's keys, rank them
+        if (t == 0) sm.ncol = 0;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            if (in_window(u)) {
+                const uint32_t slot = atomicAdd(&sm.ncol, 1u);
+                sm.ckey[slot] = key[u];
+                sm.cidx[slot] = jb + u;
             }
         }
         __syncthreads();
-        block_topk_lds<kThreads>(lk, c, k, init, local, idx, score, sm);
-    } else {
-        block_topk_lds<kThreads>(gkeys, c, k, init, local, idx, score, sm);
+        ncol = sm.ncol;
+        uint32_t keep = 0;
+        if (static_cast<uint32_t>(t) < ncol) {
+            const uint32_t mk = sm.ckey[t];
+            const int32_t mj = sm.cidx[t];
+            uint32_t rank = 0;
+            for (uint32_t x = 0; x < ncol; ++x) {
+                const uint32_t ok = sm.ckey[x];
+                rank += (ok > mk || (ok == mk && sm.cidx[x] < mj)) ? 1u : 0u;
+            }
+            keep = rank < need ? 1u : 0u;
+        }
+        __syncthreads();                      // every rank read before the flags overwrite
+        if (static_cast<uint32_t>(t) < ncol) sm.ckey[t] = keep;
+        __syncthreads();
+    }
+    // selection flags of this thread's blocks
+    Mask smask = 0;
+    if (mode == 2) {                      // lowest `need` window blocks in block order
+        uint32_t n_eq = 0;
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) n_eq += in_window(u) ? 1u : 0u;
+        uint32_t r = block_incl_scan<kWaves>(n_eq, sm.scan_tmp) - n_eq;
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            if (in_window(u)) {
+                if (r < need) smask |= Mask(1) << u;
+                ++r;
+            }
+        }
+    } else if (mode != 3) {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            if (!cand(u)) continue;
+            bool s = key[u] > hi;
+            if (!s && in_window(u)) {
+                if (mode == 0) {
+                    s = true;
+                } else {
+                    for (uint32_t x = 0; x < ncol; ++x)
+                        if (sm.cidx[x] == jb + u) { s = sm.ckey[x] != 0u; break; }
+                }
+            }
+            if (s) smask |= Mask(1) << u;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+        if (u < cnt && !cand(u)) smask |= Mask(1) << u;     // forced
+    const uint32_t n_sel = sizeof(Mask) == 8 ? __popcll(static_cast<uint64_t>(smask))
+                                             : __popc(static_cast<uint32_t>(smask));
+    uint32_t pos = block_incl_scan<kWaves>(n_sel, sm.scan_tmp) - n_sel;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        if ((smask >> u) & 1u) {
+            if (pos < static_cast<uint32_t>(k)) {
+                idx[pos] = jb + u;
+                if (score) score[pos] = key_to_score(key[u]);
+            }
+            ++pos;
+        }
+    }
+    // every selected block is written above; slots past the total stay padding
+    if (t == kThreads - 1) sm.total = pos;
+    __syncthreads();
+    for (int r = static_cast<int>(sm.total) + t; r < k; r += kThreads) {
+        idx[r] = -1;
+        if (score) score[r] = kNaN;
     }
 }
 
