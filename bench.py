@@ -190,25 +190,31 @@ def bench_decode(cfg_index: int, args, torch, tbs, gh, replicas: int) -> dict:
     s1 = T.event()
     torch.cuda.synchronize()
     eager_ms = s0.elapsed_time(s1) / args.steps
-    # whole steps, HIP-graph replay (one graph per replica)
+    # whole steps, HIP-graph replay: one graph holds one step on each of the R
+    # replicas (R "layers" of one decode token), replayed back to back; a second
+    # graph holds the K mod R remaining steps, so exactly K steps are timed
     graph_ms = None
     if args.graph:
-        graphs = []
+        reps, rem = divmod(args.steps, R)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
+        graphs = []
         with torch.cuda.stream(side):
-            for r in range(R):
+            for n_steps in ([R] if reps else []) + ([rem] if rem else []):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=side):
-                    step(r)
+                    for r in range(n_steps):
+                        step(r)
                 graphs.append(g)
         torch.cuda.current_stream().wait_stream(side)
-        for t in range(args.warmup):
-            graphs[t % R].replay()
+        for _ in range(max(1, args.warmup // R)):
+            graphs[0].replay()
         torch.cuda.synchronize()
         g0 = T.event()
-        for t in range(args.steps):
-            graphs[t % R].replay()
+        for _ in range(reps):
+            graphs[0].replay()
+        if rem:
+            graphs[-1].replay()
         g1 = T.event()
         torch.cuda.synchronize()
         graph_ms = g0.elapsed_time(g1) / args.steps
