@@ -332,8 +332,15 @@ def bench_prefill(args, torch, tbs, gh) -> dict:
     # scoring GEMM work of one pass: Hq * d * 2 * sum_i n_vis(i)
     nvis = np.array([num_kernels(i + 1, p, s) for i in range(L)], dtype=np.int64)
     score_flops_pass = float(2 * d * hq * nvis.sum())
+    # K/V reuse of the attention kernel: a thread block serves 16 consecutive rows
+    # of one KV head and streams the union of their selected blocks once
+    grp = gi[: (L // 16) * 16].reshape(L // 16, 16, hkv, k).transpose(0, 2, 1, 3).reshape(-1, 16 * k)
+    union = np.array([np.unique(r[r >= 0]).size for r in grp])
+    pairs = (grp >= 0).sum(axis=1)
     res = {
         "workload": wl.name, "rows": L, "chunk": C, "useful_attn_flops": useful,
+        "union_blocks_per_16_rows": float(union.mean()),
+        "kv_reuse_per_loaded_block": float(pairs.sum() / union.sum()),
         "attn_ms": attn_ms, "select_ms": sel_ms, "compress_ms": float(ph[:, 0].sum()),
         "total_ms": total_ms, "tflops_attn": useful / (attn_ms * 1e-3) / 1e12,
         "tflops_path": useful / (total_ms * 1e-3) / 1e12,

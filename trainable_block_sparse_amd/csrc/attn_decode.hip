@@ -37,11 +37,15 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(
     __shared__ DecSmem sm;
     const int b = blockIdx.z, g = blockIdx.y, sp = blockIdx.x, t = threadIdx.x;
     const int w = t >> 6, l = t & 63, lg = l >> 4, lc = l & 15;
+    const size_t bg = static_cast<size_t>(b) * hkv + g;
+    const int e0 = sp * kDecBlocksPerSplit;
+    const int e1 = (e0 + kDecBlocksPerSplit < topk) ? e0 + kDecBlocksPerSplit : topk;
+    // the wave's first block id is loaded together with the offsets (one round trip)
+    const int32_t blk_first = (e0 + w < e1) ? idx[bg * topk + e0 + w] : -1;
     const int64_t o0 = kv_off[b], cap = kv_off[b + 1] - o0;
     int64_t n = kv_lens ? kv_lens[b] : cap;
     n = n < cap ? n : cap;
     const int64_t lim = n;                       // decode row i = n - 1 sees keys t < n
-    const size_t bg = static_cast<size_t>(b) * hkv + g;
     const bf16_t* kh = k + (o0 * hkv + static_cast<int64_t>(g) * cap) * kHeadDim;
     const bf16_t* vh = v + (o0 * hkv + static_cast<int64_t>(g) * cap) * kHeadDim;
 
@@ -62,10 +66,8 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(
         for (int h = 0; h < 2; ++h) o[c][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float mrun = -INFINITY, lrun = 0.f;
 
-    const int e0 = sp * kDecBlocksPerSplit;
-    const int e1 = (e0 + kDecBlocksPerSplit < topk) ? e0 + kDecBlocksPerSplit : topk;
     for (int e = e0 + w; e < e1; e += kDecWaves) {
-        const int32_t blk = idx[bg * topk + e];
+        const int32_t blk = e == e0 + w ? blk_first : idx[bg * topk + e];
         if (blk < 0) continue;
         for (int sub = 0; sub < m; sub += 64) {
             const int64_t t0 = static_cast<int64_t>(blk) * m + sub;
@@ -213,8 +215,20 @@ __global__ __launch_bounds__(256) void attn_decode_merge(const float* __restrict
     __shared__ float inv_den[kGroup];
     const int g = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
     const size_t bg = static_cast<size_t>(b) * hkv + g;
+    const int h = t >> 4, c0 = (t & 15) * 8;
+    // the first kPre splits' outputs are loaded with the (m, l) pairs, in one round trip
+    constexpr int kPre = 16;
+    float4 pre[kPre][2];
+#pragma unroll
+    for (int x = 0; x < kPre; ++x) {
+        if (x < nsplit) {
+            const float4* src = reinterpret_cast<const float4*>(part_o + ((bg * nsplit + x) * kGroup + h) * kHeadDim + c0);
+            pre[x][0] = src[0];
+            pre[x][1] = src[1];
+        }
+    }
     {
-        const int h = t >> 4, r = t & 15;        // 16 threads per head
+        const int r = t & 15;                    // 16 threads per head
         const float2* pm = part_ml + bg * nsplit * kGroup + h;
         float gm = -INFINITY;
         for (int x = r; x < nsplit; x += 16) gm = fmaxf(gm, pm[static_cast<size_t>(x) * kGroup].x);
@@ -230,17 +244,20 @@ __global__ __launch_bounds__(256) void attn_decode_merge(const float* __restrict
         if (r == 0) inv_den[h] = den > 0.f ? 1.f / den : 0.f;
     }
     __syncthreads();
-    const int h = t >> 4, c0 = (t & 15) * 8;
     float res[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int x = 0; x < nsplit; ++x) {
-        const float w = wgt[h][x];
-        const float4* src = reinterpret_cast<const float4*>(part_o + ((bg * nsplit + x) * kGroup + h) * kHeadDim + c0);
-        const float4 a0 = src[0], a1 = src[1];
+    auto accum = [&](float w, const float4& a0, const float4& a1) {
         res[0] = fmaf(w, a0.x, res[0]); res[1] = fmaf(w, a0.y, res[1]);
         res[2] = fmaf(w, a0.z, res[2]); res[3] = fmaf(w, a0.w, res[3]);
         res[4] = fmaf(w, a1.x, res[4]); res[5] = fmaf(w, a1.y, res[5]);
         res[6] = fmaf(w, a1.z, res[6]); res[7] = fmaf(w, a1.w, res[7]);
+    };
+#pragma unroll
+    for (int x = 0; x < kPre; ++x)
+        if (x < nsplit) accum(wgt[h][x], pre[x][0], pre[x][1]);
+#pragma unroll 4
+    for (int x = kPre; x < nsplit; ++x) {
+        const float4* src = reinterpret_cast<const float4*>(part_o + ((bg * nsplit + x) * kGroup + h) * kHeadDim + c0);
+        accum(wgt[h][x], src[0], src[1]);
     }
     const float inv = inv_den[h];
     T* dst = out + (static_cast<size_t>(b) * hq + static_cast<size_t>(g) * kGroup + h) * kHeadDim + c0;

@@ -6,11 +6,12 @@
 //
 // Every query row picks its own 64 blocks, so the matrix tile of a (row, block)
 // pair is 16 heads x 64 keys.  A thread block owns 16 consecutive rows of one
-// KV head; wave w (of 8) takes rows w and w+8.  The block builds the union of
-// the rows' selected blocks and streams it through LDS with direct
-// global->LDS loads (K as stored, V as V^T tiles built by vt_build), two stages
-// of two blocks, so the next two blocks load while the current two compute.
-// For each block a wave runs each of its rows that selected it:
+// KV head, one row per wave (16 waves, four per SIMD, so that the latency of
+// one wave's dependent MFMA / softmax chain hides behind the others).  The
+// block builds the union of the rows' selected blocks and streams it through
+// LDS with direct global->LDS loads (K as stored, V as V^T tiles built by
+// vt_build), four blocks per barrier interval.
+// For each block the waves whose row selected it run:
 //   S^T[key][head] = K_blk . Q_row^T          16 MFMA 16x16x32
 //   O^T[d][head]  += V^T_blk . P_row^T        16 MFMA 16x16x32
 // One head sits in each lane column, so softmax state is per lane.  The
@@ -19,6 +20,8 @@
 // the old reference (p <= 256, exact in fp32 and bf16), which skips the
 // cross-lane max and the rescale on almost every block.  Row sums stay per lane
 // until the end.  Keys after the row (t > i) are masked in the row's own block.
+// Thread blocks are placed so that each XCD (own L2) serves consecutive row
+// groups of one KV head.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -26,12 +29,16 @@ namespace infv2 {
 
 constexpr int kPB = 64;          // KV block size served here
 constexpr int kPRows = 16;       // query rows per thread block
-constexpr int kPWaves = 8;
-constexpr int kPRowsW = 2;       // query rows per wave
+constexpr int kPWaves = 16;      // one query row per wave, four waves per SIMD
+constexpr int kPRowsW = 16 / kPWaves;                // query rows per wave
+constexpr int kKBatch = 1;       // K-steps whose fragments are read from LDS at once
+constexpr int kVBatch = 2;       // V^T d-tiles whose fragments are read from LDS at once
+constexpr int kTileLoads = 16 / kPWaves;             // 1 KB global->LDS loads per wave per tile
 constexpr int kPThreads = kPWaves * 64;
 constexpr int kMaxWords = 512;   // bitmap words: up to 16384 blocks
 constexpr int kUnionCap = 2048;  // union entries: 16 rows x top-k, top-k <= 128
-constexpr int kGroup2 = 2;       // union blocks per LDS stage (two stages)
+constexpr int kGroup2 = 2;       // union blocks per LDS stage; two stages = one interval
+constexpr int kXcds = 8;         // thread blocks are dealt round-robin to the 8 XCDs
 constexpr float kRescaleSlack = 8.f;   // log2 units
 
 // V^T tiles store the 64 keys of a block in the order the P^T operand of the
@@ -79,7 +86,7 @@ struct UnionSmem {
     uint32_t mask[kUnionCap];         // which of the 16 rows selected each union block
     uint32_t bits[kMaxWords];
     uint32_t wbase[kMaxWords];
-    uint32_t scan_tmp[16];
+    uint32_t scan_tmp[kPWaves + 1];
 };
 typedef bf16_t StageTiles[kGroup2][kPB * kHeadDim];   // 2 x 16 KB (K) or 2 x 16 KB (V^T)
 
@@ -94,15 +101,21 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
     const bf16_t* __restrict__ q, int rows, int64_t q_start, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ vt, const int64_t* __restrict__ kv_off,
     const int32_t* __restrict__ idx, bf16_t* __restrict__ out, int hq, int hkv, int topk,
-    int64_t nblk, float scale_log2) {
+    int64_t nblk, int nrg, float scale_log2) {
     // The two stages are distinct LDS objects and every access below names its
     // stage, so the compiler can see that reading one stage does not depend on
     // the direct global->LDS loads still filling the other one.
     __shared__ __attribute__((aligned(16))) StageTiles k_a, v_a, k_b, v_b;
     __shared__ UnionSmem sm;
-    const int g = blockIdx.y, t = threadIdx.x;
+    // XCD-aware placement: thread block b runs on XCD b % 8; give each XCD a
+    // contiguous range of (KV head, row group) work items
+    const int nwg = static_cast<int>(gridDim.x);
+    const int xcd = static_cast<int>(blockIdx.x) % kXcds, kx = static_cast<int>(blockIdx.x) / kXcds;
+    const int qx = nwg / kXcds, rx = nwg % kXcds;
+    const int lid = xcd * qx + (xcd < rx ? xcd : rx) + kx;
+    const int g = lid / nrg, r0 = (lid % nrg) * kPRows;
+    const int t = threadIdx.x;
     const int w = t >> 6, l = t & 63, lg = l >> 4, lc = l & 15;
-    const int r0 = blockIdx.x * kPRows;
     const int64_t cap = kv_off[1] - kv_off[0];
     const bf16_t* kh = k + (kv_off[0] * hkv + static_cast<int64_t>(g) * cap) * kHeadDim;
     const bf16_t* vth = vt + static_cast<int64_t>(g) * nblk * kHeadDim * kPB;
@@ -151,12 +164,12 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
     bf16x8_t qf[kPRowsW][4];
     f32x4_t o[kPRowsW][8];
     float mref[kPRowsW], lsum[kPRowsW];       // per lane: reference max of head lc, partial row sum
-    int64_t qpos[kPRowsW];
+    int32_t qpos[kPRowsW];
 #pragma unroll
     for (int i = 0; i < kPRowsW; ++i) {
         const int row = r0 + kPWaves * i + w;
         const int rr = row < rows ? row : rows - 1;
-        qpos[i] = q_start + row;
+        qpos[i] = static_cast<int32_t>(q_start + row);
         const bf16_t* qrow = q + (static_cast<size_t>(rr) * hq + static_cast<size_t>(g) * kGroup + lc) * kHeadDim;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) qf[i][ks] = as_bf16x8(ldg16(qrow + 32 * ks + 8 * lg));
@@ -167,26 +180,34 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // only the tile loads stay in flight below
 
-    // ---- stream the union through LDS with direct global->LDS loads.
-    // Each wave issues 2 K and 2 V^T instructions per block (1 KB of LDS each).
+    // ---- stream the union through LDS with direct global->LDS loads.  Each
+    // wave fills 2 KB of each K and V^T tile (2 instructions each); the lane part
+    // of the address is fixed, only the block part (wave-uniform) changes.
+    int koff_l[kTileLoads], voff_l[kTileLoads], key_l[kTileLoads];
+#pragma unroll
+    for (int j = 0; j < kTileLoads; ++j) {
+        const int sg = kTileLoads * w + j;
+        key_l[j] = 4 * sg + (l >> 4);                       // keys 4 sg .. 4 sg + 3
+        koff_l[j] = key_l[j] * kHeadDim + 8 * ((l & 15) ^ (key_l[j] & 15));
+        const int d = 8 * sg + (l >> 3);                    // V^T rows 8 sg .. 8 sg + 7
+        voff_l[j] = d * kPB + 8 * ((l & 7) ^ ((d >> 1) & 7));
+    }
     auto issue = [&](StageTiles& kt, StageTiles& vtt, int u) {
         const int slot = u % kGroup2;
         const int32_t blk = sm.list[u];
+        const int64_t k0 = static_cast<int64_t>(blk) * kPB;
+        const bool partial = k0 + kPB > nlim;               // last block of the chunk
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int sg = 2 * w + j;
-            {   // K: bytes [1 KB sg, +1 KB) of the tile = keys 4 sg .. 4 sg + 3
-                const int key = 4 * sg + (l >> 4), phys = l & 15;
-                int64_t gk = static_cast<int64_t>(blk) * kPB + key;
-                gk = gk < nlim ? gk : nlim - 1;             // keys past the chunk are masked anyway
-                const bf16_t* src = kh + gk * kHeadDim + 8 * (phys ^ (key & 15));
-                __builtin_amdgcn_global_load_lds(src, &kt[slot][sg * 512], 16, 0, 0);
+        for (int j = 0; j < kTileLoads; ++j) {
+            const int sg = kTileLoads * w + j;
+            const bf16_t* ksrc = kh + k0 * kHeadDim + koff_l[j];
+            if (partial) {                                  // clamp: keys past the chunk are masked anyway
+                int64_t gk = k0 + key_l[j];
+                gk = gk < nlim ? gk : nlim - 1;
+                ksrc = kh + gk * kHeadDim + 8 * ((l & 15) ^ (key_l[j] & 15));
             }
-            {   // V^T: bytes [1 KB sg, +1 KB) of the tile = d rows 8 sg .. 8 sg + 7
-                const int d = 8 * sg + (l >> 3), phys = l & 7;
-                const bf16_t* src = vth + (static_cast<int64_t>(blk) * kHeadDim + d) * kPB + 8 * (phys ^ ((d >> 1) & 7));
-                __builtin_amdgcn_global_load_lds(src, &vtt[slot][sg * 512], 16, 0, 0);
-            }
+            __builtin_amdgcn_global_load_lds(ksrc, &kt[slot][sg * 512], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vth + k0 * kHeadDim + voff_l[j], &vtt[slot][sg * 512], 16, 0, 0);
         }
     };
     auto compute = [&](const StageTiles& kt, const StageTiles& vtt, int u) {
@@ -197,45 +218,57 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
         int cntr[kPRowsW];
 #pragma unroll
         for (int i = 0; i < kPRowsW; ++i) {
-            int64_t c = qpos[i] + 1 - static_cast<int64_t>(blk) * kPB;
-            c = c < kPB ? c : kPB;
-            cntr[i] = static_cast<int>(c);
-            if (((msk >> (kPWaves * i + w)) & 1u) && c > 0) act |= 1u << i;
+            cntr[i] = qpos[i] + 1 - blk * kPB;               // keys of the block at or before the row
+            if (((msk >> (kPWaves * i + w)) & 1u) && cntr[i] > 0) act |= 1u << i;
         }
         act = __builtin_amdgcn_readfirstlane(act);          // wave-uniform by construction
         if (!act) return;
+        // K fragments, kKBatch K-steps at a time (their LDS latencies overlap);
+        // lane holds K[key 16 mt + lc][32 ks + 8 lg ..]
+        f32x4_t s[kPRowsW][4];
+#pragma unroll
+        for (int i = 0; i < kPRowsW; ++i)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) s[i][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; kb += kKBatch) {
+            uint4 kf[kKBatch][4];
+#pragma unroll
+            for (int ks = 0; ks < kKBatch; ++ks)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) kf[ks][mt] = k_frag(kt, slot, 16 * mt + lc, 4 * (kb + ks) + lg);
+#pragma unroll
+            for (int i = 0; i < kPRowsW; ++i) {
+                if (!((act >> i) & 1u)) continue;
+#pragma unroll
+                for (int ks = 0; ks < kKBatch; ++ks)
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+                        s[i][mt] = mfma32(as_bf16x8(kf[ks][mt]), qf[i][kb + ks], s[i][mt]);
+            }
+        }
         bf16x8_t pf[kPRowsW][2];
 #pragma unroll
         for (int i = 0; i < kPRowsW; ++i) {
             if (!((act >> i) & 1u)) continue;
-            // S^T for row i: lane holds S[head lc][key 16 mt + 4 lg + r]
-            f32x4_t s[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) s[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-                    s[mt] = mfma32(as_bf16x8(k_frag(kt, slot, 16 * mt + lc, 4 * ks + lg)), qf[i][ks], s[mt]);
+            // raw logits; the scale (> 0) is applied to the max and inside the exp
             float lm = -INFINITY;
             if (__builtin_amdgcn_readfirstlane(cntr[i]) >= kPB) {
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        s[mt][r] *= scale_log2;
-                        lm = fmaxf(lm, s[mt][r]);
-                    }
+                    for (int r = 0; r < 4; ++r) lm = fmaxf(lm, s[i][mt][r]);
             } else {
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float x = (16 * mt + 4 * lg + r) < cntr[i] ? s[mt][r] * scale_log2 : -INFINITY;
-                        s[mt][r] = x;
+                        const float x = (16 * mt + 4 * lg + r) < cntr[i] ? s[i][mt][r] : -INFINITY;
+                        s[i][mt][r] = x;
                         lm = fmaxf(lm, x);
                     }
             }
+            lm *= scale_log2;
             // raise the reference only when some head of the row overshoots it
             if (__any(lm > mref[i] + kRescaleSlack)) {
                 float mx = fmaxf(lm, __shfl_xor(lm, 16, 64));
@@ -254,48 +287,53 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float p = fast_exp2(s[mt][r] - mref[i]);   // masked keys: 2^-inf = 0
-                    s[mt][r] = p;
+                    const float p = fast_exp2(fmaf(s[i][mt][r], scale_log2, -mref[i]));   // masked: 2^-inf = 0
+                    s[i][mt][r] = p;
                     ls += p;
                 }
             lsum[i] += ls;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 uint4 pu;
-                pu.x = pack_rne(s[2 * kk][0], s[2 * kk][1]);
-                pu.y = pack_rne(s[2 * kk][2], s[2 * kk][3]);
-                pu.z = pack_rne(s[2 * kk + 1][0], s[2 * kk + 1][1]);
-                pu.w = pack_rne(s[2 * kk + 1][2], s[2 * kk + 1][3]);
+                pu.x = pack_rne(s[i][2 * kk][0], s[i][2 * kk][1]);
+                pu.y = pack_rne(s[i][2 * kk][2], s[i][2 * kk][3]);
+                pu.z = pack_rne(s[i][2 * kk + 1][0], s[i][2 * kk + 1][1]);
+                pu.w = pack_rne(s[i][2 * kk + 1][2], s[i][2 * kk + 1][3]);
                 pf[i][kk] = as_bf16x8(pu);
             }
         }
+        // V^T fragments, kVBatch d-tiles at a time
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            const bf16x8_t v0 = as_bf16x8(vt_frag(vtt, slot, 16 * mt + lc, lg));
-            const bf16x8_t v1 = as_bf16x8(vt_frag(vtt, slot, 16 * mt + lc, 4 + lg));
+        for (int mb = 0; mb < 8; mb += kVBatch) {
+            uint4 vf[kVBatch][2];
 #pragma unroll
-            for (int i = 0; i < kPRowsW; ++i) {
-                if (!((act >> i) & 1u)) continue;
-                o[i][mt] = mfma32(v0, pf[i][0], o[i][mt]);
-                o[i][mt] = mfma32(v1, pf[i][1], o[i][mt]);
+            for (int x = 0; x < kVBatch; ++x) {
+                vf[x][0] = vt_frag(vtt, slot, 16 * (mb + x) + lc, lg);
+                vf[x][1] = vt_frag(vtt, slot, 16 * (mb + x) + lc, 4 + lg);
             }
+#pragma unroll
+            for (int x = 0; x < kVBatch; ++x)
+#pragma unroll
+                for (int i = 0; i < kPRowsW; ++i) {
+                    if (!((act >> i) & 1u)) continue;
+                    o[i][mb + x] = mfma32(as_bf16x8(vf[x][0]), pf[i][0], o[i][mb + x]);
+                    o[i][mb + x] = mfma32(as_bf16x8(vf[x][1]), pf[i][1], o[i][mb + x]);
+                }
         }
     };
-    // one group of kGroup2 blocks per stage: wait for this stage (every wave's
-    // loads, then the barrier), start the next group into the other stage, then
-    // compute this one while those loads are in flight.  The loads are waited
-    // for with vmcnt(0) only: they are not relied on to retire in issue order.
-    auto run_group = [&](StageTiles& kc, StageTiles& vc, StageTiles& kn, StageTiles& vn, int u0) {
+    // Four blocks per barrier interval: load them (both stages), wait, then
+    // compute.  Loads and compute do not overlap, but each interval holds twice
+    // the work of a double-buffered pair of two-block stages, which evens out
+    // the random share of active (row, block) pairs between the SIMDs; the
+    // wait at each barrier is set by the busiest SIMD, not by the load.
+    for (int u0 = 0; u0 < n_u; u0 += 2 * kGroup2) {
+        __syncthreads();                                    // previous blocks consumed
+        for (int x = u0; x < u0 + kGroup2 && x < n_u; ++x) issue(k_a, v_a, x);
+        for (int x = u0 + kGroup2; x < u0 + 2 * kGroup2 && x < n_u; ++x) issue(k_b, v_b, x);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        for (int x = u0 + kGroup2; x < u0 + 2 * kGroup2 && x < n_u; ++x) issue(kn, vn, x);
-        for (int u = u0; u < u0 + kGroup2 && u < n_u; ++u) compute(kc, vc, u);
-    };
-    __syncthreads();
-    for (int x = 0; x < kGroup2 && x < n_u; ++x) issue(k_a, v_a, x);
-    for (int u0 = 0; u0 < n_u; u0 += 2 * kGroup2) {
-        run_group(k_a, v_a, k_b, v_b, u0);
-        if (u0 + kGroup2 < n_u) run_group(k_b, v_b, k_a, v_a, u0 + kGroup2);
+        for (int u = u0; u < u0 + kGroup2 && u < n_u; ++u) compute(k_a, v_a, u);
+        for (int u = u0 + kGroup2; u < u0 + 2 * kGroup2 && u < n_u; ++u) compute(k_b, v_b, u);
     }
 
     // ---- epilogue: row sum over the four lanes of each head; lane holds
@@ -343,9 +381,10 @@ hipError_t launch_attn_prefill_mfma(const Shape& sh, const void* q, int rows, in
     if (e != hipSuccess) return e;
     const float scale_log2 = sh.attn_scale * 1.4426950408889634f;
     KernelTimer kt(INFV2_KERNEL_ATTN_PREFILL, st);
-    attn_prefill_mfma<<<dim3((rows + kPRows - 1) / kPRows, sh.hkv), kPThreads, 0, st>>>(
+    const int nrg = (rows + kPRows - 1) / kPRows;
+    attn_prefill_mfma<<<dim3(static_cast<unsigned>(nrg) * sh.hkv), kPThreads, 0, st>>>(
         static_cast<const bf16_t*>(q), rows, q_start, static_cast<const bf16_t*>(k), vt, kv_off,
-        idx, static_cast<bf16_t*>(out), sh.hq, sh.hkv, sh.topk, nblk, scale_log2);
+        idx, static_cast<bf16_t*>(out), sh.hq, sh.hkv, sh.topk, nblk, nrg, scale_log2);
     return hipGetLastError();
 }
 

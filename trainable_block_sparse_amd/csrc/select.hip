@@ -272,7 +272,8 @@ __global__ __launch_bounds__(256) void sel_dec_scores(
     // loads: issue them together (one memory round trip)
     float zz[kGroup];
     {
-        const float* z = logits + bg * kGroup * nc_ld + (j < nvis ? j : 0);
+        // clamped to the row, not to nvis: the address does not wait for the length
+        const float* z = logits + bg * kGroup * nc_ld + (j < nc_ld ? j : nc_ld - 1);
 #pragma unroll
         for (int h = 0; h < kGroup; ++h) zz[h] = z[h * nc_ld];
     }
