@@ -98,6 +98,31 @@ def roofline_of(times: dict, work: dict, bound: str, peak: float, unit: str, sca
             "work_per_launch": work[dom]}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCE = {"attn_decode": "attn_decode.hip", "select_logits": "select.hip",
+                 "attn_prefill": "attn_prefill.hip"}
+
+
+def source_digest(kernel: str) -> str:
+    import hashlib
+    path = os.path.join(ROOT, "trainable_block_sparse_amd", "csrc", KERNEL_SOURCE[kernel])
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE
+    counter runs, scaled by what the same counters read for a copy of known size;
+    None when no measurement exists or the kernel's source changed since."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if kernel not in KERNEL_SOURCE or rec.get("source_sha256") != source_digest(kernel):
+        return None
+    return 1024.0 * (rec["fetch_kib_per_launch"] / rec["fetch_scale"]
+                     + rec["write_kib_per_launch"] / rec["write_scale"])
+
+
 # ----------------------------------------------------------------------------- decode
 DECODE_FAMILIES = ("compress", "select_logits", "select_scores", "select_topk", "attn_decode",
                    "attn_merge")
@@ -356,6 +381,7 @@ def bench_prefill(args, torch, tbs, gh) -> dict:
     res["tflops_attn_kernel"] = useful / (kt["attn_prefill"]["us_per_step"] * 1e-6) / 1e12
     res["roofline"] = roofline_of(kt, {"attn_prefill": useful / n_attn}, "mfma", BF16_PEAK_TFLOPS,
                                   "TFLOP/s", 1e12)
+    res["roofline"]["traffic"] = measured_traffic("attn_prefill")
     res["_idx"] = gi
     res["_wl"] = wl
     return res
@@ -449,6 +475,9 @@ def main() -> int:
     ap.add_argument("--no-batched", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run 8 device-to-device copies of MIB MiB (reference kernel for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--only", choices=["decode", "prefill", "batched"], default=None,
                     help="run one workload only and print its record (for profiling)")
     args = ap.parse_args()
@@ -466,6 +495,16 @@ def main() -> int:
         return 2
     tbs.load_library()
     torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy calibration: 8 copies of {args.copy_calibration} MiB")
 
     if args.only:
         if args.only == "decode":
@@ -488,6 +527,7 @@ def main() -> int:
         log(f"batched decode: {bat['ms_per_step'] * 1e3:.1f} us/step, per call {bat['per_call_us']}")
 
     roof = main_res["roofline"]
+    roof["traffic"] = measured_traffic(roof["kernel"])
     out = {
         "metric": METRIC,
         "value": main_res["tok_per_s"],
