@@ -181,6 +181,32 @@ def test_decode_first_token_attends_itself():
     assert np.array_equal(out[0], want)
 
 
+def test_decode_batch_with_an_empty_sequence():
+    """An empty cache (length 0) in a packed batch: no blocks (all ids -1), a zero
+    output row, and the other sequences unaffected."""
+    h = _harness()
+    wl = _small(lens=[700, 0, 1, 3000], topk=8, local=2, seed=61)
+    _say("decode batch with an empty sequence: lens [700, 0, 1, 3000]")
+    dev = h.DeviceWorkload(wl)
+    dev.compress()
+    idx_t, _ = dev.select_decode()
+    out = h.from_device(dev.attn_decode(idx_t), "bf16")
+    idx = idx_t.cpu().numpy().astype(np.int64)
+    assert (idx[1] == -1).all()
+    assert not out[1].any()
+    prm = params_of(wl)
+    q = wl.q_f64()
+    cks = dev.ck_host()
+    for b in [0, 2, 3]:
+        K = wl.k_f64(b)
+        n = K.shape[1]
+        for g in range(wl.num_kv_heads):
+            rs = ref.select_row(q[b, 16 * g:16 * g + 16], cks[b][g], n - 1, prm)
+            assert not accept_selection(idx[b, g], rs).startswith("fail")
+        want = ref.attend_with_selection(q[b:b + 1], K, wl.v_f64(b), [n - 1], idx[b:b + 1], prm)
+        assert_close(out[b], want[0], "bf16", f"seq {b}")
+
+
 @pytest.mark.parametrize("cfg", [0, 1, 2, 4])
 def test_decode_configs(cfg):
     wl = make_config(cfg)
