@@ -57,6 +57,9 @@
  * group forms the 16-row side of a 16x16 MFMA tile), block_size a multiple of
  * 16 in [16, 256], 1 <= kernel_stride <= kernel_size <= 256, topk <= 1024,
  * at most 16384 blocks per sequence.  Other values return INFV2_ERR_UNSUPPORTED.
+ * bf16 inputs run on the matrix cores (prefill attention there needs
+ * block_size 64 and topk <= 128); fp32 inputs and the other bf16 prefill
+ * shapes run on vector-ALU kernels with fp32 accumulation.
  */
 #ifndef INFV2_H
 #define INFV2_H
@@ -165,9 +168,9 @@ int32_t infv2_compress_keys(const infv2_config* cfg, const void* k, const int64_
  *                each selected block (-inf if no kernel is visible in it,
  *                NaN in padding slots)
  *   ws           device workspace of ws_bytes >= infv2_workspace_bytes(op =
- *                SELECT_DECODE or SELECT_PREFILL).  It must be zero-filled
- *                before its first use; every call leaves it ready for the
- *                next one.
+ *                SELECT_DECODE or SELECT_PREFILL).  No initial contents are
+ *                needed: the call clears and writes everything it reads.
+ *                Calls that overlap in time need distinct workspaces.
  */
 int32_t infv2_select_blocks(const infv2_config* cfg, int32_t mode, const void* q, int32_t rows,
                             int64_t q_start, const void* ck, const int64_t* ck_offsets,
@@ -186,8 +189,8 @@ int32_t infv2_select_blocks(const infv2_config* cfg, int32_t mode, const void* q
  *   block_idx    device int32 [batch][Hkv][topk] from infv2_select_blocks
  *                (entries -1 are skipped)
  *   out          device, io_dtype [batch][Hq][d] (written)
- *   ws           workspace (infv2_workspace_bytes op = ATTN_DECODE), zero-filled
- *                before first use, left ready for the next call
+ *   ws           workspace (infv2_workspace_bytes op = ATTN_DECODE); no initial
+ *                contents are needed
  */
 int32_t infv2_sparse_attn_decode(const infv2_config* cfg, const void* q, const void* k,
                                  const void* v, const int64_t* kv_offsets, const int64_t* kv_lens,
@@ -205,7 +208,9 @@ int32_t infv2_sparse_attn_decode(const infv2_config* cfg, const void* q, const v
  *   kv_offsets   device int64 [2]
  *   block_idx    device int32 [rows][Hkv][topk]
  *   out          device, io_dtype [rows][Hq][d] (written)
- *   ws           workspace (op = ATTN_PREFILL; may be 0 bytes)
+ *   ws           workspace (op = ATTN_PREFILL: the V^T tiles of the prefix, rebuilt
+ *                by every call; 0 bytes, and NULL allowed, when the vector-ALU
+ *                path serves the config); no initial contents are needed
  */
 int32_t infv2_sparse_attn_prefill(const infv2_config* cfg, const void* q, int32_t rows,
                                   int64_t q_start, const void* k, const void* v,

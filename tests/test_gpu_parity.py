@@ -181,6 +181,16 @@ def test_decode_first_token_attends_itself():
     assert np.array_equal(out[0], want)
 
 
+@pytest.mark.parametrize("m", [32, 128])
+def test_other_block_sizes(m):
+    """Block sizes other than 64: decode (matrix cores, partial 64-key tiles) and
+    prefill (vector-ALU attention)."""
+    wl = _small(lens=[900, 2600], topk=6, local=2, seed=71 + m, block_size=m)
+    _run_decode(wl, label=f"decode block {m}")
+    wl = _small(mode="prefill", lens=[1300], topk=6, local=2, seed=72 + m, block_size=m)
+    _run_prefill(wl, 500, label=f"prefill block {m}")
+
+
 def test_decode_batch_with_an_empty_sequence():
     """An empty cache (length 0) in a packed batch: no blocks (all ids -1), a zero
     output row, and the other sequences unaffected."""
