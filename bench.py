@@ -154,10 +154,10 @@ def decode_kernel_bytes(wl, ck_bytes: int, n_list) -> dict:
     }
 
 
-def bench_decode(cfg_index: int, args, torch, tbs, gh, replicas: int) -> dict:
+def bench_decode(cfg_index: int, args, torch, tbs, gh, replicas: int, ck_dtype=None) -> dict:
     from synth import make_config, extra_decode_queries
     wl = make_config(cfg_index)
-    ck_dtype = args.ck_dtype
+    ck_dtype = ck_dtype or args.ck_dtype
     dev = gh.DeviceWorkload(wl, ck_dtype)
     dev.compress()
     cfg = dev.cfg
@@ -387,9 +387,9 @@ def bench_prefill(args, torch, tbs, gh) -> dict:
     return res
 
 
-def bench_batched(args, torch, tbs, gh) -> dict:
+def bench_batched(args, torch, tbs, gh, ck_dtype=None) -> dict:
     # one step reads ~160 MiB, so three replicas already keep the MALL cold
-    return bench_decode(4, args, torch, tbs, gh, replicas=min(args.replicas, 4))
+    return bench_decode(4, args, torch, tbs, gh, replicas=min(args.replicas, 4), ck_dtype=ck_dtype)
 
 
 # ----------------------------------------------------------------------------- CPU oracle
@@ -474,6 +474,8 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-batched", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ck-bf16", action="store_true",
+                    help="skip the extra decode records with bf16 compressed keys")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run 8 device-to-device copies of MIB MiB (reference kernel for "
@@ -525,6 +527,15 @@ def main() -> int:
     bat = None if args.no_batched else bench_batched(args, torch, tbs, gh)
     if bat:
         log(f"batched decode: {bat['ms_per_step'] * 1e3:.1f} us/step, per call {bat['per_call_us']}")
+    # the same decode workloads with bf16 compressed keys (the documented option)
+    alt = {}
+    if not args.no_ck_bf16 and args.ck_dtype == "fp32":
+        alt["decode_128k_ck_bf16"] = bench_decode(2, args, torch, tbs, gh, replicas=args.replicas,
+                                                  ck_dtype="bf16")
+        if not args.no_batched:
+            alt["batched_decode_16x_ck_bf16"] = bench_batched(args, torch, tbs, gh, ck_dtype="bf16")
+        for k2, r2 in alt.items():
+            log(f"{k2}: {r2['ms_per_step'] * 1e3:.1f} us/step")
 
     roof = main_res["roofline"]
     roof["traffic"] = measured_traffic(roof["kernel"])
@@ -549,6 +560,9 @@ def main() -> int:
         out["prefill_32k"] = {k: v for k, v in pre.items() if not k.startswith("_")}
     if bat:
         out["batched_decode_16x"] = bat
+    for k2, r2 in alt.items():
+        out[k2] = {x: r2[x] for x in ("workload", "batch", "ms_per_step", "tok_per_s", "hbm_gbps_step",
+                                      "per_call_us", "kernels", "bytes_per_step", "roofline", "parity")}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline_decode(args.cpu_seconds)
