@@ -85,22 +85,6 @@ __device__ __forceinline__ float sum16(float v) {
     return v;
 }
 
-// inclusive prefix sum over the 256 threads of a block (4 waves); `tmp` holds 4 words
-__device__ __forceinline__ uint32_t block_incl_scan256(uint32_t v, uint32_t* tmp) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t u = __shfl_up(v, o, 64);
-        if (lane >= o) v += u;
-    }
-    if (lane == 63) tmp[wid] = v;
-    __syncthreads();
-    uint32_t add = 0;
-    for (int w = 0; w < wid; ++w) add += tmp[w];
-    __syncthreads();
-    return v + add;
-}
-
 }  // namespace infv2
 
 namespace infv2 {
