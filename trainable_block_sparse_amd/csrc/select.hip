@@ -594,36 +594,46 @@ __global__ __launch_bounds__(256) void sel_pre_mfma(
         }
     }
 
+    // compressed-key tile loads run one tile ahead, in registers: the loads of
+    // tile t+1 are in flight while tile t is computed from LDS
+    uint4 pk[4];                  // bf16 keys: one 16-byte chunk per x
+    float4 pa[4], pb[4];          // fp32 keys: two 16-byte halves per x
+    auto fetch = [&](int64_t jt) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int e = t + 256 * x, r = e >> 4, c = e & 15;
+            if (kCkBf16) {
+                const bf16_t* src = static_cast<const bf16_t*>(ck) + cbase;
+                pk[x] = (jt + r < vmax) ? ldg16(src + (jt + r) * kHeadDim + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
+            } else {
+                const float* src = static_cast<const float*>(ck) + cbase;
+                pa[x] = make_float4(0.f, 0.f, 0.f, 0.f);
+                pb[x] = pa[x];
+                if (jt + r < vmax) {
+                    pa[x] = *reinterpret_cast<const float4*>(src + (jt + r) * kHeadDim + 8 * c);
+                    pb[x] = *reinterpret_cast<const float4*>(src + (jt + r) * kHeadDim + 8 * c + 4);
+                }
+            }
+        }
+    };
+    if (vmax > 0) fetch(0);
     for (int64_t j0 = 0; j0 < vmax; j0 += kPreTileK) {
         __syncthreads();
         // stage 64 kernels; chunk c of kernel r at c ^ (r & 15)
-        if (kCkBf16) {
-            const bf16_t* src = static_cast<const bf16_t*>(ck) + cbase;
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int e = t + 256 * x, r = e >> 4, c = e & 15;
-                uint4 v = make_uint4(0u, 0u, 0u, 0u);
-                if (j0 + r < vmax) v = ldg16(src + (j0 + r) * kHeadDim + 8 * c);
-                *reinterpret_cast<uint4*>(&ck_hi[r * kHeadDim + 8 * (c ^ (r & 15))]) = v;
-            }
-        } else {
-            const float* src = static_cast<const float*>(ck) + cbase;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int e = t + 256 * x, r = e >> 4, c = e & 15;
-                float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-                if (j0 + r < vmax) {
-                    a = *reinterpret_cast<const float4*>(src + (j0 + r) * kHeadDim + 8 * c);
-                    b = *reinterpret_cast<const float4*>(src + (j0 + r) * kHeadDim + 8 * c + 4);
-                }
-                const float xv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        for (int x = 0; x < 4; ++x) {
+            const int e = t + 256 * x, r = e >> 4, c = e & 15;
+            const int off = r * kHeadDim + 8 * (c ^ (r & 15));
+            if (kCkBf16) {
+                *reinterpret_cast<uint4*>(&ck_hi[off]) = pk[x];
+            } else {
+                const float xv[8] = {pa[x].x, pa[x].y, pa[x].z, pa[x].w, pb[x].x, pb[x].y, pb[x].z, pb[x].w};
                 float hi[8], lo[8];
 #pragma unroll
                 for (int e8 = 0; e8 < 8; ++e8) {
                     hi[e8] = bf16_to_f32(f32_to_bf16(xv[e8]));
                     lo[e8] = xv[e8] - hi[e8];
                 }
-                const int off = r * kHeadDim + 8 * (c ^ (r & 15));
                 *reinterpret_cast<uint4*>(&ck_hi[off]) =
                     make_uint4(pack_exact(hi[0], hi[1]), pack_exact(hi[2], hi[3]), pack_exact(hi[4], hi[5]), pack_exact(hi[6], hi[7]));
                 *reinterpret_cast<uint4*>(&ck_lo[off]) =
@@ -631,6 +641,7 @@ __global__ __launch_bounds__(256) void sel_pre_mfma(
             }
         }
         __syncthreads();
+        if (j0 + kPreTileK < vmax) fetch(j0 + kPreTileK);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             f32x4_t z[4];
@@ -654,17 +665,29 @@ __global__ __launch_bounds__(256) void sel_pre_mfma(
             for (int i = 0; i < 4; ++i) {
                 const bool ok = jk < vis[i];
                 if (kPass == 1) {
+                    // running (max, sum) with a lazy max: the reference moves only
+                    // when some lane's logit exceeds it by more than 2^8, so the
+                    // common path is one exp per logit and no divergence
+                    float x[4];
+                    bool over = false;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        if (!ok) continue;
-                        const float x = z[i][r] * zscale;
-                        if (x > mr[i][r]) {
-                            lr[i][r] = lr[i][r] * fast_exp2(mr[i][r] - x) + 1.f;
-                            mr[i][r] = x;
-                        } else {
-                            lr[i][r] += fast_exp2(x - mr[i][r]);
+                        x[r] = ok ? z[i][r] * zscale : -INFINITY;
+                        over |= x[r] > mr[i][r] + 8.f;
+                    }
+                    if (__any(over)) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float mn = fmaxf(mr[i][r], x[r]);
+                            if (mn != -INFINITY) {
+                                lr[i][r] = lr[i][r] * fast_exp2(mr[i][r] - mn);   // 2^-inf = 0
+                                mr[i][r] = mn;
+                            }
                         }
                     }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        lr[i][r] += (x[r] == -INFINITY) ? 0.f : fast_exp2(x[r] - mr[i][r]);
                 } else {
                     float acc = 0.f;
 #pragma unroll
