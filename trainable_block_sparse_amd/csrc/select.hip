@@ -743,13 +743,15 @@ __global__ __launch_bounds__(256) void sel_pre_mfma(
 }
 
 // ------------------------------------------------------------------ prefill, top-k
-template <int kPer>
-__global__ __launch_bounds__(256) void sel_pre_topk(int64_t q_start, int hkv, int m, int topk,
-                                                    int init, int local, int64_t nblk_max, int per,
-                                                    const uint32_t* __restrict__ keys,
-                                                    int32_t* __restrict__ idx,
-                                                    float* __restrict__ score) {
-    __shared__ TopkSmem<256> sm;
+// kThreads = 64 (one wave per row: no cross-wave barriers, every (row, KV head)
+// block resident at once) unless a row has too many blocks for 16 per lane.
+template <int kThreads, int kPer>
+__global__ __launch_bounds__(kThreads) void sel_pre_topk(int64_t q_start, int hkv, int m, int topk,
+                                                         int init, int local, int64_t nblk_max,
+                                                         int per, const uint32_t* __restrict__ keys,
+                                                         int32_t* __restrict__ idx,
+                                                         float* __restrict__ score) {
+    __shared__ TopkSmem<kThreads> sm;
     const int row = blockIdx.x, g = blockIdx.y;
     const size_t rg = static_cast<size_t>(row) * hkv + g;
     int64_t c = (q_start + row) / m;
@@ -761,8 +763,8 @@ __global__ __launch_bounds__(256) void sel_pre_topk(int64_t q_start, int hkv, in
     uint32_t key[kPer];
 #pragma unroll
     for (int u = 0; u < kPer; ++u) key[u] = u < cnt ? gk[jb + u] : 0u;
-    block_topk_regs<256>(key, jb, cnt, static_cast<int>(c), topk, init, local, idx + rg * topk,
-                         score ? score + rg * topk : nullptr, sm);
+    block_topk_regs<kThreads>(key, jb, cnt, static_cast<int>(c), topk, init, local, idx + rg * topk,
+                              score ? score + rg * topk : nullptr, sm);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -787,8 +789,18 @@ static void launch_topk_dec(const Shape& sh, int batch, int64_t nblk_max, const 
 
 static void launch_topk_pre(const Shape& sh, int rows, int64_t q_start, int64_t nblk_max,
                             const uint32_t* keys, int32_t* idx, float* score, hipStream_t st) {
+    const int per64 = topk_per(nblk_max, 64);
+    if (per64 <= 16) {
+#define INFV2_L(P) sel_pre_topk<64, P><<<dim3(rows, sh.hkv), 64, 0, st>>>( \
+        q_start, sh.hkv, sh.m, sh.topk, sh.init, sh.local, nblk_max, per64, keys, idx, score)
+        if (per64 <= 2) INFV2_L(2);
+        else if (per64 <= 8) INFV2_L(8);
+        else INFV2_L(16);
+#undef INFV2_L
+        return;
+    }
     const int per = topk_per(nblk_max, 256);
-#define INFV2_L(P) sel_pre_topk<P><<<dim3(rows, sh.hkv), 256, 0, st>>>( \
+#define INFV2_L(P) sel_pre_topk<256, P><<<dim3(rows, sh.hkv), 256, 0, st>>>( \
         q_start, sh.hkv, sh.m, sh.topk, sh.init, sh.local, nblk_max, per, keys, idx, score)
     INFV2_TOPK_DISPATCH(per, INFV2_L);
 #undef INFV2_L
