@@ -191,6 +191,18 @@ def test_other_block_sizes(m):
     _run_prefill(wl, 500, label=f"prefill block {m}")
 
 
+def test_large_topk():
+    """Top-k at the supported maximum in decode (1024 blocks: 256 attention
+    splits, a wide top-k window) and a bf16 prefill with top-k 160 (above what
+    the matrix-core prefill attention takes, so the vector-ALU path serves it)."""
+    wl = _small(lens=[1024 * 64 + 77, 1500 * 64], hkv=1, topk=1024, local=4, seed=81, n_planted=6)
+    _run_decode(wl, label="decode top-k 1024")
+    wl = _small(mode="prefill", lens=[12000], topk=160, local=4, seed=82, n_planted=6)
+    rng = np.random.default_rng(82)
+    pos = sorted(set(rng.integers(0, 12000, 40).tolist()) | {0, 10239, 10240, 11999})
+    _run_prefill(wl, 4000, positions=pos, label="prefill top-k 160")
+
+
 def test_decode_batch_with_an_empty_sequence():
     """An empty cache (length 0) in a packed batch: no blocks (all ids -1), a zero
     output row, and the other sequences unaffected."""
