@@ -270,6 +270,83 @@ def bench_decode(cfg_index: int, args, torch, tbs, gh, replicas: int, ck_dtype=N
     return res
 
 
+def bench_decode_loop(args, torch, tbs, gh) -> dict:
+    """Decode loop at 128K: each step appends one token per sequence to its cache
+    (infv2_append_kv: K/V rows and the compressed key the token completes), then
+    selects and attends.  The caches have room for the appended tokens; lengths
+    advance on every step, graph replays included."""
+    from synth import make_config, extra_decode_queries
+    wl = make_config(2)
+    dev = gh.DeviceWorkload(wl, args.ck_dtype)
+    cfg = dev.cfg
+    B, hkv, d = wl.batch, wl.num_kv_heads, wl.head_dim
+    n0 = int(wl.lens[0])
+    R = args.replicas
+    room = args.warmup + 2 * args.steps + 64     # every append of every timing pass fits
+    cap = n0 + room
+    # caches of capacity n0 + room holding the n0-token prefix
+    def padded(t):
+        x = torch.zeros((hkv, cap, d), dtype=t.dtype, device="cuda")
+        x[:, :n0] = t.view(hkv, n0, d)
+        return x.view(-1)
+    Ks = [padded(dev.k) for _ in range(R)]
+    Vs = [padded(dev.v) for _ in range(R)]
+    nc_cap = num_kernels(cap, wl.kernel_size, wl.kernel_stride)
+    ck_off = torch.tensor([0, nc_cap], dtype=torch.int64, device="cuda")
+    kv_off = torch.tensor([0, cap], dtype=torch.int64, device="cuda")
+    ck0 = torch.zeros(hkv * nc_cap * d, dtype=dev.ck.dtype, device="cuda")
+    ncur = num_kernels(n0, wl.kernel_size, wl.kernel_stride)
+    ck0.view(hkv, nc_cap, d)[:, :ncur] = dev.ck.view(hkv, -1, d)[:, :ncur]
+    CKs = [ck0.clone() for _ in range(R)]
+    lens = [torch.tensor([n0], dtype=torch.int64, device="cuda") for _ in range(R)]
+    qs = gh.to_device(extra_decode_queries(wl, R))
+    kn = qs[:, :, :hkv].contiguous()                     # any [B][Hkv][d] rows serve as new K/V
+    vn = qs[:, :, hkv:2 * hkv].contiguous()
+    idx = torch.empty((B, hkv, cfg.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(dev.q)
+    ws_sel = dev.ws(tbs.OP_SELECT_DECODE, B, B, cap)
+    ws_att = dev.ws(tbs.OP_ATTN_DECODE, B, B, cap)
+
+    def step(r):
+        tbs.infv2_append_kv(cfg, kn[r], vn[r], Ks[r], Vs[r], kv_off, lens[r], ck_off, CKs[r], B)
+        tbs.infv2_select_blocks(cfg, tbs.INFV2_MODE_DECODE, qs[r], B, 0, CKs[r], ck_off, kv_off,
+                                lens[r], B, cap, idx, None, ws_sel)
+        tbs.infv2_sparse_attn_decode(cfg, qs[r], Ks[r], Vs[r], kv_off, lens[r], B, cap, idx, out,
+                                     ws_att)
+
+    T = Timer(torch)
+    for t in range(args.warmup):
+        step(t % R)
+    torch.cuda.synchronize()
+    s0 = T.event()
+    for t in range(args.steps):
+        step(t % R)
+    s1 = T.event()
+    torch.cuda.synchronize()
+    eager_ms = s0.elapsed_time(s1) / args.steps
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for r in range(R):
+                step(r)
+    torch.cuda.current_stream().wait_stream(side)
+    reps = max(1, args.steps // R)
+    g0 = T.event()
+    for _ in range(reps):
+        g.replay()
+    g1 = T.event()
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / (reps * R)
+    kt = kernel_times(tbs, torch, lambda t: step(t % R), min(args.steps, 40), ("append",))
+    final_len = int(lens[0].item())
+    return {"workload": "decode_loop_bf16_128k", "batch": B, "start_len": n0, "final_len_replica0": final_len,
+            "ms_per_step_eager": eager_ms, "ms_per_step_graph": graph_ms,
+            "tok_per_s": B / (graph_ms * 1e-3), "append_us_per_launch": kt["append"]["us_per_launch"],
+            "note": "graph of one step per replica; lengths advance on every replay"}
+
+
 def decode_spot_parity(wl, dev, qs, outs, idx, select, attn, ck_dtype, torch, gh) -> str:
     from oracle import infv2_ref as ref
     from tests.parity import accept_selection, assert_close
@@ -474,6 +551,7 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-batched", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-loop", action="store_true", help="skip the append + select + attend loop record")
     ap.add_argument("--no-ck-bf16", action="store_true",
                     help="skip the extra decode records with bf16 compressed keys")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -527,6 +605,9 @@ def main() -> int:
     bat = None if args.no_batched else bench_batched(args, torch, tbs, gh)
     if bat:
         log(f"batched decode: {bat['ms_per_step'] * 1e3:.1f} us/step, per call {bat['per_call_us']}")
+    loop = None if args.no_loop else bench_decode_loop(args, torch, tbs, gh)
+    if loop:
+        log(f"decode loop 128K (append + select + attend): {loop['ms_per_step_graph'] * 1e3:.1f} us/step")
     # the same decode workloads with bf16 compressed keys (the documented option)
     alt = {}
     if not args.no_ck_bf16 and args.ck_dtype == "fp32":
@@ -560,6 +641,8 @@ def main() -> int:
         out["prefill_32k"] = {k: v for k, v in pre.items() if not k.startswith("_")}
     if bat:
         out["batched_decode_16x"] = bat
+    if loop:
+        out["decode_loop_128k"] = loop
     for k2, r2 in alt.items():
         out[k2] = {x: r2[x] for x in ("workload", "batch", "ms_per_step", "tok_per_s", "hbm_gbps_step",
                                       "per_call_us", "kernels", "bytes_per_step", "roofline", "parity")}

@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define INFV2_ABI_VERSION 2
+#define INFV2_ABI_VERSION 3
 
 typedef enum infv2_status {
     INFV2_OK = 0,
@@ -145,6 +145,29 @@ int32_t infv2_compress_keys(const infv2_config* cfg, const void* k, const int64_
                             int64_t max_new, void* ck, void* stream);
 
 /*
+ * infv2_append_kv -- the step before decoding attention: one new token per
+ * sequence enters the cache, and the compressed keys follow incrementally
+ * ("Semantic kernels": kernel j covers [j*s, j*s + p); with complete kernels
+ * only, the token at position n completes kernel (n + 1 - p) / s exactly when
+ * n + 1 >= p and s divides n + 1 - p, i.e. one new kernel every s tokens).
+ *
+ * For every sequence b with n = kv_lens[b] < capacity: writes k_new[b] and
+ * v_new[b] at position n of its cache region, stores the compressed key of
+ * the kernel the token completes (same float64 mean and single rounding as
+ * infv2_compress_keys; skipped if ck_offsets leave no room for it), and sets
+ * kv_lens[b] = n + 1.  A sequence whose cache is full is left unchanged.
+ *
+ *   k_new, v_new device, io_dtype [batch][Hkv][d]
+ *   k, v         device, io_dtype, packed caches (see Layouts), updated in place
+ *   kv_offsets   device int64 [batch+1] (capacities)
+ *   kv_lens      device int64 [batch], read and advanced in place
+ *   ck_offsets, ck   as for infv2_compress_keys (ck updated in place)
+ */
+int32_t infv2_append_kv(const infv2_config* cfg, const void* k_new, const void* v_new, void* k,
+                        void* v, const int64_t* kv_offsets, int64_t* kv_lens,
+                        const int64_t* ck_offsets, void* ck, int32_t batch, void* stream);
+
+/*
  * infv2_select_blocks -- step 1b, paragraphs "Semantic kernels" (eqs.
  * r_kernel, r_block), "Query group sharing" (eq. r_group), "Top-K
  * implementation and the LSE bottleneck" (two passes: LogSumExp, then
@@ -166,7 +189,10 @@ int32_t infv2_compress_keys(const infv2_config* cfg, const void* k, const int64_
  *   block_idx    device int32 [rows][Hkv][topk] (written)
  *   block_score  device float [rows][Hkv][topk] or NULL: the block score of
  *                each selected block (-inf if no kernel is visible in it,
- *                NaN in padding slots)
+ *                NaN in padding slots).  With NULL and every row shorter than
+ *                topk*block_size (max_len, or q_start + rows, <= topk*m) the
+ *                selection is dense by definition and no score is computed:
+ *                only the ids are written and ws is not touched.
  *   ws           device workspace of ws_bytes >= infv2_workspace_bytes(op =
  *                SELECT_DECODE or SELECT_PREFILL).  No initial contents are
  *                needed: the call clears and writes everything it reads.
@@ -257,7 +283,8 @@ typedef enum infv2_kernel {
     INFV2_KERNEL_ATTN_MERGE = 6,        /* decode: merge of the partials */
     INFV2_KERNEL_ATTN_PREFILL = 7,      /* prefill: attention over the selected blocks */
     INFV2_KERNEL_VT_BUILD = 8,          /* prefill: transposed V tiles */
-    INFV2_KERNEL_COUNT = 9
+    INFV2_KERNEL_APPEND = 9,            /* decode: cache append + incremental compressed key */
+    INFV2_KERNEL_COUNT = 10
 } infv2_kernel;
 
 int32_t infv2_timing_start(int32_t kernel);

@@ -122,6 +122,25 @@ def compress_keys(K: np.ndarray, p: int, s: int, ck_dtype: str = "fp32") -> np.n
     return round_to_storage(ck, ck_dtype)
 
 
+def append_token(K: np.ndarray, V: np.ndarray, n: int, k_new: np.ndarray, v_new: np.ndarray,
+                 ck: np.ndarray, p: int, s: int, ck_dtype: str = "fp32") -> int:
+    """One decode step's cache update, in place: the new token's key and value
+    go to position n, and the kernel the token completes (if any) gets its
+    compressed key.  Returns the new length n + 1.
+
+    [IV2 Semantic kernels] with the complete-kernel reading: kernel j^ covers
+    [j^ s, j^ s + p), so the token at position n completes kernel
+    (n + 1 - p) / s exactly when n + 1 >= p and s divides n + 1 - p.
+    K, V: [Hkv][cap][d]; k_new, v_new: [Hkv][d]; ck: [Hkv][ccap][d].
+    """
+    K[:, n, :] = k_new
+    V[:, n, :] = v_new
+    if n + 1 >= p and (n + 1 - p) % s == 0:
+        jh = (n + 1 - p) // s
+        ck[:, jh, :] = round_to_storage(K[:, jh * s: jh * s + p, :].sum(axis=1) / p, ck_dtype)
+    return n + 1
+
+
 # ---------------------------------------------------------------------------
 # step 2: which kernels touch which block
 # ---------------------------------------------------------------------------

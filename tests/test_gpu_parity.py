@@ -167,6 +167,89 @@ def test_compress_incremental_token_by_token(ck_dtype):
         assert np.array_equal(cks[b], want), f"sequence {b}"
 
 
+@pytest.mark.parametrize("io,ck_dtype", [("bf16", "fp32"), ("bf16", "bf16"), ("fp32", "fp32")])
+def test_append_kv_token_by_token(io, ck_dtype):
+    """Decode-loop cache growth through infv2_append_kv: caches that start with a
+    prefix, then one appended token per call, end up equal to the full K/V bit
+    for bit, with compressed keys equal to the oracle's and lengths advanced; a
+    full cache is left unchanged."""
+    import trainable_block_sparse_amd as tbs
+    h = _harness()
+    wl = _small(lens=[400, 97, 1000], io=io, topk=8, local=2, seed=91)
+    _say(f"append_kv io={io} ck={ck_dtype}")
+    dev = h.DeviceWorkload(wl, ck_dtype)
+    final = wl.lens.astype(np.int64)
+    start = np.array([300, 10, 937], dtype=np.int64)
+    offs = wl.kv_offsets
+    hkv, d = wl.num_kv_heads, wl.head_dim
+    # caches hold only the prefix; compressed keys of the prefix
+    k_full, v_full = dev.k.clone(), dev.v.clone()
+    for b in range(wl.batch):
+        base, cap = int(offs[b]) * hkv * d, int(final[b])
+        kb = dev.k[base: base + hkv * cap * d].view(hkv, cap, d)
+        vb = dev.v[base: base + hkv * cap * d].view(hkv, cap, d)
+        kb[:, int(start[b]):].zero_()
+        vb[:, int(start[b]):].zero_()
+    lens = torch.tensor(start, dtype=torch.int64, device="cuda")
+    dev.compress(kv_lens=lens)
+    steps = int((final - start).max()) + 2            # two extra calls hit full caches
+    for step in range(steps):
+        pos = np.minimum(start + step, final - 1)     # rows fed when a cache is already full are ignored
+        kn = torch.stack([k_full[int(offs[b]) * hkv * d:].view(-1)[: hkv * int(final[b]) * d]
+                          .view(hkv, int(final[b]), d)[:, int(pos[b])] for b in range(wl.batch)])
+        vn = torch.stack([v_full[int(offs[b]) * hkv * d:].view(-1)[: hkv * int(final[b]) * d]
+                          .view(hkv, int(final[b]), d)[:, int(pos[b])] for b in range(wl.batch)])
+        tbs.infv2_append_kv(dev.cfg, kn.contiguous(), vn.contiguous(), dev.k, dev.v, dev.kv_offsets,
+                            lens, dev.ck_offsets, dev.ck, wl.batch)
+    torch.cuda.synchronize()
+    assert lens.cpu().numpy().tolist() == final.tolist()
+    assert torch.equal(dev.k, k_full) and torch.equal(dev.v, v_full)
+    cks = dev.ck_host()
+    for b in range(wl.batch):
+        assert np.array_equal(cks[b], ref.compress_keys(wl.k_f64(b), wl.kernel_size,
+                                                        wl.kernel_stride, ck_dtype)), f"seq {b}"
+
+
+def test_dense_rows_without_scores():
+    """Rows shorter than k*m with no block scores requested: the ids-only path
+    gives the dense selection and the attention equals the oracle's."""
+    import trainable_block_sparse_amd as tbs
+    h = _harness()
+    wl = _small(lens=[500, 1, 512, 64], topk=8, local=2, seed=92)
+    _say("dense decode rows without scores")
+    dev = h.DeviceWorkload(wl)
+    dev.compress()
+    B = wl.batch
+    idx = torch.full((B, 2, 8), 7, dtype=torch.int32, device="cuda")
+    tbs.infv2_select_blocks(dev.cfg, tbs.INFV2_MODE_DECODE, dev.q, B, 0, dev.ck, dev.ck_offsets,
+                            dev.kv_offsets, dev.kv_lens, B, dev.max_len, idx, None,
+                            dev.ws(tbs.OP_SELECT_DECODE, B, B, dev.max_len))
+    out = h.from_device(dev.attn_decode(idx), "bf16")
+    got = idx.cpu().numpy()
+    prm = params_of(wl)
+    q = wl.q_f64()
+    for b in range(B):
+        n = int(wl.lens[b])
+        c = (n - 1) // 64
+        want = np.array([r if r <= c else -1 for r in range(8)])
+        assert (got[b] == want).all(), (b, got[b])
+        ref_out = ref.attend_with_selection(q[b:b + 1], wl.k_f64(b), wl.v_f64(b), [n - 1],
+                                            got[b:b + 1].astype(np.int64), prm)[0]
+        assert_close(out[b], ref_out, "bf16", f"dense seq {b}")
+    _say("dense prefill rows without scores")
+    wp = _small(mode="prefill", lens=[700], topk=12, local=2, seed=93)
+    devp = h.DeviceWorkload(wp)
+    devp.compress()
+    idxp = torch.full((700, 2, 12), 7, dtype=torch.int32, device="cuda")
+    tbs.infv2_select_blocks(devp.cfg, tbs.INFV2_MODE_PREFILL, devp.q, 700, 0, devp.ck,
+                            devp.ck_offsets, devp.kv_offsets, None, 1, 700, idxp, None,
+                            devp.ws(tbs.OP_SELECT_PREFILL, 700, 1, 700))
+    gp = idxp.cpu().numpy()
+    for i in [0, 63, 64, 400, 699]:
+        c = i // 64
+        assert (gp[i] == np.array([r if r <= c else -1 for r in range(12)])).all(), i
+
+
 def test_decode_first_token_attends_itself():
     h = _harness()
     wl = _small(lens=[1], topk=4, local=1, seed=27)

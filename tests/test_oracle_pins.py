@@ -412,3 +412,30 @@ def test_bf16_compressed_keys_round_the_exact_mean_once():
     ck = ref.compress_keys(K, 8, 4, "bf16")
     assert np.array_equal(ck, ref.round_to_storage(exact, "bf16"))
     assert np.max(np.abs(ck - exact) / np.maximum(np.abs(exact), 1e-30)) <= 2.0 ** -8
+
+
+def test_append_token_by_token_equals_compressing_the_whole_cache():
+    # the cache after n appends equals the cache holding the n tokens, and its
+    # compressed keys equal a fresh compression of those tokens (bit for bit)
+    rng = np.random.default_rng(17)
+    hkv, n, d, p, s = 2, 150, 8, 8, 4
+    Kfull = rng.standard_normal((hkv, n, d))
+    Vfull = rng.standard_normal((hkv, n, d))
+    for ck_dtype in ["fp32", "bf16"]:
+        K = np.zeros((hkv, n + 5, d))
+        V = np.zeros_like(K)
+        ck = np.full((hkv, ref.num_kernels(n, p, s) + 3, d), np.nan)
+        ln = 0
+        completed = []
+        for t in range(n):
+            before = np.isnan(ck[:, :, 0]).sum()
+            ln = ref.append_token(K, V, ln, Kfull[:, t], Vfull[:, t], ck, p, s, ck_dtype)
+            if np.isnan(ck[:, :, 0]).sum() < before:
+                completed.append(t)
+        assert ln == n
+        assert np.array_equal(K[:, :n], Kfull) and np.array_equal(V[:, :n], Vfull)
+        nc = ref.num_kernels(n, p, s)
+        assert np.array_equal(ck[:, :nc], ref.compress_keys(Kfull, p, s, ck_dtype))
+        assert np.isnan(ck[:, nc:]).all()
+        # kernel j completes at token j s + p - 1
+        assert completed == [j * s + p - 1 for j in range(nc)]

@@ -23,7 +23,7 @@ INFV2_MODE_DECODE, INFV2_MODE_PREFILL = 0, 1
 OP_COMPRESS, OP_SELECT_DECODE, OP_SELECT_PREFILL, OP_ATTN_DECODE, OP_ATTN_PREFILL = range(5)
 # kernel families for infv2_timing_start (infv2_kernel in infv2.h)
 KERNELS = ("compress", "select_logits", "select_scores", "select_prefill", "select_topk",
-           "attn_decode", "attn_merge", "attn_prefill", "vt_build")
+           "attn_decode", "attn_merge", "attn_prefill", "vt_build", "append")
 KERNEL_ID = {name: i for i, name in enumerate(KERNELS)}
 STATUS = {0: "INFV2_OK", 1: "INFV2_ERR_NULL", 2: "INFV2_ERR_SHAPE", 3: "INFV2_ERR_UNSUPPORTED",
           4: "INFV2_ERR_WORKSPACE", 5: "INFV2_ERR_DEVICE"}
@@ -88,6 +88,7 @@ def load_library(path: str = LIB_PATH):
     cfgp = ctypes.POINTER(_CConfig)
     sig = {
         "infv2_compress_keys": (i32, [cfgp, vp, vp, vp, vp, vp, i32, i64, i64, vp, vp]),
+        "infv2_append_kv": (i32, [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp]),
         "infv2_select_blocks": (i32, [cfgp, i32, vp, i32, i64, vp, vp, vp, vp, i32, i64, vp, vp,
                                       vp, sz, vp]),
         "infv2_sparse_attn_decode": (i32, [cfgp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, sz, vp]),
@@ -106,7 +107,7 @@ def load_library(path: str = LIB_PATH):
     return lib
 
 
-EXPORTED = ("infv2_compress_keys", "infv2_select_blocks", "infv2_sparse_attn_decode",
+EXPORTED = ("infv2_compress_keys", "infv2_append_kv", "infv2_select_blocks", "infv2_sparse_attn_decode",
             "infv2_sparse_attn_prefill", "infv2_workspace_bytes", "infv2_num_kernels",
             "infv2_status_str", "infv2_abi_version", "infv2_timing_start", "infv2_timing_stop")
 
@@ -180,6 +181,14 @@ def infv2_compress_keys(cfg: Config, k, kv_offsets, kv_lens, ck_offsets, ck_begi
     _check(load_library().infv2_compress_keys(
         ctypes.byref(c), _ptr(k), _ptr(kv_offsets), _ptr(kv_lens), _ptr(ck_offsets),
         _ptr(ck_begin), batch, max_len, max_new, _ptr(ck), _stream(stream)), "infv2_compress_keys")
+
+
+def infv2_append_kv(cfg: Config, k_new, v_new, k, v, kv_offsets, kv_lens, ck_offsets, ck,
+                    batch: int, stream=None) -> None:
+    c = cfg.to_c()
+    _check(load_library().infv2_append_kv(ctypes.byref(c), _ptr(k_new), _ptr(v_new), _ptr(k), _ptr(v),
+                                          _ptr(kv_offsets), _ptr(kv_lens), _ptr(ck_offsets), _ptr(ck),
+                                          batch, _stream(stream)), "infv2_append_kv")
 
 
 def infv2_select_blocks(cfg: Config, mode: int, q, rows: int, q_start: int, ck, ck_offsets,

@@ -123,6 +123,74 @@ __global__ __launch_bounds__(256) void compress_few_kernel(
     else static_cast<float*>(ck_out)[dst] = static_cast<float>(mean);
 }
 
+// One decode step's cache update: one block per sequence (all its KV heads, so
+// the length is read by every thread before it is advanced).  Writes the new
+// token's K and V rows at position n = kv_lens[b], then, if the token completes
+// kernel j = (n + 1 - p) / s, its compressed key with the same float64 sum and
+// single rounding as compress_kernel (the new row is taken from k_new, the
+// p - 1 older rows from the cache), and finally kv_lens[b] = n + 1.  A full
+// cache (n >= capacity) or a compressed-key region without room for kernel j
+// leaves the sequence unchanged.
+template <typename Tin, bool kCkBf16>
+__global__ __launch_bounds__(256) void append_kv_kernel(
+    const Tin* __restrict__ k_new, const Tin* __restrict__ v_new, Tin* __restrict__ k,
+    Tin* __restrict__ v, const int64_t* __restrict__ kv_off, int64_t* __restrict__ kv_lens,
+    const int64_t* __restrict__ ck_off, void* __restrict__ ck_out, int hkv, int p, int s) {
+    __shared__ double part[8][kHeadDim];
+    const int b = blockIdx.x, t = threadIdx.x;
+    const int64_t o0 = kv_off[b], cap = kv_off[b + 1] - o0;
+    const int64_t n = kv_lens[b];
+    if (n < 0 || n >= cap) return;                       // uniform: full cache, no change
+    const int64_t c0 = ck_off[b], ccap = ck_off[b + 1] - c0;
+    const bool completes = n + 1 >= p && (n + 1 - p) % s == 0;
+    const int64_t j = completes ? (n + 1 - p) / s : -1;
+    const bool store_ck = completes && j < ccap;
+    const int grp = t >> 5, col = (t & 31) * 4;
+    for (int g = 0; g < hkv; ++g) {
+        const Tin* kn = k_new + (static_cast<int64_t>(b) * hkv + g) * kHeadDim;
+        const Tin* vn = v_new + (static_cast<int64_t>(b) * hkv + g) * kHeadDim;
+        const int64_t row0 = (o0 * hkv + static_cast<int64_t>(g) * cap) * kHeadDim;
+        if (t < kHeadDim) k[row0 + n * kHeadDim + t] = kn[t];
+        else v[row0 + n * kHeadDim + (t - kHeadDim)] = vn[t - kHeadDim];
+        if (!store_ck) continue;                         // uniform
+        // rows j s .. j s + p - 1; the last one is the new token
+        double acc0 = 0.0, acc1 = 0.0, acc2 = 0.0, acc3 = 0.0;
+        for (int r = grp; r < p; r += 8) {
+            float x[4];
+            if (r == p - 1) load4(kn + col, x);
+            else load4(k + row0 + (j * s + r) * kHeadDim + col, x);
+            acc0 += x[0]; acc1 += x[1]; acc2 += x[2]; acc3 += x[3];
+        }
+        part[grp][col] = acc0; part[grp][col + 1] = acc1; part[grp][col + 2] = acc2; part[grp][col + 3] = acc3;
+        __syncthreads();
+        if (t < kHeadDim) {
+            double sum = 0.0;
+#pragma unroll
+            for (int g2 = 0; g2 < 8; ++g2) sum += part[g2][t];
+            const double mean = sum / static_cast<double>(p);
+            const int64_t dst = ((c0 * hkv + static_cast<int64_t>(g) * ccap) + j) * kHeadDim + t;
+            if (kCkBf16) static_cast<bf16_t*>(ck_out)[dst] = f64_to_bf16(mean);
+            else static_cast<float*>(ck_out)[dst] = static_cast<float>(mean);
+        }
+        __syncthreads();                                 // part reused by the next head
+    }
+    __syncthreads();                                     // every thread has read kv_lens[b]
+    if (t == 0) kv_lens[b] = n + 1;
+}
+
+hipError_t launch_append_kv(const Shape& sh, const void* k_new, const void* v_new, void* k,
+                            void* v, const int64_t* kv_off, int64_t* kv_lens,
+                            const int64_t* ck_off, void* ck, int batch, hipStream_t st) {
+    KernelTimer kt(INFV2_KERNEL_APPEND, st);
+#define INFV2_APPEND(TIN, CKB) append_kv_kernel<TIN, CKB><<<dim3(batch), 256, 0, st>>>( \
+        static_cast<const TIN*>(k_new), static_cast<const TIN*>(v_new), static_cast<TIN*>(k), \
+        static_cast<TIN*>(v), kv_off, kv_lens, ck_off, ck, sh.hkv, sh.p, sh.s)
+    if (sh.io_bf16) { if (sh.ck_bf16) INFV2_APPEND(bf16_t, true); else INFV2_APPEND(bf16_t, false); }
+    else { if (sh.ck_bf16) INFV2_APPEND(float, true); else INFV2_APPEND(float, false); }
+#undef INFV2_APPEND
+    return hipGetLastError();
+}
+
 hipError_t launch_compress(const Shape& sh, const void* k, const int64_t* kv_off,
                            const int64_t* kv_lens, const int64_t* ck_off, const int64_t* ck_begin,
                            int batch, int64_t max_new, void* ck, hipStream_t st) {

@@ -115,6 +115,19 @@ int32_t infv2_compress_keys(const infv2_config* c, const void* k, const int64_t*
                                             static_cast<hipStream_t>(stream)));
 }
 
+int32_t infv2_append_kv(const infv2_config* c, const void* k_new, const void* v_new, void* k,
+                        void* v, const int64_t* kv_offsets, int64_t* kv_lens,
+                        const int64_t* ck_offsets, void* ck, int32_t batch, void* stream) {
+    int32_t st = check_config(c);
+    if (st != INFV2_OK) return st;
+    if (!k_new || !v_new || !k || !v || !kv_offsets || !kv_lens || !ck_offsets || !ck)
+        return INFV2_ERR_NULL;
+    if (batch < 1) return INFV2_ERR_SHAPE;
+    return status_of(infv2::launch_append_kv(make_shape(c), k_new, v_new, k, v, kv_offsets,
+                                             kv_lens, ck_offsets, ck, batch,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 int32_t infv2_select_blocks(const infv2_config* c, int32_t mode, const void* q, int32_t rows,
                             int64_t q_start, const void* ck, const int64_t* ck_offsets,
                             const int64_t* kv_offsets, const int64_t* kv_lens, int32_t batch,

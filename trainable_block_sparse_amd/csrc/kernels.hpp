@@ -57,6 +57,10 @@ hipError_t launch_compress(const Shape& sh, const void* k, const int64_t* kv_off
                            const int64_t* kv_lens, const int64_t* ck_off, const int64_t* ck_begin,
                            int batch, int64_t max_new, void* ck, hipStream_t st);
 
+hipError_t launch_append_kv(const Shape& sh, const void* k_new, const void* v_new, void* k,
+                            void* v, const int64_t* kv_off, int64_t* kv_lens,
+                            const int64_t* ck_off, void* ck, int batch, hipStream_t st);
+
 hipError_t launch_select_decode(const Shape& sh, const void* q, const void* ck,
                                 const int64_t* ck_off, const int64_t* kv_off,
                                 const int64_t* kv_lens, int batch, int64_t max_len,

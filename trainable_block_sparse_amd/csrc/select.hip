@@ -23,6 +23,7 @@
 //   sel_pre_mfma<2> the same logits again: group score, block max.
 //   (sel_pre_lse / sel_pre_scores: the vector-ALU versions for fp32 queries)
 //   sel_pre_topk    one block per (row, KV head).
+// Rows shorter than k*m without requested scores: sel_dense_ids only.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "topk.hpp"
@@ -767,6 +768,44 @@ __global__ __launch_bounds__(kThreads) void sel_pre_topk(int64_t q_start, int hk
                               score ? score + rg * topk : nullptr, sm);
 }
 
+// ------------------------------------------------------------------ dense rows
+// Every row shorter than k*m selects all its blocks ("Initial and local tokens
+// always selected": below k*m tokens the method is exactly dense attention).
+// When no block scores are requested, the ids need no scoring at all: one
+// thread per (row, KV head, slot).  Decode row b ends at kv_lens[b] - 1;
+// prefill row r sits at q_start + r.
+__global__ __launch_bounds__(256) void sel_dense_ids(int mode_decode, int rows, int64_t q_start,
+                                                     const int64_t* __restrict__ kv_off,
+                                                     const int64_t* __restrict__ kv_lens, int hkv,
+                                                     int m, int topk, int64_t nblk_max,
+                                                     int32_t* __restrict__ idx) {
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t total = static_cast<int64_t>(rows) * hkv * topk;
+    if (e >= total) return;
+    const int slot = static_cast<int>(e % topk);
+    const int row = static_cast<int>(e / (static_cast<int64_t>(hkv) * topk));
+    int64_t c;
+    if (mode_decode) {
+        const int64_t cap = kv_off[row + 1] - kv_off[row];
+        int64_t n = kv_lens ? kv_lens[row] : cap;
+        n = n < cap ? n : cap;
+        c = n > 0 ? (n - 1) / m : -1;
+    } else {
+        c = (q_start + row) / m;
+    }
+    c = c < nblk_max - 1 ? c : nblk_max - 1;
+    idx[e] = slot <= c ? slot : -1;
+}
+
+static void launch_dense_ids(const Shape& sh, int mode_decode, int rows, int64_t q_start,
+                             const int64_t* kv_off, const int64_t* kv_lens, int64_t nblk_max,
+                             int32_t* idx, hipStream_t st) {
+    const int64_t total = static_cast<int64_t>(rows) * sh.hkv * sh.topk;
+    KernelTimer kt(INFV2_KERNEL_SELECT_TOPK, st);
+    sel_dense_ids<<<dim3(static_cast<unsigned>((total + 255) / 256)), 256, 0, st>>>(
+        mode_decode, rows, q_start, kv_off, kv_lens, sh.hkv, sh.m, sh.topk, nblk_max, idx);
+}
+
 // ------------------------------------------------------------------ launchers
 // keys per thread: the smallest register-array size that covers nblk_max / 256
 #define INFV2_TOPK_DISPATCH(per, LAUNCH) \
@@ -843,6 +882,10 @@ hipError_t launch_select_decode(const Shape& sh, const void* q, const void* ck,
                                 const int64_t* kv_lens, int batch, int64_t max_len,
                                 int32_t* idx, float* score, void* ws, hipStream_t st) {
     const SelectDecodeWs w = select_decode_ws(sh, batch, max_len);
+    if (!score && max_len <= static_cast<int64_t>(sh.topk) * sh.m) {   // every row dense
+        launch_dense_ids(sh, 1, batch, 0, kv_off, kv_lens, w.nblk_max, idx, st);
+        return hipGetLastError();
+    }
     char* base = static_cast<char*>(ws);
     if (sh.io_bf16) {
         if (sh.ck_bf16) dec_launch<bf16_t, bf16_t>(sh, q, ck, ck_off, kv_off, kv_lens, batch, w, base, idx, score, st);
@@ -902,6 +945,10 @@ hipError_t launch_select_prefill(const Shape& sh, const void* q, int rows, int64
                                  const void* ck, const int64_t* ck_off, int64_t max_len,
                                  int32_t* idx, float* score, void* ws, hipStream_t st) {
     const SelectPrefillWs w = select_prefill_ws(sh, rows, max_len);
+    if (!score && q_start + rows <= static_cast<int64_t>(sh.topk) * sh.m) {   // every row dense
+        launch_dense_ids(sh, 0, rows, q_start, nullptr, nullptr, w.nblk_max, idx, st);
+        return hipGetLastError();
+    }
     char* base = static_cast<char*>(ws);
     if (sh.io_bf16) {
         if (sh.ck_bf16) pre_launch<bf16_t, bf16_t>(sh, q, rows, q_start, ck, ck_off, w, base, idx, score, st);
