@@ -464,6 +464,60 @@ def bench_prefill(args, torch, tbs, gh) -> dict:
     return res
 
 
+def bench_varlen_prefill(args, torch, tbs, gh) -> dict:
+    """Serving-style prefill: 8 sequences of 4K-16K tokens (lengths drawn by seed)
+    prefilled whole in one varlen call each for compress, selection and attention."""
+    from synth import make_workload, f32_to_bf16_bits
+    rng = np.random.default_rng(12)
+    lens = rng.integers(4096, 16384, size=8, endpoint=True).tolist()
+    wl = make_workload(name="varlen_prefill_bf16_8x4k-16k", mode="decode", io_dtype="bf16", lens=lens,
+                       num_q_heads=32, num_kv_heads=2, topk=64, init_blocks=1, local_blocks=4,
+                       n_planted=32, seed=12)
+    dev = gh.DeviceWorkload(wl, args.ck_dtype)
+    cfg = dev.cfg
+    rows = np.array(lens, dtype=np.int32)
+    starts = np.zeros(len(lens), dtype=np.int64)
+    T = int(rows.sum())
+    q = gh.to_device(f32_to_bf16_bits(rng.standard_normal((T, 32, 128), dtype=np.float32)))
+    idx = torch.empty((T, 2, 64), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    mx = int(rows.max())
+    ws_s = dev.ws(tbs.OP_SELECT_PREFILL, mx, 1, mx)
+    ws_a = dev.ws(tbs.OP_ATTN_PREFILL, mx, 1, mx)
+    Timer_ = Timer(torch)
+
+    def run():
+        e0 = Timer_.event()
+        tbs.infv2_compress_keys(cfg, dev.k, dev.kv_offsets, dev.kv_lens, dev.ck_offsets, None,
+                                wl.batch, dev.max_len, -1, dev.ck)
+        e1 = Timer_.event()
+        tbs.infv2_select_blocks_varlen(cfg, q, rows, starts, dev.ck, dev.ck_offsets, dev.kv_offsets,
+                                       idx, None, ws_s)
+        e2 = Timer_.event()
+        tbs.infv2_sparse_attn_prefill_varlen(cfg, q, rows, starts, dev.k, dev.v, dev.kv_offsets, idx,
+                                             out, ws_a)
+        e3 = Timer_.event()
+        return e0, e1, e2, e3
+
+    run()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(max(1, args.prefill_reps)):
+        ev = run()
+        torch.cuda.synchronize()
+        times.append([a.elapsed_time(b) for a, b in zip(ev[:-1], ev[1:])])
+    tm = np.median(np.array(times), axis=0)
+    gi = idx.cpu().numpy()
+    pos = np.concatenate([np.arange(n) for n in lens])
+    nn = np.concatenate([np.full(n, n) for n in lens])
+    tok = attended_tokens(gi, pos, nn, 64)
+    useful = float(4 * 128 * 16 * tok.sum())
+    return {"workload": wl.name, "lens": lens, "rows": T, "compress_ms": float(tm[0]),
+            "select_ms": float(tm[1]), "attn_ms": float(tm[2]), "total_ms": float(tm.sum()),
+            "useful_attn_flops": useful, "tflops_attn": useful / (tm[2] * 1e-3) / 1e12,
+            "tflops_path": useful / (tm.sum() * 1e-3) / 1e12}
+
+
 def bench_batched(args, torch, tbs, gh, ck_dtype=None) -> dict:
     # one step reads ~160 MiB, so three replicas already keep the MALL cold
     return bench_decode(4, args, torch, tbs, gh, replicas=min(args.replicas, 4), ck_dtype=ck_dtype)
@@ -605,6 +659,10 @@ def main() -> int:
     bat = None if args.no_batched else bench_batched(args, torch, tbs, gh)
     if bat:
         log(f"batched decode: {bat['ms_per_step'] * 1e3:.1f} us/step, per call {bat['per_call_us']}")
+    varlen = None if args.no_prefill else bench_varlen_prefill(args, torch, tbs, gh)
+    if varlen:
+        log(f"varlen prefill 8 x 4K-16K: attn {varlen['attn_ms']:.2f} ms, total {varlen['total_ms']:.2f} ms, "
+            f"{varlen['tflops_attn']:.1f} TFLOPS")
     loop = None if args.no_loop else bench_decode_loop(args, torch, tbs, gh)
     if loop:
         log(f"decode loop 128K (append + select + attend): {loop['ms_per_step_graph'] * 1e3:.1f} us/step")
@@ -643,6 +701,8 @@ def main() -> int:
         out["batched_decode_16x"] = bat
     if loop:
         out["decode_loop_128k"] = loop
+    if varlen:
+        out["prefill_varlen_8x4k-16k"] = varlen
     for k2, r2 in alt.items():
         out[k2] = {x: r2[x] for x in ("workload", "batch", "ms_per_step", "tok_per_s", "hbm_gbps_step",
                                       "per_call_us", "kernels", "bytes_per_step", "roofline", "parity")}

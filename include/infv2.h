@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define INFV2_ABI_VERSION 3
+#define INFV2_ABI_VERSION 4
 
 typedef enum infv2_status {
     INFV2_OK = 0,
@@ -242,6 +242,34 @@ int32_t infv2_sparse_attn_prefill(const infv2_config* cfg, const void* q, int32_
                                   int64_t q_start, const void* k, const void* v,
                                   const int64_t* kv_offsets, const int32_t* block_idx, void* out,
                                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Varlen prefill: several sequences in one call (serving-style prefill).  The
+ * rows of the call are packed sequence after sequence: rows_per_seq[b] rows of
+ * sequence b, the first at position q_start_per_seq[b] ("Design principles
+ * summary": every query token selects its own blocks, so sequences are
+ * independent).  Both arrays are HOST arrays of `batch` entries, checked
+ * before anything is launched; everything else is as for the single-sequence
+ * calls, with kv_offsets / ck_offsets describing all `batch` sequences ([batch+1]).
+ * Compressed keys up to n_c(q_start_per_seq[b] + rows_per_seq[b]) must be
+ * present (infv2_compress_keys over the batch).  The workspace must hold the
+ * largest single-sequence need: infv2_workspace_bytes(op, rows = max rows,
+ * batch = 1, max_len = max (q_start + rows)).  Sequences run one after another
+ * on the stream through the single-sequence kernels.
+ *
+ *   q, block_idx, block_score, out   packed over all rows of the call
+ */
+int32_t infv2_select_blocks_varlen(const infv2_config* cfg, const void* q, int32_t batch,
+                                   const int32_t* rows_per_seq, const int64_t* q_start_per_seq,
+                                   const void* ck, const int64_t* ck_offsets,
+                                   const int64_t* kv_offsets, int32_t* block_idx,
+                                   float* block_score, void* ws, size_t ws_bytes, void* stream);
+int32_t infv2_sparse_attn_prefill_varlen(const infv2_config* cfg, const void* q, int32_t batch,
+                                         const int32_t* rows_per_seq,
+                                         const int64_t* q_start_per_seq, const void* k,
+                                         const void* v, const int64_t* kv_offsets,
+                                         const int32_t* block_idx, void* out, void* ws,
+                                         size_t ws_bytes, void* stream);
 
 /* Workspace size in bytes for operation `op` (infv2_op) at the given sizes. */
 int32_t infv2_workspace_bytes(const infv2_config* cfg, int32_t op, int32_t rows, int32_t batch,

@@ -149,3 +149,33 @@ def test_timing_session_state_machine(lib):
     assert tbs.infv2_timing_stop() == (0.0, 0)
     hdr = open(HEADER).read()
     assert int(re.search(r"INFV2_KERNEL_COUNT = (\d+)", hdr).group(1)) == len(tbs.KERNELS)
+
+
+def test_varlen_prefill_and_append_validation(lib):
+    import numpy as np
+    cfg = tbs.Config()
+    c = _c(cfg)
+    rows = np.array([100, 0, 300], dtype=np.int32)
+    starts = np.array([0, 50, 1000], dtype=np.int64)
+    R, S = rows.ctypes.data, starts.ctypes.data
+    need = max(tbs.infv2_workspace_bytes(cfg, tbs.OP_SELECT_PREFILL, int(r), 1, int(s + r))
+               for r, s in zip(rows, starts) if r > 0)
+    sel = lib.infv2_select_blocks_varlen
+    assert sel(c, FAKE, 3, None, S, FAKE, FAKE, FAKE, FAKE, None, FAKE, need, None) == ENULL
+    assert sel(c, FAKE, 0, R, S, FAKE, FAKE, FAKE, FAKE, None, FAKE, need, None) == ESHAPE
+    assert sel(c, FAKE, 3, R, S, FAKE, FAKE, FAKE, FAKE, None, FAKE, need - 1, None) == EWS
+    bad = np.array([100, -1, 300], dtype=np.int32)
+    assert sel(c, FAKE, 3, bad.ctypes.data, S, FAKE, FAKE, FAKE, FAKE, None, FAKE, need, None) == ESHAPE
+    far = np.array([0, 0, 16385 * 64], dtype=np.int64)
+    assert sel(c, FAKE, 3, R, far.ctypes.data, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40,
+               None) == EUNSUP
+    zero = np.zeros(3, dtype=np.int32)
+    assert sel(c, FAKE, 3, zero.ctypes.data, S, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == OK
+    att = lib.infv2_sparse_attn_prefill_varlen
+    need_a = max(tbs.infv2_workspace_bytes(cfg, tbs.OP_ATTN_PREFILL, int(r), 1, int(s + r))
+                 for r, s in zip(rows, starts) if r > 0)
+    assert att(c, FAKE, 3, R, S, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need_a - 1, None) == EWS
+    assert att(c, FAKE, 3, R, S, None, FAKE, FAKE, FAKE, FAKE, FAKE, need_a, None) == ENULL
+    app = lib.infv2_append_kv
+    assert app(c, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 2, None) == ENULL
+    assert app(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == ESHAPE

@@ -435,6 +435,68 @@ def test_selection_with_massive_ties():
     _run_prefill(wl, 1500, label="prefill all-equal scores")
 
 
+def test_varlen_prefill_equals_per_sequence_calls():
+    """Serving-style prefill: three sequences, each with a chunk of rows starting
+    mid-sequence, in one varlen call.  Selections and outputs equal the
+    single-sequence calls bit for bit and the oracle on sampled rows."""
+    import trainable_block_sparse_amd as tbs
+    from synth import f32_to_bf16_bits
+    h = _harness()
+    wl = _small(lens=[5000, 1200, 9000], topk=16, local=4, seed=101)
+    _say("varlen prefill: 3 sequences, chunks (2000@3000, 700@500, 3000@6000)")
+    dev = h.DeviceWorkload(wl)
+    dev.compress()
+    starts = np.array([3000, 500, 6000], dtype=np.int64)
+    rows = np.array([2000, 700, 3000], dtype=np.int32)
+    rng = np.random.default_rng(101)
+    qf = rng.standard_normal((int(rows.sum()), wl.num_q_heads, wl.head_dim), dtype=np.float32)
+    qbits = f32_to_bf16_bits(qf)
+    q = h.to_device(qbits)
+    cfg, hkv, k = dev.cfg, wl.num_kv_heads, 16
+    T = int(rows.sum())
+    idx_v = torch.empty((T, hkv, k), dtype=torch.int32, device="cuda")
+    out_v = torch.empty_like(q)
+    max_len = int((starts + rows).max())
+    ws_s = dev.ws(tbs.OP_SELECT_PREFILL, int(rows.max()), 1, max_len)
+    ws_a = torch.zeros(max(256, tbs.infv2_workspace_bytes(cfg, tbs.OP_ATTN_PREFILL, int(rows.max()), 1,
+                                                         max_len)), dtype=torch.uint8, device="cuda")
+    tbs.infv2_select_blocks_varlen(cfg, q, rows, starts, dev.ck, dev.ck_offsets, dev.kv_offsets,
+                                   idx_v, None, ws_s)
+    tbs.infv2_sparse_attn_prefill_varlen(cfg, q, rows, starts, dev.k, dev.v, dev.kv_offsets, idx_v,
+                                         out_v, ws_a)
+    torch.cuda.synchronize()
+    r0 = 0
+    prm = params_of(wl)
+    for b in range(3):
+        r1 = r0 + int(rows[b])
+        idx_s = torch.empty((int(rows[b]), hkv, k), dtype=torch.int32, device="cuda")
+        out_s = torch.empty((int(rows[b]), wl.num_q_heads, wl.head_dim), dtype=q.dtype, device="cuda")
+        nb = int(starts[b]) + int(rows[b])
+        tbs.infv2_select_blocks(cfg, tbs.INFV2_MODE_PREFILL, q[r0:r1], int(rows[b]), int(starts[b]),
+                                dev.ck, dev.ck_offsets[b:], dev.kv_offsets[b:], None, 1, nb, idx_s,
+                                None, ws_s)
+        tbs.infv2_sparse_attn_prefill(cfg, q[r0:r1], int(rows[b]), int(starts[b]), dev.k, dev.v,
+                                      dev.kv_offsets[b:], idx_s, out_s, ws_a)
+        torch.cuda.synchronize()
+        assert torch.equal(idx_v[r0:r1], idx_s), f"seq {b}: selection"
+        assert torch.equal(out_v[r0:r1], out_s), f"seq {b}: output"
+        # oracle on a few rows of the chunk
+        K = wl.k_f64(b)
+        ck = dev.ck_host()[b]
+        qrows = h.from_device(q[r0:r1], "bf16")
+        picks = [0, int(rows[b]) // 2, int(rows[b]) - 1]
+        gi = idx_v[r0:r1].cpu().numpy().astype(np.int64)
+        for loc in picks:
+            i = int(starts[b]) + loc
+            for g in range(hkv):
+                rs = ref.select_row(qrows[loc, 16 * g:16 * g + 16], ck[g], i, prm)
+                assert not accept_selection(gi[loc, g], rs).startswith("fail"), (b, loc, g)
+        want = ref.attend_with_selection(qrows[picks], K, wl.v_f64(b), [int(starts[b]) + x for x in picks],
+                                         gi[picks], prm)
+        assert_close(h.from_device(out_v[r0:r1], "bf16")[picks], want, "bf16", f"varlen seq {b}")
+        r0 = r1
+
+
 def test_decode_equals_last_prefill_row():
     h = _harness()
     wl = _small(mode="prefill", lens=[1500], topk=8, local=2, seed=34)

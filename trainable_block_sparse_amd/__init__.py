@@ -89,6 +89,9 @@ def load_library(path: str = LIB_PATH):
     sig = {
         "infv2_compress_keys": (i32, [cfgp, vp, vp, vp, vp, vp, i32, i64, i64, vp, vp]),
         "infv2_append_kv": (i32, [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp]),
+        "infv2_select_blocks_varlen": (i32, [cfgp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "infv2_sparse_attn_prefill_varlen": (i32, [cfgp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                                   vp]),
         "infv2_select_blocks": (i32, [cfgp, i32, vp, i32, i64, vp, vp, vp, vp, i32, i64, vp, vp,
                                       vp, sz, vp]),
         "infv2_sparse_attn_decode": (i32, [cfgp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, sz, vp]),
@@ -108,7 +111,8 @@ def load_library(path: str = LIB_PATH):
 
 
 EXPORTED = ("infv2_compress_keys", "infv2_append_kv", "infv2_select_blocks", "infv2_sparse_attn_decode",
-            "infv2_sparse_attn_prefill", "infv2_workspace_bytes", "infv2_num_kernels",
+            "infv2_sparse_attn_prefill", "infv2_select_blocks_varlen",
+            "infv2_sparse_attn_prefill_varlen", "infv2_workspace_bytes", "infv2_num_kernels",
             "infv2_status_str", "infv2_abi_version", "infv2_timing_start", "infv2_timing_stop")
 
 
@@ -133,6 +137,10 @@ def _stream(stream) -> Optional[int]:
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _check(st: int, where: str) -> None:
@@ -181,6 +189,36 @@ def infv2_compress_keys(cfg: Config, k, kv_offsets, kv_lens, ck_offsets, ck_begi
     _check(load_library().infv2_compress_keys(
         ctypes.byref(c), _ptr(k), _ptr(kv_offsets), _ptr(kv_lens), _ptr(ck_offsets),
         _ptr(ck_begin), batch, max_len, max_new, _ptr(ck), _stream(stream)), "infv2_compress_keys")
+
+
+def _host_arrays(rows_per_seq, q_start_per_seq):
+    """Host int32 / int64 arrays (kept alive by the caller's frame)."""
+    import numpy as np
+    r = np.ascontiguousarray(rows_per_seq, dtype=np.int32)
+    s = np.ascontiguousarray(q_start_per_seq, dtype=np.int64)
+    if r.shape != s.shape or r.ndim != 1:
+        raise ValueError("rows_per_seq and q_start_per_seq must be 1-D of the same length")
+    return r, s
+
+
+def infv2_select_blocks_varlen(cfg: Config, q, rows_per_seq, q_start_per_seq, ck, ck_offsets,
+                               kv_offsets, block_idx, block_score, ws, stream=None) -> None:
+    c = cfg.to_c()
+    r, s = _host_arrays(rows_per_seq, q_start_per_seq)
+    _check(load_library().infv2_select_blocks_varlen(
+        ctypes.byref(c), _ptr(q), int(r.shape[0]), r.ctypes.data, s.ctypes.data, _ptr(ck),
+        _ptr(ck_offsets), _ptr(kv_offsets), _ptr(block_idx), _ptr(block_score), _ptr(ws),
+        _nbytes(ws), _stream(stream)), "infv2_select_blocks_varlen")
+
+
+def infv2_sparse_attn_prefill_varlen(cfg: Config, q, rows_per_seq, q_start_per_seq, k, v,
+                                     kv_offsets, block_idx, out, ws, stream=None) -> None:
+    c = cfg.to_c()
+    r, s = _host_arrays(rows_per_seq, q_start_per_seq)
+    _check(load_library().infv2_sparse_attn_prefill_varlen(
+        ctypes.byref(c), _ptr(q), int(r.shape[0]), r.ctypes.data, s.ctypes.data, _ptr(k), _ptr(v),
+        _ptr(kv_offsets), _ptr(block_idx), _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream)),
+        "infv2_sparse_attn_prefill_varlen")
 
 
 def infv2_append_kv(cfg: Config, k_new, v_new, k, v, kv_offsets, kv_lens, ck_offsets, ck,

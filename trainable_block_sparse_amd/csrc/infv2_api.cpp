@@ -194,3 +194,97 @@ int32_t infv2_sparse_attn_prefill(const infv2_config* c, const void* q, int32_t 
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- varlen prefill
+// Several sequences per call (serving-style prefill).  Each sequence's rows run
+// through the single-sequence path with its offsets advanced: kv_offsets + b
+// and ck_offsets + b describe sequence b alone.  Every host array is checked
+// before the first launch.
+
+namespace {
+
+int32_t check_varlen(const infv2_config* c, int32_t batch, const int32_t* rows,
+                     const int64_t* q_start, int32_t op, size_t ws_bytes, const void* ws) {
+    if (!rows || !q_start) return INFV2_ERR_NULL;
+    if (batch < 1) return INFV2_ERR_SHAPE;
+    size_t need = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+        if (rows[b] < 0 || q_start[b] < 0) return INFV2_ERR_SHAPE;
+        const int32_t st = check_len(c, q_start[b] + rows[b]);
+        if (st != INFV2_OK) return st;
+        if (rows[b] == 0) continue;
+        const size_t nb = ws_bytes_for(c, op, rows[b], 1, q_start[b] + rows[b]);
+        need = nb > need ? nb : need;
+    }
+    if (need > 0 && (!ws || ws_bytes < need)) return INFV2_ERR_WORKSPACE;
+    return INFV2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t infv2_select_blocks_varlen(const infv2_config* c, const void* q, int32_t batch,
+                                   const int32_t* rows_per_seq, const int64_t* q_start_per_seq,
+                                   const void* ck, const int64_t* ck_offsets,
+                                   const int64_t* kv_offsets, int32_t* block_idx,
+                                   float* block_score, void* ws, size_t ws_bytes, void* stream) {
+    int32_t st = check_config(c);
+    if (st != INFV2_OK) return st;
+    if (!q || !ck || !ck_offsets || !kv_offsets || !block_idx) return INFV2_ERR_NULL;
+    if ((st = check_varlen(c, batch, rows_per_seq, q_start_per_seq, INFV2_OP_SELECT_PREFILL,
+                           ws_bytes, ws)) != INFV2_OK)
+        return st;
+    const Shape sh = make_shape(c);
+    const size_t qrow = static_cast<size_t>(c->num_q_heads) * c->head_dim *
+                        (c->io_dtype == INFV2_BF16 ? 2 : 4);
+    const size_t irow = static_cast<size_t>(c->num_kv_heads) * c->topk;
+    int64_t r0 = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+        const int32_t rows = rows_per_seq[b];
+        if (rows > 0) {
+            const hipError_t e = infv2::launch_select_prefill(
+                sh, static_cast<const char*>(q) + r0 * qrow, rows, q_start_per_seq[b], ck,
+                ck_offsets + b, q_start_per_seq[b] + rows, block_idx + r0 * irow,
+                block_score ? block_score + r0 * irow : nullptr, ws,
+                static_cast<hipStream_t>(stream));
+            if (e != hipSuccess) return INFV2_ERR_DEVICE;
+        }
+        r0 += rows;
+    }
+    return INFV2_OK;
+}
+
+int32_t infv2_sparse_attn_prefill_varlen(const infv2_config* c, const void* q, int32_t batch,
+                                         const int32_t* rows_per_seq,
+                                         const int64_t* q_start_per_seq, const void* k,
+                                         const void* v, const int64_t* kv_offsets,
+                                         const int32_t* block_idx, void* out, void* ws,
+                                         size_t ws_bytes, void* stream) {
+    int32_t st = check_config(c);
+    if (st != INFV2_OK) return st;
+    if (!q || !k || !v || !kv_offsets || !block_idx || !out) return INFV2_ERR_NULL;
+    if ((st = check_varlen(c, batch, rows_per_seq, q_start_per_seq, INFV2_OP_ATTN_PREFILL,
+                           ws_bytes, ws)) != INFV2_OK)
+        return st;
+    const Shape sh = make_shape(c);
+    const size_t qrow = static_cast<size_t>(c->num_q_heads) * c->head_dim *
+                        (c->io_dtype == INFV2_BF16 ? 2 : 4);
+    const size_t irow = static_cast<size_t>(c->num_kv_heads) * c->topk;
+    int64_t r0 = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+        const int32_t rows = rows_per_seq[b];
+        if (rows > 0) {
+            const hipError_t e = infv2::launch_attn_prefill(
+                sh, static_cast<const char*>(q) + r0 * qrow, rows, q_start_per_seq[b], k, v,
+                kv_offsets + b, block_idx + r0 * irow, static_cast<char*>(out) + r0 * qrow, ws,
+                static_cast<hipStream_t>(stream));
+            if (e != hipSuccess) return INFV2_ERR_DEVICE;
+        }
+        r0 += rows;
+    }
+    return INFV2_OK;
+}
+
+}  // extern "C"
+
