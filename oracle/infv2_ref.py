@@ -30,7 +30,9 @@ Readings taken where the pages are silent or garbled:
 
 Every function here is pinned by tests/test_oracle_pins.py against closed
 forms, invariants, a brute-force loop implementation (oracle/brute.py) and an
-independent dense attention (oracle/dense_ref.py).
+independent dense attention (oracle/dense_ref.py); the backward functions are
+pinned by central differences of the forward, by autograd of dense causal
+attention when every block is selected, and by the softmax invariants.
 """
 from __future__ import annotations
 
@@ -352,3 +354,88 @@ def attend_with_selection(q_rows: np.ndarray, K: np.ndarray, V: np.ndarray,
             qg = q_rows[r, g * G:(g + 1) * G]
             out[r, g * G:(g + 1) * G] = attend_row(qg, K[g], V[g], int(i), np.asarray(sel[r, g]), prm)[0]
     return out
+
+
+# ---------------------------------------------------------------------------
+# backward of step 7: training through the sparse attention
+# ---------------------------------------------------------------------------
+def attend_row_grad(qg: np.ndarray, Kg: np.ndarray, Vg: np.ndarray, i: int, sel: np.ndarray,
+                    prm: Params, dog: np.ndarray):
+    """Gradients of one row's attention (the group's heads) for an upstream gradient dog [G][d].
+
+    [IV2 Training-time considerations] and [IV2 Why mean pooling]: top-k is not
+    differentiable and no gradient passes through the selection, so the selected
+    set is a constant here and the compressed keys, which only feed the
+    selection, receive none; K and V receive gradient only through the
+    attention of stage 2.  With a = scale * q K_T^T, P = softmax(a) per head and
+    o = P V_T, the chain rule gives
+        dV_T = P^T dO,   dP = dO V_T^T,   dA = P * (dP - rowsum(P * dP)),
+        dq = scale * dA K_T,   dK_T = scale * dA^T q.
+    Returns (dq [G][d], T, dK_T [|T|][d], dV_T [|T|][d], lse [G]); a row with no
+    visible selected token has output 0 and every gradient 0.
+    """
+    n = Kg.shape[0]
+    T = selected_tokens(sel, i, n, prm.block_size)
+    G, d = qg.shape
+    if T.size == 0:
+        return (np.zeros((G, d)), T, np.zeros((0, d)), np.zeros((0, d)),
+                np.full(G, NEG_INF))
+    kt, vt = Kg[T], Vg[T]
+    a = prm.scale * (qg @ kt.T)                  # [G][|T|]
+    amax = a.max(axis=1)
+    lse = amax + np.log(np.exp(a - amax[:, None]).sum(axis=1))
+    prob = np.exp(a - lse[:, None])
+    dv_t = prob.T @ dog                          # [|T|][d]
+    dprob = dog @ vt.T                           # [G][|T|]
+    da = prob * (dprob - (prob * dprob).sum(axis=1, keepdims=True))
+    dq = prm.scale * (da @ kt)
+    dk_t = prm.scale * (da.T @ qg)
+    return dq, T, dk_t, dv_t, lse
+
+
+def attention_backward(q_rows: np.ndarray, K: np.ndarray, V: np.ndarray, positions: Sequence[int],
+                       sel: np.ndarray, prm: Params, dout: np.ndarray):
+    """Gradients of sum(dout * attend_with_selection(q_rows, K, V, positions, sel)).
+
+    q_rows, dout [R][Hq][d]; K, V [Hkv][n][d]; sel [R][Hkv][k].  Contributions
+    of every row to a token's dK / dV are summed.  Returns (dQ [R][Hq][d],
+    dK [Hkv][n][d], dV [Hkv][n][d], lse [R][Hq]).
+    """
+    G, hkv = prm.group, prm.num_kv_heads
+    dQ = np.zeros(q_rows.shape)
+    dK = np.zeros(K.shape)
+    dV = np.zeros(V.shape)
+    lse = np.zeros(q_rows.shape[:2])
+    for r, i in enumerate(positions):
+        for g in range(hkv):
+            hs = slice(g * G, (g + 1) * G)
+            dq, T, dk_t, dv_t, l = attend_row_grad(q_rows[r, hs], K[g], V[g], int(i),
+                                                   np.asarray(sel[r, g]), prm, dout[r, hs])
+            dQ[r, hs] = dq
+            dK[g, T] += dk_t
+            dV[g, T] += dv_t
+            lse[r, hs] = l
+    return dQ, dK, dV, lse
+
+
+def block_grad(q_rows: np.ndarray, K: np.ndarray, V: np.ndarray, positions: Sequence[int],
+               sel: np.ndarray, prm: Params, dout: np.ndarray, g: int, j: int):
+    """dK and dV of the tokens of block j of KV head g only, summed over the rows
+    that selected it (the same chain rule as attend_row_grad).  Cheaper than
+    attention_backward when a few blocks of a long sequence are checked.
+    Returns (dK [m'][d], dV [m'][d]) for tokens j*m .. min((j+1)*m, n) - 1."""
+    G, m = prm.group, prm.block_size
+    n = K.shape[1]
+    t0, t1 = j * m, min((j + 1) * m, n)
+    dk = np.zeros((t1 - t0, K.shape[2]))
+    dv = np.zeros((t1 - t0, V.shape[2]))
+    hs = slice(g * G, (g + 1) * G)
+    for r, i in enumerate(positions):
+        if j not in set(np.asarray(sel[r, g]).tolist()) or t0 > i:
+            continue
+        dq, T, dk_t, dv_t, _ = attend_row_grad(q_rows[r, hs], K[g], V[g], int(i),
+                                               np.asarray(sel[r, g]), prm, dout[r, hs])
+        mask = (T >= t0) & (T < t1)
+        dk[T[mask] - t0] += dk_t[mask]
+        dv[T[mask] - t0] += dv_t[mask]
+    return dk, dv

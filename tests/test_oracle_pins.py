@@ -439,3 +439,120 @@ def test_append_token_by_token_equals_compressing_the_whole_cache():
         assert np.isnan(ck[:, nc:]).all()
         # kernel j completes at token j s + p - 1
         assert completed == [j * s + p - 1 for j in range(nc)]
+
+
+# ---------------------------------------------------------------------------
+# backward of the sparse attention (training through stage 2)
+# ---------------------------------------------------------------------------
+def _bwd_case(seed, n=14, positions=(3, 7, 9, 13), sel_rows=None):
+    """Tiny case: d=4, Hq=4, Hkv=2, m=4; random valid selections (ascending, -1 padded)."""
+    prm = _params(head_dim=4, num_q_heads=4, num_kv_heads=2, block_size=4, kernel_size=2,
+                  kernel_stride=2, topk=3, local_blocks=1)
+    rng = np.random.default_rng(seed)
+    R = len(positions)
+    q = rng.standard_normal((R, 4, 4))
+    K = rng.standard_normal((2, n, 4))
+    V = rng.standard_normal((2, n, 4))
+    dout = rng.standard_normal((R, 4, 4))
+    sel = np.full((R, 2, prm.topk), -1, dtype=np.int64)
+    for r, i in enumerate(positions):
+        c = i // prm.block_size
+        for g in range(2):
+            # own block always, plus a random subset of the earlier ones
+            others = rng.permutation(c)[:rng.integers(0, prm.topk)].tolist()
+            blocks = sorted(set(others[:prm.topk - 1] + [c]))
+            sel[r, g, :len(blocks)] = blocks
+    if sel_rows is not None:
+        sel = sel_rows(sel)
+    return prm, q, K, V, dout, sel, list(positions)
+
+
+def test_backward_matches_central_differences_of_the_forward():
+    """[IV2 Training-time considerations]: gradients flow to q, K, V through the
+    attention over a fixed selection.  The analytic oracle gradient must equal
+    the numerical derivative of the (separately pinned) forward oracle."""
+    prm, q, K, V, dout, sel, pos = _bwd_case(5)
+
+    def loss(q_, K_, V_):
+        return float((dout * ref.attend_with_selection(q_, K_, V_, pos, sel, prm)).sum())
+
+    dQ, dK, dV, _ = ref.attention_backward(q, K, V, pos, sel, prm, dout)
+    h = 1e-5
+    for arr, grad, which in ((q, dQ, 0), (K, dK, 1), (V, dV, 2)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            args = [q.copy(), K.copy(), V.copy()]
+            args[which][idx] += h
+            fp = loss(*args)
+            args[which][idx] -= 2 * h
+            fm = loss(*args)
+            num[idx] = (fp - fm) / (2 * h)
+        assert np.max(np.abs(num - grad)) < 1e-8 * max(1.0, np.max(np.abs(grad))), which
+    # at least some tokens get no gradient (not attended by any row) and some do
+    assert np.any(np.all(dK == 0, axis=-1)) and np.any(np.any(dK != 0, axis=-1))
+
+
+def test_backward_dense_case_equals_autograd_of_causal_attention():
+    """[IV2 Initial and local tokens always selected]: with every block selected the
+    method is dense causal attention, whose gradient torch's autograd gives."""
+    import torch
+    n = 14
+    pos = list(range(n))
+    prm, q, K, V, dout, sel, _ = _bwd_case(6, n=n, positions=pos)
+    nb = -(-n // prm.block_size)
+    sel = np.full((n, 2, nb), -1, dtype=np.int64)
+    for r, i in enumerate(pos):
+        sel[r, :, :i // prm.block_size + 1] = np.arange(i // prm.block_size + 1)
+    prm = ref.Params(**{**prm.__dict__, "topk": nb})
+    dQ, dK, dV, _ = ref.attention_backward(q, K, V, pos, sel, prm, dout)
+
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, K, V))
+    kx = tk.repeat_interleave(2, dim=0)          # head h uses KV head h // G
+    vx = tv.repeat_interleave(2, dim=0)
+    logits = torch.einsum("rhd,htd->hrt", tq, kx) * prm.scale
+    mask = torch.tensor(np.arange(n)[None, :] <= np.array(pos)[:, None])
+    logits = logits.masked_fill(~mask[None], float("-inf"))
+    out = torch.einsum("hrt,htd->rhd", torch.softmax(logits, dim=-1), vx)
+    (out * torch.tensor(dout)).sum().backward()
+    assert np.allclose(dQ, tq.grad.numpy(), rtol=0, atol=1e-12)
+    assert np.allclose(dK, tk.grad.numpy(), rtol=0, atol=1e-12)
+    assert np.allclose(dV, tv.grad.numpy(), rtol=0, atol=1e-12)
+
+
+def test_backward_invariants_and_block_slices():
+    """Softmax structure: each row's probabilities sum to one, so per row and head
+    sum_t dA_t = 0 (the keys' gradients sum to zero over the sequence) and
+    sum_t dV_t = dO; tokens no row attends get no gradient; block_grad is the
+    per-block slice of the full backward."""
+    prm, q, K, V, dout, sel, pos = _bwd_case(7, n=22, positions=(0, 5, 8, 12, 17, 21))
+    dQ, dK, dV, lse = ref.attention_backward(q, K, V, pos, sel, prm, dout)
+    G = prm.group
+    for g in range(2):
+        assert np.allclose(dK[g].sum(axis=0), 0.0, atol=1e-12)
+        assert np.allclose(dV[g].sum(axis=0), dout[:, g * G:(g + 1) * G].sum(axis=(0, 1)), atol=1e-12)
+        seen = np.zeros(K.shape[1], dtype=bool)
+        for r, i in enumerate(pos):
+            seen[ref.selected_tokens(sel[r, g], i, K.shape[1], prm.block_size)] = True
+        assert np.all(dK[g][~seen] == 0) and np.all(dV[g][~seen] == 0)
+        for j in range(-(-K.shape[1] // prm.block_size)):
+            bk, bv = ref.block_grad(q, K, V, pos, sel, prm, dout, g, j)
+            t0 = j * prm.block_size
+            assert np.allclose(bk, dK[g, t0:t0 + len(bk)], atol=1e-13)
+            assert np.allclose(bv, dV[g, t0:t0 + len(bv)], atol=1e-13)
+    # lse is the forward's LogSumExp
+    for r, i in enumerate(pos):
+        for g in range(2):
+            _, l, _ = ref.attend_row(q[r, g * G:(g + 1) * G], K[g], V[g], i, sel[r, g], prm)
+            assert np.allclose(lse[r, g * G:(g + 1) * G], l, atol=1e-13)
+
+
+def test_backward_row_without_visible_tokens_is_zero():
+    """A row whose selection holds no token at or before it (all -1 padding) has
+    output 0 (the kernels' convention) and contributes no gradient."""
+    prm, q, K, V, dout, sel, pos = _bwd_case(8, sel_rows=lambda s: np.where(
+        np.arange(s.shape[0])[:, None, None] == 1, -1, s))
+    dQ, dK, dV, _ = ref.attention_backward(q, K, V, pos, sel, prm, dout)
+    assert np.all(dQ[1] == 0)
+    dQ2, dK2, dV2, _ = ref.attention_backward(np.delete(q, 1, 0), K, V, [p for r, p in enumerate(pos) if r != 1],
+                                              np.delete(sel, 1, 0), prm, np.delete(dout, 1, 0))
+    assert np.allclose(dK, dK2, atol=1e-14) and np.allclose(dV, dV2, atol=1e-14)
