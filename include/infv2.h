@@ -12,6 +12,7 @@
  *   infv2_select_blocks        step 1b: kernel softmax, group mean, block max, top-k
  *   infv2_sparse_attn_decode   step 2 for one new token per sequence
  *   infv2_sparse_attn_prefill  step 2 for a chunk of consecutive query rows
+ *   infv2_sparse_attn_prefill_bwd  gradients of step 2 (training)
  *
  * Conventions shared by every call
  * --------------------------------
@@ -71,7 +72,7 @@
 extern "C" {
 #endif
 
-#define INFV2_ABI_VERSION 4
+#define INFV2_ABI_VERSION 5
 
 typedef enum infv2_status {
     INFV2_OK = 0,
@@ -97,7 +98,8 @@ typedef enum infv2_op {         /* operation ids for infv2_workspace_bytes */
     INFV2_OP_SELECT_DECODE = 1,
     INFV2_OP_SELECT_PREFILL = 2,
     INFV2_OP_ATTN_DECODE = 3,
-    INFV2_OP_ATTN_PREFILL = 4
+    INFV2_OP_ATTN_PREFILL = 4,
+    INFV2_OP_ATTN_PREFILL_BWD = 5
 } infv2_op;
 
 /* Method hyper-parameters (names follow the pages' notation). */
@@ -271,6 +273,41 @@ int32_t infv2_sparse_attn_prefill_varlen(const infv2_config* cfg, const void* q,
                                          const int32_t* block_idx, void* out, void* ws,
                                          size_t ws_bytes, void* stream);
 
+/*
+ * infv2_sparse_attn_prefill_bwd -- gradients of step 2 for a chunk of rows
+ * ("Training-time considerations": top-k is not differentiable, so the
+ * selection is held fixed and no gradient reaches the compressed keys, which
+ * only feed it; K and V receive gradient only through the attention over the
+ * selected blocks, and "Why mean pooling": that is how training still shapes
+ * the keys the selection pools).
+ *
+ * For the loss L with dL/dout = dout, per query head and with P the softmax
+ * of attn_scale * q.k over the row's selected tokens (t <= i):
+ *   dq = attn_scale * sum_t P_t (dout.v_t - dout.out) k_t,
+ *   dk_t = attn_scale * sum over the rows and heads attending t of P_t (dout.v_t - dout.out) q,
+ *   dv_t = sum over the rows and heads attending t of P_t dout.
+ *
+ *   q, rows, q_start, k, v, kv_offsets, block_idx   as for infv2_sparse_attn_prefill
+ *                (the entries of one row of block_idx must be distinct, as
+ *                infv2_select_blocks writes them; entries < 0 or past the
+ *                row's block range are ignored)
+ *   out          device, io_dtype [rows][Hq][d]: the forward output for these inputs
+ *   dout         device, io_dtype [rows][Hq][d]: gradient of the loss w.r.t. out
+ *   dq           device, io_dtype [rows][Hq][d] (written)
+ *   dk, dv       device, io_dtype, same layout as k and v: tokens 0 .. q_start +
+ *                rows - 1 of every KV head are written with the sum over this
+ *                call's rows (0 where no row attends the token); later tokens
+ *                are not touched.  A chunked caller sums the calls' results.
+ *   ws           workspace (op = ATTN_PREFILL_BWD, rows, max_len = q_start + rows);
+ *                no initial contents are needed
+ * rows * topk must not exceed 2^30.  rows == 0 writes nothing.
+ */
+int32_t infv2_sparse_attn_prefill_bwd(const infv2_config* cfg, const void* q, int32_t rows,
+                                      int64_t q_start, const void* k, const void* v,
+                                      const int64_t* kv_offsets, const int32_t* block_idx,
+                                      const void* out, const void* dout, void* dq, void* dk,
+                                      void* dv, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace size in bytes for operation `op` (infv2_op) at the given sizes. */
 int32_t infv2_workspace_bytes(const infv2_config* cfg, int32_t op, int32_t rows, int32_t batch,
                               int64_t max_len, size_t* bytes);
@@ -310,9 +347,12 @@ typedef enum infv2_kernel {
     INFV2_KERNEL_ATTN_DECODE = 5,       /* decode: attention over the selected blocks (partials) */
     INFV2_KERNEL_ATTN_MERGE = 6,        /* decode: merge of the partials */
     INFV2_KERNEL_ATTN_PREFILL = 7,      /* prefill: attention over the selected blocks */
-    INFV2_KERNEL_VT_BUILD = 8,          /* prefill: transposed V tiles */
+    INFV2_KERNEL_VT_BUILD = 8,          /* prefill: transposed V tiles (K tiles in the backward) */
     INFV2_KERNEL_APPEND = 9,            /* decode: cache append + incremental compressed key */
-    INFV2_KERNEL_COUNT = 10
+    INFV2_KERNEL_BWD_ROW = 10,          /* backward: dq, LogSumExp and dout.out per row */
+    INFV2_KERNEL_BWD_INDEX = 11,        /* backward: the rows that selected each block */
+    INFV2_KERNEL_BWD_COL = 12,          /* backward: dk and dv per block */
+    INFV2_KERNEL_COUNT = 13
 } infv2_kernel;
 
 int32_t infv2_timing_start(int32_t kernel);

@@ -12,5 +12,6 @@ from .gen import (  # noqa: F401
     f32_to_bf16_bits,
     make_config,
     make_workload,
+    upstream_grad,
     CONFIGS,
 )

@@ -206,3 +206,11 @@ def extra_decode_queries(wl: Workload, count: int, seed: int = 1_000_003) -> np.
     rng = np.random.default_rng(seed + wl.seed)
     qf = rng.standard_normal((count, wl.batch, wl.num_q_heads, wl.head_dim), dtype=np.float32)
     return _encode(qf, wl.io_dtype)
+
+
+def upstream_grad(wl: Workload, seed: int = 2_000_003) -> np.ndarray:
+    """A gradient of the loss w.r.t. the attention output, shaped like ``wl.q``:
+    i.i.d. N(0, 1), encoded in the workload's io dtype (own stream)."""
+    rng = np.random.default_rng(seed + wl.seed)
+    g = rng.standard_normal(wl.q.shape, dtype=np.float32)
+    return _encode(g, wl.io_dtype)

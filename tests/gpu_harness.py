@@ -149,3 +149,28 @@ class DeviceWorkload:
             scores.append(s)
             outs.append(o)
         return torch.cat(idxs), torch.cat(scores), torch.cat(outs)
+
+    # ---------------------------------------------------------------- backward
+    def attn_prefill_bwd(self, q0: int, q1: int, idx: torch.Tensor, out: torch.Tensor,
+                         dout: torch.Tensor, dk: Optional[torch.Tensor] = None,
+                         dv: Optional[torch.Tensor] = None):
+        """Gradients of rows [q0, q1) (idx, out, dout hold those rows only).  dk / dv
+        default to fresh buffers filled with NaN so untouched tokens stay visible."""
+        rows = q1 - q0
+        q = self.q[q0:q1]
+        dq = torch.empty_like(q)
+        if dk is None:
+            dk = nan_like(self.k)
+        if dv is None:
+            dv = nan_like(self.v)
+        ws = self.ws(tbs.OP_ATTN_PREFILL_BWD, rows, 1, q1)
+        tbs.infv2_sparse_attn_prefill_bwd(self.cfg, q, rows, q0, self.k, self.v, self.kv_offsets,
+                                          idx, out, dout, dq, dk, dv, ws)
+        return dq, dk, dv
+
+
+def nan_like(t: torch.Tensor) -> torch.Tensor:
+    """Same shape and storage type, every element a quiet NaN (fp32 or bf16 bits)."""
+    if t.dtype == torch.int16:
+        return torch.full_like(t, 0x7FC0)
+    return torch.full_like(t, float("nan"))

@@ -179,3 +179,29 @@ def test_varlen_prefill_and_append_validation(lib):
     app = lib.infv2_append_kv
     assert app(c, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 2, None) == ENULL
     assert app(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == ESHAPE
+
+
+def test_backward_validation(lib):
+    cfg = tbs.Config()
+    c = _c(cfg)
+    bwd = lib.infv2_sparse_attn_prefill_bwd
+    rows, q0 = 1000, 3000
+    need = tbs.infv2_workspace_bytes(cfg, tbs.OP_ATTN_PREFILL_BWD, rows, 1, q0 + rows)
+    assert need > 0
+    # grows with the rows and with the prefix (more blocks per KV head)
+    assert tbs.infv2_workspace_bytes(cfg, tbs.OP_ATTN_PREFILL_BWD, 2 * rows, 1, q0 + 2 * rows) > need
+    ptrs = [FAKE] * 10          # q k v kv_offsets block_idx out dout dq dk dv
+    def call(p=ptrs, r=rows, s=q0, ws=FAKE, nb=need):
+        qq, k, v, off, idx, out, dout, dq, dk, dv = p
+        return bwd(c, qq, r, s, k, v, off, idx, out, dout, dq, dk, dv, ws, nb, None)
+    for x in range(10):
+        p = list(ptrs)
+        p[x] = None
+        assert call(p) == ENULL, x
+    assert call(r=-1) == ESHAPE
+    assert call(s=-5) == ESHAPE
+    assert call(nb=need - 1) == EWS
+    assert call(ws=None) == EWS
+    assert call(r=0, ws=None, nb=0) == OK          # nothing to do, nothing launched
+    assert call(r=1 << 21, s=0) == EUNSUP          # rows * topk above 2^30
+    assert call(s=16384 * 64) == EUNSUP            # more blocks than supported

@@ -20,10 +20,12 @@ LIB_PATH = os.path.join(_HERE, "libinfv2.so")
 
 INFV2_FP32, INFV2_BF16 = 0, 1
 INFV2_MODE_DECODE, INFV2_MODE_PREFILL = 0, 1
-OP_COMPRESS, OP_SELECT_DECODE, OP_SELECT_PREFILL, OP_ATTN_DECODE, OP_ATTN_PREFILL = range(5)
+(OP_COMPRESS, OP_SELECT_DECODE, OP_SELECT_PREFILL, OP_ATTN_DECODE, OP_ATTN_PREFILL,
+ OP_ATTN_PREFILL_BWD) = range(6)
 # kernel families for infv2_timing_start (infv2_kernel in infv2.h)
 KERNELS = ("compress", "select_logits", "select_scores", "select_prefill", "select_topk",
-           "attn_decode", "attn_merge", "attn_prefill", "vt_build", "append")
+           "attn_decode", "attn_merge", "attn_prefill", "vt_build", "append", "bwd_row",
+           "bwd_index", "bwd_col")
 KERNEL_ID = {name: i for i, name in enumerate(KERNELS)}
 STATUS = {0: "INFV2_OK", 1: "INFV2_ERR_NULL", 2: "INFV2_ERR_SHAPE", 3: "INFV2_ERR_UNSUPPORTED",
           4: "INFV2_ERR_WORKSPACE", 5: "INFV2_ERR_DEVICE"}
@@ -96,6 +98,8 @@ def load_library(path: str = LIB_PATH):
                                       vp, sz, vp]),
         "infv2_sparse_attn_decode": (i32, [cfgp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, sz, vp]),
         "infv2_sparse_attn_prefill": (i32, [cfgp, vp, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "infv2_sparse_attn_prefill_bwd": (i32, [cfgp, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                vp, vp, sz, vp]),
         "infv2_workspace_bytes": (i32, [cfgp, i32, i32, i32, i64, ctypes.POINTER(sz)]),
         "infv2_num_kernels": (i64, [cfgp, i64]),
         "infv2_status_str": (ctypes.c_char_p, [i32]),
@@ -112,7 +116,7 @@ def load_library(path: str = LIB_PATH):
 
 EXPORTED = ("infv2_compress_keys", "infv2_append_kv", "infv2_select_blocks", "infv2_sparse_attn_decode",
             "infv2_sparse_attn_prefill", "infv2_select_blocks_varlen",
-            "infv2_sparse_attn_prefill_varlen", "infv2_workspace_bytes", "infv2_num_kernels",
+            "infv2_sparse_attn_prefill_varlen", "infv2_sparse_attn_prefill_bwd", "infv2_workspace_bytes", "infv2_num_kernels",
             "infv2_status_str", "infv2_abi_version", "infv2_timing_start", "infv2_timing_stop")
 
 
@@ -257,6 +261,15 @@ def infv2_sparse_attn_prefill(cfg: Config, q, rows: int, q_start: int, k, v, kv_
     _check(load_library().infv2_sparse_attn_prefill(
         ctypes.byref(c), _ptr(q), rows, q_start, _ptr(k), _ptr(v), _ptr(kv_offsets),
         _ptr(block_idx), _ptr(out), _ptr(ws), nbytes, _stream(stream)), "infv2_sparse_attn_prefill")
+
+
+def infv2_sparse_attn_prefill_bwd(cfg: Config, q, rows: int, q_start: int, k, v, kv_offsets,
+                                  block_idx, out, dout, dq, dk, dv, ws, stream=None) -> None:
+    c = cfg.to_c()
+    _check(load_library().infv2_sparse_attn_prefill_bwd(
+        ctypes.byref(c), _ptr(q), rows, q_start, _ptr(k), _ptr(v), _ptr(kv_offsets),
+        _ptr(block_idx), _ptr(out), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+        _nbytes(ws), _stream(stream)), "infv2_sparse_attn_prefill_bwd")
 
 
 def workspace(cfg: Config, op: int, rows: int, batch: int, max_len: int, device="cuda"):

@@ -61,6 +61,7 @@ size_t ws_bytes_for(const infv2_config* c, int32_t op, int32_t rows, int32_t bat
         case INFV2_OP_SELECT_PREFILL: return infv2::select_prefill_ws(sh, rows, max_len).total;
         case INFV2_OP_ATTN_DECODE: return infv2::attn_decode_ws(sh, batch).total;
         case INFV2_OP_ATTN_PREFILL: return infv2::attn_prefill_ws_bytes(sh, max_len);
+        case INFV2_OP_ATTN_PREFILL_BWD: return rows > 0 ? infv2::bwd_ws(sh, rows, max_len).total : 0;
         default: return 0;
     }
 }
@@ -94,7 +95,7 @@ int32_t infv2_workspace_bytes(const infv2_config* c, int32_t op, int32_t rows, i
     int32_t st = check_config(c);
     if (st != INFV2_OK) return st;
     if ((st = check_len(c, max_len)) != INFV2_OK) return st;
-    if (op < INFV2_OP_COMPRESS || op > INFV2_OP_ATTN_PREFILL || rows < 0 || batch < 0) return INFV2_ERR_SHAPE;
+    if (op < INFV2_OP_COMPRESS || op > INFV2_OP_ATTN_PREFILL_BWD || rows < 0 || batch < 0) return INFV2_ERR_SHAPE;
     *bytes = ws_bytes_for(c, op, rows, batch, max_len);
     return INFV2_OK;
 }
@@ -191,6 +192,26 @@ int32_t infv2_sparse_attn_prefill(const infv2_config* c, const void* q, int32_t 
     return status_of(infv2::launch_attn_prefill(make_shape(c), q, rows, q_start, k, v, kv_offsets,
                                                 block_idx, out, ws,
                                                 static_cast<hipStream_t>(stream)));
+}
+
+int32_t infv2_sparse_attn_prefill_bwd(const infv2_config* c, const void* q, int32_t rows,
+                                      int64_t q_start, const void* k, const void* v,
+                                      const int64_t* kv_offsets, const int32_t* block_idx,
+                                      const void* out, const void* dout, void* dq, void* dk,
+                                      void* dv, void* ws, size_t ws_bytes, void* stream) {
+    int32_t st = check_config(c);
+    if (st != INFV2_OK) return st;
+    if (!q || !k || !v || !kv_offsets || !block_idx || !out || !dout || !dq || !dk || !dv)
+        return INFV2_ERR_NULL;
+    if (rows < 0 || q_start < 0) return INFV2_ERR_SHAPE;
+    if (static_cast<int64_t>(rows) * c->topk > (int64_t(1) << 30)) return INFV2_ERR_UNSUPPORTED;
+    if ((st = check_len(c, q_start + rows)) != INFV2_OK) return st;
+    if (rows == 0) return INFV2_OK;
+    const size_t need = ws_bytes_for(c, INFV2_OP_ATTN_PREFILL_BWD, rows, 1, q_start + rows);
+    if (!ws || ws_bytes < need) return INFV2_ERR_WORKSPACE;
+    return status_of(infv2::launch_attn_prefill_bwd(make_shape(c), q, rows, q_start, k, v,
+                                                    kv_offsets, block_idx, out, dout, dq, dk, dv,
+                                                    ws, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -91,6 +91,27 @@ hipError_t launch_attn_prefill(const Shape& sh, const void* q, int rows, int64_t
                                const void* k, const void* v, const int64_t* kv_off,
                                const int32_t* idx, void* out, void* ws, hipStream_t st);
 
+// backward of the prefill attention (attn_bwd.hip, attn_bwd_mfma.hip)
+struct BwdWs {
+    size_t lse, delta, counts, totals, col_start, list, kt, total;
+    int nblk, nchunk;
+    int64_t list_ld;
+};
+BwdWs bwd_ws(const Shape& sh, int rows, int64_t max_len);
+bool bwd_mfma_ok(const Shape& sh);
+size_t bwd_kt_bytes(const Shape& sh, int64_t max_len);
+hipError_t launch_inverse_index(const Shape& sh, const BwdWs& w, int rows, const int32_t* idx,
+                                char* base, hipStream_t st);
+hipError_t launch_attn_prefill_bwd(const Shape& sh, const void* q, int rows, int64_t q_start,
+                                   const void* k, const void* v, const int64_t* kv_off,
+                                   const int32_t* idx, const void* out, const void* dout,
+                                   void* dq, void* dk, void* dv, void* ws, hipStream_t st);
+hipError_t launch_attn_prefill_bwd_mfma(const Shape& sh, const BwdWs& w, const void* q, int rows,
+                                        int64_t q_start, const void* k, const void* v,
+                                        const int64_t* kv_off, const int32_t* idx,
+                                        const void* out, const void* dout, void* dq, void* dk,
+                                        void* dv, char* ws, hipStream_t st);
+
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace infv2
