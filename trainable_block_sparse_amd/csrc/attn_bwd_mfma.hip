@@ -1,17 +1,547 @@
-// Matrix-core kernels of the attention backward (bf16, block 64).
+// Matrix-core kernels of the attention backward (bf16, KV block 64).
+// MiniCPM4 summary page, "InfLLM v2" section, "Training-time considerations":
+// gradients reach q, K and V only through the attention over the selected
+// blocks; the selection is held fixed.  The arithmetic is the one stated in
+// attn_bwd.hip; here it runs on 16x16x32 bf16 MFMA with fp32 accumulation.
+//
+// Row pass (bwd_row_mfma): like the forward prefill kernel, a thread block owns
+// 16 consecutive rows of one KV head (one row per wave) and streams the union
+// of their selected blocks through LDS (K and V as stored, K^T as transposed
+// tiles).  Per (row, block):
+//   S^T  = K . Q^T          16 MFMA     dP^T = V . dO^T       16 MFMA
+//   dA^T = P^T (dP^T - D), P against a lazily raised reference max
+//   dQ^T += K^T . dA^T      16 MFMA (dA in bf16)
+// and the row's LogSumExp (log2 units of the scaled logits) and D = dO . O go
+// to the workspace for the column pass.
+//
+// Column pass (bwd_col_mfma): a thread block owns (KV head, block) and a segment
+// of at most kSeg rows of the block's row list (from the inverse index); wave w
+// owns keys 16 w .. 16 w + 15 and keeps their K and V fragments in registers.
+// Rows go in pairs, the 32-wide contraction of the dk / dv products being
+// (2 rows x 16 heads).  Per pair:
+//   S = Q . K^T, dP = dO . V^T          4 x 4 MFMA (two rows, Q and dO)
+//   P = 2^(S scale - lse), dA = P (dP - D)
+//   dV^T += dO^T . P,  dK^T += Q^T . dA 16 MFMA
+// The Q^T and dO^T operands (heads along the contraction) are produced from the
+// row-major tiles by one 16x16x16 product with the identity per 16x16 tile,
+// which lands each value exactly where the operand layout wants it.  The pairs'
+// Q and dO tiles are double-buffered in LDS with direct global->LDS loads.
+// A block whose list is longer than kSeg rows is split into segments whose
+// fp32 partials are summed in segment order by bwd_col_finish, so results do
+// not depend on scheduling.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "prefill_tiles.hpp"
 
 namespace infv2 {
 
-bool bwd_mfma_ok(const Shape&) { return false; }
-size_t bwd_kt_bytes(const Shape&, int64_t) { return 0; }
+constexpr int kRWaves = kUWaves;       // row pass: one row per wave
+constexpr int kRThreads = kUThreads;
+constexpr int kCThreads = 256;         // column pass: 4 waves x 16 keys
+constexpr int kSeg = 2048;             // rows per column segment
+constexpr int kXcdsB = 8;
+constexpr float kSlackB = 8.f;         // log2 units, as in the forward
 
-hipError_t launch_attn_prefill_bwd_mfma(const Shape&, const BwdWs&, const void*, int, int64_t,
-                                        const void*, const void*, const int64_t*, const int32_t*,
-                                        const void*, const void*, void*, void*, void*, char*,
-                                        hipStream_t) {
-    return hipErrorNotSupported;
+bool bwd_mfma_ok(const Shape& sh) {
+    return sh.io_bf16 && sh.m == kPB && kURows * sh.topk <= kUnionCap;
+}
+
+size_t bwd_kt_bytes(const Shape& sh, int64_t max_len) {
+    const int64_t nblk = (max_len + kPB - 1) / kPB;
+    return static_cast<size_t>(sh.hkv) * nblk * kHeadDim * kPB * sizeof(bf16_t);
+}
+
+// work items of the column pass: one per (column, segment); upper bound used for
+// the grid and the partial buffers
+static int64_t max_col_items(const Shape& sh, const BwdWs& w) {
+    return static_cast<int64_t>(sh.hkv) * w.nblk + (static_cast<int64_t>(sh.hkv) * w.list_ld) / kSeg + 1;
+}
+
+size_t bwd_mfma_extra_bytes(const Shape& sh, const BwdWs& w) {
+    const int64_t items = max_col_items(sh, w);
+    const int64_t ncol = static_cast<int64_t>(sh.hkv) * w.nblk;
+    return align256(static_cast<size_t>(ncol + 1) * sizeof(int32_t)) +          // item_start
+           align256(static_cast<size_t>(items) * 2 * kPB * kHeadDim * sizeof(float));  // partials
+}
+
+// XCD-aware placement: thread block b runs on XCD b % 8; hand each XCD a
+// contiguous range of work items
+__device__ __forceinline__ int xcd_remap(int b, int nwg) {
+    const int xcd = b % kXcdsB, kx = b / kXcdsB;
+    const int qx = nwg / kXcdsB, rx = nwg % kXcdsB;
+    return xcd * qx + (xcd < rx ? xcd : rx) + kx;
+}
+
+__device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b) {
+    const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        s = fmaf(__uint_as_float(av[i] << 16), __uint_as_float(bv[i] << 16), s);
+        s = fmaf(__uint_as_float(av[i] & 0xffff0000u), __uint_as_float(bv[i] & 0xffff0000u), s);
+    }
+    return s;
+}
+
+// ---------------------------------------------------------------- row pass
+__global__ __launch_bounds__(kRThreads, 1) void bwd_row_mfma(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ out, const bf16_t* __restrict__ dout,
+    int rows, int64_t q_start, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ kt, const int64_t* __restrict__ kv_off,
+    const int32_t* __restrict__ idx, bf16_t* __restrict__ dq, float* __restrict__ lse2,
+    float* __restrict__ delta, int hq, int hkv, int topk, int64_t nblk, int nrg, float scale_log2,
+    float scale) {
+    // two stages (distinct LDS objects, named at every access) of one block each
+    __shared__ __attribute__((aligned(16))) BlockTile k_a, v_a, t_a, k_b, v_b, t_b;
+    __shared__ UnionSmem sm;
+    const int lid = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+    const int g = lid / nrg, r0 = (lid % nrg) * kURows;
+    const int t = threadIdx.x;
+    const int w = t >> 6, l = t & 63, lg = l >> 4, lc = l & 15;
+    const int64_t cap = kv_off[1] - kv_off[0];
+    const size_t hoff = (kv_off[0] * hkv + static_cast<int64_t>(g) * cap) * kHeadDim;
+    const bf16_t* kh = k + hoff;
+    const bf16_t* vh = v + hoff;
+    const bf16_t* kth = kt + static_cast<int64_t>(g) * nblk * kHeadDim * kPB;
+    const int64_t nlim = q_start + rows;
+
+    const int n_u = build_union(sm, idx, rows, r0, hkv, g, topk, nblk);
+
+    // ---- row state: wave w owns row r0 + w; lane holds head lc, d = 32 ks + 8 lg ..
+    const int row = r0 + w;
+    const int rr = row < rows ? row : rows - 1;
+    const int32_t qpos = static_cast<int32_t>(q_start + row);
+    const size_t roff = (static_cast<size_t>(rr) * hq + static_cast<size_t>(g) * kGroup + lc) * kHeadDim;
+    bf16x8_t qf[4], dof[4];
+    float dd = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const uint4 qv = ldg16(q + roff + 32 * ks + 8 * lg);
+        const uint4 dv = ldg16(dout + roff + 32 * ks + 8 * lg);
+        const uint4 ov = ldg16(out + roff + 32 * ks + 8 * lg);
+        qf[ks] = as_bf16x8(qv);
+        dof[ks] = as_bf16x8(dv);
+        dd += dot8_bf16(dv, ov);
+    }
+    dd += __shfl_xor(dd, 16, 64);
+    dd += __shfl_xor(dd, 32, 64);              // D of head lc
+    f32x4_t acc[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float mref = -INFINITY, lsum = 0.f;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    // ---- tile loads: each wave fills 1 KB of each tile (one 16-byte load per lane)
+    const int key_l = 4 * w + (l >> 4);                          // keys 4 w .. 4 w + 3
+    const int koff_l = key_l * kHeadDim + 8 * ((l & 15) ^ (key_l & 15));
+    const int d_l = 8 * w + (l >> 3);                            // K^T rows 8 w .. 8 w + 7
+    const int toff_l = d_l * kPB + 8 * ((l & 7) ^ ((d_l >> 1) & 7));
+    auto issue = [&](BlockTile& kt_, BlockTile& vt_, BlockTile& tt_, int u) {
+        const int32_t blk = sm.list[u];
+        const int64_t k0 = static_cast<int64_t>(blk) * kPB;
+        int64_t off = k0 * kHeadDim + koff_l;
+        if (k0 + kPB > nlim) {                                   // clamp: later keys are masked
+            int64_t gk = k0 + key_l;
+            gk = gk < nlim ? gk : nlim - 1;
+            off = gk * kHeadDim + 8 * ((l & 15) ^ (key_l & 15));
+        }
+        __builtin_amdgcn_global_load_lds(kh + off, &kt_[w * 512], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vh + off, &vt_[w * 512], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(kth + k0 * kHeadDim + toff_l, &tt_[w * 512], 16, 0, 0);
+    };
+    auto compute = [&](const BlockTile& kt_, const BlockTile& vt_, const BlockTile& tt_, int u) {
+        const int32_t blk = sm.list[u];
+        const int cntr = qpos + 1 - blk * kPB;                   // keys of the block at or before the row
+        const bool act = ((sm.mask[u] >> w) & 1u) && row < rows && cntr > 0;
+        if (!__builtin_amdgcn_readfirstlane(static_cast<int>(act))) return;
+        f32x4_t s[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            s[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                s[mt] = mfma32(as_bf16x8(k_frag(kt_, 16 * mt + lc, 4 * ks + lg)), qf[ks], s[mt]);
+        }
+        // lane holds S^T[key 16 mt + 4 lg + r][head lc]
+        float lm = -INFINITY;
+        if (__builtin_amdgcn_readfirstlane(cntr) >= kPB) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) lm = fmaxf(lm, s[mt][r]);
+        } else {
+            const int lim_l = cntr - 4 * lg;                     // key 16 mt + 4 lg + r visible iff 16 mt + r < lim_l
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float x = (16 * mt + r) < lim_l ? s[mt][r] : -INFINITY;
+                    s[mt][r] = x;
+                    lm = fmaxf(lm, x);
+                }
+        }
+        lm *= scale_log2;
+        if (__any(lm > mref + kSlackB)) {
+            float mx = fmaxf(lm, __shfl_xor(lm, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float mnew = fmaxf(mref, mx);
+            const float alpha = (mref == -INFINITY) ? 0.f : fast_exp2(mref - mnew);
+            lsum *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[mt][r] *= alpha;
+            mref = mnew;
+        }
+        // dP^T one 16-key tile at a time (keeps few registers live), then dA^T
+        float ls = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            f32x4_t dp = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                dp = mfma32(as_bf16x8(k_frag(vt_, 16 * mt + lc, 4 * ks + lg)), dof[ks], dp);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = fast_exp2(fmaf(s[mt][r], scale_log2, -mref));   // masked: 0
+                ls += p;
+                s[mt][r] = p * (dp[r] - dd);
+            }
+        }
+        lsum += ls;
+        bf16x8_t af[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            uint4 pu;
+            pu.x = pack_rne(s[2 * kk][0], s[2 * kk][1]);
+            pu.y = pack_rne(s[2 * kk][2], s[2 * kk][3]);
+            pu.z = pack_rne(s[2 * kk + 1][0], s[2 * kk + 1][1]);
+            pu.w = pack_rne(s[2 * kk + 1][2], s[2 * kk + 1][3]);
+            af[kk] = as_bf16x8(pu);
+        }
+        // K^T fragments two d-tiles at a time (bounds the registers in flight)
+#pragma unroll
+        for (int mb = 0; mb < 8; mb += 2) {
+            uint4 tf[2][2];
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                tf[x][0] = vt_frag(tt_, 16 * (mb + x) + lc, lg);
+                tf[x][1] = vt_frag(tt_, 16 * (mb + x) + lc, 4 + lg);
+            }
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                acc[mb + x] = mfma32(as_bf16x8(tf[x][0]), af[0], acc[mb + x]);
+                acc[mb + x] = mfma32(as_bf16x8(tf[x][1]), af[1], acc[mb + x]);
+            }
+        }
+    };
+    for (int u0 = 0; u0 < n_u; u0 += 2) {
+        __syncthreads();                                         // previous blocks consumed
+        issue(k_a, v_a, t_a, u0);
+        if (u0 + 1 < n_u) issue(k_b, v_b, t_b, u0 + 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        compute(k_a, v_a, t_a, u0);
+        if (u0 + 1 < n_u) compute(k_b, v_b, t_b, u0 + 1);
+    }
+
+    // ---- epilogue: lane holds dQ^T[d = 16 mt + 4 lg + r][head lc]
+    float lt = lsum + __shfl_xor(lsum, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    if (row >= rows) return;
+    const float inv = lt > 0.f ? scale / lt : 0.f;
+    bf16_t* dst = dq + (static_cast<size_t>(row) * hq + static_cast<size_t>(g) * kGroup + lc) * kHeadDim + 4 * lg;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+        uint2 pk;
+        pk.x = pack_rne(acc[mt][0] * inv, acc[mt][1] * inv);
+        pk.y = pack_rne(acc[mt][2] * inv, acc[mt][3] * inv);
+        *reinterpret_cast<uint2*>(dst + 16 * mt) = pk;
+    }
+    if (lg == 0) {
+        const size_t o = static_cast<size_t>(row) * hq + static_cast<size_t>(g) * kGroup + lc;
+        lse2[o] = lt > 0.f ? mref + log2f(lt) : INFINITY;    // +inf: nothing visible, P = 0
+        delta[o] = dd;
+    }
+}
+
+// ---------------------------------------------------------------- column pass
+// items per column (1 + one per further kSeg rows) and their exclusive scan
+__global__ __launch_bounds__(1024) void bwd_items_kernel(const int32_t* __restrict__ col_start,
+                                                         int nblk, int ncol,
+                                                         int32_t* __restrict__ item_start) {
+    __shared__ uint32_t tmp[17];
+    __shared__ uint32_t tile_total;
+    const int t = threadIdx.x;
+    uint32_t carry = 0;
+    for (int base = 0; base < ncol; base += 1024) {
+        const int c = base + t;
+        uint32_t n = 0;
+        if (c < ncol) {
+            const int g = c / nblk, j = c % nblk;
+            const int32_t* cs = col_start + static_cast<size_t>(g) * (nblk + 1);
+            const int32_t len = cs[j + 1] - cs[j];
+            n = len > kSeg ? static_cast<uint32_t>((len + kSeg - 1) / kSeg) : 1u;
+        }
+        const uint32_t incl = block_incl_scan<16>(n, tmp);
+        if (c < ncol) item_start[c] = static_cast<int32_t>(carry + incl - n);
+        if (t == 1023) tile_total = incl;
+        __syncthreads();
+        carry += tile_total;
+        __syncthreads();
+    }
+    if (t == 0) item_start[ncol] = static_cast<int32_t>(carry);
+}
+
+// identity operand of the 16x16x16 product: lane holds I[4 lg + e][lc]
+__device__ __forceinline__ s16x4_t identity_b(int lg, int lc) {
+    s16x4_t b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) b[e] = (4 * lg + e == lc) ? static_cast<short>(0x3F80) : static_cast<short>(0);
+    return b;
+}
+
+typedef bf16_t RowTiles[4][kGroup * kHeadDim];   // Q_A, Q_B, dO_A, dO_B (4 KB each)
+
+__global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout, int rows, int64_t q_start,
+    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const int64_t* __restrict__ kv_off,
+    const int32_t* __restrict__ col_start, const int32_t* __restrict__ list, int64_t list_ld,
+    const int32_t* __restrict__ item_start, const float* __restrict__ lse2,
+    const float* __restrict__ delta, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv,
+    float* __restrict__ partial, int hq, int hkv, int nblk, float scale_log2, float scale) {
+    __shared__ __attribute__((aligned(16))) RowTiles rt_a, rt_b;
+    const int ncol = hkv * nblk;
+    const int item = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+    if (item >= item_start[ncol]) return;
+    // column of this item: last c with item_start[c] <= item
+    int lo = 0, hi = ncol - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (item_start[mid] <= item) lo = mid; else hi = mid - 1;
+    }
+    const int col = lo, g = col / nblk, j = col % nblk;
+    const int seg = item - item_start[col];
+    const int nseg = item_start[col + 1] - item_start[col];
+    const int32_t* cs = col_start + static_cast<size_t>(g) * (nblk + 1);
+    const int32_t* lst = list + static_cast<size_t>(g) * list_ld;
+    const int32_t beg = cs[j] + seg * kSeg;
+    const int32_t end = (cs[j + 1] < beg + kSeg) ? cs[j + 1] : beg + kSeg;
+
+    const int t = threadIdx.x, w = t >> 6, l = t & 63, lg = l >> 4, lc = l & 15;
+    const int64_t lim = q_start + rows;
+    const int64_t cap = kv_off[1] - kv_off[0];
+    const size_t hoff = (kv_off[0] * hkv + static_cast<int64_t>(g) * cap) * kHeadDim;
+    const int64_t key = static_cast<int64_t>(j) * kPB + 16 * w + lc;      // this lane's key
+    const int64_t keyc = key < lim ? key : lim - 1;
+    bf16x8_t kf[4], vf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        kf[ks] = as_bf16x8(ldg16(k + hoff + keyc * kHeadDim + 32 * ks + 8 * lg));
+        vf[ks] = as_bf16x8(ldg16(v + hoff + keyc * kHeadDim + 32 * ks + 8 * lg));
+    }
+    f32x4_t av[8], ak[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) { av[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f}; ak[dt] = av[dt]; }
+    const s16x4_t ident = identity_b(lg, lc);
+
+    // stage slot t of each tile: head h = t / 16 holds chunk (t % 16) ^ h there
+    const int sh_h = t >> 4, sh_c = (t & 15) ^ (t >> 4);
+    auto tile_src = [&](const bf16_t* base, int r) {
+        return base + (static_cast<size_t>(r) * hq + static_cast<size_t>(g) * kGroup + sh_h) * kHeadDim + 8 * sh_c;
+    };
+    float4 nl[2], nd[2];                                  // lse / D of the next pair, heads 4 lg ..
+    int nra = 0, nrb = 0;
+    auto issue = [&](RowTiles& rt, int e) {
+        nra = lst[e];
+        nrb = (e + 1 < end) ? lst[e + 1] : nra;
+        __builtin_amdgcn_global_load_lds(tile_src(q, nra), &rt[0][w * 512], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(tile_src(q, nrb), &rt[1][w * 512], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(tile_src(dout, nra), &rt[2][w * 512], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(tile_src(dout, nrb), &rt[3][w * 512], 16, 0, 0);
+        const size_t oa = static_cast<size_t>(nra) * hq + static_cast<size_t>(g) * kGroup + 4 * lg;
+        const size_t ob = static_cast<size_t>(nrb) * hq + static_cast<size_t>(g) * kGroup + 4 * lg;
+        nl[0] = *reinterpret_cast<const float4*>(lse2 + oa);
+        nl[1] = *reinterpret_cast<const float4*>(lse2 + ob);
+        nd[0] = *reinterpret_cast<const float4*>(delta + oa);
+        nd[1] = *reinterpret_cast<const float4*>(delta + ob);
+    };
+    // A operand of S / dP: lane holds X[head lc][d = 32 ks + 8 lg ..]
+    auto a_frag = [&](const RowTiles& rt, int x, int ks) {
+        const int c = 4 * ks + lg;
+        return as_bf16x8(*reinterpret_cast<const uint4*>(&rt[x][lc * kHeadDim + 8 * (c ^ lc)]));
+    };
+    // A operand of the identity product: lane holds X[head lc][d = 16 dt + 4 lg .. + 4]
+    auto t_frag = [&](const RowTiles& rt, int x, int dt) {
+        const int c = 2 * dt + (lg >> 1);
+        return *reinterpret_cast<const s16x4_t*>(&rt[x][lc * kHeadDim + 8 * (c ^ lc) + 4 * (lg & 1)]);
+    };
+    auto compute = [&](const RowTiles& rt, int ra, int rb, bool has_b, const float4 (&cl)[2],
+                       const float4 (&cd)[2]) {
+        f32x4_t s[2], dp[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) { s[x] = f32x4_t{0.f, 0.f, 0.f, 0.f}; dp[x] = s[x]; }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                s[x] = mfma32(a_frag(rt, x, ks), kf[ks], s[x]);
+                dp[x] = mfma32(a_frag(rt, 2 + x, ks), vf[ks], dp[x]);
+            }
+        }
+        // lane holds S[head 4 lg + r][key 16 w + lc] of rows A (x = 0) and B (x = 1)
+        float pv[2][4], av_[2][4];
+        const int64_t pa = q_start + ra, pb = q_start + rb;
+        const bool visa = key < lim && key <= pa;
+        const bool visb = has_b && key < lim && key <= pb;
+        const float la[4] = {cl[0].x, cl[0].y, cl[0].z, cl[0].w}, lb[4] = {cl[1].x, cl[1].y, cl[1].z, cl[1].w};
+        const float da[4] = {cd[0].x, cd[0].y, cd[0].z, cd[0].w}, db[4] = {cd[1].x, cd[1].y, cd[1].z, cd[1].w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            pv[0][r] = visa ? fast_exp2(fmaf(s[0][r], scale_log2, -la[r])) : 0.f;
+            pv[1][r] = visb ? fast_exp2(fmaf(s[1][r], scale_log2, -lb[r])) : 0.f;
+            av_[0][r] = pv[0][r] * (dp[0][r] - da[r]);
+            av_[1][r] = pv[1][r] * (dp[1][r] - db[r]);
+        }
+        // B operands: k = 8 lg + e <-> (row e / 4, head 4 lg + e % 4), n = key lc
+        uint4 pu, du;
+        pu.x = pack_rne(pv[0][0], pv[0][1]); pu.y = pack_rne(pv[0][2], pv[0][3]);
+        pu.z = pack_rne(pv[1][0], pv[1][1]); pu.w = pack_rne(pv[1][2], pv[1][3]);
+        du.x = pack_rne(av_[0][0], av_[0][1]); du.y = pack_rne(av_[0][2], av_[0][3]);
+        du.z = pack_rne(av_[1][0], av_[1][1]); du.w = pack_rne(av_[1][2], av_[1][3]);
+        const bf16x8_t pb_ = as_bf16x8(pu), db_ = as_bf16x8(du);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            // transposes: lane gets X[head 4 lg + r][d = 16 dt + lc] (exact bf16 values)
+            const f32x4_t z = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            const f32x4_t qa = mfma16(t_frag(rt, 0, dt), ident, z);
+            const f32x4_t qb = mfma16(t_frag(rt, 1, dt), ident, z);
+            const f32x4_t oa = mfma16(t_frag(rt, 2, dt), ident, z);
+            const f32x4_t ob = mfma16(t_frag(rt, 3, dt), ident, z);
+            uint4 qt, ot;
+            qt.x = pack_exact(qa[0], qa[1]); qt.y = pack_exact(qa[2], qa[3]);
+            qt.z = pack_exact(qb[0], qb[1]); qt.w = pack_exact(qb[2], qb[3]);
+            ot.x = pack_exact(oa[0], oa[1]); ot.y = pack_exact(oa[2], oa[3]);
+            ot.z = pack_exact(ob[0], ob[1]); ot.w = pack_exact(ob[2], ob[3]);
+            av[dt] = mfma32(as_bf16x8(ot), pb_, av[dt]);
+            ak[dt] = mfma32(as_bf16x8(qt), db_, ak[dt]);
+            if (dt & 1) __builtin_amdgcn_sched_barrier(0);      // two d-tiles of transposes in flight
+        }
+    };
+    const int npairs = (end - beg + 1) >> 1;
+    if (npairs > 0) issue(rt_a, beg);
+    for (int p = 0; p < npairs; ++p) {
+        const int ra = nra, rb = nrb;
+        const bool has_b = beg + 2 * p + 1 < end;
+        const float4 cl[2] = {nl[0], nl[1]}, cd[2] = {nd[0], nd[1]};
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();                      // pair p landed; pair p - 1 consumed by every wave
+        if (p & 1) {
+            if (p + 1 < npairs) issue(rt_a, beg + 2 * (p + 1));
+            compute(rt_b, ra, rb, has_b, cl, cd);
+        } else {
+            if (p + 1 < npairs) issue(rt_b, beg + 2 * (p + 1));
+            compute(rt_a, ra, rb, has_b, cl, cd);
+        }
+    }
+
+    // ---- epilogue: lane holds dV^T / dK^T[d = 16 dt + 4 lg + r][key 16 w + lc]
+    if (nseg == 1) {
+        if (key >= lim) return;
+        bf16_t* pk = dk + hoff + key * kHeadDim + 4 * lg;
+        bf16_t* pv = dv + hoff + key * kHeadDim + 4 * lg;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            uint2 a, b;
+            a.x = pack_rne(ak[dt][0] * scale, ak[dt][1] * scale);
+            a.y = pack_rne(ak[dt][2] * scale, ak[dt][3] * scale);
+            b.x = pack_rne(av[dt][0], av[dt][1]);
+            b.y = pack_rne(av[dt][2], av[dt][3]);
+            *reinterpret_cast<uint2*>(pk + 16 * dt) = a;
+            *reinterpret_cast<uint2*>(pv + 16 * dt) = b;
+        }
+    } else {
+        // fp32 partial of this segment: [2][64 keys][128 d]
+        float* pk = partial + static_cast<size_t>(item) * 2 * kPB * kHeadDim + (16 * w + lc) * kHeadDim + 4 * lg;
+        float* pv = pk + kPB * kHeadDim;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            *reinterpret_cast<float4*>(pk + 16 * dt) = make_float4(ak[dt][0], ak[dt][1], ak[dt][2], ak[dt][3]);
+            *reinterpret_cast<float4*>(pv + 16 * dt) = make_float4(av[dt][0], av[dt][1], av[dt][2], av[dt][3]);
+        }
+    }
+}
+
+// sums the segments of split columns in segment order and writes bf16 dk / dv
+__global__ __launch_bounds__(256) void bwd_col_finish(
+    const int32_t* __restrict__ item_start, const float* __restrict__ partial, int64_t lim,
+    const int64_t* __restrict__ kv_off, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv,
+    int hkv, int nblk, float scale) {
+    const int col = blockIdx.x, g = col / nblk, j = col % nblk, t = threadIdx.x;
+    const int i0 = item_start[col], n = item_start[col + 1] - i0;
+    if (n <= 1) return;
+    const int64_t cap = kv_off[1] - kv_off[0];
+    const size_t hoff = (kv_off[0] * hkv + static_cast<int64_t>(g) * cap) * kHeadDim;
+    // thread t: 32 consecutive values of the [2][64][128] partial
+    for (int e = t * 4; e < 2 * kPB * kHeadDim; e += 256 * 4) {
+        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int x = 0; x < n; ++x) {
+            const float4 p = *reinterpret_cast<const float4*>(partial + static_cast<size_t>(i0 + x) * 2 * kPB * kHeadDim + e);
+            s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+        }
+        const int which = e / (kPB * kHeadDim), rem = e % (kPB * kHeadDim);
+        const int64_t key = static_cast<int64_t>(j) * kPB + rem / kHeadDim;
+        if (key >= lim) continue;
+        const float f = which == 0 ? scale : 1.f;
+        uint2 pk;
+        pk.x = pack_rne(s.x * f, s.y * f);
+        pk.y = pack_rne(s.z * f, s.w * f);
+        bf16_t* dst = (which == 0 ? dk : dv) + hoff + key * kHeadDim + rem % kHeadDim;
+        *reinterpret_cast<uint2*>(dst) = pk;
+    }
+}
+
+hipError_t launch_attn_prefill_bwd_mfma(const Shape& sh, const BwdWs& w, const void* q, int rows,
+                                        int64_t q_start, const void* k, const void* v,
+                                        const int64_t* kv_off, const int32_t* idx,
+                                        const void* out, const void* dout, void* dq, void* dk,
+                                        void* dv, char* base, hipStream_t st) {
+    const int64_t n = q_start + rows;
+    const int64_t nblk = w.nblk;
+    float* lse2 = reinterpret_cast<float*>(base + w.lse);
+    float* delta = reinterpret_cast<float*>(base + w.delta);
+    bf16_t* kt = reinterpret_cast<bf16_t*>(base + w.kt);
+    int32_t* item_start = reinterpret_cast<int32_t*>(base + w.extra);
+    const int ncol = sh.hkv * w.nblk;
+    float* partial = reinterpret_cast<float*>(base + w.extra + align256(static_cast<size_t>(ncol + 1) * sizeof(int32_t)));
+    const float scale_log2 = sh.attn_scale * 1.4426950408889634f;
+    hipError_t e = launch_vt_build(k, kv_off, sh.hkv, n, nblk, kt, st);
+    if (e != hipSuccess) return e;
+    {
+        KernelTimer tm(INFV2_KERNEL_BWD_ROW, st);
+        const int nrg = (rows + kURows - 1) / kURows;
+        bwd_row_mfma<<<dim3(static_cast<unsigned>(nrg) * sh.hkv), kRThreads, 0, st>>>(
+            static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(out),
+            static_cast<const bf16_t*>(dout), rows, q_start, static_cast<const bf16_t*>(k),
+            static_cast<const bf16_t*>(v), kt, kv_off, idx, static_cast<bf16_t*>(dq), lse2, delta,
+            sh.hq, sh.hkv, sh.topk, nblk, nrg, scale_log2, sh.attn_scale);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if ((e = launch_inverse_index(sh, w, rows, idx, base, st)) != hipSuccess) return e;
+    const int32_t* cstart = reinterpret_cast<const int32_t*>(base + w.col_start);
+    const int32_t* list = reinterpret_cast<const int32_t*>(base + w.list);
+    KernelTimer tm(INFV2_KERNEL_BWD_COL, st);
+    bwd_items_kernel<<<1, 1024, 0, st>>>(cstart, w.nblk, ncol, item_start);
+    const int64_t items = max_col_items(sh, w);
+    bwd_col_mfma<<<dim3(static_cast<unsigned>(items)), kCThreads, 0, st>>>(
+        static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(dout), rows, q_start,
+        static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), kv_off, cstart, list,
+        w.list_ld, item_start, lse2, delta, static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv),
+        partial, sh.hq, sh.hkv, w.nblk, scale_log2, sh.attn_scale);
+    bwd_col_finish<<<dim3(static_cast<unsigned>(ncol)), 256, 0, st>>>(
+        item_start, partial, n, kv_off, static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), sh.hkv,
+        w.nblk, sh.attn_scale);
+    return hipGetLastError();
 }
 
 }  // namespace infv2

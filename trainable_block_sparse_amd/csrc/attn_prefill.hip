@@ -24,10 +24,10 @@
 // groups of one KV head.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "prefill_tiles.hpp"
 
 namespace infv2 {
 
-constexpr int kPB = 64;          // KV block size served here
 constexpr int kPRows = 16;       // query rows per thread block
 constexpr int kPWaves = 16;      // one query row per wave, four waves per SIMD
 constexpr int kPRowsW = 16 / kPWaves;                // query rows per wave
@@ -35,18 +35,10 @@ constexpr int kKBatch = 1;       // K-steps whose fragments are read from LDS at
 constexpr int kVBatch = 2;       // V^T d-tiles whose fragments are read from LDS at once
 constexpr int kTileLoads = 16 / kPWaves;             // 1 KB global->LDS loads per wave per tile
 constexpr int kPThreads = kPWaves * 64;
-constexpr int kMaxWords = 512;   // bitmap words: up to 16384 blocks
-constexpr int kUnionCap = 2048;  // union entries: 16 rows x top-k, top-k <= 128
+static_assert(kPThreads == kUThreads && kPRows == kURows, "rows and threads of the union build");
 constexpr int kGroup2 = 2;       // union blocks per LDS stage; two stages = one interval
 constexpr int kXcds = 8;         // thread blocks are dealt round-robin to the 8 XCDs
 constexpr float kRescaleSlack = 8.f;   // log2 units
-
-// V^T tiles store the 64 keys of a block in the order the P^T operand of the
-// PV product uses: position 32 kk + 8 g + 4 a + r holds key 32 kk + 16 a + 4 g + r.
-__device__ __forceinline__ int vt_key_of_pos(int pos) {
-    const int kk = pos >> 5, w = pos & 31, g = w >> 3, a = (w >> 2) & 1, r = w & 3;
-    return 32 * kk + 16 * a + 4 * g + r;
-}
 
 // vt[g][blk][d][pos] = V[g][blk*64 + key(pos)][d]; keys at or past n read as zero.
 __global__ __launch_bounds__(256) void vt_build(const bf16_t* __restrict__ v,
@@ -78,24 +70,7 @@ __global__ __launch_bounds__(256) void vt_build(const bf16_t* __restrict__ v,
     }
 }
 
-// K tile: 64 keys x 16 chunks of 16 B; chunk c of key r sits at c ^ (r & 15).
-// V^T tile: 128 d x 8 chunks of 16 B; chunk c of row d sits at c ^ ((d >> 1) & 7).
-// Both swizzles make the 16-lane 16-byte column reads below conflict-free.
-struct UnionSmem {
-    int32_t list[kUnionCap];          // union of the rows' blocks, ascending (<= 16 * topk)
-    uint32_t mask[kUnionCap];         // which of the 16 rows selected each union block
-    uint32_t bits[kMaxWords];
-    uint32_t wbase[kMaxWords];
-    uint32_t scan_tmp[kPWaves + 1];
-};
-typedef bf16_t StageTiles[kGroup2][kPB * kHeadDim];   // 2 x 16 KB (K) or 2 x 16 KB (V^T)
-
-__device__ __forceinline__ uint4 k_frag(const StageTiles& t, int slot, int key, int chunk) {
-    return *reinterpret_cast<const uint4*>(&t[slot][key * kHeadDim + 8 * (chunk ^ (key & 15))]);
-}
-__device__ __forceinline__ uint4 vt_frag(const StageTiles& t, int slot, int d, int chunk) {
-    return *reinterpret_cast<const uint4*>(&t[slot][d * kPB + 8 * (chunk ^ ((d >> 1) & 7))]);
-}
+typedef BlockTile StageTiles[kGroup2];              // 2 x 16 KB (K) or 2 x 16 KB (V^T)
 
 __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
     const bf16_t* __restrict__ q, int rows, int64_t q_start, const bf16_t* __restrict__ k,
@@ -121,44 +96,8 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
     const bf16_t* vth = vt + static_cast<int64_t>(g) * nblk * kHeadDim * kPB;
     const int64_t nlim = q_start + rows;                     // keys needed are < nlim
 
-    // ---- union of the 16 rows' selected blocks (bitmap -> ascending list + row masks)
-    const int nwords = static_cast<int>((nblk + 31) / 32);
-    for (int x = t; x < nwords; x += kPThreads) sm.bits[x] = 0u;
-    __syncthreads();
-    const int nent = kPRows * topk;
-    for (int e = t; e < nent; e += kPThreads) {
-        const int row = r0 + e / topk;
-        if (row >= rows) continue;
-        const int32_t blk = idx[(static_cast<size_t>(row) * hkv + g) * topk + e % topk];
-        if (blk >= 0 && blk < nblk) atomicOr(&sm.bits[blk >> 5], 1u << (blk & 31));
-    }
-    __syncthreads();
-    const uint32_t word_t = t < nwords ? sm.bits[t] : 0u;      // one bitmap word per thread
-    const uint32_t cnt_t = __popc(word_t);
-    const uint32_t base_t = block_incl_scan<kPWaves>(cnt_t, sm.scan_tmp) - cnt_t;
-    if (t < nwords) {
-        sm.wbase[t] = base_t;
-        uint32_t bw = word_t, pos = base_t;
-        while (bw) {
-            const int bit = __ffs(bw) - 1;
-            bw &= bw - 1;
-            sm.list[pos] = t * 32 + bit;
-            sm.mask[pos] = 0u;
-            ++pos;
-        }
-    }
-    if (t == kPThreads - 1) sm.scan_tmp[kPWaves] = base_t + cnt_t;
-    __syncthreads();
-    const int n_u = static_cast<int>(sm.scan_tmp[kPWaves]);
-    for (int e = t; e < nent; e += kPThreads) {
-        const int tok = e / topk, row = r0 + tok;
-        if (row >= rows) continue;
-        const int32_t blk = idx[(static_cast<size_t>(row) * hkv + g) * topk + e % topk];
-        if (blk < 0 || blk >= nblk) continue;
-        const uint32_t word = sm.bits[blk >> 5];
-        const uint32_t pos = sm.wbase[blk >> 5] + __popc(word & ((1u << (blk & 31)) - 1u));
-        atomicOr(&sm.mask[pos], 1u << tok);
-    }
+    // ---- union of the 16 rows' selected blocks (ascending list + row masks)
+    const int n_u = build_union(sm, idx, rows, r0, hkv, g, topk, nblk);
 
     // ---- per-wave row state: wave w owns rows r0 + 8 i + w (i < 2)
     bf16x8_t qf[kPRowsW][4];
@@ -236,7 +175,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
 #pragma unroll
             for (int ks = 0; ks < kKBatch; ++ks)
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) kf[ks][mt] = k_frag(kt, slot, 16 * mt + lc, 4 * (kb + ks) + lg);
+                for (int mt = 0; mt < 4; ++mt) kf[ks][mt] = k_frag(kt[slot], 16 * mt + lc, 4 * (kb + ks) + lg);
 #pragma unroll
             for (int i = 0; i < kPRowsW; ++i) {
                 if (!((act >> i) & 1u)) continue;
@@ -308,8 +247,8 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
             uint4 vf[kVBatch][2];
 #pragma unroll
             for (int x = 0; x < kVBatch; ++x) {
-                vf[x][0] = vt_frag(vtt, slot, 16 * (mb + x) + lc, lg);
-                vf[x][1] = vt_frag(vtt, slot, 16 * (mb + x) + lc, 4 + lg);
+                vf[x][0] = vt_frag(vtt[slot], 16 * (mb + x) + lc, lg);
+                vf[x][1] = vt_frag(vtt[slot], 16 * (mb + x) + lc, 4 + lg);
             }
 #pragma unroll
             for (int x = 0; x < kVBatch; ++x)
@@ -356,6 +295,14 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
     }
 }
 
+hipError_t launch_vt_build(const void* src, const int64_t* kv_off, int hkv, int64_t n,
+                           int64_t nblk, void* dst, hipStream_t st) {
+    KernelTimer kt(INFV2_KERNEL_VT_BUILD, st);
+    vt_build<<<dim3(static_cast<unsigned>(nblk), hkv), 256, 0, st>>>(
+        static_cast<const bf16_t*>(src), kv_off, hkv, n, nblk, static_cast<bf16_t*>(dst));
+    return hipGetLastError();
+}
+
 bool attn_prefill_mfma_ok(const Shape& sh) {
     return sh.io_bf16 && sh.m == kPB && kPRows * sh.topk <= kUnionCap;
 }
@@ -372,12 +319,7 @@ hipError_t launch_attn_prefill_mfma(const Shape& sh, const void* q, int rows, in
     const int64_t n = q_start + rows;
     const int64_t nblk = (n + kPB - 1) / kPB;
     bf16_t* vt = static_cast<bf16_t*>(ws);
-    {
-        KernelTimer kt(INFV2_KERNEL_VT_BUILD, st);
-        vt_build<<<dim3(static_cast<unsigned>(nblk), sh.hkv), 256, 0, st>>>(
-            static_cast<const bf16_t*>(v), kv_off, sh.hkv, n, nblk, vt);
-    }
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_vt_build(v, kv_off, sh.hkv, n, nblk, vt, st);
     if (e != hipSuccess) return e;
     const float scale_log2 = sh.attn_scale * 1.4426950408889634f;
     KernelTimer kt(INFV2_KERNEL_ATTN_PREFILL, st);

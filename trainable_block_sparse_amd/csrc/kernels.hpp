@@ -82,6 +82,9 @@ hipError_t launch_attn_decode_merge(const Shape& sh, const float* part_o, const 
                                     void* out, int batch, int nsplit, hipStream_t st);
 
 bool attn_prefill_mfma_ok(const Shape& sh);
+// transposed 64-key tiles of K or V for the matrix-core prefill kernels
+hipError_t launch_vt_build(const void* src, const int64_t* kv_off, int hkv, int64_t n,
+                           int64_t nblk, void* dst, hipStream_t st);
 size_t attn_prefill_ws_bytes(const Shape& sh, int64_t max_len);
 hipError_t launch_attn_prefill_mfma(const Shape& sh, const void* q, int rows, int64_t q_start,
                                     const void* k, const void* v, const int64_t* kv_off,
@@ -93,13 +96,14 @@ hipError_t launch_attn_prefill(const Shape& sh, const void* q, int rows, int64_t
 
 // backward of the prefill attention (attn_bwd.hip, attn_bwd_mfma.hip)
 struct BwdWs {
-    size_t lse, delta, counts, totals, col_start, list, kt, total;
+    size_t lse, delta, counts, totals, col_start, list, kt, extra, total;
     int nblk, nchunk;
     int64_t list_ld;
 };
 BwdWs bwd_ws(const Shape& sh, int rows, int64_t max_len);
 bool bwd_mfma_ok(const Shape& sh);
 size_t bwd_kt_bytes(const Shape& sh, int64_t max_len);
+size_t bwd_mfma_extra_bytes(const Shape& sh, const BwdWs& w);
 hipError_t launch_inverse_index(const Shape& sh, const BwdWs& w, int rows, const int32_t* idx,
                                 char* base, hipStream_t st);
 hipError_t launch_attn_prefill_bwd(const Shape& sh, const void* q, int rows, int64_t q_start,

@@ -1,0 +1,96 @@
+// Shared pieces of the prefill kernels that stream each selected block through
+// LDS once per group of 16 consecutive query rows (forward attention and the
+// row pass of its backward): the union of the rows' selected blocks (ascending
+// list of distinct blocks and, per block, the mask of the rows that selected
+// it) and the swizzled LDS tiles of a 64-key block.
+#pragma once
+
+#include "common.hpp"
+
+namespace infv2 {
+
+constexpr int kURows = 16;        // query rows per group
+constexpr int kUWaves = 16;       // waves of the thread blocks that build it
+constexpr int kUThreads = kUWaves * 64;
+constexpr int kUMaxWords = 512;   // bitmap words: up to 16384 blocks
+constexpr int kUnionCap = 2048;   // union entries: 16 rows x top-k, top-k <= 128
+
+struct UnionSmem {
+    int32_t list[kUnionCap];          // union of the rows' blocks, ascending (<= 16 * topk)
+    uint32_t mask[kUnionCap];         // which of the 16 rows selected each union block
+    uint32_t bits[kUMaxWords];
+    uint32_t wbase[kUMaxWords];
+    uint32_t scan_tmp[kUWaves + 1];
+};
+
+// Called by all kUThreads threads; returns the number of union blocks (the
+// list and masks are valid after the call's final barrier).  Entries < 0 or
+// >= nblk are ignored; rows >= rows_total contribute nothing.
+__device__ inline int build_union(UnionSmem& sm, const int32_t* __restrict__ idx, int rows_total,
+                                  int r0, int hkv, int g, int topk, int64_t nblk) {
+    const int t = threadIdx.x;
+    const int nwords = static_cast<int>((nblk + 31) / 32);
+    for (int x = t; x < nwords; x += kUThreads) sm.bits[x] = 0u;
+    __syncthreads();
+    const int nent = kURows * topk;
+    for (int e = t; e < nent; e += kUThreads) {
+        const int row = r0 + e / topk;
+        if (row >= rows_total) continue;
+        const int32_t blk = idx[(static_cast<size_t>(row) * hkv + g) * topk + e % topk];
+        if (blk >= 0 && blk < nblk) atomicOr(&sm.bits[blk >> 5], 1u << (blk & 31));
+    }
+    __syncthreads();
+    const uint32_t word_t = t < nwords ? sm.bits[t] : 0u;      // one bitmap word per thread
+    const uint32_t cnt_t = __popc(word_t);
+    const uint32_t base_t = block_incl_scan<kUWaves>(cnt_t, sm.scan_tmp) - cnt_t;
+    if (t < nwords) {
+        sm.wbase[t] = base_t;
+        uint32_t bw = word_t, pos = base_t;
+        while (bw) {
+            const int bit = __ffs(bw) - 1;
+            bw &= bw - 1;
+            sm.list[pos] = t * 32 + bit;
+            sm.mask[pos] = 0u;
+            ++pos;
+        }
+    }
+    if (t == kUThreads - 1) sm.scan_tmp[kUWaves] = base_t + cnt_t;
+    __syncthreads();
+    const int n_u = static_cast<int>(sm.scan_tmp[kUWaves]);
+    for (int e = t; e < nent; e += kUThreads) {
+        const int tok = e / topk, row = r0 + tok;
+        if (row >= rows_total) continue;
+        const int32_t blk = idx[(static_cast<size_t>(row) * hkv + g) * topk + e % topk];
+        if (blk < 0 || blk >= nblk) continue;
+        const uint32_t word = sm.bits[blk >> 5];
+        const uint32_t pos = sm.wbase[blk >> 5] + __popc(word & ((1u << (blk & 31)) - 1u));
+        atomicOr(&sm.mask[pos], 1u << tok);
+    }
+    __syncthreads();
+    return n_u;
+}
+
+constexpr int kPB = 64;           // KV block size of the matrix-core prefill kernels
+
+// K tile: 64 keys x 16 chunks of 16 B; chunk c of key r sits at c ^ (r & 15).
+// Transposed tile (V^T, K^T): 128 d x 8 chunks of 16 B; chunk c of row d sits at
+// c ^ ((d >> 1) & 7).  Both swizzles make 16-lane 16-byte column reads conflict-free.
+typedef bf16_t BlockTile[kPB * kHeadDim];            // 16 KB
+
+__device__ __forceinline__ uint4 k_frag(const BlockTile& t, int key, int chunk) {
+    return *reinterpret_cast<const uint4*>(&t[key * kHeadDim + 8 * (chunk ^ (key & 15))]);
+}
+__device__ __forceinline__ uint4 vt_frag(const BlockTile& t, int d, int chunk) {
+    return *reinterpret_cast<const uint4*>(&t[d * kPB + 8 * (chunk ^ ((d >> 1) & 7))]);
+}
+
+// Transposed tiles store the 64 keys of a block in the order the P^T operand of
+// a 16x16x32 product over keys uses (the accumulator layout of S^T = K Q^T, two
+// 16-key tiles per K-step): position 32 kk + 8 g + 4 a + r holds key
+// 32 kk + 16 a + 4 g + r.
+__device__ __forceinline__ int vt_key_of_pos(int pos) {
+    const int kk = pos >> 5, w = pos & 31, g = w >> 3, a = (w >> 2) & 1, r = w & 3;
+    return 32 * kk + 16 * a + 4 * g + r;
+}
+
+}  // namespace infv2
