@@ -11,7 +11,8 @@ reads its compressed keys and selected K/V from HBM rather than from the 256 MiB
 Infinity Cache.  Inputs are resident in HBM before timing starts.
 
 Also reported on the same line: 32K chunked prefill (TFLOPS of useful
-selected-block attention FLOPs), batched decode of 16 sequences of 64K-128K,
+selected-block attention FLOPs), the 32K training backward (gradients of q, K
+and V through the sparse attention), batched decode of 16 sequences of 64K-128K,
 the roofline fraction of the dominant kernel, and the float64 CPU oracle timed
 on this host on a bounded sample.
 
@@ -518,6 +519,87 @@ def bench_varlen_prefill(args, torch, tbs, gh) -> dict:
             "tflops_path": useful / (tm.sum() * 1e-3) / 1e12}
 
 
+BACKWARD_FAMILIES = ("vt_build", "bwd_row", "bwd_index", "bwd_col")
+
+
+def bench_backward(args, torch, tbs, gh, pre: dict) -> dict:
+    """Training backward of the 32K prefill: gradients of all 32768 rows in one
+    call (dq, and dk / dv of the whole sequence), on the forward's selection and
+    output.  Algorithmic FLOPs: the five products of an attention backward
+    (S, dP, dQ, dK, dV), 10 d FLOPs per (head, attended token)."""
+    from synth import upstream_grad
+    wl = pre["_wl"]
+    L = int(wl.lens[0])
+    dev = gh.DeviceWorkload(wl, args.ck_dtype)
+    idx, _, out = dev.prefill(wl.chunk)
+    dout = gh.to_device(upstream_grad(wl))
+    dq = torch.empty_like(dev.q)
+    dk = torch.empty_like(dev.k)
+    dv = torch.empty_like(dev.v)
+    ws = dev.ws(tbs.OP_ATTN_PREFILL_BWD, L, 1, L)
+    cfg = dev.cfg
+    T = Timer(torch)
+
+    def run(t=0):
+        tbs.infv2_sparse_attn_prefill_bwd(cfg, dev.q, L, 0, dev.k, dev.v, dev.kv_offsets, idx, out,
+                                          dout, dq, dk, dv, ws)
+
+    run()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(max(1, args.prefill_reps)):
+        e0 = T.event()
+        run()
+        e1 = T.event()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    gi = idx.cpu().numpy()
+    G, d = wl.num_q_heads // wl.num_kv_heads, wl.head_dim
+    tok = float(attended_tokens(gi, np.arange(L), np.full(L, L), wl.block_size).sum())
+    algo = 10.0 * d * G * tok
+    kt = kernel_times(tbs, torch, run, max(1, args.prefill_reps), BACKWARD_FAMILIES)
+    # algorithmic products per kernel: row pass S, dP, dQ; column pass dK, dV
+    # (it also recomputes S and dP, counted in "performed" only)
+    work = {"bwd_row": 6.0 * d * G * tok / kt["bwd_row"]["launches_per_step"],
+            "bwd_col": 4.0 * d * G * tok / kt["bwd_col"]["launches_per_step"]}
+    roof = roofline_of(kt, work, "mfma", BF16_PEAK_TFLOPS, "TFLOP/s", 1e12)
+    if roof["kernel"] == "bwd_col":
+        roof["performed_frac"] = roof["frac"] * 2.0
+    roof["traffic"] = None
+    per_kernel = {f: {"tflops_algorithmic": w / (kt[f]["us_per_launch"] * 1e-6) / 1e12,
+                      "frac": w / (kt[f]["us_per_launch"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS}
+                  for f, w in work.items()}
+    # sampled parity: dq of a few rows against the oracle (float64)
+    parity = backward_spot_parity(wl, gi, dq, dout, torch, gh)
+    return {"workload": "prefill_backward_bf16_32k", "rows": L, "ms": ms,
+            "algorithmic_flops": algo, "tflops": algo / (ms * 1e-3) / 1e12,
+            "attended_tokens_per_row_head": tok / (L * wl.num_kv_heads),
+            "kernels": kt, "per_kernel": per_kernel, "roofline": roof, "parity": parity}
+
+
+def backward_spot_parity(wl, gi, dq_t, dout_t, torch, gh) -> str:
+    from oracle import infv2_ref as ref
+    prm = ref.Params(head_dim=128, num_q_heads=32, num_kv_heads=2, block_size=64, kernel_size=32,
+                     kernel_stride=16, topk=64, init_blocks=1, local_blocks=4)
+    K, V = wl.k_f64(0), wl.v_f64(0)
+    q = wl.decoded(wl.q)
+    dout = gh.from_device(dout_t, "bf16")
+    dq = gh.from_device(dq_t, "bf16")
+    L = q.shape[0]
+    worst = 0.0
+    for i in (0, 4095, L // 2, L - 1):
+        for g in range(2):
+            hs = slice(16 * g, 16 * g + 16)
+            want = ref.attend_row_grad(q[i, hs], K[g], V[g], i, gi[i, g], prm, dout[i, hs])[0]
+            s = max(1.0, float(np.abs(want).max()))
+            err = np.abs(dq[i, hs] - want) / s - (2e-2 + 1e-2 * np.abs(want) / s)
+            worst = max(worst, float(np.abs(dq[i, hs] - want).max() / s))
+            if err.max() > 0:
+                return f"FAIL dq row {i} head {g}: scaled err {worst:.2e}"
+    return f"ok: dq of 4 rows x 2 heads vs the float64 oracle, scaled max err {worst:.1e}"
+
+
 def bench_batched(args, torch, tbs, gh, ck_dtype=None) -> dict:
     # one step reads ~160 MiB, so three replicas already keep the MALL cold
     return bench_decode(4, args, torch, tbs, gh, replicas=min(args.replicas, 4), ck_dtype=ck_dtype)
@@ -606,13 +688,14 @@ def main() -> int:
     ap.add_argument("--no-batched", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-loop", action="store_true", help="skip the append + select + attend loop record")
+    ap.add_argument("--no-backward", action="store_true", help="skip the 32K training-backward record")
     ap.add_argument("--no-ck-bf16", action="store_true",
                     help="skip the extra decode records with bf16 compressed keys")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run 8 device-to-device copies of MIB MiB (reference kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--only", choices=["decode", "prefill", "batched"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "batched", "backward"], default=None,
                     help="run one workload only and print its record (for profiling)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -645,6 +728,9 @@ def main() -> int:
             rec = bench_decode(2, args, torch, tbs, gh, replicas=args.replicas)
         elif args.only == "prefill":
             rec = {k: v for k, v in bench_prefill(args, torch, tbs, gh).items() if not k.startswith("_")}
+        elif args.only == "backward":
+            from synth import make_config
+            rec = bench_backward(args, torch, tbs, gh, {"_wl": make_config(3)})
         else:
             rec = bench_batched(args, torch, tbs, gh)
         print(json.dumps({"only": args.only, "record": rec}))
@@ -663,6 +749,10 @@ def main() -> int:
     if varlen:
         log(f"varlen prefill 8 x 4K-16K: attn {varlen['attn_ms']:.2f} ms, total {varlen['total_ms']:.2f} ms, "
             f"{varlen['tflops_attn']:.1f} TFLOPS")
+    bwd = None if (args.no_prefill or args.no_backward) else bench_backward(args, torch, tbs, gh, pre)
+    if bwd:
+        log(f"backward 32K (training, one call): {bwd['ms']:.2f} ms, {bwd['tflops']:.1f} TFLOPS "
+            f"algorithmic; {bwd['parity']}")
     loop = None if args.no_loop else bench_decode_loop(args, torch, tbs, gh)
     if loop:
         log(f"decode loop 128K (append + select + attend): {loop['ms_per_step_graph'] * 1e3:.1f} us/step")
@@ -703,6 +793,8 @@ def main() -> int:
         out["decode_loop_128k"] = loop
     if varlen:
         out["prefill_varlen_8x4k-16k"] = varlen
+    if bwd:
+        out["prefill_backward_32k"] = bwd
     for k2, r2 in alt.items():
         out[k2] = {x: r2[x] for x in ("workload", "batch", "ms_per_step", "tok_per_s", "hbm_gbps_step",
                                       "per_call_us", "kernels", "bytes_per_step", "roofline", "parity")}

@@ -23,8 +23,9 @@
 //   P = 2^(S scale - lse), dA = P (dP - D)
 //   dV^T += dO^T . P,  dK^T += Q^T . dA 16 MFMA
 // The Q^T and dO^T operands (heads along the contraction) are produced from the
-// row-major tiles by one 16x16x16 product with the identity per 16x16 tile,
-// which lands each value exactly where the operand layout wants it.  The pairs'
+// S / dP operands themselves by a 16x16x32 product with a 0/1 selector of 16 of
+// the 32 columns, which lands each value exactly where the operand layout wants
+// it (and reads LDS only in the conflict-free 16-byte pattern).  The pairs'
 // Q and dO tiles are double-buffered in LDS with direct global->LDS loads.
 // A block whose list is longer than kSeg rows is split into segments whose
 // fp32 partials are summed in segment order by bwd_col_finish, so results do
@@ -293,12 +294,18 @@ __global__ __launch_bounds__(1024) void bwd_items_kernel(const int32_t* __restri
     if (t == 0) item_start[ncol] = static_cast<int32_t>(carry);
 }
 
-// identity operand of the 16x16x16 product: lane holds I[4 lg + e][lc]
-__device__ __forceinline__ s16x4_t identity_b(int lg, int lc) {
-    s16x4_t b;
+// selector operand of the 16x16x32 product that picks columns 16 h .. 16 h + 15 of
+// A: lane holds B[8 lg + e][lc] = 1 if 8 lg + e == 16 h + lc, else 0
+__device__ __forceinline__ bf16x8_t select_b(int h, int lg, int lc) {
+    uint4 u;
+    uint32_t* w = reinterpret_cast<uint32_t*>(&u);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) b[e] = (4 * lg + e == lc) ? static_cast<short>(0x3F80) : static_cast<short>(0);
-    return b;
+    for (int e2 = 0; e2 < 4; ++e2) {
+        const uint32_t lo = (8 * lg + 2 * e2 == 16 * h + lc) ? 0x3F80u : 0u;
+        const uint32_t hi = (8 * lg + 2 * e2 + 1 == 16 * h + lc) ? 0x3F80u : 0u;
+        w[e2] = lo | (hi << 16);
+    }
+    return as_bf16x8(u);
 }
 
 typedef bf16_t RowTiles[4][kGroup * kHeadDim];   // Q_A, Q_B, dO_A, dO_B (4 KB each)
@@ -343,7 +350,7 @@ __global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
     f32x4_t av[8], ak[8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) { av[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f}; ak[dt] = av[dt]; }
-    const s16x4_t ident = identity_b(lg, lc);
+    const bf16x8_t sel0 = select_b(0, lg, lc), sel1 = select_b(1, lg, lc);
 
     // stage slot t of each tile: head h = t / 16 holds chunk (t % 16) ^ h there
     const int sh_h = t >> 4, sh_c = (t & 15) ^ (t >> 4);
@@ -371,13 +378,10 @@ __global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
         const int c = 4 * ks + lg;
         return as_bf16x8(*reinterpret_cast<const uint4*>(&rt[x][lc * kHeadDim + 8 * (c ^ lc)]));
     };
-    // A operand of the identity product: lane holds X[head lc][d = 16 dt + 4 lg .. + 4]
-    auto t_frag = [&](const RowTiles& rt, int x, int dt) {
-        const int c = 2 * dt + (lg >> 1);
-        return *reinterpret_cast<const s16x4_t*>(&rt[x][lc * kHeadDim + 8 * (c ^ lc) + 4 * (lg & 1)]);
-    };
-    auto compute = [&](const RowTiles& rt, int ra, int rb, bool has_b, const float4 (&cl)[2],
-                       const float4 (&cd)[2]) {
+    // fr[x][ks] = a_frag(x, ks): every LDS read of a pair happens before the next
+    // pair's loads are issued, so its products overlap those loads
+    auto compute = [&](const bf16x8_t (&fr)[4][4], int ra, int rb, bool has_b,
+                       const float4 (&cl)[2], const float4 (&cd)[2]) {
         f32x4_t s[2], dp[2];
 #pragma unroll
         for (int x = 0; x < 2; ++x) { s[x] = f32x4_t{0.f, 0.f, 0.f, 0.f}; dp[x] = s[x]; }
@@ -385,8 +389,8 @@ __global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
         for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
-                s[x] = mfma32(a_frag(rt, x, ks), kf[ks], s[x]);
-                dp[x] = mfma32(a_frag(rt, 2 + x, ks), vf[ks], dp[x]);
+                s[x] = mfma32(fr[x][ks], kf[ks], s[x]);
+                dp[x] = mfma32(fr[2 + x][ks], vf[ks], dp[x]);
             }
         }
         // lane holds S[head 4 lg + r][key 16 w + lc] of rows A (x = 0) and B (x = 1)
@@ -412,12 +416,14 @@ __global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
         const bf16x8_t pb_ = as_bf16x8(pu), db_ = as_bf16x8(du);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-            // transposes: lane gets X[head 4 lg + r][d = 16 dt + lc] (exact bf16 values)
+            // transposes: lane gets X[head 4 lg + r][d = 16 dt + lc] (exact bf16
+            // values), d-tile dt being half dt % 2 of the S / dP operand of K-step dt / 2
             const f32x4_t z = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            const f32x4_t qa = mfma16(t_frag(rt, 0, dt), ident, z);
-            const f32x4_t qb = mfma16(t_frag(rt, 1, dt), ident, z);
-            const f32x4_t oa = mfma16(t_frag(rt, 2, dt), ident, z);
-            const f32x4_t ob = mfma16(t_frag(rt, 3, dt), ident, z);
+            const bf16x8_t sel = (dt & 1) ? sel1 : sel0;
+            const f32x4_t qa = mfma32(fr[0][dt >> 1], sel, z);
+            const f32x4_t qb = mfma32(fr[1][dt >> 1], sel, z);
+            const f32x4_t oa = mfma32(fr[2][dt >> 1], sel, z);
+            const f32x4_t ob = mfma32(fr[3][dt >> 1], sel, z);
             uint4 qt, ot;
             qt.x = pack_exact(qa[0], qa[1]); qt.y = pack_exact(qa[2], qa[3]);
             qt.z = pack_exact(qb[0], qb[1]); qt.w = pack_exact(qb[2], qb[3]);
@@ -428,6 +434,13 @@ __global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
             if (dt & 1) __builtin_amdgcn_sched_barrier(0);      // two d-tiles of transposes in flight
         }
     };
+    auto load_frags = [&](const RowTiles& rt, bf16x8_t (&fr)[4][4]) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) fr[x][ks] = a_frag(rt, x, ks);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    };
     const int npairs = (end - beg + 1) >> 1;
     if (npairs > 0) issue(rt_a, beg);
     for (int p = 0; p < npairs; ++p) {
@@ -436,13 +449,15 @@ __global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
         const float4 cl[2] = {nl[0], nl[1]}, cd[2] = {nd[0], nd[1]};
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();                      // pair p landed; pair p - 1 consumed by every wave
+        bf16x8_t fr[4][4];
         if (p & 1) {
+            load_frags(rt_b, fr);
             if (p + 1 < npairs) issue(rt_a, beg + 2 * (p + 1));
-            compute(rt_b, ra, rb, has_b, cl, cd);
         } else {
+            load_frags(rt_a, fr);
             if (p + 1 < npairs) issue(rt_b, beg + 2 * (p + 1));
-            compute(rt_a, ra, rb, has_b, cl, cd);
         }
+        compute(fr, ra, rb, has_b, cl, cd);
     }
 
     // ---- epilogue: lane holds dV^T / dK^T[d = 16 dt + 4 lg + r][key 16 w + lc]

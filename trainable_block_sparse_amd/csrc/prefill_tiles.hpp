@@ -10,7 +10,7 @@
 namespace infv2 {
 
 constexpr int kURows = 16;        // query rows per group
-constexpr int kUWaves = 16;       // waves of the thread blocks that build it
+constexpr int kUWaves = 16;       // most waves of the thread blocks that build it
 constexpr int kUThreads = kUWaves * 64;
 constexpr int kUMaxWords = 512;   // bitmap words: up to 16384 blocks
 constexpr int kUnionCap = 2048;   // union entries: 16 rows x top-k, top-k <= 128
@@ -23,17 +23,21 @@ struct UnionSmem {
     uint32_t scan_tmp[kUWaves + 1];
 };
 
-// Called by all kUThreads threads; returns the number of union blocks (the
-// list and masks are valid after the call's final barrier).  Entries < 0 or
-// >= nblk are ignored; rows >= rows_total contribute nothing.
+// Called by all kThreads threads (kThreads >= 512, so that one bitmap word per
+// thread covers 16384 blocks); returns the number of union blocks (the list and
+// masks are valid after the call's final barrier).  Entries < 0 or >= nblk are
+// ignored; rows >= rows_total contribute nothing.
+template <int kThreads = kUThreads>
 __device__ inline int build_union(UnionSmem& sm, const int32_t* __restrict__ idx, int rows_total,
                                   int r0, int hkv, int g, int topk, int64_t nblk) {
+    static_assert(kThreads >= kUMaxWords && kThreads <= kUThreads && kThreads % 64 == 0, "threads");
+    constexpr int kWaves = kThreads / 64;
     const int t = threadIdx.x;
     const int nwords = static_cast<int>((nblk + 31) / 32);
-    for (int x = t; x < nwords; x += kUThreads) sm.bits[x] = 0u;
+    for (int x = t; x < nwords; x += kThreads) sm.bits[x] = 0u;
     __syncthreads();
     const int nent = kURows * topk;
-    for (int e = t; e < nent; e += kUThreads) {
+    for (int e = t; e < nent; e += kThreads) {
         const int row = r0 + e / topk;
         if (row >= rows_total) continue;
         const int32_t blk = idx[(static_cast<size_t>(row) * hkv + g) * topk + e % topk];
@@ -42,7 +46,7 @@ __device__ inline int build_union(UnionSmem& sm, const int32_t* __restrict__ idx
     __syncthreads();
     const uint32_t word_t = t < nwords ? sm.bits[t] : 0u;      // one bitmap word per thread
     const uint32_t cnt_t = __popc(word_t);
-    const uint32_t base_t = block_incl_scan<kUWaves>(cnt_t, sm.scan_tmp) - cnt_t;
+    const uint32_t base_t = block_incl_scan<kWaves>(cnt_t, sm.scan_tmp) - cnt_t;
     if (t < nwords) {
         sm.wbase[t] = base_t;
         uint32_t bw = word_t, pos = base_t;
@@ -54,10 +58,10 @@ __device__ inline int build_union(UnionSmem& sm, const int32_t* __restrict__ idx
             ++pos;
         }
     }
-    if (t == kUThreads - 1) sm.scan_tmp[kUWaves] = base_t + cnt_t;
+    if (t == kThreads - 1) sm.scan_tmp[kUWaves] = base_t + cnt_t;
     __syncthreads();
     const int n_u = static_cast<int>(sm.scan_tmp[kUWaves]);
-    for (int e = t; e < nent; e += kUThreads) {
+    for (int e = t; e < nent; e += kThreads) {
         const int tok = e / topk, row = r0 + tok;
         if (row >= rows_total) continue;
         const int32_t blk = idx[(static_cast<size_t>(row) * hkv + g) * topk + e % topk];
