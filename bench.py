@@ -101,7 +101,8 @@ def roofline_of(times: dict, work: dict, bound: str, peak: float, unit: str, sca
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCE = {"attn_decode": "attn_decode.hip", "select_logits": "select.hip",
-                 "attn_prefill": "attn_prefill.hip"}
+                 "attn_prefill": "attn_prefill.hip", "bwd_row": "attn_bwd_mfma.hip",
+                 "bwd_col": "attn_bwd_mfma.hip"}
 
 
 def source_digest(kernel: str) -> str:
@@ -566,7 +567,7 @@ def bench_backward(args, torch, tbs, gh, pre: dict) -> dict:
     roof = roofline_of(kt, work, "mfma", BF16_PEAK_TFLOPS, "TFLOP/s", 1e12)
     if roof["kernel"] == "bwd_col":
         roof["performed_frac"] = roof["frac"] * 2.0
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(roof["kernel"])
     per_kernel = {f: {"tflops_algorithmic": w / (kt[f]["us_per_launch"] * 1e-6) / 1e12,
                       "frac": w / (kt[f]["us_per_launch"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS}
                   for f, w in work.items()}
