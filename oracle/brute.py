@@ -34,9 +34,24 @@ def brute_compress(K: Sequence[Sequence[float]], upto: int, p: int, s: int) -> L
     return out
 
 
+def brute_coarse_lse(qg, K, i: int, coarse: int, score_scale: float = 1.0):
+    """Per-head LogSumExp over the coarse kernels (spans of ``coarse`` tokens at
+    stride ``coarse``) lying wholly in [0, i]; None if there is none."""
+    kb = brute_compress(K, i + 1, coarse, coarse)
+    if not kb:
+        return None
+    out = []
+    for h in range(len(qg)):
+        z = [score_scale * math.fsum(qg[h][e] * row[e] for e in range(len(row))) for row in kb]
+        top = max(z)
+        out.append(top + math.log(math.fsum(math.exp(v - top) for v in z)))
+    return out
+
+
 def brute_block_scores(qg, K, i: int, m: int, p: int, s: int, score_scale: float = 1.0,
-                       round_ck=None):
-    """Block scores S_j (j = 0..floor(i/m)) for query heads ``qg`` at position i."""
+                       round_ck=None, lse_override=None):
+    """Block scores S_j (j = 0..floor(i/m)) for query heads ``qg`` at position i
+    (with ``lse_override`` as the per-head normaliser when given)."""
     G = len(qg)
     kb = brute_compress(K, i + 1, p, s)
     if round_ck is not None:
@@ -50,6 +65,8 @@ def brute_block_scores(qg, K, i: int, m: int, p: int, s: int, score_scale: float
             continue
         top = max(z[h])
         lse.append(top + math.log(math.fsum(math.exp(v - top) for v in z[h])))
+    if lse_override is not None and kb:
+        lse = list(lse_override)
     R = [math.fsum(math.exp(z[h][j] - lse[h]) for h in range(G)) / G for j in range(len(kb))]
     c = i // m
     S = []

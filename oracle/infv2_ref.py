@@ -208,12 +208,16 @@ def forced_blocks(c: int, init: int, local: int) -> np.ndarray:
     return f
 
 
-def select_row(qg: np.ndarray, ckg: np.ndarray, i: int, prm: Params) -> RowSelection:
+def select_row(qg: np.ndarray, ckg: np.ndarray, i: int, prm: Params,
+               lse: Optional[np.ndarray] = None) -> RowSelection:
     """Block scores and top-k selection for query position i of one group.
 
     qg: [G][d] the group's query heads (float64); ckg: [n_c][d] compressed keys
-    of the group's KV head (at least the kernels visible to row i).
+    of the group's KV head (at least the kernels visible to row i).  lse: a
+    per-head normaliser to use in place of the exact LogSumExp of pass 1 (the
+    coarse approximation, select_row_coarse); None takes the exact one.
     """
+    lse_in = lse
     m, p, s = prm.block_size, prm.kernel_size, prm.kernel_stride
     G = qg.shape[0]
     vis = num_kernels(i + 1, p, s)               # kernels lying wholly in [0, i]
@@ -225,6 +229,8 @@ def select_row(qg: np.ndarray, ckg: np.ndarray, i: int, prm: Params) -> RowSelec
     if vis > 0:
         zmax = z.max(axis=1)
         lse = zmax + np.log(np.exp(z - zmax[:, None]).sum(axis=1))
+        if lse_in is not None:
+            lse = np.asarray(lse_in, dtype=np.float64)
         prob = np.exp(z - lse[:, None])          # r_kernel per head
         # [IV2 Query group sharing, eq. r_group]: mean over the group's heads
         R = prob.sum(axis=0) / G
@@ -254,6 +260,30 @@ def select_row(qg: np.ndarray, ckg: np.ndarray, i: int, prm: Params) -> RowSelec
     sel[:chosen.shape[0]] = chosen
     return RowSelection(sel=sel, S=S, forced=forced, R=R, lse=lse, z=z, dense=dense,
                         kprime=kprime)
+
+
+def coarse_lse(qg: np.ndarray, ckcg: np.ndarray, i: int, prm: Params, coarse: int):
+    """[IV2 Efficient LSE approximation]: the per-head LogSumExp of pass 1 taken
+    over coarse kernels instead of the fine ones.  Reading: a coarse kernel is a
+    span of `coarse` tokens at stride `coarse` (complete ones only, as for the
+    fine kernels), its key the mean of those keys (compress_keys(K, coarse,
+    coarse)), and row i sees it when it lies wholly in [0, i].  Its logits use
+    the same score_scale.  Returns None when row i sees no coarse kernel.
+    """
+    vis = num_kernels(i + 1, coarse, coarse)
+    if vis == 0:
+        return None
+    z = prm.score_scale * (qg @ ckcg[:vis].T)
+    zmax = z.max(axis=1)
+    return zmax + np.log(np.exp(z - zmax[:, None]).sum(axis=1))
+
+
+def select_row_coarse(qg: np.ndarray, ckg: np.ndarray, ckcg: np.ndarray, i: int, prm: Params,
+                      coarse: int) -> RowSelection:
+    """Selection with the coarse-kernel LogSumExp in pass 1 and the fine kernels
+    in pass 2 ([IV2 Efficient LSE approximation; Complexity analysis, Stage 1]).
+    A row that sees no coarse kernel keeps the exact normaliser."""
+    return select_row(qg, ckg, i, prm, lse=coarse_lse(qg, ckcg, i, prm, coarse))
 
 
 # ---------------------------------------------------------------------------

@@ -556,3 +556,70 @@ def test_backward_row_without_visible_tokens_is_zero():
     dQ2, dK2, dV2, _ = ref.attention_backward(np.delete(q, 1, 0), K, V, [p for r, p in enumerate(pos) if r != 1],
                                               np.delete(sel, 1, 0), prm, np.delete(dout, 1, 0))
     assert np.allclose(dK, dK2, atol=1e-14) and np.allclose(dV, dV2, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# coarse-kernel LogSumExp (the pages' approximate pass 1)
+# ---------------------------------------------------------------------------
+def test_coarse_lse_equals_exact_when_coarse_kernels_are_the_fine_ones():
+    """[IV2 Efficient LSE approximation]: with non-overlapping fine kernels
+    (p = s) and coarse size s, the coarse kernels are the fine kernels, so the
+    approximation is exact: same normaliser, scores and selection."""
+    prm = _params(kernel_size=4, kernel_stride=4, topk=4, local_blocks=1)
+    rng = np.random.default_rng(60)
+    n = 140
+    K = rng.standard_normal((2, n, 16))
+    q = rng.standard_normal((n, 4, 16))
+    ck = ref.compress_keys(K, 4, 4, "fp64")
+    for i in (15, 64, 99, 139):
+        for g in range(2):
+            qg = q[i, 2 * g:2 * g + 2]
+            a = ref.select_row(qg, ck[g], i, prm)
+            b = ref.select_row_coarse(qg, ck[g], ck[g], i, prm, 4)
+            assert np.array_equal(a.sel, b.sel)
+            assert np.allclose(a.S, b.S, rtol=1e-14, atol=0) and np.allclose(a.lse, b.lse, rtol=1e-14)
+
+
+def test_coarse_lse_closed_form_for_constant_keys():
+    """Every key equal to u: every fine and coarse logit is z = q.u, so the exact
+    normaliser is z + log(n_fine) and the coarse one z + log(n_coarse); each
+    kernel's per-head score becomes 1 / n_coarse instead of 1 / n_fine."""
+    prm = _params(kernel_size=8, kernel_stride=4, topk=5)
+    rng = np.random.default_rng(61)
+    n, d, coarse = 200, 16, 32
+    u = rng.standard_normal(d)
+    K = np.broadcast_to(u, (2, n, d)).copy()
+    q = rng.standard_normal((4, d))
+    ck = ref.compress_keys(K, 8, 4, "fp64")
+    ckc = ref.compress_keys(K, coarse, coarse, "fp64")
+    for i in (63, 150, 199):
+        nf, nc = ref.num_kernels(i + 1, 8, 4), ref.num_kernels(i + 1, coarse, coarse)
+        rs = ref.select_row_coarse(q[:2], ck[0], ckc[0], i, prm, coarse)
+        z = q[:2] @ u
+        assert np.allclose(rs.lse, z + np.log(nc), rtol=1e-13)
+        assert np.allclose(rs.R, 1.0 / nc, rtol=1e-12)
+        assert np.allclose(ref.select_row(q[:2], ck[0], i, prm).R, 1.0 / nf, rtol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [62, 63])
+def test_coarse_lse_matches_brute_force(seed):
+    """The coarse normaliser, scores and selection against the pure-Python loops
+    (brute_coarse_lse, brute_block_scores with that normaliser, exhaustive top-k)."""
+    prm = _params(block_size=8, kernel_size=4, kernel_stride=2, topk=4, local_blocks=1)
+    rng = np.random.default_rng(seed)
+    n, d, G, coarse = 72, 3, 2, 16
+    K = _bf16_values(rng, (1, n, d))
+    q = _bf16_values(rng, (G, d))
+    ck = ref.compress_keys(K, 4, 2, "fp64")
+    ckc = ref.compress_keys(K, coarse, coarse, "fp64")
+    for i in (7, 15, 40, 71):
+        rs = ref.select_row_coarse(q, ck[0], ckc[0], i, prm, coarse)
+        lb = brute.brute_coarse_lse(q.tolist(), K[0].tolist(), i, coarse)
+        if lb is None:
+            assert i + 1 < coarse
+            lb = brute.brute_block_scores(q.tolist(), K[0].tolist(), i, 8, 4, 2)[2]
+        assert np.allclose(rs.lse, lb, rtol=1e-13)
+        S, _, _ = brute.brute_block_scores(q.tolist(), K[0].tolist(), i, 8, 4, 2, lse_override=lb)
+        assert np.allclose(rs.S, S, rtol=1e-12)
+        want = brute.brute_select(S, i // 8, prm.topk, prm.init_blocks, prm.local_blocks)
+        assert rs.sel[rs.sel >= 0].tolist() == want
