@@ -10,6 +10,7 @@
  *
  *   infv2_compress_keys        step 1a: compressed keys  kbar_j = Mean(K[j s : j s + p])
  *   infv2_select_blocks        step 1b: kernel softmax, group mean, block max, top-k
+ *   infv2_select_blocks_coarse step 1b with the coarse-kernel LogSumExp approximation
  *   infv2_sparse_attn_decode   step 2 for one new token per sequence
  *   infv2_sparse_attn_prefill  step 2 for a chunk of consecutive query rows
  *   infv2_sparse_attn_prefill_bwd  gradients of step 2 (training)
@@ -72,7 +73,7 @@
 extern "C" {
 #endif
 
-#define INFV2_ABI_VERSION 5
+#define INFV2_ABI_VERSION 6
 
 typedef enum infv2_status {
     INFV2_OK = 0,
@@ -99,7 +100,9 @@ typedef enum infv2_op {         /* operation ids for infv2_workspace_bytes */
     INFV2_OP_SELECT_PREFILL = 2,
     INFV2_OP_ATTN_DECODE = 3,
     INFV2_OP_ATTN_PREFILL = 4,
-    INFV2_OP_ATTN_PREFILL_BWD = 5
+    INFV2_OP_ATTN_PREFILL_BWD = 5,
+    INFV2_OP_SELECT_COARSE_DECODE = 6,
+    INFV2_OP_SELECT_COARSE_PREFILL = 7
 } infv2_op;
 
 /* Method hyper-parameters (names follow the pages' notation). */
@@ -205,6 +208,36 @@ int32_t infv2_select_blocks(const infv2_config* cfg, int32_t mode, const void* q
                             const int64_t* kv_offsets, const int64_t* kv_lens, int32_t batch,
                             int64_t max_len, int32_t* block_idx, float* block_score, void* ws,
                             size_t ws_bytes, void* stream);
+
+/*
+ * infv2_select_blocks_coarse -- infv2_select_blocks with the pages' cheaper
+ * first pass ("Efficient LSE approximation"; "Complexity analysis", Stage 1):
+ * the per-head LogSumExp is taken over coarse kernels -- spans of `coarse`
+ * tokens at stride `coarse`, complete ones only, seen by a row when they lie
+ * wholly at or before it, their keys the mean of the span -- and the second
+ * pass scores the fine kernels against that normaliser.  Selections and scores
+ * can differ from the exact call's: that is the approximation.  A row that sees
+ * no coarse kernel keeps the exact normaliser (such rows are dense, since
+ * coarse <= topk * block_size).
+ *
+ *   coarse       s_c, with kernel_size <= coarse <= min(256, topk * block_size)
+ *                (256: the largest kernel infv2_compress_keys builds)
+ *   ck_coarse    device, ck_dtype: the coarse compressed keys, as written by
+ *                infv2_compress_keys with kernel_size = kernel_stride = coarse
+ *                (same layout as ck)
+ *   ckc_offsets  device int64 [batch+1], kernel offsets of ck_coarse
+ *   ws           infv2_workspace_bytes(op = SELECT_COARSE_DECODE or
+ *                SELECT_COARSE_PREFILL); no initial contents are needed
+ *   all else     as for infv2_select_blocks (INFV2_ERR_SHAPE for a coarse size
+ *                out of range)
+ */
+int32_t infv2_select_blocks_coarse(const infv2_config* cfg, int32_t coarse, int32_t mode,
+                                   const void* q, int32_t rows, int64_t q_start, const void* ck,
+                                   const int64_t* ck_offsets, const void* ck_coarse,
+                                   const int64_t* ckc_offsets, const int64_t* kv_offsets,
+                                   const int64_t* kv_lens, int32_t batch, int64_t max_len,
+                                   int32_t* block_idx, float* block_score, void* ws,
+                                   size_t ws_bytes, void* stream);
 
 /*
  * infv2_sparse_attn_decode -- step 2 for decoding ("Complexity analysis",

@@ -174,3 +174,39 @@ def nan_like(t: torch.Tensor) -> torch.Tensor:
     if t.dtype == torch.int16:
         return torch.full_like(t, 0x7FC0)
     return torch.full_like(t, float("nan"))
+
+
+# ---------------------------------------------------------------- coarse-kernel LogSumExp
+def coarse_ck(dev: DeviceWorkload, coarse: int, upto=None):
+    """Coarse compressed keys (spans of `coarse` tokens at stride `coarse`) of every
+    sequence, written by infv2_compress_keys with that kernel size and stride.
+    Returns (ck tensor, offsets tensor, per-sequence counts)."""
+    import dataclasses
+    wl = dev.wl
+    cfg_c = dataclasses.replace(dev.cfg, kernel_size=coarse, kernel_stride=coarse)
+    lens = wl.lens if upto is None else np.asarray(upto)
+    ncs = [num_kernels(int(n), coarse, coarse) for n in lens]
+    off = np.zeros(len(ncs) + 1, dtype=np.int64)
+    off[1:] = np.cumsum(ncs)
+    tdt = torch.int16 if dev.ck_dtype == "bf16" else torch.float32
+    ck = torch.zeros(max(1, int(off[-1]) * wl.num_kv_heads * wl.head_dim), dtype=tdt, device=dev.device)
+    offs = torch.tensor(off, dtype=torch.int64, device=dev.device)
+    kv_lens = torch.tensor(lens, dtype=torch.int64, device=dev.device)
+    tbs.infv2_compress_keys(cfg_c, dev.k, dev.kv_offsets, kv_lens, offs, None, wl.batch,
+                            int(np.max(lens)), -1, ck)
+    return ck, offs, ncs
+
+
+def select_coarse(dev: DeviceWorkload, coarse: int, mode: int, q, rows: int, q_start: int,
+                  ckc, ckc_offsets, max_len: int, kv_lens=None):
+    hkv, k = dev.wl.num_kv_heads, dev.cfg.topk
+    idx = torch.empty((rows, hkv, k), dtype=torch.int32, device=dev.device)
+    score = torch.empty((rows, hkv, k), dtype=torch.float32, device=dev.device)
+    op = tbs.OP_SELECT_COARSE_DECODE if mode == tbs.INFV2_MODE_DECODE else tbs.OP_SELECT_COARSE_PREFILL
+    batch = rows if mode == tbs.INFV2_MODE_DECODE else 1
+    ws = dev.ws(op, rows, batch, max_len)
+    tbs.infv2_select_blocks_coarse(dev.cfg, coarse, mode, q, rows, q_start, dev.ck, dev.ck_offsets,
+                                   ckc, ckc_offsets, dev.kv_offsets,
+                                   dev.kv_lens if kv_lens is None else kv_lens, batch, max_len,
+                                   idx, score, ws)
+    return idx, score

@@ -205,3 +205,22 @@ def test_backward_validation(lib):
     assert call(r=0, ws=None, nb=0) == OK          # nothing to do, nothing launched
     assert call(r=1 << 21, s=0) == EUNSUP          # rows * topk above 2^30
     assert call(s=16384 * 64) == EUNSUP            # more blocks than supported
+
+
+def test_coarse_selection_validation(lib):
+    cfg = tbs.Config()            # p = 32, k = 64, m = 64
+    c = _c(cfg)
+    sel = lib.infv2_select_blocks_coarse
+    need = tbs.infv2_workspace_bytes(cfg, tbs.OP_SELECT_COARSE_DECODE, 1, 1, 131072)
+    assert need >= tbs.infv2_workspace_bytes(cfg, tbs.OP_SELECT_DECODE, 1, 1, 131072)
+    def call(coarse=128, ckc=FAKE, ws=FAKE, nb=need, mode=0):
+        return sel(c, coarse, mode, FAKE, 1, 0, FAKE, FAKE, ckc, FAKE, FAKE, None, 1, 131072,
+                   FAKE, None, ws, nb, None)
+    assert call(ckc=None) == ENULL
+    assert call(coarse=16) == ESHAPE              # finer than the kernels
+    assert call(coarse=257) == ESHAPE             # beyond the largest compressed kernel
+    small = tbs.Config(topk=3, local_blocks=2)    # k * m = 192
+    assert sel(_c(small), 193, 0, FAKE, 1, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 4096, FAKE,
+               None, FAKE, 1 << 30, None) == ESHAPE  # a scored row might see no coarse kernel
+    assert call(nb=need - 1) == EWS
+    assert call(mode=7) == ESHAPE

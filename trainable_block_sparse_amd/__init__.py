@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libinfv2.so")
 INFV2_FP32, INFV2_BF16 = 0, 1
 INFV2_MODE_DECODE, INFV2_MODE_PREFILL = 0, 1
 (OP_COMPRESS, OP_SELECT_DECODE, OP_SELECT_PREFILL, OP_ATTN_DECODE, OP_ATTN_PREFILL,
- OP_ATTN_PREFILL_BWD) = range(6)
+ OP_ATTN_PREFILL_BWD, OP_SELECT_COARSE_DECODE, OP_SELECT_COARSE_PREFILL) = range(8)
 # kernel families for infv2_timing_start (infv2_kernel in infv2.h)
 KERNELS = ("compress", "select_logits", "select_scores", "select_prefill", "select_topk",
            "attn_decode", "attn_merge", "attn_prefill", "vt_build", "append", "bwd_row",
@@ -96,6 +96,8 @@ def load_library(path: str = LIB_PATH):
                                                    vp]),
         "infv2_select_blocks": (i32, [cfgp, i32, vp, i32, i64, vp, vp, vp, vp, i32, i64, vp, vp,
                                       vp, sz, vp]),
+        "infv2_select_blocks_coarse": (i32, [cfgp, i32, i32, vp, i32, i64, vp, vp, vp, vp, vp, vp,
+                                             i32, i64, vp, vp, vp, sz, vp]),
         "infv2_sparse_attn_decode": (i32, [cfgp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, sz, vp]),
         "infv2_sparse_attn_prefill": (i32, [cfgp, vp, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp]),
         "infv2_sparse_attn_prefill_bwd": (i32, [cfgp, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -114,7 +116,8 @@ def load_library(path: str = LIB_PATH):
     return lib
 
 
-EXPORTED = ("infv2_compress_keys", "infv2_append_kv", "infv2_select_blocks", "infv2_sparse_attn_decode",
+EXPORTED = ("infv2_compress_keys", "infv2_append_kv", "infv2_select_blocks",
+            "infv2_select_blocks_coarse", "infv2_sparse_attn_decode",
             "infv2_sparse_attn_prefill", "infv2_select_blocks_varlen",
             "infv2_sparse_attn_prefill_varlen", "infv2_sparse_attn_prefill_bwd", "infv2_workspace_bytes", "infv2_num_kernels",
             "infv2_status_str", "infv2_abi_version", "infv2_timing_start", "infv2_timing_stop")
@@ -242,6 +245,17 @@ def infv2_select_blocks(cfg: Config, mode: int, q, rows: int, q_start: int, ck, 
         ctypes.byref(c), mode, _ptr(q), rows, q_start, _ptr(ck), _ptr(ck_offsets),
         _ptr(kv_offsets), _ptr(kv_lens), batch, max_len, _ptr(block_idx), _ptr(block_score),
         _ptr(ws), nbytes, _stream(stream)), "infv2_select_blocks")
+
+
+def infv2_select_blocks_coarse(cfg: Config, coarse: int, mode: int, q, rows: int, q_start: int, ck,
+                               ck_offsets, ck_coarse, ckc_offsets, kv_offsets, kv_lens, batch: int,
+                               max_len: int, block_idx, block_score, ws, stream=None) -> None:
+    c = cfg.to_c()
+    _check(load_library().infv2_select_blocks_coarse(
+        ctypes.byref(c), coarse, mode, _ptr(q), rows, q_start, _ptr(ck), _ptr(ck_offsets),
+        _ptr(ck_coarse), _ptr(ckc_offsets), _ptr(kv_offsets), _ptr(kv_lens), batch, max_len,
+        _ptr(block_idx), _ptr(block_score), _ptr(ws), _nbytes(ws), _stream(stream)),
+        "infv2_select_blocks_coarse")
 
 
 def infv2_sparse_attn_decode(cfg: Config, q, k, v, kv_offsets, kv_lens, batch: int, max_len: int,

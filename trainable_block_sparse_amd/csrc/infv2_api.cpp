@@ -62,6 +62,8 @@ size_t ws_bytes_for(const infv2_config* c, int32_t op, int32_t rows, int32_t bat
         case INFV2_OP_ATTN_DECODE: return infv2::attn_decode_ws(sh, batch).total;
         case INFV2_OP_ATTN_PREFILL: return infv2::attn_prefill_ws_bytes(sh, max_len);
         case INFV2_OP_ATTN_PREFILL_BWD: return rows > 0 ? infv2::bwd_ws(sh, rows, max_len).total : 0;
+        case INFV2_OP_SELECT_COARSE_DECODE: return infv2::select_decode_ws(sh, batch, max_len).total_coarse;
+        case INFV2_OP_SELECT_COARSE_PREFILL: return infv2::select_prefill_ws(sh, rows, max_len).total;
         default: return 0;
     }
 }
@@ -95,7 +97,7 @@ int32_t infv2_workspace_bytes(const infv2_config* c, int32_t op, int32_t rows, i
     int32_t st = check_config(c);
     if (st != INFV2_OK) return st;
     if ((st = check_len(c, max_len)) != INFV2_OK) return st;
-    if (op < INFV2_OP_COMPRESS || op > INFV2_OP_ATTN_PREFILL_BWD || rows < 0 || batch < 0) return INFV2_ERR_SHAPE;
+    if (op < INFV2_OP_COMPRESS || op > INFV2_OP_SELECT_COARSE_PREFILL || rows < 0 || batch < 0) return INFV2_ERR_SHAPE;
     *bytes = ws_bytes_for(c, op, rows, batch, max_len);
     return INFV2_OK;
 }
@@ -146,7 +148,7 @@ int32_t infv2_select_blocks(const infv2_config* c, int32_t mode, const void* q, 
         if (!ws || ws_bytes < need) return INFV2_ERR_WORKSPACE;
         return status_of(infv2::launch_select_decode(make_shape(c), q, ck, ck_offsets, kv_offsets,
                                                      kv_lens, batch, max_len, block_idx,
-                                                     block_score, ws, s));
+                                                     block_score, ws, nullptr, s));
     }
     if (mode == INFV2_MODE_PREFILL) {
         if (batch != 1 || rows < 0 || q_start < 0) return INFV2_ERR_SHAPE;
@@ -156,7 +158,45 @@ int32_t infv2_select_blocks(const infv2_config* c, int32_t mode, const void* q, 
         if (!ws || ws_bytes < need) return INFV2_ERR_WORKSPACE;
         return status_of(infv2::launch_select_prefill(make_shape(c), q, rows, q_start, ck,
                                                       ck_offsets, max_len, block_idx, block_score,
-                                                      ws, s));
+                                                      ws, nullptr, s));
+    }
+    return INFV2_ERR_SHAPE;
+}
+
+int32_t infv2_select_blocks_coarse(const infv2_config* c, int32_t coarse, int32_t mode,
+                                   const void* q, int32_t rows, int64_t q_start, const void* ck,
+                                   const int64_t* ck_offsets, const void* ck_coarse,
+                                   const int64_t* ckc_offsets, const int64_t* kv_offsets,
+                                   const int64_t* kv_lens, int32_t batch, int64_t max_len,
+                                   int32_t* block_idx, float* block_score, void* ws,
+                                   size_t ws_bytes, void* stream) {
+    int32_t st = check_config(c);
+    if (st != INFV2_OK) return st;
+    if (!q || !ck || !ck_offsets || !ck_coarse || !ckc_offsets || !block_idx) return INFV2_ERR_NULL;
+    if (coarse < c->kernel_size || coarse > 256 ||
+        static_cast<int64_t>(coarse) > static_cast<int64_t>(c->topk) * c->block_size)
+        return INFV2_ERR_SHAPE;
+    if ((st = check_len(c, max_len)) != INFV2_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const infv2::CoarseSel cs{coarse, ck_coarse, ckc_offsets};
+    if (mode == INFV2_MODE_DECODE) {
+        if (!kv_offsets) return INFV2_ERR_NULL;
+        if (batch < 1 || rows != batch) return INFV2_ERR_SHAPE;
+        const size_t need = ws_bytes_for(c, INFV2_OP_SELECT_COARSE_DECODE, rows, batch, max_len);
+        if (!ws || ws_bytes < need) return INFV2_ERR_WORKSPACE;
+        return status_of(infv2::launch_select_decode(make_shape(c), q, ck, ck_offsets, kv_offsets,
+                                                     kv_lens, batch, max_len, block_idx,
+                                                     block_score, ws, &cs, s));
+    }
+    if (mode == INFV2_MODE_PREFILL) {
+        if (batch != 1 || rows < 0 || q_start < 0) return INFV2_ERR_SHAPE;
+        if (q_start + rows > max_len) return INFV2_ERR_SHAPE;
+        if (rows == 0) return INFV2_OK;
+        const size_t need = ws_bytes_for(c, INFV2_OP_SELECT_COARSE_PREFILL, rows, batch, max_len);
+        if (!ws || ws_bytes < need) return INFV2_ERR_WORKSPACE;
+        return status_of(infv2::launch_select_prefill(make_shape(c), q, rows, q_start, ck,
+                                                      ck_offsets, max_len, block_idx, block_score,
+                                                      ws, &cs, s));
     }
     return INFV2_ERR_SHAPE;
 }
@@ -267,7 +307,7 @@ int32_t infv2_select_blocks_varlen(const infv2_config* c, const void* q, int32_t
             const hipError_t e = infv2::launch_select_prefill(
                 sh, static_cast<const char*>(q) + r0 * qrow, rows, q_start_per_seq[b], ck,
                 ck_offsets + b, q_start_per_seq[b] + rows, block_idx + r0 * irow,
-                block_score ? block_score + r0 * irow : nullptr, ws,
+                block_score ? block_score + r0 * irow : nullptr, ws, nullptr,
                 static_cast<hipStream_t>(stream));
             if (e != hipSuccess) return INFV2_ERR_DEVICE;
         }

@@ -36,6 +36,7 @@ struct Shape {
 // workspace carving (all offsets 256-byte aligned)
 struct SelectDecodeWs {
     size_t logits, partial, keys, total;
+    size_t logits_c, partial_c, lse_c, total_coarse;   // coarse-kernel LSE variant
     int nchunk_a, nchunk_b;
     int64_t nc_max, nc_ld, nblk_max;   // nc_ld: logits row stride (multiple of 4)
 };
@@ -61,14 +62,24 @@ hipError_t launch_append_kv(const Shape& sh, const void* k_new, const void* v_ne
                             void* v, const int64_t* kv_off, int64_t* kv_lens,
                             const int64_t* ck_off, void* ck, int batch, hipStream_t st);
 
+// pass 1 over coarse kernels (size = stride = coarse) with their compressed keys
+struct CoarseSel {
+    int coarse;
+    const void* ckc;
+    const int64_t* ckc_off;
+};
+
+// cs == nullptr: the exact selection
 hipError_t launch_select_decode(const Shape& sh, const void* q, const void* ck,
                                 const int64_t* ck_off, const int64_t* kv_off,
                                 const int64_t* kv_lens, int batch, int64_t max_len,
-                                int32_t* idx, float* score, void* ws, hipStream_t st);
+                                int32_t* idx, float* score, void* ws, const CoarseSel* cs,
+                                hipStream_t st);
 
 hipError_t launch_select_prefill(const Shape& sh, const void* q, int rows, int64_t q_start,
                                  const void* ck, const int64_t* ck_off, int64_t max_len,
-                                 int32_t* idx, float* score, void* ws, hipStream_t st);
+                                 int32_t* idx, float* score, void* ws, const CoarseSel* cs,
+                                 hipStream_t st);
 
 hipError_t launch_attn_decode(const Shape& sh, const void* q, const void* k, const void* v,
                               const int64_t* kv_off, const int64_t* kv_lens, int batch,

@@ -48,6 +48,20 @@ __device__ __forceinline__ int64_t last_kernel_of_block(int64_t blk, int m, int 
     return ((blk + 1) * m - 1) / s;
 }
 
+// the coarse-kernel variant adds the coarse pass-1 logits and partials (sized for
+// the smallest coarse size it accepts, the fine kernel size) and the normalisers
+static size_t coarse_extra(const Shape& sh, int batch, int64_t max_len, size_t* lc, size_t* pc, size_t* ls) {
+    const int64_t nc = max_len < sh.p ? 1 : (max_len - sh.p) / sh.p + 1;
+    const int64_t ld = (nc + 3) & ~int64_t(3);
+    const int64_t nch = (nc + kChunkA - 1) / kChunkA;
+    const size_t bg = static_cast<size_t>(batch) * sh.hkv;
+    size_t off = 0;
+    *lc = off; off += align256(bg * ld * kGroup * sizeof(float));
+    *pc = off; off += align256(bg * nch * kGroup * sizeof(float2));
+    *ls = off; off += align256(bg * kGroup * sizeof(float));
+    return off;
+}
+
 SelectDecodeWs select_decode_ws(const Shape& sh, int batch, int64_t max_len) {
     SelectDecodeWs w{};
     w.nc_max = max_len < sh.p ? 0 : (max_len - sh.p) / sh.s + 1;
@@ -63,6 +77,9 @@ SelectDecodeWs select_decode_ws(const Shape& sh, int batch, int64_t max_len) {
     w.partial = off;  off += align256(bg * w.nchunk_a * kGroup * sizeof(float2));
     w.keys = off;     off += align256(bg * w.nblk_max * sizeof(uint32_t));
     w.total = off;
+    size_t lc, pc, ls;
+    w.total_coarse = off + coarse_extra(sh, batch, max_len, &lc, &pc, &ls);
+    w.logits_c = off + lc; w.partial_c = off + pc; w.lse_c = off + ls;
     return w;
 }
 
@@ -249,11 +266,44 @@ __global__ __launch_bounds__(64) void sel_dec_logits_mfma(
 }
 
 // ------------------------------------------------------------------ decode, pass 2
+// Per-head LogSumExp from pass 1's per-chunk (max, sum-exp) partials of one
+// (sequence, KV head): called by 256 threads, 16 per head; thread t folds head
+// t / 16 and the result is valid in every thread of that head.
+__device__ __forceinline__ float fold_partials(const float2* __restrict__ pp, int nchunk, int t) {
+    const int r = t & 15;
+    constexpr int kMaxPer = 16;          // partials per thread held in registers
+    float2 pm[kMaxPer];
+#pragma unroll
+    for (int u = 0; u < kMaxPer; ++u) {
+        const int c = r + 16 * u;
+        pm[u] = c < nchunk ? pp[static_cast<size_t>(c) * kGroup] : make_float2(-INFINITY, 0.f);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kMaxPer; ++u) mx = fmaxf(mx, pm[u].x);
+    for (int c = r + 16 * kMaxPer; c < nchunk; c += 16) mx = fmaxf(mx, pp[static_cast<size_t>(c) * kGroup].x);
+    mx = max16(mx);
+    float sm = 0.f;
+    if (mx != -INFINITY) {
+#pragma unroll
+        for (int u = 0; u < kMaxPer; ++u) sm += (pm[u].x == -INFINITY) ? 0.f : pm[u].y * expf(pm[u].x - mx);
+        for (int c = r + 16 * kMaxPer; c < nchunk; c += 16) {
+            const float2 q2 = pp[static_cast<size_t>(c) * kGroup];
+            sm += (q2.x == -INFINITY) ? 0.f : q2.y * expf(q2.x - mx);
+        }
+    }
+    sm = sum16(sm);
+    return (mx == -INFINITY) ? -INFINITY : mx + logf(sm);
+}
+
+// lse_in: a per-(sequence, KV head, head) normaliser to use instead of the one
+// folded from `partial` (the coarse-kernel approximation), or NULL
 __global__ __launch_bounds__(256) void sel_dec_scores(
     const int64_t* __restrict__ kv_off, const int64_t* __restrict__ kv_lens,
     const int64_t* __restrict__ ck_off, int hkv, int m, int p, int s, int64_t nc_max,
     int64_t nc_ld, int nchunk_a, int64_t nblk_max, const float* __restrict__ logits,
-    const float2* __restrict__ partial, uint32_t* __restrict__ keys) {
+    const float2* __restrict__ partial, const float* __restrict__ lse_in,
+    uint32_t* __restrict__ keys) {
     __shared__ float ls[kGroup];
     __shared__ float rs[kChunkB];
     const int b = blockIdx.z, g = blockIdx.y, ch = blockIdx.x, t = threadIdx.x;
@@ -279,32 +329,11 @@ __global__ __launch_bounds__(256) void sel_dec_scores(
         for (int h = 0; h < kGroup; ++h) zz[h] = z[h * nc_ld];
     }
     // per-head LogSumExp from the partials of pass 1 (16 threads per head)
-    {
-        const int h = t >> 4, r = t & 15;
-        const float2* pp = partial + bg * nchunk_a * kGroup + h;
-        constexpr int kMaxPer = 16;          // partials per thread held in registers
-        float2 pm[kMaxPer];
-#pragma unroll
-        for (int u = 0; u < kMaxPer; ++u) {
-            const int c = r + 16 * u;
-            pm[u] = c < nchunk_a ? pp[static_cast<size_t>(c) * kGroup] : make_float2(-INFINITY, 0.f);
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int u = 0; u < kMaxPer; ++u) mx = fmaxf(mx, pm[u].x);
-        for (int c = r + 16 * kMaxPer; c < nchunk_a; c += 16) mx = fmaxf(mx, pp[static_cast<size_t>(c) * kGroup].x);
-        mx = max16(mx);
-        float sm = 0.f;
-        if (mx != -INFINITY) {
-#pragma unroll
-            for (int u = 0; u < kMaxPer; ++u) sm += (pm[u].x == -INFINITY) ? 0.f : pm[u].y * expf(pm[u].x - mx);
-            for (int c = r + 16 * kMaxPer; c < nchunk_a; c += 16) {
-                const float2 q2 = pp[static_cast<size_t>(c) * kGroup];
-                sm += (q2.x == -INFINITY) ? 0.f : q2.y * expf(q2.x - mx);
-            }
-        }
-        sm = sum16(sm);
-        if (r == 0) ls[h] = (mx == -INFINITY) ? -INFINITY : mx + logf(sm);
+    if (lse_in) {
+        if (t < kGroup) ls[t] = lse_in[bg * kGroup + t];
+    } else {
+        const float v = fold_partials(partial + bg * nchunk_a * kGroup + (t >> 4), nchunk_a, t);
+        if ((t & 15) == 0) ls[t >> 4] = v;
     }
     __syncthreads();
     float R = -INFINITY;
@@ -329,6 +358,29 @@ __global__ __launch_bounds__(256) void sel_dec_scores(
             atomicMax(&kb[blk], score_to_key(mx));
         }
     }
+}
+
+// ------------------------------------------------------------------ decode, coarse LSE
+// "Efficient LSE approximation": the per-head normaliser of a (sequence, KV
+// head) from the partials of pass 1 run over the coarse kernels (size and
+// stride `coarse`); a row that sees no coarse kernel keeps the exact one from
+// the fine partials.  grid (KV head, sequence), 256 threads.
+__global__ __launch_bounds__(256) void sel_dec_lse_coarse(
+    const int64_t* __restrict__ kv_off, const int64_t* __restrict__ kv_lens,
+    const int64_t* __restrict__ ckc_off, int hkv, int coarse, int nchunk_c, int nchunk_f,
+    const float2* __restrict__ partial_c, const float2* __restrict__ partial_f,
+    float* __restrict__ lse_out) {
+    const int b = blockIdx.y, g = blockIdx.x, t = threadIdx.x;
+    const int64_t cap = kv_off[b + 1] - kv_off[b];
+    int64_t n = kv_lens ? kv_lens[b] : cap;
+    n = n < cap ? n : cap;
+    const int64_t ccap = ckc_off[b + 1] - ckc_off[b];
+    int64_t nvis = num_kernels(n, coarse, coarse);
+    nvis = nvis < ccap ? nvis : ccap;
+    const size_t bg = static_cast<size_t>(b) * hkv + g;
+    const float v = nvis > 0 ? fold_partials(partial_c + bg * nchunk_c * kGroup + (t >> 4), nchunk_c, t)
+                             : fold_partials(partial_f + bg * nchunk_f * kGroup + (t >> 4), nchunk_f, t);
+    if ((t & 15) == 0) lse_out[bg * kGroup + (t >> 4)] = v;
 }
 
 // ------------------------------------------------------------------ decode, top-k
@@ -847,14 +899,38 @@ static void launch_topk_pre(const Shape& sh, int rows, int64_t q_start, int64_t 
 
 template <typename Tq, typename Tck>
 static void dec_launch(const Shape& sh, const void* q, const void* ck, const int64_t* ck_off,
-                       const int64_t* kv_off, const int64_t* kv_lens, int batch,
+                       const int64_t* kv_off, const int64_t* kv_lens, int batch, int64_t max_len,
                        const SelectDecodeWs& w, char* ws, int32_t* idx, float* score,
-                       hipStream_t st) {
+                       const CoarseSel* cs, hipStream_t st) {
     dim3 ga(w.nchunk_a, sh.hkv, batch), gb(w.nchunk_b, sh.hkv, batch);
     const int64_t ncm = w.nc_max > 0 ? w.nc_max : 1;
     float* logits = reinterpret_cast<float*>(ws + w.logits);
     float2* partial = reinterpret_cast<float2*>(ws + w.partial);
     uint32_t* keys = reinterpret_cast<uint32_t*>(ws + w.keys);
+    float* lse_c = nullptr;
+    int nch_c = 1;
+    float2* partial_c = nullptr;
+    if (cs) {
+        // pass 1 over the coarse kernels: their logits and per-chunk partials
+        const int c = cs->coarse;
+        const int64_t ncm_c = max_len < c ? 1 : (max_len - c) / c + 1;
+        const int64_t ld_c = (ncm_c + 3) & ~int64_t(3);
+        nch_c = static_cast<int>((ncm_c + kChunkA - 1) / kChunkA);
+        float* logits_c = reinterpret_cast<float*>(ws + w.logits_c);
+        partial_c = reinterpret_cast<float2*>(ws + w.partial_c);
+        lse_c = reinterpret_cast<float*>(ws + w.lse_c);
+        dim3 gc(nch_c, sh.hkv, batch);
+        KernelTimer kt(INFV2_KERNEL_SELECT_LOGITS, st);
+        if (sizeof(Tq) == 2)
+            sel_dec_logits_mfma<sizeof(Tck) == 2><<<gc, 64, 0, st>>>(
+                static_cast<const bf16_t*>(q), cs->ckc, cs->ckc_off, kv_off, kv_lens, sh.hq, sh.hkv,
+                c, c, sh.score_scale, ncm_c, ld_c, nch_c, w.nblk_max, logits_c, partial_c, keys);
+        else
+            sel_dec_logits<Tq, Tck><<<gc, 256, 0, st>>>(
+                static_cast<const Tq*>(q), static_cast<const Tck*>(cs->ckc), cs->ckc_off, kv_off,
+                kv_lens, sh.hq, sh.hkv, c, c, sh.score_scale, ncm_c, ld_c, nch_c, w.nblk_max,
+                logits_c, partial_c, keys);
+    }
     {
         KernelTimer kt(INFV2_KERNEL_SELECT_LOGITS, st);
         if (sizeof(Tq) == 2)
@@ -867,10 +943,17 @@ static void dec_launch(const Shape& sh, const void* q, const void* ck, const int
                 sh.hq, sh.hkv, sh.p, sh.s, sh.score_scale, ncm, w.nc_ld, w.nchunk_a, w.nblk_max,
                 logits, partial, keys);
     }
+    if (cs) {
+        KernelTimer kt(INFV2_KERNEL_SELECT_SCORES, st);
+        sel_dec_lse_coarse<<<dim3(sh.hkv, batch), 256, 0, st>>>(
+            kv_off, kv_lens, cs->ckc_off, sh.hkv, cs->coarse, nch_c, w.nchunk_a, partial_c, partial,
+            lse_c);
+    }
     {
         KernelTimer kt(INFV2_KERNEL_SELECT_SCORES, st);
         sel_dec_scores<<<gb, 256, 0, st>>>(kv_off, kv_lens, ck_off, sh.hkv, sh.m, sh.p, sh.s, ncm,
-                                           w.nc_ld, w.nchunk_a, w.nblk_max, logits, partial, keys);
+                                           w.nc_ld, w.nchunk_a, w.nblk_max, logits, partial, lse_c,
+                                           keys);
     }
     KernelTimer kt(INFV2_KERNEL_SELECT_TOPK, st);
     launch_topk_dec(sh, batch, w.nblk_max, kv_off, kv_lens, keys, idx, score, st);
@@ -880,7 +963,8 @@ static void dec_launch(const Shape& sh, const void* q, const void* ck, const int
 hipError_t launch_select_decode(const Shape& sh, const void* q, const void* ck,
                                 const int64_t* ck_off, const int64_t* kv_off,
                                 const int64_t* kv_lens, int batch, int64_t max_len,
-                                int32_t* idx, float* score, void* ws, hipStream_t st) {
+                                int32_t* idx, float* score, void* ws, const CoarseSel* cs,
+                                hipStream_t st) {
     const SelectDecodeWs w = select_decode_ws(sh, batch, max_len);
     if (!score && max_len <= static_cast<int64_t>(sh.topk) * sh.m) {   // every row dense
         launch_dense_ids(sh, 1, batch, 0, kv_off, kv_lens, w.nblk_max, idx, st);
@@ -888,32 +972,62 @@ hipError_t launch_select_decode(const Shape& sh, const void* q, const void* ck,
     }
     char* base = static_cast<char*>(ws);
     if (sh.io_bf16) {
-        if (sh.ck_bf16) dec_launch<bf16_t, bf16_t>(sh, q, ck, ck_off, kv_off, kv_lens, batch, w, base, idx, score, st);
-        else dec_launch<bf16_t, float>(sh, q, ck, ck_off, kv_off, kv_lens, batch, w, base, idx, score, st);
+        if (sh.ck_bf16) dec_launch<bf16_t, bf16_t>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, st);
+        else dec_launch<bf16_t, float>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, st);
     } else {
-        if (sh.ck_bf16) dec_launch<float, bf16_t>(sh, q, ck, ck_off, kv_off, kv_lens, batch, w, base, idx, score, st);
-        else dec_launch<float, float>(sh, q, ck, ck_off, kv_off, kv_lens, batch, w, base, idx, score, st);
+        if (sh.ck_bf16) dec_launch<float, bf16_t>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, st);
+        else dec_launch<float, float>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, st);
     }
     return hipGetLastError();
+}
+
+// Pass 1 (per-head LogSumExp and clearing the rows' block keys) for rows
+// [r0, r0 + nr) of the call, over compressed keys `ck` of kernel size p, stride s.
+template <typename Tq, typename Tck>
+static void pre_pass1(const Shape& sh, const void* q, int r0, int nr, int64_t q_start,
+                      const void* ck, const int64_t* ck_off, int p, int s,
+                      const SelectPrefillWs& w, float* lse, uint32_t* keys, hipStream_t st) {
+    if (nr <= 0) return;
+    const size_t qrow = static_cast<size_t>(sh.hq) * kHeadDim;
+    float* l = lse + static_cast<size_t>(r0) * sh.hq;
+    uint32_t* kb = keys + static_cast<size_t>(r0) * sh.hkv * w.nblk_max;
+    KernelTimer kt(INFV2_KERNEL_SELECT_PREFILL, st);
+    if (sizeof(Tq) == 2) {
+        dim3 gm((nr + kPreRowsG - 1) / kPreRowsG, sh.hkv);
+        sel_pre_mfma<1, sizeof(Tck) == 2><<<gm, 256, 0, st>>>(
+            static_cast<const bf16_t*>(q) + r0 * qrow, nr, q_start + r0, ck, ck_off, sh.hq, sh.hkv,
+            sh.m, p, s, sh.score_scale, w.nblk_max, l, kb);
+    } else {
+        dim3 g1((nr + kRowsPre - 1) / kRowsPre, sh.hkv);
+        sel_pre_lse<Tq, Tck><<<g1, 256, 0, st>>>(static_cast<const Tq*>(q) + r0 * qrow, nr,
+                                                q_start + r0, static_cast<const Tck*>(ck), ck_off,
+                                                sh.hq, sh.hkv, p, s, sh.score_scale, w.nblk_max, l,
+                                                kb);
+    }
 }
 
 template <typename Tq, typename Tck>
 static void pre_launch(const Shape& sh, const void* q, int rows, int64_t q_start, const void* ck,
                        const int64_t* ck_off, const SelectPrefillWs& w, char* ws, int32_t* idx,
-                       float* score, hipStream_t st) {
+                       float* score, const CoarseSel* cs, hipStream_t st) {
     dim3 g1((rows + kRowsPre - 1) / kRowsPre, sh.hkv);
     float* lse = reinterpret_cast<float*>(ws + w.lse);
     uint32_t* keys = reinterpret_cast<uint32_t*>(ws + w.keys);
+    if (cs) {
+        // rows that see a coarse kernel take pass 1 over the coarse kernels; the
+        // few before the first one (dense rows) keep the exact normaliser
+        int64_t nf = static_cast<int64_t>(cs->coarse) - 1 - q_start;
+        nf = nf < 0 ? 0 : (nf > rows ? rows : nf);
+        pre_pass1<Tq, Tck>(sh, q, 0, static_cast<int>(nf), q_start, ck, ck_off, sh.p, sh.s, w, lse, keys, st);
+        pre_pass1<Tq, Tck>(sh, q, static_cast<int>(nf), rows - static_cast<int>(nf), q_start, cs->ckc,
+                           cs->ckc_off, cs->coarse, cs->coarse, w, lse, keys, st);
+    } else {
+        pre_pass1<Tq, Tck>(sh, q, 0, rows, q_start, ck, ck_off, sh.p, sh.s, w, lse, keys, st);
+    }
     if (sizeof(Tq) == 2) {
         constexpr bool kB = sizeof(Tck) == 2;
         dim3 gm((rows + kPreRowsG - 1) / kPreRowsG, sh.hkv);
         const bf16_t* qq = static_cast<const bf16_t*>(q);
-        {
-            KernelTimer kt(INFV2_KERNEL_SELECT_PREFILL, st);
-            sel_pre_mfma<1, kB><<<gm, 256, 0, st>>>(qq, rows, q_start, ck, ck_off, sh.hq, sh.hkv,
-                                                    sh.m, sh.p, sh.s, sh.score_scale, w.nblk_max,
-                                                    lse, keys);
-        }
         {
             KernelTimer kt(INFV2_KERNEL_SELECT_PREFILL, st);
             sel_pre_mfma<2, kB><<<gm, 256, 0, st>>>(qq, rows, q_start, ck, ck_off, sh.hq, sh.hkv,
@@ -923,12 +1037,6 @@ static void pre_launch(const Shape& sh, const void* q, int rows, int64_t q_start
         KernelTimer kt(INFV2_KERNEL_SELECT_TOPK, st);
         launch_topk_pre(sh, rows, q_start, w.nblk_max, keys, idx, score, st);
         return;
-    }
-    {
-        KernelTimer kt(INFV2_KERNEL_SELECT_PREFILL, st);
-        sel_pre_lse<Tq, Tck><<<g1, 256, 0, st>>>(static_cast<const Tq*>(q), rows, q_start,
-                                                static_cast<const Tck*>(ck), ck_off, sh.hq, sh.hkv,
-                                                sh.p, sh.s, sh.score_scale, w.nblk_max, lse, keys);
     }
     {
         KernelTimer kt(INFV2_KERNEL_SELECT_PREFILL, st);
@@ -943,7 +1051,8 @@ static void pre_launch(const Shape& sh, const void* q, int rows, int64_t q_start
 
 hipError_t launch_select_prefill(const Shape& sh, const void* q, int rows, int64_t q_start,
                                  const void* ck, const int64_t* ck_off, int64_t max_len,
-                                 int32_t* idx, float* score, void* ws, hipStream_t st) {
+                                 int32_t* idx, float* score, void* ws, const CoarseSel* cs,
+                                 hipStream_t st) {
     const SelectPrefillWs w = select_prefill_ws(sh, rows, max_len);
     if (!score && q_start + rows <= static_cast<int64_t>(sh.topk) * sh.m) {   // every row dense
         launch_dense_ids(sh, 0, rows, q_start, nullptr, nullptr, w.nblk_max, idx, st);
@@ -951,11 +1060,11 @@ hipError_t launch_select_prefill(const Shape& sh, const void* q, int rows, int64
     }
     char* base = static_cast<char*>(ws);
     if (sh.io_bf16) {
-        if (sh.ck_bf16) pre_launch<bf16_t, bf16_t>(sh, q, rows, q_start, ck, ck_off, w, base, idx, score, st);
-        else pre_launch<bf16_t, float>(sh, q, rows, q_start, ck, ck_off, w, base, idx, score, st);
+        if (sh.ck_bf16) pre_launch<bf16_t, bf16_t>(sh, q, rows, q_start, ck, ck_off, w, base, idx, score, cs, st);
+        else pre_launch<bf16_t, float>(sh, q, rows, q_start, ck, ck_off, w, base, idx, score, cs, st);
     } else {
-        if (sh.ck_bf16) pre_launch<float, bf16_t>(sh, q, rows, q_start, ck, ck_off, w, base, idx, score, st);
-        else pre_launch<float, float>(sh, q, rows, q_start, ck, ck_off, w, base, idx, score, st);
+        if (sh.ck_bf16) pre_launch<float, bf16_t>(sh, q, rows, q_start, ck, ck_off, w, base, idx, score, cs, st);
+        else pre_launch<float, float>(sh, q, rows, q_start, ck, ck_off, w, base, idx, score, cs, st);
     }
     return hipGetLastError();
 }
