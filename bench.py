@@ -601,6 +601,123 @@ def backward_spot_parity(wl, gi, dq_t, dout_t, torch, gh) -> str:
     return f"ok: dq of 4 rows x 2 heads vs the float64 oracle, scaled max err {worst:.1e}"
 
 
+def _agreement(a: np.ndarray, e: np.ndarray):
+    """(share of identical (row, KV head) selections, share of the exact selection's
+    blocks also chosen) between approximate ids `a` and exact ids `e` [rows][Hkv][k]."""
+    same = float(np.mean(np.all(a == e, axis=-1)))
+    shared = total = 0
+    for x, y in zip(a.reshape(-1, a.shape[-1]), e.reshape(-1, e.shape[-1])):
+        yy = y[y >= 0]
+        shared += np.intersect1d(x[x >= 0], yy).size
+        total += yy.size
+    return same, shared / max(1, total)
+
+
+def bench_coarse(args, torch, tbs, gh) -> dict:
+    """The coarse-kernel LogSumExp selection against the exact one: selection time
+    per call and agreement of the selections, at 128K decode (32 replicas, a new
+    query per step, as the main line) and over the 32K prefill (chunks of 4096)."""
+    from synth import make_config, extra_decode_queries
+    out = {}
+    # ---- decode, 128K, batch 1
+    wl = make_config(2)
+    dev = gh.DeviceWorkload(wl, args.ck_dtype)
+    dev.compress()
+    cfg, B, n = dev.cfg, wl.batch, dev.max_len
+    R = args.replicas
+    qs = gh.to_device(extra_decode_queries(wl, R))
+    CKs = [dev.ck] + [dev.ck.clone() for _ in range(R - 1)]
+    T = Timer(torch)
+    idx = torch.empty((B, wl.num_kv_heads, cfg.topk), dtype=torch.int32, device="cuda")
+    ws_e = dev.ws(tbs.OP_SELECT_DECODE, B, B, n)
+    ws_c = dev.ws(tbs.OP_SELECT_COARSE_DECODE, B, B, n)
+
+    def time_calls(fn):
+        for t in range(args.warmup):
+            fn(t % R)
+        torch.cuda.synchronize()
+        e0 = T.event()
+        for t in range(args.steps):
+            fn(t % R)
+        e1 = T.event()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / args.steps
+
+    def exact(r, out_idx=idx):
+        tbs.infv2_select_blocks(cfg, tbs.INFV2_MODE_DECODE, qs[r], B, 0, CKs[r], dev.ck_offsets,
+                                dev.kv_offsets, dev.kv_lens, B, n, out_idx, None, ws_e)
+    dec = {"workload": wl.name, "replicas": R, "exact_select_us": time_calls(exact)}
+    ref_idx = []
+    for r in range(R):
+        e = torch.empty_like(idx)
+        exact(r, e)
+        ref_idx.append(e)
+    ref_idx = torch.stack(ref_idx).cpu().numpy()
+    for c in (64, 128, 256):
+        ckc, ckc_off, _ = gh.coarse_ck(dev, c)
+        CCs = [ckc] + [ckc.clone() for _ in range(R - 1)]
+
+        def coarse(r, out_idx=idx, c=c, CCs=CCs, ckc_off=ckc_off):
+            tbs.infv2_select_blocks_coarse(cfg, c, tbs.INFV2_MODE_DECODE, qs[r], B, 0, CKs[r],
+                                           dev.ck_offsets, CCs[r], ckc_off, dev.kv_offsets,
+                                           dev.kv_lens, B, n, out_idx, None, ws_c)
+        us = time_calls(coarse)
+        got = []
+        for r in range(R):
+            e = torch.empty_like(idx)
+            coarse(r, e)
+            got.append(e)
+        same, shared = _agreement(torch.stack(got).cpu().numpy(), ref_idx)
+        dec[f"coarse_{c}"] = {"select_us": us, "same_selection": same, "blocks_shared": shared}
+        del CCs
+    out["decode_128k"] = dec
+    del CKs
+    torch.cuda.empty_cache()
+    # ---- prefill, 32K in 4096-row chunks (selection only; compressed keys built once)
+    wp = make_config(3)
+    devp = gh.DeviceWorkload(wp, args.ck_dtype)
+    devp.compress()
+    L, C = int(wp.lens[0]), wp.chunk
+    hkv, k = wp.num_kv_heads, devp.cfg.topk
+    idx_e = torch.empty((L, hkv, k), dtype=torch.int32, device="cuda")
+    idx_c = torch.empty_like(idx_e)
+    ws_p = devp.ws(tbs.OP_SELECT_COARSE_PREFILL, C, 1, L)
+
+    def pre_exact():
+        for q0 in range(0, L, C):
+            q1 = min(L, q0 + C)
+            tbs.infv2_select_blocks(devp.cfg, tbs.INFV2_MODE_PREFILL, devp.q[q0:q1], q1 - q0, q0,
+                                    devp.ck, devp.ck_offsets, devp.kv_offsets, None, 1, q1,
+                                    idx_e[q0:q1], None, ws_p)
+
+    def time_once(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(max(1, args.prefill_reps)):
+            e0 = T.event(); fn(); e1 = T.event()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+    pre = {"workload": wp.name, "exact_select_ms": time_once(pre_exact)}
+    ie = idx_e.cpu().numpy()
+    scored = np.arange(L) // wp.block_size + 1 > k
+    for c in (64, 128, 256):
+        ckc, ckc_off, _ = gh.coarse_ck(devp, c)
+
+        def pre_coarse(c=c, ckc=ckc, ckc_off=ckc_off):
+            for q0 in range(0, L, C):
+                q1 = min(L, q0 + C)
+                tbs.infv2_select_blocks_coarse(devp.cfg, c, tbs.INFV2_MODE_PREFILL, devp.q[q0:q1],
+                                               q1 - q0, q0, devp.ck, devp.ck_offsets, ckc, ckc_off,
+                                               devp.kv_offsets, None, 1, q1, idx_c[q0:q1], None, ws_p)
+        ms = time_once(pre_coarse)
+        same, shared = _agreement(idx_c.cpu().numpy()[scored], ie[scored])
+        pre[f"coarse_{c}"] = {"select_ms": ms, "same_selection": same, "blocks_shared": shared}
+    out["prefill_32k"] = pre
+    return out
+
+
 def bench_batched(args, torch, tbs, gh, ck_dtype=None) -> dict:
     # one step reads ~160 MiB, so three replicas already keep the MALL cold
     return bench_decode(4, args, torch, tbs, gh, replicas=min(args.replicas, 4), ck_dtype=ck_dtype)
@@ -690,13 +807,15 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-loop", action="store_true", help="skip the append + select + attend loop record")
     ap.add_argument("--no-backward", action="store_true", help="skip the 32K training-backward record")
+    ap.add_argument("--no-coarse", action="store_true", help="skip the coarse-kernel LSE selection record")
     ap.add_argument("--no-ck-bf16", action="store_true",
                     help="skip the extra decode records with bf16 compressed keys")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run 8 device-to-device copies of MIB MiB (reference kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--only", choices=["decode", "prefill", "batched", "backward"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "batched", "backward", "coarse"],
+                    default=None,
                     help="run one workload only and print its record (for profiling)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -729,6 +848,8 @@ def main() -> int:
             rec = bench_decode(2, args, torch, tbs, gh, replicas=args.replicas)
         elif args.only == "prefill":
             rec = {k: v for k, v in bench_prefill(args, torch, tbs, gh).items() if not k.startswith("_")}
+        elif args.only == "coarse":
+            rec = bench_coarse(args, torch, tbs, gh)
         elif args.only == "backward":
             from synth import make_config
             rec = bench_backward(args, torch, tbs, gh, {"_wl": make_config(3)})
@@ -754,6 +875,14 @@ def main() -> int:
     if bwd:
         log(f"backward 32K (training, one call): {bwd['ms']:.2f} ms, {bwd['tflops']:.1f} TFLOPS "
             f"algorithmic; {bwd['parity']}")
+    coarse = None if args.no_coarse else bench_coarse(args, torch, tbs, gh)
+    if coarse:
+        d2, p2 = coarse["decode_128k"], coarse["prefill_32k"]
+        log(f"coarse LSE: decode select {d2['exact_select_us']:.1f} us exact vs "
+            + ", ".join(f"{c}: {d2[f'coarse_{c}']['select_us']:.1f} us "
+                        f"({d2[f'coarse_{c}']['blocks_shared']:.0%} shared)" for c in (64, 128, 256))
+            + f"; prefill select {p2['exact_select_ms']:.2f} ms exact vs "
+            + ", ".join(f"{c}: {p2[f'coarse_{c}']['select_ms']:.2f} ms" for c in (64, 128, 256)))
     loop = None if args.no_loop else bench_decode_loop(args, torch, tbs, gh)
     if loop:
         log(f"decode loop 128K (append + select + attend): {loop['ms_per_step_graph'] * 1e3:.1f} us/step")
@@ -796,6 +925,8 @@ def main() -> int:
         out["prefill_varlen_8x4k-16k"] = varlen
     if bwd:
         out["prefill_backward_32k"] = bwd
+    if coarse:
+        out["coarse_lse_selection"] = coarse
     for k2, r2 in alt.items():
         out[k2] = {x: r2[x] for x in ("workload", "batch", "ms_per_step", "tok_per_s", "hbm_gbps_step",
                                       "per_call_us", "kernels", "bytes_per_step", "roofline", "parity")}
