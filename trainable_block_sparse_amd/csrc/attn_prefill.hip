@@ -98,6 +98,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
 
     // ---- union of the 16 rows' selected blocks (ascending list + row masks)
     const int n_u = build_union(sm, idx, rows, r0, hkv, g, topk, nblk);
+    balance_union(sm, n_u);                   // intervals spread their work over the SIMDs
 
     // ---- per-wave row state: wave w owns rows r0 + 8 i + w (i < 2)
     bf16x8_t qf[kPRowsW][4];
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
     }
     auto issue = [&](StageTiles& kt, StageTiles& vtt, int u) {
         const int slot = u % kGroup2;
-        const int32_t blk = sm.list[u];
+        const int32_t blk = sm.list[sm.order[u]];
         const int64_t k0 = static_cast<int64_t>(blk) * kPB;
         const bool partial = k0 + kPB > nlim;               // last block of the chunk
 #pragma unroll
@@ -151,8 +152,8 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
     };
     auto compute = [&](const StageTiles& kt, const StageTiles& vtt, int u) {
         const int slot = u % kGroup2;
-        const int32_t blk = sm.list[u];
-        const uint32_t msk = sm.mask[u];
+        const int32_t blk = sm.list[sm.order[u]];
+        const uint32_t msk = sm.mask[sm.order[u]];
         uint32_t act = 0;
         int cntr[kPRowsW];
 #pragma unroll

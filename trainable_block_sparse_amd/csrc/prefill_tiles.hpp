@@ -18,6 +18,9 @@ constexpr int kUnionCap = 2048;   // union entries: 16 rows x top-k, top-k <= 12
 struct UnionSmem {
     int32_t list[kUnionCap];          // union of the rows' blocks, ascending (<= 16 * topk)
     uint32_t mask[kUnionCap];         // which of the 16 rows selected each union block
+    uint16_t order[kUnionCap];        // streaming order (balance_union), or the identity
+    uint32_t bcount[2][kUWaves][5];   // balance_union: per-wave bucket counts, then their prefix
+    uint32_t bsize[5];                // balance_union: bucket sizes
     uint32_t bits[kUMaxWords];
     uint32_t wbase[kUMaxWords];
     uint32_t scan_tmp[kUWaves + 1];
@@ -95,6 +98,81 @@ __device__ __forceinline__ uint4 vt_frag(const BlockTile& t, int d, int chunk) {
 __device__ __forceinline__ int vt_key_of_pos(int pos) {
     const int kk = pos >> 5, w = pos & 31, g = w >> 3, a = (w >> 2) & 1, r = w & 3;
     return 32 * kk + 16 * a + 4 * g + r;
+}
+
+// Streaming order of the union that spreads each barrier interval's work over
+// the SIMDs.  Wave w of a 16-wave block runs on SIMD w % 4 and owns row w, so a
+// block's work on SIMD s is the number of rows w = s (mod 4) in its mask.  Each
+// block goes to the bucket of its busiest SIMD (a fifth bucket for blocks whose
+// SIMD counts differ by at most one), and the buckets are interleaved round
+// robin, so consecutive blocks -- the blocks of one interval -- load different
+// SIMDs.  The order is stable within a bucket.  Called by all kThreads threads
+// after build_union; order[] is valid after its final barrier.
+template <int kThreads = kUThreads>
+__device__ inline void balance_union(UnionSmem& sm, int n_u) {
+    constexpr int kWaves = kThreads / 64, kB = 5;
+    static_assert(kThreads * 2 >= kUnionCap, "two entries per thread at most");
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    int bk[2];
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+        const int u = rd * kThreads + t;
+        int b = -1;
+        if (u < n_u) {
+            const uint32_t m = sm.mask[u];
+            int best = 0, bc = __popc(m & 0x1111u), mn = bc;
+#pragma unroll
+            for (int x = 1; x < 4; ++x) {
+                const int c = __popc(m & (0x1111u << x));
+                if (c > bc) { bc = c; best = x; }
+                mn = c < mn ? c : mn;
+            }
+            b = (bc - mn <= 1) ? 4 : best;
+        }
+        bk[rd] = b;
+#pragma unroll
+        for (int x = 0; x < kB; ++x) {
+            const uint64_t bal = __ballot(b == x);
+            if (lane == 0) sm.bcount[rd][w][x] = static_cast<uint32_t>(__popcll(bal));
+        }
+    }
+    __syncthreads();
+    // exclusive prefix of the bucket counts over (round, wave), and the bucket sizes
+    if (t < 5) {
+        uint32_t run = 0;
+        for (int rd = 0; rd < 2; ++rd)
+            for (int y = 0; y < kWaves; ++y) {
+                const uint32_t c = sm.bcount[rd][y][t];
+                sm.bcount[rd][y][t] = run;
+                run += c;
+            }
+        sm.bsize[t] = run;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+        const int u = rd * kThreads + t;
+        const int b = bk[rd];
+        uint32_t i = 0;                              // index of u inside its bucket
+#pragma unroll
+        for (int x = 0; x < kB; ++x) {
+            const uint64_t bx = __ballot(b == x);
+            if (b == x) i = sm.bcount[rd][w][x] + __popcll(bx & ((uint64_t(1) << lane) - 1));
+        }
+        if (u < n_u) {
+            // round robin over the buckets: every bucket's items before index i,
+            // then the buckets before b that still have an item i
+            uint32_t pos = 0;
+#pragma unroll
+            for (int x = 0; x < kB; ++x) {
+                const uint32_t nx = sm.bsize[x];
+                pos += nx < i ? nx : i;
+                if (x < b && nx > i) ++pos;
+            }
+            sm.order[pos] = static_cast<uint16_t>(u);
+        }
+    }
+    __syncthreads();
 }
 
 }  // namespace infv2
