@@ -319,6 +319,7 @@ __global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
     const float* __restrict__ delta, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv,
     float* __restrict__ partial, int hq, int hkv, int nblk, float scale_log2, float scale) {
     __shared__ __attribute__((aligned(16))) RowTiles rt_a, rt_b;
+    __shared__ int32_t seg_rows[kSeg];      // this segment of the row list
     const int ncol = hkv * nblk;
     const int item = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
     if (item >= item_start[ncol]) return;
@@ -361,8 +362,8 @@ __global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
     float4 nl[2], nd[2];                                  // lse / D of the next pair, heads 4 lg ..
     int nra = 0, nrb = 0;
     auto issue = [&](RowTiles& rt, int e) {
-        nra = lst[e];
-        nrb = (e + 1 < end) ? lst[e + 1] : nra;
+        nra = seg_rows[e - beg];
+        nrb = (e + 1 < end) ? seg_rows[e + 1 - beg] : nra;
         __builtin_amdgcn_global_load_lds(tile_src(q, nra), &rt[0][w * 512], 16, 0, 0);
         __builtin_amdgcn_global_load_lds(tile_src(q, nrb), &rt[1][w * 512], 16, 0, 0);
         __builtin_amdgcn_global_load_lds(tile_src(dout, nra), &rt[2][w * 512], 16, 0, 0);
@@ -442,6 +443,10 @@ __global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
             for (int ks = 0; ks < 4; ++ks) fr[x][ks] = a_frag(rt, x, ks);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     };
+    // the row ids come through LDS, so that a pair's tile loads do not wait on
+    // a global load of its row ids
+    for (int e = t; e < end - beg; e += kCThreads) seg_rows[e] = lst[beg + e];
+    __syncthreads();
     const int npairs = (end - beg + 1) >> 1;
     if (npairs > 0) issue(rt_a, beg);
     for (int p = 0; p < npairs; ++p) {

@@ -106,11 +106,15 @@ __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast
 
 // two floats that hold bf16 values exactly -> packed bf16 pair (no rounding needed)
 __device__ __forceinline__ uint32_t pack_exact(float lo, float hi) {
-    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+    // one byte permute: bytes 2, 3 of lo, then bytes 2, 3 of hi
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
-// two floats -> packed bf16 pair, round to nearest even
+// two floats -> packed bf16 pair, round to nearest even (one paired conversion)
 __device__ __forceinline__ uint32_t pack_rne(float lo, float hi) {
-    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+    typedef float f32x2_v __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+    const f32x2_v x = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_v));
 }
 
 }  // namespace infv2
