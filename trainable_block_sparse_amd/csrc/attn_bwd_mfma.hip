@@ -310,6 +310,56 @@ __device__ __forceinline__ bf16x8_t select_b(int h, int lg, int lc) {
 }
 
 typedef bf16_t RowTiles[4][kGroup * kHeadDim];   // Q_A, Q_B, dO_A, dO_B (4 KB each)
+constexpr int kCStages = 4;                       // LDS ring of the column pass: 3 pairs in flight
+constexpr int kCLoads = 5;                        // global->LDS loads per wave and pair
+
+// The column pass reads LDS by hand.  The compiler cannot tell the ring slots
+// apart, so before any LDS read it would wait for every outstanding global->LDS
+// load, leaving one pair in flight; here the ring's own accounting decides.
+// Row ids of pair p of the segment (rows 2p, 2p + 1).
+__device__ __forceinline__ void lds_read_ids(uint32_t a, int& r0, int& r1) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 v;
+    asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a) : "memory");
+    r0 = static_cast<int>(v.x);
+    r1 = static_cast<int>(v.y);
+}
+
+// The 16 A fragments of a pair (tile x at byte offset 4096 x of the slot, K-step
+// ks at the lane's offset a[ks]) and the lane's lse / D values (four 16-float rows
+// at al); returns when all have landed.
+__device__ __forceinline__ void lds_read_pair(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                              uint32_t al, bf16x8_t (&fr)[4][4], f32x4_t (&ls)[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %20\n\tds_read_b128 %1, %21\n\t"
+        "ds_read_b128 %2, %22\n\tds_read_b128 %3, %23\n\t"
+        "ds_read_b128 %4, %20 offset:4096\n\tds_read_b128 %5, %21 offset:4096\n\t"
+        "ds_read_b128 %6, %22 offset:4096\n\tds_read_b128 %7, %23 offset:4096\n\t"
+        "ds_read_b128 %8, %20 offset:8192\n\tds_read_b128 %9, %21 offset:8192\n\t"
+        "ds_read_b128 %10, %22 offset:8192\n\tds_read_b128 %11, %23 offset:8192\n\t"
+        "ds_read_b128 %12, %20 offset:12288\n\tds_read_b128 %13, %21 offset:12288\n\t"
+        "ds_read_b128 %14, %22 offset:12288\n\tds_read_b128 %15, %23 offset:12288\n\t"
+        "ds_read_b128 %16, %24\n\tds_read_b128 %17, %24 offset:64\n\t"
+        "ds_read_b128 %18, %24 offset:128\n\tds_read_b128 %19, %24 offset:192\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(fr[0][0]), "=&v"(fr[0][1]), "=&v"(fr[0][2]), "=&v"(fr[0][3]),
+          "=&v"(fr[1][0]), "=&v"(fr[1][1]), "=&v"(fr[1][2]), "=&v"(fr[1][3]),
+          "=&v"(fr[2][0]), "=&v"(fr[2][1]), "=&v"(fr[2][2]), "=&v"(fr[2][3]),
+          "=&v"(fr[3][0]), "=&v"(fr[3][1]), "=&v"(fr[3][2]), "=&v"(fr[3][3]),
+          "=&v"(ls[0]), "=&v"(ls[1]), "=&v"(ls[2]), "=&v"(ls[3])
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(al)
+        : "memory");
+}
+
+// wait until this wave's loads of the current pair have landed (at most `later`
+// further pairs' loads outstanding; loads complete in order), then a barrier
+// makes every wave's share visible and frees the slot read one pair earlier
+__device__ __forceinline__ void ring_wait(int later) {
+    static_assert(kCStages == 4 && kCLoads == 5, "vmcnt immediates below");
+    if (later >= 2) asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
+    else if (later == 1) asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 __global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout, int rows, int64_t q_start,
@@ -318,8 +368,9 @@ __global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
     const int32_t* __restrict__ item_start, const float* __restrict__ lse2,
     const float* __restrict__ delta, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv,
     float* __restrict__ partial, int hq, int hkv, int nblk, float scale_log2, float scale) {
-    __shared__ __attribute__((aligned(16))) RowTiles rt_a, rt_b;
-    __shared__ int32_t seg_rows[kSeg];      // this segment of the row list
+    __shared__ __attribute__((aligned(16))) RowTiles ring[kCStages];
+    __shared__ __attribute__((aligned(16))) float lsd[kCStages][kCThreads / 64][64];  // per wave
+    __shared__ __attribute__((aligned(16))) int32_t seg_rows[kSeg + 2];  // the segment's row ids
     const int ncol = hkv * nblk;
     const int item = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
     if (item >= item_start[ncol]) return;
@@ -336,6 +387,7 @@ __global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
     const int32_t* lst = list + static_cast<size_t>(g) * list_ld;
     const int32_t beg = cs[j] + seg * kSeg;
     const int32_t end = (cs[j + 1] < beg + kSeg) ? cs[j + 1] : beg + kSeg;
+    const int n = end - beg;
 
     const int t = threadIdx.x, w = t >> 6, l = t & 63, lg = l >> 4, lc = l & 15;
     const int64_t lim = q_start + rows;
@@ -349,41 +401,52 @@ __global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
         kf[ks] = as_bf16x8(ldg16(k + hoff + keyc * kHeadDim + 32 * ks + 8 * lg));
         vf[ks] = as_bf16x8(ldg16(v + hoff + keyc * kHeadDim + 32 * ks + 8 * lg));
     }
+    {
+        int32_t r[kSeg / kCThreads];         // all loads first, then the LDS writes
+#pragma unroll
+        for (int i = 0; i < kSeg / kCThreads; ++i) r[i] = (t + i * kCThreads < n) ? lst[beg + t + i * kCThreads] : 0;
+#pragma unroll
+        for (int i = 0; i < kSeg / kCThreads; ++i) seg_rows[t + i * kCThreads] = r[i];
+    }
     f32x4_t av[8], ak[8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) { av[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f}; ak[dt] = av[dt]; }
     const bf16x8_t sel0 = select_b(0, lg, lc), sel1 = select_b(1, lg, lc);
+    __syncthreads();                         // row ids in LDS; K / V fragments landed
 
     // stage slot t of each tile: head h = t / 16 holds chunk (t % 16) ^ h there
     const int sh_h = t >> 4, sh_c = (t & 15) ^ (t >> 4);
     auto tile_src = [&](const bf16_t* base, int r) {
         return base + (static_cast<size_t>(r) * hq + static_cast<size_t>(g) * kGroup + sh_h) * kHeadDim + 8 * sh_c;
     };
-    float4 nl[2], nd[2];                                  // lse / D of the next pair, heads 4 lg ..
-    int nra = 0, nrb = 0;
-    auto issue = [&](RowTiles& rt, int e) {
-        nra = seg_rows[e - beg];
-        nrb = (e + 1 < end) ? seg_rows[e + 1 - beg] : nra;
-        __builtin_amdgcn_global_load_lds(tile_src(q, nra), &rt[0][w * 512], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(tile_src(q, nrb), &rt[1][w * 512], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(tile_src(dout, nra), &rt[2][w * 512], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(tile_src(dout, nrb), &rt[3][w * 512], 16, 0, 0);
-        const size_t oa = static_cast<size_t>(nra) * hq + static_cast<size_t>(g) * kGroup + 4 * lg;
-        const size_t ob = static_cast<size_t>(nrb) * hq + static_cast<size_t>(g) * kGroup + 4 * lg;
-        nl[0] = *reinterpret_cast<const float4*>(lse2 + oa);
-        nl[1] = *reinterpret_cast<const float4*>(lse2 + ob);
-        nd[0] = *reinterpret_cast<const float4*>(delta + oa);
-        nd[1] = *reinterpret_cast<const float4*>(delta + ob);
+    // lse / D slot of this wave: lane l loads quantity l / 16 (lse A, lse B, D A,
+    // D B) of head l % 16
+    const float* ld_src = (l < 32 ? lse2 : delta) + static_cast<size_t>(g) * kGroup + (l & 15);
+    const bool ld_b = (l & 16) != 0;
+    const uint32_t ids0 = lds_offset(&seg_rows[0]);
+    auto issue = [&](int p) {
+        const int s = p % kCStages;
+        int ra, rb;
+        lds_read_ids(ids0 + 8u * p, ra, rb);
+        if (2 * p + 1 >= n) rb = ra;
+        __builtin_amdgcn_global_load_lds(tile_src(q, ra), &ring[s][0][w * 512], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(tile_src(q, rb), &ring[s][1][w * 512], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(tile_src(dout, ra), &ring[s][2][w * 512], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(tile_src(dout, rb), &ring[s][3][w * 512], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(ld_src + static_cast<size_t>(ld_b ? rb : ra) * hq,
+                                         &lsd[s][w][0], 4, 0, 0);
     };
-    // A operand of S / dP: lane holds X[head lc][d = 32 ks + 8 lg ..]
-    auto a_frag = [&](const RowTiles& rt, int x, int ks) {
-        const int c = 4 * ks + lg;
-        return as_bf16x8(*reinterpret_cast<const uint4*>(&rt[x][lc * kHeadDim + 8 * (c ^ lc)]));
-    };
-    // fr[x][ks] = a_frag(x, ks): every LDS read of a pair happens before the next
-    // pair's loads are issued, so its products overlap those loads
+    // lane's byte offsets of its A fragments inside a tile (chunks XOR-swizzled by head)
+    uint32_t fa[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) fa[ks] = 2u * (lc * kHeadDim + 8 * ((4 * ks + lg) ^ lc));
+    const uint32_t ring0 = lds_offset(&ring[0][0][0]);
+    const uint32_t lsd0 = lds_offset(&lsd[0][w][0]) + 16u * lg;
+
+    // fr[x][ks]: A fragment of tile x (Q_A, Q_B, dO_A, dO_B), K-step ks;
+    // ls: lse of rows A, B, then D of rows A, B, heads 4 lg .. 4 lg + 3
     auto compute = [&](const bf16x8_t (&fr)[4][4], int ra, int rb, bool has_b,
-                       const float4 (&cl)[2], const float4 (&cd)[2]) {
+                       const f32x4_t (&ls)[4]) {
         f32x4_t s[2], dp[2];
 #pragma unroll
         for (int x = 0; x < 2; ++x) { s[x] = f32x4_t{0.f, 0.f, 0.f, 0.f}; dp[x] = s[x]; }
@@ -400,8 +463,7 @@ __global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
         const int64_t pa = q_start + ra, pb = q_start + rb;
         const bool visa = key < lim && key <= pa;
         const bool visb = has_b && key < lim && key <= pb;
-        const float la[4] = {cl[0].x, cl[0].y, cl[0].z, cl[0].w}, lb[4] = {cl[1].x, cl[1].y, cl[1].z, cl[1].w};
-        const float da[4] = {cd[0].x, cd[0].y, cd[0].z, cd[0].w}, db[4] = {cd[1].x, cd[1].y, cd[1].z, cd[1].w};
+        const f32x4_t la = ls[0], lb = ls[1], da = ls[2], db = ls[3];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             pv[0][r] = visa ? fast_exp2(fmaf(s[0][r], scale_log2, -la[r])) : 0.f;
@@ -436,34 +498,21 @@ __global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
             if (dt & 1) __builtin_amdgcn_sched_barrier(0);      // two d-tiles of transposes in flight
         }
     };
-    auto load_frags = [&](const RowTiles& rt, bf16x8_t (&fr)[4][4]) {
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) fr[x][ks] = a_frag(rt, x, ks);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    };
-    // the row ids come through LDS, so that a pair's tile loads do not wait on
-    // a global load of its row ids
-    for (int e = t; e < end - beg; e += kCThreads) seg_rows[e] = lst[beg + e];
-    __syncthreads();
-    const int npairs = (end - beg + 1) >> 1;
-    if (npairs > 0) issue(rt_a, beg);
+    const int npairs = (n + 1) >> 1;
+    for (int p = 0; p < kCStages - 1 && p < npairs; ++p) issue(p);
     for (int p = 0; p < npairs; ++p) {
-        const int ra = nra, rb = nrb;
-        const bool has_b = beg + 2 * p + 1 < end;
-        const float4 cl[2] = {nl[0], nl[1]}, cd[2] = {nd[0], nd[1]};
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();                      // pair p landed; pair p - 1 consumed by every wave
+        const int left = npairs - 1 - p;
+        ring_wait(left < kCStages - 2 ? left : kCStages - 2);
+        if (p + kCStages - 1 < npairs) issue(p + kCStages - 1);
+        const uint32_t sb = ring0 + static_cast<uint32_t>((p % kCStages) * sizeof(RowTiles));
         bf16x8_t fr[4][4];
-        if (p & 1) {
-            load_frags(rt_b, fr);
-            if (p + 1 < npairs) issue(rt_a, beg + 2 * (p + 1));
-        } else {
-            load_frags(rt_a, fr);
-            if (p + 1 < npairs) issue(rt_b, beg + 2 * (p + 1));
-        }
-        compute(fr, ra, rb, has_b, cl, cd);
+        f32x4_t ls[4];
+        lds_read_pair(sb + fa[0], sb + fa[1], sb + fa[2], sb + fa[3],
+                      lsd0 + static_cast<uint32_t>((p % kCStages) * (kCThreads / 64) * 64 * sizeof(float)),
+                      fr, ls);
+        int ra, rb;
+        lds_read_ids(ids0 + 8u * p, ra, rb);
+        compute(fr, ra, rb, 2 * p + 1 < n, ls);
     }
 
     // ---- epilogue: lane holds dV^T / dK^T[d = 16 dt + 4 lg + r][key 16 w + lc]
