@@ -109,6 +109,10 @@ __device__ __forceinline__ uint32_t pack_exact(float lo, float hi) {
     // one byte permute: bytes 2, 3 of lo, then bytes 2, 3 of hi
     return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
+// LDS byte offset of a __shared__ object: the low half of its generic address
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
 // two floats -> packed bf16 pair, round to nearest even (one paired conversion)
 __device__ __forceinline__ uint32_t pack_rne(float lo, float hi) {
     typedef float f32x2_v __attribute__((ext_vector_type(2)));
