@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kRThreads, 1) void bwd_row_mfma(
     const int d_l = 8 * w + (l >> 3);                            // K^T rows 8 w .. 8 w + 7
     const int toff_l = d_l * kPB + 8 * ((l & 7) ^ ((d_l >> 1) & 7));
     auto issue = [&](BlockTile& kt_, BlockTile& vt_, BlockTile& tt_, int u) {
-        const int32_t blk = sm.list[sm.order[u]];
+        const int32_t blk = sm.list[u];
         const int64_t k0 = static_cast<int64_t>(blk) * kPB;
         int64_t off = k0 * kHeadDim + koff_l;
         if (k0 + kPB > nlim) {                                   // clamp: later keys are masked
@@ -152,9 +152,9 @@ __global__ __launch_bounds__(kRThreads, 1) void bwd_row_mfma(
         __builtin_amdgcn_global_load_lds(kth + k0 * kHeadDim + toff_l, &tt_[w * 512], 16, 0, 0);
     };
     auto compute = [&](const BlockTile& kt_, const BlockTile& vt_, const BlockTile& tt_, int u) {
-        const int32_t blk = sm.list[sm.order[u]];
+        const int32_t blk = sm.list[u];
         const int cntr = qpos + 1 - blk * kPB;                   // keys of the block at or before the row
-        const bool act = ((sm.mask[sm.order[u]] >> w) & 1u) && row < rows && cntr > 0;
+        const bool act = ((sm.mask[u] >> w) & 1u) && row < rows && cntr > 0;
         if (!__builtin_amdgcn_readfirstlane(static_cast<int>(act))) return;
         f32x4_t s[4];
 #pragma unroll

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
     }
     auto issue = [&](StageTiles& kt, StageTiles& vtt, int u) {
         const int slot = u % kGroup2;
-        const int32_t blk = sm.list[sm.order[u]];
+        const int32_t blk = sm.list[u];
         const int64_t k0 = static_cast<int64_t>(blk) * kPB;
         const bool partial = k0 + kPB > nlim;               // last block of the chunk
 #pragma unroll
@@ -152,8 +152,8 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
     };
     auto compute = [&](const StageTiles& kt, const StageTiles& vtt, int u) {
         const int slot = u % kGroup2;
-        const int32_t blk = sm.list[sm.order[u]];
-        const uint32_t msk = sm.mask[sm.order[u]];
+        const int32_t blk = sm.list[u];
+        const uint32_t msk = sm.mask[u];
         uint32_t act = 0;
         int cntr[kPRowsW];
 #pragma unroll

@@ -18,7 +18,7 @@ constexpr int kUnionCap = 2048;   // union entries: 16 rows x top-k, top-k <= 12
 struct UnionSmem {
     int32_t list[kUnionCap];          // union of the rows' blocks, ascending (<= 16 * topk)
     uint32_t mask[kUnionCap];         // which of the 16 rows selected each union block
-    uint16_t order[kUnionCap];        // streaming order (balance_union), or the identity
+    uint16_t order[kUnionCap];        // balance_union scratch: the streaming order
     uint32_t bcount[2][kUWaves][5];   // balance_union: per-wave bucket counts, then their prefix
     uint32_t bsize[5];                // balance_union: bucket sizes
     uint32_t bits[kUMaxWords];
@@ -107,7 +107,8 @@ __device__ __forceinline__ int vt_key_of_pos(int pos) {
 // SIMD counts differ by at most one), and the buckets are interleaved round
 // robin, so consecutive blocks -- the blocks of one interval -- load different
 // SIMDs.  The order is stable within a bucket.  Called by all kThreads threads
-// after build_union; order[] is valid after its final barrier.
+// after build_union; on return list[] and mask[] hold the union in streaming
+// order (order[] is scratch).
 template <int kThreads = kUThreads>
 __device__ inline void balance_union(UnionSmem& sm, int n_u) {
     constexpr int kWaves = kThreads / 64, kB = 5;
@@ -170,6 +171,29 @@ __device__ inline void balance_union(UnionSmem& sm, int n_u) {
                 if (x < b && nx > i) ++pos;
             }
             sm.order[pos] = static_cast<uint16_t>(u);
+        }
+    }
+    __syncthreads();
+    // apply the order: list[] and mask[] become the streaming order itself, so
+    // a consumer finds block u with one LDS read
+    int32_t bl[2];
+    uint32_t bm[2];
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+        const int u = rd * kThreads + t;
+        if (u < n_u) {
+            const int o = sm.order[u];
+            bl[rd] = sm.list[o];
+            bm[rd] = sm.mask[o];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+        const int u = rd * kThreads + t;
+        if (u < n_u) {
+            sm.list[u] = bl[rd];
+            sm.mask[u] = bm[rd];
         }
     }
     __syncthreads();
