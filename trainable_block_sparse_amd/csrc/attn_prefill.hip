@@ -77,10 +77,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
     const bf16_t* __restrict__ vt, const int64_t* __restrict__ kv_off,
     const int32_t* __restrict__ idx, bf16_t* __restrict__ out, int hq, int hkv, int topk,
     int64_t nblk, int nrg, float scale_log2) {
-    // The two stages are distinct LDS objects and every access below names its
-    // stage, so the compiler can see that reading one stage does not depend on
-    // the direct global->LDS loads still filling the other one.
-    __shared__ __attribute__((aligned(16))) StageTiles k_a, v_a, k_b, v_b;
+    __shared__ __attribute__((aligned(16))) StageTiles kst[2], vst[2];   // two stages
     __shared__ UnionSmem sm;
     // XCD-aware placement: thread block b runs on XCD b % 8; give each XCD a
     // contiguous range of (KV head, row group) work items
@@ -118,7 +115,13 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
         mref[i] = -INFINITY;
         lsum[i] = 0.f;
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // only the tile loads stay in flight below
+    // make the compiler wait for the q fragments here, where it sees the use;
+    // otherwise it keeps them pending and waits for all loads (the next
+    // interval's tile loads included) inside the products
+#pragma unroll
+    for (int i = 0; i < kPRowsW; ++i)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) asm volatile("" :: "v"(qf[i][ks]));
 
     // ---- stream the union through LDS with direct global->LDS loads.  Each
     // wave fills 2 KB of each K and V^T tile (2 instructions each); the lane part
@@ -146,8 +149,8 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
                 gk = gk < nlim ? gk : nlim - 1;
                 ksrc = kh + gk * kHeadDim + 8 * ((l & 15) ^ (key_l[j] & 15));
             }
-            __builtin_amdgcn_global_load_lds(ksrc, &kt[slot][sg * 512], 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vth + k0 * kHeadDim + voff_l[j], &vtt[slot][sg * 512], 16, 0, 0);
+            dma16(ksrc, lds_offset(&kt[slot][sg * 512]));
+            dma16(vth + k0 * kHeadDim + voff_l[j], lds_offset(&vtt[slot][sg * 512]));
         }
     };
     auto compute = [&](const StageTiles& kt, const StageTiles& vtt, int u) {
@@ -266,14 +269,20 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
     // the work of a double-buffered pair of two-block stages, which evens out
     // the random share of active (row, block) pairs between the SIMDs; the
     // wait at each barrier is set by the busiest SIMD, not by the load.
-    for (int u0 = 0; u0 < n_u; u0 += 2 * kGroup2) {
-        __syncthreads();                                    // previous blocks consumed
-        for (int x = u0; x < u0 + kGroup2 && x < n_u; ++x) issue(k_a, v_a, x);
-        for (int x = u0 + kGroup2; x < u0 + 2 * kGroup2 && x < n_u; ++x) issue(k_b, v_b, x);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        for (int u = u0; u < u0 + kGroup2 && u < n_u; ++u) compute(k_a, v_a, u);
-        for (int u = u0 + kGroup2; u < u0 + 2 * kGroup2 && u < n_u; ++u) compute(k_b, v_b, u);
+    const int n_iv = (n_u + kGroup2 - 1) / kGroup2;
+    for (int x = 0; x < kGroup2 && x < n_u; ++x) issue(kst[0], vst[0], x);
+    for (int iv = 0; iv < n_iv; ++iv) {
+        // interval iv landed (the only loads in flight); every wave is done
+        // with interval iv - 1, whose stage now takes interval iv + 1, one
+        // block's loads before each block of products
+        dma_wait_barrier();
+        const int sx = (iv + 1) & 1, sc = iv & 1;
+#pragma unroll
+        for (int b = 0; b < kGroup2; ++b) {
+            const int xn = (iv + 1) * kGroup2 + b, u = iv * kGroup2 + b;
+            if (xn < n_u) issue(kst[sx], vst[sx], xn);
+            if (u < n_u) compute(kst[sc], vst[sc], u);
+        }
     }
 
     // ---- epilogue: row sum over the four lanes of each head; lane holds
