@@ -92,8 +92,7 @@ __global__ __launch_bounds__(kRThreads, 1) void bwd_row_mfma(
     const int32_t* __restrict__ idx, bf16_t* __restrict__ dq, float* __restrict__ lse2,
     float* __restrict__ delta, int hq, int hkv, int topk, int64_t nblk, int nrg, float scale_log2,
     float scale) {
-    // two stages (distinct LDS objects, named at every access) of one block each
-    __shared__ __attribute__((aligned(16))) BlockTile k_a, v_a, t_a, k_b, v_b, t_b;
+    __shared__ __attribute__((aligned(16))) BlockTile kst[2], vst[2], tst[2];   // two stages of one block
     __shared__ UnionSmem sm;
     const int lid = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
     const int g = lid / nrg, r0 = (lid % nrg) * kURows;
@@ -131,7 +130,10 @@ __global__ __launch_bounds__(kRThreads, 1) void bwd_row_mfma(
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float mref = -INFINITY, lsum = 0.f;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // the compiler waits for q and dO here, where it sees their use, and not
+    // for every outstanding load (the next block's tiles) inside the products
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) asm volatile("" :: "v"(qf[ks]), "v"(dof[ks]));
 
     // ---- tile loads: each wave fills 1 KB of each tile (one 16-byte load per lane)
     const int key_l = 4 * w + (l >> 4);                          // keys 4 w .. 4 w + 3
@@ -147,9 +149,9 @@ __global__ __launch_bounds__(kRThreads, 1) void bwd_row_mfma(
             gk = gk < nlim ? gk : nlim - 1;
             off = gk * kHeadDim + 8 * ((l & 15) ^ (key_l & 15));
         }
-        __builtin_amdgcn_global_load_lds(kh + off, &kt_[w * 512], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vh + off, &vt_[w * 512], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(kth + k0 * kHeadDim + toff_l, &tt_[w * 512], 16, 0, 0);
+        dma16(kh + off, lds_offset(&kt_[w * 512]));
+        dma16(vh + off, lds_offset(&vt_[w * 512]));
+        dma16(kth + k0 * kHeadDim + toff_l, lds_offset(&tt_[w * 512]));
     };
     auto compute = [&](const BlockTile& kt_, const BlockTile& vt_, const BlockTile& tt_, int u) {
         const int32_t blk = sm.list[u];
@@ -237,14 +239,14 @@ __global__ __launch_bounds__(kRThreads, 1) void bwd_row_mfma(
             }
         }
     };
-    for (int u0 = 0; u0 < n_u; u0 += 2) {
-        __syncthreads();                                         // previous blocks consumed
-        issue(k_a, v_a, t_a, u0);
-        if (u0 + 1 < n_u) issue(k_b, v_b, t_b, u0 + 1);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        compute(k_a, v_a, t_a, u0);
-        if (u0 + 1 < n_u) compute(k_b, v_b, t_b, u0 + 1);
+    // one block per barrier interval, double-buffered: block u + 1 loads under
+    // the products of block u
+    if (n_u > 0) issue(kst[0], vst[0], tst[0], 0);
+    for (int u = 0; u < n_u; ++u) {
+        dma_wait_barrier();                  // block u landed; every wave is done with u - 1
+        const int sx = (u + 1) & 1, sc = u & 1;
+        if (u + 1 < n_u) issue(kst[sx], vst[sx], tst[sx], u + 1);
+        compute(kst[sc], vst[sc], tst[sc], u);
     }
 
     // ---- epilogue: lane holds dQ^T[d = 16 mt + 4 lg + r][head lc]
