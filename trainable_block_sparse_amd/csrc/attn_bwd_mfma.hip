@@ -22,11 +22,10 @@
 //   S = Q . K^T, dP = dO . V^T          4 x 4 MFMA (two rows, Q and dO)
 //   P = 2^(S scale - lse), dA = P (dP - D)
 //   dV^T += dO^T . P,  dK^T += Q^T . dA 16 MFMA
-// The Q^T and dO^T operands (heads along the contraction) are produced from the
-// S / dP operands themselves by a 16x16x32 product with a 0/1 selector of 16 of
-// the 32 columns, which lands each value exactly where the operand layout wants
-// it (and reads LDS only in the conflict-free 16-byte pattern).  The pairs'
-// Q and dO tiles are double-buffered in LDS with direct global->LDS loads.
+// The Q^T and dO^T operands (heads along the contraction) come from the same
+// LDS tiles through transpose reads (ds_read_b64_tr_b16).  The pairs' Q, dO,
+// lse and D go through a four-slot LDS ring with direct global->LDS loads,
+// three pairs in flight.
 // A block whose list is longer than kSeg rows is split into segments whose
 // fp32 partials are summed in segment order by bwd_col_finish, so results do
 // not depend on scheduling.
@@ -297,60 +296,26 @@ __global__ __launch_bounds__(1024) void bwd_items_kernel(const int32_t* __restri
     if (t == 0) item_start[ncol] = static_cast<int32_t>(carry);
 }
 
-// selector operand of the 16x16x32 product that picks columns 16 h .. 16 h + 15 of
-// A: lane holds B[8 lg + e][lc] = 1 if 8 lg + e == 16 h + lc, else 0
-__device__ __forceinline__ bf16x8_t select_b(int h, int lg, int lc) {
-    uint4 u;
-    uint32_t* w = reinterpret_cast<uint32_t*>(&u);
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-        const uint32_t lo = (8 * lg + 2 * e2 == 16 * h + lc) ? 0x3F80u : 0u;
-        const uint32_t hi = (8 * lg + 2 * e2 + 1 == 16 * h + lc) ? 0x3F80u : 0u;
-        w[e2] = lo | (hi << 16);
-    }
-    return as_bf16x8(u);
-}
-
 typedef bf16_t RowTiles[4][kGroup * kHeadDim];   // Q_A, Q_B, dO_A, dO_B (4 KB each)
 constexpr int kCStages = 4;                       // LDS ring of the column pass: 3 pairs in flight
 constexpr int kCLoads = 5;                        // global->LDS loads per wave and pair
 
-// The column pass reads LDS by hand.  The compiler cannot tell the ring slots
-// apart, so before any LDS read it would wait for every outstanding global->LDS
-// load, leaving one pair in flight; here the ring's own accounting decides.
-// Row ids of pair p of the segment (rows 2p, 2p + 1).
-__device__ __forceinline__ void lds_read_ids(uint32_t a, int& r0, int& r1) {
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    u32x2 v;
-    asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a) : "memory");
-    r0 = static_cast<int>(v.x);
-    r1 = static_cast<int>(v.y);
+// Direct global->LDS load of 4 B per lane (lane i writes bytes 4 i .. 4 i + 3
+// from the wave-uniform `lds`), issued by hand like dma16.
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
+    asm volatile("global_load_lds_dword %0, off" :: "v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory");
 }
 
-// The 16 A fragments of a pair (tile x at byte offset 4096 x of the slot, K-step
-// ks at the lane's offset a[ks]) and the lane's lse / D values (four 16-float rows
-// at al); returns when all have landed.
-__device__ __forceinline__ void lds_read_pair(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
-                                              uint32_t al, bf16x8_t (&fr)[4][4], f32x4_t (&ls)[4]) {
-    asm volatile(
-        "ds_read_b128 %0, %20\n\tds_read_b128 %1, %21\n\t"
-        "ds_read_b128 %2, %22\n\tds_read_b128 %3, %23\n\t"
-        "ds_read_b128 %4, %20 offset:4096\n\tds_read_b128 %5, %21 offset:4096\n\t"
-        "ds_read_b128 %6, %22 offset:4096\n\tds_read_b128 %7, %23 offset:4096\n\t"
-        "ds_read_b128 %8, %20 offset:8192\n\tds_read_b128 %9, %21 offset:8192\n\t"
-        "ds_read_b128 %10, %22 offset:8192\n\tds_read_b128 %11, %23 offset:8192\n\t"
-        "ds_read_b128 %12, %20 offset:12288\n\tds_read_b128 %13, %21 offset:12288\n\t"
-        "ds_read_b128 %14, %22 offset:12288\n\tds_read_b128 %15, %23 offset:12288\n\t"
-        "ds_read_b128 %16, %24\n\tds_read_b128 %17, %24 offset:64\n\t"
-        "ds_read_b128 %18, %24 offset:128\n\tds_read_b128 %19, %24 offset:192\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(fr[0][0]), "=&v"(fr[0][1]), "=&v"(fr[0][2]), "=&v"(fr[0][3]),
-          "=&v"(fr[1][0]), "=&v"(fr[1][1]), "=&v"(fr[1][2]), "=&v"(fr[1][3]),
-          "=&v"(fr[2][0]), "=&v"(fr[2][1]), "=&v"(fr[2][2]), "=&v"(fr[2][3]),
-          "=&v"(fr[3][0]), "=&v"(fr[3][1]), "=&v"(fr[3][2]), "=&v"(fr[3][3]),
-          "=&v"(ls[0]), "=&v"(ls[1]), "=&v"(ls[2]), "=&v"(ls[3])
-        : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(al)
-        : "memory");
+// LDS transpose read of 8 bytes per lane: inside each group of 16 lanes, lane i
+// receives as its element e (e = 0..3) halfword i % 4 of the 8 bytes that lane
+// 4 e + i / 4 addresses.
+__device__ __forceinline__ uint2 lds_read_tr16(uint32_t byte_offset) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<lds_s16x4*>(static_cast<uintptr_t>(byte_offset)));
+    return __builtin_bit_cast(uint2, v);
 }
 
 // wait until this wave's loads of the current pair have landed (at most `later`
@@ -413,8 +378,11 @@ __global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
     f32x4_t av[8], ak[8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) { av[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f}; ak[dt] = av[dt]; }
-    const bf16x8_t sel0 = select_b(0, lg, lc), sel1 = select_b(1, lg, lc);
-    __syncthreads();                         // row ids in LDS; K / V fragments landed
+    // the compiler waits for K and V here, where it sees their use, and not for
+    // every outstanding load (the ring's) inside the products
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) asm volatile("" :: "v"(kf[ks]), "v"(vf[ks]));
+    __syncthreads();                         // row ids in LDS
 
     // stage slot t of each tile: head h = t / 16 holds chunk (t % 16) ^ h there
     const int sh_h = t >> 4, sh_c = (t & 15) ^ (t >> 4);
@@ -425,30 +393,44 @@ __global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
     // D B) of head l % 16
     const float* ld_src = (l < 32 ? lse2 : delta) + static_cast<size_t>(g) * kGroup + (l & 15);
     const bool ld_b = (l & 16) != 0;
-    const uint32_t ids0 = lds_offset(&seg_rows[0]);
+    // The ring is filled by hand-issued loads (the compiler does not see them, so
+    // it does not wait for all of them before each LDS read); ring_wait orders
+    // them against the reads.
     auto issue = [&](int p) {
         const int s = p % kCStages;
-        int ra, rb;
-        lds_read_ids(ids0 + 8u * p, ra, rb);
-        if (2 * p + 1 >= n) rb = ra;
-        __builtin_amdgcn_global_load_lds(tile_src(q, ra), &ring[s][0][w * 512], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(tile_src(q, rb), &ring[s][1][w * 512], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(tile_src(dout, ra), &ring[s][2][w * 512], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(tile_src(dout, rb), &ring[s][3][w * 512], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(ld_src + static_cast<size_t>(ld_b ? rb : ra) * hq,
-                                         &lsd[s][w][0], 4, 0, 0);
+        const int ra = seg_rows[2 * p];
+        const int rb = (2 * p + 1 < n) ? seg_rows[2 * p + 1] : ra;
+        dma16(tile_src(q, ra), lds_offset(&ring[s][0][w * 512]));
+        dma16(tile_src(q, rb), lds_offset(&ring[s][1][w * 512]));
+        dma16(tile_src(dout, ra), lds_offset(&ring[s][2][w * 512]));
+        dma16(tile_src(dout, rb), lds_offset(&ring[s][3][w * 512]));
+        dma4(ld_src + static_cast<size_t>(ld_b ? rb : ra) * hq, lds_offset(&lsd[s][w][0]));
     };
-    // lane's byte offsets of its A fragments inside a tile (chunks XOR-swizzled by head)
-    uint32_t fa[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) fa[ks] = 2u * (lc * kHeadDim + 8 * ((4 * ks + lg) ^ lc));
-    const uint32_t ring0 = lds_offset(&ring[0][0][0]);
-    const uint32_t lsd0 = lds_offset(&lsd[0][w][0]) + 16u * lg;
+    // Transposed operands (d along M, (row, head) along K) come straight from
+    // the tiles by transpose reads: for d-tile dt this lane reads the 4 values
+    // d = 16 dt + 4 (lc % 4) .. + 3 of head 4 lg + lc / 4, which hands lane lc
+    // element e = X[head 4 lg + e][d = 16 dt + lc].
+    const int th = 4 * lg + (lc >> 2), tb = (lc >> 1) & 1;
+    const uint32_t tr0 = 2u * static_cast<uint32_t>(th * kHeadDim + 4 * (lc & 1));
 
-    // fr[x][ks]: A fragment of tile x (Q_A, Q_B, dO_A, dO_B), K-step ks;
-    // ls: lse of rows A, B, then D of rows A, B, heads 4 lg .. 4 lg + 3
-    auto compute = [&](const bf16x8_t (&fr)[4][4], int ra, int rb, bool has_b,
-                       const f32x4_t (&ls)[4]) {
+    auto compute = [&](int p) {
+        const int sl = p % kCStages;
+        const RowTiles& rt = ring[sl];
+        // A fragments of tile x (Q_A, Q_B, dO_A, dO_B), K-step ks: lane holds
+        // X[head lc][d = 32 ks + 8 lg ..] (chunks XOR-swizzled by head)
+        bf16x8_t fr[4][4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                fr[x][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&rt[x][lc * kHeadDim + 8 * ((4 * ks + lg) ^ lc)]));
+        const int ra = seg_rows[2 * p], rb = seg_rows[2 * p + 1];
+        const bool has_b = 2 * p + 1 < n;
+        // lse of rows A, B and D of rows A, B, heads 4 lg .. 4 lg + 3
+        const f32x4_t la = *reinterpret_cast<const f32x4_t*>(&lsd[sl][w][4 * lg]);
+        const f32x4_t lb = *reinterpret_cast<const f32x4_t*>(&lsd[sl][w][16 + 4 * lg]);
+        const f32x4_t da = *reinterpret_cast<const f32x4_t*>(&lsd[sl][w][32 + 4 * lg]);
+        const f32x4_t db = *reinterpret_cast<const f32x4_t*>(&lsd[sl][w][48 + 4 * lg]);
         f32x4_t s[2], dp[2];
 #pragma unroll
         for (int x = 0; x < 2; ++x) { s[x] = f32x4_t{0.f, 0.f, 0.f, 0.f}; dp[x] = s[x]; }
@@ -465,7 +447,6 @@ __global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
         const int64_t pa = q_start + ra, pb = q_start + rb;
         const bool visa = key < lim && key <= pa;
         const bool visb = has_b && key < lim && key <= pb;
-        const f32x4_t la = ls[0], lb = ls[1], da = ls[2], db = ls[3];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             pv[0][r] = visa ? fast_exp2(fmaf(s[0][r], scale_log2, -la[r])) : 0.f;
@@ -480,41 +461,25 @@ __global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
         du.x = pack_rne(av_[0][0], av_[0][1]); du.y = pack_rne(av_[0][2], av_[0][3]);
         du.z = pack_rne(av_[1][0], av_[1][1]); du.w = pack_rne(av_[1][2], av_[1][3]);
         const bf16x8_t pb_ = as_bf16x8(pu), db_ = as_bf16x8(du);
+        const uint32_t rt0 = lds_offset(&rt[0][0]) + tr0;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-            // transposes: lane gets X[head 4 lg + r][d = 16 dt + lc] (exact bf16
-            // values), d-tile dt being half dt % 2 of the S / dP operand of K-step dt / 2
-            const f32x4_t z = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            const bf16x8_t sel = (dt & 1) ? sel1 : sel0;
-            const f32x4_t qa = mfma32(fr[0][dt >> 1], sel, z);
-            const f32x4_t qb = mfma32(fr[1][dt >> 1], sel, z);
-            const f32x4_t oa = mfma32(fr[2][dt >> 1], sel, z);
-            const f32x4_t ob = mfma32(fr[3][dt >> 1], sel, z);
-            uint4 qt, ot;
-            qt.x = pack_exact(qa[0], qa[1]); qt.y = pack_exact(qa[2], qa[3]);
-            qt.z = pack_exact(qb[0], qb[1]); qt.w = pack_exact(qb[2], qb[3]);
-            ot.x = pack_exact(oa[0], oa[1]); ot.y = pack_exact(oa[2], oa[3]);
-            ot.z = pack_exact(ob[0], ob[1]); ot.w = pack_exact(ob[2], ob[3]);
-            av[dt] = mfma32(as_bf16x8(ot), pb_, av[dt]);
-            ak[dt] = mfma32(as_bf16x8(qt), db_, ak[dt]);
-            if (dt & 1) __builtin_amdgcn_sched_barrier(0);      // two d-tiles of transposes in flight
+            const uint32_t o = rt0 + 16u * static_cast<uint32_t>((2 * dt + tb) ^ th);
+            const uint2 qa = lds_read_tr16(o), qb = lds_read_tr16(o + 4096u);
+            const uint2 oa = lds_read_tr16(o + 8192u), ob = lds_read_tr16(o + 12288u);
+            // K index 8 lg + e <-> (row e / 4, head 4 lg + e % 4), as in pb_ / db_
+            av[dt] = mfma32(as_bf16x8(make_uint4(oa.x, oa.y, ob.x, ob.y)), pb_, av[dt]);
+            ak[dt] = mfma32(as_bf16x8(make_uint4(qa.x, qa.y, qb.x, qb.y)), db_, ak[dt]);
         }
     };
+
     const int npairs = (n + 1) >> 1;
     for (int p = 0; p < kCStages - 1 && p < npairs; ++p) issue(p);
     for (int p = 0; p < npairs; ++p) {
         const int left = npairs - 1 - p;
         ring_wait(left < kCStages - 2 ? left : kCStages - 2);
         if (p + kCStages - 1 < npairs) issue(p + kCStages - 1);
-        const uint32_t sb = ring0 + static_cast<uint32_t>((p % kCStages) * sizeof(RowTiles));
-        bf16x8_t fr[4][4];
-        f32x4_t ls[4];
-        lds_read_pair(sb + fa[0], sb + fa[1], sb + fa[2], sb + fa[3],
-                      lsd0 + static_cast<uint32_t>((p % kCStages) * (kCThreads / 64) * 64 * sizeof(float)),
-                      fr, ls);
-        int ra, rb;
-        lds_read_ids(ids0 + 8u * p, ra, rb);
-        compute(fr, ra, rb, 2 * p + 1 < n, ls);
+        compute(p);
     }
 
     // ---- epilogue: lane holds dV^T / dK^T[d = 16 dt + 4 lg + r][key 16 w + lc]
