@@ -520,7 +520,7 @@ def bench_varlen_prefill(args, torch, tbs, gh) -> dict:
             "tflops_path": useful / (tm.sum() * 1e-3) / 1e12}
 
 
-BACKWARD_FAMILIES = ("vt_build", "bwd_row", "bwd_index", "bwd_col")
+BACKWARD_FAMILIES = ("bwd_row", "bwd_index", "bwd_col")
 
 
 def bench_backward(args, torch, tbs, gh, pre: dict) -> dict:

@@ -380,7 +380,7 @@ typedef enum infv2_kernel {
     INFV2_KERNEL_ATTN_DECODE = 5,       /* decode: attention over the selected blocks (partials) */
     INFV2_KERNEL_ATTN_MERGE = 6,        /* decode: merge of the partials */
     INFV2_KERNEL_ATTN_PREFILL = 7,      /* prefill: attention over the selected blocks */
-    INFV2_KERNEL_VT_BUILD = 8,          /* prefill: transposed V tiles (K tiles in the backward) */
+    INFV2_KERNEL_VT_BUILD = 8,          /* prefill: transposed V tiles */
     INFV2_KERNEL_APPEND = 9,            /* decode: cache append + incremental compressed key */
     INFV2_KERNEL_BWD_ROW = 10,          /* backward: dq, LogSumExp and dout.out per row */
     INFV2_KERNEL_BWD_INDEX = 11,        /* backward: the rows that selected each block */

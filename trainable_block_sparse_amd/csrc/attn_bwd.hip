@@ -44,8 +44,6 @@ BwdWs bwd_ws(const Shape& sh, int rows, int64_t max_len) {
     w.totals = off;     off += align256(static_cast<size_t>(sh.hkv) * w.nblk * sizeof(int32_t));
     w.col_start = off;  off += align256(static_cast<size_t>(sh.hkv) * (w.nblk + 1) * sizeof(int32_t));
     w.list = off;       off += align256(static_cast<size_t>(sh.hkv) * w.list_ld * sizeof(int32_t));
-    w.kt = off;
-    if (bwd_mfma_ok(sh)) off += align256(bwd_kt_bytes(sh, max_len));
     w.extra = off;
     if (bwd_mfma_ok(sh)) off += bwd_mfma_extra_bytes(sh, w);
     w.total = off;

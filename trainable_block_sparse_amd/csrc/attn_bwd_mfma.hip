@@ -6,8 +6,9 @@
 //
 // Row pass (bwd_row_mfma): like the forward prefill kernel, a thread block owns
 // 16 consecutive rows of one KV head (one row per wave) and streams the union
-// of their selected blocks through LDS (K and V as stored, K^T as transposed
-// tiles).  Per (row, block):
+// of their selected blocks through LDS (K and V as stored; the K^T operand comes
+// from the K tile by transpose reads), two blocks per barrier interval with the
+// next interval's loads in flight.  Per (row, block):
 //   S^T  = K . Q^T          16 MFMA     dP^T = V . dO^T       16 MFMA
 //   dA^T = P^T (dP^T - D), P against a lazily raised reference max
 //   dQ^T += K^T . dA^T      16 MFMA (dA in bf16)
@@ -38,6 +39,7 @@ namespace infv2 {
 constexpr int kRWaves = kUWaves;       // row pass: one row per wave
 constexpr int kRThreads = kUThreads;
 constexpr int kCThreads = 256;         // column pass: 4 waves x 16 keys
+constexpr int kRSlots = 4;             // row pass: two LDS stages of two blocks (32 KB each)
 constexpr int kSeg = 2048;             // rows per column segment
 constexpr int kXcdsB = 8;
 constexpr float kSlackB = 8.f;         // log2 units, as in the forward
@@ -46,9 +48,15 @@ bool bwd_mfma_ok(const Shape& sh) {
     return sh.io_bf16 && sh.m == kPB && kURows * sh.topk <= kUnionCap;
 }
 
-size_t bwd_kt_bytes(const Shape& sh, int64_t max_len) {
-    const int64_t nblk = (max_len + kPB - 1) / kPB;
-    return static_cast<size_t>(sh.hkv) * nblk * kHeadDim * kPB * sizeof(bf16_t);
+// LDS transpose read of 8 bytes per lane: inside each group of 16 lanes, lane i
+// receives as its element e (e = 0..3) halfword i % 4 of the 8 bytes that lane
+// 4 e + i / 4 addresses.
+__device__ __forceinline__ uint2 lds_read_tr16(uint32_t byte_offset) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<lds_s16x4*>(static_cast<uintptr_t>(byte_offset)));
+    return __builtin_bit_cast(uint2, v);
 }
 
 // work items of the column pass: one per (column, segment); upper bound used for
@@ -87,11 +95,11 @@ __device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b) {
 __global__ __launch_bounds__(kRThreads, 1) void bwd_row_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ out, const bf16_t* __restrict__ dout,
     int rows, int64_t q_start, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const bf16_t* __restrict__ kt, const int64_t* __restrict__ kv_off,
+    const int64_t* __restrict__ kv_off,
     const int32_t* __restrict__ idx, bf16_t* __restrict__ dq, float* __restrict__ lse2,
     float* __restrict__ delta, int hq, int hkv, int topk, int64_t nblk, int nrg, float scale_log2,
     float scale) {
-    __shared__ __attribute__((aligned(16))) BlockTile kst[2], vst[2], tst[2];   // two stages of one block
+    __shared__ __attribute__((aligned(16))) BlockTile kst[kRSlots], vst[kRSlots];   // stage x: slots 2 x, 2 x + 1
     __shared__ UnionSmem sm;
     const int lid = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
     const int g = lid / nrg, r0 = (lid % nrg) * kURows;
@@ -101,7 +109,6 @@ __global__ __launch_bounds__(kRThreads, 1) void bwd_row_mfma(
     const size_t hoff = (kv_off[0] * hkv + static_cast<int64_t>(g) * cap) * kHeadDim;
     const bf16_t* kh = k + hoff;
     const bf16_t* vh = v + hoff;
-    const bf16_t* kth = kt + static_cast<int64_t>(g) * nblk * kHeadDim * kPB;
     const int64_t nlim = q_start + rows;
 
     const int n_u = build_union(sm, idx, rows, r0, hkv, g, topk, nblk);
@@ -137,9 +144,7 @@ __global__ __launch_bounds__(kRThreads, 1) void bwd_row_mfma(
     // ---- tile loads: each wave fills 1 KB of each tile (one 16-byte load per lane)
     const int key_l = 4 * w + (l >> 4);                          // keys 4 w .. 4 w + 3
     const int koff_l = key_l * kHeadDim + 8 * ((l & 15) ^ (key_l & 15));
-    const int d_l = 8 * w + (l >> 3);                            // K^T rows 8 w .. 8 w + 7
-    const int toff_l = d_l * kPB + 8 * ((l & 7) ^ ((d_l >> 1) & 7));
-    auto issue = [&](BlockTile& kt_, BlockTile& vt_, BlockTile& tt_, int u) {
+    auto issue = [&](BlockTile& kt_, BlockTile& vt_, int u) {
         const int32_t blk = sm.list[u];
         const int64_t k0 = static_cast<int64_t>(blk) * kPB;
         int64_t off = k0 * kHeadDim + koff_l;
@@ -150,9 +155,15 @@ __global__ __launch_bounds__(kRThreads, 1) void bwd_row_mfma(
         }
         dma16(kh + off, lds_offset(&kt_[w * 512]));
         dma16(vh + off, lds_offset(&vt_[w * 512]));
-        dma16(kth + k0 * kHeadDim + toff_l, lds_offset(&tt_[w * 512]));
     };
-    auto compute = [&](const BlockTile& kt_, const BlockTile& vt_, const BlockTile& tt_, int u) {
+    // K^T operands of dQ^T = K^T dA^T come from the K tile by transpose reads:
+    // for d-tile dt and keys 32 kk + 16 a + 4 lg + 0..3 this lane reads the 4
+    // values d = 16 dt + 4 (lc % 4) .. + 3 of key 32 kk + 16 a + kq, which hands
+    // lane lc element e = K[key 32 kk + 16 a + 4 lg + e][d = 16 dt + lc] -- the
+    // key order of the dA^T operand (the accumulator layout of S^T)
+    const int kq = 4 * lg + (lc >> 2), kqb = (lc >> 1) & 1;
+    const uint32_t kq0 = static_cast<uint32_t>(kq * kHeadDim * 2 + 8 * (lc & 1));
+    auto compute = [&](const BlockTile& kt_, const BlockTile& vt_, int u) {
         const int32_t blk = sm.list[u];
         const int cntr = qpos + 1 - blk * kPB;                   // keys of the block at or before the row
         const bool act = ((sm.mask[u] >> w) & 1u) && row < rows && cntr > 0;
@@ -222,30 +233,30 @@ __global__ __launch_bounds__(kRThreads, 1) void bwd_row_mfma(
             pu.w = pack_rne(s[2 * kk + 1][2], s[2 * kk + 1][3]);
             af[kk] = as_bf16x8(pu);
         }
-        // K^T fragments two d-tiles at a time (bounds the registers in flight)
+        const uint32_t kb0 = lds_offset(&kt_[0]) + kq0;
 #pragma unroll
-        for (int mb = 0; mb < 8; mb += 2) {
-            uint4 tf[2][2];
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                tf[x][0] = vt_frag(tt_, 16 * (mb + x) + lc, lg);
-                tf[x][1] = vt_frag(tt_, 16 * (mb + x) + lc, 4 + lg);
-            }
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                acc[mb + x] = mfma32(as_bf16x8(tf[x][0]), af[0], acc[mb + x]);
-                acc[mb + x] = mfma32(as_bf16x8(tf[x][1]), af[1], acc[mb + x]);
-            }
+        for (int dt = 0; dt < 8; ++dt) {
+            // chunk 2 dt + kqb of key 32 kk + 16 a + kq sits at chunk (2 dt + kqb) ^ kq
+            const uint32_t o = kb0 + 16u * static_cast<uint32_t>((2 * dt + kqb) ^ kq);
+            const uint2 a0 = lds_read_tr16(o), a1 = lds_read_tr16(o + 16u * kHeadDim * 2);
+            const uint2 b0 = lds_read_tr16(o + 32u * kHeadDim * 2), b1 = lds_read_tr16(o + 48u * kHeadDim * 2);
+            acc[dt] = mfma32(as_bf16x8(make_uint4(a0.x, a0.y, a1.x, a1.y)), af[0], acc[dt]);
+            acc[dt] = mfma32(as_bf16x8(make_uint4(b0.x, b0.y, b1.x, b1.y)), af[1], acc[dt]);
         }
     };
-    // one block per barrier interval, double-buffered: block u + 1 loads under
-    // the products of block u
-    if (n_u > 0) issue(kst[0], vst[0], tst[0], 0);
-    for (int u = 0; u < n_u; ++u) {
-        dma_wait_barrier();                  // block u landed; every wave is done with u - 1
-        const int sx = (u + 1) & 1, sc = u & 1;
-        if (u + 1 < n_u) issue(kst[sx], vst[sx], tst[sx], u + 1);
-        compute(kst[sc], vst[sc], tst[sc], u);
+    // two-block barrier intervals, double-buffered: one block of the next
+    // interval's loads is issued before each block of products
+    const int n_iv = (n_u + 1) / 2;
+    for (int x = 0; x < 2 && x < n_u; ++x) issue(kst[x], vst[x], x);
+    for (int iv = 0; iv < n_iv; ++iv) {
+        dma_wait_barrier();
+        const int sx = ((iv + 1) & 1) * 2, sc = (iv & 1) * 2;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int xn = 2 * (iv + 1) + b, u = 2 * iv + b;
+            if (xn < n_u) issue(kst[sx + b], vst[sx + b], xn);
+            if (u < n_u) compute(kst[sc + b], vst[sc + b], u);
+        }
     }
 
     // ---- epilogue: lane holds dQ^T[d = 16 mt + 4 lg + r][head lc]
@@ -307,16 +318,6 @@ __device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
                  : "memory");
 }
 
-// LDS transpose read of 8 bytes per lane: inside each group of 16 lanes, lane i
-// receives as its element e (e = 0..3) halfword i % 4 of the 8 bytes that lane
-// 4 e + i / 4 addresses.
-__device__ __forceinline__ uint2 lds_read_tr16(uint32_t byte_offset) {
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        reinterpret_cast<lds_s16x4*>(static_cast<uintptr_t>(byte_offset)));
-    return __builtin_bit_cast(uint2, v);
-}
 
 // wait until this wave's loads of the current pair have landed (at most `later`
 // further pairs' loads outstanding; loads complete in order), then a barrier
@@ -547,20 +548,18 @@ hipError_t launch_attn_prefill_bwd_mfma(const Shape& sh, const BwdWs& w, const v
     const int64_t nblk = w.nblk;
     float* lse2 = reinterpret_cast<float*>(base + w.lse);
     float* delta = reinterpret_cast<float*>(base + w.delta);
-    bf16_t* kt = reinterpret_cast<bf16_t*>(base + w.kt);
     int32_t* item_start = reinterpret_cast<int32_t*>(base + w.extra);
     const int ncol = sh.hkv * w.nblk;
     float* partial = reinterpret_cast<float*>(base + w.extra + align256(static_cast<size_t>(ncol + 1) * sizeof(int32_t)));
     const float scale_log2 = sh.attn_scale * 1.4426950408889634f;
-    hipError_t e = launch_vt_build(k, kv_off, sh.hkv, n, nblk, kt, st);
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
     {
         KernelTimer tm(INFV2_KERNEL_BWD_ROW, st);
         const int nrg = (rows + kURows - 1) / kURows;
         bwd_row_mfma<<<dim3(static_cast<unsigned>(nrg) * sh.hkv), kRThreads, 0, st>>>(
             static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(out),
             static_cast<const bf16_t*>(dout), rows, q_start, static_cast<const bf16_t*>(k),
-            static_cast<const bf16_t*>(v), kt, kv_off, idx, static_cast<bf16_t*>(dq), lse2, delta,
+            static_cast<const bf16_t*>(v), kv_off, idx, static_cast<bf16_t*>(dq), lse2, delta,
             sh.hq, sh.hkv, sh.topk, nblk, nrg, scale_log2, sh.attn_scale);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }

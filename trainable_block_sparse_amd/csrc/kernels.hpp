@@ -107,13 +107,12 @@ hipError_t launch_attn_prefill(const Shape& sh, const void* q, int rows, int64_t
 
 // backward of the prefill attention (attn_bwd.hip, attn_bwd_mfma.hip)
 struct BwdWs {
-    size_t lse, delta, counts, totals, col_start, list, kt, extra, total;
+    size_t lse, delta, counts, totals, col_start, list, extra, total;
     int nblk, nchunk;
     int64_t list_ld;
 };
 BwdWs bwd_ws(const Shape& sh, int rows, int64_t max_len);
 bool bwd_mfma_ok(const Shape& sh);
-size_t bwd_kt_bytes(const Shape& sh, int64_t max_len);
 size_t bwd_mfma_extra_bytes(const Shape& sh, const BwdWs& w);
 hipError_t launch_inverse_index(const Shape& sh, const BwdWs& w, int rows, const int32_t* idx,
                                 char* base, hipStream_t st);
