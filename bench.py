@@ -379,7 +379,7 @@ def decode_spot_parity(wl, dev, qs, outs, idx, select, attn, ck_dtype, torch, gh
 
 
 # ----------------------------------------------------------------------------- prefill
-PREFILL_FAMILIES = ("compress", "select_prefill", "select_topk", "vt_build", "attn_prefill")
+PREFILL_FAMILIES = ("compress", "select_prefill", "select_topk", "attn_prefill")
 
 
 def bench_prefill(args, torch, tbs, gh) -> dict:

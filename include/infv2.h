@@ -269,9 +269,8 @@ int32_t infv2_sparse_attn_decode(const infv2_config* cfg, const void* q, const v
  *   kv_offsets   device int64 [2]
  *   block_idx    device int32 [rows][Hkv][topk]
  *   out          device, io_dtype [rows][Hq][d] (written)
- *   ws           workspace (op = ATTN_PREFILL: the V^T tiles of the prefix, rebuilt
- *                by every call; 0 bytes, and NULL allowed, when the vector-ALU
- *                path serves the config); no initial contents are needed
+ *   ws           workspace (op = ATTN_PREFILL); infv2_workspace_bytes returns 0
+ *                for this op, so NULL is allowed; kept for ABI stability
  */
 int32_t infv2_sparse_attn_prefill(const infv2_config* cfg, const void* q, int32_t rows,
                                   int64_t q_start, const void* k, const void* v,
@@ -380,7 +379,7 @@ typedef enum infv2_kernel {
     INFV2_KERNEL_ATTN_DECODE = 5,       /* decode: attention over the selected blocks (partials) */
     INFV2_KERNEL_ATTN_MERGE = 6,        /* decode: merge of the partials */
     INFV2_KERNEL_ATTN_PREFILL = 7,      /* prefill: attention over the selected blocks */
-    INFV2_KERNEL_VT_BUILD = 8,          /* prefill: transposed V tiles */
+    INFV2_KERNEL_VT_BUILD = 8,          /* reserved: no kernel is timed under this id */
     INFV2_KERNEL_APPEND = 9,            /* decode: cache append + incremental compressed key */
     INFV2_KERNEL_BWD_ROW = 10,          /* backward: dq, LogSumExp and dout.out per row */
     INFV2_KERNEL_BWD_INDEX = 11,        /* backward: the rows that selected each block */

@@ -48,17 +48,6 @@ bool bwd_mfma_ok(const Shape& sh) {
     return sh.io_bf16 && sh.m == kPB && kURows * sh.topk <= kUnionCap;
 }
 
-// LDS transpose read of 8 bytes per lane: inside each group of 16 lanes, lane i
-// receives as its element e (e = 0..3) halfword i % 4 of the 8 bytes that lane
-// 4 e + i / 4 addresses.
-__device__ __forceinline__ uint2 lds_read_tr16(uint32_t byte_offset) {
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        reinterpret_cast<lds_s16x4*>(static_cast<uintptr_t>(byte_offset)));
-    return __builtin_bit_cast(uint2, v);
-}
-
 // work items of the column pass: one per (column, segment); upper bound used for
 // the grid and the partial buffers
 static int64_t max_col_items(const Shape& sh, const BwdWs& w) {

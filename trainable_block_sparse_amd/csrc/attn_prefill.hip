@@ -9,8 +9,9 @@
 // KV head, one row per wave (16 waves, four per SIMD, so that the latency of
 // one wave's dependent MFMA / softmax chain hides behind the others).  The
 // block builds the union of the rows' selected blocks and streams it through
-// LDS with direct global->LDS loads (K as stored, V as V^T tiles built by
-// vt_build), four blocks per barrier interval.
+// LDS with direct global->LDS loads (K and V as stored; the V^T operand comes
+// from the V tile by transpose reads), two blocks per barrier interval with the
+// next interval's loads in flight under the current one's products.
 // For each block the waves whose row selected it run:
 //   S^T[key][head] = K_blk . Q_row^T          16 MFMA 16x16x32
 //   O^T[d][head]  += V^T_blk . P_row^T        16 MFMA 16x16x32
@@ -40,41 +41,11 @@ constexpr int kGroup2 = 2;       // union blocks per LDS stage; two stages = one
 constexpr int kXcds = 8;         // thread blocks are dealt round-robin to the 8 XCDs
 constexpr float kRescaleSlack = 8.f;   // log2 units
 
-// vt[g][blk][d][pos] = V[g][blk*64 + key(pos)][d]; keys at or past n read as zero.
-__global__ __launch_bounds__(256) void vt_build(const bf16_t* __restrict__ v,
-                                                const int64_t* __restrict__ kv_off, int hkv,
-                                                int64_t n, int64_t nblk, bf16_t* __restrict__ vt) {
-    __shared__ bf16_t tile[kPB][kHeadDim + 8];
-    const int blk = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
-    const int64_t cap = kv_off[1] - kv_off[0];
-    const bf16_t* vh = v + (kv_off[0] * hkv + static_cast<int64_t>(g) * cap) * kHeadDim;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int e = t + 256 * i, row = e >> 4, c = e & 15;
-        const int64_t key = static_cast<int64_t>(blk) * kPB + row;
-        uint4 val = make_uint4(0u, 0u, 0u, 0u);
-        if (key < n) val = ldg16(vh + key * kHeadDim + 8 * c);
-        *reinterpret_cast<uint4*>(&tile[row][8 * c]) = val;
-    }
-    __syncthreads();
-    bf16_t* dst = vt + ((static_cast<int64_t>(g) * nblk + blk) * kHeadDim) * kPB;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int e = t + 256 * i, d = e >> 3, p0 = (e & 7) * 8;
-        uint32_t w[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            w[j] = static_cast<uint32_t>(tile[vt_key_of_pos(p0 + 2 * j)][d]) |
-                   (static_cast<uint32_t>(tile[vt_key_of_pos(p0 + 2 * j + 1)][d]) << 16);
-        *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(d) * kPB + p0) = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-}
-
 typedef BlockTile StageTiles[kGroup2];              // 2 x 16 KB (K) or 2 x 16 KB (V^T)
 
 __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
     const bf16_t* __restrict__ q, int rows, int64_t q_start, const bf16_t* __restrict__ k,
-    const bf16_t* __restrict__ vt, const int64_t* __restrict__ kv_off,
+    const bf16_t* __restrict__ v, const int64_t* __restrict__ kv_off,
     const int32_t* __restrict__ idx, bf16_t* __restrict__ out, int hq, int hkv, int topk,
     int64_t nblk, int nrg, float scale_log2) {
     __shared__ __attribute__((aligned(16))) StageTiles kst[2], vst[2];   // two stages
@@ -90,7 +61,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
     const int w = t >> 6, l = t & 63, lg = l >> 4, lc = l & 15;
     const int64_t cap = kv_off[1] - kv_off[0];
     const bf16_t* kh = k + (kv_off[0] * hkv + static_cast<int64_t>(g) * cap) * kHeadDim;
-    const bf16_t* vth = vt + static_cast<int64_t>(g) * nblk * kHeadDim * kPB;
+    const bf16_t* vh = v + (kv_off[0] * hkv + static_cast<int64_t>(g) * cap) * kHeadDim;
     const int64_t nlim = q_start + rows;                     // keys needed are < nlim
 
     // ---- union of the 16 rows' selected blocks (ascending list + row masks)
@@ -124,18 +95,16 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
         for (int ks = 0; ks < 4; ++ks) asm volatile("" :: "v"(qf[i][ks]));
 
     // ---- stream the union through LDS with direct global->LDS loads.  Each
-    // wave fills 2 KB of each K and V^T tile (2 instructions each); the lane part
-    // of the address is fixed, only the block part (wave-uniform) changes.
-    int koff_l[kTileLoads], voff_l[kTileLoads], key_l[kTileLoads];
+    // wave fills 1 KB of each K and V tile; the lane part of the address is
+    // fixed, only the block part (wave-uniform) changes.
+    int koff_l[kTileLoads], key_l[kTileLoads];
 #pragma unroll
     for (int j = 0; j < kTileLoads; ++j) {
         const int sg = kTileLoads * w + j;
         key_l[j] = 4 * sg + (l >> 4);                       // keys 4 sg .. 4 sg + 3
         koff_l[j] = key_l[j] * kHeadDim + 8 * ((l & 15) ^ (key_l[j] & 15));
-        const int d = 8 * sg + (l >> 3);                    // V^T rows 8 sg .. 8 sg + 7
-        voff_l[j] = d * kPB + 8 * ((l & 7) ^ ((d >> 1) & 7));
     }
-    auto issue = [&](StageTiles& kt, StageTiles& vtt, int u) {
+    auto issue = [&](StageTiles& kt, StageTiles& vs, int u) {
         const int slot = u % kGroup2;
         const int32_t blk = sm.list[u];
         const int64_t k0 = static_cast<int64_t>(blk) * kPB;
@@ -143,17 +112,24 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
 #pragma unroll
         for (int j = 0; j < kTileLoads; ++j) {
             const int sg = kTileLoads * w + j;
-            const bf16_t* ksrc = kh + k0 * kHeadDim + koff_l[j];
-            if (partial) {                                  // clamp: keys past the chunk are masked anyway
+            int64_t off = k0 * kHeadDim + koff_l[j];
+            if (partial) {                                  // clamp: keys past the chunk get P = 0
                 int64_t gk = k0 + key_l[j];
                 gk = gk < nlim ? gk : nlim - 1;
-                ksrc = kh + gk * kHeadDim + 8 * ((l & 15) ^ (key_l[j] & 15));
+                off = gk * kHeadDim + 8 * ((l & 15) ^ (key_l[j] & 15));
             }
-            dma16(ksrc, lds_offset(&kt[slot][sg * 512]));
-            dma16(vth + k0 * kHeadDim + voff_l[j], lds_offset(&vtt[slot][sg * 512]));
+            dma16(kh + off, lds_offset(&kt[slot][sg * 512]));
+            dma16(vh + off, lds_offset(&vs[slot][sg * 512]));
         }
     };
-    auto compute = [&](const StageTiles& kt, const StageTiles& vtt, int u) {
+    // V^T operands of O^T = V^T P^T come from the V tile by transpose reads:
+    // for d-tile mt and keys 32 kk + 16 a + 4 lg + 0..3 this lane reads the 4
+    // values d = 16 mt + 4 (lc % 4) .. + 3 of key 32 kk + 16 a + kq, which hands
+    // lane lc element e = V[key 32 kk + 16 a + 4 lg + e][d = 16 mt + lc] -- the
+    // key order of the P^T operand (the accumulator layout of S^T)
+    const int kq = 4 * lg + (lc >> 2), kqb = (lc >> 1) & 1;
+    const uint32_t kq0 = static_cast<uint32_t>(kq * kHeadDim * 2 + 8 * (lc & 1));
+    auto compute = [&](const StageTiles& kt, const StageTiles& vs, int u) {
         const int slot = u % kGroup2;
         const int32_t blk = sm.list[u];
         const uint32_t msk = sm.mask[u];
@@ -246,13 +222,18 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
             }
         }
         // V^T fragments, kVBatch d-tiles at a time
+        const uint32_t vb0 = lds_offset(&vs[slot][0]) + kq0;
 #pragma unroll
         for (int mb = 0; mb < 8; mb += kVBatch) {
             uint4 vf[kVBatch][2];
 #pragma unroll
             for (int x = 0; x < kVBatch; ++x) {
-                vf[x][0] = vt_frag(vtt[slot], 16 * (mb + x) + lc, lg);
-                vf[x][1] = vt_frag(vtt[slot], 16 * (mb + x) + lc, 4 + lg);
+                // chunk 2 mt + kqb of key 32 kk + 16 a + kq sits at chunk (2 mt + kqb) ^ kq
+                const uint32_t o = vb0 + 16u * static_cast<uint32_t>((2 * (mb + x) + kqb) ^ kq);
+                const uint2 a0 = lds_read_tr16(o), a1 = lds_read_tr16(o + 16u * kHeadDim * 2);
+                const uint2 b0 = lds_read_tr16(o + 32u * kHeadDim * 2), b1 = lds_read_tr16(o + 48u * kHeadDim * 2);
+                vf[x][0] = make_uint4(a0.x, a0.y, a1.x, a1.y);
+                vf[x][1] = make_uint4(b0.x, b0.y, b1.x, b1.y);
             }
 #pragma unroll
             for (int x = 0; x < kVBatch; ++x)
@@ -264,11 +245,8 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
                 }
         }
     };
-    // Four blocks per barrier interval: load them (both stages), wait, then
-    // compute.  Loads and compute do not overlap, but each interval holds twice
-    // the work of a double-buffered pair of two-block stages, which evens out
-    // the random share of active (row, block) pairs between the SIMDs; the
-    // wait at each barrier is set by the busiest SIMD, not by the load.
+    // Two-block barrier intervals, double-buffered: the loads of interval iv + 1
+    // run under the products of interval iv.
     const int n_iv = (n_u + kGroup2 - 1) / kGroup2;
     for (int x = 0; x < kGroup2 && x < n_u; ++x) issue(kst[0], vst[0], x);
     for (int iv = 0; iv < n_iv; ++iv) {
@@ -305,37 +283,24 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
     }
 }
 
-hipError_t launch_vt_build(const void* src, const int64_t* kv_off, int hkv, int64_t n,
-                           int64_t nblk, void* dst, hipStream_t st) {
-    KernelTimer kt(INFV2_KERNEL_VT_BUILD, st);
-    vt_build<<<dim3(static_cast<unsigned>(nblk), hkv), 256, 0, st>>>(
-        static_cast<const bf16_t*>(src), kv_off, hkv, n, nblk, static_cast<bf16_t*>(dst));
-    return hipGetLastError();
-}
-
 bool attn_prefill_mfma_ok(const Shape& sh) {
     return sh.io_bf16 && sh.m == kPB && kPRows * sh.topk <= kUnionCap;
 }
 
-size_t attn_prefill_ws_bytes(const Shape& sh, int64_t max_len) {
-    if (!attn_prefill_mfma_ok(sh)) return 0;
-    const int64_t nblk = (max_len + kPB - 1) / kPB;
-    return align256(static_cast<size_t>(sh.hkv) * nblk * kHeadDim * kPB * sizeof(bf16_t));
-}
+size_t attn_prefill_ws_bytes(const Shape&, int64_t) { return 0; }   // no workspace
 
 hipError_t launch_attn_prefill_mfma(const Shape& sh, const void* q, int rows, int64_t q_start,
                                     const void* k, const void* v, const int64_t* kv_off,
                                     const int32_t* idx, void* out, void* ws, hipStream_t st) {
     const int64_t n = q_start + rows;
     const int64_t nblk = (n + kPB - 1) / kPB;
-    bf16_t* vt = static_cast<bf16_t*>(ws);
-    hipError_t e = launch_vt_build(v, kv_off, sh.hkv, n, nblk, vt, st);
-    if (e != hipSuccess) return e;
+    (void)ws;
     const float scale_log2 = sh.attn_scale * 1.4426950408889634f;
     KernelTimer kt(INFV2_KERNEL_ATTN_PREFILL, st);
     const int nrg = (rows + kPRows - 1) / kPRows;
     attn_prefill_mfma<<<dim3(static_cast<unsigned>(nrg) * sh.hkv), kPThreads, 0, st>>>(
-        static_cast<const bf16_t*>(q), rows, q_start, static_cast<const bf16_t*>(k), vt, kv_off,
+        static_cast<const bf16_t*>(q), rows, q_start, static_cast<const bf16_t*>(k),
+        static_cast<const bf16_t*>(v), kv_off,
         idx, static_cast<bf16_t*>(out), sh.hq, sh.hkv, sh.topk, nblk, nrg, scale_log2);
     return hipGetLastError();
 }

@@ -94,8 +94,6 @@ hipError_t launch_attn_decode_merge(const Shape& sh, const float* part_o, const 
 
 bool attn_prefill_mfma_ok(const Shape& sh);
 // transposed 64-key tiles of K or V for the matrix-core prefill kernels
-hipError_t launch_vt_build(const void* src, const int64_t* kv_off, int hkv, int64_t n,
-                           int64_t nblk, void* dst, hipStream_t st);
 size_t attn_prefill_ws_bytes(const Shape& sh, int64_t max_len);
 hipError_t launch_attn_prefill_mfma(const Shape& sh, const void* q, int rows, int64_t q_start,
                                     const void* k, const void* v, const int64_t* kv_off,

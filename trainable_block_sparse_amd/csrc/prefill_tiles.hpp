@@ -88,30 +88,29 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
     asm volatile("global_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
                  : "memory");
 }
+// LDS transpose read of 8 bytes per lane: inside each group of 16 lanes, lane i
+// receives as its element e (e = 0..3) halfword i % 4 of the 8 bytes that lane
+// 4 e + i / 4 addresses.
+__device__ __forceinline__ uint2 lds_read_tr16(uint32_t byte_offset) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<lds_s16x4*>(static_cast<uintptr_t>(byte_offset)));
+    return __builtin_bit_cast(uint2, v);
+}
+
 // wait for every outstanding global load of this wave, then a block barrier
 __device__ __forceinline__ void dma_wait_barrier() {
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// K tile: 64 keys x 16 chunks of 16 B; chunk c of key r sits at c ^ (r & 15).
-// Transposed tile (V^T, K^T): 128 d x 8 chunks of 16 B; chunk c of row d sits at
-// c ^ ((d >> 1) & 7).  Both swizzles make 16-lane 16-byte column reads conflict-free.
+// K / V tile: 64 keys x 16 chunks of 16 B; chunk c of key r sits at c ^ (r & 15),
+// which makes 16-lane 16-byte column reads conflict-free.  Transposed operands
+// (d along M, keys along K) are read from the same tile with lds_read_tr16.
 typedef bf16_t BlockTile[kPB * kHeadDim];            // 16 KB
 
 __device__ __forceinline__ uint4 k_frag(const BlockTile& t, int key, int chunk) {
     return *reinterpret_cast<const uint4*>(&t[key * kHeadDim + 8 * (chunk ^ (key & 15))]);
-}
-__device__ __forceinline__ uint4 vt_frag(const BlockTile& t, int d, int chunk) {
-    return *reinterpret_cast<const uint4*>(&t[d * kPB + 8 * (chunk ^ ((d >> 1) & 7))]);
-}
-
-// Transposed tiles store the 64 keys of a block in the order the P^T operand of
-// a 16x16x32 product over keys uses (the accumulator layout of S^T = K Q^T, two
-// 16-key tiles per K-step): position 32 kk + 8 g + 4 a + r holds key
-// 32 kk + 16 a + 4 g + r.
-__device__ __forceinline__ int vt_key_of_pos(int pos) {
-    const int kk = pos >> 5, w = pos & 31, g = w >> 3, a = (w >> 2) & 1, r = w & 3;
-    return 32 * kk + 16 * a + 4 * g + r;
 }
 
 // Streaming order of the union that spreads each barrier interval's work over
