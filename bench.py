@@ -106,9 +106,15 @@ KERNEL_SOURCE = {"attn_decode": "attn_decode.hip", "select_logits": "select.hip"
 
 
 def source_digest(kernel: str) -> str:
+    """SHA-256 over the kernel's source file and every shared header of csrc/."""
+    import glob
     import hashlib
-    path = os.path.join(ROOT, "trainable_block_sparse_amd", "csrc", KERNEL_SOURCE[kernel])
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+    csrc = os.path.join(ROOT, "trainable_block_sparse_amd", "csrc")
+    h = hashlib.sha256()
+    for path in [os.path.join(csrc, KERNEL_SOURCE[kernel])] + sorted(glob.glob(os.path.join(csrc, "*.hpp"))):
+        h.update(os.path.basename(path).encode())
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(kernel: str):
