@@ -593,7 +593,9 @@ __global__ __launch_bounds__(256) void sel_pre_mfma(
     int64_t nblk_max, float* __restrict__ lse, uint32_t* __restrict__ keys) {
     __shared__ __attribute__((aligned(16))) bf16_t ck_hi[kPreTileK * kHeadDim];
     __shared__ __attribute__((aligned(16))) bf16_t ck_lo[kCkBf16 ? 8 : kPreTileK * kHeadDim];
-    __shared__ float rs[kPreRowsG][kPreTileK];
+    __shared__ float rs[kPreRowsG][kPreTileK + 1];   // +1: column reads across rows conflict-free
+    __shared__ int32_t vrow[kPreRowsG];              // kernels visible to each row
+    __shared__ int32_t bk[256][2];                   // pass 2: tile-relative kernel range per block
     const int g = blockIdx.y, t = threadIdx.x;
     const int w = t >> 6, l = t & 63, lg = l >> 4, lc = l & 15;
     const int r0 = blockIdx.x * kPreRowsG;
@@ -620,6 +622,11 @@ __global__ __launch_bounds__(256) void sel_pre_mfma(
         const bf16_t* qrow = q + (static_cast<size_t>(rr) * hq + static_cast<size_t>(g) * kGroup + lc) * kHeadDim;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) qf[i][ks] = as_bf16x8(ldg16(qrow + 32 * ks + 8 * lg));
+    }
+    if (t < kPreRowsG) {
+        const int row = r0 + t;
+        int64_t v = row < rows ? num_kernels(q_start + row + 1, p, s) : 0;
+        vrow[t] = static_cast<int32_t>(v < ccap ? v : ccap);
     }
     if (kPass == 1) {
         // pass 1 owns clearing the block-score keys of its rows
@@ -753,24 +760,39 @@ __global__ __launch_bounds__(256) void sel_pre_mfma(
         }
         if (kPass == 2) {
             __syncthreads();
-            // block max over this tile's kernels, one (row, block) per thread
-            const int64_t jhi_t = (j0 + kPreTileK < vmax ? j0 + kPreTileK : vmax) - 1;
-            const int64_t blo = (j0 * s) / m, bhi = (jhi_t * s + p - 1) / m;
-            const int nbt = static_cast<int>(bhi - blo + 1);
-            for (int e = t; e < kPreRowsG * nbt; e += 256) {
-                const int rr = e / nbt, row = r0 + rr;
-                if (row >= rows) continue;
-                const int64_t blk = blo + e % nbt;
-                int64_t v = num_kernels(q_start + row + 1, p, s);
-                v = v < ccap ? v : ccap;
-                int64_t k0 = first_kernel_of_block(blk, m, p, s), k1 = last_kernel_of_block(blk, m, s);
-                k0 = k0 > j0 ? k0 : j0;
-                const int64_t jhi = (jhi_t < v - 1) ? jhi_t : v - 1;
-                k1 = k1 < jhi ? k1 : jhi;
-                if (k0 > k1) continue;
-                float mx = rs[rr][k0 - j0];
-                for (int64_t kk = k0 + 1; kk <= k1; ++kk) mx = fmaxf(mx, rs[rr][kk - j0]);
-                atomicMax(&keys[(static_cast<size_t>(row) * hkv + g) * nblk_max + blk], score_to_key(mx));
+            // block max over this tile's kernels.  Each block's kernel range
+            // (relative to the tile) is computed once, then one (row, block)
+            // per thread, rows fastest.  32-bit arithmetic: kernel and block
+            // counts are below 2^31.
+            const int j0i = static_cast<int>(j0);
+            const int jhi_t = static_cast<int>((j0 + kPreTileK < vmax ? j0 + kPreTileK : vmax) - 1);
+            const int blo = (j0i * s) / m, bhi = (jhi_t * s + p - 1) / m;
+            for (int b0 = blo; b0 <= bhi; b0 += 256) {
+                const int nb = (bhi - b0 + 1) < 256 ? (bhi - b0 + 1) : 256;
+                if (t < nb) {
+                    const int blk = b0 + t;
+                    int k0 = blk * m - p;                          // first kernel: floor((blk m - p) / s) + 1, >= 0
+                    k0 = (k0 >= 0 ? k0 / s : -((-k0 + s - 1) / s)) + 1;
+                    k0 = k0 > j0i ? k0 : j0i;
+                    int k1 = ((blk + 1) * m - 1) / s;              // last kernel
+                    k1 = k1 < jhi_t ? k1 : jhi_t;
+                    bk[t][0] = k0 - j0i;
+                    bk[t][1] = k1 - j0i;
+                }
+                __syncthreads();
+                for (int e = t; e < kPreRowsG * nb; e += 256) {
+                    const int rr = e & (kPreRowsG - 1), b = e / kPreRowsG, row = r0 + rr;
+                    if (row >= rows) continue;
+                    const int k0 = bk[b][0];
+                    int k1 = bk[b][1];
+                    const int kv = vrow[rr] - 1 - j0i;            // last kernel the row sees
+                    k1 = k1 < kv ? k1 : kv;
+                    if (k0 > k1) continue;
+                    float mx = rs[rr][k0];
+                    for (int kk = k0 + 1; kk <= k1; ++kk) mx = fmaxf(mx, rs[rr][kk]);
+                    atomicMax(&keys[(static_cast<size_t>(row) * hkv + g) * nblk_max + b0 + b], score_to_key(mx));
+                }
+                __syncthreads();
             }
         }
     }
