@@ -574,7 +574,7 @@ __global__ __launch_bounds__(256) void sel_pre_scores(
 }
 
 // ------------------------------------------------------------------ prefill passes on the matrix cores
-// Thread block = 16 query rows of one KV head (wave w: rows w, w+4, w+8, w+12),
+// Thread block = 16 query rows of one KV head (8 waves, wave w: rows w, w + 8),
 // streaming the compressed keys in tiles of 64 kernels through LDS (bf16; fp32
 // keys split into hi + lo tiles at staging).  Z[head][kernel] = Q . CK^T with Q
 // as the A operand (lane: head lc, 8 consecutive d) and the CK tile as B, so
@@ -585,9 +585,13 @@ __global__ __launch_bounds__(256) void sel_pre_scores(
 //           adds; block max of R over the tile, atomicMax into the row's keys
 constexpr int kPreRowsG = 16;
 constexpr int kPreTileK = 64;
+constexpr int kPreWaves = 8;                          // wave w: rows w + 8 i
+constexpr int kPreRW = kPreRowsG / kPreWaves;         // query rows per wave
+constexpr int kPreThreads = kPreWaves * 64;
+constexpr int kPreLoads = kPreTileK * 16 / kPreThreads;   // 16-byte chunks per thread and tile
 
 template <int kPass, bool kCkBf16>
-__global__ __launch_bounds__(256) void sel_pre_mfma(
+__global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
     const bf16_t* __restrict__ q, int rows, int64_t q_start, const void* __restrict__ ck,
     const int64_t* __restrict__ ck_off, int hq, int hkv, int m, int p, int s, float score_scale,
     int64_t nblk_max, float* __restrict__ lse, uint32_t* __restrict__ keys) {
@@ -595,7 +599,7 @@ __global__ __launch_bounds__(256) void sel_pre_mfma(
     __shared__ __attribute__((aligned(16))) bf16_t ck_lo[kCkBf16 ? 8 : kPreTileK * kHeadDim];
     __shared__ float rs[kPreRowsG][kPreTileK + 1];   // +1: column reads across rows conflict-free
     __shared__ int32_t vrow[kPreRowsG];              // kernels visible to each row
-    __shared__ int32_t bk[256][2];                   // pass 2: tile-relative kernel range per block
+    __shared__ int32_t bk[kPreThreads][2];                   // pass 2: tile-relative kernel range per block
     const int g = blockIdx.y, t = threadIdx.x;
     const int w = t >> 6, l = t & 63, lg = l >> 4, lc = l & 15;
     const int r0 = blockIdx.x * kPreRowsG;
@@ -604,8 +608,8 @@ __global__ __launch_bounds__(256) void sel_pre_mfma(
     constexpr float kLog2e = 1.4426950408889634f;
     const float zscale = score_scale * kLog2e;
 
-    int64_t vis[4];
-    bf16x8_t qf[4][4];
+    int64_t vis[kPreRW];
+    bf16x8_t qf[kPreRW][4];
     int64_t vmax = 0;
     for (int rr = 0; rr < kPreRowsG; ++rr) {
         const int row = r0 + rr;
@@ -614,8 +618,8 @@ __global__ __launch_bounds__(256) void sel_pre_mfma(
         vmax = v > vmax ? v : vmax;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = r0 + w + 4 * i;
+    for (int i = 0; i < kPreRW; ++i) {
+        const int row = r0 + w + kPreWaves * i;
         int64_t v = row < rows ? num_kernels(q_start + row + 1, p, s) : 0;
         vis[i] = v < ccap ? v : ccap;
         const int rr = row < rows ? row : rows - 1;
@@ -634,19 +638,19 @@ __global__ __launch_bounds__(256) void sel_pre_mfma(
             const int row = r0 + rr;
             if (row >= rows) break;
             uint32_t* kb = keys + (static_cast<size_t>(row) * hkv + g) * nblk_max;
-            for (int64_t jb = t; jb < nblk_max; jb += 256) kb[jb] = 0u;
+            for (int64_t jb = t; jb < nblk_max; jb += kPreThreads) kb[jb] = 0u;
         }
     }
     // pass 1 state: running (max, sum) for heads 4 lg + r; pass 2: LSE2 of those heads
-    float mr[4][4], lr[4][4];
+    float mr[kPreRW][4], lr[kPreRW][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kPreRW; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) { mr[i][r] = -INFINITY; lr[i][r] = 0.f; }
     if (kPass == 2) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = r0 + w + 4 * i;
+        for (int i = 0; i < kPreRW; ++i) {
+            const int row = r0 + w + kPreWaves * i;
             const int rr = row < rows ? row : rows - 1;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -656,12 +660,12 @@ __global__ __launch_bounds__(256) void sel_pre_mfma(
 
     // compressed-key tile loads run one tile ahead, in registers: the loads of
     // tile t+1 are in flight while tile t is computed from LDS
-    uint4 pk[4];                  // bf16 keys: one 16-byte chunk per x
-    float4 pa[4], pb[4];          // fp32 keys: two 16-byte halves per x
+    uint4 pk[kPreLoads];                  // bf16 keys: one 16-byte chunk per x
+    float4 pa[kPreLoads], pb[kPreLoads];          // fp32 keys: two 16-byte halves per x
     auto fetch = [&](int64_t jt) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int e = t + 256 * x, r = e >> 4, c = e & 15;
+        for (int x = 0; x < kPreLoads; ++x) {
+            const int e = t + kPreThreads * x, r = e >> 4, c = e & 15;
             if (kCkBf16) {
                 const bf16_t* src = static_cast<const bf16_t*>(ck) + cbase;
                 pk[x] = (jt + r < vmax) ? ldg16(src + (jt + r) * kHeadDim + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
@@ -681,8 +685,8 @@ __global__ __launch_bounds__(256) void sel_pre_mfma(
         __syncthreads();
         // stage 64 kernels; chunk c of kernel r at c ^ (r & 15)
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int e = t + 256 * x, r = e >> 4, c = e & 15;
+        for (int x = 0; x < kPreLoads; ++x) {
+            const int e = t + kPreThreads * x, r = e >> 4, c = e & 15;
             const int off = r * kHeadDim + 8 * (c ^ (r & 15));
             if (kCkBf16) {
                 *reinterpret_cast<uint4*>(&ck_hi[off]) = pk[x];
@@ -704,25 +708,25 @@ __global__ __launch_bounds__(256) void sel_pre_mfma(
         if (j0 + kPreTileK < vmax) fetch(j0 + kPreTileK);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-            f32x4_t z[4];
+            f32x4_t z[kPreRW];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) z[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < kPreRW; ++i) z[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             const int kr = 16 * nt + lc;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int off = kr * kHeadDim + 8 * ((4 * ks + lg) ^ (kr & 15));
                 const bf16x8_t bh = as_bf16x8(*reinterpret_cast<const uint4*>(&ck_hi[off]));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) z[i] = mfma32(qf[i][ks], bh, z[i]);
+                for (int i = 0; i < kPreRW; ++i) z[i] = mfma32(qf[i][ks], bh, z[i]);
                 if (!kCkBf16) {
                     const bf16x8_t bl = as_bf16x8(*reinterpret_cast<const uint4*>(&ck_lo[off]));
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) z[i] = mfma32(qf[i][ks], bl, z[i]);
+                    for (int i = 0; i < kPreRW; ++i) z[i] = mfma32(qf[i][ks], bl, z[i]);
                 }
             }
             const int64_t jk = j0 + kr;          // this lane's kernel column
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < kPreRW; ++i) {
                 const bool ok = jk < vis[i];
                 if (kPass == 1) {
                     // running (max, sum) with a lazy max: the reference moves only
@@ -754,7 +758,7 @@ __global__ __launch_bounds__(256) void sel_pre_mfma(
                     for (int r = 0; r < 4; ++r) acc += fast_exp2(z[i][r] * zscale - mr[i][r]);
                     acc += __shfl_xor(acc, 16, 64);
                     acc += __shfl_xor(acc, 32, 64);
-                    if (lg == 0) rs[w + 4 * i][kr] = ok ? acc * (1.0f / kGroup) : -INFINITY;
+                    if (lg == 0) rs[w + kPreWaves * i][kr] = ok ? acc * (1.0f / kGroup) : -INFINITY;
                 }
             }
         }
@@ -767,8 +771,8 @@ __global__ __launch_bounds__(256) void sel_pre_mfma(
             const int j0i = static_cast<int>(j0);
             const int jhi_t = static_cast<int>((j0 + kPreTileK < vmax ? j0 + kPreTileK : vmax) - 1);
             const int blo = (j0i * s) / m, bhi = (jhi_t * s + p - 1) / m;
-            for (int b0 = blo; b0 <= bhi; b0 += 256) {
-                const int nb = (bhi - b0 + 1) < 256 ? (bhi - b0 + 1) : 256;
+            for (int b0 = blo; b0 <= bhi; b0 += kPreThreads) {
+                const int nb = (bhi - b0 + 1) < kPreThreads ? (bhi - b0 + 1) : kPreThreads;
                 if (t < nb) {
                     const int blk = b0 + t;
                     int k0 = blk * m - p;                          // first kernel: floor((blk m - p) / s) + 1, >= 0
@@ -780,7 +784,7 @@ __global__ __launch_bounds__(256) void sel_pre_mfma(
                     bk[t][1] = k1 - j0i;
                 }
                 __syncthreads();
-                for (int e = t; e < kPreRowsG * nb; e += 256) {
+                for (int e = t; e < kPreRowsG * nb; e += kPreThreads) {
                     const int rr = e & (kPreRowsG - 1), b = e / kPreRowsG, row = r0 + rr;
                     if (row >= rows) continue;
                     const int k0 = bk[b][0];
@@ -799,8 +803,8 @@ __global__ __launch_bounds__(256) void sel_pre_mfma(
     if (kPass == 1) {
         // fold the 16 kernel columns: lanes with equal lg hold the same heads
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = r0 + w + 4 * i;
+        for (int i = 0; i < kPreRW; ++i) {
+            const int row = r0 + w + kPreWaves * i;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float mx = mr[i][r];
@@ -1016,7 +1020,7 @@ static void pre_pass1(const Shape& sh, const void* q, int r0, int nr, int64_t q_
     KernelTimer kt(INFV2_KERNEL_SELECT_PREFILL, st);
     if (sizeof(Tq) == 2) {
         dim3 gm((nr + kPreRowsG - 1) / kPreRowsG, sh.hkv);
-        sel_pre_mfma<1, sizeof(Tck) == 2><<<gm, 256, 0, st>>>(
+        sel_pre_mfma<1, sizeof(Tck) == 2><<<gm, kPreThreads, 0, st>>>(
             static_cast<const bf16_t*>(q) + r0 * qrow, nr, q_start + r0, ck, ck_off, sh.hq, sh.hkv,
             sh.m, p, s, sh.score_scale, w.nblk_max, l, kb);
     } else {
@@ -1052,7 +1056,7 @@ static void pre_launch(const Shape& sh, const void* q, int rows, int64_t q_start
         const bf16_t* qq = static_cast<const bf16_t*>(q);
         {
             KernelTimer kt(INFV2_KERNEL_SELECT_PREFILL, st);
-            sel_pre_mfma<2, kB><<<gm, 256, 0, st>>>(qq, rows, q_start, ck, ck_off, sh.hq, sh.hkv,
+            sel_pre_mfma<2, kB><<<gm, kPreThreads, 0, st>>>(qq, rows, q_start, ck, ck_off, sh.hq, sh.hkv,
                                                     sh.m, sh.p, sh.s, sh.score_scale, w.nblk_max,
                                                     lse, keys);
         }
