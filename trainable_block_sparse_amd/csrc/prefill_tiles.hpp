@@ -15,31 +15,36 @@ constexpr int kUThreads = kUWaves * 64;
 constexpr int kUMaxWords = 512;   // bitmap words: up to 16384 blocks
 constexpr int kUnionCap = 2048;   // union entries: 16 rows x top-k, top-k <= 128
 
-struct UnionSmem {
-    int32_t list[kUnionCap];          // union of the rows' blocks, ascending (<= 16 * topk)
-    uint32_t mask[kUnionCap];         // which of the 16 rows selected each union block
-    uint16_t order[kUnionCap];        // balance_union scratch: the streaming order
-    uint32_t bcount[2][kUWaves][5];   // balance_union: per-wave bucket counts, then their prefix
+// Union of the selected blocks of kRows consecutive rows (one wave per row),
+// at most kCap entries.
+template <int kRows, int kCap>
+struct UnionSmemT {
+    int32_t list[kCap];               // union of the rows' blocks, ascending (<= kRows * topk)
+    uint32_t mask[kCap];              // which of the kRows rows selected each union block
+    uint16_t order[kCap];             // balance_union scratch: the streaming order
+    uint32_t bcount[2][kRows][5];     // balance_union: per-wave bucket counts, then their prefix
     uint32_t bsize[5];                // balance_union: bucket sizes
     uint32_t bits[kUMaxWords];
     uint32_t wbase[kUMaxWords];
     uint32_t scan_tmp[kUWaves + 1];
 };
+using UnionSmem = UnionSmemT<kURows, kUnionCap>;
 
 // Called by all kThreads threads (kThreads >= 512, so that one bitmap word per
 // thread covers 16384 blocks); returns the number of union blocks (the list and
 // masks are valid after the call's final barrier).  Entries < 0 or >= nblk are
 // ignored; rows >= rows_total contribute nothing.
-template <int kThreads = kUThreads>
-__device__ inline int build_union(UnionSmem& sm, const int32_t* __restrict__ idx, int rows_total,
-                                  int r0, int hkv, int g, int topk, int64_t nblk) {
+template <int kThreads = kUThreads, int kRows, int kCap>
+__device__ inline int build_union(UnionSmemT<kRows, kCap>& sm, const int32_t* __restrict__ idx,
+                                  int rows_total, int r0, int hkv, int g, int topk, int64_t nblk) {
     static_assert(kThreads >= kUMaxWords && kThreads <= kUThreads && kThreads % 64 == 0, "threads");
+    static_assert(kRows <= 32, "one mask bit per row");
     constexpr int kWaves = kThreads / 64;
     const int t = threadIdx.x;
     const int nwords = static_cast<int>((nblk + 31) / 32);
     for (int x = t; x < nwords; x += kThreads) sm.bits[x] = 0u;
     __syncthreads();
-    const int nent = kURows * topk;
+    const int nent = kRows * topk;
     for (int e = t; e < nent; e += kThreads) {
         const int row = r0 + e / topk;
         if (row >= rows_total) continue;
@@ -114,7 +119,7 @@ __device__ __forceinline__ uint4 k_frag(const BlockTile& t, int key, int chunk) 
 }
 
 // Streaming order of the union that spreads each barrier interval's work over
-// the SIMDs.  Wave w of a 16-wave block runs on SIMD w % 4 and owns row w, so a
+// the SIMDs.  Wave w of the block runs on SIMD w % 4 and owns row w, so a
 // block's work on SIMD s is the number of rows w = s (mod 4) in its mask.  Each
 // block goes to the bucket of its busiest SIMD (a fifth bucket for blocks whose
 // SIMD counts differ by at most one), and the buckets are interleaved round
@@ -122,10 +127,15 @@ __device__ __forceinline__ uint4 k_frag(const BlockTile& t, int key, int chunk) 
 // SIMDs.  The order is stable within a bucket.  Called by all kThreads threads
 // after build_union; on return list[] and mask[] hold the union in streaming
 // order (order[] is scratch).
-template <int kThreads = kUThreads>
-__device__ inline void balance_union(UnionSmem& sm, int n_u) {
+template <int kThreads = kUThreads, int kRows, int kCap>
+__device__ inline void balance_union(UnionSmemT<kRows, kCap>& sm, int n_u) {
     constexpr int kWaves = kThreads / 64, kB = 5;
-    static_assert(kThreads * 2 >= kUnionCap, "two entries per thread at most");
+    static_assert(kThreads * 2 >= kCap, "two entries per thread at most");
+    static_assert(kWaves == kRows && kRows % 4 == 0, "one row per wave, waves w and w + 4 on one SIMD");
+    // rows on SIMD 0: 0, 4, 8, ...
+    constexpr uint32_t kSimd0 = kRows == 4 ? 0x1u : kRows == 8 ? 0x11u : kRows == 12 ? 0x111u
+                              : kRows == 16 ? 0x1111u : kRows == 20 ? 0x11111u : kRows == 24 ? 0x111111u
+                              : kRows == 28 ? 0x1111111u : 0x11111111u;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     int bk[2];
 #pragma unroll
@@ -134,10 +144,10 @@ __device__ inline void balance_union(UnionSmem& sm, int n_u) {
         int b = -1;
         if (u < n_u) {
             const uint32_t m = sm.mask[u];
-            int best = 0, bc = __popc(m & 0x1111u), mn = bc;
+            int best = 0, bc = __popc(m & kSimd0), mn = bc;
 #pragma unroll
             for (int x = 1; x < 4; ++x) {
-                const int c = __popc(m & (0x1111u << x));
+                const int c = __popc(m & (kSimd0 << x));
                 if (c > bc) { bc = c; best = x; }
                 mn = c < mn ? c : mn;
             }
