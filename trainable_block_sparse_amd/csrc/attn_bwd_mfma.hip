@@ -102,6 +102,7 @@ __global__ __launch_bounds__(kRThreads, 1) void bwd_row_mfma(
 
     const int n_u = build_union(sm, idx, rows, r0, hkv, g, topk, nblk);
     balance_union(sm, n_u);                   // intervals spread their work over the SIMDs
+    refine_pairs(sm, n_u);                    // and exchanges between intervals even it out further
 
     // ---- row state: wave w owns row r0 + w; lane holds head lc, d = 32 ks + 8 lg ..
     const int row = r0 + w;

@@ -67,6 +67,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
     // ---- union of the 16 rows' selected blocks (ascending list + row masks)
     const int n_u = build_union(sm, idx, rows, r0, hkv, g, topk, nblk);
     balance_union(sm, n_u);                   // intervals spread their work over the SIMDs
+    refine_pairs(sm, n_u);                    // and exchanges between intervals even it out further
 
     // ---- per-wave row state: wave w owns rows r0 + 8 i + w (i < 2)
     bf16x8_t qf[kPRowsW][4];

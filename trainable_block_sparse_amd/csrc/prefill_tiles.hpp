@@ -222,4 +222,59 @@ __device__ inline void balance_union(UnionSmemT<kRows, kCap>& sm, int n_u) {
     __syncthreads();
 }
 
+// Two-block barrier intervals (blocks 2 i and 2 i + 1): one pass of pairwise
+// exchanges between intervals i and i + d (d = 1, 2, 3) that lowers the sum of
+// the two intervals' costs.  An interval's cost is the largest SIMD load, with
+// a wave that owns both blocks counted 1.6x per block (its two products run
+// back to back); the exchange takes the cheaper of swapping the second blocks
+// or swapping A's second block with B's first.  Intervals of one sub-pass are
+// disjoint (i mod 2d < d, then >= d), so the threads do not race.  Called by all
+// kThreads threads after balance_union; list[] and mask[] are updated in place.
+template <int kThreads = kUThreads, int kRows, int kCap>
+__device__ inline void refine_pairs(UnionSmemT<kRows, kCap>& sm, int n_u) {
+    static_assert(kThreads * 2 >= kCap, "one interval per thread");
+    constexpr uint32_t kSimd0 = kRows == 4 ? 0x1u : kRows == 8 ? 0x11u : kRows == 12 ? 0x111u
+                              : kRows == 16 ? 0x1111u : kRows == 20 ? 0x11111u : kRows == 24 ? 0x111111u
+                              : kRows == 28 ? 0x1111111u : 0x11111111u;
+    auto cost = [](uint32_t a, uint32_t b) {   // 5 x (SIMD load), 8 x (2 products of one wave)
+        uint32_t c = 0;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const uint32_t sx = kSimd0 << x;
+            const uint32_t sum = 5u * (__popc(a & sx) + __popc(b & sx));
+            const uint32_t two = (a & b & sx) ? 16u : (((a | b) & sx) ? 8u : 0u);
+            const uint32_t v = sum > two ? sum : two;
+            c = v > c ? v : c;
+        }
+        return c;
+    };
+    const int t = threadIdx.x;
+    const int n_full = n_u / 2;                 // intervals with two blocks
+#pragma unroll
+    for (int d = 1; d <= 3; ++d) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int i = t;
+            if (i + d < n_full && (i % (2 * d)) / d == h) {
+                const int pa = 2 * i, pb = 2 * (i + d);
+                const uint32_t a0 = sm.mask[pa], a1 = sm.mask[pa + 1];
+                const uint32_t b0 = sm.mask[pb], b1 = sm.mask[pb + 1];
+                const uint32_t cur = cost(a0, a1) + cost(b0, b1);
+                const uint32_t o1 = cost(a0, b1) + cost(b0, a1);   // swap the second blocks
+                const uint32_t o2 = cost(a0, b0) + cost(a1, b1);   // swap A's second with B's first
+                if (o1 < cur && o1 <= o2) {
+                    const int32_t la = sm.list[pa + 1];
+                    sm.list[pa + 1] = sm.list[pb + 1]; sm.mask[pa + 1] = b1;
+                    sm.list[pb + 1] = la;              sm.mask[pb + 1] = a1;
+                } else if (o2 < cur) {
+                    const int32_t la = sm.list[pa + 1];
+                    sm.list[pa + 1] = sm.list[pb]; sm.mask[pa + 1] = b0;
+                    sm.list[pb] = la;              sm.mask[pb] = a1;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
 }  // namespace infv2
