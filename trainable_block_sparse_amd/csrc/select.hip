@@ -589,6 +589,7 @@ constexpr int kPreWaves = 8;                          // wave w: rows w + 8 i
 constexpr int kPreRW = kPreRowsG / kPreWaves;         // query rows per wave
 constexpr int kPreThreads = kPreWaves * 64;
 constexpr int kPreLoads = kPreTileK * 16 / kPreThreads;   // 16-byte chunks per thread and tile
+constexpr float kPreMrInit = -1e30f;                  // pass 1 reference before any visible logit
 
 template <int kPass, bool kCkBf16>
 __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
@@ -610,12 +611,13 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
 
     int64_t vis[kPreRW];
     bf16x8_t qf[kPreRW][4];
-    int64_t vmax = 0;
-    for (int rr = 0; rr < kPreRowsG; ++rr) {
-        const int row = r0 + rr;
-        int64_t v = row < rows ? num_kernels(q_start + row + 1, p, s) : 0;
-        v = v < ccap ? v : ccap;
-        vmax = v > vmax ? v : vmax;
+    int64_t vmax = 0;                     // the group's last valid row sees the most kernels
+    {
+        const int last = (r0 + kPreRowsG - 1 < rows ? r0 + kPreRowsG - 1 : rows - 1);
+        if (last >= r0) {
+            const int64_t v = num_kernels(q_start + last + 1, p, s);
+            vmax = v < ccap ? v : ccap;
+        }
     }
 #pragma unroll
     for (int i = 0; i < kPreRW; ++i) {
@@ -646,7 +648,7 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
 #pragma unroll
     for (int i = 0; i < kPreRW; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) { mr[i][r] = -INFINITY; lr[i][r] = 0.f; }
+        for (int r = 0; r < 4; ++r) { mr[i][r] = kPreMrInit; lr[i][r] = 0.f; }
     if (kPass == 2) {
 #pragma unroll
         for (int i = 0; i < kPreRW; ++i) {
@@ -743,15 +745,14 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const float mn = fmaxf(mr[i][r], x[r]);
-                            if (mn != -INFINITY) {
-                                lr[i][r] = lr[i][r] * fast_exp2(mr[i][r] - mn);   // 2^-inf = 0
-                                mr[i][r] = mn;
-                            }
+                            lr[i][r] = lr[i][r] * fast_exp2(mr[i][r] - mn);   // finite reference: no NaN
+                            mr[i][r] = mn;
                         }
                     }
+                    // the reference is finite (kPreMrInit at first), so masked logits
+                    // (-inf) give 2^-inf = 0 without a test
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        lr[i][r] += (x[r] == -INFINITY) ? 0.f : fast_exp2(x[r] - mr[i][r]);
+                    for (int r = 0; r < 4; ++r) lr[i][r] += fast_exp2(x[r] - mr[i][r]);
                 } else {
                     float acc = 0.f;
 #pragma unroll
@@ -810,12 +811,12 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
                 float mx = mr[i][r];
 #pragma unroll
                 for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-                float sm = (mr[i][r] == -INFINITY) ? 0.f : lr[i][r] * fast_exp2(mr[i][r] - mx);
+                float sm = lr[i][r] * fast_exp2(mr[i][r] - mx);   // lanes still at kPreMrInit hold 0
 #pragma unroll
                 for (int o = 1; o < 16; o <<= 1) sm += __shfl_xor(sm, o, 64);
                 if (lc == 0 && row < rows)
                     lse[static_cast<size_t>(row) * hq + g * kGroup + 4 * lg + r] =
-                        (mx == -INFINITY) ? -INFINITY : (mx + __log2f(sm)) * 0.6931471805599453f;
+                        (mx == kPreMrInit) ? -INFINITY : (mx + __log2f(sm)) * 0.6931471805599453f;
             }
         }
     }
