@@ -734,25 +734,28 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
                     // running (max, sum) with a lazy max: the reference moves only
                     // when some lane's logit exceeds it by more than 2^8, so the
                     // common path is one exp per logit and no divergence
-                    float x[4];
+                    // d = logit - reference in one FMA; masked logits are -inf
+                    float d[4];
                     bool over = false;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        x[r] = ok ? z[i][r] * zscale : -INFINITY;
-                        over |= x[r] > mr[i][r] + 8.f;
+                        d[r] = ok ? fmaf(z[i][r], zscale, -mr[i][r]) : -INFINITY;
+                        over |= d[r] > 8.f;
                     }
                     if (__any(over)) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            const float mn = fmaxf(mr[i][r], x[r]);
+                            const float x = ok ? z[i][r] * zscale : -INFINITY;
+                            const float mn = fmaxf(mr[i][r], x);
                             lr[i][r] = lr[i][r] * fast_exp2(mr[i][r] - mn);   // finite reference: no NaN
                             mr[i][r] = mn;
+                            d[r] = x - mn;
                         }
                     }
                     // the reference is finite (kPreMrInit at first), so masked logits
                     // (-inf) give 2^-inf = 0 without a test
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) lr[i][r] += fast_exp2(x[r] - mr[i][r]);
+                    for (int r = 0; r < 4; ++r) lr[i][r] += fast_exp2(d[r]);
                 } else {
                     float acc = 0.f;
 #pragma unroll
