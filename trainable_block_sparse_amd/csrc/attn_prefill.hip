@@ -11,7 +11,9 @@
 // block builds the union of the rows' selected blocks and streams it through
 // LDS with direct global->LDS loads (K and V as stored; the V^T operand comes
 // from the V tile by transpose reads), two blocks per barrier interval with the
-// next interval's loads in flight under the current one's products.
+// next interval's loads in flight under the current one's products.  The
+// streaming order spreads each interval's (row, block) pairs over the SIMDs
+// (balance_union, refine_pairs).
 // For each block the waves whose row selected it run:
 //   S^T[key][head] = K_blk . Q_row^T          16 MFMA 16x16x32
 //   O^T[d][head]  += V^T_blk . P_row^T        16 MFMA 16x16x32
@@ -37,7 +39,7 @@ constexpr int kVBatch = 2;       // V^T d-tiles whose fragments are read from LD
 constexpr int kTileLoads = 16 / kPWaves;             // 1 KB global->LDS loads per wave per tile
 constexpr int kPThreads = kPWaves * 64;
 static_assert(kPThreads == kUThreads && kPRows == kURows, "rows and threads of the union build");
-constexpr int kGroup2 = 2;       // union blocks per LDS stage; two stages = one interval
+constexpr int kGroup2 = 2;       // union blocks per LDS stage = per barrier interval; two stages
 constexpr int kXcds = 8;         // thread blocks are dealt round-robin to the 8 XCDs
 constexpr float kRescaleSlack = 8.f;   // log2 units
 
