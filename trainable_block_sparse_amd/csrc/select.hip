@@ -31,6 +31,8 @@
 namespace infv2 {
 
 constexpr int kChunkA = 64;      // kernels per block in sel_dec_logits
+constexpr int kLogWaves = 2;     // waves per 64-kernel chunk in sel_dec_logits_mfma (4 was no faster)
+constexpr int kLogTiles = 4 / kLogWaves;   // 16-kernel tiles per wave
 constexpr int kChunkB = 256;     // kernels per block in sel_dec_scores
 constexpr int kRowsPre = 4;      // query rows per block in the prefill passes
 constexpr int kTilePre = 64;     // kernels per LDS tile in the prefill passes
@@ -161,17 +163,17 @@ __global__ __launch_bounds__(256) void sel_dec_logits(
 }
 
 // ------------------------------------------------------------------ decode, pass 1 on the matrix cores
-// Two waves per block score 64 kernels (32 each).  Z^T[kernel][head] = CK (64x128) . Q^T:
+// kLogWaves waves per block score 64 kernels (64 / kLogWaves each).  Z^T[kernel][head] = CK (64x128) . Q^T:
 // the compressed keys are the A operand as stored (lane: 8 consecutive d of one
 // kernel); fp32 keys are split into bf16 hi + lo (x = hi + lo + O(2^-17 |x|)),
 // two MFMAs per tile, products exact in fp32.  Z^T puts one head per lane column.
 template <bool kCkBf16>
-__global__ __launch_bounds__(128) void sel_dec_logits_mfma(
+__global__ __launch_bounds__(kLogWaves * 64) void sel_dec_logits_mfma(
     const bf16_t* __restrict__ q, const void* __restrict__ ck, const int64_t* __restrict__ ck_off,
     const int64_t* __restrict__ kv_off, const int64_t* __restrict__ kv_lens, int hq, int hkv,
     int p, int s, float score_scale, int64_t nc_max, int64_t nc_ld, int nchunk, int64_t nblk_max,
     float* __restrict__ logits, float2* __restrict__ partial, uint32_t* __restrict__ keys) {
-    __shared__ float2 xm[kGroup];        // wave 1's (max, sum) per head
+    __shared__ float2 xm[kLogWaves][kGroup];   // each wave's (max, sum) per head
     const int b = blockIdx.z, g = blockIdx.y, ch = blockIdx.x, t = threadIdx.x;
     const int l = t & 63, wv = t >> 6, lg = l >> 4, lc = l & 15;
     const int64_t cap = kv_off[b + 1] - kv_off[b];
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(128) void sel_dec_logits_mfma(
         uint32_t* kb = keys + bg * nblk_max;
         const int64_t per = (nblk_max + nchunk - 1) / nchunk;
         const int64_t e = (ch + 1) * per < nblk_max ? (ch + 1) * per : nblk_max;
-        for (int64_t j = ch * per + t; j < e; j += 128) kb[j] = 0u;
+        for (int64_t j = ch * per + t; j < e; j += kLogWaves * 64) kb[j] = 0u;
     }
     const bf16_t* qrow = q + (static_cast<size_t>(b) * hq + static_cast<size_t>(g) * kGroup + lc) * kHeadDim;
     bf16x8_t qf[4];
@@ -194,11 +196,11 @@ __global__ __launch_bounds__(128) void sel_dec_logits_mfma(
     for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(ldg16(qrow + 32 * ks + 8 * lg));
     const int64_t j0 = static_cast<int64_t>(ch) * kChunkA;
     const int64_t cbase = (ck_off[b] * hkv + static_cast<int64_t>(g) * ccap);
-    // wave wv: kernel tiles mt = 2 wv, 2 wv + 1
-    f32x4_t z[2];
+    // wave wv: kernel tiles mt = kLogTiles wv ..
+    f32x4_t z[kLogTiles];
 #pragma unroll
-    for (int m2 = 0; m2 < 2; ++m2) {
-        const int mt = 2 * wv + m2;
+    for (int m2 = 0; m2 < kLogTiles; ++m2) {
+        const int mt = kLogTiles * wv + m2;
         f32x4_t& zt = z[m2];
         zt = f32x4_t{0.f, 0.f, 0.f, 0.f};
         int64_t j = j0 + 16 * mt + lc;
@@ -238,8 +240,8 @@ __global__ __launch_bounds__(128) void sel_dec_logits_mfma(
     // lane holds Z[head lc][kernel j0 + 16 mt + 4 lg + r]
     float mx = -INFINITY;
 #pragma unroll
-    for (int m2 = 0; m2 < 2; ++m2) {
-        const int mt = 2 * wv + m2;
+    for (int m2 = 0; m2 < kLogTiles; ++m2) {
+        const int mt = kLogTiles * wv + m2;
         const int64_t jb = j0 + 16 * mt + 4 * lg;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -260,21 +262,26 @@ __global__ __launch_bounds__(128) void sel_dec_logits_mfma(
     float sm = 0.f;
     if (mx != -INFINITY) {
 #pragma unroll
-        for (int m2 = 0; m2 < 2; ++m2)
+        for (int m2 = 0; m2 < kLogTiles; ++m2)
 #pragma unroll
             for (int r = 0; r < 4; ++r) sm += (z[m2][r] == -INFINITY) ? 0.f : expf(z[m2][r] - mx);
     }
     sm += __shfl_xor(sm, 16, 64);
     sm += __shfl_xor(sm, 32, 64);
-    // the two waves' (max, sum) of each head combine into the chunk's partial
-    if (wv == 1 && lg == 0) xm[lc] = make_float2(mx, sm);
+    // the waves' (max, sum) of each head combine into the chunk's partial
+    if (lg == 0) xm[wv][lc] = make_float2(mx, sm);
     __syncthreads();
     if (wv == 0 && lg == 0) {
-        const float2 o = xm[lc];
-        const float m2 = fmaxf(mx, o.x);
+        float m2 = -INFINITY;
+#pragma unroll
+        for (int x = 0; x < kLogWaves; ++x) m2 = fmaxf(m2, xm[x][lc].x);
         float s2 = 0.f;
         if (m2 != -INFINITY) {
-            s2 = (mx == -INFINITY ? 0.f : sm * expf(mx - m2)) + (o.x == -INFINITY ? 0.f : o.y * expf(o.x - m2));
+#pragma unroll
+            for (int x = 0; x < kLogWaves; ++x) {
+                const float2 o = xm[x][lc];
+                s2 += (o.x == -INFINITY) ? 0.f : o.y * expf(o.x - m2);
+            }
         }
         partial[(bg * nchunk + ch) * kGroup + lc] = make_float2(m2, s2);
     }
@@ -968,7 +975,7 @@ static void dec_launch(const Shape& sh, const void* q, const void* ck, const int
         dim3 gc(nch_c, sh.hkv, batch);
         KernelTimer kt(INFV2_KERNEL_SELECT_LOGITS, st);
         if (sizeof(Tq) == 2)
-            sel_dec_logits_mfma<sizeof(Tck) == 2><<<gc, 128, 0, st>>>(
+            sel_dec_logits_mfma<sizeof(Tck) == 2><<<gc, kLogWaves * 64, 0, st>>>(
                 static_cast<const bf16_t*>(q), cs->ckc, cs->ckc_off, kv_off, kv_lens, sh.hq, sh.hkv,
                 c, c, sh.score_scale, ncm_c, ld_c, nch_c, w.nblk_max, logits_c, partial_c, keys);
         else
@@ -980,7 +987,7 @@ static void dec_launch(const Shape& sh, const void* q, const void* ck, const int
     {
         KernelTimer kt(INFV2_KERNEL_SELECT_LOGITS, st);
         if (sizeof(Tq) == 2)
-            sel_dec_logits_mfma<sizeof(Tck) == 2><<<ga, 128, 0, st>>>(
+            sel_dec_logits_mfma<sizeof(Tck) == 2><<<ga, kLogWaves * 64, 0, st>>>(
                 static_cast<const bf16_t*>(q), ck, ck_off, kv_off, kv_lens, sh.hq, sh.hkv, sh.p,
                 sh.s, sh.score_scale, ncm, w.nc_ld, w.nchunk_a, w.nblk_max, logits, partial, keys);
         else
