@@ -30,6 +30,8 @@
 
 namespace infv2 {
 
+constexpr float kLog2eF = 1.4426950408889634f;   // exp(x) = 2^(x log2 e) on the transcendental unit
+constexpr float kLn2F = 0.6931471805599453f;
 constexpr int kChunkA = 64;      // kernels per block in sel_dec_logits
 constexpr int kLogWaves = 2;     // waves per 64-kernel chunk in sel_dec_logits_mfma (4 was no faster)
 constexpr int kLogTiles = 4 / kLogWaves;   // 16-kernel tiles per wave
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(kLogWaves * 64) void sel_dec_logits_mfma(
 #pragma unroll
         for (int m2 = 0; m2 < kLogTiles; ++m2)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sm += (z[m2][r] == -INFINITY) ? 0.f : expf(z[m2][r] - mx);
+            for (int r = 0; r < 4; ++r) sm += fast_exp2((z[m2][r] - mx) * kLog2eF);   // exp(-inf) = 0
     }
     sm += __shfl_xor(sm, 16, 64);
     sm += __shfl_xor(sm, 32, 64);
@@ -280,7 +282,7 @@ __global__ __launch_bounds__(kLogWaves * 64) void sel_dec_logits_mfma(
 #pragma unroll
             for (int x = 0; x < kLogWaves; ++x) {
                 const float2 o = xm[x][lc];
-                s2 += (o.x == -INFINITY) ? 0.f : o.y * expf(o.x - m2);
+                s2 += (o.x == -INFINITY) ? 0.f : o.y * fast_exp2((o.x - m2) * kLog2eF);
             }
         }
         partial[(bg * nchunk + ch) * kGroup + lc] = make_float2(m2, s2);
@@ -309,14 +311,14 @@ __device__ __forceinline__ float fold_partials(const float2* __restrict__ pp, in
     float sm = 0.f;
     if (mx != -INFINITY) {
 #pragma unroll
-        for (int u = 0; u < kMaxPer; ++u) sm += (pm[u].x == -INFINITY) ? 0.f : pm[u].y * expf(pm[u].x - mx);
+        for (int u = 0; u < kMaxPer; ++u) sm += (pm[u].x == -INFINITY) ? 0.f : pm[u].y * fast_exp2((pm[u].x - mx) * kLog2eF);
         for (int c = r + 16 * kMaxPer; c < nchunk; c += 16) {
             const float2 q2 = pp[static_cast<size_t>(c) * kGroup];
-            sm += (q2.x == -INFINITY) ? 0.f : q2.y * expf(q2.x - mx);
+            sm += (q2.x == -INFINITY) ? 0.f : q2.y * fast_exp2((q2.x - mx) * kLog2eF);
         }
     }
     sm = sum16(sm);
-    return (mx == -INFINITY) ? -INFINITY : mx + logf(sm);
+    return (mx == -INFINITY) ? -INFINITY : mx + __log2f(sm) * kLn2F;
 }
 
 // lse_in: a per-(sequence, KV head, head) normaliser to use instead of the one
@@ -363,7 +365,7 @@ __global__ __launch_bounds__(256) void sel_dec_scores(
     if (j < nvis) {
         float acc = 0.f;
 #pragma unroll
-        for (int h = 0; h < kGroup; ++h) acc += expf(zz[h] - ls[h]);
+        for (int h = 0; h < kGroup; ++h) acc += fast_exp2((zz[h] - ls[h]) * kLog2eF);
         R = acc * (1.0f / kGroup);
     }
     rs[t] = R;
