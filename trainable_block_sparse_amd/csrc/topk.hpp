@@ -95,6 +95,10 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
     uint32_t lo = 0, hi = 0, need = kp;
     int mode = 3;
     if (kp > 0) {
+        // the first histogram is cleared here; the barrier after the min / max
+        // orders the clearing before its increments
+#pragma unroll
+        for (int x = t; x < kTopkBins; x += kThreads) sm.hist[x] = 0;
         uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
@@ -117,14 +121,16 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
             lo = sm.rmin[x] < lo ? sm.rmin[x] : lo;
             hi = sm.rmax[x] > hi ? sm.rmax[x] : hi;
         }
-        for (;;) {
+        for (bool first = true;; first = false) {
             const uint32_t span = hi - lo;
             if (span == 0) { mode = 2; break; }
             const int bits = 32 - __clz(span);
             const int sh = bits > 10 ? bits - 10 : 0;
+            if (!first) {
 #pragma unroll
-            for (int x = t; x < kTopkBins; x += kThreads) sm.hist[x] = 0;
-            __syncthreads();
+                for (int x = t; x < kTopkBins; x += kThreads) sm.hist[x] = 0;
+                __syncthreads();
+            }
 #pragma unroll
             for (int u = 0; u < kPer; ++u)
                 if (cand(u) && key[u] >= lo && key[u] <= hi) atomicAdd(&sm.hist[(key[u] - lo) >> sh], 1u);
@@ -163,15 +169,18 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
     }
     auto in_window = [&](int u) { return cand(u) && key[u] >= lo && key[u] <= hi; };
     uint32_t ncol = 0;
+    int16_t slot_of[kPer];                // mode 1: where each window key was collected
     if (mode == 1) {                      // collect the window's keys, rank them
         if (t == 0) sm.ncol = 0;
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
+            slot_of[u] = -1;
             if (in_window(u)) {
                 const uint32_t slot = atomicAdd(&sm.ncol, 1u);
                 sm.ckey[slot] = key[u];
                 sm.cidx[slot] = jb + u;
+                slot_of[u] = static_cast<int16_t>(slot);
             }
         }
         __syncthreads();
@@ -214,8 +223,7 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
                 if (mode == 0) {
                     s = true;
                 } else {
-                    for (uint32_t x = 0; x < ncol; ++x)
-                        if (sm.cidx[x] == jb + u) { s = sm.ckey[x] != 0u; break; }
+                    s = sm.ckey[slot_of[u]] != 0u;       // keep flag of the key's own slot
                 }
             }
             if (s) smask |= Mask(1) << u;
@@ -226,7 +234,11 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
         if (u < cnt && !cand(u)) smask |= Mask(1) << u;     // forced
     const uint32_t n_sel = sizeof(Mask) == 8 ? __popcll(static_cast<uint64_t>(smask))
                                              : __popc(static_cast<uint32_t>(smask));
-    uint32_t pos = block_incl_scan<kWaves>(n_sel, sm.scan_tmp) - n_sel;
+    const uint32_t incl = block_incl_scan<kWaves>(n_sel, sm.scan_tmp);
+    // the total is known before any store, so no barrier waits for the stores
+    if (t == kThreads - 1) sm.total = incl;
+    __syncthreads();
+    uint32_t pos = incl - n_sel;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
         if ((smask >> u) & 1u) {
@@ -237,9 +249,7 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
             ++pos;
         }
     }
-    // every selected block is written above; slots past the total stay padding
-    if (t == kThreads - 1) sm.total = pos;
-    __syncthreads();
+    // slots past the total are padding
     for (int r = static_cast<int>(sm.total) + t; r < k; r += kThreads) {
         idx[r] = -1;
         if (score) score[r] = kNaN;
