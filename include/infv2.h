@@ -355,11 +355,16 @@ int32_t infv2_abi_version(void);
 
 /*
  * Kernel timing, for benchmarks and profiling only (not part of the method).
- * While a timing session is open, every launch of the chosen kernel family is
- * bracketed by a pair of HIP events recorded on the stream it is launched on,
- * so one kernel can be timed on its own although an entry point launches
- * several.  Launches on a stream that is being captured into a graph are not
- * bracketed.  This is the only global state of the library: one session at a
+ * While a timing session is open, every launch of the chosen kernel family gets
+ * a pair of HIP events, so one kernel can be timed on its own although an entry
+ * point launches several.  For a family of one kernel per launch site (the
+ * attention, scoring, append and backward-pass kernels) the launch itself
+ * stamps the pair with the kernel's own begin and end (hipExtLaunchKernel);
+ * for the others (compression, top-k, the backward's inverse index) the pair
+ * is recorded on the stream before and after the launches of one call.  The
+ * backward column family times its main kernel, not the small work-list and
+ * reduction kernels around it.  Launches on a stream that is being captured
+ * into a graph are not timed.  This is the only global state of the library: one session at a
  * time per process, guarded by a mutex.
  *
  * infv2_timing_start  opens a session for `kernel` (an infv2_kernel id);
@@ -367,7 +372,7 @@ int32_t infv2_abi_version(void);
  *                     open.
  * infv2_timing_stop   closes it, waits for the recorded events and returns
  *                     the summed duration in milliseconds and the number of
- *                     bracketed launches; INFV2_ERR_SHAPE if no session is
+ *                     timed launches; INFV2_ERR_SHAPE if no session is
  *                     open, INFV2_ERR_DEVICE if an event failed.
  */
 typedef enum infv2_kernel {

@@ -193,8 +193,7 @@ hipError_t launch_attn_decode(const Shape& sh, const void* q, const void* k, con
     if (sh.io_bf16) {
         e = launch_attn_decode_mfma(sh, q, k, v, kv_off, kv_lens, batch, idx, po, pml, w.nsplit, st);
     } else {
-        KernelTimer kt(INFV2_KERNEL_ATTN_DECODE, st);
-        attn_decode_kernel<float><<<grid, 256, 0, st>>>(static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), kv_off, kv_lens, idx, po, pml, sh.hq, sh.hkv, sh.m, sh.topk, w.nsplit, sh.attn_scale);
+        launch_timed(INFV2_KERNEL_ATTN_DECODE, attn_decode_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), kv_off, kv_lens, idx, po, pml, sh.hq, sh.hkv, sh.m, sh.topk, w.nsplit, sh.attn_scale);
         e = hipGetLastError();
     }
     if (e != hipSuccess) return e;
@@ -208,11 +207,10 @@ hipError_t launch_attn_prefill(const Shape& sh, const void* q, int rows, int64_t
     if (attn_prefill_mfma_ok(sh))
         return launch_attn_prefill_mfma(sh, q, rows, q_start, k, v, kv_off, idx, out, ws, st);
     dim3 grid(rows, sh.hkv);
-    KernelTimer kt(INFV2_KERNEL_ATTN_PREFILL, st);
     if (sh.io_bf16)
-        attn_prefill_kernel<bf16_t><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(q), q_start, static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), kv_off, idx, static_cast<bf16_t*>(out), sh.hq, sh.hkv, sh.m, sh.topk, sh.attn_scale);
+        launch_timed(INFV2_KERNEL_ATTN_PREFILL, attn_prefill_kernel<bf16_t>, grid, dim3(256), 0, st, static_cast<const bf16_t*>(q), q_start, static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), kv_off, idx, static_cast<bf16_t*>(out), sh.hq, sh.hkv, sh.m, sh.topk, sh.attn_scale);
     else
-        attn_prefill_kernel<float><<<grid, 256, 0, st>>>(static_cast<const float*>(q), q_start, static_cast<const float*>(k), static_cast<const float*>(v), kv_off, idx, static_cast<float*>(out), sh.hq, sh.hkv, sh.m, sh.topk, sh.attn_scale);
+        launch_timed(INFV2_KERNEL_ATTN_PREFILL, attn_prefill_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(q), q_start, static_cast<const float*>(k), static_cast<const float*>(v), kv_off, idx, static_cast<float*>(out), sh.hq, sh.hkv, sh.m, sh.topk, sh.attn_scale);
     return hipGetLastError();
 }
 

@@ -396,11 +396,10 @@ hipError_t launch_attn_prefill_bwd(const Shape& sh, const void* q, int rows, int
         return launch_attn_prefill_bwd_mfma(sh, w, q, rows, q_start, k, v, kv_off, idx, out, dout, dq, dk, dv, base, st);
     hipError_t e;
     {
-        KernelTimer kt(INFV2_KERNEL_BWD_ROW, st);
         if (sh.io_bf16)
-            bwd_row_kernel<bf16_t><<<dim3(rows, sh.hkv), 256, 0, st>>>(static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(out), static_cast<const bf16_t*>(dout), q_start, static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), kv_off, idx, static_cast<bf16_t*>(dq), lse, delta, sh.hq, sh.hkv, sh.m, sh.topk, sh.attn_scale);
+            launch_timed(INFV2_KERNEL_BWD_ROW, bwd_row_kernel<bf16_t>, dim3(rows, sh.hkv), dim3(256), 0, st, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(out), static_cast<const bf16_t*>(dout), q_start, static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), kv_off, idx, static_cast<bf16_t*>(dq), lse, delta, sh.hq, sh.hkv, sh.m, sh.topk, sh.attn_scale);
         else
-            bwd_row_kernel<float><<<dim3(rows, sh.hkv), 256, 0, st>>>(static_cast<const float*>(q), static_cast<const float*>(out), static_cast<const float*>(dout), q_start, static_cast<const float*>(k), static_cast<const float*>(v), kv_off, idx, static_cast<float*>(dq), lse, delta, sh.hq, sh.hkv, sh.m, sh.topk, sh.attn_scale);
+            launch_timed(INFV2_KERNEL_BWD_ROW, bwd_row_kernel<float>, dim3(rows, sh.hkv), dim3(256), 0, st, static_cast<const float*>(q), static_cast<const float*>(out), static_cast<const float*>(dout), q_start, static_cast<const float*>(k), static_cast<const float*>(v), kv_off, idx, static_cast<float*>(dq), lse, delta, sh.hq, sh.hkv, sh.m, sh.topk, sh.attn_scale);
         e = hipGetLastError();
     }
     if (e != hipSuccess) return e;
@@ -408,12 +407,11 @@ hipError_t launch_attn_prefill_bwd(const Shape& sh, const void* q, int rows, int
     const int32_t* cstart = reinterpret_cast<const int32_t*>(base + w.col_start);
     const int32_t* list = reinterpret_cast<const int32_t*>(base + w.list);
     const int nsub = (sh.m + kBTok - 1) / kBTok;
-    KernelTimer kt(INFV2_KERNEL_BWD_COL, st);
     const dim3 grid(w.nblk * nsub, sh.hkv);
     if (sh.io_bf16)
-        bwd_col_kernel<bf16_t><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(dout), q_start, rows, static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), kv_off, cstart, list, w.list_ld, lse, delta, static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), sh.hq, sh.hkv, sh.m, w.nblk, nsub, sh.attn_scale);
+        launch_timed(INFV2_KERNEL_BWD_COL, bwd_col_kernel<bf16_t>, grid, dim3(256), 0, st, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(dout), q_start, rows, static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), kv_off, cstart, list, w.list_ld, lse, delta, static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), sh.hq, sh.hkv, sh.m, w.nblk, nsub, sh.attn_scale);
     else
-        bwd_col_kernel<float><<<grid, 256, 0, st>>>(static_cast<const float*>(q), static_cast<const float*>(dout), q_start, rows, static_cast<const float*>(k), static_cast<const float*>(v), kv_off, cstart, list, w.list_ld, lse, delta, static_cast<float*>(dk), static_cast<float*>(dv), sh.hq, sh.hkv, sh.m, w.nblk, nsub, sh.attn_scale);
+        launch_timed(INFV2_KERNEL_BWD_COL, bwd_col_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(q), static_cast<const float*>(dout), q_start, rows, static_cast<const float*>(k), static_cast<const float*>(v), kv_off, cstart, list, w.list_ld, lse, delta, static_cast<float*>(dk), static_cast<float*>(dv), sh.hq, sh.hkv, sh.m, w.nblk, nsub, sh.attn_scale);
     return hipGetLastError();
 }
 

@@ -544,9 +544,9 @@ hipError_t launch_attn_prefill_bwd_mfma(const Shape& sh, const BwdWs& w, const v
     const float scale_log2 = sh.attn_scale * 1.4426950408889634f;
     hipError_t e = hipSuccess;
     {
-        KernelTimer tm(INFV2_KERNEL_BWD_ROW, st);
         const int nrg = (rows + kURows - 1) / kURows;
-        bwd_row_mfma<<<dim3(static_cast<unsigned>(nrg) * sh.hkv), kRThreads, 0, st>>>(
+        launch_timed(INFV2_KERNEL_BWD_ROW, bwd_row_mfma,
+                     dim3(static_cast<unsigned>(nrg) * sh.hkv), dim3(kRThreads), 0, st,
             static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(out),
             static_cast<const bf16_t*>(dout), rows, q_start, static_cast<const bf16_t*>(k),
             static_cast<const bf16_t*>(v), kv_off, idx, static_cast<bf16_t*>(dq), lse2, delta,
@@ -556,10 +556,10 @@ hipError_t launch_attn_prefill_bwd_mfma(const Shape& sh, const BwdWs& w, const v
     if ((e = launch_inverse_index(sh, w, rows, idx, base, st)) != hipSuccess) return e;
     const int32_t* cstart = reinterpret_cast<const int32_t*>(base + w.col_start);
     const int32_t* list = reinterpret_cast<const int32_t*>(base + w.list);
-    KernelTimer tm(INFV2_KERNEL_BWD_COL, st);
     bwd_items_kernel<<<1, 1024, 0, st>>>(cstart, w.nblk, ncol, item_start);
     const int64_t items = max_col_items(sh, w);
-    bwd_col_mfma<<<dim3(static_cast<unsigned>(items)), kCThreads, 0, st>>>(
+    launch_timed(INFV2_KERNEL_BWD_COL, bwd_col_mfma, dim3(static_cast<unsigned>(items)),
+                 dim3(kCThreads), 0, st,
         static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(dout), rows, q_start,
         static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), kv_off, cstart, list,
         w.list_ld, item_start, lse2, delta, static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv),

@@ -271,8 +271,7 @@ hipError_t launch_attn_decode_mfma(const Shape& sh, const void* q, const void* k
                                    hipStream_t st) {
     dim3 grid(nsplit, sh.hkv, batch);
     const float scale_log2 = sh.attn_scale * 1.4426950408889634f;
-    KernelTimer kt(INFV2_KERNEL_ATTN_DECODE, st);
-    attn_decode_mfma<<<grid, 256, 0, st>>>(
+    launch_timed(INFV2_KERNEL_ATTN_DECODE, attn_decode_mfma, grid, dim3(256), 0, st,
         static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
         kv_off, kv_lens, idx, part_o, part_ml, sh.hq, sh.hkv, sh.m, sh.topk, nsplit, scale_log2);
     return hipGetLastError();
@@ -281,13 +280,12 @@ hipError_t launch_attn_decode_mfma(const Shape& sh, const void* q, const void* k
 hipError_t launch_attn_decode_merge(const Shape& sh, const float* part_o, const float2* part_ml,
                                     void* out, int batch, int nsplit, hipStream_t st) {
     dim3 grid(sh.hkv, batch);
-    KernelTimer kt(INFV2_KERNEL_ATTN_MERGE, st);
     if (sh.io_bf16)
-        attn_decode_merge<bf16_t><<<grid, 256, 0, st>>>(part_o, part_ml, static_cast<bf16_t*>(out),
-                                                        sh.hq, sh.hkv, nsplit);
+        launch_timed(INFV2_KERNEL_ATTN_MERGE, attn_decode_merge<bf16_t>, grid, dim3(256), 0, st,
+                     part_o, part_ml, static_cast<bf16_t*>(out), sh.hq, sh.hkv, nsplit);
     else
-        attn_decode_merge<float><<<grid, 256, 0, st>>>(part_o, part_ml, static_cast<float*>(out),
-                                                       sh.hq, sh.hkv, nsplit);
+        launch_timed(INFV2_KERNEL_ATTN_MERGE, attn_decode_merge<float>, grid, dim3(256), 0, st,
+                     part_o, part_ml, static_cast<float*>(out), sh.hq, sh.hkv, nsplit);
     return hipGetLastError();
 }
 

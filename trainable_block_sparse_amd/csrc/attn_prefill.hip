@@ -299,9 +299,9 @@ hipError_t launch_attn_prefill_mfma(const Shape& sh, const void* q, int rows, in
     const int64_t nblk = (n + kPB - 1) / kPB;
     (void)ws;
     const float scale_log2 = sh.attn_scale * 1.4426950408889634f;
-    KernelTimer kt(INFV2_KERNEL_ATTN_PREFILL, st);
     const int nrg = (rows + kPRows - 1) / kPRows;
-    attn_prefill_mfma<<<dim3(static_cast<unsigned>(nrg) * sh.hkv), kPThreads, 0, st>>>(
+    launch_timed(INFV2_KERNEL_ATTN_PREFILL, attn_prefill_mfma,
+                 dim3(static_cast<unsigned>(nrg) * sh.hkv), dim3(kPThreads), 0, st,
         static_cast<const bf16_t*>(q), rows, q_start, static_cast<const bf16_t*>(k),
         static_cast<const bf16_t*>(v), kv_off,
         idx, static_cast<bf16_t*>(out), sh.hq, sh.hkv, sh.topk, nblk, nrg, scale_log2);

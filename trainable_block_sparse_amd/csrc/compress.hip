@@ -181,9 +181,8 @@ __global__ __launch_bounds__(256) void append_kv_kernel(
 hipError_t launch_append_kv(const Shape& sh, const void* k_new, const void* v_new, void* k,
                             void* v, const int64_t* kv_off, int64_t* kv_lens,
                             const int64_t* ck_off, void* ck, int batch, hipStream_t st) {
-    KernelTimer kt(INFV2_KERNEL_APPEND, st);
-#define INFV2_APPEND(TIN, CKB) append_kv_kernel<TIN, CKB><<<dim3(batch), 256, 0, st>>>( \
-        static_cast<const TIN*>(k_new), static_cast<const TIN*>(v_new), static_cast<TIN*>(k), \
+#define INFV2_APPEND(TIN, CKB) launch_timed(INFV2_KERNEL_APPEND, append_kv_kernel<TIN, CKB>, \
+        dim3(batch), dim3(256), 0, st, static_cast<const TIN*>(k_new), static_cast<const TIN*>(v_new), static_cast<TIN*>(k), \
         static_cast<TIN*>(v), kv_off, kv_lens, ck_off, ck, sh.hkv, sh.p, sh.s)
     if (sh.io_bf16) { if (sh.ck_bf16) INFV2_APPEND(bf16_t, true); else INFV2_APPEND(bf16_t, false); }
     else { if (sh.ck_bf16) INFV2_APPEND(float, true); else INFV2_APPEND(float, false); }

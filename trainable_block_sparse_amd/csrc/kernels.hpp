@@ -2,6 +2,7 @@
 // Arguments are already validated by the entry points in infv2_api.cpp.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -13,8 +14,9 @@ namespace infv2 {
 constexpr int kHeadDim = 128;     // d supported by the kernels
 constexpr int kGroup = 16;        // query heads per KV head supported by the kernels
 
-// Brackets one kernel launch with HIP events while a timing session for its
-// family (an infv2_kernel id) is open; does nothing otherwise (timing.cpp).
+// Brackets the launches made in its scope with HIP events recorded on the
+// stream while a timing session for the family (an infv2_kernel id) is open;
+// does nothing otherwise (timing.cpp).  Used for families of several kernels.
 class KernelTimer {
   public:
     KernelTimer(int kernel, hipStream_t st);
@@ -26,6 +28,24 @@ class KernelTimer {
     hipStream_t st_;
     void* stop_ = nullptr;
 };
+
+// Start and stop events for one launch of a kernel of family `kernel` on `st`
+// while a timing session for that family is open and `st` is not capturing;
+// both null otherwise (timing.cpp).
+void launch_events(int kernel, hipStream_t st, hipEvent_t* start, hipEvent_t* stop);
+
+// Launches f<<<grid, block, shmem, st>>>(args...) (arguments converted to the
+// kernel's parameter types).  While a session for `kernel` is open the launch
+// itself stamps the two events with the dispatch's begin and end, so the
+// session sees the kernel's own duration, without the gaps that events recorded
+// between launches add.
+template <typename F, typename... Args>
+inline void launch_timed(int kernel, F f, dim3 grid, dim3 block, uint32_t shmem, hipStream_t st,
+                         Args... args) {
+    hipEvent_t a = nullptr, b = nullptr;
+    launch_events(kernel, st, &a, &b);
+    hipExtLaunchKernelGGL(f, grid, block, shmem, st, a, b, 0u, args...);
+}
 
 struct Shape {
     int hq, hkv, d, m, p, s, topk, init, local;

@@ -975,40 +975,39 @@ static void dec_launch(const Shape& sh, const void* q, const void* ck, const int
         partial_c = reinterpret_cast<float2*>(ws + w.partial_c);
         lse_c = reinterpret_cast<float*>(ws + w.lse_c);
         dim3 gc(nch_c, sh.hkv, batch);
-        KernelTimer kt(INFV2_KERNEL_SELECT_LOGITS, st);
         if (sizeof(Tq) == 2)
-            sel_dec_logits_mfma<sizeof(Tck) == 2><<<gc, kLogWaves * 64, 0, st>>>(
+            launch_timed(INFV2_KERNEL_SELECT_LOGITS, sel_dec_logits_mfma<sizeof(Tck) == 2>, gc,
+                         dim3(kLogWaves * 64), 0, st,
                 static_cast<const bf16_t*>(q), cs->ckc, cs->ckc_off, kv_off, kv_lens, sh.hq, sh.hkv,
                 c, c, sh.score_scale, ncm_c, ld_c, nch_c, w.nblk_max, logits_c, partial_c, keys);
         else
-            sel_dec_logits<Tq, Tck><<<gc, 256, 0, st>>>(
+            launch_timed(INFV2_KERNEL_SELECT_LOGITS, sel_dec_logits<Tq, Tck>, gc, dim3(256), 0, st,
                 static_cast<const Tq*>(q), static_cast<const Tck*>(cs->ckc), cs->ckc_off, kv_off,
                 kv_lens, sh.hq, sh.hkv, c, c, sh.score_scale, ncm_c, ld_c, nch_c, w.nblk_max,
                 logits_c, partial_c, keys);
     }
     {
-        KernelTimer kt(INFV2_KERNEL_SELECT_LOGITS, st);
         if (sizeof(Tq) == 2)
-            sel_dec_logits_mfma<sizeof(Tck) == 2><<<ga, kLogWaves * 64, 0, st>>>(
+            launch_timed(INFV2_KERNEL_SELECT_LOGITS, sel_dec_logits_mfma<sizeof(Tck) == 2>, ga,
+                         dim3(kLogWaves * 64), 0, st,
                 static_cast<const bf16_t*>(q), ck, ck_off, kv_off, kv_lens, sh.hq, sh.hkv, sh.p,
                 sh.s, sh.score_scale, ncm, w.nc_ld, w.nchunk_a, w.nblk_max, logits, partial, keys);
         else
-            sel_dec_logits<Tq, Tck><<<ga, 256, 0, st>>>(
+            launch_timed(INFV2_KERNEL_SELECT_LOGITS, sel_dec_logits<Tq, Tck>, ga, dim3(256), 0, st,
                 static_cast<const Tq*>(q), static_cast<const Tck*>(ck), ck_off, kv_off, kv_lens,
                 sh.hq, sh.hkv, sh.p, sh.s, sh.score_scale, ncm, w.nc_ld, w.nchunk_a, w.nblk_max,
                 logits, partial, keys);
     }
     if (cs) {
-        KernelTimer kt(INFV2_KERNEL_SELECT_SCORES, st);
-        sel_dec_lse_coarse<<<dim3(sh.hkv, batch), 256, 0, st>>>(
+        launch_timed(INFV2_KERNEL_SELECT_SCORES, sel_dec_lse_coarse, dim3(sh.hkv, batch), dim3(256),
+                     0, st,
             kv_off, kv_lens, cs->ckc_off, sh.hkv, cs->coarse, nch_c, w.nchunk_a, partial_c, partial,
             lse_c);
     }
     {
-        KernelTimer kt(INFV2_KERNEL_SELECT_SCORES, st);
-        sel_dec_scores<<<gb, 256, 0, st>>>(kv_off, kv_lens, ck_off, sh.hkv, sh.m, sh.p, sh.s, ncm,
-                                           w.nc_ld, w.nchunk_a, w.nblk_max, logits, partial, lse_c,
-                                           keys);
+        launch_timed(INFV2_KERNEL_SELECT_SCORES, sel_dec_scores, gb, dim3(256), 0, st, kv_off,
+                     kv_lens, ck_off, sh.hkv, sh.m, sh.p, sh.s, ncm, w.nc_ld, w.nchunk_a,
+                     w.nblk_max, logits, partial, lse_c, keys);
     }
     KernelTimer kt(INFV2_KERNEL_SELECT_TOPK, st);
     launch_topk_dec(sh, batch, w.nblk_max, kv_off, kv_lens, keys, idx, score, st);
@@ -1046,18 +1045,18 @@ static void pre_pass1(const Shape& sh, const void* q, int r0, int nr, int64_t q_
     const size_t qrow = static_cast<size_t>(sh.hq) * kHeadDim;
     float* l = lse + static_cast<size_t>(r0) * sh.hq;
     uint32_t* kb = keys + static_cast<size_t>(r0) * sh.hkv * w.nblk_max;
-    KernelTimer kt(INFV2_KERNEL_SELECT_PREFILL, st);
     if (sizeof(Tq) == 2) {
         dim3 gm((nr + kPreRowsG - 1) / kPreRowsG, sh.hkv);
-        sel_pre_mfma<1, sizeof(Tck) == 2><<<gm, kPreThreads, 0, st>>>(
+        launch_timed(INFV2_KERNEL_SELECT_PREFILL, sel_pre_mfma<1, sizeof(Tck) == 2>, gm,
+                     dim3(kPreThreads), 0, st,
             static_cast<const bf16_t*>(q) + r0 * qrow, nr, q_start + r0, ck, ck_off, sh.hq, sh.hkv,
             sh.m, p, s, sh.score_scale, w.nblk_max, l, kb);
     } else {
         dim3 g1((nr + kRowsPre - 1) / kRowsPre, sh.hkv);
-        sel_pre_lse<Tq, Tck><<<g1, 256, 0, st>>>(static_cast<const Tq*>(q) + r0 * qrow, nr,
-                                                q_start + r0, static_cast<const Tck*>(ck), ck_off,
-                                                sh.hq, sh.hkv, p, s, sh.score_scale, w.nblk_max, l,
-                                                kb);
+        launch_timed(INFV2_KERNEL_SELECT_PREFILL, sel_pre_lse<Tq, Tck>, g1, dim3(256), 0, st,
+                     static_cast<const Tq*>(q) + r0 * qrow, nr, q_start + r0,
+                     static_cast<const Tck*>(ck), ck_off, sh.hq, sh.hkv, p, s, sh.score_scale,
+                     w.nblk_max, l, kb);
     }
 }
 
@@ -1084,21 +1083,18 @@ static void pre_launch(const Shape& sh, const void* q, int rows, int64_t q_start
         dim3 gm((rows + kPreRowsG - 1) / kPreRowsG, sh.hkv);
         const bf16_t* qq = static_cast<const bf16_t*>(q);
         {
-            KernelTimer kt(INFV2_KERNEL_SELECT_PREFILL, st);
-            sel_pre_mfma<2, kB><<<gm, kPreThreads, 0, st>>>(qq, rows, q_start, ck, ck_off, sh.hq, sh.hkv,
-                                                    sh.m, sh.p, sh.s, sh.score_scale, w.nblk_max,
-                                                    lse, keys);
+            launch_timed(INFV2_KERNEL_SELECT_PREFILL, sel_pre_mfma<2, kB>, gm, dim3(kPreThreads), 0,
+                         st, qq, rows, q_start, ck, ck_off, sh.hq, sh.hkv, sh.m, sh.p, sh.s,
+                         sh.score_scale, w.nblk_max, lse, keys);
         }
         KernelTimer kt(INFV2_KERNEL_SELECT_TOPK, st);
         launch_topk_pre(sh, rows, q_start, w.nblk_max, keys, idx, score, st);
         return;
     }
     {
-        KernelTimer kt(INFV2_KERNEL_SELECT_PREFILL, st);
-        sel_pre_scores<Tq, Tck><<<g1, 256, 0, st>>>(static_cast<const Tq*>(q), rows, q_start,
-                                                   static_cast<const Tck*>(ck), ck_off, sh.hq,
-                                                   sh.hkv, sh.m, sh.p, sh.s, sh.score_scale,
-                                                   w.nblk_max, lse, keys);
+        launch_timed(INFV2_KERNEL_SELECT_PREFILL, sel_pre_scores<Tq, Tck>, g1, dim3(256), 0, st,
+                     static_cast<const Tq*>(q), rows, q_start, static_cast<const Tck*>(ck), ck_off,
+                     sh.hq, sh.hkv, sh.m, sh.p, sh.s, sh.score_scale, w.nblk_max, lse, keys);
     }
     KernelTimer kt(INFV2_KERNEL_SELECT_TOPK, st);
     launch_topk_pre(sh, rows, q_start, w.nblk_max, keys, idx, score, st);

@@ -1,5 +1,6 @@
-// Kernel timing sessions (infv2_timing_start / infv2_timing_stop): HIP events
-// recorded on the launch stream around every launch of one kernel family.
+// Kernel timing sessions (infv2_timing_start / infv2_timing_stop): a pair of HIP
+// events per launch of one kernel family, stamped by the launch itself
+// (launch_timed) or recorded on the stream around a scope (KernelTimer).
 // Benchmark support only; the method's entry points never depend on it.
 #include <hip/hip_runtime.h>
 
@@ -30,8 +31,10 @@ hipEvent_t take_event(Session& s) {
         s.pool.pop_back();
         return e;
     }
+    // timing only: no system-scope fence, so recording the event adds no L2
+    // write-back and invalidation to the timed kernel
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     return e;
 }
 
@@ -58,6 +61,22 @@ KernelTimer::KernelTimer(int kernel, hipStream_t st) : st_(st) {
 
 KernelTimer::~KernelTimer() {
     if (stop_) hipEventRecord(static_cast<hipEvent_t>(stop_), st_);
+}
+
+void launch_events(int kernel, hipStream_t st, hipEvent_t* start, hipEvent_t* stop) {
+    *start = *stop = nullptr;
+    Session& s = session();
+    std::lock_guard<std::mutex> lk(s.mu);
+    if (s.kernel != kernel || capturing(st)) return;
+    hipEvent_t a = take_event(s), b = take_event(s);
+    if (!a || !b) {
+        if (a) s.pool.push_back(a);
+        if (b) s.pool.push_back(b);
+        return;
+    }
+    s.pairs.emplace_back(a, b);
+    *start = a;
+    *stop = b;
 }
 
 }  // namespace infv2
