@@ -67,13 +67,35 @@ class Timer:
         return e
 
 
-def kernel_times(tbs, torch, run, steps: int, families) -> dict:
-    """Live per-kernel times: the library brackets every launch of one kernel
-    family with HIP events on its launch stream while a session is open; one
-    eager pass of `steps` steps per family."""
+_SLEEP_CYCLES_PER_MS = None
+
+
+def queue_ahead(torch, ms: float) -> None:
+    """Occupy the stream for about `ms` with a spin kernel, so that the launches
+    queued behind it while it spins run back to back, as in a graph replay,
+    instead of each starting on an idle GPU after the host's launch latency."""
+    global _SLEEP_CYCLES_PER_MS
+    if _SLEEP_CYCLES_PER_MS is None:
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.cuda._sleep(1_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_MS = 1_000_000 / max(a.elapsed_time(b), 1e-3)
+    torch.cuda._sleep(int(_SLEEP_CYCLES_PER_MS * ms))
+
+
+def kernel_times(tbs, torch, run, steps: int, families, ahead_ms: float = 50.0) -> dict:
+    """Live per-kernel times: the library stamps every launch of one kernel
+    family with a pair of HIP events while a session is open; one eager pass of
+    `steps` steps per family, queued behind a spin kernel of `ahead_ms` so the
+    GPU runs the pass back to back."""
     out = {}
     for fam in families:
         torch.cuda.synchronize()
+        queue_ahead(torch, ahead_ms)
         tbs.infv2_timing_start(fam)
         try:
             for t in range(steps):

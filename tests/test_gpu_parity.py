@@ -322,6 +322,14 @@ def test_decode_configs(cfg):
     _run_decode(wl, label=f"config {cfg} decode")
 
 
+@pytest.mark.parametrize("topk,n", [(256, 20000), (1024, 70000)])
+def test_decode_split_limits(topk, n):
+    # one selected block per split at k = 256 (256 splits, small batch) and four
+    # per split at the largest k (again 256 splits): the merge's limit both ways
+    wl = _small(lens=[n], hkv=1, topk=topk, local=4, seed=29, n_planted=8)
+    _run_decode(wl, label=f"decode k={topk}")
+
+
 def test_decode_max_blocks_per_sequence():
     wl = _small(lens=[16384 * 64], hkv=1, topk=64, local=4, seed=28, n_planted=8)
     _run_decode(wl, label="decode 16384 blocks")

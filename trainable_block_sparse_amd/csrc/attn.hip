@@ -8,9 +8,10 @@
 // Both stage 64-token K/V tiles of a selected block in LDS and keep an online
 // softmax (running max, running sum, unnormalised output) per head.
 //   attn_decode_kernel   grid (split, KV head, sequence): each block handles
-//                        kBlocksPerSplit of the selected blocks and writes a
-//                        partial (max, sum, output); attn_decode_merge
-//                        combines them by their LogSumExp.
+//                        the split's selected blocks (one or four, chosen with
+//                        the workspace) and writes a partial (max, sum,
+//                        output); attn_decode_merge combines them by their
+//                        LogSumExp.
 //   attn_prefill_kernel  grid (row, KV head): all selected blocks of one row,
 //                        causal within the query's own block (t <= i).
 #include "common.hpp"
@@ -18,16 +19,22 @@
 
 namespace infv2 {
 
-constexpr int kBlocksPerSplit = 4;
 constexpr int kTok = 64;             // tokens per LDS tile
 
 AttnDecodeWs attn_decode_ws(const Shape& sh, int batch) {
     AttnDecodeWs w{};
-    w.nsplit = (sh.topk + kBlocksPerSplit - 1) / kBlocksPerSplit;
+    // four selected blocks per split, or one where four would give fewer thread
+    // blocks than the chip has compute units (small batches)
+    const int64_t wide = static_cast<int64_t>(batch) * sh.hkv * ((sh.topk + 3) / 4);
+    w.bps = (wide < kDecodeFewBlocks && sh.topk <= kDecodeMaxSplit) ? 1 : 4;
+    w.nsplit = (sh.topk + w.bps - 1) / w.bps;
+    // room for the larger of the two split counts, so the size never shrinks
+    // as the batch grows (a workspace sized for a batch serves every smaller one)
+    const size_t nalloc = sh.topk <= kDecodeMaxSplit ? sh.topk : w.nsplit;
     const size_t bg = static_cast<size_t>(batch) * sh.hkv;
     size_t off = 0;
-    w.part_o = off;   off += align256(bg * w.nsplit * kGroup * kHeadDim * sizeof(float));
-    w.part_ml = off;  off += align256(bg * w.nsplit * kGroup * sizeof(float2));
+    w.part_o = off;   off += align256(bg * nalloc * kGroup * kHeadDim * sizeof(float));
+    w.part_ml = off;  off += align256(bg * nalloc * kGroup * sizeof(float2));
     w.total = off;
     return w;
 }
@@ -133,7 +140,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int64_t* __restrict__ kv_off, const int64_t* __restrict__ kv_lens,
     const int32_t* __restrict__ idx, float* __restrict__ part_o, float2* __restrict__ part_ml,
-    int hq, int hkv, int m, int topk, int nsplit, float scale) {
+    int hq, int hkv, int m, int topk, int nsplit, int bps, float scale) {
     __shared__ AttnSmem sm;
     const int b = blockIdx.z, g = blockIdx.y, sp = blockIdx.x, t = threadIdx.x;
     const int64_t o0 = kv_off[b], cap = kv_off[b + 1] - o0;
@@ -145,8 +152,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     load_q_group(sm, q + (static_cast<size_t>(b) * hq + static_cast<size_t>(g) * kGroup) * kHeadDim);
     float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float mrun = -INFINITY, lrun = 0.f;
-    const int jb = sp * kBlocksPerSplit;
-    const int je = (jb + kBlocksPerSplit < topk) ? jb + kBlocksPerSplit : topk;
+    const int jb = sp * bps;
+    const int je = (jb + bps < topk) ? jb + bps : topk;
     attend_blocks<T>(sm, kh, vh, idx + bg * topk, jb, je, n - 1, n, m, scale, o, mrun, lrun);
 
     const int h = t >> 4, c0 = (t & 15) * 8;
@@ -191,9 +198,9 @@ hipError_t launch_attn_decode(const Shape& sh, const void* q, const void* k, con
     float2* pml = reinterpret_cast<float2*>(base + w.part_ml);
     hipError_t e;
     if (sh.io_bf16) {
-        e = launch_attn_decode_mfma(sh, q, k, v, kv_off, kv_lens, batch, idx, po, pml, w.nsplit, st);
+        e = launch_attn_decode_mfma(sh, q, k, v, kv_off, kv_lens, batch, idx, po, pml, w.nsplit, w.bps, st);
     } else {
-        launch_timed(INFV2_KERNEL_ATTN_DECODE, attn_decode_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), kv_off, kv_lens, idx, po, pml, sh.hq, sh.hkv, sh.m, sh.topk, w.nsplit, sh.attn_scale);
+        launch_timed(INFV2_KERNEL_ATTN_DECODE, attn_decode_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), kv_off, kv_lens, idx, po, pml, sh.hq, sh.hkv, sh.m, sh.topk, w.nsplit, w.bps, sh.attn_scale);
         e = hipGetLastError();
     }
     if (e != hipSuccess) return e;

@@ -4,42 +4,43 @@
 // group sharing" (the 16 heads of a group read each selected block once, which
 // is what makes the 16-row matrix tile a real contraction).
 //
-// Grid (split, KV head, sequence), 4 waves per block.  Each wave owns whole
-// 64-token pieces of selected blocks and keeps everything in registers:
+// Grid (split, KV head, sequence), W waves per block and one selected block per
+// wave: W = 4, or W = 1 when four-block splits would leave most compute units
+// idle (small batches).  Each wave owns whole 64-token pieces of its block and
+// keeps everything in registers:
 //   S^T[key][head] = K_blk (64x128) . Q^T (128x16)      16 MFMA 16x16x32
 //   V^T tiles      = V_blk . I  (identity MFMA, exact)  32 MFMA 16x16x16
 //   O^T[d][head]  += V^T (128x64) . P^T (64x16)         16 MFMA 16x16x32
 // K rows are the A operand exactly as stored (16 contiguous bytes per lane), so
 // K and V stream from HBM with 16-byte coalesced loads and never touch LDS.
 // The S^T layout puts one query head per lane column, so the online softmax
-// rescale is a per-lane scalar.  The four waves merge in LDS and each block
-// writes one partial (max, sum, output); attn_decode_merge combines the splits
-// by their LogSumExp in a second kernel.
+// rescale is a per-lane scalar.  The waves of a block merge in LDS and each
+// block writes one partial (max, sum, output); attn_decode_merge combines the
+// splits by their LogSumExp in a second kernel.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace infv2 {
 
-constexpr int kDecWaves = 4;
-constexpr int kDecBlocksPerSplit = 4;   // selected blocks per thread block (one per wave)
-
+template <int W>
 struct DecSmem {
-    float o[kDecWaves][kGroup][kHeadDim + 4];
-    float m[kDecWaves][kGroup];
-    float l[kDecWaves][kGroup];
+    float o[W][kGroup][kHeadDim + 4];
+    float m[W][kGroup];
+    float l[W][kGroup];
 };
 
-__global__ __launch_bounds__(256) void attn_decode_mfma(
+template <int W>
+__global__ __launch_bounds__(64 * W) void attn_decode_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const int64_t* __restrict__ kv_off, const int64_t* __restrict__ kv_lens,
     const int32_t* __restrict__ idx, float* __restrict__ part_o, float2* __restrict__ part_ml,
     int hq, int hkv, int m, int topk, int nsplit, float scale_log2) {
-    __shared__ DecSmem sm;
+    static_assert(W == 1 || W == 4, "one or four waves");
     const int b = blockIdx.z, g = blockIdx.y, sp = blockIdx.x, t = threadIdx.x;
     const int w = t >> 6, l = t & 63, lg = l >> 4, lc = l & 15;
     const size_t bg = static_cast<size_t>(b) * hkv + g;
-    const int e0 = sp * kDecBlocksPerSplit;
-    const int e1 = (e0 + kDecBlocksPerSplit < topk) ? e0 + kDecBlocksPerSplit : topk;
+    const int e0 = sp * W;
+    const int e1 = (e0 + W < topk) ? e0 + W : topk;
     // the wave's first block id is loaded together with the offsets (one round trip)
     const int32_t blk_first = (e0 + w < e1) ? idx[bg * topk + e0 + w] : -1;
     const int64_t o0 = kv_off[b], cap = kv_off[b + 1] - o0;
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(
         for (int h = 0; h < 2; ++h) o[c][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float mrun = -INFINITY, lrun = 0.f;
 
-    for (int e = e0 + w; e < e1; e += kDecWaves) {
+    for (int e = e0 + w; e < e1; e += W) {
         const int32_t blk = e == e0 + w ? blk_first : idx[bg * topk + e];
         if (blk < 0) continue;
         for (int sub = 0; sub < m; sub += 64) {
@@ -170,108 +171,128 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(
         }
     }
     // O^T lane layout: O[head lc][d = 32 c + 8 lg + 4 hf + r]
+    if constexpr (W == 1) {
+        float* po = part_o + ((bg * nsplit + sp) * kGroup + lc) * kHeadDim + 8 * lg;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-            *reinterpret_cast<float4*>(&sm.o[w][lc][32 * c + 8 * lg + 4 * hf]) =
-                make_float4(o[c][hf][0], o[c][hf][1], o[c][hf][2], o[c][hf][3]);
-    if (lg == 0) { sm.m[w][lc] = mrun; sm.l[w][lc] = lrun; }
-    __syncthreads();
+            for (int hf = 0; hf < 2; ++hf)
+                *reinterpret_cast<float4*>(po + 32 * c + 4 * hf) =
+                    make_float4(o[c][hf][0], o[c][hf][1], o[c][hf][2], o[c][hf][3]);
+        if (lg == 0) part_ml[(bg * nsplit + sp) * kGroup + lc] = make_float2(mrun, lrun);
+        return;
+    } else {
+        __shared__ DecSmem<W> sm;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+                *reinterpret_cast<float4*>(&sm.o[w][lc][32 * c + 8 * lg + 4 * hf]) =
+                    make_float4(o[c][hf][0], o[c][hf][1], o[c][hf][2], o[c][hf][3]);
+        if (lg == 0) { sm.m[w][lc] = mrun; sm.l[w][lc] = lrun; }
+        __syncthreads();
 
-    // merge the four waves: thread -> head h, 8 columns
-    const int h = t >> 4, c0 = (t & 15) * 8;
-    float mx = -INFINITY;
+        // merge the waves: thread -> head h, 8 columns
+        const int h = t >> 4, c0 = (t & 15) * 8;
+        float mx = -INFINITY;
 #pragma unroll
-    for (int x = 0; x < kDecWaves; ++x) mx = fmaxf(mx, sm.m[x][h]);
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
-    if (mx != -INFINITY) {
+        for (int x = 0; x < W; ++x) mx = fmaxf(mx, sm.m[x][h]);
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        float den = 0.f;
+        if (mx != -INFINITY) {
 #pragma unroll
-        for (int x = 0; x < kDecWaves; ++x) {
-            if (sm.m[x][h] == -INFINITY) continue;
-            const float wgt = exp2f(sm.m[x][h] - mx);
-            den += wgt * sm.l[x][h];
+            for (int x = 0; x < W; ++x) {
+                if (sm.m[x][h] == -INFINITY) continue;
+                const float wgt = exp2f(sm.m[x][h] - mx);
+                den += wgt * sm.l[x][h];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = fmaf(wgt, sm.o[x][h][c0 + e], acc[e]);
+                for (int e = 0; e < 8; ++e) acc[e] = fmaf(wgt, sm.o[x][h][c0 + e], acc[e]);
+            }
         }
+        float* po = part_o + ((bg * nsplit + sp) * kGroup + h) * kHeadDim + c0;
+        *reinterpret_cast<float4*>(po) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        *reinterpret_cast<float4*>(po + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        if ((t & 15) == 0) part_ml[(bg * nsplit + sp) * kGroup + h] = make_float2(mx, den);
     }
-    float* po = part_o + ((bg * nsplit + sp) * kGroup + h) * kHeadDim + c0;
-    *reinterpret_cast<float4*>(po) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    *reinterpret_cast<float4*>(po + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
-    if ((t & 15) == 0) part_ml[(bg * nsplit + sp) * kGroup + h] = make_float2(mx, den);
-
 }
 
 // Merge of the split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
-// m in log2 units.  Grid (KV head, sequence); thread -> head t/16, 8 columns.
+// m in log2 units.  Grid (query head of the group, KV head, sequence).  Thread t
+// takes the (m, l) pair of split t, and output columns 4 (t % 32) .. +3 of the
+// splits t / 32, t / 32 + 8, ...; the eight split groups are summed in LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_decode_merge(const float* __restrict__ part_o,
                                                          const float2* __restrict__ part_ml,
                                                          T* __restrict__ out, int hq, int hkv,
                                                          int nsplit) {
-    constexpr int kMaxSplit = 256;        // top-k <= 1024 at 4 blocks per split
-    __shared__ float wgt[kGroup][kMaxSplit];
-    __shared__ float inv_den[kGroup];
-    const int g = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+    constexpr int kSg = 8;                 // split groups
+    constexpr int kPre = 8;                // splits per thread loaded with the (m, l) pairs
+    static_assert(kDecodeMaxSplit <= 256, "one (m, l) pair per thread");
+    __shared__ float wgt[kDecodeMaxSplit];
+    __shared__ float red[2][4];
+    __shared__ float4 part[kSg][kHeadDim / 4];
+    const int h = blockIdx.x, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+    const int sg = t >> 5, cq = t & 31, wv = t >> 6;
     const size_t bg = static_cast<size_t>(b) * hkv + g;
-    const int h = t >> 4, c0 = (t & 15) * 8;
-    // the first kPre splits' outputs are loaded with the (m, l) pairs, in one round trip
-    constexpr int kPre = 16;
-    float4 pre[kPre][2];
+    const size_t stride = static_cast<size_t>(kGroup) * kHeadDim / 4;     // float4 per split
+    const float4* po = reinterpret_cast<const float4*>(part_o) +
+                       (bg * nsplit * kGroup + h) * (kHeadDim / 4) + cq;
+    float4 pre[kPre];
 #pragma unroll
-    for (int x = 0; x < kPre; ++x) {
-        if (x < nsplit) {
-            const float4* src = reinterpret_cast<const float4*>(part_o + ((bg * nsplit + x) * kGroup + h) * kHeadDim + c0);
-            pre[x][0] = src[0];
-            pre[x][1] = src[1];
-        }
-    }
-    {
-        const int r = t & 15;                    // 16 threads per head
-        const float2* pm = part_ml + bg * nsplit * kGroup + h;
-        float gm = -INFINITY;
-        for (int x = r; x < nsplit; x += 16) gm = fmaxf(gm, pm[static_cast<size_t>(x) * kGroup].x);
-        gm = max16(gm);
-        float den = 0.f;
-        for (int x = r; x < nsplit; x += 16) {
-            const float2 ml = pm[static_cast<size_t>(x) * kGroup];
-            const float w = (gm == -INFINITY || ml.x == -INFINITY) ? 0.f : exp2f(ml.x - gm);
-            wgt[h][x] = w;
-            den += w * ml.y;
-        }
-        den = sum16(den);
-        if (r == 0) inv_den[h] = den > 0.f ? 1.f / den : 0.f;
-    }
+    for (int i = 0; i < kPre; ++i)
+        if (sg + kSg * i < nsplit) pre[i] = po[(sg + kSg * i) * stride];
+    float2 ml = make_float2(-INFINITY, 0.f);
+    if (t < nsplit) ml = part_ml[(bg * nsplit + t) * kGroup + h];
+    float gm = wave_max(ml.x);
+    if ((t & 63) == 0) red[0][wv] = gm;
     __syncthreads();
-    float res[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    auto accum = [&](float w, const float4& a0, const float4& a1) {
-        res[0] = fmaf(w, a0.x, res[0]); res[1] = fmaf(w, a0.y, res[1]);
-        res[2] = fmaf(w, a0.z, res[2]); res[3] = fmaf(w, a0.w, res[3]);
-        res[4] = fmaf(w, a1.x, res[4]); res[5] = fmaf(w, a1.y, res[5]);
-        res[6] = fmaf(w, a1.z, res[6]); res[7] = fmaf(w, a1.w, res[7]);
+    gm = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    const float wt = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - gm);
+    if (t < nsplit) wgt[t] = wt;
+    const float den_w = wave_sum(wt * ml.y);
+    if ((t & 63) == 0) red[1][wv] = den_w;
+    __syncthreads();
+    const float den = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto add = [&](float w, const float4& a) {
+        acc.x = fmaf(w, a.x, acc.x); acc.y = fmaf(w, a.y, acc.y);
+        acc.z = fmaf(w, a.z, acc.z); acc.w = fmaf(w, a.w, acc.w);
     };
 #pragma unroll
-    for (int x = 0; x < kPre; ++x)
-        if (x < nsplit) accum(wgt[h][x], pre[x][0], pre[x][1]);
+    for (int i = 0; i < kPre; ++i)
+        if (sg + kSg * i < nsplit) add(wgt[sg + kSg * i], pre[i]);
 #pragma unroll 4
-    for (int x = kPre; x < nsplit; ++x) {
-        const float4* src = reinterpret_cast<const float4*>(part_o + ((bg * nsplit + x) * kGroup + h) * kHeadDim + c0);
-        accum(wgt[h][x], src[0], src[1]);
-    }
-    const float inv = inv_den[h];
-    T* dst = out + (static_cast<size_t>(b) * hq + static_cast<size_t>(g) * kGroup + h) * kHeadDim + c0;
+    for (int x = sg + kSg * kPre; x < nsplit; x += kSg) add(wgt[x], po[x * stride]);
+    part[sg][cq] = acc;
+    __syncthreads();
+    if (t < kHeadDim / 4) {
+        float4 r = part[0][t];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) io<T>::store(dst + e, res[e] * inv);
+        for (int j = 1; j < kSg; ++j) {
+            const float4 a = part[j][t];
+            r.x += a.x; r.y += a.y; r.z += a.z; r.w += a.w;
+        }
+        const float inv = den > 0.f ? 1.f / den : 0.f;
+        T* dst = out + (static_cast<size_t>(b) * hq + static_cast<size_t>(g) * kGroup + h) * kHeadDim + 4 * t;
+        io<T>::store(dst + 0, r.x * inv);
+        io<T>::store(dst + 1, r.y * inv);
+        io<T>::store(dst + 2, r.z * inv);
+        io<T>::store(dst + 3, r.w * inv);
+    }
 }
 
 hipError_t launch_attn_decode_mfma(const Shape& sh, const void* q, const void* k, const void* v,
                                    const int64_t* kv_off, const int64_t* kv_lens, int batch,
                                    const int32_t* idx, float* part_o, float2* part_ml, int nsplit,
-                                   hipStream_t st) {
+                                   int bps, hipStream_t st) {
     dim3 grid(nsplit, sh.hkv, batch);
     const float scale_log2 = sh.attn_scale * 1.4426950408889634f;
-    launch_timed(INFV2_KERNEL_ATTN_DECODE, attn_decode_mfma, grid, dim3(256), 0, st,
+    if (bps == 1)
+        launch_timed(INFV2_KERNEL_ATTN_DECODE, attn_decode_mfma<1>, grid, dim3(64), 0, st,
+            static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
+            kv_off, kv_lens, idx, part_o, part_ml, sh.hq, sh.hkv, sh.m, sh.topk, nsplit, scale_log2);
+    else
+        launch_timed(INFV2_KERNEL_ATTN_DECODE, attn_decode_mfma<4>, grid, dim3(256), 0, st,
         static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
         kv_off, kv_lens, idx, part_o, part_ml, sh.hq, sh.hkv, sh.m, sh.topk, nsplit, scale_log2);
     return hipGetLastError();
@@ -279,7 +300,7 @@ hipError_t launch_attn_decode_mfma(const Shape& sh, const void* q, const void* k
 
 hipError_t launch_attn_decode_merge(const Shape& sh, const float* part_o, const float2* part_ml,
                                     void* out, int batch, int nsplit, hipStream_t st) {
-    dim3 grid(sh.hkv, batch);
+    dim3 grid(kGroup, sh.hkv, batch);
     if (sh.io_bf16)
         launch_timed(INFV2_KERNEL_ATTN_MERGE, attn_decode_merge<bf16_t>, grid, dim3(256), 0, st,
                      part_o, part_ml, static_cast<bf16_t*>(out), sh.hq, sh.hkv, nsplit);

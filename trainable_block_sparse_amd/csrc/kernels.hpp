@@ -68,9 +68,13 @@ struct SelectPrefillWs {
 };
 SelectPrefillWs select_prefill_ws(const Shape& sh, int rows, int64_t max_len);
 
+// Decode attention: the selected blocks are cut into nsplit splits of bps
+// blocks (1 or 4), each giving one partial (max, sum, output) per head.
+constexpr int kDecodeFewBlocks = 256;   // below this many 4-block splits, 1-block splits
+constexpr int kDecodeMaxSplit = 256;    // splits the merge kernel takes
 struct AttnDecodeWs {
     size_t part_o, part_ml, total;
-    int nsplit;
+    int nsplit, bps;
 };
 AttnDecodeWs attn_decode_ws(const Shape& sh, int batch);
 
@@ -108,7 +112,7 @@ hipError_t launch_attn_decode(const Shape& sh, const void* q, const void* k, con
 hipError_t launch_attn_decode_mfma(const Shape& sh, const void* q, const void* k, const void* v,
                                    const int64_t* kv_off, const int64_t* kv_lens, int batch,
                                    const int32_t* idx, float* part_o, float2* part_ml, int nsplit,
-                                   hipStream_t st);
+                                   int bps, hipStream_t st);
 hipError_t launch_attn_decode_merge(const Shape& sh, const float* part_o, const float2* part_ml,
                                     void* out, int batch, int nsplit, hipStream_t st);
 
