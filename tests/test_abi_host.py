@@ -70,6 +70,18 @@ def test_workspace_sizes_grow_with_the_problem(lib):
     assert tbs.infv2_workspace_bytes(cfg, tbs.OP_SELECT_PREFILL, 4096, 1, 32768) >= 4096 * 2 * 512 * 4
 
 
+@pytest.mark.parametrize("topk,hkv", [(64, 2), (8, 1), (256, 1), (1024, 4)])
+def test_decode_attention_workspace_never_shrinks_with_the_batch(lib, topk, hkv):
+    # the split of the selected blocks (one or four per thread block) depends on
+    # the batch; a workspace sized for a batch must still serve every smaller one
+    cfg = tbs.Config(num_q_heads=16 * hkv, num_kv_heads=hkv, topk=topk, local_blocks=2)
+    sizes = [tbs.infv2_workspace_bytes(cfg, tbs.OP_ATTN_DECODE, b, b, 131072) for b in range(1, 65)]
+    assert all(x <= y for x, y in zip(sizes, sizes[1:])), sizes
+    # room for one partial (16 heads x d fp32 + the (max, sum) pairs) per split
+    per_split = 16 * 128 * 4
+    assert sizes[0] >= hkv * min(topk, 256 if topk <= 256 else (topk + 3) // 4) * per_split
+
+
 def _c(cfg):
     return ctypes.byref(cfg.to_c())
 
