@@ -58,7 +58,7 @@ __device__ __forceinline__ float key_to_score(uint32_t k) {
 }
 
 // ---------------------------------------------------------------- method arithmetic helpers
-__device__ __forceinline__ int64_t num_kernels(int64_t n, int p, int s) {
+__host__ __device__ __forceinline__ int64_t num_kernels(int64_t n, int p, int s) {
     return n < p ? 0 : (n - p) / s + 1;
 }
 
@@ -112,6 +112,19 @@ __device__ __forceinline__ uint32_t pack_exact(float lo, float hi) {
 // LDS byte offset of a __shared__ object: the low half of its generic address
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+// Direct global->LDS load of 16 B per lane (lane i writes bytes 16 i .. 16 i + 15
+// from `lds`, which is wave-uniform).  Issued by hand: the compiler then knows
+// nothing of the LDS write and does not wait for every outstanding load before
+// each LDS read (it cannot tell the stages of a ring apart).  The caller waits
+// for the load (s_waitcnt vmcnt) and synchronises before reading the data.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+    asm volatile("global_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory");
+}
+// wait for every outstanding global access of this wave, then a block barrier
+__device__ __forceinline__ void dma_wait_barrier() {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 }
 // two floats -> packed bf16 pair, round to nearest even (one paired conversion)
 __device__ __forceinline__ uint32_t pack_rne(float lo, float hi) {

@@ -63,7 +63,7 @@ size_t ws_bytes_for(const infv2_config* c, int32_t op, int32_t rows, int32_t bat
         case INFV2_OP_ATTN_PREFILL: return infv2::attn_prefill_ws_bytes(sh, max_len);
         case INFV2_OP_ATTN_PREFILL_BWD: return rows > 0 ? infv2::bwd_ws(sh, rows, max_len).total : 0;
         case INFV2_OP_SELECT_COARSE_DECODE: return infv2::select_decode_ws(sh, batch, max_len).total_coarse;
-        case INFV2_OP_SELECT_COARSE_PREFILL: return infv2::select_prefill_ws(sh, rows, max_len).total;
+        case INFV2_OP_SELECT_COARSE_PREFILL: return infv2::select_prefill_ws(sh, rows, max_len).total_coarse;
         default: return 0;
     }
 }

@@ -65,6 +65,10 @@ SelectDecodeWs select_decode_ws(const Shape& sh, int batch, int64_t max_len);
 struct SelectPrefillWs {
     size_t lse, keys, total;
     int64_t nblk_max;
+    // fp32 compressed keys: their hi / lo bf16 rows, [2][Hkv][ld][d], for the
+    // fine kernels (hl, ld) and, in the coarse-LSE call, the coarse ones (hlc, ldc)
+    size_t hl, hlc, total_coarse;
+    int64_t ld, ldc;
 };
 SelectPrefillWs select_prefill_ws(const Shape& sh, int rows, int64_t max_len);
 

@@ -84,15 +84,6 @@ __device__ inline int build_union(UnionSmemT<kRows, kCap>& sm, const int32_t* __
 
 constexpr int kPB = 64;           // KV block size of the matrix-core prefill kernels
 
-// Direct global->LDS load of 16 B per lane (lane i writes bytes 16 i .. 16 i + 15
-// from `lds`, which is wave-uniform).  Issued by hand: the compiler then knows
-// nothing of the LDS write and does not wait for every outstanding load before
-// each LDS read (it cannot tell the stages of a ring apart).  The caller waits
-// for the load (s_waitcnt vmcnt) and synchronises before reading the data.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-    asm volatile("global_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
-                 : "memory");
-}
 // LDS transpose read of 8 bytes per lane: inside each group of 16 lanes, lane i
 // receives as its element e (e = 0..3) halfword i % 4 of the 8 bytes that lane
 // 4 e + i / 4 addresses.
@@ -104,10 +95,6 @@ __device__ __forceinline__ uint2 lds_read_tr16(uint32_t byte_offset) {
     return __builtin_bit_cast(uint2, v);
 }
 
-// wait for every outstanding global load of this wave, then a block barrier
-__device__ __forceinline__ void dma_wait_barrier() {
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // K / V tile: 64 keys x 16 chunks of 16 B; chunk c of key r sits at c ^ (r & 15),
 // which makes 16-lane 16-byte column reads conflict-free.  Transposed operands

@@ -94,7 +94,19 @@ SelectPrefillWs select_prefill_ws(const Shape& sh, int rows, int64_t max_len) {
     size_t off = 0;
     w.lse = off;  off += align256(static_cast<size_t>(rows) * sh.hq * sizeof(float));
     w.keys = off; off += align256(static_cast<size_t>(rows) * sh.hkv * w.nblk_max * sizeof(uint32_t));
-    w.total = off;
+    if (!sh.ck_bf16) {
+        // every kernel a row below max_len can see; a coarse kernel (size and
+        // stride >= p) is at most one per p tokens
+        w.ld = num_kernels(max_len, sh.p, sh.s);
+        w.ld = w.ld < 1 ? 1 : w.ld;
+        w.ldc = max_len / sh.p + 1;
+        w.hl = off;   off += align256(static_cast<size_t>(2) * sh.hkv * w.ld * kHeadDim * sizeof(bf16_t));
+        w.total = off;
+        w.hlc = off;  off += align256(static_cast<size_t>(2) * sh.hkv * w.ldc * kHeadDim * sizeof(bf16_t));
+        w.total_coarse = off;
+    } else {
+        w.total = w.total_coarse = off;
+    }
     return w;
 }
 
@@ -613,16 +625,49 @@ constexpr int kPreTileK = 64;
 constexpr int kPreWaves = 8;                          // wave w: rows w + 8 i
 constexpr int kPreRW = kPreRowsG / kPreWaves;         // query rows per wave
 constexpr int kPreThreads = kPreWaves * 64;
-constexpr int kPreLoads = kPreTileK * 16 / kPreThreads;   // 16-byte chunks per thread and tile
+constexpr int kPreLoads = kPreTileK * 16 / kPreThreads;   // 16-byte loads per thread, tile and part
 constexpr float kPreMrInit = -1e30f;                  // pass 1 reference before any visible logit
+
+// fp32 compressed keys -> the bf16 pair the scoring products use: hi = x rounded
+// to bf16, lo = (x - hi) rounded to bf16, so that hi . q + lo . q carries x to
+// about 16 significant bits.  Written once per call as [part][KV head][ld][d]
+// (part 0 hi, 1 lo) for kernels 0 .. nk - 1 (those the call's rows see), instead
+// of by every thread block that stages a tile.  Thread -> one 8-value chunk.
+__global__ __launch_bounds__(256) void ck_split_hilo(const float* __restrict__ ck,
+                                                     const int64_t* __restrict__ ck_off, int hkv,
+                                                     int64_t nk, int64_t ld, bf16_t* __restrict__ hl) {
+    const int g = blockIdx.y;
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t ccap = ck_off[1] - ck_off[0];
+    const int64_t r = e >> 4;
+    const int c = static_cast<int>(e & 15);
+    if (r >= nk || r >= ccap) return;
+    const float* src = ck + (ck_off[0] * hkv + static_cast<int64_t>(g) * ccap + r) * kHeadDim + 8 * c;
+    const float4 a = *reinterpret_cast<const float4*>(src);
+    const float4 b = *reinterpret_cast<const float4*>(src + 4);
+    const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float hi[8], lo[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        hi[i] = bf16_to_f32(f32_to_bf16(x[i]));
+        lo[i] = x[i] - hi[i];
+    }
+    const int64_t o = (static_cast<int64_t>(g) * ld + r) * kHeadDim + 8 * c;
+    *reinterpret_cast<uint4*>(hl + o) =
+        make_uint4(pack_exact(hi[0], hi[1]), pack_exact(hi[2], hi[3]), pack_exact(hi[4], hi[5]), pack_exact(hi[6], hi[7]));
+    *reinterpret_cast<uint4*>(hl + static_cast<int64_t>(hkv) * ld * kHeadDim + o) =
+        make_uint4(pack_rne(lo[0], lo[1]), pack_rne(lo[2], lo[3]), pack_rne(lo[4], lo[5]), pack_rne(lo[6], lo[7]));
+}
 
 template <int kPass, bool kCkBf16>
 __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
     const bf16_t* __restrict__ q, int rows, int64_t q_start, const void* __restrict__ ck,
-    const int64_t* __restrict__ ck_off, int hq, int hkv, int m, int p, int s, float score_scale,
-    int64_t nblk_max, float* __restrict__ lse, uint32_t* __restrict__ keys) {
-    __shared__ __attribute__((aligned(16))) bf16_t ck_hi[kPreTileK * kHeadDim];
-    __shared__ __attribute__((aligned(16))) bf16_t ck_lo[kCkBf16 ? 8 : kPreTileK * kHeadDim];
+    const int64_t* __restrict__ ck_off, const bf16_t* __restrict__ hl, int64_t ld, int hq,
+    int hkv, int m, int p, int s, float score_scale, int64_t nblk_max, float* __restrict__ lse,
+    uint32_t* __restrict__ keys) {
+    // two stages of 64-kernel tiles: bf16 keys, or the hi and lo parts of fp32 keys
+    __shared__ __attribute__((aligned(16))) bf16_t ck_hi[2][kPreTileK * kHeadDim];
+    __shared__ __attribute__((aligned(16))) bf16_t ck_lo[kCkBf16 ? 1 : 2][kCkBf16 ? 8 : kPreTileK * kHeadDim];
     __shared__ float rs[kPreRowsG][kPreTileK + 1];   // +1: column reads across rows conflict-free
     __shared__ int32_t vrow[kPreRowsG];              // kernels visible to each row
     __shared__ int32_t bk[kPreThreads][2];                   // pass 2: tile-relative kernel range per block
@@ -630,11 +675,15 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
     const int w = t >> 6, l = t & 63, lg = l >> 4, lc = l & 15;
     const int r0 = blockIdx.x * kPreRowsG;
     const int64_t ccap = ck_off[1] - ck_off[0];
-    const int64_t cbase = (ck_off[0] * hkv + static_cast<int64_t>(g) * ccap) * kHeadDim;
+    // kernel rows of this KV head: the bf16 keys as stored, or the hi / lo rows
+    // that ck_split_hilo wrote for fp32 keys ([part][KV head][ld][d])
+    const bf16_t* src_hi = kCkBf16 ? static_cast<const bf16_t*>(ck) + (ck_off[0] * hkv + static_cast<int64_t>(g) * ccap) * kHeadDim
+                                   : hl + static_cast<int64_t>(g) * ld * kHeadDim;
+    const bf16_t* src_lo = kCkBf16 ? nullptr : hl + (static_cast<int64_t>(hkv) + g) * ld * kHeadDim;
     constexpr float kLog2e = 1.4426950408889634f;
     const float zscale = score_scale * kLog2e;
 
-    int64_t vis[kPreRW];
+    int32_t vis[kPreRW];              // kernels visible to the row (counts < 2^31)
     bf16x8_t qf[kPreRW][4];
     int64_t vmax = 0;                     // the group's last valid row sees the most kernels
     {
@@ -648,7 +697,7 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
     for (int i = 0; i < kPreRW; ++i) {
         const int row = r0 + w + kPreWaves * i;
         int64_t v = row < rows ? num_kernels(q_start + row + 1, p, s) : 0;
-        vis[i] = v < ccap ? v : ccap;
+        vis[i] = static_cast<int32_t>(v < ccap ? v : ccap);
         const int rr = row < rows ? row : rows - 1;
         const bf16_t* qrow = q + (static_cast<size_t>(rr) * hq + static_cast<size_t>(g) * kGroup + lc) * kHeadDim;
 #pragma unroll
@@ -685,73 +734,75 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
         }
     }
 
-    // compressed-key tile loads run one tile ahead, in registers: the loads of
-    // tile t+1 are in flight while tile t is computed from LDS
-    uint4 pk[kPreLoads];                  // bf16 keys: one 16-byte chunk per x
-    float4 pa[kPreLoads], pb[kPreLoads];          // fp32 keys: two 16-byte halves per x
-    auto fetch = [&](int64_t jt) {
+    // Tiles stream through LDS with direct global->LDS loads, one tile ahead.
+    // Load x of wave w fills 1 KB: tile rows 4 (kPreLoads w + x) .. + 3, lane l
+    // writing stored chunk l % 16 of its row, which holds source chunk
+    // (l % 16) ^ (row % 16) (chunk c of kernel r sits at c ^ (r & 15)).
+    int dr[kPreLoads], dc[kPreLoads];
+#pragma unroll
+    for (int x = 0; x < kPreLoads; ++x) {
+        const int e = (kPreLoads * w + x) * 64 + l;
+        dr[x] = e >> 4;
+        dc[x] = (e & 15) ^ (dr[x] & 15);
+    }
+    auto issue = [&](int64_t jt, int stg) {
 #pragma unroll
         for (int x = 0; x < kPreLoads; ++x) {
-            const int e = t + kPreThreads * x, r = e >> 4, c = e & 15;
-            if (kCkBf16) {
-                const bf16_t* src = static_cast<const bf16_t*>(ck) + cbase;
-                pk[x] = (jt + r < vmax) ? ldg16(src + (jt + r) * kHeadDim + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
-            } else {
-                const float* src = static_cast<const float*>(ck) + cbase;
-                pa[x] = make_float4(0.f, 0.f, 0.f, 0.f);
-                pb[x] = pa[x];
-                if (jt + r < vmax) {
-                    pa[x] = *reinterpret_cast<const float4*>(src + (jt + r) * kHeadDim + 8 * c);
-                    pb[x] = *reinterpret_cast<const float4*>(src + (jt + r) * kHeadDim + 8 * c + 4);
-                }
-            }
+            int64_t r = jt + dr[x];
+            r = r < vmax ? r : vmax - 1;         // rows past the last visible kernel are never read
+            const int64_t so = r * kHeadDim + 8 * dc[x];
+            const int dst = (kPreLoads * w + x) * 512;          // bf16 elements (1 KB)
+            dma16(src_hi + so, lds_offset(&ck_hi[stg][dst]));
+            if (!kCkBf16) dma16(src_lo + so, lds_offset(&ck_lo[stg][dst]));
         }
     };
-    if (vmax > 0) fetch(0);
-    for (int64_t j0 = 0; j0 < vmax; j0 += kPreTileK) {
-        __syncthreads();
-        // stage 64 kernels; chunk c of kernel r at c ^ (r & 15)
+    // make the compiler wait for the q fragments and pass 2's normalisers here,
+    // where it sees a use: otherwise it keeps them pending into the tile loop and
+    // waits there for every outstanding load, the next tile's included
 #pragma unroll
-        for (int x = 0; x < kPreLoads; ++x) {
-            const int e = t + kPreThreads * x, r = e >> 4, c = e & 15;
-            const int off = r * kHeadDim + 8 * (c ^ (r & 15));
-            if (kCkBf16) {
-                *reinterpret_cast<uint4*>(&ck_hi[off]) = pk[x];
-            } else {
-                const float xv[8] = {pa[x].x, pa[x].y, pa[x].z, pa[x].w, pb[x].x, pb[x].y, pb[x].z, pb[x].w};
-                float hi[8], lo[8];
+    for (int i = 0; i < kPreRW; ++i) {
 #pragma unroll
-                for (int e8 = 0; e8 < 8; ++e8) {
-                    hi[e8] = bf16_to_f32(f32_to_bf16(xv[e8]));
-                    lo[e8] = xv[e8] - hi[e8];
-                }
-                *reinterpret_cast<uint4*>(&ck_hi[off]) =
-                    make_uint4(pack_exact(hi[0], hi[1]), pack_exact(hi[2], hi[3]), pack_exact(hi[4], hi[5]), pack_exact(hi[6], hi[7]));
-                *reinterpret_cast<uint4*>(&ck_lo[off]) =
-                    make_uint4(pack_rne(lo[0], lo[1]), pack_rne(lo[2], lo[3]), pack_rne(lo[4], lo[5]), pack_rne(lo[6], lo[7]));
-            }
-        }
-        __syncthreads();
-        if (j0 + kPreTileK < vmax) fetch(j0 + kPreTileK);
+        for (int ks = 0; ks < 4; ++ks) asm volatile("" :: "v"(qf[i][ks]));
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            f32x4_t z[kPreRW];
-#pragma unroll
-            for (int i = 0; i < kPreRW; ++i) z[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < 4; ++r) asm volatile("" :: "v"(mr[i][r]));
+    }
+    if (vmax > 0) issue(0, 0);
+    int stg = 0;
+    for (int64_t j0 = 0; j0 < vmax; j0 += kPreTileK, stg ^= 1) {
+        // tile j0 landed (the only loads in flight) and every wave is done with
+        // the previous tile, whose stage now takes the next one
+        dma_wait_barrier();
+        if (j0 + kPreTileK < vmax) issue(j0 + kPreTileK, stg ^ 1);
+        // B fragments of a 16-kernel column tile: lane holds CK[kernel 16 nt + lc]
+        // [32 ks + 8 lg ..], hi and lo parts, all eight LDS reads issued together
+        uint4 fh[1][4], fl[1][4];
+        auto frags = [&](int nt, int buf) {
             const int kr = 16 * nt + lc;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int off = kr * kHeadDim + 8 * ((4 * ks + lg) ^ (kr & 15));
-                const bf16x8_t bh = as_bf16x8(*reinterpret_cast<const uint4*>(&ck_hi[off]));
+                fh[buf][ks] = *reinterpret_cast<const uint4*>(&ck_hi[stg][off]);
+                if (!kCkBf16) fl[buf][ks] = *reinterpret_cast<const uint4*>(&ck_lo[stg][off]);
+            }
+        };
 #pragma unroll
-                for (int i = 0; i < kPreRW; ++i) z[i] = mfma32(qf[i][ks], bh, z[i]);
+        for (int nt = 0; nt < 4; ++nt) {
+            const int cur = 0;
+            frags(nt, cur);
+            f32x4_t z[kPreRW];
+#pragma unroll
+            for (int i = 0; i < kPreRW; ++i) z[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+                for (int i = 0; i < kPreRW; ++i) z[i] = mfma32(qf[i][ks], as_bf16x8(fh[cur][ks]), z[i]);
                 if (!kCkBf16) {
-                    const bf16x8_t bl = as_bf16x8(*reinterpret_cast<const uint4*>(&ck_lo[off]));
 #pragma unroll
-                    for (int i = 0; i < kPreRW; ++i) z[i] = mfma32(qf[i][ks], bl, z[i]);
+                    for (int i = 0; i < kPreRW; ++i) z[i] = mfma32(qf[i][ks], as_bf16x8(fl[cur][ks]), z[i]);
                 }
             }
-            const int64_t jk = j0 + kr;          // this lane's kernel column
+            const int kr = 16 * nt + lc;
+            const int32_t jk = static_cast<int32_t>(j0) + kr;   // this lane's kernel column
 #pragma unroll
             for (int i = 0; i < kPreRW; ++i) {
                 const bool ok = jk < vis[i];
@@ -762,10 +813,21 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
                     // d = logit - reference in one FMA; masked logits are -inf
                     float d[4];
                     bool over = false;
+                    // tiles the row sees whole (all but its last) skip the mask
+                    const bool full = __builtin_amdgcn_readfirstlane(
+                        static_cast<int>(static_cast<int32_t>(j0) + kPreTileK <= vis[i])) != 0;
+                    if (full) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        d[r] = ok ? fmaf(z[i][r], zscale, -mr[i][r]) : -INFINITY;
-                        over |= d[r] > 8.f;
+                        for (int r = 0; r < 4; ++r) {
+                            d[r] = fmaf(z[i][r], zscale, -mr[i][r]);
+                            over |= d[r] > 8.f;
+                        }
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            d[r] = ok ? fmaf(z[i][r], zscale, -mr[i][r]) : -INFINITY;
+                            over |= d[r] > 8.f;
+                        }
                     }
                     if (__any(over)) {
 #pragma unroll
@@ -1037,10 +1099,21 @@ hipError_t launch_select_decode(const Shape& sh, const void* q, const void* ck,
 
 // Pass 1 (per-head LogSumExp and clearing the rows' block keys) for rows
 // [r0, r0 + nr) of the call, over compressed keys `ck` of kernel size p, stride s.
+// fp32 keys of kernels 0 .. nk - 1 -> their hi / lo rows (ck_split_hilo)
+static void split_hilo(const Shape& sh, const void* ck, const int64_t* ck_off, int64_t nk,
+                       int64_t ld, bf16_t* hl, hipStream_t st) {
+    nk = nk < ld ? nk : ld;
+    if (nk <= 0) return;
+    const dim3 grid(static_cast<unsigned>((nk * 16 + 255) / 256), sh.hkv);
+    launch_timed(INFV2_KERNEL_SELECT_PREFILL, ck_split_hilo, grid, dim3(256), 0, st,
+                 static_cast<const float*>(ck), ck_off, sh.hkv, nk, ld, hl);
+}
+
 template <typename Tq, typename Tck>
 static void pre_pass1(const Shape& sh, const void* q, int r0, int nr, int64_t q_start,
-                      const void* ck, const int64_t* ck_off, int p, int s,
-                      const SelectPrefillWs& w, float* lse, uint32_t* keys, hipStream_t st) {
+                      const void* ck, const int64_t* ck_off, int p, int s, const bf16_t* hl,
+                      int64_t ld, const SelectPrefillWs& w, float* lse, uint32_t* keys,
+                      hipStream_t st) {
     if (nr <= 0) return;
     const size_t qrow = static_cast<size_t>(sh.hq) * kHeadDim;
     float* l = lse + static_cast<size_t>(r0) * sh.hq;
@@ -1049,8 +1122,8 @@ static void pre_pass1(const Shape& sh, const void* q, int r0, int nr, int64_t q_
         dim3 gm((nr + kPreRowsG - 1) / kPreRowsG, sh.hkv);
         launch_timed(INFV2_KERNEL_SELECT_PREFILL, sel_pre_mfma<1, sizeof(Tck) == 2>, gm,
                      dim3(kPreThreads), 0, st,
-            static_cast<const bf16_t*>(q) + r0 * qrow, nr, q_start + r0, ck, ck_off, sh.hq, sh.hkv,
-            sh.m, p, s, sh.score_scale, w.nblk_max, l, kb);
+            static_cast<const bf16_t*>(q) + r0 * qrow, nr, q_start + r0, ck, ck_off, hl, ld, sh.hq,
+            sh.hkv, sh.m, p, s, sh.score_scale, w.nblk_max, l, kb);
     } else {
         dim3 g1((nr + kRowsPre - 1) / kRowsPre, sh.hkv);
         launch_timed(INFV2_KERNEL_SELECT_PREFILL, sel_pre_lse<Tq, Tck>, g1, dim3(256), 0, st,
@@ -1067,16 +1140,25 @@ static void pre_launch(const Shape& sh, const void* q, int rows, int64_t q_start
     dim3 g1((rows + kRowsPre - 1) / kRowsPre, sh.hkv);
     float* lse = reinterpret_cast<float*>(ws + w.lse);
     uint32_t* keys = reinterpret_cast<uint32_t*>(ws + w.keys);
+    // matrix-core passes over fp32 keys read their hi / lo rows, made once here
+    constexpr bool kSplit = sizeof(Tq) == 2 && sizeof(Tck) == 4;
+    bf16_t* hl = kSplit ? reinterpret_cast<bf16_t*>(ws + w.hl) : nullptr;
+    bf16_t* hlc = kSplit && cs ? reinterpret_cast<bf16_t*>(ws + w.hlc) : nullptr;
+    if (kSplit) split_hilo(sh, ck, ck_off, num_kernels(q_start + rows, sh.p, sh.s), w.ld, hl, st);
     if (cs) {
         // rows that see a coarse kernel take pass 1 over the coarse kernels; the
         // few before the first one (dense rows) keep the exact normaliser
         int64_t nf = static_cast<int64_t>(cs->coarse) - 1 - q_start;
         nf = nf < 0 ? 0 : (nf > rows ? rows : nf);
-        pre_pass1<Tq, Tck>(sh, q, 0, static_cast<int>(nf), q_start, ck, ck_off, sh.p, sh.s, w, lse, keys, st);
+        if (kSplit)
+            split_hilo(sh, cs->ckc, cs->ckc_off, num_kernels(q_start + rows, cs->coarse, cs->coarse),
+                       w.ldc, hlc, st);
+        pre_pass1<Tq, Tck>(sh, q, 0, static_cast<int>(nf), q_start, ck, ck_off, sh.p, sh.s, hl, w.ld,
+                           w, lse, keys, st);
         pre_pass1<Tq, Tck>(sh, q, static_cast<int>(nf), rows - static_cast<int>(nf), q_start, cs->ckc,
-                           cs->ckc_off, cs->coarse, cs->coarse, w, lse, keys, st);
+                           cs->ckc_off, cs->coarse, cs->coarse, hlc, w.ldc, w, lse, keys, st);
     } else {
-        pre_pass1<Tq, Tck>(sh, q, 0, rows, q_start, ck, ck_off, sh.p, sh.s, w, lse, keys, st);
+        pre_pass1<Tq, Tck>(sh, q, 0, rows, q_start, ck, ck_off, sh.p, sh.s, hl, w.ld, w, lse, keys, st);
     }
     if (sizeof(Tq) == 2) {
         constexpr bool kB = sizeof(Tck) == 2;
@@ -1084,8 +1166,8 @@ static void pre_launch(const Shape& sh, const void* q, int rows, int64_t q_start
         const bf16_t* qq = static_cast<const bf16_t*>(q);
         {
             launch_timed(INFV2_KERNEL_SELECT_PREFILL, sel_pre_mfma<2, kB>, gm, dim3(kPreThreads), 0,
-                         st, qq, rows, q_start, ck, ck_off, sh.hq, sh.hkv, sh.m, sh.p, sh.s,
-                         sh.score_scale, w.nblk_max, lse, keys);
+                         st, qq, rows, q_start, ck, ck_off, hl, w.ld, sh.hq, sh.hkv, sh.m, sh.p,
+                         sh.s, sh.score_scale, w.nblk_max, lse, keys);
         }
         KernelTimer kt(INFV2_KERNEL_SELECT_TOPK, st);
         launch_topk_pre(sh, rows, q_start, w.nblk_max, keys, idx, score, st);
