@@ -19,6 +19,7 @@
 // fence inside a kernel costs a write-back and invalidation of the whole L2 of
 // the XCD on gfx950, once per block.
 // Prefill (rows of one sequence, causal visibility per row):
+//   ck_split_hilo   fp32 compressed keys -> hi / lo bf16 rows, once per call.
 //   sel_pre_mfma<1> 16 rows per block on the matrix cores: per-head LogSumExp.
 //   sel_pre_mfma<2> the same logits again: group score, block max.
 //   (sel_pre_lse / sel_pre_scores: the vector-ALU versions for fp32 queries)
@@ -612,8 +613,9 @@ __global__ __launch_bounds__(256) void sel_pre_scores(
 
 // ------------------------------------------------------------------ prefill passes on the matrix cores
 // Thread block = 16 query rows of one KV head (8 waves, wave w: rows w, w + 8),
-// streaming the compressed keys in tiles of 64 kernels through LDS (bf16; fp32
-// keys split into hi + lo tiles at staging).  Z[head][kernel] = Q . CK^T with Q
+// streaming the compressed keys in tiles of 64 kernels through two LDS stages
+// by direct global->LDS loads (bf16 keys as stored; fp32 keys as the hi + lo
+// bf16 rows ck_split_hilo writes once per call).  Z[head][kernel] = Q . CK^T with Q
 // as the A operand (lane: head lc, 8 consecutive d) and the CK tile as B, so
 // each lane holds 4 heads (4 lg + r) of one kernel column (lc) per 16x16 tile.
 //   pass 1: per-lane online (max, sum) of 2^(log2e z) per head, folded over
