@@ -809,33 +809,24 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
             for (int i = 0; i < kPreRW; ++i) {
                 const bool ok = jk < vis[i];
                 if (kPass == 1) {
-                    // running (max, sum) with a lazy max: the reference moves only
-                    // when some lane's logit exceeds it by more than 2^8, so the
-                    // common path is one exp per logit and no divergence
-                    // d = logit - reference in one FMA; masked logits are -inf
+                    // running (max, sum) with a lazy max: the reference of a head
+                    // (shared by its 16 kernel-column lanes) moves only when some
+                    // logit exceeds it by more than 2^8, so the common path is one
+                    // FMA, one exp and one add per logit and no divergence.
+                    // d = logit - reference; masked logits are -inf
                     float d[4];
-                    bool over = false;
-                    // tiles the row sees whole (all but its last) skip the mask
-                    const bool full = __builtin_amdgcn_readfirstlane(
-                        static_cast<int>(static_cast<int32_t>(j0) + kPreTileK <= vis[i])) != 0;
-                    if (full) {
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            d[r] = fmaf(z[i][r], zscale, -mr[i][r]);
-                            over |= d[r] > 8.f;
-                        }
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            d[r] = ok ? fmaf(z[i][r], zscale, -mr[i][r]) : -INFINITY;
-                            over |= d[r] > 8.f;
-                        }
-                    }
-                    if (__any(over)) {
+                    for (int r = 0; r < 4; ++r)
+                        d[r] = ok ? fmaf(z[i][r], zscale, -mr[i][r]) : -INFINITY;
+                    if (__builtin_amdgcn_ballot_w64(d[0] > 8.f || d[1] > 8.f || d[2] > 8.f || d[3] > 8.f) != 0) {
+                        // raise the references to the max over the head's 16 columns
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const float x = ok ? z[i][r] * zscale : -INFINITY;
-                            const float mn = fmaxf(mr[i][r], x);
+                            float cm = x;
+#pragma unroll
+                            for (int o = 1; o < 16; o <<= 1) cm = fmaxf(cm, __shfl_xor(cm, o, 64));
+                            const float mn = fmaxf(mr[i][r], cm);
                             lr[i][r] = lr[i][r] * fast_exp2(mr[i][r] - mn);   // finite reference: no NaN
                             mr[i][r] = mn;
                             d[r] = x - mn;
