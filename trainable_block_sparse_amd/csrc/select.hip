@@ -768,13 +768,23 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
 #pragma unroll
         for (int r = 0; r < 4; ++r) asm volatile("" :: "v"(mr[i][r]));
     }
+    // pass 2: a tile's block-max update (at most one per thread with the usual
+    // sizes) is issued after the next tile's loads, so that the wait for those
+    // loads at the top of the tile after does not also wait for fresh atomics
+    uint32_t* pend = nullptr;
+    uint32_t pend_key = 0u;
     if (vmax > 0) issue(0, 0);
     int stg = 0;
     for (int64_t j0 = 0; j0 < vmax; j0 += kPreTileK, stg ^= 1) {
-        // tile j0 landed (the only loads in flight) and every wave is done with
-        // the previous tile, whose stage now takes the next one
+        // tile j0 landed (with the previous tile's deferred updates, both issued
+        // a tile ago) and every wave is done with the previous tile, whose stage
+        // now takes the next one
         dma_wait_barrier();
         if (j0 + kPreTileK < vmax) issue(j0 + kPreTileK, stg ^ 1);
+        if (kPass == 2 && pend) {
+            atomicMax(pend, pend_key);
+            pend = nullptr;
+        }
         // B fragments of a 16-kernel column tile: lane holds CK[kernel 16 nt + lc]
         // [32 ks + 8 lg ..], hi and lo parts, all eight LDS reads issued together
         uint4 fh[1][4], fl[1][4];
@@ -878,12 +888,19 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
                     if (k0 > k1) continue;
                     float mx = rs[rr][k0];
                     for (int kk = k0 + 1; kk <= k1; ++kk) mx = fmaxf(mx, rs[rr][kk]);
-                    atomicMax(&keys[(static_cast<size_t>(row) * hkv + g) * nblk_max + b0 + b], score_to_key(mx));
+                    uint32_t* dst = &keys[(static_cast<size_t>(row) * hkv + g) * nblk_max + b0 + b];
+                    if (!pend) {              // the thread's first update waits for the next tile
+                        pend = dst;
+                        pend_key = score_to_key(mx);
+                    } else {
+                        atomicMax(dst, score_to_key(mx));
+                    }
                 }
                 __syncthreads();
             }
         }
     }
+    if (kPass == 2 && pend) atomicMax(pend, pend_key);
     if (kPass == 1) {
         // fold the 16 kernel columns: lanes with equal lg hold the same heads
 #pragma unroll
