@@ -129,12 +129,12 @@ def test_coarse_decode_configs(cfg, coarse):
     _run_decode(make_config(cfg), coarse, label=f"config {cfg} coarse {coarse}")
 
 
-def _run_prefill(wl, coarse, chunk, positions=None, label="coarse prefill"):
+def _run_prefill(wl, coarse, chunk, positions=None, label="coarse prefill", ck_dtype="fp32"):
     h = _h()
     import trainable_block_sparse_amd as tbs
     L = int(wl.lens[0])
-    _say(f"{label}: L={L} chunk={chunk} coarse={coarse} io={wl.io_dtype}")
-    dev = h.DeviceWorkload(wl)
+    _say(f"{label}: L={L} chunk={chunk} coarse={coarse} io={wl.io_dtype} ck={ck_dtype}")
+    dev = h.DeviceWorkload(wl, ck_dtype)
     idx_e, _, _ = dev.prefill(chunk)                 # exact (also writes the fine compressed keys)
     ckc, ckc_off, _ = h.coarse_ck(dev, coarse)
     idxs, scores = [], []
@@ -148,10 +148,10 @@ def _run_prefill(wl, coarse, chunk, positions=None, label="coarse prefill"):
     idx = torch.cat(idxs).cpu().numpy().astype(np.int64)
     score = torch.cat(scores).cpu().numpy().astype(np.float64)
     idx_e = idx_e.cpu().numpy().astype(np.int64)
-    prm = _params(wl)
+    prm = _params(wl, ck_dtype)
     K = wl.k_f64(0)
-    ck = ref.compress_keys(K, wl.kernel_size, wl.kernel_stride, "fp32")
-    ckc_o = ref.compress_keys(K, coarse, coarse, "fp32")
+    ck = ref.compress_keys(K, wl.kernel_size, wl.kernel_stride, ck_dtype)
+    ckc_o = ref.compress_keys(K, coarse, coarse, ck_dtype)
     q = wl.q_f64()
     G = prm.group
     pos = list(range(L)) if positions is None else list(positions)
@@ -174,6 +174,8 @@ def test_coarse_prefill_small_chunks():
                        topk=6, local_blocks=1, n_planted=3, seed=72)
     _run_prefill(wl, 64, 300, label="coarse prefill 64")
     _run_prefill(wl, 256, 1000, label="coarse prefill 256")
+    # bf16 compressed keys: both passes read the key rows as stored
+    _run_prefill(wl, 128, 400, label="coarse prefill 128 ck-bf16", ck_dtype="bf16")
 
 
 def test_coarse_prefill_fp32():
