@@ -785,6 +785,26 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
             atomicMax(pend, pend_key);
             pend = nullptr;
         }
+        // pass 2: the tile's blocks and their kernel ranges (relative to the tile;
+        // 32-bit arithmetic: kernel and block counts are below 2^31), the first
+        // kPreThreads blocks here, where the barrier after the products covers them
+        const int j0i = static_cast<int>(j0);
+        const int jhi_t = static_cast<int>((j0 + kPreTileK < vmax ? j0 + kPreTileK : vmax) - 1);
+        const int blo = (j0i * s) / m, bhi = (jhi_t * s + p - 1) / m;
+        auto block_ranges = [&](int b0) {
+            const int nb = (bhi - b0 + 1) < kPreThreads ? (bhi - b0 + 1) : kPreThreads;
+            if (t < nb) {
+                const int blk = b0 + t;
+                int k0 = blk * m - p;                          // first kernel: floor((blk m - p) / s) + 1, >= 0
+                k0 = (k0 >= 0 ? k0 / s : -((-k0 + s - 1) / s)) + 1;
+                k0 = k0 > j0i ? k0 : j0i;
+                int k1 = ((blk + 1) * m - 1) / s;              // last kernel
+                k1 = k1 < jhi_t ? k1 : jhi_t;
+                bk[t][0] = k0 - j0i;
+                bk[t][1] = k1 - j0i;
+            }
+        };
+        if (kPass == 2) block_ranges(blo);
         // B fragments of a 16-kernel column tile: lane holds CK[kernel 16 nt + lc]
         // [32 ks + 8 lg ..], hi and lo parts, all eight LDS reads issued together
         uint4 fh[1][4], fl[1][4];
@@ -858,26 +878,14 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
         }
         if (kPass == 2) {
             __syncthreads();
-            // block max over this tile's kernels.  Each block's kernel range
-            // (relative to the tile) is computed once, then one (row, block)
-            // per thread, rows fastest.  32-bit arithmetic: kernel and block
-            // counts are below 2^31.
-            const int j0i = static_cast<int>(j0);
-            const int jhi_t = static_cast<int>((j0 + kPreTileK < vmax ? j0 + kPreTileK : vmax) - 1);
-            const int blo = (j0i * s) / m, bhi = (jhi_t * s + p - 1) / m;
+            // block max over this tile's kernels: one (row, block) per thread,
+            // rows fastest
             for (int b0 = blo; b0 <= bhi; b0 += kPreThreads) {
                 const int nb = (bhi - b0 + 1) < kPreThreads ? (bhi - b0 + 1) : kPreThreads;
-                if (t < nb) {
-                    const int blk = b0 + t;
-                    int k0 = blk * m - p;                          // first kernel: floor((blk m - p) / s) + 1, >= 0
-                    k0 = (k0 >= 0 ? k0 / s : -((-k0 + s - 1) / s)) + 1;
-                    k0 = k0 > j0i ? k0 : j0i;
-                    int k1 = ((blk + 1) * m - 1) / s;              // last kernel
-                    k1 = k1 < jhi_t ? k1 : jhi_t;
-                    bk[t][0] = k0 - j0i;
-                    bk[t][1] = k1 - j0i;
+                if (b0 != blo) {                  // more blocks than threads: the next ranges
+                    block_ranges(b0);
+                    __syncthreads();
                 }
-                __syncthreads();
                 for (int e = t; e < kPreRowsG * nb; e += kPreThreads) {
                     const int rr = e & (kPreRowsG - 1), b = e / kPreRowsG, row = r0 + rr;
                     if (row >= rows) continue;
@@ -896,7 +904,7 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
                         atomicMax(dst, score_to_key(mx));
                     }
                 }
-                __syncthreads();
+                if (b0 + kPreThreads <= bhi) __syncthreads();   // ranges read before they are replaced
             }
         }
     }
