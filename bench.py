@@ -87,14 +87,37 @@ def queue_ahead(torch, ms: float) -> None:
     torch.cuda._sleep(int(_SLEEP_CYCLES_PER_MS * ms))
 
 
+MALL_BYTES = 256 << 20          # Infinity Cache of the MI355X
+COLD_PASS_BYTES = 2 * MALL_BYTES  # bytes a timed pass must touch between two uses of a replica
+_FLUSH = None
+
+
+def flush_mall(torch) -> None:
+    """Evict the Infinity Cache (and L2): read and write 1 GiB of scratch, four
+    times the cache, so that the next steps find their inputs only in HBM."""
+    global _FLUSH
+    if _FLUSH is None:
+        _FLUSH = torch.empty(2 * (256 << 20), dtype=torch.int32, device="cuda")
+    a, b = _FLUSH[: 128 << 20], _FLUSH[128 << 20:]
+    b.copy_(a)
+    a.copy_(b)
+
+
+def cold_replicas(step_bytes: int, floor: int = 8) -> int:
+    """Replicas rotated per step so that a replica is used again only after at
+    least COLD_PASS_BYTES of other steps' data."""
+    return max(floor, -(-COLD_PASS_BYTES // max(1, step_bytes)))
+
+
 def kernel_times(tbs, torch, run, steps: int, families, ahead_ms: float = 50.0) -> dict:
     """Live per-kernel times: the library stamps every launch of one kernel
     family with a pair of HIP events while a session is open; one eager pass of
-    `steps` steps per family, queued behind a spin kernel of `ahead_ms` so the
-    GPU runs the pass back to back."""
+    `steps` steps per family, after an Infinity-Cache flush and queued behind a
+    spin kernel of `ahead_ms` so the GPU runs the pass back to back."""
     out = {}
     for fam in families:
         torch.cuda.synchronize()
+        flush_mall(torch)
         queue_ahead(torch, ahead_ms)
         tbs.infv2_timing_start(fam)
         try:
@@ -184,16 +207,26 @@ def decode_kernel_bytes(wl, ck_bytes: int, n_list) -> dict:
     }
 
 
-def bench_decode(cfg_index: int, args, torch, tbs, gh, replicas: int, ck_dtype=None) -> dict:
+def bench_decode(cfg_index: int, args, torch, tbs, gh, replicas: int = 0, ck_dtype=None) -> dict:
+    """One decode step per replica of the cache.  The timed region holds exactly
+    `steps` steps, replica (warmup + t) mod R at step t, after an Infinity-Cache
+    flush; R is large enough that a replica is used again only after at least
+    COLD_PASS_BYTES of other steps, so every step reads its compressed keys and
+    selected K/V from HBM."""
     from synth import make_config, extra_decode_queries
     wl = make_config(cfg_index)
     ck_dtype = ck_dtype or args.ck_dtype
+    ckb = 2 if ck_dtype == "bf16" else 4
+    lens = [int(n) for n in wl.lens]
+    nb = decode_bytes(wl, ckb, lens)
+    kb = decode_kernel_bytes(wl, ckb, lens)
+    step_bytes = sum(nb.values())
+    R = replicas if replicas > 0 else cold_replicas(step_bytes)
     dev = gh.DeviceWorkload(wl, ck_dtype)
     dev.compress()
     cfg = dev.cfg
     B, n_max = wl.batch, dev.max_len
-    R = replicas
-    log(f"config {cfg_index}: {wl.name}, B={B}, replicas={R}")
+    log(f"config {cfg_index}: {wl.name}, B={B}, replicas={R} ({R * step_bytes / 2**20:.0f} MiB per rotation)")
     qs = gh.to_device(extra_decode_queries(wl, R))                # [R][B][Hq][d]
     Ks = [dev.k] + [dev.k.clone() for _ in range(R - 1)]
     Vs = [dev.v] + [dev.v.clone() for _ in range(R - 1)]
@@ -223,65 +256,58 @@ def bench_decode(cfg_index: int, args, torch, tbs, gh, replicas: int, ck_dtype=N
         select(r)
         attn(r)
 
+    W, K = args.warmup, args.steps
+    order = [(W + t) % R for t in range(K)]            # replicas of the timed steps
     T = Timer(torch)
-    for t in range(args.warmup):
+    for t in range(W):
         step(t % R)
     torch.cuda.synchronize()
     # per-entry-point times, eager launches with events between the calls
+    flush_mall(torch)
     ev = []
-    for t in range(args.steps):
-        r = t % R
+    for r in order:
         e0 = T.event(); compress(r); e1 = T.event(); select(r); e2 = T.event(); attn(r); e3 = T.event()
         ev.append((e0, e1, e2, e3))
     torch.cuda.synchronize()
     per = np.array([[a.elapsed_time(b) for a, b in zip(x[:-1], x[1:])] for x in ev]) * 1e3  # us
     per_us = dict(zip(["compress", "select", "attn"], per.mean(axis=0).tolist()))
-    kt = kernel_times(tbs, torch, lambda t: step(t % R), args.steps, DECODE_FAMILIES)
+    kt = kernel_times(tbs, torch, lambda t: step(order[t % K]), K, DECODE_FAMILIES)
     # whole steps, eager
     torch.cuda.synchronize()
+    flush_mall(torch)
     s0 = T.event()
-    for t in range(args.steps):
-        step(t % R)
+    for r in order:
+        step(r)
     s1 = T.event()
     torch.cuda.synchronize()
-    eager_ms = s0.elapsed_time(s1) / args.steps
-    # whole steps, HIP-graph replay: one graph holds one step on each of the R
-    # replicas (R "layers" of one decode token), replayed back to back; a second
-    # graph holds the K mod R remaining steps, so exactly K steps are timed
+    eager_ms = s0.elapsed_time(s1) / K
+    # whole steps, HIP-graph replay: one graph holds the K timed steps (K
+    # "layers" of one decode token), captured once, warmed once, then replayed
+    # after a cache flush
     graph_ms = None
     if args.graph:
-        reps, rem = divmod(args.steps, R)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
-        graphs = []
+        g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(side):
-            for n_steps in ([R] if reps else []) + ([rem] if rem else []):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=side):
-                    for r in range(n_steps):
-                        step(r)
-                graphs.append(g)
+            with torch.cuda.graph(g, stream=side):
+                for r in order:
+                    step(r)
         torch.cuda.current_stream().wait_stream(side)
-        for _ in range(max(1, args.warmup // R)):
-            graphs[0].replay()
+        g.replay()
         torch.cuda.synchronize()
+        flush_mall(torch)
         g0 = T.event()
-        for _ in range(reps):
-            graphs[0].replay()
-        if rem:
-            graphs[-1].replay()
+        g.replay()
         g1 = T.event()
         torch.cuda.synchronize()
-        graph_ms = g0.elapsed_time(g1) / args.steps
+        graph_ms = g0.elapsed_time(g1) / K
     ms = graph_ms if graph_ms is not None else eager_ms
-    ckb = 2 if ck_dtype == "bf16" else 4
-    nb = decode_bytes(wl, ckb, [int(n) for n in wl.lens])
-    kb = decode_kernel_bytes(wl, ckb, [int(n) for n in wl.lens])
-    step_bytes = sum(nb.values())
     for f, v in kt.items():
         if f in kb and v["us_per_launch"]:
             v["bytes_per_launch"] = kb[f]
             v["gbps"] = kb[f] / (v["us_per_launch"] * 1e-6) / 1e9
+    distinct = len(set(order))
     res = {
         "workload": wl.name, "batch": B, "lens_min": int(wl.lens.min()), "lens_max": n_max,
         "ms_per_step": ms, "ms_per_step_eager": eager_ms, "ms_per_step_graph": graph_ms,
@@ -289,6 +315,12 @@ def bench_decode(cfg_index: int, args, torch, tbs, gh, replicas: int, ck_dtype=N
         "bytes_per_step": step_bytes,
         "bytes_per_call": nb, "hbm_gbps_step": step_bytes / (ms * 1e-3) / 1e9,
         "replicas": R,
+        "cache_state": {
+            "flushed_before_timing": True,
+            "touched_mib_per_pass": distinct * step_bytes / 2**20,
+            "reuse_distance_mib": (R * step_bytes / 2**20) if K > R else None,
+            "note": "1 GiB read+write before each timed pass evicts the 256 MiB Infinity Cache; "
+                    "inside a pass a replica recurs only after R steps"},
         "roofline": roofline_of(kt, {"select_logits": kb["select_logits"],
                                      "attn_decode": kb["attn_decode"]},
                                 "hbm", HBM_PEAK_GBS, "GB/s", 1e9),
@@ -311,8 +343,10 @@ def bench_decode_loop(args, torch, tbs, gh) -> dict:
     cfg = dev.cfg
     B, hkv, d = wl.batch, wl.num_kv_heads, wl.head_dim
     n0 = int(wl.lens[0])
-    R = args.replicas
-    room = args.warmup + 2 * args.steps + 64     # every append of every timing pass fits
+    step_bytes = sum(decode_bytes(wl, 2 if args.ck_dtype == "bf16" else 4, [n0]).values())
+    R = args.replicas if args.replicas > 0 else cold_replicas(step_bytes)
+    W, K = args.warmup, args.steps
+    room = W + 4 * K + 64                         # every append of every timing pass fits
     cap = n0 + room
     # caches of capacity n0 + room holding the n0-token prefix
     def padded(t):
@@ -344,37 +378,41 @@ def bench_decode_loop(args, torch, tbs, gh) -> dict:
         tbs.infv2_sparse_attn_decode(cfg, qs[r], Ks[r], Vs[r], kv_off, lens[r], B, cap, idx, out,
                                      ws_att)
 
+    order = [(W + t) % R for t in range(K)]
     T = Timer(torch)
-    for t in range(args.warmup):
+    for t in range(W):
         step(t % R)
     torch.cuda.synchronize()
+    flush_mall(torch)
     s0 = T.event()
-    for t in range(args.steps):
-        step(t % R)
+    for r in order:
+        step(r)
     s1 = T.event()
     torch.cuda.synchronize()
-    eager_ms = s0.elapsed_time(s1) / args.steps
+    eager_ms = s0.elapsed_time(s1) / K
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(side):
         with torch.cuda.graph(g, stream=side):
-            for r in range(R):
+            for r in order:
                 step(r)
     torch.cuda.current_stream().wait_stream(side)
-    reps = max(1, args.steps // R)
+    g.replay()
+    torch.cuda.synchronize()
+    flush_mall(torch)
     g0 = T.event()
-    for _ in range(reps):
-        g.replay()
+    g.replay()
     g1 = T.event()
     torch.cuda.synchronize()
-    graph_ms = g0.elapsed_time(g1) / (reps * R)
-    kt = kernel_times(tbs, torch, lambda t: step(t % R), min(args.steps, 40), ("append",))
+    graph_ms = g0.elapsed_time(g1) / K
+    kt = kernel_times(tbs, torch, lambda t: step(order[t % K]), K, ("append",))
     final_len = int(lens[0].item())
     return {"workload": "decode_loop_bf16_128k", "batch": B, "start_len": n0, "final_len_replica0": final_len,
-            "ms_per_step_eager": eager_ms, "ms_per_step_graph": graph_ms,
+            "ms_per_step_eager": eager_ms, "ms_per_step_graph": graph_ms, "replicas": R,
             "tok_per_s": B / (graph_ms * 1e-3), "append_us_per_launch": kt["append"]["us_per_launch"],
-            "note": "graph of one step per replica; lengths advance on every replay"}
+            "note": "graph of the timed steps, replayed after a cache flush; lengths advance on "
+                    "every replay"}
 
 
 def decode_spot_parity(wl, dev, qs, outs, idx, select, attn, ck_dtype, torch, gh) -> str:
@@ -652,7 +690,7 @@ def bench_coarse(args, torch, tbs, gh) -> dict:
     dev = gh.DeviceWorkload(wl, args.ck_dtype)
     dev.compress()
     cfg, B, n = dev.cfg, wl.batch, dev.max_len
-    R = args.replicas
+    R = args.replicas if args.replicas > 0 else cold_replicas(dev.ck.numel() * dev.ck.element_size())
     qs = gh.to_device(extra_decode_queries(wl, R))
     CKs = [dev.ck] + [dev.ck.clone() for _ in range(R - 1)]
     T = Timer(torch)
@@ -664,9 +702,10 @@ def bench_coarse(args, torch, tbs, gh) -> dict:
         for t in range(args.warmup):
             fn(t % R)
         torch.cuda.synchronize()
+        flush_mall(torch)
         e0 = T.event()
         for t in range(args.steps):
-            fn(t % R)
+            fn((args.warmup + t) % R)
         e1 = T.event()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / args.steps
@@ -747,11 +786,39 @@ def bench_coarse(args, torch, tbs, gh) -> dict:
 
 
 def bench_batched(args, torch, tbs, gh, ck_dtype=None) -> dict:
-    # one step reads ~160 MiB, so three replicas already keep the MALL cold
-    return bench_decode(4, args, torch, tbs, gh, replicas=min(args.replicas, 4), ck_dtype=ck_dtype)
+    # one step reads ~170 MB: four replicas put 2x the Infinity Cache between two uses
+    return bench_decode(4, args, torch, tbs, gh, replicas=args.replicas, ck_dtype=ck_dtype)
 
 
 # ----------------------------------------------------------------------------- CPU oracle
+def host_info() -> dict:
+    """CPU model and the BLAS library NumPy uses, for the CPU-baseline record."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = None
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        blas = " ".join(str(b.get(k)) for k in ("name", "version") if b.get(k))
+    except Exception:  # pragma: no cover - reporting only
+        pass
+    try:
+        import threadpoolctl
+        apis = sorted({f"{x.get('internal_api')} ({x.get('threading_layer')})"
+                       for x in threadpoolctl.threadpool_info() if x.get("user_api") == "blas"})
+        if apis:
+            blas = f"{blas}; runtime {', '.join(apis)}" if blas else ", ".join(apis)
+    except Exception:  # pragma: no cover - reporting only
+        pass
+    return {"cpu_model": model, "blas": blas, "host_cpus": len(os.sched_getaffinity(0))}
+
+
 def blas_threads() -> int:
     try:
         import threadpoolctl
@@ -785,6 +852,7 @@ def cpu_baseline_decode(seconds: float) -> dict:
         if el >= seconds and steps >= 3:
             break
     return {"value": steps / el, "unit": "tok/s", "cores": blas_threads(), "kind": "oracle",
+            **host_info(),
             "sample": f"{steps} decode steps of the 128K config (B=1), float64 NumPy, "
                       f"{el:.1f} s, cache state (compressed keys) precomputed"}
 
@@ -815,6 +883,7 @@ def cpu_baseline_prefill(seconds: float, pre: dict) -> dict:
     tok = attended_tokens(gi, np.array(done), np.full(len(done), L), 64)
     flops = float(4 * 128 * 16 * tok.sum())
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            **host_info(),
             "sample": f"{len(done)} random rows of the last 4096-row chunk of the 32K prefill "
                       f"(selection + attention), {el:.1f} s; useful attention FLOPs / time"}
 
@@ -825,8 +894,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--replicas", type=int, default=32,
-                    help="independent cache copies rotated per step (defeats the 256 MiB MALL)")
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="independent cache copies rotated per step; 0 (default): enough for "
+                         "512 MiB between two uses of a copy (defeats the 256 MiB Infinity Cache)")
     ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--ck-dtype", default="fp32", choices=["fp32", "bf16"])
     ap.add_argument("--graph", type=int, default=1)
@@ -937,7 +1007,7 @@ def main() -> int:
         "config": {"workload": "decode_bf16_128k", "batch": 1, "context": 131072, "num_q_heads": 32,
                    "num_kv_heads": 2, "head_dim": 128, "block_size": 64, "kernel_size": 32,
                    "kernel_stride": 16, "topk": 64, "init_blocks": 1, "local_blocks": 4,
-                   "ck_dtype": args.ck_dtype, "cache_replicas": args.replicas,
+                   "ck_dtype": args.ck_dtype, "cache_replicas": main_res["replicas"],
                    "graph_replay": bool(args.graph)},
         "hbm_gbps": main_res["hbm_gbps_step"],
         "roofline": roof,

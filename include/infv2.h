@@ -73,12 +73,13 @@
 extern "C" {
 #endif
 
-#define INFV2_ABI_VERSION 6
+#define INFV2_ABI_VERSION 7
 
 typedef enum infv2_status {
     INFV2_OK = 0,
     INFV2_ERR_NULL = 1,         /* a required pointer is NULL */
-    INFV2_ERR_SHAPE = 2,        /* sizes inconsistent (e.g. Hq % Hkv != 0, k < |F|) */
+    INFV2_ERR_SHAPE = 2,        /* sizes inconsistent (e.g. Hq % Hkv != 0, k < |F|), or a
+                                   negative or non-finite scale */
     INFV2_ERR_UNSUPPORTED = 3,  /* valid but not implemented on this device path */
     INFV2_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than infv2_workspace_bytes */
     INFV2_ERR_DEVICE = 5        /* a HIP launch failed */
@@ -118,8 +119,9 @@ typedef struct infv2_config {
     int32_t local_blocks;   /* blocks of the local window ending at the query's block */
     int32_t io_dtype;       /* infv2_dtype of q, k, v and out */
     int32_t ck_dtype;       /* infv2_dtype of the compressed keys (FP32 default) */
-    float   score_scale;    /* selection logit scale (the pages print none: 1.0) */
-    float   attn_scale;     /* attention logit scale, usually 1/sqrt(d) */
+    float   score_scale;    /* selection logit scale, > 0; 0 selects the default 1.0 (the
+                               pages print the kernel softmax with no scale) */
+    float   attn_scale;     /* attention logit scale, > 0; 0 selects the default 1/sqrt(d) */
 } infv2_config;
 
 /*

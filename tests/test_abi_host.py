@@ -101,9 +101,25 @@ def _compress(lib, cfg, k=FAKE, off=FAKE, ckoff=FAKE, ck=FAKE, batch=1, max_len=
     (tbs.Config(block_size=48 + 1), EUNSUP),
     (tbs.Config(topk=2048), EUNSUP),
     (tbs.Config(kernel_size=512, kernel_stride=16), EUNSUP),
+    (tbs.Config(attn_scale=-0.5), ESHAPE),                         # negative scales
+    (tbs.Config(score_scale=-1.0), ESHAPE),
+    (tbs.Config(attn_scale=float("inf")), ESHAPE),
+    (tbs.Config(score_scale=float("nan")), ESHAPE),
 ])
 def test_invalid_configs_rejected(lib, cfg, want):
     assert _compress(lib, cfg) == want
+
+
+def test_zero_scales_select_the_defaults(lib):
+    # 0 in the C struct means the default (score 1.0, attention 1/sqrt(d)); the
+    # binding passes 0 when no attention scale is given and computes none itself
+    assert tbs.Config().to_c().attn_scale == 0.0
+    assert tbs.Config(attn_scale=0.25).to_c().attn_scale == 0.25
+    # accepted by the validation (a workspace query launches nothing)
+    for cfg in (tbs.Config(), tbs.Config(score_scale=0.0), tbs.Config(attn_scale=0.0, score_scale=0.0)):
+        assert tbs.infv2_workspace_bytes(cfg, tbs.OP_SELECT_DECODE, 1, 1, 1000) > 0
+    with pytest.raises(tbs.Infv2Error):
+        tbs.infv2_workspace_bytes(tbs.Config(attn_scale=-1.0), tbs.OP_SELECT_DECODE, 1, 1, 1000)
 
 
 def test_null_pointers_and_sizes_rejected(lib):

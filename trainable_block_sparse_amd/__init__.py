@@ -10,7 +10,6 @@ every call raises.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from dataclasses import dataclass
 from typing import Optional
@@ -62,11 +61,11 @@ class Config:
     io_dtype: str = "bf16"
     ck_dtype: str = "fp32"
     score_scale: float = 1.0
-    attn_scale: Optional[float] = None     # None: 1/sqrt(head_dim)
+    attn_scale: Optional[float] = None     # None: the library's default (0 in the C struct)
 
     def to_c(self) -> _CConfig:
         dt = {"fp32": INFV2_FP32, "bf16": INFV2_BF16}
-        scale = (1.0 / math.sqrt(self.head_dim)) if self.attn_scale is None else self.attn_scale
+        scale = 0.0 if self.attn_scale is None else self.attn_scale
         return _CConfig(self.head_dim, self.num_q_heads, self.num_kv_heads, self.block_size,
                         self.kernel_size, self.kernel_stride, self.topk, self.init_blocks,
                         self.local_blocks, dt[self.io_dtype], dt[self.ck_dtype],

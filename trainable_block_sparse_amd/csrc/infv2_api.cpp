@@ -26,7 +26,9 @@ int32_t check_config(const infv2_config* c) {
     if (c->kernel_size < c->kernel_stride) return INFV2_ERR_SHAPE;
     if (c->topk < static_cast<int64_t>(c->init_blocks) + c->local_blocks) return INFV2_ERR_SHAPE;
     if (!dtype_ok(c->io_dtype) || !dtype_ok(c->ck_dtype)) return INFV2_ERR_SHAPE;
+    // scales: 0 selects the default (make_shape), negative values are rejected
     if (!isfinite(c->score_scale) || !isfinite(c->attn_scale)) return INFV2_ERR_SHAPE;
+    if (c->score_scale < 0.f || c->attn_scale < 0.f) return INFV2_ERR_SHAPE;
     // implemented subset
     if (c->head_dim != infv2::kHeadDim) return INFV2_ERR_UNSUPPORTED;
     if (c->num_q_heads / c->num_kv_heads != infv2::kGroup) return INFV2_ERR_UNSUPPORTED;
@@ -48,7 +50,11 @@ Shape make_shape(const infv2_config* c) {
     s.m = c->block_size; s.p = c->kernel_size; s.s = c->kernel_stride;
     s.topk = c->topk; s.init = c->init_blocks; s.local = c->local_blocks;
     s.io_bf16 = c->io_dtype == INFV2_BF16; s.ck_bf16 = c->ck_dtype == INFV2_BF16;
-    s.score_scale = c->score_scale; s.attn_scale = c->attn_scale;
+    // defaults: selection logits unscaled, as printed in "Semantic kernels";
+    // attention scaled by 1/sqrt(d), standard scaled dot-product attention
+    s.score_scale = c->score_scale == 0.f ? 1.f : c->score_scale;
+    s.attn_scale = c->attn_scale == 0.f ? static_cast<float>(1.0 / sqrt(static_cast<double>(c->head_dim)))
+                                        : c->attn_scale;
     return s;
 }
 
