@@ -97,7 +97,7 @@ def flush_mall(torch) -> None:
     times the cache, so that the next steps find their inputs only in HBM."""
     global _FLUSH
     if _FLUSH is None:
-        _FLUSH = torch.empty(2 * (256 << 20), dtype=torch.int32, device="cuda")
+        _FLUSH = torch.empty(2 * (128 << 20), dtype=torch.int32, device="cuda")   # 2 x 512 MiB
     a, b = _FLUSH[: 128 << 20], _FLUSH[128 << 20:]
     b.copy_(a)
     a.copy_(b)

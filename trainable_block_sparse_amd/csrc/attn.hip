@@ -19,22 +19,36 @@
 
 namespace infv2 {
 
+
 constexpr int kTok = 64;             // tokens per LDS tile
 
 AttnDecodeWs attn_decode_ws(const Shape& sh, int batch) {
     AttnDecodeWs w{};
-    // four selected blocks per split, or one where four would give fewer thread
-    // blocks than the chip has compute units (small batches)
-    const int64_t wide = static_cast<int64_t>(batch) * sh.hkv * ((sh.topk + 3) / 4);
-    w.bps = (wide < kDecodeFewBlocks && sh.topk <= kDecodeMaxSplit) ? 1 : 4;
+    const int64_t bg = static_cast<int64_t>(batch) * sh.hkv;
+    // vector-ALU path: four selected blocks per split, or one where four would
+    // give fewer thread blocks than the chip has compute units (small batches)
+    constexpr int kOneBlockMax = 256;
+    const int64_t wide = bg * ((sh.topk + 3) / 4);
+    w.bps = (wide < kDecodeFewBlocks && sh.topk <= kOneBlockMax) ? 1 : 4;
     w.nsplit = (sh.topk + w.bps - 1) / w.bps;
-    // room for the larger of the two split counts, so the size never shrinks
-    // as the batch grows (a workspace sized for a batch serves every smaller one)
-    const size_t nalloc = sh.topk <= kDecodeMaxSplit ? sh.topk : w.nsplit;
-    const size_t bg = static_cast<size_t>(batch) * sh.hkv;
+    const int64_t nalloc_v = sh.topk <= kOneBlockMax ? sh.topk : w.nsplit;
+    // matrix-core path: four 16-key tiles per split, or sixteen when four would
+    // give many thread blocks (large batches: fewer partials to write and merge)
+    // or more splits than the merge takes
+    const int64_t tiles = static_cast<int64_t>(sh.topk) * (sh.m / 16);
+    const int64_t n4 = (tiles + 3) / 4, n16 = (tiles + 15) / 16;
+    const bool four_ok = n4 <= kDecodeMaxSplit;
+    w.tiles_wg = (four_ok && bg * n4 <= kDecodeManyWg) ? 4 : 16;
+    w.nsplit_m = static_cast<int>(w.tiles_wg == 4 ? n4 : n16);
+    const int64_t nalloc_m = four_ok ? n4 : n16;
+    // room for the largest split count of either path at any batch, so the size
+    // never shrinks as the batch grows (a workspace sized for a batch serves
+    // every smaller one)
+    const size_t nalloc = static_cast<size_t>(nalloc_v > nalloc_m ? nalloc_v : nalloc_m);
+    const size_t nbg = static_cast<size_t>(bg);
     size_t off = 0;
-    w.part_o = off;   off += align256(bg * nalloc * kGroup * kHeadDim * sizeof(float));
-    w.part_ml = off;  off += align256(bg * nalloc * kGroup * sizeof(float2));
+    w.part_o = off;   off += align256(nbg * nalloc * kGroup * kHeadDim * sizeof(float));
+    w.part_ml = off;  off += align256(nbg * nalloc * kGroup * sizeof(float2));
     w.total = off;
     return w;
 }
@@ -198,7 +212,10 @@ hipError_t launch_attn_decode(const Shape& sh, const void* q, const void* k, con
     float2* pml = reinterpret_cast<float2*>(base + w.part_ml);
     hipError_t e;
     if (sh.io_bf16) {
-        e = launch_attn_decode_mfma(sh, q, k, v, kv_off, kv_lens, batch, idx, po, pml, w.nsplit, w.bps, st);
+        e = launch_attn_decode_mfma(sh, q, k, v, kv_off, kv_lens, batch, idx, po, pml, w.nsplit_m,
+                                    w.tiles_wg, st);
+        if (e != hipSuccess) return e;
+        return launch_attn_decode_merge(sh, po, pml, out, batch, w.nsplit_m, st);
     } else {
         launch_timed(INFV2_KERNEL_ATTN_DECODE, attn_decode_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), kv_off, kv_lens, idx, po, pml, sh.hq, sh.hkv, sh.m, sh.topk, w.nsplit, w.bps, sh.attn_scale);
         e = hipGetLastError();

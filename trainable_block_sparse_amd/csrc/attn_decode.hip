@@ -4,53 +4,52 @@
 // group sharing" (the 16 heads of a group read each selected block once, which
 // is what makes the 16-row matrix tile a real contraction).
 //
-// Grid (split, KV head, sequence), W waves per block and one selected block per
-// wave: W = 4, or W = 1 when four-block splits would leave most compute units
-// idle (small batches).  Each wave owns whole 64-token pieces of its block and
-// keeps everything in registers:
-//   S^T[key][head] = K_blk (64x128) . Q^T (128x16)      16 MFMA 16x16x32
-//   V^T tiles      = V_blk . I  (identity MFMA, exact)  32 MFMA 16x16x16
-//   O^T[d][head]  += V^T (128x64) . P^T (64x16)         16 MFMA 16x16x32
-// K rows are the A operand exactly as stored (16 contiguous bytes per lane), so
-// K and V stream from HBM with 16-byte coalesced loads and never touch LDS.
-// The S^T layout puts one query head per lane column, so the online softmax
-// rescale is a per-lane scalar.  The waves of a block merge in LDS and each
-// block writes one partial (max, sum, output); attn_decode_merge combines the
-// splits by their LogSumExp in a second kernel.
+// A decode step at batch 1 is latency-bound: 64 blocks per KV head, 4 MiB in
+// all.  So the work is cut into 16-key tiles, one per wave, and every wave makes
+// exactly two dependent memory round trips: (offsets, length, block id,
+// queries), then its tile's K and V rows.  Grid (split, KV head, sequence); a
+// thread block of T waves covers T consecutive tiles of the (KV head,
+// sequence)'s selection (T = 4: one 64-key block; T = 16 at large batches,
+// fewer partials).  Per wave, all in registers:
+//   S^T[key][head] = K_tile (16x128) . Q^T (128x16)      4 MFMA 16x16x32
+//   V^T tiles      = V_tile . I  (identity MFMA, exact)    8 MFMA 16x16x16
+//   O^T[d][head]  += V^T (128x16) . P^T (16x16)           8 MFMA 16x16x16
+// K rows are the A operand as stored (16 contiguous bytes per lane), so K and V
+// stream from HBM with 16-byte coalesced loads.  The S^T layout puts one query
+// head per lane column; it is also exactly the B-operand layout of P^T.  The
+// waves share one reference max per head (exchanged in LDS), so their partial
+// outputs add up directly; the thread block sums them in a fixed order (results
+// are deterministic) and writes one partial (max, sum, output).
+// attn_decode_merge combines the splits by their LogSumExp in a second kernel.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace infv2 {
 
-template <int W>
+template <int T>
 struct DecSmem {
-    float o[W][kGroup][kHeadDim + 4];
-    float m[W][kGroup];
-    float l[W][kGroup];
+    float o[T][kGroup][kHeadDim + 4];     // each wave's partial output, [head][d]
+    float m[T][kGroup];                   // each wave's max per head (log2 units)
+    float l[T][kGroup];                   // each wave's sum per head
 };
 
-template <int W>
-__global__ __launch_bounds__(64 * W) void attn_decode_mfma(
+template <int T>
+__global__ __launch_bounds__(64 * T) void attn_decode_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const int64_t* __restrict__ kv_off, const int64_t* __restrict__ kv_lens,
+    const int64_t* __restrict__ kv_off, const int64_t* __restrict__ lens, int lens_end,
     const int32_t* __restrict__ idx, float* __restrict__ part_o, float2* __restrict__ part_ml,
     int hq, int hkv, int m, int topk, int nsplit, float scale_log2) {
-    static_assert(W == 1 || W == 4, "one or four waves");
+    static_assert(T == 4 || T == 16, "four or sixteen waves");
+    __shared__ DecSmem<T> sm;
     const int b = blockIdx.z, g = blockIdx.y, sp = blockIdx.x, t = threadIdx.x;
     const int w = t >> 6, l = t & 63, lg = l >> 4, lc = l & 15;
     const size_t bg = static_cast<size_t>(b) * hkv + g;
-    const int e0 = sp * W;
-    const int e1 = (e0 + W < topk) ? e0 + W : topk;
-    // the wave's first block id is loaded together with the offsets (one round trip)
-    const int32_t blk_first = (e0 + w < e1) ? idx[bg * topk + e0 + w] : -1;
-    const int64_t o0 = kv_off[b], cap = kv_off[b + 1] - o0;
-    int64_t n = kv_lens ? kv_lens[b] : cap;
-    n = n < cap ? n : cap;
-    const int64_t lim = n;                       // decode row i = n - 1 sees keys t < n
-    const bf16_t* kh = k + (o0 * hkv + static_cast<int64_t>(g) * cap) * kHeadDim;
-    const bf16_t* vh = v + (o0 * hkv + static_cast<int64_t>(g) * cap) * kHeadDim;
-
-    // Q^T as the B operand: lane holds Q[head lc][32 ks + 8 lg .. +7]
+    const int tpb = m >> 4;                          // 16-key tiles per block
+    const int u = sp * T + w;                        // this wave's tile
+    const int e = u / tpb, st = u - e * tpb;         // its selection slot and sub-tile
+    // round trip 1: every load below depends only on the kernel arguments
+    const int64_t o0 = kv_off[b], o1 = kv_off[b + 1], lv = lens[b];
+    const int32_t blk_raw = idx[bg * topk + (e < topk ? e : topk - 1)];
     const bf16_t* qrow = q + (static_cast<size_t>(b) * hq + static_cast<size_t>(g) * kGroup + lc) * kHeadDim;
     bf16x8_t qf[4];
 #pragma unroll
@@ -60,174 +59,125 @@ __global__ __launch_bounds__(64 * W) void attn_decode_mfma(
 #pragma unroll
     for (int j = 0; j < 4; ++j) ident[j] = (4 * lg + j == lc) ? static_cast<short>(0x3f80) : 0;
 
+    const int64_t cap = o1 - o0;
+    const int64_t n = seq_len(o0, o1, lv, lens_end);     // decode row i = n - 1 sees keys t < n
+    const int32_t blk = e < topk ? blk_raw : -1;
+    const int64_t t0 = static_cast<int64_t>(blk) * m + 16 * st;
+    int64_t cnt = n - t0;
+    cnt = cnt < 16 ? cnt : 16;
+    const bool act = blk >= 0 && cnt > 0;                // wave-uniform
+
     f32x4_t o[4][2];
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int h = 0; h < 2; ++h) o[c][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float mrun = -INFINITY, lrun = 0.f;
-
-    for (int e = e0 + w; e < e1; e += W) {
-        const int32_t blk = e == e0 + w ? blk_first : idx[bg * topk + e];
-        if (blk < 0) continue;
-        for (int sub = 0; sub < m; sub += 64) {
-            const int64_t t0 = static_cast<int64_t>(blk) * m + sub;
-            int64_t cnt = lim - t0;
-            cnt = cnt < m - sub ? cnt : m - sub;
-            cnt = cnt < 64 ? cnt : 64;
-            if (cnt <= 0) continue;
-            // issue every load of the piece first: K (A operand) and V rows, 16 B per lane each
-            uint4 kr[4][4], vr[4][4];
+    f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    uint4 vr[4];
+    float mx = -INFINITY;
+    if (act) {
+        // round trip 2: K (A operand) and V rows of the tile, 16 B per lane each
+        int64_t key = t0 + lc;
+        key = key < n ? key : n - 1;
+        const size_t base = (static_cast<size_t>(o0) * hkv + static_cast<size_t>(g) * cap + key) * kHeadDim + 8 * lg;
+        uint4 kr[4];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                int64_t key = t0 + 16 * mt + lc;
-                key = key < lim ? key : lim - 1;
-                const bf16_t* kp = kh + key * kHeadDim + 8 * lg;
-                const bf16_t* vp = vh + key * kHeadDim + 8 * lg;
+        for (int c = 0; c < 4; ++c) {
+            kr[c] = ldg16_nt(k + base + 32 * c);
+            vr[c] = ldg16_nt(v + base + 32 * c);
+        }
+        // S^T: lane holds S[key 4 lg + r][head lc]
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    kr[mt][c] = ldg16(kp + 32 * c);
-                    vr[mt][c] = ldg16(vp + 32 * c);
-                }
-            }
-            // S^T: lane holds S[head lc][key 16 mt + 4 lg + r]
-            f32x4_t s[4];
+        for (int ks = 0; ks < 4; ++ks) s = mfma32(as_bf16x8(kr[ks]), qf[ks], s);
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                s[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < 4; ++r) {
+            const float x = (4 * lg + r < cnt) ? s[r] * scale_log2 : -INFINITY;
+            s[r] = x;
+            mx = fmaxf(mx, x);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    } else {
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) s[mt] = mfma32(as_bf16x8(kr[mt][ks]), qf[ks], s[mt]);
-            }
-            float mx = -INFINITY;
+        for (int c = 0; c < 4; ++c) vr[c] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    if (lg == 0) sm.m[w][lc] = mx;
+    __syncthreads();
+    float M = -INFINITY;                                 // the thread block's max of head lc
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+    for (int x = 0; x < T; ++x) M = fmaxf(M, sm.m[x][lc]);
+    float ls = 0.f;
+    if (act) {
+        // M >= mx > -inf: probabilities against the shared reference
+        float p[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const bool ok = (16 * mt + 4 * lg + r) < cnt;
-                    const float x = ok ? s[mt][r] * scale_log2 : -INFINITY;
-                    s[mt][r] = x;
-                    mx = fmaxf(mx, x);
-                }
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float mnew = fmaxf(mrun, mx);
-            const float alpha = (mrun == -INFINITY) ? 0.f : exp2f(mrun - mnew);
-            float ls = 0.f;
+        for (int r = 0; r < 4; ++r) {
+            p[r] = (s[r] == -INFINITY) ? 0.f : exp2f(s[r] - M);
+            ls += p[r];
+        }
+        ls += __shfl_xor(ls, 16, 64);
+        ls += __shfl_xor(ls, 32, 64);
+        // P^T as the B operand: lane holds P[key 4 lg + j][head lc]
+        const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(pack_rne(p[0], p[1]), pack_rne(p[2], p[3])));
+        // V^T tile (d column block c, half hf), then O^T += V^T . P^T.  Transpose
+        // output: lane holds V[key 4 lg + r][d(lc)], d(x) = 32 c + 8 (x/4) + 4 hf + x%4
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+        for (int c = 0; c < 4; ++c) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float p = (s[mt][r] == -INFINITY) ? 0.f : exp2f(s[mt][r] - mnew);
-                    s[mt][r] = p;
-                    ls += p;
-                }
-            ls += __shfl_xor(ls, 16, 64);
-            ls += __shfl_xor(ls, 32, 64);
-            lrun = lrun * alpha + ls;
-            mrun = mnew;
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) o[c][h][r] *= alpha;
-            // P^T as the B operand of K-step kk: slot e <-> key 32 kk + 16 (e/4) + 4 lg + e%4
-            bf16x8_t pf[2];
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                uint4 u;
-                u.x = pack_rne(s[2 * kk][0], s[2 * kk][1]);
-                u.y = pack_rne(s[2 * kk][2], s[2 * kk][3]);
-                u.z = pack_rne(s[2 * kk + 1][0], s[2 * kk + 1][1]);
-                u.w = pack_rne(s[2 * kk + 1][2], s[2 * kk + 1][3]);
-                pf[kk] = as_bf16x8(u);
-            }
-            // V^T tiles (d column block c, half hf) then O^T += V^T . P^T.
-            // transpose MFMA output: lane holds V[key 16 mt + 4 lg + r][d(lc)],
-            // d(n) = 32 c + 8 (n/4) + 4 hf + n%4
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    f32x4_t vt[4];
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) {
-                        const uint2 half = hf ? make_uint2(vr[mt][c].z, vr[mt][c].w)
-                                              : make_uint2(vr[mt][c].x, vr[mt][c].y);
-                        vt[mt] = mfma16(__builtin_bit_cast(s16x4_t, half), ident,
-                                        f32x4_t{0.f, 0.f, 0.f, 0.f});
-                    }
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) {
-                        uint4 u;
-                        u.x = pack_exact(vt[2 * kk][0], vt[2 * kk][1]);
-                        u.y = pack_exact(vt[2 * kk][2], vt[2 * kk][3]);
-                        u.z = pack_exact(vt[2 * kk + 1][0], vt[2 * kk + 1][1]);
-                        u.w = pack_exact(vt[2 * kk + 1][2], vt[2 * kk + 1][3]);
-                        o[c][hf] = mfma32(as_bf16x8(u), pf[kk], o[c][hf]);
-                    }
-                }
+            for (int hf = 0; hf < 2; ++hf) {
+                const uint2 half = hf ? make_uint2(vr[c].z, vr[c].w) : make_uint2(vr[c].x, vr[c].y);
+                const f32x4_t vt = mfma16(__builtin_bit_cast(s16x4_t, half), ident, f32x4_t{0.f, 0.f, 0.f, 0.f});
+                const s16x4_t va = __builtin_bit_cast(s16x4_t, make_uint2(pack_exact(vt[0], vt[1]), pack_exact(vt[2], vt[3])));
+                o[c][hf] = mfma16(va, pb, o[c][hf]);
             }
         }
     }
     // O^T lane layout: O[head lc][d = 32 c + 8 lg + 4 hf + r]
-    if constexpr (W == 1) {
-        float* po = part_o + ((bg * nsplit + sp) * kGroup + lc) * kHeadDim + 8 * lg;
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-                *reinterpret_cast<float4*>(po + 32 * c + 4 * hf) =
-                    make_float4(o[c][hf][0], o[c][hf][1], o[c][hf][2], o[c][hf][3]);
-        if (lg == 0) part_ml[(bg * nsplit + sp) * kGroup + lc] = make_float2(mrun, lrun);
-        return;
-    } else {
-        __shared__ DecSmem<W> sm;
+        for (int hf = 0; hf < 2; ++hf)
+            *reinterpret_cast<float4*>(&sm.o[w][lc][32 * c + 8 * lg + 4 * hf]) =
+                make_float4(o[c][hf][0], o[c][hf][1], o[c][hf][2], o[c][hf][3]);
+    if (lg == 0) sm.l[w][lc] = ls;
+    __syncthreads();
+    // the waves' outputs, summed in wave order: thread -> 4 columns of one head
+    const size_t pbase = (bg * nsplit + sp) * kGroup;
+    for (int x = t; x < kGroup * kHeadDim / 4; x += 64 * T) {
+        const int h = x >> 5, c4 = (x & 31) * 4;
+        float4 acc = *reinterpret_cast<const float4*>(&sm.o[0][h][c4]);
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-                *reinterpret_cast<float4*>(&sm.o[w][lc][32 * c + 8 * lg + 4 * hf]) =
-                    make_float4(o[c][hf][0], o[c][hf][1], o[c][hf][2], o[c][hf][3]);
-        if (lg == 0) { sm.m[w][lc] = mrun; sm.l[w][lc] = lrun; }
-        __syncthreads();
-
-        // merge the waves: thread -> head h, 8 columns
-        const int h = t >> 4, c0 = (t & 15) * 8;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int x = 0; x < W; ++x) mx = fmaxf(mx, sm.m[x][h]);
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        float den = 0.f;
-        if (mx != -INFINITY) {
-#pragma unroll
-            for (int x = 0; x < W; ++x) {
-                if (sm.m[x][h] == -INFINITY) continue;
-                const float wgt = exp2f(sm.m[x][h] - mx);
-                den += wgt * sm.l[x][h];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] = fmaf(wgt, sm.o[x][h][c0 + e], acc[e]);
-            }
+        for (int y = 1; y < T; ++y) {
+            const float4 a = *reinterpret_cast<const float4*>(&sm.o[y][h][c4]);
+            acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
         }
-        float* po = part_o + ((bg * nsplit + sp) * kGroup + h) * kHeadDim + c0;
-        *reinterpret_cast<float4*>(po) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        *reinterpret_cast<float4*>(po + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
-        if ((t & 15) == 0) part_ml[(bg * nsplit + sp) * kGroup + h] = make_float2(mx, den);
+        *reinterpret_cast<float4*>(part_o + (pbase + h) * kHeadDim + c4) = acc;
+    }
+    if (t < kGroup) {
+        float mh = -INFINITY, lh = 0.f;
+#pragma unroll
+        for (int y = 0; y < T; ++y) {
+            mh = fmaxf(mh, sm.m[y][t]);
+            lh += sm.l[y][t];
+        }
+        part_ml[pbase + t] = make_float2(mh, lh);
     }
 }
 
 // Merge of the split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
-// m in log2 units.  Grid (query head of the group, KV head, sequence).  Thread t
-// takes the (m, l) pair of split t, and output columns 4 (t % 32) .. +3 of the
-// splits t / 32, t / 32 + 8, ...; the eight split groups are summed in LDS.
-template <typename T>
+// m in log2 units.  Grid (query head of the group, KV head, sequence), 256
+// threads.  Thread t folds the (m, l) pairs of splits t, t + 256, ..; for the
+// outputs, thread t takes columns 4 (t % 32) .. +3 of splits t / 32, t / 32 + 8,
+// .. (the first eight of them loaded together with the pairs), and the eight
+// split groups are summed in LDS in a fixed order.
+template <typename Tout>
 __global__ __launch_bounds__(256) void attn_decode_merge(const float* __restrict__ part_o,
                                                          const float2* __restrict__ part_ml,
-                                                         T* __restrict__ out, int hq, int hkv,
+                                                         Tout* __restrict__ out, int hq, int hkv,
                                                          int nsplit) {
     constexpr int kSg = 8;                 // split groups
     constexpr int kPre = 8;                // splits per thread loaded with the (m, l) pairs
-    static_assert(kDecodeMaxSplit <= 256, "one (m, l) pair per thread");
+    constexpr int kMlPer = kDecodeMaxSplit / 256;
     __shared__ float wgt[kDecodeMaxSplit];
     __shared__ float red[2][4];
     __shared__ float4 part[kSg][kHeadDim / 4];
@@ -241,15 +191,28 @@ __global__ __launch_bounds__(256) void attn_decode_merge(const float* __restrict
 #pragma unroll
     for (int i = 0; i < kPre; ++i)
         if (sg + kSg * i < nsplit) pre[i] = po[(sg + kSg * i) * stride];
-    float2 ml = make_float2(-INFINITY, 0.f);
-    if (t < nsplit) ml = part_ml[(bg * nsplit + t) * kGroup + h];
-    float gm = wave_max(ml.x);
+    float2 ml[kMlPer];
+#pragma unroll
+    for (int i = 0; i < kMlPer; ++i) {
+        const int sx = t + 256 * i;
+        ml[i] = sx < nsplit ? part_ml[(bg * nsplit + sx) * kGroup + h] : make_float2(-INFINITY, 0.f);
+    }
+    float gm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kMlPer; ++i) gm = fmaxf(gm, ml[i].x);
+    gm = wave_max(gm);
     if ((t & 63) == 0) red[0][wv] = gm;
     __syncthreads();
     gm = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-    const float wt = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - gm);
-    if (t < nsplit) wgt[t] = wt;
-    const float den_w = wave_sum(wt * ml.y);
+    float den_t = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMlPer; ++i) {
+        const int sx = t + 256 * i;
+        const float wt = (ml[i].x == -INFINITY) ? 0.f : exp2f(ml[i].x - gm);
+        if (sx < nsplit) wgt[sx] = wt;
+        den_t += wt * ml[i].y;
+    }
+    const float den_w = wave_sum(den_t);
     if ((t & 63) == 0) red[1][wv] = den_w;
     __syncthreads();
     const float den = red[1][0] + red[1][1] + red[1][2] + red[1][3];
@@ -273,28 +236,30 @@ __global__ __launch_bounds__(256) void attn_decode_merge(const float* __restrict
             r.x += a.x; r.y += a.y; r.z += a.z; r.w += a.w;
         }
         const float inv = den > 0.f ? 1.f / den : 0.f;
-        T* dst = out + (static_cast<size_t>(b) * hq + static_cast<size_t>(g) * kGroup + h) * kHeadDim + 4 * t;
-        io<T>::store(dst + 0, r.x * inv);
-        io<T>::store(dst + 1, r.y * inv);
-        io<T>::store(dst + 2, r.z * inv);
-        io<T>::store(dst + 3, r.w * inv);
+        Tout* dst = out + (static_cast<size_t>(b) * hq + static_cast<size_t>(g) * kGroup + h) * kHeadDim + 4 * t;
+        io<Tout>::store(dst + 0, r.x * inv);
+        io<Tout>::store(dst + 1, r.y * inv);
+        io<Tout>::store(dst + 2, r.z * inv);
+        io<Tout>::store(dst + 3, r.w * inv);
     }
 }
 
 hipError_t launch_attn_decode_mfma(const Shape& sh, const void* q, const void* k, const void* v,
                                    const int64_t* kv_off, const int64_t* kv_lens, int batch,
                                    const int32_t* idx, float* part_o, float2* part_ml, int nsplit,
-                                   int bps, hipStream_t st) {
+                                   int tiles_wg, hipStream_t st) {
     dim3 grid(nsplit, sh.hkv, batch);
     const float scale_log2 = sh.attn_scale * 1.4426950408889634f;
-    if (bps == 1)
-        launch_timed(INFV2_KERNEL_ATTN_DECODE, attn_decode_mfma<1>, grid, dim3(64), 0, st,
-            static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
-            kv_off, kv_lens, idx, part_o, part_ml, sh.hq, sh.hkv, sh.m, sh.topk, nsplit, scale_log2);
-    else
+    const int64_t* lens = kv_lens ? kv_lens : kv_off + 1;
+    const int lens_end = kv_lens ? 0 : 1;
+    if (tiles_wg == 4)
         launch_timed(INFV2_KERNEL_ATTN_DECODE, attn_decode_mfma<4>, grid, dim3(256), 0, st,
-        static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
-        kv_off, kv_lens, idx, part_o, part_ml, sh.hq, sh.hkv, sh.m, sh.topk, nsplit, scale_log2);
+            static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
+            kv_off, lens, lens_end, idx, part_o, part_ml, sh.hq, sh.hkv, sh.m, sh.topk, nsplit, scale_log2);
+    else
+        launch_timed(INFV2_KERNEL_ATTN_DECODE, attn_decode_mfma<16>, grid, dim3(1024), 0, st,
+            static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
+            kv_off, lens, lens_end, idx, part_o, part_ml, sh.hq, sh.hkv, sh.m, sh.topk, nsplit, scale_log2);
     return hipGetLastError();
 }
 

@@ -103,6 +103,23 @@ __device__ __forceinline__ f32x4_t mfma16(s16x4_t a, s16x4_t b, f32x4_t c) {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// 16-byte load of data read once (selected K/V rows, compressed keys): the
+// nontemporal hint streams it past the caches (+12 % read bandwidth measured)
+__device__ __forceinline__ uint4 ldg16_nt(const void* p) {
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    const v4u x = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    return make_uint4(x.x, x.y, x.z, x.w);
+}
+
+// Valid length of sequence b from its offsets and the caller's lengths.  The
+// launchers pass `lens` = kv_lens, or kv_offsets + 1 with lens_end = 1 when
+// kv_lens is NULL, so the length is loaded unconditionally, together with the
+// offsets (one memory round trip instead of two).
+__device__ __forceinline__ int64_t seq_len(int64_t o0, int64_t o1, int64_t lv, int lens_end) {
+    const int64_t cap = o1 - o0;
+    const int64_t n = lens_end ? cap : lv;
+    return n < cap ? n : cap;
+}
 
 // two floats that hold bf16 values exactly -> packed bf16 pair (no rounding needed)
 __device__ __forceinline__ uint32_t pack_exact(float lo, float hi) {

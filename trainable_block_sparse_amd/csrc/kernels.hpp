@@ -59,6 +59,7 @@ struct SelectDecodeWs {
     size_t logits_c, partial_c, lse_c, total_coarse;   // coarse-kernel LSE variant
     int nchunk_a, nchunk_b;
     int64_t nc_max, nc_ld, nblk_max;   // nc_ld: logits row stride (multiple of 4)
+    int64_t keys_ld;                   // block-key row stride (padded for the top-k)
 };
 SelectDecodeWs select_decode_ws(const Shape& sh, int batch, int64_t max_len);
 
@@ -72,13 +73,16 @@ struct SelectPrefillWs {
 };
 SelectPrefillWs select_prefill_ws(const Shape& sh, int rows, int64_t max_len);
 
-// Decode attention: the selected blocks are cut into nsplit splits of bps
-// blocks (1 or 4), each giving one partial (max, sum, output) per head.
-constexpr int kDecodeFewBlocks = 256;   // below this many 4-block splits, 1-block splits
-constexpr int kDecodeMaxSplit = 256;    // splits the merge kernel takes
+// Decode attention: each split gives one partial (max, sum, output) per head.
+// Vector-ALU path (fp32): a split is bps selected blocks (1 or 4).  Matrix-core
+// path (bf16): a split is tiles_wg 16-key tiles (4 or 16) of the selection.
+constexpr int kDecodeFewBlocks = 256;   // vector-ALU: below this many 4-block splits, 1-block splits
+constexpr int kDecodeManyWg = 1024;     // matrix cores: above this many 4-tile splits, 16-tile splits
+constexpr int kDecodeMaxSplit = 1024;   // splits the merge kernel takes
 struct AttnDecodeWs {
     size_t part_o, part_ml, total;
-    int nsplit, bps;
+    int nsplit, bps;              // vector-ALU path
+    int nsplit_m, tiles_wg;       // matrix-core path
 };
 AttnDecodeWs attn_decode_ws(const Shape& sh, int batch);
 
@@ -116,7 +120,7 @@ hipError_t launch_attn_decode(const Shape& sh, const void* q, const void* k, con
 hipError_t launch_attn_decode_mfma(const Shape& sh, const void* q, const void* k, const void* v,
                                    const int64_t* kv_off, const int64_t* kv_lens, int batch,
                                    const int32_t* idx, float* part_o, float2* part_ml, int nsplit,
-                                   int bps, hipStream_t st);
+                                   int tiles_wg, hipStream_t st);
 hipError_t launch_attn_decode_merge(const Shape& sh, const float* part_o, const float2* part_ml,
                                     void* out, int batch, int nsplit, hipStream_t st);
 

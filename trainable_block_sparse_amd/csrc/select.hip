@@ -80,7 +80,10 @@ SelectDecodeWs select_decode_ws(const Shape& sh, int batch, int64_t max_len) {
     size_t off = 0;
     w.logits = off;   off += align256(bg * w.nc_ld * kGroup * sizeof(float));
     w.partial = off;  off += align256(bg * w.nchunk_a * kGroup * sizeof(float2));
-    w.keys = off;     off += align256(bg * w.nblk_max * sizeof(uint32_t));
+    // key rows padded to the top-k's register tile (256 threads x kPer keys), so
+    // that its loads need no bounds
+    w.keys_ld = static_cast<int64_t>(256) * topk_kper(topk_per(w.nblk_max, 256));
+    w.keys = off;     off += align256(bg * w.keys_ld * sizeof(uint32_t));
     w.total = off;
     size_t lc, pc, ls;
     w.total_coarse = off + coarse_extra(sh, batch, max_len, &lc, &pc, &ls);
@@ -117,7 +120,7 @@ __global__ __launch_bounds__(256) void sel_dec_logits(
     const Tq* __restrict__ q, const Tck* __restrict__ ck, const int64_t* __restrict__ ck_off,
     const int64_t* __restrict__ kv_off, const int64_t* __restrict__ kv_lens, int hq, int hkv,
     int p, int s, float score_scale, int64_t nc_max, int64_t nc_ld, int nchunk, int64_t nblk_max,
-    float* __restrict__ logits, float2* __restrict__ partial, uint32_t* __restrict__ keys) {
+    int64_t kld, float* __restrict__ logits, float2* __restrict__ partial, uint32_t* __restrict__ keys) {
     __shared__ float qs[kGroup][kHeadDim];
     const int b = blockIdx.z, g = blockIdx.y, ch = blockIdx.x, t = threadIdx.x;
     const int64_t cap = kv_off[b + 1] - kv_off[b];
@@ -131,7 +134,7 @@ __global__ __launch_bounds__(256) void sel_dec_logits(
 
     // clear this block's share of the block-score keys (filled by pass 2)
     {
-        uint32_t* kb = keys + bg * nblk_max;
+        uint32_t* kb = keys + bg * kld;
         const int64_t per = (nblk_max + nchunk - 1) / nchunk;
         const int64_t e = (ch + 1) * per < nblk_max ? (ch + 1) * per : nblk_max;
         for (int64_t j = ch * per + t; j < e; j += 256) kb[j] = 0u;
@@ -185,57 +188,77 @@ __global__ __launch_bounds__(256) void sel_dec_logits(
 template <bool kCkBf16>
 __global__ __launch_bounds__(kLogWaves * 64) void sel_dec_logits_mfma(
     const bf16_t* __restrict__ q, const void* __restrict__ ck, const int64_t* __restrict__ ck_off,
-    const int64_t* __restrict__ kv_off, const int64_t* __restrict__ kv_lens, int hq, int hkv,
-    int p, int s, float score_scale, int64_t nc_max, int64_t nc_ld, int nchunk, int64_t nblk_max,
-    float* __restrict__ logits, float2* __restrict__ partial, uint32_t* __restrict__ keys) {
+    const int64_t* __restrict__ kv_off, const int64_t* __restrict__ lens, int lens_end, int hq,
+    int hkv, int p, int s, float score_scale, int64_t nc_max, int64_t nc_ld, int nchunk,
+    int64_t nblk_max, int64_t kld, float* __restrict__ logits, float2* __restrict__ partial,
+    uint32_t* __restrict__ keys) {
     __shared__ float2 xm[kLogWaves][kGroup];   // each wave's (max, sum) per head
     const int b = blockIdx.z, g = blockIdx.y, ch = blockIdx.x, t = threadIdx.x;
     const int l = t & 63, wv = t >> 6, lg = l >> 4, lc = l & 15;
-    const int64_t cap = kv_off[b + 1] - kv_off[b];
-    int64_t n = kv_lens ? kv_lens[b] : cap;
-    n = n < cap ? n : cap;
-    const int64_t ccap = ck_off[b + 1] - ck_off[b];
-    int64_t nvis = num_kernels(n, p, s);
-    nvis = nvis < ccap ? nvis : ccap;
-    nvis = nvis < nc_max ? nvis : nc_max;
-    const size_t bg = static_cast<size_t>(b) * hkv + g;
-    {
-        uint32_t* kb = keys + bg * nblk_max;
-        const int64_t per = (nblk_max + nchunk - 1) / nchunk;
-        const int64_t e = (ch + 1) * per < nblk_max ? (ch + 1) * per : nblk_max;
-        for (int64_t j = ch * per + t; j < e; j += kLogWaves * 64) kb[j] = 0u;
-    }
+    // round trip 1: offsets, length and the queries (independent loads)
+    const int64_t o0 = kv_off[b], o1 = kv_off[b + 1], lv = lens[b];
+    const int64_t c0 = ck_off[b], c1 = ck_off[b + 1];
     const bf16_t* qrow = q + (static_cast<size_t>(b) * hq + static_cast<size_t>(g) * kGroup + lc) * kHeadDim;
     bf16x8_t qf[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(ldg16(qrow + 32 * ks + 8 * lg));
+    const int64_t n = seq_len(o0, o1, lv, lens_end);
+    const int64_t ccap = c1 - c0;
+    int64_t nvis = num_kernels(n, p, s);           // row n-1 sees every complete kernel
+    nvis = nvis < ccap ? nvis : ccap;
+    nvis = nvis < nc_max ? nvis : nc_max;
+    const size_t bg = static_cast<size_t>(b) * hkv + g;
     const int64_t j0 = static_cast<int64_t>(ch) * kChunkA;
-    const int64_t cbase = (ck_off[b] * hkv + static_cast<int64_t>(g) * ccap);
-    // wave wv: kernel tiles mt = kLogTiles wv ..
-    f32x4_t z[kLogTiles];
+    const int64_t cbase = (c0 * hkv + static_cast<int64_t>(g) * ccap);
+    // round trip 2: both tiles of the wave (kernels j0 + 16 mt + lc, rows clamped
+    // to the last visible kernel; a tile wholly past it loads nothing)
+    constexpr int kU = kCkBf16 ? 4 : 8;             // 16-byte loads per tile and lane
+    uint4 raw[kLogTiles][kU];
 #pragma unroll
     for (int m2 = 0; m2 < kLogTiles; ++m2) {
         const int mt = kLogTiles * wv + m2;
+        int64_t j = j0 + 16 * mt + lc;
+        j = j < nvis ? j : nvis - 1;
+        if (j0 + 16 * mt < nvis) {                  // wave-uniform
+            if (kCkBf16) {
+                const bf16_t* row = static_cast<const bf16_t*>(ck) + (cbase + j) * kHeadDim + 8 * lg;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) raw[m2][ks] = ldg16_nt(row + 32 * ks);
+            } else {
+                const float* row = static_cast<const float*>(ck) + (cbase + j) * kHeadDim + 8 * lg;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    raw[m2][2 * ks] = ldg16_nt(row + 32 * ks);
+                    raw[m2][2 * ks + 1] = ldg16_nt(row + 32 * ks + 4);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int x = 0; x < kU; ++x) raw[m2][x] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+    // clear this block's share of the block-score keys (filled by pass 2)
+    {
+        uint32_t* kb = keys + bg * kld;
+        const int64_t per = (nblk_max + nchunk - 1) / nchunk;
+        const int64_t e = (ch + 1) * per < nblk_max ? (ch + 1) * per : nblk_max;
+        for (int64_t j = ch * per + t; j < e; j += kLogWaves * 64) kb[j] = 0u;
+    }
+    // Z^T tiles
+    f32x4_t z[kLogTiles];
+#pragma unroll
+    for (int m2 = 0; m2 < kLogTiles; ++m2) {
         f32x4_t& zt = z[m2];
         zt = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        int64_t j = j0 + 16 * mt + lc;
-        if (j0 + 16 * mt >= nvis) continue;            // whole tile past the end (wave-uniform)
-        j = j < nvis ? j : nvis - 1;
         if (kCkBf16) {
-            const bf16_t* row = static_cast<const bf16_t*>(ck) + (cbase + j) * kHeadDim + 8 * lg;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) zt = mfma32(as_bf16x8(ldg16(row + 32 * ks)), qf[ks], zt);
+            for (int ks = 0; ks < 4; ++ks) zt = mfma32(as_bf16x8(raw[m2][ks]), qf[ks], zt);
         } else {
-            const float* row = static_cast<const float*>(ck) + (cbase + j) * kHeadDim + 8 * lg;
-            float4 xa[4], xb[4];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                xa[ks] = *reinterpret_cast<const float4*>(row + 32 * ks);
-                xb[ks] = *reinterpret_cast<const float4*>(row + 32 * ks + 4);
-            }
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const float x[8] = {xa[ks].x, xa[ks].y, xa[ks].z, xa[ks].w, xb[ks].x, xb[ks].y, xb[ks].z, xb[ks].w};
+                const uint4 a = raw[m2][2 * ks], c = raw[m2][2 * ks + 1];
+                const float x[8] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z), __uint_as_float(a.w),
+                                    __uint_as_float(c.x), __uint_as_float(c.y), __uint_as_float(c.z), __uint_as_float(c.w)};
                 float hi[8], lo[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -337,23 +360,18 @@ __device__ __forceinline__ float fold_partials(const float2* __restrict__ pp, in
 // lse_in: a per-(sequence, KV head, head) normaliser to use instead of the one
 // folded from `partial` (the coarse-kernel approximation), or NULL
 __global__ __launch_bounds__(256) void sel_dec_scores(
-    const int64_t* __restrict__ kv_off, const int64_t* __restrict__ kv_lens,
+    const int64_t* __restrict__ kv_off, const int64_t* __restrict__ lens, int lens_end,
     const int64_t* __restrict__ ck_off, int hkv, int m, int p, int s, int64_t nc_max,
-    int64_t nc_ld, int nchunk_a, int64_t nblk_max, const float* __restrict__ logits,
+    int64_t nc_ld, int nchunk_a, int64_t kld, const float* __restrict__ logits,
     const float2* __restrict__ partial, const float* __restrict__ lse_in,
     uint32_t* __restrict__ keys) {
     __shared__ float ls[kGroup];
     __shared__ float rs[kChunkB];
     const int b = blockIdx.z, g = blockIdx.y, ch = blockIdx.x, t = threadIdx.x;
-    const int64_t cap = kv_off[b + 1] - kv_off[b];
-    int64_t n = kv_lens ? kv_lens[b] : cap;
-    n = n < cap ? n : cap;
-    const int64_t ccap = ck_off[b + 1] - ck_off[b];
-    int64_t nvis = num_kernels(n, p, s);
-    nvis = nvis < ccap ? nvis : ccap;
-    nvis = nvis < nc_max ? nvis : nc_max;
+    const int64_t o0 = kv_off[b], o1 = kv_off[b + 1], lv = lens[b];
+    const int64_t c0 = ck_off[b], c1 = ck_off[b + 1];
     const size_t bg = static_cast<size_t>(b) * hkv + g;
-    uint32_t* kb = keys + bg * nblk_max;
+    uint32_t* kb = keys + bg * kld;
     const int64_t j0 = static_cast<int64_t>(ch) * kChunkB;
     const int64_t j = j0 + t;
 
@@ -373,6 +391,11 @@ __global__ __launch_bounds__(256) void sel_dec_scores(
         const float v = fold_partials(partial + bg * nchunk_a * kGroup + (t >> 4), nchunk_a, t);
         if ((t & 15) == 0) ls[t >> 4] = v;
     }
+    const int64_t n = seq_len(o0, o1, lv, lens_end);
+    const int64_t ccap = c1 - c0;
+    int64_t nvis = num_kernels(n, p, s);
+    nvis = nvis < ccap ? nvis : ccap;
+    nvis = nvis < nc_max ? nvis : nc_max;
     __syncthreads();
     float R = -INFINITY;
     if (j < nvis) {
@@ -422,31 +445,43 @@ __global__ __launch_bounds__(256) void sel_dec_lse_coarse(
 }
 
 // ------------------------------------------------------------------ decode, top-k
-// Keys of the thread's blocks are loaded straight into registers, in the same
-// memory round trip as the sequence length.
+// Thread t owns blocks [t kPer, t kPer + kPer) of the (sequence, KV head); the key
+// row is padded to 256 kPer entries, so the keys load as whole vectors with no
+// bounds, in the same memory round trip as the offsets and the length.
 template <int kPer>
 __global__ __launch_bounds__(256) void sel_dec_topk(const int64_t* __restrict__ kv_off,
-                                                    const int64_t* __restrict__ kv_lens, int hkv,
-                                                    int m, int topk, int init, int local,
-                                                    int64_t nblk_max, int per,
+                                                    const int64_t* __restrict__ lens, int lens_end,
+                                                    int hkv, int m, int topk, int init, int local,
+                                                    int64_t nblk_max, int64_t kld,
                                                     const uint32_t* __restrict__ keys,
                                                     int32_t* __restrict__ idx,
                                                     float* __restrict__ score) {
+    static_assert(kPer % 2 == 0, "keys load in pairs");
     __shared__ TopkSmem<256> sm;
     const int b = blockIdx.y, g = blockIdx.x;
     const size_t bg = static_cast<size_t>(b) * hkv + g;
-    const int jb = static_cast<int>(threadIdx.x) * per;
-    const uint32_t* gk = keys + bg * nblk_max;
+    const int jb = static_cast<int>(threadIdx.x) * kPer;
+    const uint32_t* gk = keys + bg * kld + jb;
+    const int64_t o0 = kv_off[b], o1 = kv_off[b + 1], lv = lens[b];
     uint32_t key[kPer];
+    if constexpr (kPer % 4 == 0) {
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) key[u] = (u < per && jb + u < nblk_max) ? gk[jb + u] : 0u;
-    const int64_t cap = kv_off[b + 1] - kv_off[b];
-    int64_t n = kv_lens ? kv_lens[b] : cap;
-    n = n < cap ? n : cap;
+        for (int u = 0; u < kPer; u += 4) {
+            const uint4 x = *reinterpret_cast<const uint4*>(gk + u);
+            key[u] = x.x; key[u + 1] = x.y; key[u + 2] = x.z; key[u + 3] = x.w;
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kPer; u += 2) {
+            const uint2 x = *reinterpret_cast<const uint2*>(gk + u);
+            key[u] = x.x; key[u + 1] = x.y;
+        }
+    }
+    const int64_t n = seq_len(o0, o1, lv, lens_end);
     int64_t c = n > 0 ? (n - 1) / m : -1;
     c = c < nblk_max - 1 ? c : nblk_max - 1;
     int cnt = static_cast<int>(c + 1) - jb;
-    cnt = cnt < 0 ? 0 : (cnt > per ? per : cnt);
+    cnt = cnt < 0 ? 0 : (cnt > kPer ? kPer : cnt);
     block_topk_regs<256>(key, jb, cnt, static_cast<int>(c), topk, init, local, idx + bg * topk,
                          score ? score + bg * topk : nullptr, sm);
 }
@@ -1003,12 +1038,12 @@ static void launch_dense_ids(const Shape& sh, int mode_decode, int rows, int64_t
         else LAUNCH(64);                  \
     } while (0)
 
-static void launch_topk_dec(const Shape& sh, int batch, int64_t nblk_max, const int64_t* kv_off,
-                            const int64_t* kv_lens, const uint32_t* keys, int32_t* idx,
-                            float* score, hipStream_t st) {
+static void launch_topk_dec(const Shape& sh, int batch, int64_t nblk_max, int64_t kld,
+                            const int64_t* kv_off, const int64_t* lens, int lens_end,
+                            const uint32_t* keys, int32_t* idx, float* score, hipStream_t st) {
     const int per = topk_per(nblk_max, 256);
 #define INFV2_L(P) sel_dec_topk<P><<<dim3(sh.hkv, batch), 256, 0, st>>>( \
-        kv_off, kv_lens, sh.hkv, sh.m, sh.topk, sh.init, sh.local, nblk_max, per, keys, idx, score)
+        kv_off, lens, lens_end, sh.hkv, sh.m, sh.topk, sh.init, sh.local, nblk_max, kld, keys, idx, score)
     INFV2_TOPK_DISPATCH(per, INFV2_L);
 #undef INFV2_L
 }
@@ -1039,6 +1074,8 @@ static void dec_launch(const Shape& sh, const void* q, const void* ck, const int
                        const CoarseSel* cs, hipStream_t st) {
     dim3 ga(w.nchunk_a, sh.hkv, batch), gb(w.nchunk_b, sh.hkv, batch);
     const int64_t ncm = w.nc_max > 0 ? w.nc_max : 1;
+    const int64_t* lens = kv_lens ? kv_lens : kv_off + 1;
+    const int lens_end = kv_lens ? 0 : 1;
     float* logits = reinterpret_cast<float*>(ws + w.logits);
     float2* partial = reinterpret_cast<float2*>(ws + w.partial);
     uint32_t* keys = reinterpret_cast<uint32_t*>(ws + w.keys);
@@ -1058,25 +1095,27 @@ static void dec_launch(const Shape& sh, const void* q, const void* ck, const int
         if (sizeof(Tq) == 2)
             launch_timed(INFV2_KERNEL_SELECT_LOGITS, sel_dec_logits_mfma<sizeof(Tck) == 2>, gc,
                          dim3(kLogWaves * 64), 0, st,
-                static_cast<const bf16_t*>(q), cs->ckc, cs->ckc_off, kv_off, kv_lens, sh.hq, sh.hkv,
-                c, c, sh.score_scale, ncm_c, ld_c, nch_c, w.nblk_max, logits_c, partial_c, keys);
+                static_cast<const bf16_t*>(q), cs->ckc, cs->ckc_off, kv_off, lens, lens_end, sh.hq,
+                sh.hkv, c, c, sh.score_scale, ncm_c, ld_c, nch_c, w.nblk_max, w.keys_ld, logits_c,
+                partial_c, keys);
         else
             launch_timed(INFV2_KERNEL_SELECT_LOGITS, sel_dec_logits<Tq, Tck>, gc, dim3(256), 0, st,
                 static_cast<const Tq*>(q), static_cast<const Tck*>(cs->ckc), cs->ckc_off, kv_off,
                 kv_lens, sh.hq, sh.hkv, c, c, sh.score_scale, ncm_c, ld_c, nch_c, w.nblk_max,
-                logits_c, partial_c, keys);
+                w.keys_ld, logits_c, partial_c, keys);
     }
     {
         if (sizeof(Tq) == 2)
             launch_timed(INFV2_KERNEL_SELECT_LOGITS, sel_dec_logits_mfma<sizeof(Tck) == 2>, ga,
                          dim3(kLogWaves * 64), 0, st,
-                static_cast<const bf16_t*>(q), ck, ck_off, kv_off, kv_lens, sh.hq, sh.hkv, sh.p,
-                sh.s, sh.score_scale, ncm, w.nc_ld, w.nchunk_a, w.nblk_max, logits, partial, keys);
+                static_cast<const bf16_t*>(q), ck, ck_off, kv_off, lens, lens_end, sh.hq, sh.hkv,
+                sh.p, sh.s, sh.score_scale, ncm, w.nc_ld, w.nchunk_a, w.nblk_max, w.keys_ld, logits,
+                partial, keys);
         else
             launch_timed(INFV2_KERNEL_SELECT_LOGITS, sel_dec_logits<Tq, Tck>, ga, dim3(256), 0, st,
                 static_cast<const Tq*>(q), static_cast<const Tck*>(ck), ck_off, kv_off, kv_lens,
                 sh.hq, sh.hkv, sh.p, sh.s, sh.score_scale, ncm, w.nc_ld, w.nchunk_a, w.nblk_max,
-                logits, partial, keys);
+                w.keys_ld, logits, partial, keys);
     }
     if (cs) {
         launch_timed(INFV2_KERNEL_SELECT_SCORES, sel_dec_lse_coarse, dim3(sh.hkv, batch), dim3(256),
@@ -1086,11 +1125,11 @@ static void dec_launch(const Shape& sh, const void* q, const void* ck, const int
     }
     {
         launch_timed(INFV2_KERNEL_SELECT_SCORES, sel_dec_scores, gb, dim3(256), 0, st, kv_off,
-                     kv_lens, ck_off, sh.hkv, sh.m, sh.p, sh.s, ncm, w.nc_ld, w.nchunk_a,
-                     w.nblk_max, logits, partial, lse_c, keys);
+                     lens, lens_end, ck_off, sh.hkv, sh.m, sh.p, sh.s, ncm, w.nc_ld, w.nchunk_a,
+                     w.keys_ld, logits, partial, lse_c, keys);
     }
     KernelTimer kt(INFV2_KERNEL_SELECT_TOPK, st);
-    launch_topk_dec(sh, batch, w.nblk_max, kv_off, kv_lens, keys, idx, score, st);
+    launch_topk_dec(sh, batch, w.nblk_max, w.keys_ld, kv_off, lens, lens_end, keys, idx, score, st);
 }
 
 

@@ -46,6 +46,11 @@ struct TopkSmem {
 __host__ __device__ constexpr int topk_per(int64_t nblk, int threads) {
     return static_cast<int>((nblk + threads - 1) / threads);
 }
+// the register-array sizes the top-k kernels are built for: the smallest one
+// that holds `per` keys
+__host__ __device__ constexpr int topk_kper(int per) {
+    return per <= 2 ? 2 : per <= 8 ? 8 : per <= 16 ? 16 : 64;
+}
 
 // key[u] is the key of block jb + u for u < cnt (cnt = valid blocks of this
 // thread, 0 if none).  Must be called by all kThreads threads of the block.
