@@ -42,8 +42,29 @@ def from_device(t: torch.Tensor, io_dtype: str) -> np.ndarray:
     return a.astype(np.float64)
 
 
+CANARY_PAD = 4096                   # elements guarded before and after each output buffer
+_CANARY = {torch.int32: 0x5A5A5A5A, torch.float32: 0x7FA5A5A5, torch.int16: 0x7FA5}
+
+
+def _canary_fill(t: torch.Tensor) -> None:
+    if t.dtype == torch.float32:
+        t.view(torch.int32).fill_(_CANARY[torch.float32])
+    else:
+        t.fill_(_CANARY[t.dtype])
+
+
+def _canary_ok(t: torch.Tensor) -> bool:
+    if t.dtype == torch.float32:
+        t = t.view(torch.int32)
+        return bool((t == _CANARY[torch.float32]).all())
+    return bool((t == _CANARY[t.dtype]).all())
+
+
 class DeviceWorkload:
-    """A workload resident in GPU memory plus the calls of the hot path."""
+    """A workload resident in GPU memory plus the calls of the hot path.  Every
+    output buffer the calls write (compressed keys, block ids and scores,
+    attention outputs) sits between two guard regions of CANARY_PAD elements
+    holding a fixed pattern; check_canaries() asserts that no call wrote there."""
 
     def __init__(self, wl: Workload, ck_dtype: str = "fp32", device: str = "cuda", **cfg_over):
         self.wl = wl
@@ -63,8 +84,27 @@ class DeviceWorkload:
         self.ck_offsets = torch.tensor(off, dtype=torch.int64, device=device)
         total = int(off[-1]) * wl.num_kv_heads * wl.head_dim
         tdt = torch.int16 if ck_dtype == "bf16" else torch.float32
-        self.ck = torch.zeros(max(total, 1), dtype=tdt, device=device)
+        self._canaries = []
+        self.ck = self.guarded((max(total, 1),), tdt)
+        self.ck.zero_()
         self._ws = {}
+
+    # ---------------------------------------------------------------- guarded outputs
+    def guarded(self, shape, dtype) -> torch.Tensor:
+        """An output tensor of `shape` inside a canary-filled buffer."""
+        n = int(np.prod(shape))
+        full = torch.empty(n + 2 * CANARY_PAD, dtype=dtype, device=self.device)
+        _canary_fill(full)
+        self._canaries.append((full, n))
+        return full[CANARY_PAD:CANARY_PAD + n].view(tuple(shape))
+
+    def check_canaries(self) -> int:
+        """Assert every guard region is untouched; returns how many were checked."""
+        torch.cuda.synchronize()
+        for full, n in self._canaries:
+            assert _canary_ok(full[:CANARY_PAD]), "a call wrote before its output buffer"
+            assert _canary_ok(full[CANARY_PAD + n:]), "a call wrote past its output buffer"
+        return len(self._canaries)
 
     # ---------------------------------------------------------------- workspaces
     def ws(self, op: int, rows: int, batch: int, max_len: int) -> torch.Tensor:
@@ -101,8 +141,8 @@ class DeviceWorkload:
     # ---------------------------------------------------------------- decode
     def select_decode(self, q: Optional[torch.Tensor] = None):
         B, hkv, k = self.wl.batch, self.wl.num_kv_heads, self.cfg.topk
-        idx = torch.empty((B, hkv, k), dtype=torch.int32, device=self.device)
-        score = torch.empty((B, hkv, k), dtype=torch.float32, device=self.device)
+        idx = self.guarded((B, hkv, k), torch.int32)
+        score = self.guarded((B, hkv, k), torch.float32)
         ws = self.ws(tbs.OP_SELECT_DECODE, B, B, self.max_len)
         tbs.infv2_select_blocks(self.cfg, tbs.INFV2_MODE_DECODE, self.q if q is None else q, B, 0,
                                 self.ck, self.ck_offsets, self.kv_offsets, self.kv_lens, B,
@@ -111,7 +151,8 @@ class DeviceWorkload:
 
     def attn_decode(self, idx: torch.Tensor, q: Optional[torch.Tensor] = None) -> torch.Tensor:
         B = self.wl.batch
-        out = torch.empty_like(self.q if q is None else q)
+        qq = self.q if q is None else q
+        out = self.guarded(tuple(qq.shape), qq.dtype)
         ws = self.ws(tbs.OP_ATTN_DECODE, B, B, self.max_len)
         tbs.infv2_sparse_attn_decode(self.cfg, self.q if q is None else q, self.k, self.v,
                                      self.kv_offsets, self.kv_lens, B, self.max_len, idx, out, ws)
@@ -129,12 +170,12 @@ class DeviceWorkload:
         rows = q1 - q0
         hkv, k = wl.num_kv_heads, self.cfg.topk
         q = self.q[q0:q1]
-        idx = torch.empty((rows, hkv, k), dtype=torch.int32, device=self.device)
-        score = torch.empty((rows, hkv, k), dtype=torch.float32, device=self.device)
+        idx = self.guarded((rows, hkv, k), torch.int32)
+        score = self.guarded((rows, hkv, k), torch.float32)
         ws = self.ws(tbs.OP_SELECT_PREFILL, rows, 1, q1)
         tbs.infv2_select_blocks(self.cfg, tbs.INFV2_MODE_PREFILL, q, rows, q0, self.ck,
                                 self.ck_offsets, self.kv_offsets, None, 1, q1, idx, score, ws)
-        out = torch.empty_like(q)
+        out = self.guarded(tuple(q.shape), q.dtype)
         wsa = self.ws(tbs.OP_ATTN_PREFILL, rows, 1, q1)
         tbs.infv2_sparse_attn_prefill(self.cfg, q, rows, q0, self.k, self.v, self.kv_offsets, idx,
                                       out, wsa)

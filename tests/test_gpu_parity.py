@@ -107,7 +107,7 @@ def _run_decode(wl, ck_dtype="fp32", label="decode"):
         want[b] = ref.attend_with_selection(q[b:b + 1], wl.k_f64(b), wl.v_f64(b), [n - 1],
                                             idx[b:b + 1], prm)[0]
     err = assert_close(out, want, wl.io_dtype, label)
-    _say(f"{label}: output max abs err {err:.2e}")
+    _say(f"{label}: output max abs err {err:.2e}, {dev.check_canaries()} guarded buffers untouched")
     return dev, idx, out
 
 
@@ -363,7 +363,8 @@ def _run_prefill(wl, chunk, ck_dtype="fp32", positions=None, label="prefill"):
     _check_rows(np.array(idx_rows), np.array(score_rows), rows, label)
     want = ref.attend_with_selection(q[pos], K, V, pos, idx[pos], prm)
     err = assert_close(out[pos], want, wl.io_dtype, label)
-    _say(f"{label}: output max abs err {err:.2e} over {len(pos)} rows")
+    _say(f"{label}: output max abs err {err:.2e} over {len(pos)} rows, "
+         f"{dev.check_canaries()} guarded buffers untouched")
     return dev, idx, out
 
 
@@ -391,13 +392,102 @@ def test_prefill_bf16_ck_and_forced_only():
     _run_prefill(wl, 250, label="prefill forced-only")
 
 
-def test_prefill_config3_sampled_rows():
+def test_prefill_config3_last_chunk_all_rows():
+    """Config 3 (32K, chunks of 4096): every row of the last chunk (all 256
+    16-row groups of the attention kernel), plus sampled rows of the others."""
     wl = make_config(3)
     rng = np.random.default_rng(303)
     L = int(wl.lens[0])
-    pos = sorted(set(rng.integers(0, L, 48).tolist()) | set(range(L - 160, L))
+    pos = sorted(set(rng.integers(0, L - wl.chunk, 48).tolist()) | set(range(L - wl.chunk, L))
                  | {0, 63, 64, 4095, 4096, 4097, 8191})
     _run_prefill(wl, wl.chunk, positions=pos, label="config 3 prefill")
+
+
+def _boundary_ties(rows):
+    """Selections whose k'-th and (k'+1)-th candidate scores are exactly equal."""
+    n = 0
+    for rs in rows:
+        cand = np.nonzero(~rs.forced)[0]
+        sc = np.sort(rs.S[cand])[::-1]
+        if rs.kprime > 0 and sc.shape[0] > rs.kprime and sc[rs.kprime - 1] == sc[rs.kprime]:
+            n += 1
+    return n
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_decode_configs_many_queries(cfg):
+    """Configs 1 and 2 at full size over 32 decode queries each: selections,
+    block scores and outputs against the oracle, in guarded buffers; reports how
+    many selections had an exact tie at the k-boundary."""
+    from synth import extra_decode_queries
+    h = _harness()
+    wl = make_config(cfg)
+    nq = 32
+    _say(f"config {cfg} decode, {nq} queries")
+    dev = h.DeviceWorkload(wl)
+    dev.compress()
+    qbits = extra_decode_queries(wl, nq)                       # [nq][1][Hq][d]
+    prm = params_of(wl)
+    K, V = wl.k_f64(0), wl.v_f64(0)
+    n = K.shape[1]
+    ck = dev.ck_host()[0]
+    assert np.array_equal(ck, ref.compress_keys(K, wl.kernel_size, wl.kernel_stride, "fp32"))
+    from synth import bf16_bits_to_f32
+    rows, idx_rows, score_rows, outs, wants = [], [], [], [], []
+    for r in range(nq):
+        q_t = h.to_device(qbits[r])
+        idx_t, score_t = dev.select_decode(q_t)
+        out = h.from_device(dev.attn_decode(idx_t, q_t), "bf16")
+        q = bf16_bits_to_f32(qbits[r]).astype(np.float64)
+        gi = idx_t.cpu().numpy().astype(np.int64)
+        gs = score_t.cpu().numpy().astype(np.float64)
+        for g in range(wl.num_kv_heads):
+            rows.append(ref.select_row(q[0, 16 * g:16 * g + 16], ck[g], n - 1, prm))
+            idx_rows.append(gi[0, g])
+            score_rows.append(gs[0, g])
+        want = ref.attend_with_selection(q, K, V, [n - 1], gi, prm)
+        assert_close(out, want, "bf16", f"config {cfg} query {r}")
+    exact, band = _check_rows(np.array(idx_rows), np.array(score_rows), rows, f"config {cfg} decode x{nq}")
+    _say(f"config {cfg}: {_boundary_ties(rows)} of {len(rows)} selections have an exact tie at the "
+         f"k-boundary; {dev.check_canaries()} guarded buffers untouched")
+
+
+@pytest.mark.parametrize("m,p,s,topk,L", [(16, 256, 256, 24, 20000), (128, 64, 32, 12, 6000)])
+def test_prefill_other_kernel_geometries(m, p, s, topk, L):
+    """bf16 prefill with kernel sizes and strides other than 32 / 16: a 64-kernel
+    tile of stride 256 spans more than 512 blocks of 16 (the selection's
+    multi-range path), and kernels of 64 at stride 32 over blocks of 128."""
+    wl = _small(mode="prefill", lens=[L], topk=topk, local=2, seed=140 + m, block_size=m,
+                kernel_size=p, kernel_stride=s)
+    rng = np.random.default_rng(140 + m)
+    pos = sorted(set(rng.integers(0, L, 96).tolist()) | set(range(L - 64, L)) | {p - 1, p, L // 2})
+    _run_prefill(wl, 4096, positions=pos, label=f"prefill m={m} p={p} s={s}")
+
+
+def test_default_scales_equal_explicit_ones():
+    """attn_scale = 0 and score_scale = 0 in the C struct select 1/sqrt(d) and 1:
+    the same bits as passing those values."""
+    import dataclasses
+    import math as _m
+    import trainable_block_sparse_amd as tbs
+    h = _harness()
+    wl = _small(lens=[5000, 900], topk=8, local=2, seed=151)
+    _say("default scales vs explicit")
+    dev = h.DeviceWorkload(wl)
+    dev.compress()
+    idx0, _ = dev.select_decode()
+    out0 = dev.attn_decode(idx0)
+    dev.cfg = dataclasses.replace(dev.cfg, attn_scale=float(np.float32(1.0 / _m.sqrt(128))),
+                                  score_scale=1.0)
+    idx1, _ = dev.select_decode()
+    out1 = dev.attn_decode(idx1)
+    dev.cfg = dataclasses.replace(dev.cfg, attn_scale=0.0, score_scale=0.0)
+    idx2, _ = dev.select_decode()
+    out2 = dev.attn_decode(idx2)
+    torch.cuda.synchronize()
+    assert torch.equal(idx0, idx1) and torch.equal(out0, out1)
+    assert torch.equal(idx0, idx2) and torch.equal(out0, out2)
+    assert tbs.Config().to_c().attn_scale == 0.0
 
 
 def _with_keys(wl, keys_of_seq):
