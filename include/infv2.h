@@ -82,7 +82,8 @@ typedef enum infv2_status {
                                    negative or non-finite scale */
     INFV2_ERR_UNSUPPORTED = 3,  /* valid but not implemented on this device path */
     INFV2_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than infv2_workspace_bytes */
-    INFV2_ERR_DEVICE = 5        /* a HIP launch failed */
+    INFV2_ERR_DEVICE = 5,       /* a HIP launch failed */
+    INFV2_ERR_SCRATCH = 6       /* the call needs more than the library's static scratch */
 } infv2_status;
 
 typedef enum infv2_dtype {
@@ -278,6 +279,26 @@ int32_t infv2_sparse_attn_prefill(const infv2_config* cfg, const void* q, int32_
                                   int64_t q_start, const void* k, const void* v,
                                   const int64_t* kv_offsets, const int32_t* block_idx, void* out,
                                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * infv2_sparse_attn_decode_noalloc -- infv2_sparse_attn_decode for callers that
+ * cannot allocate device memory (code captured into a HIP graph, tight serving
+ * loops, harnesses that forbid hipMalloc): no workspace argument.  The split
+ * partials go to a static device array of INFV2_NOALLOC_SCRATCH_BYTES inside the
+ * library (one per GPU, held until the process ends); the call allocates
+ * nothing.  Same arguments, results and errors as infv2_sparse_attn_decode,
+ * plus INFV2_ERR_SCRATCH (nothing enqueued) when infv2_workspace_bytes(op =
+ * ATTN_DECODE) for these sizes exceeds INFV2_NOALLOC_SCRATCH_BYTES, and
+ * INFV2_ERR_DEVICE if the scratch address cannot be obtained.  Every call on a
+ * GPU uses that GPU's one array, so calls that overlap in time on one GPU (on
+ * different streams) race; calls ordered on one stream are safe.  The scratch
+ * needs no initial contents (every partial is written before it is read).
+ */
+#define INFV2_NOALLOC_SCRATCH_BYTES (32u << 20)
+int32_t infv2_sparse_attn_decode_noalloc(const infv2_config* cfg, const void* q, const void* k,
+                                         const void* v, const int64_t* kv_offsets,
+                                         const int64_t* kv_lens, int32_t batch, int64_t max_len,
+                                         const int32_t* block_idx, void* out, void* stream);
 
 /*
  * Varlen prefill: several sequences in one call (serving-style prefill).  The

@@ -49,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_abi_version_and_status_strings(lib):
     ver = int(re.search(r"#define INFV2_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
     assert tbs.infv2_abi_version() == ver
-    for st in range(6):
+    for st in range(7):
         assert tbs.infv2_status_str(st).startswith("INFV2_")
 
 

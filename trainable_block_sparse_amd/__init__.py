@@ -27,7 +27,8 @@ KERNELS = ("compress", "select_logits", "select_scores", "select_prefill", "sele
            "bwd_index", "bwd_col")
 KERNEL_ID = {name: i for i, name in enumerate(KERNELS)}
 STATUS = {0: "INFV2_OK", 1: "INFV2_ERR_NULL", 2: "INFV2_ERR_SHAPE", 3: "INFV2_ERR_UNSUPPORTED",
-          4: "INFV2_ERR_WORKSPACE", 5: "INFV2_ERR_DEVICE"}
+          4: "INFV2_ERR_WORKSPACE", 5: "INFV2_ERR_DEVICE", 6: "INFV2_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 32 << 20      # INFV2_NOALLOC_SCRATCH_BYTES
 
 
 class Infv2Error(RuntimeError):
@@ -98,6 +99,7 @@ def load_library(path: str = LIB_PATH):
         "infv2_select_blocks_coarse": (i32, [cfgp, i32, i32, vp, i32, i64, vp, vp, vp, vp, vp, vp,
                                              i32, i64, vp, vp, vp, sz, vp]),
         "infv2_sparse_attn_decode": (i32, [cfgp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, sz, vp]),
+        "infv2_sparse_attn_decode_noalloc": (i32, [cfgp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp]),
         "infv2_sparse_attn_prefill": (i32, [cfgp, vp, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp]),
         "infv2_sparse_attn_prefill_bwd": (i32, [cfgp, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp,
                                                 vp, vp, sz, vp]),
@@ -116,7 +118,7 @@ def load_library(path: str = LIB_PATH):
 
 
 EXPORTED = ("infv2_compress_keys", "infv2_append_kv", "infv2_select_blocks",
-            "infv2_select_blocks_coarse", "infv2_sparse_attn_decode",
+            "infv2_select_blocks_coarse", "infv2_sparse_attn_decode", "infv2_sparse_attn_decode_noalloc",
             "infv2_sparse_attn_prefill", "infv2_select_blocks_varlen",
             "infv2_sparse_attn_prefill_varlen", "infv2_sparse_attn_prefill_bwd", "infv2_workspace_bytes", "infv2_num_kernels",
             "infv2_status_str", "infv2_abi_version", "infv2_timing_start", "infv2_timing_stop")
@@ -265,6 +267,14 @@ def infv2_sparse_attn_decode(cfg: Config, q, k, v, kv_offsets, kv_lens, batch: i
         ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(kv_offsets), _ptr(kv_lens), batch,
         max_len, _ptr(block_idx), _ptr(out), _ptr(ws), nbytes, _stream(stream)),
         "infv2_sparse_attn_decode")
+
+
+def infv2_sparse_attn_decode_noalloc(cfg: Config, q, k, v, kv_offsets, kv_lens, batch: int,
+                                     max_len: int, block_idx, out, stream=None) -> None:
+    c = cfg.to_c()
+    _check(load_library().infv2_sparse_attn_decode_noalloc(
+        ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(kv_offsets), _ptr(kv_lens), batch,
+        max_len, _ptr(block_idx), _ptr(out), _stream(stream)), "infv2_sparse_attn_decode_noalloc")
 
 
 def infv2_sparse_attn_prefill(cfg: Config, q, rows: int, q_start: int, k, v, kv_offsets,

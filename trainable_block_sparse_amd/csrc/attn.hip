@@ -14,11 +14,42 @@
 //                        LogSumExp.
 //   attn_prefill_kernel  grid (row, KV head): all selected blocks of one row,
 //                        causal within the query's own block (t <= i).
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace infv2 {
 
+// Scratch of infv2_sparse_attn_decode_noalloc: the decode attention's split
+// partials live in this file-scope device array instead of a caller workspace.
+// Every device the library runs on holds its own copy until the process ends.
+// Host code never passes the array's name to a kernel (on the host it is only a
+// stand-in for the symbol): it uses the device address that hipGetSymbolAddress
+// returns, fetched once per device on the first call made on that device.
+static __device__ __align__(256) char scratch[INFV2_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 constexpr int kTok = 64;             // tokens per LDS tile
 

@@ -88,6 +88,7 @@ const char* infv2_status_str(int32_t s) {
         case INFV2_ERR_UNSUPPORTED: return "INFV2_ERR_UNSUPPORTED: valid but not implemented on this path";
         case INFV2_ERR_WORKSPACE: return "INFV2_ERR_WORKSPACE: workspace missing or too small";
         case INFV2_ERR_DEVICE: return "INFV2_ERR_DEVICE: a HIP launch failed";
+        case INFV2_ERR_SCRATCH: return "INFV2_ERR_SCRATCH: the call needs more than the library's static scratch";
         default: return "INFV2: unknown status";
     }
 }
@@ -220,6 +221,24 @@ int32_t infv2_sparse_attn_decode(const infv2_config* c, const void* q, const voi
     if (!ws || ws_bytes < need) return INFV2_ERR_WORKSPACE;
     return status_of(infv2::launch_attn_decode(make_shape(c), q, k, v, kv_offsets, kv_lens, batch,
                                                block_idx, out, ws,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int32_t infv2_sparse_attn_decode_noalloc(const infv2_config* c, const void* q, const void* k,
+                                         const void* v, const int64_t* kv_offsets,
+                                         const int64_t* kv_lens, int32_t batch, int64_t max_len,
+                                         const int32_t* block_idx, void* out, void* stream) {
+    int32_t st = check_config(c);
+    if (st != INFV2_OK) return st;
+    if (!q || !k || !v || !kv_offsets || !block_idx || !out) return INFV2_ERR_NULL;
+    if (batch < 1) return INFV2_ERR_SHAPE;
+    if ((st = check_len(c, max_len)) != INFV2_OK) return st;
+    const size_t need = ws_bytes_for(c, INFV2_OP_ATTN_DECODE, batch, batch, max_len);
+    if (need > INFV2_NOALLOC_SCRATCH_BYTES) return INFV2_ERR_SCRATCH;
+    void* scratch = nullptr;
+    if (infv2::decode_scratch(&scratch) != hipSuccess) return INFV2_ERR_DEVICE;
+    return status_of(infv2::launch_attn_decode(make_shape(c), q, k, v, kv_offsets, kv_lens, batch,
+                                               block_idx, out, scratch,
                                                static_cast<hipStream_t>(stream)));
 }
 

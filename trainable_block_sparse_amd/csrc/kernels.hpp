@@ -113,6 +113,11 @@ hipError_t launch_select_prefill(const Shape& sh, const void* q, int rows, int64
                                  int32_t* idx, float* score, void* ws, const CoarseSel* cs,
                                  hipStream_t st);
 
+// Device address of this device's static decode scratch (INFV2_NOALLOC_SCRATCH_BYTES,
+// looked up once per device); the no-allocation decode entry point passes it as
+// the workspace.
+hipError_t decode_scratch(void** ptr);
+
 hipError_t launch_attn_decode(const Shape& sh, const void* q, const void* k, const void* v,
                               const int64_t* kv_off, const int64_t* kv_lens, int batch,
                               const int32_t* idx, void* out, void* ws, hipStream_t st);
