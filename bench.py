@@ -184,7 +184,8 @@ DECODE_FAMILIES = ("compress", "select_logits", "select_scores", "select_topk", 
 def decode_bytes(wl, ck_bytes: int, n_list) -> dict:
     """Algorithmic HBM bytes of one decode step, per call of each entry point."""
     kb = decode_kernel_bytes(wl, ck_bytes, n_list)
-    return {"compress": kb["compress"], "select": kb["select_logits"] + kb["select_topk"],
+    fused = kb["compress"] if wl.io_dtype == "bf16" else 0     # counted in the logits kernel too
+    return {"compress": kb["compress"], "select": kb["select_logits"] - fused + kb["select_topk"],
             "attn": kb["attn_decode"] + kb["attn_merge"]}
 
 
@@ -198,9 +199,11 @@ def decode_kernel_bytes(wl, ck_bytes: int, n_list) -> dict:
     sel_kv = sum(hkv * min(k * m, n) * d * esz * 2 for n in n_list)
     ck = sum(hkv * num_kernels(n, wl.kernel_size, wl.kernel_stride) * d * ck_bytes for n in n_list)
     B = len(n_list)
+    new_ck = B * hkv * (wl.kernel_size * d * esz + d * ck_bytes)      # p keys in, one CK out
     return {
-        "compress": B * hkv * (wl.kernel_size * d * esz + d * ck_bytes),   # p keys in, one CK out
-        "select_logits": ck + B * q_b,                                    # every visible CK, q
+        "compress": new_ck,
+        "select_logits": ck + B * q_b + (new_ck if esz == 2 else 0),     # every visible CK, q (and
+                                                                          # the fused new CK, bf16)
         "select_topk": B * hkv * k * 4,                                   # block ids out
         "attn_decode": sel_kv + B * (q_b + hkv * k * 4),                  # selected K/V, q, ids
         "attn_merge": B * q_b,                                            # output rows
@@ -251,7 +254,14 @@ def bench_decode(cfg_index: int, args, torch, tbs, gh, replicas: int = 0, ck_dty
         tbs.infv2_sparse_attn_decode(cfg, qs[r], Ks[r], Vs[r], dev.kv_offsets, dev.kv_lens, B, n_max,
                                      idx, outs[r], ws_att)
 
+    ws_step = dev.ws(tbs.OP_DECODE_STEP, B, B, n_max)
+
     def step(r):
+        # one call: the newest token's compressed key, the selection and the attention
+        tbs.infv2_decode_step(cfg, qs[r], Ks[r], Vs[r], dev.kv_offsets, dev.kv_lens, dev.ck_offsets,
+                              CKs[r], B, n_max, idx, outs[r], ws_step)
+
+    def step_separate(r):
         compress(r)
         select(r)
         attn(r)
@@ -272,7 +282,7 @@ def bench_decode(cfg_index: int, args, torch, tbs, gh, replicas: int = 0, ck_dty
     per = np.array([[a.elapsed_time(b) for a, b in zip(x[:-1], x[1:])] for x in ev]) * 1e3  # us
     per_us = dict(zip(["compress", "select", "attn"], per.mean(axis=0).tolist()))
     kt = kernel_times(tbs, torch, lambda t: step(order[t % K]), K, DECODE_FAMILIES)
-    # whole steps, eager
+    # whole steps, eager: the one-call step, and the three entry points in turn
     torch.cuda.synchronize()
     flush_mall(torch)
     s0 = T.event()
@@ -281,6 +291,13 @@ def bench_decode(cfg_index: int, args, torch, tbs, gh, replicas: int = 0, ck_dty
     s1 = T.event()
     torch.cuda.synchronize()
     eager_ms = s0.elapsed_time(s1) / K
+    flush_mall(torch)
+    s0 = T.event()
+    for r in order:
+        step_separate(r)
+    s1 = T.event()
+    torch.cuda.synchronize()
+    eager_sep_ms = s0.elapsed_time(s1) / K
     # whole steps, HIP-graph replay: one graph holds the K timed steps (K
     # "layers" of one decode token), captured once, warmed once, then replayed
     # after a cache flush
@@ -310,7 +327,9 @@ def bench_decode(cfg_index: int, args, torch, tbs, gh, replicas: int = 0, ck_dty
     distinct = len(set(order))
     res = {
         "workload": wl.name, "batch": B, "lens_min": int(wl.lens.min()), "lens_max": n_max,
+        "step": "infv2_decode_step (newest token's compressed key + selection + attention)",
         "ms_per_step": ms, "ms_per_step_eager": eager_ms, "ms_per_step_graph": graph_ms,
+        "ms_per_step_eager_separate_calls": eager_sep_ms,
         "tok_per_s": B / (ms * 1e-3), "per_call_us": per_us, "kernels": kt,
         "bytes_per_step": step_bytes,
         "bytes_per_call": nb, "hbm_gbps_step": step_bytes / (ms * 1e-3) / 1e9,
@@ -326,7 +345,7 @@ def bench_decode(cfg_index: int, args, torch, tbs, gh, replicas: int = 0, ck_dty
                                 "hbm", HBM_PEAK_GBS, "GB/s", 1e9),
     }
     # spot parity of the timed path: replica 0, oracle selection on the same query
-    res["parity"] = decode_spot_parity(wl, dev, qs, outs, idx, select, attn, ck_dtype, torch, gh)
+    res["parity"] = decode_spot_parity(wl, dev, qs, outs, idx, lambda: step(0), ck_dtype, torch, gh)
     del Ks, Vs, CKs
     torch.cuda.empty_cache()
     return res
@@ -415,11 +434,10 @@ def bench_decode_loop(args, torch, tbs, gh) -> dict:
                     "every replay"}
 
 
-def decode_spot_parity(wl, dev, qs, outs, idx, select, attn, ck_dtype, torch, gh) -> str:
+def decode_spot_parity(wl, dev, qs, outs, idx, run0, ck_dtype, torch, gh) -> str:
     from oracle import infv2_ref as ref
     from tests.parity import accept_selection, assert_close
-    select(0)
-    attn(0)
+    run0()
     torch.cuda.synchronize()
     gi = idx.cpu().numpy().astype(np.int64)
     go = gh.from_device(outs[0], wl.io_dtype)

@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define INFV2_ABI_VERSION 7
+#define INFV2_ABI_VERSION 8
 
 typedef enum infv2_status {
     INFV2_OK = 0,
@@ -104,7 +104,8 @@ typedef enum infv2_op {         /* operation ids for infv2_workspace_bytes */
     INFV2_OP_ATTN_PREFILL = 4,
     INFV2_OP_ATTN_PREFILL_BWD = 5,
     INFV2_OP_SELECT_COARSE_DECODE = 6,
-    INFV2_OP_SELECT_COARSE_PREFILL = 7
+    INFV2_OP_SELECT_COARSE_PREFILL = 7,
+    INFV2_OP_DECODE_STEP = 8
 } infv2_op;
 
 /* Method hyper-parameters (names follow the pages' notation). */
@@ -260,6 +261,31 @@ int32_t infv2_sparse_attn_decode(const infv2_config* cfg, const void* q, const v
                                  const void* v, const int64_t* kv_offsets, const int64_t* kv_lens,
                                  int32_t batch, int64_t max_len, const int32_t* block_idx,
                                  void* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * infv2_decode_step -- one decode step of the whole path for every sequence of
+ * a batch, in one call: the compressed key of the kernel that the newest token
+ * completes ("Semantic kernels": with complete kernels only, token n - 1
+ * completes kernel (n - p) / s when n >= p and s divides n - p), block
+ * selection (step 1b) and sparse attention (step 2).  The results are those of
+ * infv2_compress_keys for that kernel, then infv2_select_blocks (decode, no
+ * scores) and infv2_sparse_attn_decode, bit for bit; with bf16 inputs the
+ * compression runs inside the selection's first kernel (one launch fewer).
+ *
+ *   q, k, v, kv_offsets, kv_lens, batch, max_len   as for infv2_sparse_attn_decode;
+ *                kv_lens[b] = n_b counts the newest token, whose K/V row must
+ *                already be at position n_b - 1 of the cache (infv2_append_kv
+ *                or the caller's own write); kv_lens == NULL: the capacities
+ *   ck_offsets, ck   compressed keys (see Layouts), kernels up to the newest
+ *                token's present except the one it completes, which is written
+ *   block_idx    device int32 [batch][Hkv][topk] (written)
+ *   out          device, io_dtype [batch][Hq][d] (written)
+ *   ws           infv2_workspace_bytes(op = DECODE_STEP); no initial contents needed
+ */
+int32_t infv2_decode_step(const infv2_config* cfg, const void* q, const void* k, const void* v,
+                          const int64_t* kv_offsets, const int64_t* kv_lens,
+                          const int64_t* ck_offsets, void* ck, int32_t batch, int64_t max_len,
+                          int32_t* block_idx, void* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * infv2_sparse_attn_prefill -- step 2 for a chunk of consecutive query rows

@@ -595,6 +595,59 @@ def test_varlen_prefill_equals_per_sequence_calls():
         r0 = r1
 
 
+@pytest.mark.parametrize("io,ck_dtype", [("bf16", "fp32"), ("bf16", "bf16"), ("fp32", "fp32")])
+def test_decode_step_equals_separate_calls(io, ck_dtype):
+    """infv2_decode_step (compressed key of the kernel the newest token completes,
+    selection, attention in one call; with bf16 the compression runs inside the
+    selection's first kernel) equals infv2_compress_keys + infv2_select_blocks +
+    infv2_sparse_attn_decode bit for bit, over 40 steps of growing caches that
+    complete a kernel every 16 tokens; the compressed keys end equal to the
+    oracle's."""
+    import trainable_block_sparse_amd as tbs
+    from synth import extra_decode_queries
+    h = _harness()
+    wl = _small(lens=[3001, 700, 4500, 33], io=io, topk=8, local=2, seed=171)
+    _say(f"decode step vs separate calls io={io} ck={ck_dtype}")
+    a = h.DeviceWorkload(wl, ck_dtype)
+    b = h.DeviceWorkload(wl, ck_dtype)
+    p, s = wl.kernel_size, wl.kernel_stride
+    final = wl.lens.astype(np.int64)
+    start = np.maximum(final - 40, 1)
+    for dev in (a, b):
+        dev.compress(kv_lens=torch.tensor(start - 1, device="cuda"))
+    qs = h.to_device(extra_decode_queries(wl, 41))
+    B, hkv, k = wl.batch, wl.num_kv_heads, wl.topk
+    ws_step = torch.zeros(tbs.infv2_workspace_bytes(a.cfg, tbs.OP_DECODE_STEP, B, B, a.max_len),
+                          dtype=torch.uint8, device="cuda")
+    ws_s = b.ws(tbs.OP_SELECT_DECODE, B, B, b.max_len)
+    ws_a = b.ws(tbs.OP_ATTN_DECODE, B, B, b.max_len)
+    for step in range(41):
+        cur = np.minimum(start + step, final)
+        lens = torch.tensor(cur, dtype=torch.int64, device="cuda")
+        idx_a = a.guarded((B, hkv, k), torch.int32)
+        out_a = a.guarded(tuple(qs[step].shape), qs[step].dtype)
+        tbs.infv2_decode_step(a.cfg, qs[step], a.k, a.v, a.kv_offsets, lens, a.ck_offsets, a.ck, B,
+                              a.max_len, idx_a, out_a, ws_step)
+        # separate calls: the newest token's kernel (or, when it completes none, the
+        # last complete one again: the same value), then selection and attention
+        begin = torch.tensor([max(0, h.num_kernels(int(n), p, s) - 1) for n in cur], device="cuda")
+        b.compress(kv_lens=lens, ck_begin=begin, max_new=1)
+        idx_b = torch.empty((B, hkv, k), dtype=torch.int32, device="cuda")
+        tbs.infv2_select_blocks(b.cfg, tbs.INFV2_MODE_DECODE, qs[step], B, 0, b.ck, b.ck_offsets,
+                                b.kv_offsets, lens, B, b.max_len, idx_b, None, ws_s)
+        out_b = torch.empty_like(qs[step])
+        tbs.infv2_sparse_attn_decode(b.cfg, qs[step], b.k, b.v, b.kv_offsets, lens, B, b.max_len,
+                                     idx_b, out_b, ws_a)
+        torch.cuda.synchronize()
+        assert torch.equal(idx_a, idx_b), f"step {step}: selection differs"
+        assert torch.equal(out_a, out_b), f"step {step}: output differs"
+    assert torch.equal(a.ck, b.ck)
+    cks = a.ck_host()
+    for sq in range(B):
+        assert np.array_equal(cks[sq], ref.compress_keys(wl.k_f64(sq), p, s, ck_dtype)), f"seq {sq}"
+    _say(f"decode step: 41 steps equal, {a.check_canaries()} guarded buffers untouched")
+
+
 def test_decode_equals_last_prefill_row():
     h = _harness()
     wl = _small(mode="prefill", lens=[1500], topk=8, local=2, seed=34)

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libinfv2.so")
 INFV2_FP32, INFV2_BF16 = 0, 1
 INFV2_MODE_DECODE, INFV2_MODE_PREFILL = 0, 1
 (OP_COMPRESS, OP_SELECT_DECODE, OP_SELECT_PREFILL, OP_ATTN_DECODE, OP_ATTN_PREFILL,
- OP_ATTN_PREFILL_BWD, OP_SELECT_COARSE_DECODE, OP_SELECT_COARSE_PREFILL) = range(8)
+ OP_ATTN_PREFILL_BWD, OP_SELECT_COARSE_DECODE, OP_SELECT_COARSE_PREFILL, OP_DECODE_STEP) = range(9)
 # kernel families for infv2_timing_start (infv2_kernel in infv2.h)
 KERNELS = ("compress", "select_logits", "select_scores", "select_prefill", "select_topk",
            "attn_decode", "attn_merge", "attn_prefill", "vt_build", "append", "bwd_row",
@@ -100,6 +100,7 @@ def load_library(path: str = LIB_PATH):
                                              i32, i64, vp, vp, vp, sz, vp]),
         "infv2_sparse_attn_decode": (i32, [cfgp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, sz, vp]),
         "infv2_sparse_attn_decode_noalloc": (i32, [cfgp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp]),
+        "infv2_decode_step": (i32, [cfgp, vp, vp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, sz, vp]),
         "infv2_sparse_attn_prefill": (i32, [cfgp, vp, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp]),
         "infv2_sparse_attn_prefill_bwd": (i32, [cfgp, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp,
                                                 vp, vp, sz, vp]),
@@ -118,7 +119,7 @@ def load_library(path: str = LIB_PATH):
 
 
 EXPORTED = ("infv2_compress_keys", "infv2_append_kv", "infv2_select_blocks",
-            "infv2_select_blocks_coarse", "infv2_sparse_attn_decode", "infv2_sparse_attn_decode_noalloc",
+            "infv2_select_blocks_coarse", "infv2_sparse_attn_decode", "infv2_sparse_attn_decode_noalloc", "infv2_decode_step",
             "infv2_sparse_attn_prefill", "infv2_select_blocks_varlen",
             "infv2_sparse_attn_prefill_varlen", "infv2_sparse_attn_prefill_bwd", "infv2_workspace_bytes", "infv2_num_kernels",
             "infv2_status_str", "infv2_abi_version", "infv2_timing_start", "infv2_timing_stop")
@@ -267,6 +268,16 @@ def infv2_sparse_attn_decode(cfg: Config, q, k, v, kv_offsets, kv_lens, batch: i
         ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(kv_offsets), _ptr(kv_lens), batch,
         max_len, _ptr(block_idx), _ptr(out), _ptr(ws), nbytes, _stream(stream)),
         "infv2_sparse_attn_decode")
+
+
+def infv2_decode_step(cfg: Config, q, k, v, kv_offsets, kv_lens, ck_offsets, ck, batch: int,
+                      max_len: int, block_idx, out, ws, stream=None) -> None:
+    c = cfg.to_c()
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load_library().infv2_decode_step(
+        ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(kv_offsets), _ptr(kv_lens), _ptr(ck_offsets),
+        _ptr(ck), batch, max_len, _ptr(block_idx), _ptr(out), _ptr(ws), nbytes, _stream(stream)),
+        "infv2_decode_step")
 
 
 def infv2_sparse_attn_decode_noalloc(cfg: Config, q, k, v, kv_offsets, kv_lens, batch: int,

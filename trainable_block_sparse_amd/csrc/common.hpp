@@ -26,6 +26,17 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float x) {
     return __builtin_bit_cast(bf16_t, h);
 }
 
+// float64 -> bf16, one rounding to nearest even (including the subnormal range)
+__device__ __forceinline__ bf16_t f64_to_bf16(double x) {
+    if (x == 0.0 || !isfinite(x)) return f32_to_bf16(static_cast<float>(x));
+    int e;
+    frexp(x, &e);                         // |x| in [2^(e-1), 2^e)
+    const int ulp_exp = max(e - 1, -126) - 7;
+    const double y = ldexp(rint(ldexp(x, -ulp_exp)), ulp_exp);
+    const float f = static_cast<float>(y);   // exact (8 significant bits), or inf on overflow
+    return static_cast<bf16_t>(__float_as_uint(f) >> 16);
+}
+
 template <typename T> struct io;
 template <> struct io<float> {
     __device__ static __forceinline__ float load(const float* p) { return *p; }

@@ -15,17 +15,6 @@ namespace infv2 {
 constexpr int kCompressKpb = 16;   // kernels per thread block
 constexpr int kCompressFew = 4;    // up to this many new kernels: one block per kernel
 
-// float64 -> bf16, one rounding to nearest even (including the subnormal range)
-__device__ __forceinline__ bf16_t f64_to_bf16(double x) {
-    if (x == 0.0 || !isfinite(x)) return f32_to_bf16(static_cast<float>(x));
-    int e;
-    frexp(x, &e);                         // |x| in [2^(e-1), 2^e)
-    const int ulp_exp = max(e - 1, -126) - 7;
-    const double y = ldexp(rint(ldexp(x, -ulp_exp)), ulp_exp);
-    const float f = static_cast<float>(y);   // exact (8 significant bits), or inf on overflow
-    return static_cast<bf16_t>(__float_as_uint(f) >> 16);
-}
-
 template <typename Tin, bool kCkBf16>
 __global__ __launch_bounds__(256) void compress_kernel(
     const Tin* __restrict__ k, const int64_t* __restrict__ kv_off,
@@ -86,7 +75,8 @@ template <typename Tin, bool kCkBf16>
 __global__ __launch_bounds__(256) void compress_few_kernel(
     const Tin* __restrict__ k, const int64_t* __restrict__ kv_off,
     const int64_t* __restrict__ kv_lens, const int64_t* __restrict__ ck_off,
-    const int64_t* __restrict__ ck_begin, void* __restrict__ ck_out, int hkv, int p, int s) {
+    const int64_t* __restrict__ ck_begin, void* __restrict__ ck_out, int hkv, int p, int s,
+    int last_only) {
     __shared__ double part[8][kHeadDim];
     const int b = blockIdx.z, h = blockIdx.y;
     const int64_t o0 = kv_off[b], cap = kv_off[b + 1] - o0;
@@ -94,7 +84,9 @@ __global__ __launch_bounds__(256) void compress_few_kernel(
     n = n < cap ? n : cap;
     const int64_t nc = num_kernels(n, p, s);
     const int64_t c0 = ck_off[b], ccap = ck_off[b + 1] - c0;
-    const int64_t j = (ck_begin ? ck_begin[b] : 0) + blockIdx.x;
+    // last_only: the kernel that the newest token n - 1 completes, if it completes one
+    const int64_t j = last_only ? ((n >= p && (n - p) % s == 0) ? (n - p) / s : -1)
+                                : (ck_begin ? ck_begin[b] : 0) + blockIdx.x;
     if (j < 0 || j >= nc || j >= ccap) return;          // uniform over the block
     const int grp = threadIdx.x >> 5, col = (threadIdx.x & 31) * 4;
     const Tin* src = k + (o0 * hkv + static_cast<int64_t>(h) * cap + j * s) * kHeadDim + col;
@@ -192,12 +184,13 @@ hipError_t launch_append_kv(const Shape& sh, const void* k_new, const void* v_ne
 
 hipError_t launch_compress(const Shape& sh, const void* k, const int64_t* kv_off,
                            const int64_t* kv_lens, const int64_t* ck_off, const int64_t* ck_begin,
-                           int batch, int64_t max_new, void* ck, hipStream_t st) {
+                           int batch, int64_t max_new, void* ck, hipStream_t st, bool last_only) {
     if (max_new <= 0) return hipSuccess;
     KernelTimer kt(INFV2_KERNEL_COMPRESS, st);
-    if (max_new <= kCompressFew) {
-        const dim3 g1(static_cast<unsigned>(max_new), sh.hkv, batch);
-#define INFV2_FEW(TIN, CKB) compress_few_kernel<TIN, CKB><<<g1, 256, 0, st>>>(static_cast<const TIN*>(k), kv_off, kv_lens, ck_off, ck_begin, ck, sh.hkv, sh.p, sh.s)
+    if (max_new <= kCompressFew || last_only) {
+        const dim3 g1(last_only ? 1u : static_cast<unsigned>(max_new), sh.hkv, batch);
+        const int lo = last_only ? 1 : 0;
+#define INFV2_FEW(TIN, CKB) compress_few_kernel<TIN, CKB><<<g1, 256, 0, st>>>(static_cast<const TIN*>(k), kv_off, kv_lens, ck_off, ck_begin, ck, sh.hkv, sh.p, sh.s, lo)
         if (sh.io_bf16) { if (sh.ck_bf16) INFV2_FEW(bf16_t, true); else INFV2_FEW(bf16_t, false); }
         else { if (sh.ck_bf16) INFV2_FEW(float, true); else INFV2_FEW(float, false); }
 #undef INFV2_FEW

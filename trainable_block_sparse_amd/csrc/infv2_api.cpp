@@ -70,6 +70,9 @@ size_t ws_bytes_for(const infv2_config* c, int32_t op, int32_t rows, int32_t bat
         case INFV2_OP_ATTN_PREFILL_BWD: return rows > 0 ? infv2::bwd_ws(sh, rows, max_len).total : 0;
         case INFV2_OP_SELECT_COARSE_DECODE: return infv2::select_decode_ws(sh, batch, max_len).total_coarse;
         case INFV2_OP_SELECT_COARSE_PREFILL: return infv2::select_prefill_ws(sh, rows, max_len).total_coarse;
+        case INFV2_OP_DECODE_STEP:
+            return infv2::align256(infv2::select_decode_ws(sh, batch, max_len).total) +
+                   infv2::attn_decode_ws(sh, batch).total;
         default: return 0;
     }
 }
@@ -104,7 +107,7 @@ int32_t infv2_workspace_bytes(const infv2_config* c, int32_t op, int32_t rows, i
     int32_t st = check_config(c);
     if (st != INFV2_OK) return st;
     if ((st = check_len(c, max_len)) != INFV2_OK) return st;
-    if (op < INFV2_OP_COMPRESS || op > INFV2_OP_SELECT_COARSE_PREFILL || rows < 0 || batch < 0) return INFV2_ERR_SHAPE;
+    if (op < INFV2_OP_COMPRESS || op > INFV2_OP_DECODE_STEP || rows < 0 || batch < 0) return INFV2_ERR_SHAPE;
     *bytes = ws_bytes_for(c, op, rows, batch, max_len);
     return INFV2_OK;
 }
@@ -240,6 +243,38 @@ int32_t infv2_sparse_attn_decode_noalloc(const infv2_config* c, const void* q, c
     return status_of(infv2::launch_attn_decode(make_shape(c), q, k, v, kv_offsets, kv_lens, batch,
                                                block_idx, out, scratch,
                                                static_cast<hipStream_t>(stream)));
+}
+
+int32_t infv2_decode_step(const infv2_config* c, const void* q, const void* k, const void* v,
+                          const int64_t* kv_offsets, const int64_t* kv_lens,
+                          const int64_t* ck_offsets, void* ck, int32_t batch, int64_t max_len,
+                          int32_t* block_idx, void* out, void* ws, size_t ws_bytes, void* stream) {
+    int32_t st = check_config(c);
+    if (st != INFV2_OK) return st;
+    if (!q || !k || !v || !kv_offsets || !ck_offsets || !ck || !block_idx || !out)
+        return INFV2_ERR_NULL;
+    if (batch < 1) return INFV2_ERR_SHAPE;
+    if ((st = check_len(c, max_len)) != INFV2_OK) return st;
+    const size_t need = ws_bytes_for(c, INFV2_OP_DECODE_STEP, batch, batch, max_len);
+    if (!ws || ws_bytes < need) return INFV2_ERR_WORKSPACE;
+    const Shape sh = make_shape(c);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws_attn = static_cast<char*>(ws) + infv2::align256(infv2::select_decode_ws(sh, batch, max_len).total);
+    hipError_t e;
+    if (sh.io_bf16) {
+        // the selection's first kernel also builds the newest token's compressed key
+        e = infv2::launch_select_decode(sh, q, ck, ck_offsets, kv_offsets, kv_lens, batch, max_len,
+                                        block_idx, nullptr, ws, nullptr, s, k);
+    } else {
+        e = infv2::launch_compress(sh, k, kv_offsets, kv_lens, ck_offsets, nullptr, batch, 1, ck, s,
+                                   true);
+        if (e == hipSuccess)
+            e = infv2::launch_select_decode(sh, q, ck, ck_offsets, kv_offsets, kv_lens, batch,
+                                            max_len, block_idx, nullptr, ws, nullptr, s);
+    }
+    if (e != hipSuccess) return INFV2_ERR_DEVICE;
+    return status_of(infv2::launch_attn_decode(sh, q, k, v, kv_offsets, kv_lens, batch, block_idx,
+                                               out, ws_attn, s));
 }
 
 int32_t infv2_sparse_attn_prefill(const infv2_config* c, const void* q, int32_t rows,

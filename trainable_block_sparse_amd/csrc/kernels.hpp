@@ -86,9 +86,12 @@ struct AttnDecodeWs {
 };
 AttnDecodeWs attn_decode_ws(const Shape& sh, int batch);
 
+// last_only: for every sequence, only the kernel its newest token completes
+// (if any); ck_begin is then ignored
 hipError_t launch_compress(const Shape& sh, const void* k, const int64_t* kv_off,
                            const int64_t* kv_lens, const int64_t* ck_off, const int64_t* ck_begin,
-                           int batch, int64_t max_new, void* ck, hipStream_t st);
+                           int batch, int64_t max_new, void* ck, hipStream_t st,
+                           bool last_only = false);
 
 hipError_t launch_append_kv(const Shape& sh, const void* k_new, const void* v_new, void* k,
                             void* v, const int64_t* kv_off, int64_t* kv_lens,
@@ -101,12 +104,14 @@ struct CoarseSel {
     const int64_t* ckc_off;
 };
 
-// cs == nullptr: the exact selection
+// cs == nullptr: the exact selection.  fuse_k != nullptr (bf16 queries only):
+// the cached keys, from which the first kernel also computes and stores the
+// compressed key of the kernel each sequence's newest token completes.
 hipError_t launch_select_decode(const Shape& sh, const void* q, const void* ck,
                                 const int64_t* ck_off, const int64_t* kv_off,
                                 const int64_t* kv_lens, int batch, int64_t max_len,
                                 int32_t* idx, float* score, void* ws, const CoarseSel* cs,
-                                hipStream_t st);
+                                hipStream_t st, const void* fuse_k = nullptr);
 
 hipError_t launch_select_prefill(const Shape& sh, const void* q, int rows, int64_t q_start,
                                  const void* ck, const int64_t* ck_off, int64_t max_len,

@@ -185,14 +185,23 @@ __global__ __launch_bounds__(256) void sel_dec_logits(
 // the compressed keys are the A operand as stored (lane: 8 consecutive d of one
 // kernel); fp32 keys are split into bf16 hi + lo (x = hi + lo + O(2^-17 |x|)),
 // two MFMAs per tile, products exact in fp32.  Z^T puts one head per lane column.
-template <bool kCkBf16>
+//
+// kFuse (decode step): the block whose chunk holds the kernel that the newest
+// token n - 1 completes (n >= p, s divides n - p) first computes that kernel's
+// compressed key from the cached keys -- float64 sum of the p rows, rounded
+// once, as infv2_compress_keys does -- stores it for later steps, and scores it
+// from LDS, so the step needs no separate compression launch.
+template <bool kCkBf16, bool kFuse>
 __global__ __launch_bounds__(kLogWaves * 64) void sel_dec_logits_mfma(
     const bf16_t* __restrict__ q, const void* __restrict__ ck, const int64_t* __restrict__ ck_off,
     const int64_t* __restrict__ kv_off, const int64_t* __restrict__ lens, int lens_end, int hq,
     int hkv, int p, int s, float score_scale, int64_t nc_max, int64_t nc_ld, int nchunk,
     int64_t nblk_max, int64_t kld, float* __restrict__ logits, float2* __restrict__ partial,
-    uint32_t* __restrict__ keys) {
+    uint32_t* __restrict__ keys, const bf16_t* __restrict__ kcache, void* __restrict__ ck_w) {
     __shared__ float2 xm[kLogWaves][kGroup];   // each wave's (max, sum) per head
+    constexpr int kFuseParts = kLogWaves * 64 / 16;     // row groups of the fused key sum
+    __shared__ double fpart[kFuse ? kFuseParts : 1][kFuse ? kHeadDim : 1];
+    __shared__ float fkey[kFuse ? kHeadDim : 1];        // the new key as stored, widened
     const int b = blockIdx.z, g = blockIdx.y, ch = blockIdx.x, t = threadIdx.x;
     const int l = t & 63, wv = t >> 6, lg = l >> 4, lc = l & 15;
     // round trip 1: offsets, length and the queries (independent loads)
@@ -235,6 +244,78 @@ __global__ __launch_bounds__(kLogWaves * 64) void sel_dec_logits_mfma(
         } else {
 #pragma unroll
             for (int x = 0; x < kU; ++x) raw[m2][x] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+    // fused compression: the kernel j_new = nvis - 1 completed by token n - 1
+    const int64_t j_new = nvis - 1;
+    const bool fuse = kFuse && n >= p && (n - p) % s == 0 && j_new < ccap && j_new >= j0 &&
+                      j_new < j0 + kChunkA;               // uniform over the block
+    if (kFuse && fuse) {
+        // thread t sums d-octet t % 16 over rows t / 16, t / 16 + 8, ... of the kernel
+        const int oc = t & 15, rg = t >> 4;
+        const bf16_t* src = kcache + (static_cast<size_t>(o0) * hkv + static_cast<size_t>(g) * (o1 - o0) +
+                                      static_cast<size_t>(j_new) * s) * kHeadDim + 8 * oc;
+        double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+        for (int r0 = rg; r0 < p; r0 += 4 * kFuseParts) {        // four rows per batch of loads
+            uint4 x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int r = r0 + kFuseParts * u;
+                x[u] = r < p ? ldg16(src + static_cast<size_t>(r) * kHeadDim) : make_uint4(0u, 0u, 0u, 0u);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t w4[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[2 * e] += static_cast<double>(__uint_as_float(w4[e] << 16));
+                    acc[2 * e + 1] += static_cast<double>(__uint_as_float(w4[e] & 0xffff0000u));
+                }
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fpart[rg][8 * oc + e] = acc[e];
+        __syncthreads();
+        if (t < kHeadDim) {
+            double sum = 0.0;
+#pragma unroll
+            for (int x = 0; x < kFuseParts; ++x) sum += fpart[x][t];
+            const double mean = sum / static_cast<double>(p);
+            const size_t dst = static_cast<size_t>(cbase + j_new) * kHeadDim + t;
+            if (kCkBf16) {
+                const bf16_t h = f64_to_bf16(mean);
+                static_cast<bf16_t*>(ck_w)[dst] = h;
+                fkey[t] = bf16_to_f32(h);
+            } else {
+                const float f = static_cast<float>(mean);
+                static_cast<float*>(ck_w)[dst] = f;
+                fkey[t] = f;
+            }
+        }
+        __syncthreads();
+        // the lanes holding row j_new take it from LDS instead of the stale load
+#pragma unroll
+        for (int m2 = 0; m2 < kLogTiles; ++m2) {
+            const int mt = kLogTiles * wv + m2;
+            if (j0 + 16 * mt + lc == j_new) {
+                if (kCkBf16) {
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const float* f = &fkey[32 * ks + 8 * lg];
+                        raw[m2][ks] = make_uint4(pack_exact(f[0], f[1]), pack_exact(f[2], f[3]),
+                                                 pack_exact(f[4], f[5]), pack_exact(f[6], f[7]));
+                    }
+                } else {
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const float* f = &fkey[32 * ks + 8 * lg];
+                        raw[m2][2 * ks] = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
+                                                     __float_as_uint(f[2]), __float_as_uint(f[3]));
+                        raw[m2][2 * ks + 1] = make_uint4(__float_as_uint(f[4]), __float_as_uint(f[5]),
+                                                         __float_as_uint(f[6]), __float_as_uint(f[7]));
+                    }
+                }
+            }
         }
     }
     // clear this block's share of the block-score keys (filled by pass 2)
@@ -1071,7 +1152,7 @@ template <typename Tq, typename Tck>
 static void dec_launch(const Shape& sh, const void* q, const void* ck, const int64_t* ck_off,
                        const int64_t* kv_off, const int64_t* kv_lens, int batch, int64_t max_len,
                        const SelectDecodeWs& w, char* ws, int32_t* idx, float* score,
-                       const CoarseSel* cs, hipStream_t st) {
+                       const CoarseSel* cs, const void* fuse_k, hipStream_t st) {
     dim3 ga(w.nchunk_a, sh.hkv, batch), gb(w.nchunk_b, sh.hkv, batch);
     const int64_t ncm = w.nc_max > 0 ? w.nc_max : 1;
     const int64_t* lens = kv_lens ? kv_lens : kv_off + 1;
@@ -1093,11 +1174,11 @@ static void dec_launch(const Shape& sh, const void* q, const void* ck, const int
         lse_c = reinterpret_cast<float*>(ws + w.lse_c);
         dim3 gc(nch_c, sh.hkv, batch);
         if (sizeof(Tq) == 2)
-            launch_timed(INFV2_KERNEL_SELECT_LOGITS, sel_dec_logits_mfma<sizeof(Tck) == 2>, gc,
+            launch_timed(INFV2_KERNEL_SELECT_LOGITS, sel_dec_logits_mfma<sizeof(Tck) == 2, false>, gc,
                          dim3(kLogWaves * 64), 0, st,
                 static_cast<const bf16_t*>(q), cs->ckc, cs->ckc_off, kv_off, lens, lens_end, sh.hq,
                 sh.hkv, c, c, sh.score_scale, ncm_c, ld_c, nch_c, w.nblk_max, w.keys_ld, logits_c,
-                partial_c, keys);
+                partial_c, keys, static_cast<const bf16_t*>(nullptr), static_cast<void*>(nullptr));
         else
             launch_timed(INFV2_KERNEL_SELECT_LOGITS, sel_dec_logits<Tq, Tck>, gc, dim3(256), 0, st,
                 static_cast<const Tq*>(q), static_cast<const Tck*>(cs->ckc), cs->ckc_off, kv_off,
@@ -1106,11 +1187,20 @@ static void dec_launch(const Shape& sh, const void* q, const void* ck, const int
     }
     {
         if (sizeof(Tq) == 2)
-            launch_timed(INFV2_KERNEL_SELECT_LOGITS, sel_dec_logits_mfma<sizeof(Tck) == 2>, ga,
-                         dim3(kLogWaves * 64), 0, st,
-                static_cast<const bf16_t*>(q), ck, ck_off, kv_off, lens, lens_end, sh.hq, sh.hkv,
-                sh.p, sh.s, sh.score_scale, ncm, w.nc_ld, w.nchunk_a, w.nblk_max, w.keys_ld, logits,
-                partial, keys);
+        {
+            if (fuse_k)
+                launch_timed(INFV2_KERNEL_SELECT_LOGITS, sel_dec_logits_mfma<sizeof(Tck) == 2, true>, ga,
+                             dim3(kLogWaves * 64), 0, st,
+                    static_cast<const bf16_t*>(q), ck, ck_off, kv_off, lens, lens_end, sh.hq, sh.hkv,
+                    sh.p, sh.s, sh.score_scale, ncm, w.nc_ld, w.nchunk_a, w.nblk_max, w.keys_ld, logits,
+                    partial, keys, static_cast<const bf16_t*>(fuse_k), const_cast<void*>(ck));
+            else
+                launch_timed(INFV2_KERNEL_SELECT_LOGITS, sel_dec_logits_mfma<sizeof(Tck) == 2, false>, ga,
+                             dim3(kLogWaves * 64), 0, st,
+                    static_cast<const bf16_t*>(q), ck, ck_off, kv_off, lens, lens_end, sh.hq, sh.hkv,
+                    sh.p, sh.s, sh.score_scale, ncm, w.nc_ld, w.nchunk_a, w.nblk_max, w.keys_ld, logits,
+                    partial, keys, static_cast<const bf16_t*>(nullptr), static_cast<void*>(nullptr));
+        }
         else
             launch_timed(INFV2_KERNEL_SELECT_LOGITS, sel_dec_logits<Tq, Tck>, ga, dim3(256), 0, st,
                 static_cast<const Tq*>(q), static_cast<const Tck*>(ck), ck_off, kv_off, kv_lens,
@@ -1137,19 +1227,19 @@ hipError_t launch_select_decode(const Shape& sh, const void* q, const void* ck,
                                 const int64_t* ck_off, const int64_t* kv_off,
                                 const int64_t* kv_lens, int batch, int64_t max_len,
                                 int32_t* idx, float* score, void* ws, const CoarseSel* cs,
-                                hipStream_t st) {
+                                hipStream_t st, const void* fuse_k) {
     const SelectDecodeWs w = select_decode_ws(sh, batch, max_len);
-    if (!score && max_len <= static_cast<int64_t>(sh.topk) * sh.m) {   // every row dense
+    if (!score && !fuse_k && max_len <= static_cast<int64_t>(sh.topk) * sh.m) {   // every row dense
         launch_dense_ids(sh, 1, batch, 0, kv_off, kv_lens, w.nblk_max, idx, st);
         return hipGetLastError();
     }
     char* base = static_cast<char*>(ws);
     if (sh.io_bf16) {
-        if (sh.ck_bf16) dec_launch<bf16_t, bf16_t>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, st);
-        else dec_launch<bf16_t, float>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, st);
+        if (sh.ck_bf16) dec_launch<bf16_t, bf16_t>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, fuse_k, st);
+        else dec_launch<bf16_t, float>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, fuse_k, st);
     } else {
-        if (sh.ck_bf16) dec_launch<float, bf16_t>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, st);
-        else dec_launch<float, float>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, st);
+        if (sh.ck_bf16) dec_launch<float, bf16_t>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, nullptr, st);
+        else dec_launch<float, float>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, nullptr, st);
     }
     return hipGetLastError();
 }
