@@ -74,25 +74,83 @@ __host__ __device__ __forceinline__ int64_t num_kernels(int64_t n, int p, int s)
 }
 
 // ---------------------------------------------------------------- wave reductions
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+// Data-parallel-primitive (DPP) lane moves of gfx9: within each row of 16 lanes
+// row_shr:n reads lane i - n (0 or `old` where that leaves the row), and
+// row_bcast:15 / row_bcast:31 hand lane 15 / lane 31 to the rows above.  A
+// wave-wide inclusive scan or reduction is then four row shifts and two
+// broadcasts: six register moves instead of six LDS permutes.
+template <int kCtrl, int kRowMask = 0xf, bool kBoundZero = true>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t old, uint32_t src) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(src),
+                                                             kCtrl, kRowMask, 0xf, kBoundZero));
+}
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
+// inclusive prefix sum over the 64 lanes (lane 63 holds the total)
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
+    v += dpp_mov<kDppShr1>(0u, v);
+    v += dpp_mov<kDppShr2>(0u, v);
+    v += dpp_mov<kDppShr4>(0u, v);
+    v += dpp_mov<kDppShr8>(0u, v);
+    v += dpp_mov<kDppBcast15, 0xa>(0u, v);
+    v += dpp_mov<kDppBcast31, 0xc>(0u, v);
     return v;
+}
+// maximum / minimum over the 64 lanes, in every lane
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+    v = max(v, dpp_mov<kDppShr1>(0u, v));
+    v = max(v, dpp_mov<kDppShr2>(0u, v));
+    v = max(v, dpp_mov<kDppShr4>(0u, v));
+    v = max(v, dpp_mov<kDppShr8>(0u, v));
+    v = max(v, dpp_mov<kDppBcast15, 0xa>(0u, v));
+    v = max(v, dpp_mov<kDppBcast31, 0xc>(0u, v));
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
+    constexpr uint32_t kId = 0xffffffffu;
+    v = min(v, dpp_mov<kDppShr1, 0xf, false>(kId, v));
+    v = min(v, dpp_mov<kDppShr2, 0xf, false>(kId, v));
+    v = min(v, dpp_mov<kDppShr4, 0xf, false>(kId, v));
+    v = min(v, dpp_mov<kDppShr8, 0xf, false>(kId, v));
+    v = min(v, dpp_mov<kDppBcast15, 0xa, false>(kId, v));
+    v = min(v, dpp_mov<kDppBcast31, 0xc, false>(kId, v));
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+__device__ __forceinline__ float wave_max(float v) {
+    const uint32_t kId = __float_as_uint(-INFINITY);
+    v = fmaxf(v, __uint_as_float(dpp_mov<kDppShr1, 0xf, false>(kId, __float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_mov<kDppShr2, 0xf, false>(kId, __float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_mov<kDppShr4, 0xf, false>(kId, __float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_mov<kDppShr8, 0xf, false>(kId, __float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_mov<kDppBcast15, 0xa, false>(kId, __float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_mov<kDppBcast31, 0xc, false>(kId, __float_as_uint(v))));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += __uint_as_float(dpp_mov<kDppShr1>(0u, __float_as_uint(v)));
+    v += __uint_as_float(dpp_mov<kDppShr2>(0u, __float_as_uint(v)));
+    v += __uint_as_float(dpp_mov<kDppShr4>(0u, __float_as_uint(v)));
+    v += __uint_as_float(dpp_mov<kDppShr8>(0u, __float_as_uint(v)));
+    v += __uint_as_float(dpp_mov<kDppBcast15, 0xa>(0u, __float_as_uint(v)));
+    v += __uint_as_float(dpp_mov<kDppBcast31, 0xc>(0u, __float_as_uint(v)));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
-// reductions over aligned groups of 16 lanes
+// reductions over aligned groups of 16 lanes (DPP rows): rotations by 8 and 4
+// inside the row, then the two quad butterflies; every lane gets its row's result
+constexpr int kDppRor8 = 0x128, kDppRor4 = 0x124, kDppQuadSwap2 = 0x4e, kDppQuadSwap1 = 0xb1;
 __device__ __forceinline__ float max16(float v) {
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    v = fmaxf(v, __uint_as_float(dpp_mov<kDppRor8>(0u, __float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_mov<kDppRor4>(0u, __float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_mov<kDppQuadSwap2>(0u, __float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_mov<kDppQuadSwap1>(0u, __float_as_uint(v))));
     return v;
 }
 __device__ __forceinline__ float sum16(float v) {
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    v += __uint_as_float(dpp_mov<kDppRor8>(0u, __float_as_uint(v)));
+    v += __uint_as_float(dpp_mov<kDppRor4>(0u, __float_as_uint(v)));
+    v += __uint_as_float(dpp_mov<kDppQuadSwap2>(0u, __float_as_uint(v)));
+    v += __uint_as_float(dpp_mov<kDppQuadSwap1>(0u, __float_as_uint(v)));
     return v;
 }
 
@@ -170,11 +228,7 @@ namespace infv2 {
 template <int kWaves>
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* tmp) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t u = __shfl_up(v, o, 64);
-        if (lane >= o) v += u;
-    }
+    v = wave_incl_sum(v);
     if (lane == 63) tmp[wid] = v;
     __syncthreads();
     uint32_t add = 0;

@@ -112,12 +112,8 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
                 mx = key[u] > mx ? key[u] : mx;
             }
         }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            const uint32_t a0 = __shfl_xor(mn, o, 64), a1 = __shfl_xor(mx, o, 64);
-            mn = a0 < mn ? a0 : mn;
-            mx = a1 > mx ? a1 : mx;
-        }
+        mn = wave_umin(mn);
+        mx = wave_umax(mx);
         if (lane == 0) { sm.rmin[w] = mn; sm.rmax[w] = mx; }
         __syncthreads();
         lo = 0xffffffffu; hi = 0u;
@@ -175,17 +171,21 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
     auto in_window = [&](int u) { return cand(u) && key[u] >= lo && key[u] <= hi; };
     uint32_t ncol = 0;
     int16_t slot_of[kPer];                // mode 1: where each window key was collected
-    if (mode == 1) {                      // collect the window's keys, rank them
-        if (t == 0) sm.ncol = 0;
-        __syncthreads();
+    if (mode == 1) {                      // collect the window's keys in block order, rank them
+        uint32_t nw = 0;
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) nw += in_window(u) ? 1u : 0u;
+        const uint32_t incl_w = block_incl_scan<kWaves>(nw, sm.scan_tmp);
+        if (t == kThreads - 1) sm.ncol = incl_w;
+        uint32_t slot = incl_w - nw;
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
             slot_of[u] = -1;
             if (in_window(u)) {
-                const uint32_t slot = atomicAdd(&sm.ncol, 1u);
                 sm.ckey[slot] = key[u];
                 sm.cidx[slot] = jb + u;
                 slot_of[u] = static_cast<int16_t>(slot);
+                ++slot;
             }
         }
         __syncthreads();
