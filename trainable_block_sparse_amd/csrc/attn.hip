@@ -53,6 +53,25 @@ hipError_t decode_scratch(void** ptr) {
 
 constexpr int kTok = 64;             // tokens per LDS tile
 
+// Tiles per wave of the matrix-core decode attention: one while the grid stays
+// below kDecodeWaveTarget waves (small batches are latency-bound), longer runs
+// beyond (fewer partials, loads pipelined); always a divisor of the block's
+// tpb tiles (a run stays in one block) and long enough for the merge's split
+// limit.
+static int decode_tpw(int tpb, int64_t tiles, int64_t bg) {
+    int64_t want = (bg * tiles + kDecodeWaveTarget - 1) / kDecodeWaveTarget;
+    want = want < kDecodeMaxTpw ? want : kDecodeMaxTpw;
+    const int64_t need = (tiles + 4 * kDecodeMaxSplit - 1) / (4 * kDecodeMaxSplit);
+    if (want < need) want = need;
+    int tpw = 1;
+    for (int x = 1; x <= tpb; ++x)
+        if (tpb % x == 0 && x <= want) tpw = x;
+    if (tpw < need)                                 // the smallest divisor that meets the limit
+        for (int x = tpb; x >= 1; --x)
+            if (tpb % x == 0 && x >= need) tpw = x;
+    return tpw;
+}
+
 AttnDecodeWs attn_decode_ws(const Shape& sh, int batch) {
     AttnDecodeWs w{};
     const int64_t bg = static_cast<int64_t>(batch) * sh.hkv;
@@ -63,15 +82,17 @@ AttnDecodeWs attn_decode_ws(const Shape& sh, int batch) {
     w.bps = (wide < kDecodeFewBlocks && sh.topk <= kOneBlockMax) ? 1 : 4;
     w.nsplit = (sh.topk + w.bps - 1) / w.bps;
     const int64_t nalloc_v = sh.topk <= kOneBlockMax ? sh.topk : w.nsplit;
-    // matrix-core path: four 16-key tiles per split, or sixteen when four would
-    // give many thread blocks (large batches: fewer partials to write and merge)
-    // or more splits than the merge takes
-    const int64_t tiles = static_cast<int64_t>(sh.topk) * (sh.m / 16);
-    const int64_t n4 = (tiles + 3) / 4, n16 = (tiles + 15) / 16;
-    const bool four_ok = n4 <= kDecodeMaxSplit;
-    w.tiles_wg = (four_ok && bg * n4 <= kDecodeManyWg) ? 4 : 16;
-    w.nsplit_m = static_cast<int>(w.tiles_wg == 4 ? n4 : n16);
-    const int64_t nalloc_m = four_ok ? n4 : n16;
+    // matrix-core path: four waves per split, each a run of tpw 16-key tiles:
+    // one tile while the grid stays below kDecodeWaveTarget waves (small
+    // batches are latency-bound), longer runs beyond (fewer partials, loads
+    // pipelined), and long enough that the merge takes the splits
+    const int tpb = sh.m / 16;
+    const int64_t tiles = static_cast<int64_t>(sh.topk) * tpb;
+    w.tpw = decode_tpw(tpb, tiles, bg);
+    w.nsplit_m = static_cast<int>((tiles + 4 * w.tpw - 1) / (4 * w.tpw));
+    // runs only grow with the batch: the smallest batch has the most splits
+    const int tpw1 = decode_tpw(tpb, tiles, 1);
+    const int64_t nalloc_m = (tiles + 4 * tpw1 - 1) / (4 * tpw1);
     // room for the largest split count of either path at any batch, so the size
     // never shrinks as the batch grows (a workspace sized for a batch serves
     // every smaller one)
@@ -244,7 +265,7 @@ hipError_t launch_attn_decode(const Shape& sh, const void* q, const void* k, con
     hipError_t e;
     if (sh.io_bf16) {
         e = launch_attn_decode_mfma(sh, q, k, v, kv_off, kv_lens, batch, idx, po, pml, w.nsplit_m,
-                                    w.tiles_wg, st);
+                                    w.tpw, st);
         if (e != hipSuccess) return e;
         return launch_attn_decode_merge(sh, po, pml, out, batch, w.nsplit_m, st);
     } else {

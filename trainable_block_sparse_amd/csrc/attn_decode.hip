@@ -4,51 +4,59 @@
 // group sharing" (the 16 heads of a group read each selected block once, which
 // is what makes the 16-row matrix tile a real contraction).
 //
-// A decode step at batch 1 is latency-bound: 64 blocks per KV head, 4 MiB in
-// all.  So the work is cut into 16-key tiles, one per wave, and every wave makes
-// exactly two dependent memory round trips: (offsets, length, block id,
-// queries), then its tile's K and V rows.  Grid (split, KV head, sequence); a
-// thread block of T waves covers T consecutive tiles of the (KV head,
-// sequence)'s selection (T = 4: one 64-key block; T = 16 at large batches,
-// fewer partials).  Per wave, all in registers:
+// The work is cut into 16-key tiles of the selected blocks, and every wave makes
+// two dependent memory round trips before its first product: (offsets, length,
+// block ids, queries), then its first tile's K and V rows.  At batch 1 (64
+// blocks per KV head, 4 MiB in all, latency-bound) each wave takes one tile;
+// at large batches a run of tiles, loading the next tile while it computes
+// the current one.  Per tile and wave, all in registers:
 //   S^T[key][head] = K_tile (16x128) . Q^T (128x16)      4 MFMA 16x16x32
 //   V^T tiles      = V_tile . I  (identity MFMA, exact)    8 MFMA 16x16x16
 //   O^T[d][head]  += V^T (128x16) . P^T (16x16)           8 MFMA 16x16x16
 // K rows are the A operand as stored (16 contiguous bytes per lane), so K and V
 // stream from HBM with 16-byte coalesced loads.  The S^T layout puts one query
 // head per lane column; it is also exactly the B-operand layout of P^T.  The
-// waves share one reference max per head (exchanged in LDS), so their partial
-// outputs add up directly; the thread block sums them in a fixed order (results
-// are deterministic) and writes one partial (max, sum, output).
+// thread block merges its four waves' (max, sum, output) in LDS in a fixed
+// order (results are deterministic) and writes one partial per split;
 // attn_decode_merge combines the splits by their LogSumExp in a second kernel.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace infv2 {
 
-template <int T>
 struct DecSmem {
-    float o[T][kGroup][kHeadDim + 4];     // each wave's partial output, [head][d]
-    float m[T][kGroup];                   // each wave's max per head (log2 units)
-    float l[T][kGroup];                   // each wave's sum per head
+    float o[4][kGroup][kHeadDim + 4];     // each wave's partial output, [head][d]
+    float m[4][kGroup];                   // each wave's running max per head (log2 units)
+    float l[4][kGroup];                   // each wave's running sum per head
 };
 
-template <int T>
-__global__ __launch_bounds__(64 * T) void attn_decode_mfma(
+// Grid (split, KV head, sequence), four waves per thread block.  The tiles of a
+// (sequence, KV head) are its selected blocks cut into 16-key pieces, in slot
+// order; split sp covers tiles [4 tpw sp, 4 tpw (sp + 1)), wave w of it the run
+// of tpw tiles starting at 4 tpw sp + w tpw, all in one block (tpw divides the
+// block's m / 16 tiles).  A wave keeps an online softmax (running max, sum,
+// output) over its tiles and loads tile u + 1 while it computes tile u; the
+// thread block then merges its four waves in LDS.
+// kRun = false: one tile per wave (tpw == 1), no second set of K / V registers.
+template <bool kRun>
+__global__ __launch_bounds__(256) void attn_decode_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const int64_t* __restrict__ kv_off, const int64_t* __restrict__ lens, int lens_end,
     const int32_t* __restrict__ idx, float* __restrict__ part_o, float2* __restrict__ part_ml,
-    int hq, int hkv, int m, int topk, int nsplit, float scale_log2) {
-    static_assert(T == 4 || T == 16, "four or sixteen waves");
-    __shared__ DecSmem<T> sm;
+    int hq, int hkv, int m, int topk, int nsplit, int tpw_arg, float scale_log2) {
+    const int tpw = kRun ? tpw_arg : 1;
+    __shared__ DecSmem sm;
     const int b = blockIdx.z, g = blockIdx.y, sp = blockIdx.x, t = threadIdx.x;
     const int w = t >> 6, l = t & 63, lg = l >> 4, lc = l & 15;
     const size_t bg = static_cast<size_t>(b) * hkv + g;
     const int tpb = m >> 4;                          // 16-key tiles per block
-    const int u = sp * T + w;                        // this wave's tile
-    const int e = u / tpb, st = u - e * tpb;         // its selection slot and sub-tile
+    const int ntiles = topk * tpb;
+    const int u0 = (sp * 4 + w) * tpw;               // this wave's first tile
     // round trip 1: every load below depends only on the kernel arguments
     const int64_t o0 = kv_off[b], o1 = kv_off[b + 1], lv = lens[b];
+    // the wave's tiles are tpw consecutive 16-key pieces of ONE selected block
+    // (tpw divides the block's tile count)
+    const int e = u0 / tpb, st0 = u0 - e * tpb;
     const int32_t blk_raw = idx[bg * topk + (e < topk ? e : topk - 1)];
     const bf16_t* qrow = q + (static_cast<size_t>(b) * hq + static_cast<size_t>(g) * kGroup + lc) * kHeadDim;
     bf16x8_t qf[4];
@@ -61,75 +69,92 @@ __global__ __launch_bounds__(64 * T) void attn_decode_mfma(
 
     const int64_t cap = o1 - o0;
     const int64_t n = seq_len(o0, o1, lv, lens_end);     // decode row i = n - 1 sees keys t < n
-    const int32_t blk = e < topk ? blk_raw : -1;
-    const int64_t t0 = static_cast<int64_t>(blk) * m + 16 * st;
-    int64_t cnt = n - t0;
-    cnt = cnt < 16 ? cnt : 16;
-    const bool act = blk >= 0 && cnt > 0;                // wave-uniform
+    const bf16_t* kh = k + (static_cast<size_t>(o0) * hkv + static_cast<size_t>(g) * cap) * kHeadDim + 8 * lg;
+    const bf16_t* vh = v + (static_cast<size_t>(o0) * hkv + static_cast<size_t>(g) * cap) * kHeadDim + 8 * lg;
+    const int32_t blk = (u0 < ntiles && e < topk) ? blk_raw : -1;
+    // piece x of the run: its first key and its keys below n (<= 0: nothing to do)
+    auto piece = [&](int x, int64_t& t0, int64_t& cnt) {
+        t0 = static_cast<int64_t>(blk) * m + 16 * (st0 + x);
+        cnt = blk < 0 ? 0 : n - t0;
+        cnt = cnt < 16 ? cnt : 16;
+    };
+    auto load_tile = [&](int64_t t0, int64_t cnt, uint4 (&kr)[4], uint4 (&vr)[4]) {
+        if (cnt > 0) {                               // wave-uniform
+            int64_t key = t0 + lc;
+            key = key < n ? key : n - 1;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                kr[c] = ldg16_nt(kh + key * kHeadDim + 32 * c);
+                vr[c] = ldg16_nt(vh + key * kHeadDim + 32 * c);
+            }
+        }
+    };
 
     f32x4_t o[4][2];
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int h = 0; h < 2; ++h) o[c][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    uint4 vr[4];
-    float mx = -INFINITY;
-    if (act) {
-        // round trip 2: K (A operand) and V rows of the tile, 16 B per lane each
-        int64_t key = t0 + lc;
-        key = key < n ? key : n - 1;
-        const size_t base = (static_cast<size_t>(o0) * hkv + static_cast<size_t>(g) * cap + key) * kHeadDim + 8 * lg;
-        uint4 kr[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            kr[c] = ldg16_nt(k + base + 32 * c);
-            vr[c] = ldg16_nt(v + base + 32 * c);
+    float mrun = -INFINITY, lrun = 0.f;
+    uint4 kr[4], vr[4], kn[4], vn[4];
+    int64_t t0, cnt;
+    piece(0, t0, cnt);
+    load_tile(t0, cnt, kr, vr);
+    for (int x = 0; x < tpw; ++x) {
+        // the next piece's K / V, in flight under this piece's products
+        int64_t t1 = 0, cnt1 = 0;
+        if (kRun && x + 1 < tpw) {
+            piece(x + 1, t1, cnt1);
+            load_tile(t1, cnt1, kn, vn);
         }
-        // S^T: lane holds S[key 4 lg + r][head lc]
+        if (cnt > 0) {
+            // S^T: lane holds S[key 4 lg + r][head lc]
+            f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) s = mfma32(as_bf16x8(kr[ks]), qf[ks], s);
+            for (int ks = 0; ks < 4; ++ks) s = mfma32(as_bf16x8(kr[ks]), qf[ks], s);
+            float mx = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float x = (4 * lg + r < cnt) ? s[r] * scale_log2 : -INFINITY;
-            s[r] = x;
-            mx = fmaxf(mx, x);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) vr[c] = make_uint4(0u, 0u, 0u, 0u);
-    }
-    if (lg == 0) sm.m[w][lc] = mx;
-    __syncthreads();
-    float M = -INFINITY;                                 // the thread block's max of head lc
-#pragma unroll
-    for (int x = 0; x < T; ++x) M = fmaxf(M, sm.m[x][lc]);
-    float ls = 0.f;
-    if (act) {
-        // M >= mx > -inf: probabilities against the shared reference
-        float p[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            p[r] = (s[r] == -INFINITY) ? 0.f : exp2f(s[r] - M);
-            ls += p[r];
-        }
-        ls += __shfl_xor(ls, 16, 64);
-        ls += __shfl_xor(ls, 32, 64);
-        // P^T as the B operand: lane holds P[key 4 lg + j][head lc]
-        const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(pack_rne(p[0], p[1]), pack_rne(p[2], p[3])));
-        // V^T tile (d column block c, half hf), then O^T += V^T . P^T.  Transpose
-        // output: lane holds V[key 4 lg + r][d(lc)], d(x) = 32 c + 8 (x/4) + 4 hf + x%4
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const uint2 half = hf ? make_uint2(vr[c].z, vr[c].w) : make_uint2(vr[c].x, vr[c].y);
-                const f32x4_t vt = mfma16(__builtin_bit_cast(s16x4_t, half), ident, f32x4_t{0.f, 0.f, 0.f, 0.f});
-                const s16x4_t va = __builtin_bit_cast(s16x4_t, make_uint2(pack_exact(vt[0], vt[1]), pack_exact(vt[2], vt[3])));
-                o[c][hf] = mfma16(va, pb, o[c][hf]);
+            for (int r = 0; r < 4; ++r) {
+                const float xv = (4 * lg + r < cnt) ? s[r] * scale_log2 : -INFINITY;
+                s[r] = xv;
+                mx = fmaxf(mx, xv);
             }
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float mnew = fmaxf(mrun, mx);      // finite: key 0 of the tile is below n
+            const float alpha = (mrun == -INFINITY) ? 0.f : exp2f(mrun - mnew);
+            float p[4], ls = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[r] = (s[r] == -INFINITY) ? 0.f : exp2f(s[r] - mnew);
+                ls += p[r];
+            }
+            ls += __shfl_xor(ls, 16, 64);
+            ls += __shfl_xor(ls, 32, 64);
+            lrun = lrun * alpha + ls;
+            mrun = mnew;
+            // P^T as the B operand: lane holds P[key 4 lg + j][head lc]
+            const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(pack_rne(p[0], p[1]), pack_rne(p[2], p[3])));
+            // V^T tile (d column block c, half hf), then O^T = alpha O^T + V^T . P^T.
+            // Transpose output: lane holds V[key 4 lg + r][d(lc)], d(x) = 32 c + 8 (x/4) + 4 hf + x%4
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[c][hf][r] *= alpha;
+                    const uint2 half = hf ? make_uint2(vr[c].z, vr[c].w) : make_uint2(vr[c].x, vr[c].y);
+                    const f32x4_t vt = mfma16(__builtin_bit_cast(s16x4_t, half), ident, f32x4_t{0.f, 0.f, 0.f, 0.f});
+                    const s16x4_t va = __builtin_bit_cast(s16x4_t, make_uint2(pack_exact(vt[0], vt[1]), pack_exact(vt[2], vt[3])));
+                    o[c][hf] = mfma16(va, pb, o[c][hf]);
+                }
+            }
+        }
+        if (kRun && x + 1 < tpw) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) { kr[c] = kn[c]; vr[c] = vn[c]; }
+            t0 = t1;
+            cnt = cnt1;
         }
     }
     // O^T lane layout: O[head lc][d = 32 c + 8 lg + 4 hf + r]
@@ -139,28 +164,38 @@ __global__ __launch_bounds__(64 * T) void attn_decode_mfma(
         for (int hf = 0; hf < 2; ++hf)
             *reinterpret_cast<float4*>(&sm.o[w][lc][32 * c + 8 * lg + 4 * hf]) =
                 make_float4(o[c][hf][0], o[c][hf][1], o[c][hf][2], o[c][hf][3]);
-    if (lg == 0) sm.l[w][lc] = ls;
+    if (lg == 0) { sm.m[w][lc] = mrun; sm.l[w][lc] = lrun; }
     __syncthreads();
-    // the waves' outputs, summed in wave order: thread -> 4 columns of one head
+    // merge the waves in wave order: thread -> 4 columns of one head
     const size_t pbase = (bg * nsplit + sp) * kGroup;
-    for (int x = t; x < kGroup * kHeadDim / 4; x += 64 * T) {
+    for (int x = t; x < kGroup * kHeadDim / 4; x += 256) {
         const int h = x >> 5, c4 = (x & 31) * 4;
-        float4 acc = *reinterpret_cast<const float4*>(&sm.o[0][h][c4]);
+        float M = -INFINITY;
 #pragma unroll
-        for (int y = 1; y < T; ++y) {
-            const float4 a = *reinterpret_cast<const float4*>(&sm.o[y][h][c4]);
-            acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
+        for (int y = 0; y < 4; ++y) M = fmaxf(M, sm.m[y][h]);
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+                if (sm.m[y][h] == -INFINITY) continue;
+                const float wgt = exp2f(sm.m[y][h] - M);
+                const float4 a = *reinterpret_cast<const float4*>(&sm.o[y][h][c4]);
+                acc.x = fmaf(wgt, a.x, acc.x); acc.y = fmaf(wgt, a.y, acc.y);
+                acc.z = fmaf(wgt, a.z, acc.z); acc.w = fmaf(wgt, a.w, acc.w);
+            }
         }
         *reinterpret_cast<float4*>(part_o + (pbase + h) * kHeadDim + c4) = acc;
     }
     if (t < kGroup) {
-        float mh = -INFINITY, lh = 0.f;
+        float M = -INFINITY, L = 0.f;
 #pragma unroll
-        for (int y = 0; y < T; ++y) {
-            mh = fmaxf(mh, sm.m[y][t]);
-            lh += sm.l[y][t];
+        for (int y = 0; y < 4; ++y) M = fmaxf(M, sm.m[y][t]);
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int y = 0; y < 4; ++y)
+                if (sm.m[y][t] != -INFINITY) L += sm.l[y][t] * exp2f(sm.m[y][t] - M);
         }
-        part_ml[pbase + t] = make_float2(mh, lh);
+        part_ml[pbase + t] = make_float2(M, L);
     }
 }
 
@@ -247,19 +282,21 @@ __global__ __launch_bounds__(256) void attn_decode_merge(const float* __restrict
 hipError_t launch_attn_decode_mfma(const Shape& sh, const void* q, const void* k, const void* v,
                                    const int64_t* kv_off, const int64_t* kv_lens, int batch,
                                    const int32_t* idx, float* part_o, float2* part_ml, int nsplit,
-                                   int tiles_wg, hipStream_t st) {
+                                   int tpw, hipStream_t st) {
     dim3 grid(nsplit, sh.hkv, batch);
     const float scale_log2 = sh.attn_scale * 1.4426950408889634f;
     const int64_t* lens = kv_lens ? kv_lens : kv_off + 1;
     const int lens_end = kv_lens ? 0 : 1;
-    if (tiles_wg == 4)
-        launch_timed(INFV2_KERNEL_ATTN_DECODE, attn_decode_mfma<4>, grid, dim3(256), 0, st,
+    if (tpw > 1)
+        launch_timed(INFV2_KERNEL_ATTN_DECODE, attn_decode_mfma<true>, grid, dim3(256), 0, st,
             static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
-            kv_off, lens, lens_end, idx, part_o, part_ml, sh.hq, sh.hkv, sh.m, sh.topk, nsplit, scale_log2);
+            kv_off, lens, lens_end, idx, part_o, part_ml, sh.hq, sh.hkv, sh.m, sh.topk, nsplit, tpw,
+            scale_log2);
     else
-        launch_timed(INFV2_KERNEL_ATTN_DECODE, attn_decode_mfma<16>, grid, dim3(1024), 0, st,
+        launch_timed(INFV2_KERNEL_ATTN_DECODE, attn_decode_mfma<false>, grid, dim3(256), 0, st,
             static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
-            kv_off, lens, lens_end, idx, part_o, part_ml, sh.hq, sh.hkv, sh.m, sh.topk, nsplit, scale_log2);
+            kv_off, lens, lens_end, idx, part_o, part_ml, sh.hq, sh.hkv, sh.m, sh.topk, nsplit, 1,
+            scale_log2);
     return hipGetLastError();
 }
 

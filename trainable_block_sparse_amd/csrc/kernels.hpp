@@ -75,14 +75,15 @@ SelectPrefillWs select_prefill_ws(const Shape& sh, int rows, int64_t max_len);
 
 // Decode attention: each split gives one partial (max, sum, output) per head.
 // Vector-ALU path (fp32): a split is bps selected blocks (1 or 4).  Matrix-core
-// path (bf16): a split is tiles_wg 16-key tiles (4 or 16) of the selection.
+// path (bf16): a split is four waves, each a run of tpw 16-key tiles.
 constexpr int kDecodeFewBlocks = 256;   // vector-ALU: below this many 4-block splits, 1-block splits
-constexpr int kDecodeManyWg = 1024;     // matrix cores: above this many 4-tile splits, 16-tile splits
+constexpr int kDecodeWaveTarget = 4096; // matrix cores: waves in flight before runs grow past one tile
+constexpr int kDecodeMaxTpw = 8;        // matrix cores: longest tile run of a wave
 constexpr int kDecodeMaxSplit = 1024;   // splits the merge kernel takes
 struct AttnDecodeWs {
     size_t part_o, part_ml, total;
     int nsplit, bps;              // vector-ALU path
-    int nsplit_m, tiles_wg;       // matrix-core path
+    int nsplit_m, tpw;            // matrix-core path
 };
 AttnDecodeWs attn_decode_ws(const Shape& sh, int batch);
 
@@ -130,7 +131,7 @@ hipError_t launch_attn_decode(const Shape& sh, const void* q, const void* k, con
 hipError_t launch_attn_decode_mfma(const Shape& sh, const void* q, const void* k, const void* v,
                                    const int64_t* kv_off, const int64_t* kv_lens, int batch,
                                    const int32_t* idx, float* part_o, float2* part_ml, int nsplit,
-                                   int tiles_wg, hipStream_t st);
+                                   int tpw, hipStream_t st);
 hipError_t launch_attn_decode_merge(const Shape& sh, const float* part_o, const float2* part_ml,
                                     void* out, int batch, int nsplit, hipStream_t st);
 
