@@ -131,23 +131,45 @@ def kernel_times(tbs, torch, run, steps: int, families, ahead_ms: float = 50.0) 
     return out
 
 
-def roofline_of(times: dict, work: dict, bound: str, peak: float, unit: str, scale: float) -> dict:
+def roofline_of(times: dict, work: dict, bound: str, peak: float, unit: str, scale: float,
+                workload: str) -> dict:
     """Roofline line of the dominant kernel: the largest time per step among the
     kernels that carry the step's algorithmic traffic or FLOPs (the others only
-    pass intermediates between kernels and are reported in "kernels")."""
+    pass intermediates between kernels and are reported in "kernels").  Beside
+    the live time it carries the committed rocprofv3 average of the same kernel
+    on the same workload, and the HBM traffic from the committed counter runs,
+    each only while the kernel's sources are unchanged since they were taken."""
     cand = [f for f in work if times.get(f, {}).get("us_per_launch")]
     dom = max(cand, key=lambda f: times[f]["us_per_step"])
     us = times[dom]["us_per_launch"]
     achieved = work[dom] / (us * 1e-6) / scale
+    prof = profiled(DURATION_FILE, workload, dom)
+    rp = None
+    if prof:
+        a2 = work[dom] / (prof["avg_us"] * 1e-6) / scale
+        rp = {"us_per_launch": prof["avg_us"], "achieved": a2, "frac": a2 / peak,
+              "calls": prof["calls"], "kernel": prof["kernel"],
+              "live_over_rocprof": us / prof["avg_us"], "source": "profiles/kernel_durations.json"}
+    tr = profiled(TRAFFIC_FILE, workload, dom)
+    traffic = None
+    if tr:
+        traffic = 1024.0 * (tr["fetch_kib_per_launch"] / tr["fetch_scale"]
+                            + tr["write_kib_per_launch"] / tr["write_scale"])
     return {"bound": bound, "kernel": dom, "achieved": achieved, "peak": peak, "unit": unit,
-            "frac": achieved / peak, "traffic": None, "us_per_launch": us,
-            "work_per_launch": work[dom]}
+            "frac": achieved / peak, "traffic": traffic, "us_per_launch": us,
+            "work_per_launch": work[dom], "rocprof": rp, "workload": workload}
 
 
+DURATION_FILE = os.path.join(ROOT, "profiles", "kernel_durations.json")
+CALIBRATION_MIB = 256          # size of the copies that --copy-calibration runs for the counter passes
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCE = {"attn_decode": "attn_decode.hip", "select_logits": "select.hip",
-                 "attn_prefill": "attn_prefill.hip", "bwd_row": "attn_bwd_mfma.hip",
-                 "bwd_col": "attn_bwd_mfma.hip"}
+# kernel family -> (source file, rocprofv3 kernel-name prefix)
+KERNEL_SOURCE = {"attn_decode": ("attn_decode.hip", "infv2::attn_decode_mfma"),
+                 "select_logits": ("select.hip", "infv2::sel_dec_logits_mfma"),
+                 "attn_prefill": ("attn_prefill.hip", "infv2::attn_prefill_mfma"),
+                 "select_prefill": ("select.hip", "infv2::sel_pre_mfma"),
+                 "bwd_row": ("attn_bwd_mfma.hip", "infv2::bwd_row_mfma"),
+                 "bwd_col": ("attn_bwd_mfma.hip", "infv2::bwd_col_mfma")}
 
 
 def source_digest(kernel: str) -> str:
@@ -156,24 +178,104 @@ def source_digest(kernel: str) -> str:
     import hashlib
     csrc = os.path.join(ROOT, "trainable_block_sparse_amd", "csrc")
     h = hashlib.sha256()
-    for path in [os.path.join(csrc, KERNEL_SOURCE[kernel])] + sorted(glob.glob(os.path.join(csrc, "*.hpp"))):
+    for path in [os.path.join(csrc, KERNEL_SOURCE[kernel][0])] + sorted(glob.glob(os.path.join(csrc, "*.hpp"))):
         h.update(os.path.basename(path).encode())
         h.update(open(path, "rb").read())
     return h.hexdigest()
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE
-    counter runs, scaled by what the same counters read for a copy of known size;
-    None when no measurement exists or the kernel's source changed since."""
+def profiled(path: str, workload: str, kernel: str):
+    """The committed profile record of `kernel` on `workload`, or None when there
+    is none or the kernel's sources changed since it was taken."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))[kernel]
-    except (OSError, KeyError, ValueError):
+        rec = json.load(open(path))[workload][kernel]
+    except (OSError, KeyError, ValueError, TypeError):
         return None
     if kernel not in KERNEL_SOURCE or rec.get("source_sha256") != source_digest(kernel):
         return None
-    return 1024.0 * (rec["fetch_kib_per_launch"] / rec["fetch_scale"]
-                     + rec["write_kib_per_launch"] / rec["write_scale"])
+    return rec
+
+
+def _rocprof_name_family(name: str):
+    base = name[5:] if name.startswith("void ") else name
+    for fam, (_, prefix) in KERNEL_SOURCE.items():
+        if base.startswith(prefix):
+            return fam
+    return None
+
+
+def summarize_rocprof(kind: str, workload: str, paths, command: str) -> int:
+    """Fold rocprofv3 CSV output into the committed profile records.
+    kind "stats":   paths = [<name>_kernel_stats.csv]  -> kernel_durations.json
+    kind "traffic": paths = [FETCH_SIZE counter_collection.csv, WRITE_SIZE one]
+                    -> traffic.json, each counter scaled by what it reads for the
+                    device-to-device copies of known size (--copy-calibration)."""
+    import csv
+    out_path = DURATION_FILE if kind == "stats" else TRAFFIC_FILE
+    try:
+        db = json.load(open(out_path))
+    except (OSError, ValueError):
+        db = {}
+    entry = db.setdefault(workload, {})
+    if kind == "stats":
+        for row in csv.DictReader(open(paths[0])):
+            fam = _rocprof_name_family(row["Name"])
+            if fam is None:
+                continue
+            calls = int(row["Calls"])
+            avg_us = float(row["AverageNs"]) / 1e3
+            prev = entry.get(fam)
+            if prev and prev.get("command") == command and prev["kernel"] != row["Name"]:
+                # several instantiations of one family: merge by call count
+                tot = prev["calls"] + calls
+                avg_us = (prev["avg_us"] * prev["calls"] + avg_us * calls) / tot
+                calls = tot
+            entry[fam] = {"kernel": row["Name"].split("(")[0], "calls": calls, "avg_us": avg_us,
+                          "min_us": float(row["MinNs"]) / 1e3, "max_us": float(row["MaxNs"]) / 1e3,
+                          "command": command, "source_sha256": source_digest(fam)}
+            print(f"{workload} {fam}: {calls} calls, average {avg_us:.2f} us")
+    else:
+        per = {}
+        for counter, path in zip(("FETCH_SIZE", "WRITE_SIZE"), paths):
+            vals, copies = {}, {}
+            for row in csv.DictReader(open(path)):
+                if row["Counter_Name"] != counter:
+                    continue
+                v = float(row["Counter_Value"])
+                if row["Kernel_Name"].startswith("__amd_rocclr_copyBuffer"):
+                    copies.setdefault(row["Grid_Size"], []).append(v)
+                    continue
+                fam = _rocprof_name_family(row["Kernel_Name"])
+                if fam is not None:
+                    vals.setdefault(fam, []).append(v)
+            per[counter] = (vals, copies)
+        (fv, fcopies), (wv, wcopies) = per["FETCH_SIZE"], per["WRITE_SIZE"]
+        # the calibration copies (--copy-calibration) are the copyBuffer launches
+        # whose WRITE_SIZE equals their size; FETCH_SIZE is read off the launches
+        # of the same grid in the other pass
+        want = CALIBRATION_MIB * 1024.0
+        grid = [gsz for gsz, v in wcopies.items() if abs(np.median(v) / want - 1) < 0.01]
+        if not grid or grid[0] not in fcopies:
+            print(f"no {CALIBRATION_MIB} MiB calibration copy in the counter runs", file=sys.stderr)
+            return 1
+        fcopy, wcopy = float(np.median(fcopies[grid[0]])), float(np.median(wcopies[grid[0]]))
+        # the calibration copy moves the same number of bytes in and out; its
+        # write counter is exact (checked against its size), the fetch counter is not
+        for fam in sorted(set(fv) & set(wv)):
+            entry[fam] = {"launches": len(fv[fam]),
+                          "fetch_kib_per_launch": sum(fv[fam]) / len(fv[fam]),
+                          "write_kib_per_launch": sum(wv[fam]) / len(wv[fam]),
+                          "fetch_scale": fcopy / wcopy, "write_scale": 1.0,
+                          "calibration": f"device-to-device copy of {CALIBRATION_MIB} MiB: FETCH_SIZE "
+                                         f"{fcopy:.1f} KiB, WRITE_SIZE {wcopy:.1f} KiB",
+                          "command": command,
+                          "source_sha256": source_digest(fam)}
+            e = entry[fam]
+            print(f"{workload} {fam}: {e['launches']} launches, FETCH {e['fetch_kib_per_launch']:.1f} KiB "
+                  f"(scale {e['fetch_scale']:.4f}), WRITE {e['write_kib_per_launch']:.1f} KiB")
+    json.dump(db, open(out_path, "w"), indent=1, sort_keys=True)
+    open(out_path, "a").write("\n")
+    return 0
 
 
 # ----------------------------------------------------------------------------- decode
@@ -220,6 +322,7 @@ def bench_decode(cfg_index: int, args, torch, tbs, gh, replicas: int = 0, ck_dty
     wl = make_config(cfg_index)
     ck_dtype = ck_dtype or args.ck_dtype
     ckb = 2 if ck_dtype == "bf16" else 4
+    profile_name = wl.name if ck_dtype == "fp32" else wl.name + "/ck_bf16"
     lens = [int(n) for n in wl.lens]
     nb = decode_bytes(wl, ckb, lens)
     kb = decode_kernel_bytes(wl, ckb, lens)
@@ -342,7 +445,7 @@ def bench_decode(cfg_index: int, args, torch, tbs, gh, replicas: int = 0, ck_dty
                     "inside a pass a replica recurs only after R steps"},
         "roofline": roofline_of(kt, {"select_logits": kb["select_logits"],
                                      "attn_decode": kb["attn_decode"]},
-                                "hbm", HBM_PEAK_GBS, "GB/s", 1e9),
+                                "hbm", HBM_PEAK_GBS, "GB/s", 1e9, profile_name),
     }
     # spot parity of the timed path: replica 0, oracle selection on the same query
     res["parity"] = decode_spot_parity(wl, dev, qs, outs, idx, lambda: step(0), ck_dtype, torch, gh)
@@ -543,8 +646,7 @@ def bench_prefill(args, torch, tbs, gh) -> dict:
     n_attn = kt["attn_prefill"]["launches_per_step"]
     res["tflops_attn_kernel"] = useful / (kt["attn_prefill"]["us_per_step"] * 1e-6) / 1e12
     res["roofline"] = roofline_of(kt, {"attn_prefill": useful / n_attn}, "mfma", BF16_PEAK_TFLOPS,
-                                  "TFLOP/s", 1e12)
-    res["roofline"]["traffic"] = measured_traffic("attn_prefill")
+                                  "TFLOP/s", 1e12, wl.name)
     res["_idx"] = gi
     res["_wl"] = wl
     return res
@@ -648,10 +750,9 @@ def bench_backward(args, torch, tbs, gh, pre: dict) -> dict:
     # (it also recomputes S and dP, counted in "performed" only)
     work = {"bwd_row": 6.0 * d * G * tok / kt["bwd_row"]["launches_per_step"],
             "bwd_col": 4.0 * d * G * tok / kt["bwd_col"]["launches_per_step"]}
-    roof = roofline_of(kt, work, "mfma", BF16_PEAK_TFLOPS, "TFLOP/s", 1e12)
+    roof = roofline_of(kt, work, "mfma", BF16_PEAK_TFLOPS, "TFLOP/s", 1e12, "prefill_backward_bf16_32k")
     if roof["kernel"] == "bwd_col":
         roof["performed_frac"] = roof["frac"] * 2.0
-    roof["traffic"] = measured_traffic(roof["kernel"])
     per_kernel = {f: {"tflops_algorithmic": w / (kt[f]["us_per_launch"] * 1e-6) / 1e12,
                       "frac": w / (kt[f]["us_per_launch"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS}
                   for f, w in work.items()}
@@ -927,13 +1028,25 @@ def main() -> int:
     ap.add_argument("--no-ck-bf16", action="store_true",
                     help="skip the extra decode records with bf16 compressed keys")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="also run 8 device-to-device copies of MIB MiB (reference kernel for "
-                         "scaling the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help=f"also run 8 device-to-device copies of {CALIBRATION_MIB} MiB (reference "
+                         "kernel of known size for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--only", choices=["decode", "prefill", "batched", "backward", "coarse"],
                     default=None,
                     help="run one workload only and print its record (for profiling)")
+    ap.add_argument("--summarize-rocprof", nargs="+", metavar=("KIND", "CSV"), default=None,
+                    help="fold rocprofv3 output into profiles/: 'stats <kernel_stats.csv>' or "
+                         "'traffic <FETCH_SIZE counter_collection.csv> <WRITE_SIZE one>' "
+                         "(no GPU; needs --workload and --command)")
+    ap.add_argument("--workload", default=None, help="workload name for --summarize-rocprof")
+    ap.add_argument("--command", default=None, help="the profiled command, recorded beside the figures")
     args = ap.parse_args()
+    if args.summarize_rocprof:
+        kind, paths = args.summarize_rocprof[0], args.summarize_rocprof[1:]
+        if kind not in ("stats", "traffic") or len(paths) != (1 if kind == "stats" else 2) \
+                or not args.workload or not args.command:
+            ap.error("--summarize-rocprof stats CSV | traffic FETCH_CSV WRITE_CSV, with --workload and --command")
+        return summarize_rocprof(kind, args.workload, paths, args.command)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path; "
@@ -950,14 +1063,14 @@ def main() -> int:
     torch.cuda.set_device(0)
 
     if args.copy_calibration:
-        n = args.copy_calibration * (1 << 20)
+        n = CALIBRATION_MIB * (1 << 20)
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
         for _ in range(8):
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-        log(f"copy calibration: 8 copies of {args.copy_calibration} MiB")
+        log(f"copy calibration: 8 copies of {CALIBRATION_MIB} MiB")
 
     if args.only:
         if args.only == "decode":
@@ -1013,7 +1126,6 @@ def main() -> int:
             log(f"{k2}: {r2['ms_per_step'] * 1e3:.1f} us/step")
 
     roof = main_res["roofline"]
-    roof["traffic"] = measured_traffic(roof["kernel"])
     out = {
         "metric": METRIC,
         "value": main_res["tok_per_s"],

@@ -595,19 +595,27 @@ def test_varlen_prefill_equals_per_sequence_calls():
         r0 = r1
 
 
-@pytest.mark.parametrize("io,ck_dtype", [("bf16", "fp32"), ("bf16", "bf16"), ("fp32", "fp32")])
-def test_decode_step_equals_separate_calls(io, ck_dtype):
+@pytest.mark.parametrize("io,ck_dtype,keys", [("bf16", "fp32", "random"), ("bf16", "bf16", "random"),
+                                              ("fp32", "fp32", "random"), ("bf16", "fp32", "levels"),
+                                              ("bf16", "fp32", "equal")])
+def test_decode_step_equals_separate_calls(io, ck_dtype, keys):
     """infv2_decode_step (compressed key of the kernel the newest token completes,
     selection, attention in one call; with bf16 the compression runs inside the
-    selection's first kernel) equals infv2_compress_keys + infv2_select_blocks +
+    selection's first kernel, and at small batches the top-k inside the
+    attention) equals infv2_compress_keys + infv2_select_blocks +
     infv2_sparse_attn_decode bit for bit, over 40 steps of growing caches that
     complete a kernel every 16 tokens; the compressed keys end equal to the
-    oracle's."""
+    oracle's.  keys: random, three score levels (top-k boundary inside runs of
+    equal scores) or all equal (the lowest blocks win)."""
     import trainable_block_sparse_amd as tbs
     from synth import extra_decode_queries
     h = _harness()
     wl = _small(lens=[3001, 700, 4500, 33], io=io, topk=8, local=2, seed=171)
-    _say(f"decode step vs separate calls io={io} ck={ck_dtype}")
+    if keys == "levels":
+        wl = _with_keys(wl, _levels(3, 172))
+    elif keys == "equal":
+        wl = _with_keys(wl, lambda b, shape: np.zeros(shape))
+    _say(f"decode step vs separate calls io={io} ck={ck_dtype} keys={keys}")
     a = h.DeviceWorkload(wl, ck_dtype)
     b = h.DeviceWorkload(wl, ck_dtype)
     p, s = wl.kernel_size, wl.kernel_stride

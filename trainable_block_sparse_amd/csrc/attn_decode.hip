@@ -21,6 +21,7 @@
 // attn_decode_merge combines the splits by their LogSumExp in a second kernel.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "topk.hpp"
 
 namespace infv2 {
 
@@ -30,48 +31,24 @@ struct DecSmem {
     float l[4][kGroup];                   // each wave's running sum per head
 };
 
-// Grid (split, KV head, sequence), four waves per thread block.  The tiles of a
-// (sequence, KV head) are its selected blocks cut into 16-key pieces, in slot
-// order; split sp covers tiles [4 tpw sp, 4 tpw (sp + 1)), wave w of it the run
-// of tpw tiles starting at 4 tpw sp + w tpw, all in one block (tpw divides the
-// block's m / 16 tiles).  A wave keeps an online softmax (running max, sum,
-// output) over its tiles and loads tile u + 1 while it computes tile u; the
-// thread block then merges its four waves in LDS.
+// One wave's run of tpw 16-key tiles of selected block `blk` (< 0: none), from
+// piece st0 of the block, with an online softmax (running max, sum, output),
+// loading tile x + 1 while it computes tile x; then the thread block's merge of
+// its four waves in LDS, in wave order, into the split's partial at pbase.
 // kRun = false: one tile per wave (tpw == 1), no second set of K / V registers.
 template <bool kRun>
-__global__ __launch_bounds__(256) void attn_decode_mfma(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const int64_t* __restrict__ kv_off, const int64_t* __restrict__ lens, int lens_end,
-    const int32_t* __restrict__ idx, float* __restrict__ part_o, float2* __restrict__ part_ml,
-    int hq, int hkv, int m, int topk, int nsplit, int tpw_arg, float scale_log2) {
+__device__ __forceinline__ void decode_run(DecSmem& sm, const bf16x8_t (&qf)[4], int32_t blk, int st0,
+                                           int tpw_arg, int m, int64_t n, const bf16_t* kh,
+                                           const bf16_t* vh, float scale_log2,
+                                           float* __restrict__ part_o, float2* __restrict__ part_ml,
+                                           size_t pbase) {
     const int tpw = kRun ? tpw_arg : 1;
-    __shared__ DecSmem sm;
-    const int b = blockIdx.z, g = blockIdx.y, sp = blockIdx.x, t = threadIdx.x;
+    const int t = threadIdx.x;
     const int w = t >> 6, l = t & 63, lg = l >> 4, lc = l & 15;
-    const size_t bg = static_cast<size_t>(b) * hkv + g;
-    const int tpb = m >> 4;                          // 16-key tiles per block
-    const int ntiles = topk * tpb;
-    const int u0 = (sp * 4 + w) * tpw;               // this wave's first tile
-    // round trip 1: every load below depends only on the kernel arguments
-    const int64_t o0 = kv_off[b], o1 = kv_off[b + 1], lv = lens[b];
-    // the wave's tiles are tpw consecutive 16-key pieces of ONE selected block
-    // (tpw divides the block's tile count)
-    const int e = u0 / tpb, st0 = u0 - e * tpb;
-    const int32_t blk_raw = idx[bg * topk + (e < topk ? e : topk - 1)];
-    const bf16_t* qrow = q + (static_cast<size_t>(b) * hq + static_cast<size_t>(g) * kGroup + lc) * kHeadDim;
-    bf16x8_t qf[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(ldg16(qrow + 32 * ks + 8 * lg));
     // identity B operand for the transpose MFMA: B[4 lg + j][lc] = (4 lg + j == lc)
     s16x4_t ident;
 #pragma unroll
     for (int j = 0; j < 4; ++j) ident[j] = (4 * lg + j == lc) ? static_cast<short>(0x3f80) : 0;
-
-    const int64_t cap = o1 - o0;
-    const int64_t n = seq_len(o0, o1, lv, lens_end);     // decode row i = n - 1 sees keys t < n
-    const bf16_t* kh = k + (static_cast<size_t>(o0) * hkv + static_cast<size_t>(g) * cap) * kHeadDim + 8 * lg;
-    const bf16_t* vh = v + (static_cast<size_t>(o0) * hkv + static_cast<size_t>(g) * cap) * kHeadDim + 8 * lg;
-    const int32_t blk = (u0 < ntiles && e < topk) ? blk_raw : -1;
     // piece x of the run: its first key and its keys below n (<= 0: nothing to do)
     auto piece = [&](int x, int64_t& t0, int64_t& cnt) {
         t0 = static_cast<int64_t>(blk) * m + 16 * (st0 + x);
@@ -167,7 +144,6 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(
     if (lg == 0) { sm.m[w][lc] = mrun; sm.l[w][lc] = lrun; }
     __syncthreads();
     // merge the waves in wave order: thread -> 4 columns of one head
-    const size_t pbase = (bg * nsplit + sp) * kGroup;
     for (int x = t; x < kGroup * kHeadDim / 4; x += 256) {
         const int h = x >> 5, c4 = (x & 31) * 4;
         float M = -INFINITY;
@@ -197,6 +173,108 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(
         }
         part_ml[pbase + t] = make_float2(M, L);
     }
+}
+
+// Grid (split, KV head, sequence), four waves per thread block.  The tiles of a
+// (sequence, KV head) are its selected blocks cut into 16-key pieces, in slot
+// order; split sp covers tiles [4 tpw sp, 4 tpw (sp + 1)), wave w of it the run
+// of tpw tiles starting at 4 tpw sp + w tpw, all in one block (tpw divides the
+// block's m / 16 tiles).
+template <bool kRun>
+__global__ __launch_bounds__(256) void attn_decode_mfma(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const int64_t* __restrict__ kv_off, const int64_t* __restrict__ lens, int lens_end,
+    const int32_t* __restrict__ idx, float* __restrict__ part_o, float2* __restrict__ part_ml,
+    int hq, int hkv, int m, int topk, int nsplit, int tpw_arg, float scale_log2) {
+    const int tpw = kRun ? tpw_arg : 1;
+    __shared__ DecSmem sm;
+    const int b = blockIdx.z, g = blockIdx.y, sp = blockIdx.x, t = threadIdx.x;
+    const int w = t >> 6, l = t & 63, lg = l >> 4, lc = l & 15;
+    const size_t bg = static_cast<size_t>(b) * hkv + g;
+    const int tpb = m >> 4;                          // 16-key tiles per block
+    const int ntiles = topk * tpb;
+    const int u0 = (sp * 4 + w) * tpw;               // this wave's first tile
+    // round trip 1: every load below depends only on the kernel arguments
+    const int64_t o0 = kv_off[b], o1 = kv_off[b + 1], lv = lens[b];
+    // the wave's tiles are tpw consecutive 16-key pieces of ONE selected block
+    // (tpw divides the block's tile count)
+    const int e = u0 / tpb, st0 = u0 - e * tpb;
+    const int32_t blk_raw = idx[bg * topk + (e < topk ? e : topk - 1)];
+    const bf16_t* qrow = q + (static_cast<size_t>(b) * hq + static_cast<size_t>(g) * kGroup + lc) * kHeadDim;
+    bf16x8_t qf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(ldg16(qrow + 32 * ks + 8 * lg));
+    const int64_t cap = o1 - o0;
+    const int64_t n = seq_len(o0, o1, lv, lens_end);     // decode row i = n - 1 sees keys t < n
+    const bf16_t* kh = k + (static_cast<size_t>(o0) * hkv + static_cast<size_t>(g) * cap) * kHeadDim + 8 * lg;
+    const bf16_t* vh = v + (static_cast<size_t>(o0) * hkv + static_cast<size_t>(g) * cap) * kHeadDim + 8 * lg;
+    const int32_t blk = (u0 < ntiles && e < topk) ? blk_raw : -1;
+    decode_run<kRun>(sm, qf, blk, st0, tpw, m, n, kh, vh, scale_log2, part_o, part_ml,
+                     (bg * nsplit + sp) * kGroup);
+}
+
+// Small batches: the top-k of the (sequence, KV head) runs in every thread block
+// of its attention, before the tiles, so the step needs no separate top-k launch
+// and no round trip of the block list through memory.  The selection is the
+// one the top-k kernel makes (same code, same keys); split 0 also stores it.
+// One tile per wave.  Keys: the block-score keys of the scoring pass, rows of
+// kld entries padded to 256 kPer.
+constexpr int kFusedTopkMax = 256;       // largest top-k the fused kernel keeps in LDS
+
+template <int kPer>
+__global__ __launch_bounds__(256) void attn_decode_topk_mfma(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const int64_t* __restrict__ kv_off, const int64_t* __restrict__ lens, int lens_end,
+    const uint32_t* __restrict__ keys, int64_t kld, int64_t nblk_max, int init, int local,
+    int32_t* __restrict__ idx_out, float* __restrict__ part_o, float2* __restrict__ part_ml,
+    int hq, int hkv, int m, int topk, int nsplit, float scale_log2) {
+    static_assert(kPer % 2 == 0, "keys load in pairs");
+    __shared__ union { TopkSmem<256> tk; DecSmem dec; } sm;
+    __shared__ int32_t sel[kFusedTopkMax];
+    const int b = blockIdx.z, g = blockIdx.y, sp = blockIdx.x, t = threadIdx.x;
+    const int w = t >> 6, l = t & 63, lg = l >> 4, lc = l & 15;
+    const size_t bg = static_cast<size_t>(b) * hkv + g;
+    // round trip 1: offsets, length, the block keys and the queries
+    const int64_t o0 = kv_off[b], o1 = kv_off[b + 1], lv = lens[b];
+    const int jb = t * kPer;
+    const uint32_t* gk = keys + bg * kld + jb;
+    uint32_t key[kPer];
+    if constexpr (kPer % 4 == 0) {
+#pragma unroll
+        for (int u = 0; u < kPer; u += 4) {
+            const uint4 x = *reinterpret_cast<const uint4*>(gk + u);
+            key[u] = x.x; key[u + 1] = x.y; key[u + 2] = x.z; key[u + 3] = x.w;
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kPer; u += 2) {
+            const uint2 x = *reinterpret_cast<const uint2*>(gk + u);
+            key[u] = x.x; key[u + 1] = x.y;
+        }
+    }
+    const bf16_t* qrow = q + (static_cast<size_t>(b) * hq + static_cast<size_t>(g) * kGroup + lc) * kHeadDim;
+    bf16x8_t qf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(ldg16(qrow + 32 * ks + 8 * lg));
+    const int64_t cap = o1 - o0;
+    const int64_t n = seq_len(o0, o1, lv, lens_end);
+    int64_t c = n > 0 ? (n - 1) / m : -1;
+    c = c < nblk_max - 1 ? c : nblk_max - 1;
+    int cnt = static_cast<int>(c + 1) - jb;
+    cnt = cnt < 0 ? 0 : (cnt > kPer ? kPer : cnt);
+    block_topk_regs<256>(key, jb, cnt, static_cast<int>(c), topk, init, local, sel,
+                         static_cast<float*>(nullptr), sm.tk);
+    __syncthreads();                     // the list is complete; the top-k's LDS is free
+    if (sp == 0)
+        for (int r = t; r < topk; r += 256) idx_out[bg * topk + r] = sel[r];
+    const int tpb = m >> 4;
+    const int u0 = sp * 4 + w;           // this wave's tile
+    const int e = u0 / tpb, st0 = u0 - e * tpb;
+    const int32_t blk = (e < topk) ? sel[e] : -1;
+    const bf16_t* kh = k + (static_cast<size_t>(o0) * hkv + static_cast<size_t>(g) * cap) * kHeadDim + 8 * lg;
+    const bf16_t* vh = v + (static_cast<size_t>(o0) * hkv + static_cast<size_t>(g) * cap) * kHeadDim + 8 * lg;
+    decode_run<false>(sm.dec, qf, blk, st0, 1, m, n, kh, vh, scale_log2, part_o, part_ml,
+                      (bg * nsplit + sp) * kGroup);
 }
 
 // Merge of the split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
@@ -297,6 +375,32 @@ hipError_t launch_attn_decode_mfma(const Shape& sh, const void* q, const void* k
             static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
             kv_off, lens, lens_end, idx, part_o, part_ml, sh.hq, sh.hkv, sh.m, sh.topk, nsplit, 1,
             scale_log2);
+    return hipGetLastError();
+}
+
+bool attn_decode_topk_ok(const Shape& sh, int64_t nblk_max) {
+    return sh.io_bf16 && sh.topk <= kFusedTopkMax && topk_per(nblk_max, 256) <= 16 && (sh.m & 15) == 0;
+}
+
+hipError_t launch_attn_decode_topk(const Shape& sh, const void* q, const void* k, const void* v,
+                                   const int64_t* kv_off, const int64_t* kv_lens, int batch,
+                                   const uint32_t* keys, int64_t kld, int64_t nblk_max,
+                                   int32_t* idx, float* part_o, float2* part_ml, int nsplit,
+                                   hipStream_t st) {
+    dim3 grid(nsplit, sh.hkv, batch);
+    const float scale_log2 = sh.attn_scale * 1.4426950408889634f;
+    const int64_t* lens = kv_lens ? kv_lens : kv_off + 1;
+    const int lens_end = kv_lens ? 0 : 1;
+    const int per = topk_per(nblk_max, 256);
+#define INFV2_L(P) launch_timed(INFV2_KERNEL_ATTN_DECODE, attn_decode_topk_mfma<P>, grid, dim3(256), 0, st, \
+        static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), \
+        kv_off, lens, lens_end, keys, kld, nblk_max, sh.init, sh.local, idx, part_o, part_ml, \
+        sh.hq, sh.hkv, sh.m, sh.topk, nsplit, scale_log2)
+    if (per <= 2) INFV2_L(2);
+    else if (per <= 8) INFV2_L(8);
+    else if (per <= 16) INFV2_L(16);
+    else return hipErrorInvalidValue;
+#undef INFV2_L
     return hipGetLastError();
 }
 

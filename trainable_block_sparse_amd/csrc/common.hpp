@@ -237,6 +237,25 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* tmp) {
     return v + add;
 }
 
+// the same with one barrier: `tmp` must not be written again before a barrier
+// that follows this call; `total` receives the block's sum
+template <int kWaves>
+__device__ __forceinline__ uint32_t block_incl_scan_1b(uint32_t v, uint32_t* tmp, uint32_t& total) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    v = wave_incl_sum(v);
+    if (lane == 63) tmp[wid] = v;
+    __syncthreads();
+    uint32_t add = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const uint32_t x = tmp[w];
+        add += (w < wid) ? x : 0u;
+        tot += x;
+    }
+    total = tot;
+    return v + add;
+}
+
 // 2^x on the transcendental unit (no denormal range handling: exp2(-inf) = 0)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -259,12 +259,28 @@ int32_t infv2_decode_step(const infv2_config* c, const void* q, const void* k, c
     if (!ws || ws_bytes < need) return INFV2_ERR_WORKSPACE;
     const Shape sh = make_shape(c);
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    char* ws_attn = static_cast<char*>(ws) + infv2::align256(infv2::select_decode_ws(sh, batch, max_len).total);
+    const infv2::SelectDecodeWs sw = infv2::select_decode_ws(sh, batch, max_len);
+    char* ws_attn = static_cast<char*>(ws) + infv2::align256(sw.total);
     hipError_t e;
     if (sh.io_bf16) {
-        // the selection's first kernel also builds the newest token's compressed key
+        // the selection's first kernel also builds the newest token's compressed
+        // key; at small batches (one tile per wave) the attention makes the top-k
+        // selection itself from the block-score keys
+        const infv2::AttnDecodeWs aw = infv2::attn_decode_ws(sh, batch);
+        const bool fused = aw.tpw == 1 && infv2::attn_decode_topk_ok(sh, sw.nblk_max);
         e = infv2::launch_select_decode(sh, q, ck, ck_offsets, kv_offsets, kv_lens, batch, max_len,
-                                        block_idx, nullptr, ws, nullptr, s, k);
+                                        block_idx, nullptr, ws, nullptr, s, k, fused);
+        if (e != hipSuccess) return INFV2_ERR_DEVICE;
+        if (fused) {
+            const uint32_t* keys = reinterpret_cast<const uint32_t*>(static_cast<char*>(ws) + sw.keys);
+            float* po = reinterpret_cast<float*>(ws_attn + aw.part_o);
+            float2* pml = reinterpret_cast<float2*>(ws_attn + aw.part_ml);
+            e = infv2::launch_attn_decode_topk(sh, q, k, v, kv_offsets, kv_lens, batch, keys,
+                                               sw.keys_ld, sw.nblk_max, block_idx, po, pml,
+                                               aw.nsplit_m, s);
+            if (e != hipSuccess) return status_of(e);
+            return status_of(infv2::launch_attn_decode_merge(sh, po, pml, out, batch, aw.nsplit_m, s));
+        }
     } else {
         e = infv2::launch_compress(sh, k, kv_offsets, kv_lens, ck_offsets, nullptr, batch, 1, ck, s,
                                    true);

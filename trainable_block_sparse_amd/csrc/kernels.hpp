@@ -108,11 +108,14 @@ struct CoarseSel {
 // cs == nullptr: the exact selection.  fuse_k != nullptr (bf16 queries only):
 // the cached keys, from which the first kernel also computes and stores the
 // compressed key of the kernel each sequence's newest token completes.
+// skip_topk: stop after the block-score keys (the workspace's `keys` rows), for
+// launch_attn_decode_topk, which makes the selection itself.
 hipError_t launch_select_decode(const Shape& sh, const void* q, const void* ck,
                                 const int64_t* ck_off, const int64_t* kv_off,
                                 const int64_t* kv_lens, int batch, int64_t max_len,
                                 int32_t* idx, float* score, void* ws, const CoarseSel* cs,
-                                hipStream_t st, const void* fuse_k = nullptr);
+                                hipStream_t st, const void* fuse_k = nullptr,
+                                bool skip_topk = false);
 
 hipError_t launch_select_prefill(const Shape& sh, const void* q, int rows, int64_t q_start,
                                  const void* ck, const int64_t* ck_off, int64_t max_len,
@@ -134,6 +137,16 @@ hipError_t launch_attn_decode_mfma(const Shape& sh, const void* q, const void* k
                                    int tpw, hipStream_t st);
 hipError_t launch_attn_decode_merge(const Shape& sh, const float* part_o, const float2* part_ml,
                                     void* out, int batch, int nsplit, hipStream_t st);
+// Decode attention that first makes the top-k selection from the block-score
+// keys (rows of kld, one per (sequence, KV head)) in every thread block, one
+// 16-key tile per wave (nsplit = the matrix-core path's splits at tpw 1); split
+// 0 stores the selection in idx.  attn_decode_topk_ok: shapes it takes.
+bool attn_decode_topk_ok(const Shape& sh, int64_t nblk_max);
+hipError_t launch_attn_decode_topk(const Shape& sh, const void* q, const void* k, const void* v,
+                                   const int64_t* kv_off, const int64_t* kv_lens, int batch,
+                                   const uint32_t* keys, int64_t kld, int64_t nblk_max,
+                                   int32_t* idx, float* part_o, float2* part_ml, int nsplit,
+                                   hipStream_t st);
 
 bool attn_prefill_mfma_ok(const Shape& sh);
 // transposed 64-key tiles of K or V for the matrix-core prefill kernels

@@ -34,6 +34,7 @@ namespace infv2 {
 constexpr float kLog2eF = 1.4426950408889634f;   // exp(x) = 2^(x log2 e) on the transcendental unit
 constexpr float kLn2F = 0.6931471805599453f;
 constexpr int kChunkA = 64;      // kernels per block in sel_dec_logits
+constexpr int kLogitsNtMaxBlocks = 1024;   // nontemporal key loads up to this many logits blocks
 constexpr int kLogWaves = 2;     // waves per 64-kernel chunk in sel_dec_logits_mfma (4 was no faster)
 constexpr int kLogTiles = 4 / kLogWaves;   // 16-kernel tiles per wave
 constexpr int kChunkB = 256;     // kernels per block in sel_dec_scores
@@ -186,12 +187,16 @@ __global__ __launch_bounds__(256) void sel_dec_logits(
 // kernel); fp32 keys are split into bf16 hi + lo (x = hi + lo + O(2^-17 |x|)),
 // two MFMAs per tile, products exact in fp32.  Z^T puts one head per lane column.
 //
+// kNt: nontemporal loads of the compressed keys.  They stream faster when the
+// grid is small (one sequence: a few hundred blocks) and slower when thousands
+// of blocks read at once (a batch), so the launcher picks by grid size.
+//
 // kFuse (decode step): the block whose chunk holds the kernel that the newest
 // token n - 1 completes (n >= p, s divides n - p) first computes that kernel's
 // compressed key from the cached keys -- float64 sum of the p rows, rounded
 // once, as infv2_compress_keys does -- stores it for later steps, and scores it
 // from LDS, so the step needs no separate compression launch.
-template <bool kCkBf16, bool kFuse>
+template <bool kCkBf16, bool kFuse, bool kNt>
 __global__ __launch_bounds__(kLogWaves * 64) void sel_dec_logits_mfma(
     const bf16_t* __restrict__ q, const void* __restrict__ ck, const int64_t* __restrict__ ck_off,
     const int64_t* __restrict__ kv_off, const int64_t* __restrict__ lens, int lens_end, int hq,
@@ -232,13 +237,13 @@ __global__ __launch_bounds__(kLogWaves * 64) void sel_dec_logits_mfma(
             if (kCkBf16) {
                 const bf16_t* row = static_cast<const bf16_t*>(ck) + (cbase + j) * kHeadDim + 8 * lg;
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) raw[m2][ks] = ldg16_nt(row + 32 * ks);
+                for (int ks = 0; ks < 4; ++ks) raw[m2][ks] = kNt ? ldg16_nt(row + 32 * ks) : ldg16(row + 32 * ks);
             } else {
                 const float* row = static_cast<const float*>(ck) + (cbase + j) * kHeadDim + 8 * lg;
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
-                    raw[m2][2 * ks] = ldg16_nt(row + 32 * ks);
-                    raw[m2][2 * ks + 1] = ldg16_nt(row + 32 * ks + 4);
+                    raw[m2][2 * ks] = kNt ? ldg16_nt(row + 32 * ks) : ldg16(row + 32 * ks);
+                    raw[m2][2 * ks + 1] = kNt ? ldg16_nt(row + 32 * ks + 4) : ldg16(row + 32 * ks + 4);
                 }
             }
         } else {
@@ -1152,7 +1157,7 @@ template <typename Tq, typename Tck>
 static void dec_launch(const Shape& sh, const void* q, const void* ck, const int64_t* ck_off,
                        const int64_t* kv_off, const int64_t* kv_lens, int batch, int64_t max_len,
                        const SelectDecodeWs& w, char* ws, int32_t* idx, float* score,
-                       const CoarseSel* cs, const void* fuse_k, hipStream_t st) {
+                       const CoarseSel* cs, const void* fuse_k, bool skip_topk, hipStream_t st) {
     dim3 ga(w.nchunk_a, sh.hkv, batch), gb(w.nchunk_b, sh.hkv, batch);
     const int64_t ncm = w.nc_max > 0 ? w.nc_max : 1;
     const int64_t* lens = kv_lens ? kv_lens : kv_off + 1;
@@ -1174,7 +1179,7 @@ static void dec_launch(const Shape& sh, const void* q, const void* ck, const int
         lse_c = reinterpret_cast<float*>(ws + w.lse_c);
         dim3 gc(nch_c, sh.hkv, batch);
         if (sizeof(Tq) == 2)
-            launch_timed(INFV2_KERNEL_SELECT_LOGITS, sel_dec_logits_mfma<sizeof(Tck) == 2, false>, gc,
+            launch_timed(INFV2_KERNEL_SELECT_LOGITS, sel_dec_logits_mfma<sizeof(Tck) == 2, false, true>, gc,
                          dim3(kLogWaves * 64), 0, st,
                 static_cast<const bf16_t*>(q), cs->ckc, cs->ckc_off, kv_off, lens, lens_end, sh.hq,
                 sh.hkv, c, c, sh.score_scale, ncm_c, ld_c, nch_c, w.nblk_max, w.keys_ld, logits_c,
@@ -1188,18 +1193,15 @@ static void dec_launch(const Shape& sh, const void* q, const void* ck, const int
     {
         if (sizeof(Tq) == 2)
         {
-            if (fuse_k)
-                launch_timed(INFV2_KERNEL_SELECT_LOGITS, sel_dec_logits_mfma<sizeof(Tck) == 2, true>, ga,
-                             dim3(kLogWaves * 64), 0, st,
-                    static_cast<const bf16_t*>(q), ck, ck_off, kv_off, lens, lens_end, sh.hq, sh.hkv,
-                    sh.p, sh.s, sh.score_scale, ncm, w.nc_ld, w.nchunk_a, w.nblk_max, w.keys_ld, logits,
-                    partial, keys, static_cast<const bf16_t*>(fuse_k), const_cast<void*>(ck));
-            else
-                launch_timed(INFV2_KERNEL_SELECT_LOGITS, sel_dec_logits_mfma<sizeof(Tck) == 2, false>, ga,
-                             dim3(kLogWaves * 64), 0, st,
-                    static_cast<const bf16_t*>(q), ck, ck_off, kv_off, lens, lens_end, sh.hq, sh.hkv,
-                    sh.p, sh.s, sh.score_scale, ncm, w.nc_ld, w.nchunk_a, w.nblk_max, w.keys_ld, logits,
-                    partial, keys, static_cast<const bf16_t*>(nullptr), static_cast<void*>(nullptr));
+            const bool nt = static_cast<int64_t>(ga.x) * ga.y * ga.z <= kLogitsNtMaxBlocks;
+#define INFV2_L(F, N) launch_timed(INFV2_KERNEL_SELECT_LOGITS, sel_dec_logits_mfma<sizeof(Tck) == 2, F, N>, \
+                    ga, dim3(kLogWaves * 64), 0, st, \
+                    static_cast<const bf16_t*>(q), ck, ck_off, kv_off, lens, lens_end, sh.hq, sh.hkv, \
+                    sh.p, sh.s, sh.score_scale, ncm, w.nc_ld, w.nchunk_a, w.nblk_max, w.keys_ld, logits, \
+                    partial, keys, static_cast<const bf16_t*>(fuse_k), const_cast<void*>(ck))
+            if (fuse_k) { if (nt) INFV2_L(true, true); else INFV2_L(true, false); }
+            else { if (nt) INFV2_L(false, true); else INFV2_L(false, false); }
+#undef INFV2_L
         }
         else
             launch_timed(INFV2_KERNEL_SELECT_LOGITS, sel_dec_logits<Tq, Tck>, ga, dim3(256), 0, st,
@@ -1218,6 +1220,7 @@ static void dec_launch(const Shape& sh, const void* q, const void* ck, const int
                      lens, lens_end, ck_off, sh.hkv, sh.m, sh.p, sh.s, ncm, w.nc_ld, w.nchunk_a,
                      w.keys_ld, logits, partial, lse_c, keys);
     }
+    if (skip_topk) return;
     KernelTimer kt(INFV2_KERNEL_SELECT_TOPK, st);
     launch_topk_dec(sh, batch, w.nblk_max, w.keys_ld, kv_off, lens, lens_end, keys, idx, score, st);
 }
@@ -1227,19 +1230,19 @@ hipError_t launch_select_decode(const Shape& sh, const void* q, const void* ck,
                                 const int64_t* ck_off, const int64_t* kv_off,
                                 const int64_t* kv_lens, int batch, int64_t max_len,
                                 int32_t* idx, float* score, void* ws, const CoarseSel* cs,
-                                hipStream_t st, const void* fuse_k) {
+                                hipStream_t st, const void* fuse_k, bool skip_topk) {
     const SelectDecodeWs w = select_decode_ws(sh, batch, max_len);
-    if (!score && !fuse_k && max_len <= static_cast<int64_t>(sh.topk) * sh.m) {   // every row dense
+    if (!score && !fuse_k && !skip_topk && max_len <= static_cast<int64_t>(sh.topk) * sh.m) {   // every row dense
         launch_dense_ids(sh, 1, batch, 0, kv_off, kv_lens, w.nblk_max, idx, st);
         return hipGetLastError();
     }
     char* base = static_cast<char*>(ws);
     if (sh.io_bf16) {
-        if (sh.ck_bf16) dec_launch<bf16_t, bf16_t>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, fuse_k, st);
-        else dec_launch<bf16_t, float>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, fuse_k, st);
+        if (sh.ck_bf16) dec_launch<bf16_t, bf16_t>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, fuse_k, skip_topk, st);
+        else dec_launch<bf16_t, float>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, fuse_k, skip_topk, st);
     } else {
-        if (sh.ck_bf16) dec_launch<float, bf16_t>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, nullptr, st);
-        else dec_launch<float, float>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, nullptr, st);
+        if (sh.ck_bf16) dec_launch<float, bf16_t>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, nullptr, skip_topk, st);
+        else dec_launch<float, float>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, nullptr, skip_topk, st);
     }
     return hipGetLastError();
 }

@@ -21,7 +21,8 @@
 // block asc)), or when the window is a single key value (the lowest blocks are
 // taken).  Each step shrinks the window by 2^10 (a 32-bit key range needs at
 // most four steps; typical inputs need one).  The ascending output needs one
-// block scan because ownership is contiguous.
+// block scan because ownership is contiguous.  Barriers: one for the min / max,
+// two per narrowing step, three for the rank step, one for the output scan.
 #pragma once
 
 #include <type_traits>
@@ -35,11 +36,12 @@ constexpr int kTopkBins = 1024;
 template <int kThreads>
 struct TopkSmem {
     uint32_t hist[kTopkBins];
-    uint32_t scan_tmp[kThreads / 64 + 1];
+    uint32_t scan_tmp[3][kThreads / 64];   // wave totals: narrowing, window, output scans
     uint32_t rmin[kThreads / 64], rmax[kThreads / 64];
-    uint32_t ckey[kThreads];        // the window's keys (rank step), then keep flags
+    uint32_t ckey[kThreads];        // the window's keys (rank step)
     int32_t cidx[kThreads];         // and their blocks
-    uint32_t bstar, above, ncol, total;
+    uint32_t keep[kThreads];        // and whether each is taken
+    uint32_t bstar, above, ebin;
 };
 
 // keys per thread held in registers for a block of kThreads and nblk blocks
@@ -128,6 +130,7 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
             const int bits = 32 - __clz(span);
             const int sh = bits > 10 ? bits - 10 : 0;
             if (!first) {
+                // every read of the previous histogram came before the last barrier
 #pragma unroll
                 for (int x = t; x < kTopkBins; x += kThreads) sm.hist[x] = 0;
                 __syncthreads();
@@ -145,21 +148,23 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
                 cntb[u] = sm.hist[kTopkBins - 1 - (t * kB + u)];
                 sum += cntb[u];
             }
-            const uint32_t incl = block_incl_scan<kWaves>(sum, sm.scan_tmp);
+            uint32_t total_w;
+            const uint32_t incl = block_incl_scan_1b<kWaves>(sum, sm.scan_tmp[0], total_w);
             uint32_t run = incl - sum;            // candidates in higher bins
+            // exactly one thread owns the bin of the need-th largest key
 #pragma unroll
             for (int u = 0; u < kB; ++u) {
                 if (run < need && need <= run + cntb[u]) {
                     sm.bstar = static_cast<uint32_t>(kTopkBins - 1 - (t * kB + u));
                     sm.above = run;
+                    sm.ebin = cntb[u];
                 }
                 run += cntb[u];
             }
             __syncthreads();
             const uint32_t bstar = sm.bstar;
             need -= sm.above;
-            const uint32_t e = sm.hist[bstar];
-            __syncthreads();                      // bstar / above / hist read by all
+            const uint32_t e = sm.ebin;
             const uint32_t nlo = lo + (bstar << sh);
             const uint32_t width = (sh >= 32) ? 0xffffffffu : ((1u << sh) - 1u);
             hi = (hi - nlo > width) ? nlo + width : hi;
@@ -169,14 +174,13 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
         }
     }
     auto in_window = [&](int u) { return cand(u) && key[u] >= lo && key[u] <= hi; };
-    uint32_t ncol = 0;
     int16_t slot_of[kPer];                // mode 1: where each window key was collected
     if (mode == 1) {                      // collect the window's keys in block order, rank them
         uint32_t nw = 0;
 #pragma unroll
         for (int u = 0; u < kPer; ++u) nw += in_window(u) ? 1u : 0u;
-        const uint32_t incl_w = block_incl_scan<kWaves>(nw, sm.scan_tmp);
-        if (t == kThreads - 1) sm.ncol = incl_w;
+        uint32_t ncol;
+        const uint32_t incl_w = block_incl_scan_1b<kWaves>(nw, sm.scan_tmp[1], ncol);
         uint32_t slot = incl_w - nw;
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
@@ -189,8 +193,6 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
             }
         }
         __syncthreads();
-        ncol = sm.ncol;
-        uint32_t keep = 0;
         if (static_cast<uint32_t>(t) < ncol) {
             const uint32_t mk = sm.ckey[t];
             const int32_t mj = sm.cidx[t];
@@ -199,10 +201,8 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
                 const uint32_t ok = sm.ckey[x];
                 rank += (ok > mk || (ok == mk && sm.cidx[x] < mj)) ? 1u : 0u;
             }
-            keep = rank < need ? 1u : 0u;
+            sm.keep[t] = rank < need ? 1u : 0u;
         }
-        __syncthreads();                      // every rank read before the flags overwrite
-        if (static_cast<uint32_t>(t) < ncol) sm.ckey[t] = keep;
         __syncthreads();
     }
     // selection flags of this thread's blocks
@@ -211,7 +211,8 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
         uint32_t n_eq = 0;
 #pragma unroll
         for (int u = 0; u < kPer; ++u) n_eq += in_window(u) ? 1u : 0u;
-        uint32_t r = block_incl_scan<kWaves>(n_eq, sm.scan_tmp) - n_eq;
+        uint32_t n_all;
+        uint32_t r = block_incl_scan_1b<kWaves>(n_eq, sm.scan_tmp[1], n_all) - n_eq;
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
             if (in_window(u)) {
@@ -228,7 +229,7 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
                 if (mode == 0) {
                     s = true;
                 } else {
-                    s = sm.ckey[slot_of[u]] != 0u;       // keep flag of the key's own slot
+                    s = sm.keep[slot_of[u]] != 0u;       // keep flag of the key's own slot
                 }
             }
             if (s) smask |= Mask(1) << u;
@@ -239,10 +240,8 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
         if (u < cnt && !cand(u)) smask |= Mask(1) << u;     // forced
     const uint32_t n_sel = sizeof(Mask) == 8 ? __popcll(static_cast<uint64_t>(smask))
                                              : __popc(static_cast<uint32_t>(smask));
-    const uint32_t incl = block_incl_scan<kWaves>(n_sel, sm.scan_tmp);
-    // the total is known before any store, so no barrier waits for the stores
-    if (t == kThreads - 1) sm.total = incl;
-    __syncthreads();
+    uint32_t n_total;
+    const uint32_t incl = block_incl_scan_1b<kWaves>(n_sel, sm.scan_tmp[2], n_total);
     uint32_t pos = incl - n_sel;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
@@ -255,7 +254,7 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
         }
     }
     // slots past the total are padding
-    for (int r = static_cast<int>(sm.total) + t; r < k; r += kThreads) {
+    for (int r = static_cast<int>(n_total) + t; r < k; r += kThreads) {
         idx[r] = -1;
         if (score) score[r] = kNaN;
     }
