@@ -38,8 +38,8 @@ struct TopkSmem {
     uint32_t hist[kTopkBins];
     uint32_t scan_tmp[3][kThreads / 64];   // wave totals: narrowing, window, output scans
     uint32_t rmin[kThreads / 64], rmax[kThreads / 64];
-    uint32_t ckey[kThreads];        // the window's keys (rank step)
-    int32_t cidx[kThreads];         // and their blocks
+    uint32_t ckey[kThreads + 4] __attribute__((aligned(16)));   // the window's keys (rank step)
+    int32_t cidx[kThreads + 4] __attribute__((aligned(16)));    // and their blocks
     uint32_t keep[kThreads];        // and whether each is taken
     uint32_t bstar, above, ebin;
 };
@@ -175,6 +175,8 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
     }
     auto in_window = [&](int u) { return cand(u) && key[u] >= lo && key[u] <= hi; };
     int16_t slot_of[kPer];                // mode 1: where each window key was collected
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) slot_of[u] = -1;
     if (mode == 1) {                      // collect the window's keys in block order, rank them
         uint32_t nw = 0;
 #pragma unroll
@@ -184,7 +186,6 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
         uint32_t slot = incl_w - nw;
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
-            slot_of[u] = -1;
             if (in_window(u)) {
                 sm.ckey[slot] = key[u];
                 sm.cidx[slot] = jb + u;
@@ -192,14 +193,26 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
                 ++slot;
             }
         }
+        // pad the collected keys to a multiple of four with entries that rank
+        // below every key (key 0 at a block past every real one)
+        if (static_cast<uint32_t>(t) < ((4u - (ncol & 3u)) & 3u)) {
+            sm.ckey[ncol + t] = 0u;
+            sm.cidx[ncol + t] = 0x7fffffff;
+        }
         __syncthreads();
         if (static_cast<uint32_t>(t) < ncol) {
             const uint32_t mk = sm.ckey[t];
             const int32_t mj = sm.cidx[t];
             uint32_t rank = 0;
-            for (uint32_t x = 0; x < ncol; ++x) {
-                const uint32_t ok = sm.ckey[x];
-                rank += (ok > mk || (ok == mk && sm.cidx[x] < mj)) ? 1u : 0u;
+            const uint4* ck4 = reinterpret_cast<const uint4*>(sm.ckey);
+            const int4* cj4 = reinterpret_cast<const int4*>(sm.cidx);
+            for (uint32_t x = 0; x < (ncol + 3u) / 4u; ++x) {
+                const uint4 ok = ck4[x];
+                const int4 oj = cj4[x];
+                rank += (ok.x > mk || (ok.x == mk && oj.x < mj)) ? 1u : 0u;
+                rank += (ok.y > mk || (ok.y == mk && oj.y < mj)) ? 1u : 0u;
+                rank += (ok.z > mk || (ok.z == mk && oj.z < mj)) ? 1u : 0u;
+                rank += (ok.w > mk || (ok.w == mk && oj.w < mj)) ? 1u : 0u;
             }
             sm.keep[t] = rank < need ? 1u : 0u;
         }
@@ -221,17 +234,14 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
             }
         }
     } else if (mode != 3) {
+        // keys above the window are taken; window keys by mode (all, or their keep
+        // flags, read for every block at once without branches)
+        uint32_t kf[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) kf[u] = (mode == 1) ? sm.keep[slot_of[u] < 0 ? 0 : slot_of[u]] : 1u;
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
-            if (!cand(u)) continue;
-            bool s = key[u] > hi;
-            if (!s && in_window(u)) {
-                if (mode == 0) {
-                    s = true;
-                } else {
-                    s = sm.keep[slot_of[u]] != 0u;       // keep flag of the key's own slot
-                }
-            }
+            const bool s = cand(u) && (key[u] > hi || (in_window(u) && kf[u] != 0u));
             if (s) smask |= Mask(1) << u;
         }
     }
