@@ -418,25 +418,40 @@ __global__ __launch_bounds__(kLogWaves * 64) void sel_dec_logits_mfma(
 // t / 16 and the result is valid in every thread of that head.
 __device__ __forceinline__ float fold_partials(const float2* __restrict__ pp, int nchunk, int t) {
     const int r = t & 15;
-    constexpr int kMaxPer = 16;          // partials per thread held in registers
-    float2 pm[kMaxPer];
+    constexpr int kPer = 8;              // partials per thread and load batch (128 chunks)
+    // loads are unconditional (index clamped, value masked after): no branch, so
+    // a batch is in flight at once (and the first batch with the caller's loads)
+    auto batch = [&](int base, float2 (&pm)[kPer]) {
 #pragma unroll
-    for (int u = 0; u < kMaxPer; ++u) {
-        const int c = r + 16 * u;
-        pm[u] = c < nchunk ? pp[static_cast<size_t>(c) * kGroup] : make_float2(-INFINITY, 0.f);
-    }
+        for (int u = 0; u < kPer; ++u) {
+            const int c = base + r + 16 * u;
+            pm[u] = pp[static_cast<size_t>(c < nchunk ? c : nchunk - 1) * kGroup];
+        }
+#pragma unroll
+        for (int u = 0; u < kPer; ++u)
+            if (base + r + 16 * u >= nchunk) pm[u] = make_float2(-INFINITY, 0.f);
+    };
+    float2 pm[kPer];
+    batch(0, pm);
     float mx = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < kMaxPer; ++u) mx = fmaxf(mx, pm[u].x);
-    for (int c = r + 16 * kMaxPer; c < nchunk; c += 16) mx = fmaxf(mx, pp[static_cast<size_t>(c) * kGroup].x);
+    for (int u = 0; u < kPer; ++u) mx = fmaxf(mx, pm[u].x);
+    for (int base = 16 * kPer; base < nchunk; base += 16 * kPer) {      // beyond 128 chunks
+        float2 px[kPer];
+        batch(base, px);
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) mx = fmaxf(mx, px[u].x);
+    }
     mx = max16(mx);
     float sm = 0.f;
     if (mx != -INFINITY) {
 #pragma unroll
-        for (int u = 0; u < kMaxPer; ++u) sm += (pm[u].x == -INFINITY) ? 0.f : pm[u].y * fast_exp2((pm[u].x - mx) * kLog2eF);
-        for (int c = r + 16 * kMaxPer; c < nchunk; c += 16) {
-            const float2 q2 = pp[static_cast<size_t>(c) * kGroup];
-            sm += (q2.x == -INFINITY) ? 0.f : q2.y * fast_exp2((q2.x - mx) * kLog2eF);
+        for (int u = 0; u < kPer; ++u) sm += (pm[u].x == -INFINITY) ? 0.f : pm[u].y * fast_exp2((pm[u].x - mx) * kLog2eF);
+        for (int base = 16 * kPer; base < nchunk; base += 16 * kPer) {
+            float2 px[kPer];
+            batch(base, px);
+#pragma unroll
+            for (int u = 0; u < kPer; ++u) sm += (px[u].x == -INFINITY) ? 0.f : px[u].y * fast_exp2((px[u].x - mx) * kLog2eF);
         }
     }
     sm = sum16(sm);
