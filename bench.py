@@ -1031,7 +1031,7 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"also run 8 device-to-device copies of {CALIBRATION_MIB} MiB (reference "
                          "kernel of known size for scaling the FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--only", choices=["decode", "prefill", "batched", "backward", "coarse"],
+    ap.add_argument("--only", choices=["decode", "prefill", "batched", "backward", "coarse", "varlen"],
                     default=None,
                     help="run one workload only and print its record (for profiling)")
     ap.add_argument("--summarize-rocprof", nargs="+", metavar=("KIND", "CSV"), default=None,
@@ -1079,6 +1079,8 @@ def main() -> int:
             rec = {k: v for k, v in bench_prefill(args, torch, tbs, gh).items() if not k.startswith("_")}
         elif args.only == "coarse":
             rec = bench_coarse(args, torch, tbs, gh)
+        elif args.only == "varlen":
+            rec = bench_varlen_prefill(args, torch, tbs, gh)
         elif args.only == "backward":
             from synth import make_config
             rec = bench_backward(args, torch, tbs, gh, {"_wl": make_config(3)})

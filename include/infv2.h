@@ -337,8 +337,11 @@ int32_t infv2_sparse_attn_decode_noalloc(const infv2_config* cfg, const void* q,
  * Compressed keys up to n_c(q_start_per_seq[b] + rows_per_seq[b]) must be
  * present (infv2_compress_keys over the batch).  The workspace must hold the
  * largest single-sequence need: infv2_workspace_bytes(op, rows = max rows,
- * batch = 1, max_len = max (q_start + rows)).  Sequences run one after another
- * on the stream through the single-sequence kernels.
+ * batch = 1, max_len = max (q_start + rows)).  The bf16 matrix-core attention
+ * (block size 64) runs up to 64 sequences per launch, from a table of the
+ * sequences passed with the launch; the selection, and the attention of other
+ * shapes, run sequence after sequence on the stream through the
+ * single-sequence kernels.
  *
  *   q, block_idx, block_score, out   packed over all rows of the call
  */

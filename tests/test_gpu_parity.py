@@ -597,7 +597,8 @@ def test_varlen_prefill_equals_per_sequence_calls():
 
 @pytest.mark.parametrize("io,ck_dtype,keys", [("bf16", "fp32", "random"), ("bf16", "bf16", "random"),
                                               ("fp32", "fp32", "random"), ("bf16", "fp32", "levels"),
-                                              ("bf16", "fp32", "equal")])
+                                              ("bf16", "fp32", "equal"), ("bf16", "fp32", "batch16"),
+                                              ("bf16", "bf16", "batch16")])
 def test_decode_step_equals_separate_calls(io, ck_dtype, keys):
     """infv2_decode_step (compressed key of the kernel the newest token completes,
     selection, attention in one call; with bf16 the compression runs inside the
@@ -606,11 +607,17 @@ def test_decode_step_equals_separate_calls(io, ck_dtype, keys):
     infv2_sparse_attn_decode bit for bit, over 40 steps of growing caches that
     complete a kernel every 16 tokens; the compressed keys end equal to the
     oracle's.  keys: random, three score levels (top-k boundary inside runs of
-    equal scores) or all equal (the lowest blocks win)."""
+    equal scores), all equal (the lowest blocks win), or batch16: 16 sequences
+    of 20K-40K tokens at k = 64, a grid where the logits pass takes plain loads
+    and the attention's waves run two tiles each."""
     import trainable_block_sparse_amd as tbs
     from synth import extra_decode_queries
     h = _harness()
-    wl = _small(lens=[3001, 700, 4500, 33], io=io, topk=8, local=2, seed=171)
+    if keys == "batch16":
+        lens = np.random.default_rng(173).integers(20000, 40000, size=16, endpoint=True).tolist()
+        wl = _small(lens=lens, io=io, topk=64, local=4, seed=173)
+    else:
+        wl = _small(lens=[3001, 700, 4500, 33], io=io, topk=8, local=2, seed=171)
     if keys == "levels":
         wl = _with_keys(wl, _levels(3, 172))
     elif keys == "equal":

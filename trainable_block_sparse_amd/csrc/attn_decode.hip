@@ -217,8 +217,9 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(
 // of its attention, before the tiles, so the step needs no separate top-k launch
 // and no round trip of the block list through memory.  The selection is the
 // one the top-k kernel makes (same code, same keys); split 0 also stores it.
-// One tile per wave.  Keys: the block-score keys of the scoring pass, rows of
-// kld entries padded to 256 kPer.
+// One tile per wave (at two, the redundant selections cost what the launch
+// saves).  Keys: the block-score keys of the scoring pass, rows of kld entries
+// padded to 256 kPer.
 constexpr int kFusedTopkMax = 256;       // largest top-k the fused kernel keeps in LDS
 
 template <int kPer>

@@ -46,10 +46,10 @@ constexpr float kRescaleSlack = 8.f;   // log2 units
 typedef BlockTile StageTiles[kGroup2];              // 2 x 16 KB (K) or 2 x 16 KB (V^T)
 
 __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
-    const bf16_t* __restrict__ q, int rows, int64_t q_start, const bf16_t* __restrict__ k,
-    const bf16_t* __restrict__ v, const int64_t* __restrict__ kv_off,
-    const int32_t* __restrict__ idx, bf16_t* __restrict__ out, int hq, int hkv, int topk,
-    int64_t nblk, int nrg, float scale_log2) {
+    const PrefillSeqs seqs, const bf16_t* __restrict__ q_all, const bf16_t* __restrict__ k,
+    const bf16_t* __restrict__ v, const int64_t* __restrict__ kv_off_all,
+    const int32_t* __restrict__ idx_all, bf16_t* __restrict__ out_all, int hq, int hkv, int topk,
+    float scale_log2) {
     __shared__ __attribute__((aligned(16))) StageTiles kst[2], vst[2];   // two stages
     __shared__ UnionSmem sm;
     // XCD-aware placement: thread block b runs on XCD b % 8; give each XCD a
@@ -58,7 +58,20 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
     const int xcd = static_cast<int>(blockIdx.x) % kXcds, kx = static_cast<int>(blockIdx.x) / kXcds;
     const int qx = nwg / kXcds, rx = nwg % kXcds;
     const int lid = xcd * qx + (xcd < rx ? xcd : rx) + kx;
-    const int g = lid / nrg, r0 = (lid % nrg) * kPRows;
+    // work item -> (KV head, sequence, its row group)
+    const int nrg = seqs.grp_end[seqs.n - 1];
+    const int g = lid / nrg, grp = lid % nrg;
+    int si = 0;
+    while (si + 1 < seqs.n && grp >= seqs.grp_end[si]) ++si;
+    const int r0 = (grp - (si > 0 ? seqs.grp_end[si - 1] : 0)) * kPRows;
+    const int rows = seqs.rows[si];
+    const int64_t q_start = seqs.q_start[si];
+    const size_t row0 = static_cast<size_t>(seqs.row0[si]);
+    const bf16_t* q = q_all + row0 * hq * kHeadDim;
+    bf16_t* out = out_all + row0 * hq * kHeadDim;
+    const int32_t* idx = idx_all + row0 * hkv * topk;
+    const int64_t* kv_off = kv_off_all + seqs.seq[si];
+    const int64_t nblk = (q_start + rows + kPB - 1) / kPB;
     const int t = threadIdx.x;
     const int w = t >> 6, l = t & 63, lg = l >> 4, lc = l & 15;
     const int64_t cap = kv_off[1] - kv_off[0];
@@ -292,20 +305,33 @@ bool attn_prefill_mfma_ok(const Shape& sh) {
 
 size_t attn_prefill_ws_bytes(const Shape&, int64_t) { return 0; }   // no workspace
 
+hipError_t launch_attn_prefill_mfma_seqs(const Shape& sh, const PrefillSeqs& seqs, const void* q,
+                                         const void* k, const void* v, const int64_t* kv_off,
+                                         const int32_t* idx, void* out, hipStream_t st) {
+    if (seqs.n < 1 || seqs.n > kVarlenMax) return hipErrorInvalidValue;
+    const int nrg = seqs.grp_end[seqs.n - 1];
+    if (nrg < 1) return hipSuccess;
+    const float scale_log2 = sh.attn_scale * 1.4426950408889634f;
+    launch_timed(INFV2_KERNEL_ATTN_PREFILL, attn_prefill_mfma,
+                 dim3(static_cast<unsigned>(nrg) * sh.hkv), dim3(kPThreads), 0, st, seqs,
+        static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+        static_cast<const bf16_t*>(v), kv_off, idx, static_cast<bf16_t*>(out), sh.hq, sh.hkv,
+        sh.topk, scale_log2);
+    return hipGetLastError();
+}
+
 hipError_t launch_attn_prefill_mfma(const Shape& sh, const void* q, int rows, int64_t q_start,
                                     const void* k, const void* v, const int64_t* kv_off,
                                     const int32_t* idx, void* out, void* ws, hipStream_t st) {
-    const int64_t n = q_start + rows;
-    const int64_t nblk = (n + kPB - 1) / kPB;
     (void)ws;
-    const float scale_log2 = sh.attn_scale * 1.4426950408889634f;
-    const int nrg = (rows + kPRows - 1) / kPRows;
-    launch_timed(INFV2_KERNEL_ATTN_PREFILL, attn_prefill_mfma,
-                 dim3(static_cast<unsigned>(nrg) * sh.hkv), dim3(kPThreads), 0, st,
-        static_cast<const bf16_t*>(q), rows, q_start, static_cast<const bf16_t*>(k),
-        static_cast<const bf16_t*>(v), kv_off,
-        idx, static_cast<bf16_t*>(out), sh.hq, sh.hkv, sh.topk, nblk, nrg, scale_log2);
-    return hipGetLastError();
+    PrefillSeqs seqs{};
+    seqs.n = 1;
+    seqs.grp_end[0] = (rows + kPRows - 1) / kPRows;
+    seqs.seq[0] = 0;
+    seqs.row0[0] = 0;
+    seqs.rows[0] = rows;
+    seqs.q_start[0] = q_start;
+    return launch_attn_prefill_mfma_seqs(sh, seqs, q, k, v, kv_off, idx, out, st);
 }
 
 }  // namespace infv2

@@ -405,6 +405,38 @@ int32_t infv2_sparse_attn_prefill_varlen(const infv2_config* c, const void* q, i
                            ws_bytes, ws)) != INFV2_OK)
         return st;
     const Shape sh = make_shape(c);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (infv2::attn_prefill_mfma_ok(sh)) {
+        // one launch per kVarlenMax sequences (with rows) of the call
+        infv2::PrefillSeqs seqs{};
+        int grp = 0;
+        auto flush = [&]() -> bool {
+            const bool ok = seqs.n == 0 ||
+                infv2::launch_attn_prefill_mfma_seqs(sh, seqs, q, k, v, kv_offsets, block_idx, out,
+                                                     s) == hipSuccess;
+            seqs = infv2::PrefillSeqs{};
+            grp = 0;
+            return ok;
+        };
+        int64_t r0 = 0;
+        for (int32_t b = 0; b < batch; ++b) {
+            const int32_t rows = rows_per_seq[b];
+            const int ng = (rows + 15) / 16;
+            if (rows > 0) {
+                if ((seqs.n == infv2::kVarlenMax || grp + ng > infv2::kVarlenMaxGroups) && !flush())
+                    return INFV2_ERR_DEVICE;
+                const int i = seqs.n++;
+                grp += ng;
+                seqs.grp_end[i] = grp;
+                seqs.seq[i] = b;
+                seqs.row0[i] = r0;
+                seqs.rows[i] = rows;
+                seqs.q_start[i] = q_start_per_seq[b];
+            }
+            r0 += rows;
+        }
+        return flush() ? INFV2_OK : INFV2_ERR_DEVICE;
+    }
     const size_t qrow = static_cast<size_t>(c->num_q_heads) * c->head_dim *
                         (c->io_dtype == INFV2_BF16 ? 2 : 4);
     const size_t irow = static_cast<size_t>(c->num_kv_heads) * c->topk;
@@ -414,8 +446,7 @@ int32_t infv2_sparse_attn_prefill_varlen(const infv2_config* c, const void* q, i
         if (rows > 0) {
             const hipError_t e = infv2::launch_attn_prefill(
                 sh, static_cast<const char*>(q) + r0 * qrow, rows, q_start_per_seq[b], k, v,
-                kv_offsets + b, block_idx + r0 * irow, static_cast<char*>(out) + r0 * qrow, ws,
-                static_cast<hipStream_t>(stream));
+                kv_offsets + b, block_idx + r0 * irow, static_cast<char*>(out) + r0 * qrow, ws, s);
             if (e != hipSuccess) return INFV2_ERR_DEVICE;
         }
         r0 += rows;

@@ -148,12 +148,31 @@ hipError_t launch_attn_decode_topk(const Shape& sh, const void* q, const void* k
                                    int32_t* idx, float* part_o, float2* part_ml, int nsplit,
                                    hipStream_t st);
 
+// Sequences of one prefill launch (varlen calls: several; single-sequence calls:
+// one), passed by value as kernel arguments.  Rows are packed sequence after
+// sequence; group = 16 consecutive rows of one sequence.
+constexpr int kVarlenMax = 64;          // sequences per launch
+constexpr int kVarlenMaxGroups = 1 << 24;   // row groups per launch (grid of groups x KV heads)
+struct PrefillSeqs {
+    int n;                              // sequences in this launch (1 .. kVarlenMax)
+    int grp_end[kVarlenMax];            // row groups of sequences 0 .. i together
+    int seq[kVarlenMax];                // index into kv_offsets / ck_offsets
+    int64_t row0[kVarlenMax];           // first packed row
+    int rows[kVarlenMax];
+    int64_t q_start[kVarlenMax];
+};
+
 bool attn_prefill_mfma_ok(const Shape& sh);
 // transposed 64-key tiles of K or V for the matrix-core prefill kernels
 size_t attn_prefill_ws_bytes(const Shape& sh, int64_t max_len);
 hipError_t launch_attn_prefill_mfma(const Shape& sh, const void* q, int rows, int64_t q_start,
                                     const void* k, const void* v, const int64_t* kv_off,
                                     const int32_t* idx, void* out, void* ws, hipStream_t st);
+// the sequences of `seqs` in one launch; q, idx, out point at packed row 0 and
+// kv_off at the offsets of sequence 0 of the call
+hipError_t launch_attn_prefill_mfma_seqs(const Shape& sh, const PrefillSeqs& seqs, const void* q,
+                                         const void* k, const void* v, const int64_t* kv_off,
+                                         const int32_t* idx, void* out, hipStream_t st);
 
 hipError_t launch_attn_prefill(const Shape& sh, const void* q, int rows, int64_t q_start,
                                const void* k, const void* v, const int64_t* kv_off,

@@ -181,6 +181,110 @@ __global__ __launch_bounds__(256) void sel_dec_logits(
 
 }
 
+// ------------------------------------------------------------------ decode step: the newest kernel
+// The compressed key of kernel j_new (the one token n - 1 completes) from the
+// cached keys: float64 sum of its p rows, rounded once, as infv2_compress_keys
+// does (a sum of bf16 rows is exact in float64, so the order does not matter).
+// kThreads threads: thread t sums d-octet t % 16 over rows t / 16,
+// t / 16 + kThreads / 16, ...; stores the key to ck_w[dst ..] and its stored
+// value, widened, to fkey.  Called by the whole block; ends with a barrier.
+template <bool kCkBf16, int kThreads>
+__device__ __forceinline__ void new_compressed_key(const bf16_t* __restrict__ src, int p,
+                                                   double (*fpart)[kHeadDim], float* fkey,
+                                                   void* __restrict__ ck_w, size_t dst) {
+    constexpr int kParts = kThreads / 16;            // row groups
+    const int t = threadIdx.x, oc = t & 15, rg = t >> 4;
+    double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    for (int r0 = rg; r0 < p; r0 += 4 * kParts) {    // four rows per batch of loads
+        uint4 x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = r0 + kParts * u;
+            x[u] = r < p ? ldg16(src + static_cast<size_t>(r) * kHeadDim + 8 * oc) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t w4[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += static_cast<double>(__uint_as_float(w4[e] << 16));
+                acc[2 * e + 1] += static_cast<double>(__uint_as_float(w4[e] & 0xffff0000u));
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) fpart[rg][8 * oc + e] = acc[e];
+    __syncthreads();
+    if (t < kHeadDim) {
+        double sum = 0.0;
+#pragma unroll
+        for (int x = 0; x < kParts; ++x) sum += fpart[x][t];
+        const double mean = sum / static_cast<double>(p);
+        if (kCkBf16) {
+            const bf16_t h = f64_to_bf16(mean);
+            static_cast<bf16_t*>(ck_w)[dst + t] = h;
+            fkey[t] = bf16_to_f32(h);
+        } else {
+            const float f = static_cast<float>(mean);
+            static_cast<float*>(ck_w)[dst + t] = f;
+            fkey[t] = f;
+        }
+    }
+    __syncthreads();
+}
+
+// the A-operand registers of a compressed-key row held widened in LDS (f), for
+// the lane of 8-dim group lg: bf16 keys 4 x 16 B, fp32 keys 8 x 16 B
+template <bool kCkBf16, int kU>
+__device__ __forceinline__ void key_regs_from(const float* f, int lg, uint4 (&raw)[kU]) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const float* x = &f[32 * ks + 8 * lg];
+        if (kCkBf16) {
+            raw[ks] = make_uint4(pack_exact(x[0], x[1]), pack_exact(x[2], x[3]),
+                                 pack_exact(x[4], x[5]), pack_exact(x[6], x[7]));
+        } else {
+            raw[2 * ks] = make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]),
+                                     __float_as_uint(x[2]), __float_as_uint(x[3]));
+            raw[2 * ks + 1] = make_uint4(__float_as_uint(x[4]), __float_as_uint(x[5]),
+                                         __float_as_uint(x[6]), __float_as_uint(x[7]));
+        }
+    }
+}
+
+// Z^T tile (16 kernels x 16 heads) from the A-operand registers: bf16 keys one
+// MFMA per 32-dim step; fp32 keys split into bf16 hi + lo (x = hi + lo +
+// O(2^-17 |x|)), two MFMAs per step, products exact in fp32
+template <bool kCkBf16, int kU>
+__device__ __forceinline__ f32x4_t key_tile_logits(const uint4 (&raw)[kU], const bf16x8_t (&qf)[4]) {
+    f32x4_t zt = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (kCkBf16) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) zt = mfma32(as_bf16x8(raw[ks]), qf[ks], zt);
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const uint4 a = raw[2 * ks], c = raw[2 * ks + 1];
+            const float x[8] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z), __uint_as_float(a.w),
+                                __uint_as_float(c.x), __uint_as_float(c.y), __uint_as_float(c.z), __uint_as_float(c.w)};
+            float hi[8], lo[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                hi[e] = bf16_to_f32(f32_to_bf16(x[e]));
+                lo[e] = x[e] - hi[e];
+            }
+            uint4 uh, ul;
+            uh.x = pack_exact(hi[0], hi[1]); uh.y = pack_exact(hi[2], hi[3]);
+            uh.z = pack_exact(hi[4], hi[5]); uh.w = pack_exact(hi[6], hi[7]);
+            ul.x = pack_rne(lo[0], lo[1]); ul.y = pack_rne(lo[2], lo[3]);
+            ul.z = pack_rne(lo[4], lo[5]); ul.w = pack_rne(lo[6], lo[7]);
+            zt = mfma32(as_bf16x8(uh), qf[ks], zt);
+            zt = mfma32(as_bf16x8(ul), qf[ks], zt);
+        }
+    }
+    return zt;
+}
+
 // ------------------------------------------------------------------ decode, pass 1 on the matrix cores
 // kLogWaves waves per block score 64 kernels (64 / kLogWaves each).  Z^T[kernel][head] = CK (64x128) . Q^T:
 // the compressed keys are the A operand as stored (lane: 8 consecutive d of one
@@ -205,8 +309,8 @@ __global__ __launch_bounds__(kLogWaves * 64) void sel_dec_logits_mfma(
     uint32_t* __restrict__ keys, const bf16_t* __restrict__ kcache, void* __restrict__ ck_w) {
     __shared__ float2 xm[kLogWaves][kGroup];   // each wave's (max, sum) per head
     constexpr int kFuseParts = kLogWaves * 64 / 16;     // row groups of the fused key sum
-    __shared__ double fpart[kFuse ? kFuseParts : 1][kFuse ? kHeadDim : 1];
-    __shared__ float fkey[kFuse ? kHeadDim : 1];        // the new key as stored, widened
+    __shared__ double fpart[kFuse ? kFuseParts : 1][kHeadDim];
+    __shared__ float fkey[kHeadDim];                    // the new key as stored, widened
     const int b = blockIdx.z, g = blockIdx.y, ch = blockIdx.x, t = threadIdx.x;
     const int l = t & 63, wv = t >> 6, lg = l >> 4, lc = l & 15;
     // round trip 1: offsets, length and the queries (independent loads)
@@ -256,71 +360,15 @@ __global__ __launch_bounds__(kLogWaves * 64) void sel_dec_logits_mfma(
     const bool fuse = kFuse && n >= p && (n - p) % s == 0 && j_new < ccap && j_new >= j0 &&
                       j_new < j0 + kChunkA;               // uniform over the block
     if (kFuse && fuse) {
-        // thread t sums d-octet t % 16 over rows t / 16, t / 16 + 8, ... of the kernel
-        const int oc = t & 15, rg = t >> 4;
         const bf16_t* src = kcache + (static_cast<size_t>(o0) * hkv + static_cast<size_t>(g) * (o1 - o0) +
-                                      static_cast<size_t>(j_new) * s) * kHeadDim + 8 * oc;
-        double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-        for (int r0 = rg; r0 < p; r0 += 4 * kFuseParts) {        // four rows per batch of loads
-            uint4 x[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int r = r0 + kFuseParts * u;
-                x[u] = r < p ? ldg16(src + static_cast<size_t>(r) * kHeadDim) : make_uint4(0u, 0u, 0u, 0u);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t w4[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    acc[2 * e] += static_cast<double>(__uint_as_float(w4[e] << 16));
-                    acc[2 * e + 1] += static_cast<double>(__uint_as_float(w4[e] & 0xffff0000u));
-                }
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) fpart[rg][8 * oc + e] = acc[e];
-        __syncthreads();
-        if (t < kHeadDim) {
-            double sum = 0.0;
-#pragma unroll
-            for (int x = 0; x < kFuseParts; ++x) sum += fpart[x][t];
-            const double mean = sum / static_cast<double>(p);
-            const size_t dst = static_cast<size_t>(cbase + j_new) * kHeadDim + t;
-            if (kCkBf16) {
-                const bf16_t h = f64_to_bf16(mean);
-                static_cast<bf16_t*>(ck_w)[dst] = h;
-                fkey[t] = bf16_to_f32(h);
-            } else {
-                const float f = static_cast<float>(mean);
-                static_cast<float*>(ck_w)[dst] = f;
-                fkey[t] = f;
-            }
-        }
-        __syncthreads();
+                                      static_cast<size_t>(j_new) * s) * kHeadDim;
+        new_compressed_key<kCkBf16, kLogWaves * 64>(src, p, fpart, fkey, ck_w,
+                                                    static_cast<size_t>(cbase + j_new) * kHeadDim);
         // the lanes holding row j_new take it from LDS instead of the stale load
 #pragma unroll
         for (int m2 = 0; m2 < kLogTiles; ++m2) {
             const int mt = kLogTiles * wv + m2;
-            if (j0 + 16 * mt + lc == j_new) {
-                if (kCkBf16) {
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
-                        const float* f = &fkey[32 * ks + 8 * lg];
-                        raw[m2][ks] = make_uint4(pack_exact(f[0], f[1]), pack_exact(f[2], f[3]),
-                                                 pack_exact(f[4], f[5]), pack_exact(f[6], f[7]));
-                    }
-                } else {
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
-                        const float* f = &fkey[32 * ks + 8 * lg];
-                        raw[m2][2 * ks] = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
-                                                     __float_as_uint(f[2]), __float_as_uint(f[3]));
-                        raw[m2][2 * ks + 1] = make_uint4(__float_as_uint(f[4]), __float_as_uint(f[5]),
-                                                         __float_as_uint(f[6]), __float_as_uint(f[7]));
-                    }
-                }
-            }
+            if (j0 + 16 * mt + lc == j_new) key_regs_from<kCkBf16>(fkey, lg, raw[m2]);
         }
     }
     // clear this block's share of the block-score keys (filled by pass 2)
@@ -333,34 +381,7 @@ __global__ __launch_bounds__(kLogWaves * 64) void sel_dec_logits_mfma(
     // Z^T tiles
     f32x4_t z[kLogTiles];
 #pragma unroll
-    for (int m2 = 0; m2 < kLogTiles; ++m2) {
-        f32x4_t& zt = z[m2];
-        zt = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (kCkBf16) {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) zt = mfma32(as_bf16x8(raw[m2][ks]), qf[ks], zt);
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const uint4 a = raw[m2][2 * ks], c = raw[m2][2 * ks + 1];
-                const float x[8] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z), __uint_as_float(a.w),
-                                    __uint_as_float(c.x), __uint_as_float(c.y), __uint_as_float(c.z), __uint_as_float(c.w)};
-                float hi[8], lo[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    hi[e] = bf16_to_f32(f32_to_bf16(x[e]));
-                    lo[e] = x[e] - hi[e];
-                }
-                uint4 uh, ul;
-                uh.x = pack_exact(hi[0], hi[1]); uh.y = pack_exact(hi[2], hi[3]);
-                uh.z = pack_exact(hi[4], hi[5]); uh.w = pack_exact(hi[6], hi[7]);
-                ul.x = pack_rne(lo[0], lo[1]); ul.y = pack_rne(lo[2], lo[3]);
-                ul.z = pack_rne(lo[4], lo[5]); ul.w = pack_rne(lo[6], lo[7]);
-                zt = mfma32(as_bf16x8(uh), qf[ks], zt);
-                zt = mfma32(as_bf16x8(ul), qf[ks], zt);
-            }
-        }
-    }
+    for (int m2 = 0; m2 < kLogTiles; ++m2) z[m2] = key_tile_logits<kCkBf16>(raw[m2], qf);
     // lane holds Z[head lc][kernel j0 + 16 mt + 4 lg + r]
     float mx = -INFINITY;
 #pragma unroll
