@@ -670,7 +670,7 @@ def bench_varlen_prefill(args, torch, tbs, gh) -> dict:
     idx = torch.empty((T, 2, 64), dtype=torch.int32, device="cuda")
     out = torch.empty_like(q)
     mx = int(rows.max())
-    ws_s = dev.ws(tbs.OP_SELECT_PREFILL, mx, 1, mx)
+    ws_s = dev.ws(tbs.OP_SELECT_PREFILL, T, len(lens), mx)        # all rows: one launch per kernel
     ws_a = dev.ws(tbs.OP_ATTN_PREFILL, mx, 1, mx)
     Timer_ = Timer(torch)
 

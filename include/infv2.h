@@ -335,12 +335,15 @@ int32_t infv2_sparse_attn_decode_noalloc(const infv2_config* cfg, const void* q,
  * before anything is launched; everything else is as for the single-sequence
  * calls, with kv_offsets / ck_offsets describing all `batch` sequences ([batch+1]).
  * Compressed keys up to n_c(q_start_per_seq[b] + rows_per_seq[b]) must be
- * present (infv2_compress_keys over the batch).  The workspace must hold the
- * largest single-sequence need: infv2_workspace_bytes(op, rows = max rows,
- * batch = 1, max_len = max (q_start + rows)).  The bf16 matrix-core attention
- * (block size 64) runs up to 64 sequences per launch, from a table of the
- * sequences passed with the launch; the selection, and the attention of other
- * shapes, run sequence after sequence on the stream through the
+ * present (infv2_compress_keys over the batch).  The workspace must hold at
+ * least the largest single-sequence need: infv2_workspace_bytes(op, rows = max
+ * rows, batch = 1, max_len = max (q_start + rows)).  The bf16 matrix-core
+ * attention (block size 64) runs up to 64 sequences per launch, from a table of
+ * the sequences passed with the launch.  The bf16 selection does the same when
+ * the workspace holds all rows of the call: infv2_workspace_bytes(
+ * INFV2_OP_SELECT_PREFILL, rows = total rows, batch = number of sequences with
+ * rows, max_len); with less it runs sequence after sequence.  Both give the
+ * same bits.  fp32 calls run sequence after sequence through the
  * single-sequence kernels.
  *
  *   q, block_idx, block_score, out   packed over all rows of the call
@@ -392,7 +395,9 @@ int32_t infv2_sparse_attn_prefill_bwd(const infv2_config* cfg, const void* q, in
                                       const void* out, const void* dout, void* dq, void* dk,
                                       void* dv, void* ws, size_t ws_bytes, void* stream);
 
-/* Workspace size in bytes for operation `op` (infv2_op) at the given sizes. */
+/* Workspace size in bytes for operation `op` (infv2_op) at the given sizes.
+ * SELECT_PREFILL with batch > 1: the varlen selection's one-launch workspace
+ * for `rows` rows of `batch` sequences (see infv2_select_blocks_varlen). */
 int32_t infv2_workspace_bytes(const infv2_config* cfg, int32_t op, int32_t rows, int32_t batch,
                               int64_t max_len, size_t* bytes);
 

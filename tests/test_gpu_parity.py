@@ -536,7 +536,9 @@ def test_selection_with_massive_ties():
 def test_varlen_prefill_equals_per_sequence_calls():
     """Serving-style prefill: three sequences, each with a chunk of rows starting
     mid-sequence, in one varlen call.  Selections and outputs equal the
-    single-sequence calls bit for bit and the oracle on sampled rows."""
+    single-sequence calls bit for bit and the oracle on sampled rows; the
+    selection run as one launch (workspace for all rows) equals the one run
+    sequence after sequence."""
     import trainable_block_sparse_amd as tbs
     from synth import f32_to_bf16_bits
     h = _harness()
@@ -562,7 +564,20 @@ def test_varlen_prefill_equals_per_sequence_calls():
                                    idx_v, None, ws_s)
     tbs.infv2_sparse_attn_prefill_varlen(cfg, q, rows, starts, dev.k, dev.v, dev.kv_offsets, idx_v,
                                          out_v, ws_a)
+    # a workspace for all rows of the call: the selection runs as one launch per
+    # kernel for the three sequences (above: sequence after sequence)
+    ws_all = dev.ws(tbs.OP_SELECT_PREFILL, T, 3, max_len)
+    idx_1 = torch.empty_like(idx_v)
+    score_1 = torch.empty((T, hkv, k), dtype=torch.float32, device="cuda")
+    score_v = torch.empty_like(score_1)
+    tbs.infv2_select_blocks_varlen(cfg, q, rows, starts, dev.ck, dev.ck_offsets, dev.kv_offsets,
+                                   idx_1, score_1, ws_all)
+    tbs.infv2_select_blocks_varlen(cfg, q, rows, starts, dev.ck, dev.ck_offsets, dev.kv_offsets,
+                                   idx_v, score_v, ws_s)
     torch.cuda.synchronize()
+    assert torch.equal(idx_1, idx_v), "one-launch selection differs from sequence after sequence"
+    # bit patterns: padding slots hold NaN
+    assert torch.equal(score_1.view(torch.int32), score_v.view(torch.int32)), "one-launch block scores differ"
     r0 = 0
     prm = params_of(wl)
     for b in range(3):

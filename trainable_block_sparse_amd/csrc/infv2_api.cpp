@@ -64,7 +64,9 @@ size_t ws_bytes_for(const infv2_config* c, int32_t op, int32_t rows, int32_t bat
     const Shape sh = make_shape(c);
     switch (op) {
         case INFV2_OP_SELECT_DECODE: return infv2::select_decode_ws(sh, batch, max_len).total;
-        case INFV2_OP_SELECT_PREFILL: return infv2::select_prefill_ws(sh, rows, max_len).total;
+        case INFV2_OP_SELECT_PREFILL:      // batch > 1: a varlen call's rows in one launch
+            return infv2::select_prefill_ws(sh, rows, max_len,
+                                            batch < 1 ? 1 : (batch < infv2::kVarlenMax ? batch : infv2::kVarlenMax)).total;
         case INFV2_OP_ATTN_DECODE: return infv2::attn_decode_ws(sh, batch).total;
         case INFV2_OP_ATTN_PREFILL: return infv2::attn_prefill_ws_bytes(sh, max_len);
         case INFV2_OP_ATTN_PREFILL_BWD: return rows > 0 ? infv2::bwd_ws(sh, rows, max_len).total : 0;
@@ -373,9 +375,59 @@ int32_t infv2_select_blocks_varlen(const infv2_config* c, const void* q, int32_t
                            ws_bytes, ws)) != INFV2_OK)
         return st;
     const Shape sh = make_shape(c);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
     const size_t qrow = static_cast<size_t>(c->num_q_heads) * c->head_dim *
                         (c->io_dtype == INFV2_BF16 ? 2 : 4);
     const size_t irow = static_cast<size_t>(c->num_kv_heads) * c->topk;
+    if (sh.io_bf16) {
+        // one launch per kernel for up to kVarlenMax sequences, when the workspace
+        // holds all of their rows (else sequence after sequence, below)
+        int64_t total = 0, max_len = 0;
+        int nseq = 0;
+        for (int32_t b = 0; b < batch; ++b) {
+            if (rows_per_seq[b] <= 0) continue;
+            total += rows_per_seq[b];
+            ++nseq;
+            const int64_t e = q_start_per_seq[b] + rows_per_seq[b];
+            max_len = e > max_len ? e : max_len;
+        }
+        if (nseq > 0 && total <= INT32_MAX &&
+            ws_bytes >= ws_bytes_for(c, INFV2_OP_SELECT_PREFILL, static_cast<int32_t>(total), nseq, max_len)) {
+            infv2::PrefillSeqs seqs{};
+            int grp = 0;
+            int64_t base = 0;                  // packed row of the table's row 0
+            auto flush = [&]() -> bool {
+                const bool ok = seqs.n == 0 ||
+                    infv2::launch_select_prefill_seqs(
+                        sh, seqs, static_cast<const char*>(q) + base * qrow, ck, ck_offsets, max_len,
+                        block_idx + base * irow, block_score ? block_score + base * irow : nullptr,
+                        ws, s) == hipSuccess;
+                seqs = infv2::PrefillSeqs{};
+                grp = 0;
+                return ok;
+            };
+            int64_t r0 = 0;
+            for (int32_t b = 0; b < batch; ++b) {
+                const int32_t rows = rows_per_seq[b];
+                const int ng = (rows + 15) / 16;
+                if (rows > 0) {
+                    if (seqs.n == infv2::kVarlenMax || grp + ng > infv2::kVarlenMaxGroups) {
+                        if (!flush()) return INFV2_ERR_DEVICE;
+                    }
+                    if (seqs.n == 0) base = r0;
+                    const int i = seqs.n++;
+                    grp += ng;
+                    seqs.grp_end[i] = grp;
+                    seqs.seq[i] = b;
+                    seqs.row0[i] = r0 - base;
+                    seqs.rows[i] = rows;
+                    seqs.q_start[i] = q_start_per_seq[b];
+                }
+                r0 += rows;
+            }
+            return flush() ? INFV2_OK : INFV2_ERR_DEVICE;
+        }
+    }
     int64_t r0 = 0;
     for (int32_t b = 0; b < batch; ++b) {
         const int32_t rows = rows_per_seq[b];
@@ -383,8 +435,7 @@ int32_t infv2_select_blocks_varlen(const infv2_config* c, const void* q, int32_t
             const hipError_t e = infv2::launch_select_prefill(
                 sh, static_cast<const char*>(q) + r0 * qrow, rows, q_start_per_seq[b], ck,
                 ck_offsets + b, q_start_per_seq[b] + rows, block_idx + r0 * irow,
-                block_score ? block_score + r0 * irow : nullptr, ws, nullptr,
-                static_cast<hipStream_t>(stream));
+                block_score ? block_score + r0 * irow : nullptr, ws, nullptr, s);
             if (e != hipSuccess) return INFV2_ERR_DEVICE;
         }
         r0 += rows;

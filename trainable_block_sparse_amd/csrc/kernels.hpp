@@ -63,15 +63,31 @@ struct SelectDecodeWs {
 };
 SelectDecodeWs select_decode_ws(const Shape& sh, int batch, int64_t max_len);
 
+// Sequences of one prefill launch (varlen calls: several; single-sequence calls:
+// one), passed by value as kernel arguments.  Rows are packed sequence after
+// sequence; group = 16 consecutive rows of one sequence.
+constexpr int kVarlenMax = 64;          // sequences per launch
+constexpr int kVarlenMaxGroups = 1 << 24;   // row groups per launch (grid of groups x KV heads)
+struct PrefillSeqs {
+    int n;                              // sequences in this launch (1 .. kVarlenMax)
+    int grp_end[kVarlenMax];            // row groups of sequences 0 .. i together
+    int seq[kVarlenMax];                // index into kv_offsets / ck_offsets
+    int64_t row0[kVarlenMax];           // first packed row
+    int rows[kVarlenMax];
+    int64_t q_start[kVarlenMax];
+};
+
 struct SelectPrefillWs {
     size_t lse, keys, total;
     int64_t nblk_max;
-    // fp32 compressed keys: their hi / lo bf16 rows, [2][Hkv][ld][d], for the
-    // fine kernels (hl, ld) and, in the coarse-LSE call, the coarse ones (hlc, ldc)
+    // fp32 compressed keys: their hi / lo bf16 rows, [seq][2][Hkv][ld][d], for
+    // the fine kernels (hl, ld) and, in the coarse-LSE call, the coarse ones
+    // (hlc, ldc; one sequence)
     size_t hl, hlc, total_coarse;
     int64_t ld, ldc;
 };
-SelectPrefillWs select_prefill_ws(const Shape& sh, int rows, int64_t max_len);
+// rows: all rows of the launch; nseq: its sequences (at most kVarlenMax)
+SelectPrefillWs select_prefill_ws(const Shape& sh, int rows, int64_t max_len, int nseq = 1);
 
 // Decode attention: each split gives one partial (max, sum, output) per head.
 // Vector-ALU path (fp32): a split is bps selected blocks (1 or 4).  Matrix-core
@@ -121,6 +137,13 @@ hipError_t launch_select_prefill(const Shape& sh, const void* q, int rows, int64
                                  const void* ck, const int64_t* ck_off, int64_t max_len,
                                  int32_t* idx, float* score, void* ws, const CoarseSel* cs,
                                  hipStream_t st);
+// bf16 queries: the sequences of `seqs` in one launch per kernel; q, idx, score
+// point at the table's row 0 (row0 relative to it), ck_off at the offsets of
+// sequence 0 of the call; ws sized by select_prefill_ws(rows of the table,
+// max_len, seqs.n)
+hipError_t launch_select_prefill_seqs(const Shape& sh, const PrefillSeqs& seqs, const void* q,
+                                      const void* ck, const int64_t* ck_off, int64_t max_len,
+                                      int32_t* idx, float* score, void* ws, hipStream_t st);
 
 // Device address of this device's static decode scratch (INFV2_NOALLOC_SCRATCH_BYTES,
 // looked up once per device); the no-allocation decode entry point passes it as
@@ -148,19 +171,19 @@ hipError_t launch_attn_decode_topk(const Shape& sh, const void* q, const void* k
                                    int32_t* idx, float* part_o, float2* part_ml, int nsplit,
                                    hipStream_t st);
 
-// Sequences of one prefill launch (varlen calls: several; single-sequence calls:
-// one), passed by value as kernel arguments.  Rows are packed sequence after
-// sequence; group = 16 consecutive rows of one sequence.
-constexpr int kVarlenMax = 64;          // sequences per launch
-constexpr int kVarlenMaxGroups = 1 << 24;   // row groups per launch (grid of groups x KV heads)
-struct PrefillSeqs {
-    int n;                              // sequences in this launch (1 .. kVarlenMax)
-    int grp_end[kVarlenMax];            // row groups of sequences 0 .. i together
-    int seq[kVarlenMax];                // index into kv_offsets / ck_offsets
-    int64_t row0[kVarlenMax];           // first packed row
-    int rows[kVarlenMax];
-    int64_t q_start[kVarlenMax];
-};
+// the launch's sequence holding row group grp / packed row r (relative to row0[0])
+__device__ __forceinline__ int seq_of_group(const PrefillSeqs& t, int grp) {
+    int i = 0;
+    while (i + 1 < t.n && grp >= t.grp_end[i]) ++i;
+    return i;
+}
+__device__ __forceinline__ int seq_of_row(const PrefillSeqs& t, int64_t r) {
+    int i = 0;
+    while (i + 1 < t.n && r >= t.row0[i + 1]) ++i;
+    return i;
+}
+// one-sequence table: rows at q_start, offsets kv/ck_off + 0
+PrefillSeqs one_seq(int rows, int64_t q_start);
 
 bool attn_prefill_mfma_ok(const Shape& sh);
 // transposed 64-key tiles of K or V for the matrix-core prefill kernels

@@ -92,7 +92,16 @@ SelectDecodeWs select_decode_ws(const Shape& sh, int batch, int64_t max_len) {
     return w;
 }
 
-SelectPrefillWs select_prefill_ws(const Shape& sh, int rows, int64_t max_len) {
+PrefillSeqs one_seq(int rows, int64_t q_start) {
+    PrefillSeqs t{};
+    t.n = 1;
+    t.grp_end[0] = (rows + 15) / 16;
+    t.rows[0] = rows;
+    t.q_start[0] = q_start;
+    return t;
+}
+
+SelectPrefillWs select_prefill_ws(const Shape& sh, int rows, int64_t max_len, int nseq) {
     SelectPrefillWs w{};
     w.nblk_max = (max_len + sh.m - 1) / sh.m;
     if (w.nblk_max < 1) w.nblk_max = 1;
@@ -105,7 +114,7 @@ SelectPrefillWs select_prefill_ws(const Shape& sh, int rows, int64_t max_len) {
         w.ld = num_kernels(max_len, sh.p, sh.s);
         w.ld = w.ld < 1 ? 1 : w.ld;
         w.ldc = max_len / sh.p + 1;
-        w.hl = off;   off += align256(static_cast<size_t>(2) * sh.hkv * w.ld * kHeadDim * sizeof(bf16_t));
+        w.hl = off;   off += align256(static_cast<size_t>(nseq) * 2 * sh.hkv * w.ld * kHeadDim * sizeof(bf16_t));
         w.total = off;
         w.hlc = off;  off += align256(static_cast<size_t>(2) * sh.hkv * w.ldc * kHeadDim * sizeof(bf16_t));
         w.total_coarse = off;
@@ -780,6 +789,7 @@ __global__ __launch_bounds__(256) void sel_pre_scores(
 //   pass 2: R = mean_h 2^(log2e z - LSE2_h): 4 heads in-lane + two cross-lane
 //           adds; block max of R over the tile, atomicMax into the row's keys
 constexpr int kPreRowsG = 16;
+static_assert(kPreRowsG == 16, "the launch tables count groups of 16 rows");
 constexpr int kPreTileK = 64;
 constexpr int kPreWaves = 8;                          // wave w: rows w + 8 i
 constexpr int kPreRW = kPreRowsG / kPreWaves;         // query rows per wave
@@ -792,15 +802,18 @@ constexpr float kPreMrInit = -1e30f;                  // pass 1 reference before
 // about 16 significant bits.  Written once per call as [part][KV head][ld][d]
 // (part 0 hi, 1 lo) for kernels 0 .. nk - 1 (those the call's rows see), instead
 // of by every thread block that stages a tile.  Thread -> one 8-value chunk.
-__global__ __launch_bounds__(256) void ck_split_hilo(const float* __restrict__ ck,
-                                                     const int64_t* __restrict__ ck_off, int hkv,
-                                                     int64_t nk, int64_t ld, bf16_t* __restrict__ hl) {
-    const int g = blockIdx.y;
+__global__ __launch_bounds__(256) void ck_split_hilo(const PrefillSeqs seqs, const float* __restrict__ ck,
+                                                     const int64_t* __restrict__ ck_off_all, int hkv,
+                                                     int p, int s, int64_t ld, bf16_t* __restrict__ hl_all) {
+    const int g = blockIdx.y, si = blockIdx.z;
     const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t* ck_off = ck_off_all + seqs.seq[si];
     const int64_t ccap = ck_off[1] - ck_off[0];
+    const int64_t nk = num_kernels(seqs.q_start[si] + seqs.rows[si], p, s);   // kernels its rows see
+    bf16_t* hl = hl_all + static_cast<int64_t>(si) * 2 * hkv * ld * kHeadDim;
     const int64_t r = e >> 4;
     const int c = static_cast<int>(e & 15);
-    if (r >= nk || r >= ccap) return;
+    if (r >= nk || r >= ccap || r >= ld) return;
     const float* src = ck + (ck_off[0] * hkv + static_cast<int64_t>(g) * ccap + r) * kHeadDim + 8 * c;
     const float4 a = *reinterpret_cast<const float4*>(src);
     const float4 b = *reinterpret_cast<const float4*>(src + 4);
@@ -820,10 +833,10 @@ __global__ __launch_bounds__(256) void ck_split_hilo(const float* __restrict__ c
 
 template <int kPass, bool kCkBf16>
 __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
-    const bf16_t* __restrict__ q, int rows, int64_t q_start, const void* __restrict__ ck,
-    const int64_t* __restrict__ ck_off, const bf16_t* __restrict__ hl, int64_t ld, int hq,
-    int hkv, int m, int p, int s, float score_scale, int64_t nblk_max, float* __restrict__ lse,
-    uint32_t* __restrict__ keys) {
+    const PrefillSeqs seqs, const bf16_t* __restrict__ q_all, const void* __restrict__ ck,
+    const int64_t* __restrict__ ck_off_all, const bf16_t* __restrict__ hl_all, int64_t ld, int hq,
+    int hkv, int m, int p, int s, float score_scale, int64_t nblk_max, float* __restrict__ lse_all,
+    uint32_t* __restrict__ keys_all) {
     // two stages of 64-kernel tiles: bf16 keys, or the hi and lo parts of fp32 keys
     __shared__ __attribute__((aligned(16))) bf16_t ck_hi[2][kPreTileK * kHeadDim];
     __shared__ __attribute__((aligned(16))) bf16_t ck_lo[kCkBf16 ? 1 : 2][kCkBf16 ? 8 : kPreTileK * kHeadDim];
@@ -832,7 +845,18 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
     __shared__ int32_t bk[kPreThreads][2];                   // pass 2: tile-relative kernel range per block
     const int g = blockIdx.y, t = threadIdx.x;
     const int w = t >> 6, l = t & 63, lg = l >> 4, lc = l & 15;
-    const int r0 = blockIdx.x * kPreRowsG;
+    // this block's sequence and its row group
+    const int grp = static_cast<int>(blockIdx.x);
+    const int si = seq_of_group(seqs, grp);
+    const int r0 = (grp - (si > 0 ? seqs.grp_end[si - 1] : 0)) * kPreRowsG;
+    const int rows = seqs.rows[si];
+    const int64_t q_start = seqs.q_start[si];
+    const size_t row0 = static_cast<size_t>(seqs.row0[si]);
+    const bf16_t* q = q_all + row0 * hq * kHeadDim;
+    float* lse = lse_all + row0 * hq;
+    uint32_t* keys = keys_all + row0 * hkv * nblk_max;
+    const int64_t* ck_off = ck_off_all + seqs.seq[si];
+    const bf16_t* hl = kCkBf16 ? nullptr : hl_all + static_cast<int64_t>(si) * 2 * hkv * ld * kHeadDim;
     const int64_t ccap = ck_off[1] - ck_off[0];
     // kernel rows of this KV head: the bf16 keys as stored, or the hi / lo rows
     // that ck_split_hilo wrote for fp32 keys ([part][KV head][ld][d])
@@ -1091,15 +1115,16 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
 // kThreads = 64 (one wave per row: no cross-wave barriers, every (row, KV head)
 // block resident at once) unless a row has too many blocks for 16 per lane.
 template <int kThreads, int kPer>
-__global__ __launch_bounds__(kThreads) void sel_pre_topk(int64_t q_start, int hkv, int m, int topk,
+__global__ __launch_bounds__(kThreads) void sel_pre_topk(const PrefillSeqs seqs, int hkv, int m, int topk,
                                                          int init, int local, int64_t nblk_max,
                                                          int per, const uint32_t* __restrict__ keys,
                                                          int32_t* __restrict__ idx,
                                                          float* __restrict__ score) {
     __shared__ TopkSmem<kThreads> sm;
-    const int row = blockIdx.x, g = blockIdx.y;
+    const int row = blockIdx.x, g = blockIdx.y;      // packed row (relative to the table's row 0)
+    const int si = seq_of_row(seqs, row);
     const size_t rg = static_cast<size_t>(row) * hkv + g;
-    int64_t c = (q_start + row) / m;
+    int64_t c = (seqs.q_start[si] + (row - seqs.row0[si])) / m;
     c = c < nblk_max - 1 ? c : nblk_max - 1;
     const int jb = static_cast<int>(threadIdx.x) * per;
     int cnt = static_cast<int>(c + 1) - jb;
@@ -1170,12 +1195,12 @@ static void launch_topk_dec(const Shape& sh, int batch, int64_t nblk_max, int64_
 #undef INFV2_L
 }
 
-static void launch_topk_pre(const Shape& sh, int rows, int64_t q_start, int64_t nblk_max,
+static void launch_topk_pre(const Shape& sh, const PrefillSeqs& seqs, int rows, int64_t nblk_max,
                             const uint32_t* keys, int32_t* idx, float* score, hipStream_t st) {
     const int per64 = topk_per(nblk_max, 64);
     if (per64 <= 16) {
 #define INFV2_L(P) sel_pre_topk<64, P><<<dim3(rows, sh.hkv), 64, 0, st>>>( \
-        q_start, sh.hkv, sh.m, sh.topk, sh.init, sh.local, nblk_max, per64, keys, idx, score)
+        seqs, sh.hkv, sh.m, sh.topk, sh.init, sh.local, nblk_max, per64, keys, idx, score)
         if (per64 <= 2) INFV2_L(2);
         else if (per64 <= 8) INFV2_L(8);
         else INFV2_L(16);
@@ -1184,7 +1209,7 @@ static void launch_topk_pre(const Shape& sh, int rows, int64_t q_start, int64_t 
     }
     const int per = topk_per(nblk_max, 256);
 #define INFV2_L(P) sel_pre_topk<256, P><<<dim3(rows, sh.hkv), 256, 0, st>>>( \
-        q_start, sh.hkv, sh.m, sh.topk, sh.init, sh.local, nblk_max, per, keys, idx, score)
+        seqs, sh.hkv, sh.m, sh.topk, sh.init, sh.local, nblk_max, per, keys, idx, score)
     INFV2_TOPK_DISPATCH(per, INFV2_L);
 #undef INFV2_L
 }
@@ -1285,87 +1310,96 @@ hipError_t launch_select_decode(const Shape& sh, const void* q, const void* ck,
 
 // Pass 1 (per-head LogSumExp and clearing the rows' block keys) for rows
 // [r0, r0 + nr) of the call, over compressed keys `ck` of kernel size p, stride s.
-// fp32 keys of kernels 0 .. nk - 1 -> their hi / lo rows (ck_split_hilo)
-static void split_hilo(const Shape& sh, const void* ck, const int64_t* ck_off, int64_t nk,
-                       int64_t ld, bf16_t* hl, hipStream_t st) {
-    nk = nk < ld ? nk : ld;
-    if (nk <= 0) return;
-    const dim3 grid(static_cast<unsigned>((nk * 16 + 255) / 256), sh.hkv);
-    launch_timed(INFV2_KERNEL_SELECT_PREFILL, ck_split_hilo, grid, dim3(256), 0, st,
-                 static_cast<const float*>(ck), ck_off, sh.hkv, nk, ld, hl);
+// fp32 keys -> their hi / lo rows (ck_split_hilo), for the kernels each
+// sequence's rows see, up to ld per sequence
+static void split_hilo(const Shape& sh, const PrefillSeqs& seqs, const void* ck, const int64_t* ck_off,
+                       int p, int s, int64_t ld, bf16_t* hl, hipStream_t st) {
+    if (ld <= 0) return;
+    const dim3 grid(static_cast<unsigned>((ld * 16 + 255) / 256), sh.hkv, seqs.n);
+    launch_timed(INFV2_KERNEL_SELECT_PREFILL, ck_split_hilo, grid, dim3(256), 0, st, seqs,
+                 static_cast<const float*>(ck), ck_off, sh.hkv, p, s, ld, hl);
 }
 
+// rows [r0, r0 + nr) of a one-sequence launch whose first row sits at q_start
+static PrefillSeqs sub_seq(int r0, int nr, int64_t q_start) {
+    PrefillSeqs t = one_seq(nr, q_start + r0);
+    t.row0[0] = r0;                       // relative to the launch's row 0
+    return t;
+}
+
+// Pass 1 (per-head LogSumExp and clearing the rows' block keys) over the rows of
+// table t, with compressed keys `ck` of kernel size p, stride s.  The vector-ALU
+// kernels (fp32 queries) take one sequence.
 template <typename Tq, typename Tck>
-static void pre_pass1(const Shape& sh, const void* q, int r0, int nr, int64_t q_start,
-                      const void* ck, const int64_t* ck_off, int p, int s, const bf16_t* hl,
-                      int64_t ld, const SelectPrefillWs& w, float* lse, uint32_t* keys,
-                      hipStream_t st) {
-    if (nr <= 0) return;
-    const size_t qrow = static_cast<size_t>(sh.hq) * kHeadDim;
-    float* l = lse + static_cast<size_t>(r0) * sh.hq;
-    uint32_t* kb = keys + static_cast<size_t>(r0) * sh.hkv * w.nblk_max;
+static void pre_pass1(const Shape& sh, const PrefillSeqs& t, const void* q, const void* ck,
+                      const int64_t* ck_off, int p, int s, const bf16_t* hl, int64_t ld,
+                      const SelectPrefillWs& w, float* lse, uint32_t* keys, hipStream_t st) {
+    const int groups = t.grp_end[t.n - 1];
+    if (groups <= 0) return;
     if (sizeof(Tq) == 2) {
-        dim3 gm((nr + kPreRowsG - 1) / kPreRowsG, sh.hkv);
-        launch_timed(INFV2_KERNEL_SELECT_PREFILL, sel_pre_mfma<1, sizeof(Tck) == 2>, gm,
-                     dim3(kPreThreads), 0, st,
-            static_cast<const bf16_t*>(q) + r0 * qrow, nr, q_start + r0, ck, ck_off, hl, ld, sh.hq,
-            sh.hkv, sh.m, p, s, sh.score_scale, w.nblk_max, l, kb);
+        launch_timed(INFV2_KERNEL_SELECT_PREFILL, sel_pre_mfma<1, sizeof(Tck) == 2>,
+                     dim3(groups, sh.hkv), dim3(kPreThreads), 0, st, t,
+            static_cast<const bf16_t*>(q), ck, ck_off, hl, ld, sh.hq, sh.hkv, sh.m, p, s,
+            sh.score_scale, w.nblk_max, lse, keys);
     } else {
+        const size_t r0 = static_cast<size_t>(t.row0[0]);
+        const int nr = t.rows[0];
+        const size_t qrow = static_cast<size_t>(sh.hq) * kHeadDim;
         dim3 g1((nr + kRowsPre - 1) / kRowsPre, sh.hkv);
         launch_timed(INFV2_KERNEL_SELECT_PREFILL, sel_pre_lse<Tq, Tck>, g1, dim3(256), 0, st,
-                     static_cast<const Tq*>(q) + r0 * qrow, nr, q_start + r0,
-                     static_cast<const Tck*>(ck), ck_off, sh.hq, sh.hkv, p, s, sh.score_scale,
-                     w.nblk_max, l, kb);
+                     static_cast<const Tq*>(q) + r0 * qrow, nr, t.q_start[0],
+                     static_cast<const Tck*>(ck), ck_off + t.seq[0], sh.hq, sh.hkv, p, s,
+                     sh.score_scale, w.nblk_max, lse + r0 * sh.hq, keys + r0 * sh.hkv * w.nblk_max);
     }
 }
 
+// The selection of the rows of table t (bf16 queries: any number of sequences;
+// fp32 queries and the coarse-kernel LSE: one).
 template <typename Tq, typename Tck>
-static void pre_launch(const Shape& sh, const void* q, int rows, int64_t q_start, const void* ck,
+static void pre_launch(const Shape& sh, const PrefillSeqs& t, const void* q, const void* ck,
                        const int64_t* ck_off, const SelectPrefillWs& w, char* ws, int32_t* idx,
                        float* score, const CoarseSel* cs, hipStream_t st) {
-    dim3 g1((rows + kRowsPre - 1) / kRowsPre, sh.hkv);
+    const int rows_all = static_cast<int>(t.row0[t.n - 1] + t.rows[t.n - 1]);
     float* lse = reinterpret_cast<float*>(ws + w.lse);
     uint32_t* keys = reinterpret_cast<uint32_t*>(ws + w.keys);
     // matrix-core passes over fp32 keys read their hi / lo rows, made once here
     constexpr bool kSplit = sizeof(Tq) == 2 && sizeof(Tck) == 4;
     bf16_t* hl = kSplit ? reinterpret_cast<bf16_t*>(ws + w.hl) : nullptr;
     bf16_t* hlc = kSplit && cs ? reinterpret_cast<bf16_t*>(ws + w.hlc) : nullptr;
-    if (kSplit) split_hilo(sh, ck, ck_off, num_kernels(q_start + rows, sh.p, sh.s), w.ld, hl, st);
+    if (kSplit) split_hilo(sh, t, ck, ck_off, sh.p, sh.s, w.ld, hl, st);
     if (cs) {
         // rows that see a coarse kernel take pass 1 over the coarse kernels; the
         // few before the first one (dense rows) keep the exact normaliser
+        const int rows = t.rows[0];
+        const int64_t q_start = t.q_start[0];
         int64_t nf = static_cast<int64_t>(cs->coarse) - 1 - q_start;
         nf = nf < 0 ? 0 : (nf > rows ? rows : nf);
-        if (kSplit)
-            split_hilo(sh, cs->ckc, cs->ckc_off, num_kernels(q_start + rows, cs->coarse, cs->coarse),
-                       w.ldc, hlc, st);
-        pre_pass1<Tq, Tck>(sh, q, 0, static_cast<int>(nf), q_start, ck, ck_off, sh.p, sh.s, hl, w.ld,
-                           w, lse, keys, st);
-        pre_pass1<Tq, Tck>(sh, q, static_cast<int>(nf), rows - static_cast<int>(nf), q_start, cs->ckc,
-                           cs->ckc_off, cs->coarse, cs->coarse, hlc, w.ldc, w, lse, keys, st);
+        if (kSplit) split_hilo(sh, t, cs->ckc, cs->ckc_off, cs->coarse, cs->coarse, w.ldc, hlc, st);
+        if (nf > 0)
+            pre_pass1<Tq, Tck>(sh, sub_seq(0, static_cast<int>(nf), q_start), q, ck, ck_off, sh.p,
+                               sh.s, hl, w.ld, w, lse, keys, st);
+        if (rows - nf > 0)
+            pre_pass1<Tq, Tck>(sh, sub_seq(static_cast<int>(nf), rows - static_cast<int>(nf), q_start),
+                               q, cs->ckc, cs->ckc_off, cs->coarse, cs->coarse, hlc, w.ldc, w, lse,
+                               keys, st);
     } else {
-        pre_pass1<Tq, Tck>(sh, q, 0, rows, q_start, ck, ck_off, sh.p, sh.s, hl, w.ld, w, lse, keys, st);
+        pre_pass1<Tq, Tck>(sh, t, q, ck, ck_off, sh.p, sh.s, hl, w.ld, w, lse, keys, st);
     }
     if (sizeof(Tq) == 2) {
         constexpr bool kB = sizeof(Tck) == 2;
-        dim3 gm((rows + kPreRowsG - 1) / kPreRowsG, sh.hkv);
-        const bf16_t* qq = static_cast<const bf16_t*>(q);
-        {
-            launch_timed(INFV2_KERNEL_SELECT_PREFILL, sel_pre_mfma<2, kB>, gm, dim3(kPreThreads), 0,
-                         st, qq, rows, q_start, ck, ck_off, hl, w.ld, sh.hq, sh.hkv, sh.m, sh.p,
-                         sh.s, sh.score_scale, w.nblk_max, lse, keys);
-        }
-        KernelTimer kt(INFV2_KERNEL_SELECT_TOPK, st);
-        launch_topk_pre(sh, rows, q_start, w.nblk_max, keys, idx, score, st);
-        return;
-    }
-    {
+        launch_timed(INFV2_KERNEL_SELECT_PREFILL, sel_pre_mfma<2, kB>, dim3(t.grp_end[t.n - 1], sh.hkv),
+                     dim3(kPreThreads), 0, st, t, static_cast<const bf16_t*>(q), ck, ck_off, hl,
+                     w.ld, sh.hq, sh.hkv, sh.m, sh.p, sh.s, sh.score_scale, w.nblk_max, lse, keys);
+    } else {
+        const int rows = t.rows[0];
+        dim3 g1((rows + kRowsPre - 1) / kRowsPre, sh.hkv);
         launch_timed(INFV2_KERNEL_SELECT_PREFILL, sel_pre_scores<Tq, Tck>, g1, dim3(256), 0, st,
-                     static_cast<const Tq*>(q), rows, q_start, static_cast<const Tck*>(ck), ck_off,
-                     sh.hq, sh.hkv, sh.m, sh.p, sh.s, sh.score_scale, w.nblk_max, lse, keys);
+                     static_cast<const Tq*>(q), rows, t.q_start[0], static_cast<const Tck*>(ck),
+                     ck_off + t.seq[0], sh.hq, sh.hkv, sh.m, sh.p, sh.s, sh.score_scale, w.nblk_max,
+                     lse, keys);
     }
     KernelTimer kt(INFV2_KERNEL_SELECT_TOPK, st);
-    launch_topk_pre(sh, rows, q_start, w.nblk_max, keys, idx, score, st);
+    launch_topk_pre(sh, t, rows_all, w.nblk_max, keys, idx, score, st);
 }
 
 hipError_t launch_select_prefill(const Shape& sh, const void* q, int rows, int64_t q_start,
@@ -1378,13 +1412,26 @@ hipError_t launch_select_prefill(const Shape& sh, const void* q, int rows, int64
         return hipGetLastError();
     }
     char* base = static_cast<char*>(ws);
+    const PrefillSeqs t = one_seq(rows, q_start);
     if (sh.io_bf16) {
-        if (sh.ck_bf16) pre_launch<bf16_t, bf16_t>(sh, q, rows, q_start, ck, ck_off, w, base, idx, score, cs, st);
-        else pre_launch<bf16_t, float>(sh, q, rows, q_start, ck, ck_off, w, base, idx, score, cs, st);
+        if (sh.ck_bf16) pre_launch<bf16_t, bf16_t>(sh, t, q, ck, ck_off, w, base, idx, score, cs, st);
+        else pre_launch<bf16_t, float>(sh, t, q, ck, ck_off, w, base, idx, score, cs, st);
     } else {
-        if (sh.ck_bf16) pre_launch<float, bf16_t>(sh, q, rows, q_start, ck, ck_off, w, base, idx, score, cs, st);
-        else pre_launch<float, float>(sh, q, rows, q_start, ck, ck_off, w, base, idx, score, cs, st);
+        if (sh.ck_bf16) pre_launch<float, bf16_t>(sh, t, q, ck, ck_off, w, base, idx, score, cs, st);
+        else pre_launch<float, float>(sh, t, q, ck, ck_off, w, base, idx, score, cs, st);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_select_prefill_seqs(const Shape& sh, const PrefillSeqs& seqs, const void* q,
+                                      const void* ck, const int64_t* ck_off, int64_t max_len,
+                                      int32_t* idx, float* score, void* ws, hipStream_t st) {
+    if (!sh.io_bf16 || seqs.n < 1 || seqs.n > kVarlenMax) return hipErrorInvalidValue;
+    const int rows_all = static_cast<int>(seqs.row0[seqs.n - 1] + seqs.rows[seqs.n - 1]);
+    const SelectPrefillWs w = select_prefill_ws(sh, rows_all, max_len, seqs.n);
+    char* base = static_cast<char*>(ws);
+    if (sh.ck_bf16) pre_launch<bf16_t, bf16_t>(sh, seqs, q, ck, ck_off, w, base, idx, score, nullptr, st);
+    else pre_launch<bf16_t, float>(sh, seqs, q, ck, ck_off, w, base, idx, score, nullptr, st);
     return hipGetLastError();
 }
 
