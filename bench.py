@@ -163,13 +163,13 @@ def roofline_of(times: dict, work: dict, bound: str, peak: float, unit: str, sca
 DURATION_FILE = os.path.join(ROOT, "profiles", "kernel_durations.json")
 CALIBRATION_MIB = 256          # size of the copies that --copy-calibration runs for the counter passes
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-# kernel family -> (source file, rocprofv3 kernel-name prefix)
-KERNEL_SOURCE = {"attn_decode": ("attn_decode.hip", "infv2::attn_decode_mfma"),
-                 "select_logits": ("select.hip", "infv2::sel_dec_logits_mfma"),
-                 "attn_prefill": ("attn_prefill.hip", "infv2::attn_prefill_mfma"),
-                 "select_prefill": ("select.hip", "infv2::sel_pre_mfma"),
-                 "bwd_row": ("attn_bwd_mfma.hip", "infv2::bwd_row_mfma"),
-                 "bwd_col": ("attn_bwd_mfma.hip", "infv2::bwd_col_mfma")}
+# kernel family -> (source file, rocprofv3 kernel-name prefixes)
+KERNEL_SOURCE = {"attn_decode": ("attn_decode.hip", ("infv2::attn_decode_mfma", "infv2::attn_decode_topk_mfma")),
+                 "select_logits": ("select.hip", ("infv2::sel_dec_logits_mfma",)),
+                 "attn_prefill": ("attn_prefill.hip", ("infv2::attn_prefill_mfma",)),
+                 "select_prefill": ("select.hip", ("infv2::sel_pre_mfma",)),
+                 "bwd_row": ("attn_bwd_mfma.hip", ("infv2::bwd_row_mfma",)),
+                 "bwd_col": ("attn_bwd_mfma.hip", ("infv2::bwd_col_mfma",))}
 
 
 def source_digest(kernel: str) -> str:
@@ -198,15 +198,19 @@ def profiled(path: str, workload: str, kernel: str):
 
 def _rocprof_name_family(name: str):
     base = name[5:] if name.startswith("void ") else name
-    for fam, (_, prefix) in KERNEL_SOURCE.items():
-        if base.startswith(prefix):
+    for fam, (_, prefixes) in KERNEL_SOURCE.items():
+        if base.startswith(prefixes):
             return fam
     return None
 
 
 def summarize_rocprof(kind: str, workload: str, paths, command: str) -> int:
     """Fold rocprofv3 CSV output into the committed profile records.
-    kind "stats":   paths = [<name>_kernel_stats.csv]  -> kernel_durations.json
+    kind "stats":   paths = [<name>_kernel_stats.csv, <name>_kernel_trace.csv]
+                    -> kernel_durations.json: the average over every launch of the
+                    run, and over the launches of the per-kernel timing passes
+                    (those queued behind the spin kernel; what "kernels" and the
+                    live roofline time)
     kind "traffic": paths = [FETCH_SIZE counter_collection.csv, WRITE_SIZE one]
                     -> traffic.json, each counter scaled by what it reads for the
                     device-to-device copies of known size (--copy-calibration)."""
@@ -218,22 +222,44 @@ def summarize_rocprof(kind: str, workload: str, paths, command: str) -> int:
         db = {}
     entry = db.setdefault(workload, {})
     if kind == "stats":
+        # launches inside the timing passes: after a spin kernel, up to the next
+        # copy / fill (the next pass's cache flush) or spin kernel
+        passes = {}
+        trace = sorted(csv.DictReader(open(paths[1])), key=lambda r: int(r["Start_Timestamp"]))
+        inside = False
+        for r in trace:
+            name = r["Kernel_Name"]
+            if "sleep" in name or "spin" in name:
+                inside = True
+                continue
+            if name.startswith("__amd_rocclr") or "elementwise_kernel" in name:
+                inside = False
+                continue
+            fam = _rocprof_name_family(name)
+            if inside and fam is not None:
+                passes.setdefault(fam, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        seen = set()
         for row in csv.DictReader(open(paths[0])):
             fam = _rocprof_name_family(row["Name"])
             if fam is None:
                 continue
             calls = int(row["Calls"])
             avg_us = float(row["AverageNs"]) / 1e3
-            prev = entry.get(fam)
-            if prev and prev.get("command") == command and prev["kernel"] != row["Name"]:
-                # several instantiations of one family: merge by call count
+            if fam in seen:
+                # several instantiations of one family in this run: merge by call count
+                prev = entry[fam]
                 tot = prev["calls"] + calls
-                avg_us = (prev["avg_us"] * prev["calls"] + avg_us * calls) / tot
+                avg_us = (prev["avg_us_all"] * prev["calls"] + avg_us * calls) / tot
                 calls = tot
-            entry[fam] = {"kernel": row["Name"].split("(")[0], "calls": calls, "avg_us": avg_us,
+            seen.add(fam)
+            pv = passes.get(fam, [])
+            entry[fam] = {"kernel": row["Name"].split("(")[0], "calls": calls, "avg_us_all": avg_us,
                           "min_us": float(row["MinNs"]) / 1e3, "max_us": float(row["MaxNs"]) / 1e3,
+                          "timing_pass_launches": len(pv),
+                          "avg_us": float(np.mean(pv)) if pv else avg_us,
                           "command": command, "source_sha256": source_digest(fam)}
-            print(f"{workload} {fam}: {calls} calls, average {avg_us:.2f} us")
+            print(f"{workload} {fam}: {calls} calls, average {avg_us:.2f} us; "
+                  f"{len(pv)} in timing passes, average {entry[fam]['avg_us']:.2f} us")
     else:
         per = {}
         for counter, path in zip(("FETCH_SIZE", "WRITE_SIZE"), paths):
@@ -800,7 +826,7 @@ def _agreement(a: np.ndarray, e: np.ndarray):
 
 def bench_coarse(args, torch, tbs, gh) -> dict:
     """The coarse-kernel LogSumExp selection against the exact one: selection time
-    per call and agreement of the selections, at 128K decode (32 replicas, a new
+    per call and agreement of the selections, at 128K decode (cache replicas for 512 MiB between uses, a new
     query per step, as the main line) and over the 32K prefill (chunks of 4096)."""
     from synth import make_config, extra_decode_queries
     out = {}
@@ -1035,7 +1061,8 @@ def main() -> int:
                     default=None,
                     help="run one workload only and print its record (for profiling)")
     ap.add_argument("--summarize-rocprof", nargs="+", metavar=("KIND", "CSV"), default=None,
-                    help="fold rocprofv3 output into profiles/: 'stats <kernel_stats.csv>' or "
+                    help="fold rocprofv3 output into profiles/: 'stats <kernel_stats.csv> "
+                         "<kernel_trace.csv>' or "
                          "'traffic <FETCH_SIZE counter_collection.csv> <WRITE_SIZE one>' "
                          "(no GPU; needs --workload and --command)")
     ap.add_argument("--workload", default=None, help="workload name for --summarize-rocprof")
@@ -1043,9 +1070,10 @@ def main() -> int:
     args = ap.parse_args()
     if args.summarize_rocprof:
         kind, paths = args.summarize_rocprof[0], args.summarize_rocprof[1:]
-        if kind not in ("stats", "traffic") or len(paths) != (1 if kind == "stats" else 2) \
+        if kind not in ("stats", "traffic") or len(paths) != 2 \
                 or not args.workload or not args.command:
-            ap.error("--summarize-rocprof stats CSV | traffic FETCH_CSV WRITE_CSV, with --workload and --command")
+            ap.error("--summarize-rocprof stats STATS_CSV TRACE_CSV | traffic FETCH_CSV WRITE_CSV, "
+                     "with --workload and --command")
         return summarize_rocprof(kind, args.workload, paths, args.command)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

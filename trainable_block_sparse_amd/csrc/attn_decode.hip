@@ -213,22 +213,22 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(
                      (bg * nsplit + sp) * kGroup);
 }
 
-// Small batches: the top-k of the (sequence, KV head) runs in every thread block
+// Decode step: the top-k of the (sequence, KV head) runs in every thread block
 // of its attention, before the tiles, so the step needs no separate top-k launch
 // and no round trip of the block list through memory.  The selection is the
 // one the top-k kernel makes (same code, same keys); split 0 also stores it.
-// One tile per wave (at two, the redundant selections cost what the launch
-// saves).  Keys: the block-score keys of the scoring pass, rows of kld entries
-// padded to 256 kPer.
+// Tiles as attn_decode_mfma.  Keys: the block-score keys of the scoring pass,
+// rows of kld entries padded to 256 kPer.
 constexpr int kFusedTopkMax = 256;       // largest top-k the fused kernel keeps in LDS
 
-template <int kPer>
+template <int kPer, bool kRun>
 __global__ __launch_bounds__(256) void attn_decode_topk_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const int64_t* __restrict__ kv_off, const int64_t* __restrict__ lens, int lens_end,
     const uint32_t* __restrict__ keys, int64_t kld, int64_t nblk_max, int init, int local,
     int32_t* __restrict__ idx_out, float* __restrict__ part_o, float2* __restrict__ part_ml,
-    int hq, int hkv, int m, int topk, int nsplit, float scale_log2) {
+    int hq, int hkv, int m, int topk, int nsplit, int tpw_arg, float scale_log2) {
+    const int tpw = kRun ? tpw_arg : 1;
     static_assert(kPer % 2 == 0, "keys load in pairs");
     __shared__ union { TopkSmem<256> tk; DecSmem dec; } sm;
     __shared__ int32_t sel[kFusedTopkMax];
@@ -269,13 +269,13 @@ __global__ __launch_bounds__(256) void attn_decode_topk_mfma(
     if (sp == 0)
         for (int r = t; r < topk; r += 256) idx_out[bg * topk + r] = sel[r];
     const int tpb = m >> 4;
-    const int u0 = sp * 4 + w;           // this wave's tile
+    const int u0 = (sp * 4 + w) * tpw;   // this wave's first tile
     const int e = u0 / tpb, st0 = u0 - e * tpb;
     const int32_t blk = (e < topk) ? sel[e] : -1;
     const bf16_t* kh = k + (static_cast<size_t>(o0) * hkv + static_cast<size_t>(g) * cap) * kHeadDim + 8 * lg;
     const bf16_t* vh = v + (static_cast<size_t>(o0) * hkv + static_cast<size_t>(g) * cap) * kHeadDim + 8 * lg;
-    decode_run<false>(sm.dec, qf, blk, st0, 1, m, n, kh, vh, scale_log2, part_o, part_ml,
-                      (bg * nsplit + sp) * kGroup);
+    decode_run<kRun>(sm.dec, qf, blk, st0, tpw, m, n, kh, vh, scale_log2, part_o, part_ml,
+                     (bg * nsplit + sp) * kGroup);
 }
 
 // Merge of the split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
@@ -387,20 +387,23 @@ hipError_t launch_attn_decode_topk(const Shape& sh, const void* q, const void* k
                                    const int64_t* kv_off, const int64_t* kv_lens, int batch,
                                    const uint32_t* keys, int64_t kld, int64_t nblk_max,
                                    int32_t* idx, float* part_o, float2* part_ml, int nsplit,
-                                   hipStream_t st) {
+                                   int tpw, hipStream_t st) {
     dim3 grid(nsplit, sh.hkv, batch);
     const float scale_log2 = sh.attn_scale * 1.4426950408889634f;
     const int64_t* lens = kv_lens ? kv_lens : kv_off + 1;
     const int lens_end = kv_lens ? 0 : 1;
     const int per = topk_per(nblk_max, 256);
-#define INFV2_L(P) launch_timed(INFV2_KERNEL_ATTN_DECODE, attn_decode_topk_mfma<P>, grid, dim3(256), 0, st, \
+#define INFV2_L(P, R) launch_timed(INFV2_KERNEL_ATTN_DECODE, attn_decode_topk_mfma<P, R>, grid, dim3(256), 0, st, \
         static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), \
         kv_off, lens, lens_end, keys, kld, nblk_max, sh.init, sh.local, idx, part_o, part_ml, \
-        sh.hq, sh.hkv, sh.m, sh.topk, nsplit, scale_log2)
-    if (per <= 2) INFV2_L(2);
-    else if (per <= 8) INFV2_L(8);
-    else if (per <= 16) INFV2_L(16);
-    else return hipErrorInvalidValue;
+        sh.hq, sh.hkv, sh.m, sh.topk, nsplit, tpw, scale_log2)
+    if (tpw > 1) {
+        if (per <= 2) INFV2_L(2, true); else if (per <= 8) INFV2_L(8, true); else if (per <= 16) INFV2_L(16, true);
+        else return hipErrorInvalidValue;
+    } else {
+        if (per <= 2) INFV2_L(2, false); else if (per <= 8) INFV2_L(8, false); else if (per <= 16) INFV2_L(16, false);
+        else return hipErrorInvalidValue;
+    }
 #undef INFV2_L
     return hipGetLastError();
 }

@@ -266,10 +266,10 @@ int32_t infv2_decode_step(const infv2_config* c, const void* q, const void* k, c
     hipError_t e;
     if (sh.io_bf16) {
         // the selection's first kernel also builds the newest token's compressed
-        // key; at small batches (one tile per wave) the attention makes the top-k
-        // selection itself from the block-score keys
+        // key, and the attention makes the top-k selection itself from the
+        // block-score keys
         const infv2::AttnDecodeWs aw = infv2::attn_decode_ws(sh, batch);
-        const bool fused = aw.tpw == 1 && infv2::attn_decode_topk_ok(sh, sw.nblk_max);
+        const bool fused = infv2::attn_decode_topk_ok(sh, sw.nblk_max);
         e = infv2::launch_select_decode(sh, q, ck, ck_offsets, kv_offsets, kv_lens, batch, max_len,
                                         block_idx, nullptr, ws, nullptr, s, k, fused);
         if (e != hipSuccess) return INFV2_ERR_DEVICE;
@@ -279,7 +279,7 @@ int32_t infv2_decode_step(const infv2_config* c, const void* q, const void* k, c
             float2* pml = reinterpret_cast<float2*>(ws_attn + aw.part_ml);
             e = infv2::launch_attn_decode_topk(sh, q, k, v, kv_offsets, kv_lens, batch, keys,
                                                sw.keys_ld, sw.nblk_max, block_idx, po, pml,
-                                               aw.nsplit_m, s);
+                                               aw.nsplit_m, aw.tpw, s);
             if (e != hipSuccess) return status_of(e);
             return status_of(infv2::launch_attn_decode_merge(sh, po, pml, out, batch, aw.nsplit_m, s));
         }

@@ -93,7 +93,7 @@ SelectPrefillWs select_prefill_ws(const Shape& sh, int rows, int64_t max_len, in
 // Vector-ALU path (fp32): a split is bps selected blocks (1 or 4).  Matrix-core
 // path (bf16): a split is four waves, each a run of tpw 16-key tiles.
 constexpr int kDecodeFewBlocks = 256;   // vector-ALU: below this many 4-block splits, 1-block splits
-constexpr int kDecodeWaveTarget = 4096; // matrix cores: waves in flight before runs grow past one tile
+constexpr int kDecodeWaveTarget = 2048; // matrix cores: waves in flight before runs grow past one tile
 constexpr int kDecodeMaxTpw = 8;        // matrix cores: longest tile run of a wave
 constexpr int kDecodeMaxSplit = 1024;   // splits the merge kernel takes
 struct AttnDecodeWs {
@@ -161,15 +161,15 @@ hipError_t launch_attn_decode_mfma(const Shape& sh, const void* q, const void* k
 hipError_t launch_attn_decode_merge(const Shape& sh, const float* part_o, const float2* part_ml,
                                     void* out, int batch, int nsplit, hipStream_t st);
 // Decode attention that first makes the top-k selection from the block-score
-// keys (rows of kld, one per (sequence, KV head)) in every thread block, one
-// 16-key tile per wave (nsplit = the matrix-core path's splits at tpw 1); split
-// 0 stores the selection in idx.  attn_decode_topk_ok: shapes it takes.
+// keys (rows of kld, one per (sequence, KV head)) in every thread block, with
+// the matrix-core path's splits (nsplit, tpw); split 0 stores the selection in
+// idx.  attn_decode_topk_ok: shapes it takes.
 bool attn_decode_topk_ok(const Shape& sh, int64_t nblk_max);
 hipError_t launch_attn_decode_topk(const Shape& sh, const void* q, const void* k, const void* v,
                                    const int64_t* kv_off, const int64_t* kv_lens, int batch,
                                    const uint32_t* keys, int64_t kld, int64_t nblk_max,
                                    int32_t* idx, float* part_o, float2* part_ml, int nsplit,
-                                   hipStream_t st);
+                                   int tpw, hipStream_t st);
 
 // the launch's sequence holding row group grp / packed row r (relative to row0[0])
 __device__ __forceinline__ int seq_of_group(const PrefillSeqs& t, int grp) {
