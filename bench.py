@@ -223,21 +223,24 @@ def summarize_rocprof(kind: str, workload: str, paths, command: str) -> int:
     entry = db.setdefault(workload, {})
     if kind == "stats":
         # launches inside the timing passes: after a spin kernel, up to the next
-        # copy / fill (the next pass's cache flush) or spin kernel
+        # spin kernel or the next pass's cache flush (copies of 50 us and more;
+        # the small copies inside a step do not end a pass)
         passes = {}
         trace = sorted(csv.DictReader(open(paths[1])), key=lambda r: int(r["Start_Timestamp"]))
         inside = False
         for r in trace:
             name = r["Kernel_Name"]
+            us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
             if "sleep" in name or "spin" in name:
                 inside = True
                 continue
-            if name.startswith("__amd_rocclr") or "elementwise_kernel" in name:
-                inside = False
-                continue
             fam = _rocprof_name_family(name)
-            if inside and fam is not None:
-                passes.setdefault(fam, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            if fam is None:
+                if us >= 50.0 and not name.startswith("void infv2") and not name.startswith("infv2"):
+                    inside = False
+                continue
+            if inside:
+                passes.setdefault(fam, []).append(us)
         seen = set()
         for row in csv.DictReader(open(paths[0])):
             fam = _rocprof_name_family(row["Name"])
@@ -245,16 +248,20 @@ def summarize_rocprof(kind: str, workload: str, paths, command: str) -> int:
                 continue
             calls = int(row["Calls"])
             avg_us = float(row["AverageNs"]) / 1e3
+            kname = row["Name"].split("(")[0]
+            lo, hi = float(row["MinNs"]) / 1e3, float(row["MaxNs"]) / 1e3
             if fam in seen:
                 # several instantiations of one family in this run: merge by call count
                 prev = entry[fam]
                 tot = prev["calls"] + calls
                 avg_us = (prev["avg_us_all"] * prev["calls"] + avg_us * calls) / tot
                 calls = tot
+                kname = prev["kernel"] + "; " + kname
+                lo, hi = min(lo, prev["min_us"]), max(hi, prev["max_us"])
             seen.add(fam)
             pv = passes.get(fam, [])
-            entry[fam] = {"kernel": row["Name"].split("(")[0], "calls": calls, "avg_us_all": avg_us,
-                          "min_us": float(row["MinNs"]) / 1e3, "max_us": float(row["MaxNs"]) / 1e3,
+            entry[fam] = {"kernel": kname, "calls": calls, "avg_us_all": avg_us,
+                          "min_us": lo, "max_us": hi,
                           "timing_pass_launches": len(pv),
                           "avg_us": float(np.mean(pv)) if pv else avg_us,
                           "command": command, "source_sha256": source_digest(fam)}
@@ -269,7 +276,7 @@ def summarize_rocprof(kind: str, workload: str, paths, command: str) -> int:
                     continue
                 v = float(row["Counter_Value"])
                 if row["Kernel_Name"].startswith("__amd_rocclr_copyBuffer"):
-                    copies.setdefault(row["Grid_Size"], []).append(v)
+                    copies[int(row["Dispatch_Id"])] = v
                     continue
                 fam = _rocprof_name_family(row["Kernel_Name"])
                 if fam is not None:
@@ -277,14 +284,15 @@ def summarize_rocprof(kind: str, workload: str, paths, command: str) -> int:
             per[counter] = (vals, copies)
         (fv, fcopies), (wv, wcopies) = per["FETCH_SIZE"], per["WRITE_SIZE"]
         # the calibration copies (--copy-calibration) are the copyBuffer launches
-        # whose WRITE_SIZE equals their size; FETCH_SIZE is read off the launches
-        # of the same grid in the other pass
+        # whose WRITE_SIZE equals their size; FETCH_SIZE is read off the same
+        # dispatches of the other pass (the program is deterministic)
         want = CALIBRATION_MIB * 1024.0
-        grid = [gsz for gsz, v in wcopies.items() if abs(np.median(v) / want - 1) < 0.01]
-        if not grid or grid[0] not in fcopies:
+        ids = [i for i, v in wcopies.items() if abs(v / want - 1) < 0.01 and i in fcopies]
+        if not ids:
             print(f"no {CALIBRATION_MIB} MiB calibration copy in the counter runs", file=sys.stderr)
             return 1
-        fcopy, wcopy = float(np.median(fcopies[grid[0]])), float(np.median(wcopies[grid[0]]))
+        fcopy = float(np.median([fcopies[i] for i in ids]))
+        wcopy = float(np.median([wcopies[i] for i in ids]))
         # the calibration copy moves the same number of bytes in and out; its
         # write counter is exact (checked against its size), the fetch counter is not
         for fam in sorted(set(fv) & set(wv)):
@@ -595,10 +603,39 @@ def decode_spot_parity(wl, dev, qs, outs, idx, run0, ck_dtype, torch, gh) -> str
 PREFILL_FAMILIES = ("compress", "select_prefill", "select_topk", "attn_prefill")
 
 
-def bench_prefill(args, torch, tbs, gh) -> dict:
+def prefill_spot_parity(wl, dev, gi, out, ck_dtype, rows, gh) -> str:
+    """Sampled rows of the prefill against the float64 oracle, with compressed
+    keys in ck_dtype (bf16: the oracle rounds the exact mean once too)."""
+    from oracle import infv2_ref as ref
+    from tests.parity import accept_selection, assert_close
+    prm = ref.Params(head_dim=wl.head_dim, num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
+                     block_size=wl.block_size, kernel_size=wl.kernel_size,
+                     kernel_stride=wl.kernel_stride, topk=wl.topk, init_blocks=wl.init_blocks,
+                     local_blocks=wl.local_blocks, ck_dtype=ck_dtype)
+    K, V = wl.k_f64(0), wl.v_f64(0)
+    ck = dev.ck_host()[0]
+    if not np.array_equal(ck, ref.compress_keys(K, wl.kernel_size, wl.kernel_stride, ck_dtype)):
+        raise AssertionError("bench parity: compressed keys differ from the oracle's")
+    q = wl.decoded(wl.q[rows])                       # the sampled rows only, float64
+    go = gh.from_device(out[rows], wl.io_dtype)
+    verdicts = []
+    for x, i in enumerate(rows):
+        for g in range(wl.num_kv_heads):
+            rs = ref.select_row(q[x, 16 * g:16 * g + 16], ck[g], i, prm)
+            verdicts.append(accept_selection(gi[i, g].astype(np.int64), rs))
+    want = ref.attend_with_selection(q, K, V, list(rows), gi[rows].astype(np.int64), prm)
+    assert_close(go, want, wl.io_dtype, "bench prefill spot check")
+    bad = [v for v in verdicts if v.startswith("fail")]
+    if bad:
+        raise AssertionError(f"bench parity: {bad[0]}")
+    return f"ok: {len(rows)} rows x {wl.num_kv_heads} KV heads ({', '.join(sorted(set(verdicts)))})"
+
+
+def bench_prefill(args, torch, tbs, gh, ck_dtype=None) -> dict:
     from synth import make_config
     wl = make_config(3)
-    dev = gh.DeviceWorkload(wl, args.ck_dtype)
+    ck_dtype = ck_dtype or args.ck_dtype
+    dev = gh.DeviceWorkload(wl, ck_dtype)
     L, C = int(wl.lens[0]), wl.chunk
     cfg = dev.cfg
     log(f"config 3: {wl.name}, L={L}, chunk={C}")
@@ -672,7 +709,12 @@ def bench_prefill(args, torch, tbs, gh) -> dict:
     n_attn = kt["attn_prefill"]["launches_per_step"]
     res["tflops_attn_kernel"] = useful / (kt["attn_prefill"]["us_per_step"] * 1e-6) / 1e12
     res["roofline"] = roofline_of(kt, {"attn_prefill": useful / n_attn}, "mfma", BF16_PEAK_TFLOPS,
-                                  "TFLOP/s", 1e12, wl.name)
+                                  "TFLOP/s", 1e12, wl.name if ck_dtype == "fp32" else wl.name + "/ck_bf16")
+    res["ck_dtype"] = ck_dtype
+    # spot parity: the first and last rows of the last chunk and 6 random rows
+    rng = np.random.default_rng(3)
+    rows = sorted({L - C, L - 1} | set(int(x) for x in rng.integers(0, L, 6)))
+    res["parity"] = prefill_spot_parity(wl, dev, gi, out, ck_dtype, rows, gh)
     res["_idx"] = gi
     res["_wl"] = wl
     return res
@@ -1147,11 +1189,17 @@ def main() -> int:
         log(f"decode loop 128K (append + select + attend): {loop['ms_per_step_graph'] * 1e3:.1f} us/step")
     # the same decode workloads with bf16 compressed keys (the documented option)
     alt = {}
+    out_pre_bf16 = None
     if not args.no_ck_bf16 and args.ck_dtype == "fp32":
         alt["decode_128k_ck_bf16"] = bench_decode(2, args, torch, tbs, gh, replicas=args.replicas,
                                                   ck_dtype="bf16")
         if not args.no_batched:
             alt["batched_decode_16x_ck_bf16"] = bench_batched(args, torch, tbs, gh, ck_dtype="bf16")
+        if not args.no_prefill:
+            pb = bench_prefill(args, torch, tbs, gh, ck_dtype="bf16")
+            out_pre_bf16 = {k: v for k, v in pb.items() if not k.startswith("_")}
+            log(f"prefill 32K, bf16 compressed keys: select {pb['select_ms']:.2f} ms, attn "
+                f"{pb['attn_ms']:.2f} ms, total {pb['total_ms']:.2f} ms; {pb['parity']}")
         for k2, r2 in alt.items():
             log(f"{k2}: {r2['ms_per_step'] * 1e3:.1f} us/step")
 
@@ -1188,6 +1236,8 @@ def main() -> int:
     for k2, r2 in alt.items():
         out[k2] = {x: r2[x] for x in ("workload", "batch", "ms_per_step", "tok_per_s", "hbm_gbps_step",
                                       "per_call_us", "kernels", "bytes_per_step", "roofline", "parity")}
+    if out_pre_bf16:
+        out["prefill_32k_ck_bf16"] = out_pre_bf16
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline_decode(args.cpu_seconds)
