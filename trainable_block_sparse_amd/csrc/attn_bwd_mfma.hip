@@ -120,8 +120,7 @@ __global__ __launch_bounds__(kRThreads, 1) void bwd_row_mfma(
         dof[ks] = as_bf16x8(dv);
         dd += dot8_bf16(dv, ov);
     }
-    dd += __shfl_xor(dd, 16, 64);
-    dd += __shfl_xor(dd, 32, 64);              // D of head lc
+    dd = add_xor32(add_xor16(dd));              // D of head lc
     f32x4_t acc[8];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -186,8 +185,7 @@ __global__ __launch_bounds__(kRThreads, 1) void bwd_row_mfma(
         }
         lm *= scale_log2;
         if (__any(lm > mref + kSlackB)) {
-            float mx = fmaxf(lm, __shfl_xor(lm, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float mx = max_xor32(max_xor16(lm));
             const float mnew = fmaxf(mref, mx);
             const float alpha = (mref == -INFINITY) ? 0.f : fast_exp2(mref - mnew);
             lsum *= alpha;
@@ -250,8 +248,7 @@ __global__ __launch_bounds__(kRThreads, 1) void bwd_row_mfma(
     }
 
     // ---- epilogue: lane holds dQ^T[d = 16 mt + 4 lg + r][head lc]
-    float lt = lsum + __shfl_xor(lsum, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+    const float lt = add_xor32(add_xor16(lsum));
     if (row >= rows) return;
     const float inv = lt > 0.f ? scale / lt : 0.f;
     bf16_t* dst = dq + (static_cast<size_t>(row) * hq + static_cast<size_t>(g) * kGroup + lc) * kHeadDim + 4 * lg;

@@ -96,8 +96,7 @@ __device__ __forceinline__ void decode_run(DecSmem& sm, const bf16x8_t (&qf)[4],
                 s[r] = xv;
                 mx = fmaxf(mx, xv);
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            mx = max_xor32(max_xor16(mx));
             const float mnew = fmaxf(mrun, mx);      // finite: key 0 of the tile is below n
             const float alpha = (mrun == -INFINITY) ? 0.f : exp2f(mrun - mnew);
             float p[4], ls = 0.f;
@@ -106,8 +105,7 @@ __device__ __forceinline__ void decode_run(DecSmem& sm, const bf16x8_t (&qf)[4],
                 p[r] = (s[r] == -INFINITY) ? 0.f : exp2f(s[r] - mnew);
                 ls += p[r];
             }
-            ls += __shfl_xor(ls, 16, 64);
-            ls += __shfl_xor(ls, 32, 64);
+            ls = add_xor32(add_xor16(ls));
             lrun = lrun * alpha + ls;
             mrun = mnew;
             // P^T as the B operand: lane holds P[key 4 lg + j][head lc]

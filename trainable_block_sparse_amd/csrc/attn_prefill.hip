@@ -206,8 +206,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
             lm *= scale_log2;
             // raise the reference only when some head of the row overshoots it
             if (__any(lm > mref[i] + kRescaleSlack)) {
-                float mx = fmaxf(lm, __shfl_xor(lm, 16, 64));
-                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                const float mx = max_xor32(max_xor16(lm));
                 const float mnew = fmaxf(mref[i], mx);
                 const float alpha = (mref[i] == -INFINITY) ? 0.f : fast_exp2(mref[i] - mnew);
                 lsum[i] *= alpha;
@@ -283,8 +282,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
     // O[head lc][d = 16 mt + 4 lg + r]
 #pragma unroll
     for (int i = 0; i < kPRowsW; ++i) {
-        float lt = lsum[i] + __shfl_xor(lsum[i], 16, 64);
-        lt += __shfl_xor(lt, 32, 64);
+        const float lt = add_xor32(add_xor16(lsum[i]));
         const int row = r0 + kPWaves * i + w;
         if (row >= rows) continue;
         const float inv = lt > 0.f ? 1.f / lt : 0.f;

@@ -153,6 +153,28 @@ __device__ __forceinline__ float sum16(float v) {
     v += __uint_as_float(dpp_mov<kDppQuadSwap1>(0u, __float_as_uint(v)));
     return v;
 }
+// Across rows: lane l combined with lane l ^ 16 (l ^ 32) by one lane-swap
+// instruction of gfx950 (v_permlane16_swap: odd rows of the first operand trade
+// places with even rows of the second; v_permlane32_swap: the upper half of the
+// first with the lower half of the second).  With both operands v, each lane
+// ends up holding its own value in one result and its partner's in the other,
+// so a sum or max of the two is exactly own (op) partner, with no LDS permute.
+__device__ __forceinline__ float add_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 }  // namespace infv2
 

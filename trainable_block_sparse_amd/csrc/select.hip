@@ -29,6 +29,8 @@
 #include "kernels.hpp"
 #include "topk.hpp"
 
+#include <type_traits>
+
 namespace infv2 {
 
 constexpr float kLog2eF = 1.4426950408889634f;   // exp(x) = 2^(x log2 e) on the transcendental unit
@@ -411,8 +413,7 @@ __global__ __launch_bounds__(kLogWaves * 64) void sel_dec_logits_mfma(
             for (int r = 0; r < 4; ++r) if (jb + r < nvis) dst[r] = z[m2][r];
         }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = max_xor32(max_xor16(mx));
     float sm = 0.f;
     if (mx != -INFINITY) {
 #pragma unroll
@@ -420,8 +421,7 @@ __global__ __launch_bounds__(kLogWaves * 64) void sel_dec_logits_mfma(
 #pragma unroll
             for (int r = 0; r < 4; ++r) sm += fast_exp2((z[m2][r] - mx) * kLog2eF);   // exp(-inf) = 0
     }
-    sm += __shfl_xor(sm, 16, 64);
-    sm += __shfl_xor(sm, 32, 64);
+    sm = add_xor32(add_xor16(sm));
     // the waves' (max, sum) of each head combine into the chunk's partial
     if (lg == 0) xm[wv][lc] = make_float2(mx, sm);
     __syncthreads();
@@ -869,7 +869,10 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
     int32_t vis[kPreRW];              // kernels visible to the row (counts < 2^31)
     bf16x8_t qf[kPreRW][4];
     int64_t vmax = 0;                     // the group's last valid row sees the most kernels
+    int64_t vmin = 0;                     // and its first row the fewest
     {
+        const int64_t v0 = num_kernels(q_start + r0 + 1, p, s);
+        vmin = v0 < ccap ? v0 : ccap;
         const int last = (r0 + kPreRowsG - 1 < rows ? r0 + kPreRowsG - 1 : rows - 1);
         if (last >= r0) {
             const int64_t v = num_kernels(q_start + last + 1, p, s);
@@ -955,8 +958,11 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
     uint32_t* pend = nullptr;
     uint32_t pend_key = 0u;
     if (vmax > 0) issue(0, 0);
-    int stg = 0;
-    for (int64_t j0 = 0; j0 < vmax; j0 += kPreTileK, stg ^= 1) {
+    // one 64-kernel tile; kFull (full_tag): every kernel of the tile is visible
+    // to every row of the group (all tiles but the last few), so the visibility
+    // mask drops out of the column loop
+    auto tile = [&](const int64_t j0, const int stg, auto full_tag) {
+        constexpr bool kFull = decltype(full_tag)::value;
         // tile j0 landed (with the previous tile's deferred updates, both issued
         // a tile ago) and every wave is done with the previous tile, whose stage
         // now takes the next one
@@ -998,62 +1004,62 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
                 if (!kCkBf16) fl[buf][ks] = *reinterpret_cast<const uint4*>(&ck_lo[stg][off]);
             }
         };
+        // the 16-kernel column tiles of this tile
+        {
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            const int cur = 0;
-            frags(nt, cur);
-            f32x4_t z[kPreRW];
+            for (int nt = 0; nt < 4; ++nt) {
+                const int cur = 0;
+                frags(nt, cur);
+                f32x4_t z[kPreRW];
 #pragma unroll
-            for (int i = 0; i < kPreRW; ++i) z[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                for (int i = 0; i < kPreRW; ++i) z[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+                for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-                for (int i = 0; i < kPreRW; ++i) z[i] = mfma32(qf[i][ks], as_bf16x8(fh[cur][ks]), z[i]);
-                if (!kCkBf16) {
+                    for (int i = 0; i < kPreRW; ++i) z[i] = mfma32(qf[i][ks], as_bf16x8(fh[cur][ks]), z[i]);
+                    if (!kCkBf16) {
 #pragma unroll
-                    for (int i = 0; i < kPreRW; ++i) z[i] = mfma32(qf[i][ks], as_bf16x8(fl[cur][ks]), z[i]);
-                }
-            }
-            const int kr = 16 * nt + lc;
-            const int32_t jk = static_cast<int32_t>(j0) + kr;   // this lane's kernel column
-#pragma unroll
-            for (int i = 0; i < kPreRW; ++i) {
-                const bool ok = jk < vis[i];
-                if (kPass == 1) {
-                    // running (max, sum) with a lazy max: the reference of a head
-                    // (shared by its 16 kernel-column lanes) moves only when some
-                    // logit exceeds it by more than 2^8, so the common path is one
-                    // FMA, one exp and one add per logit and no divergence.
-                    // d = logit - reference; masked logits are -inf
-                    float d[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        d[r] = ok ? fmaf(z[i][r], zscale, -mr[i][r]) : -INFINITY;
-                    if (__builtin_amdgcn_ballot_w64(d[0] > 8.f || d[1] > 8.f || d[2] > 8.f || d[3] > 8.f) != 0) {
-                        // raise the references to the max over the head's 16 columns
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const float x = ok ? z[i][r] * zscale : -INFINITY;
-                            float cm = x;
-#pragma unroll
-                            for (int o = 1; o < 16; o <<= 1) cm = fmaxf(cm, __shfl_xor(cm, o, 64));
-                            const float mn = fmaxf(mr[i][r], cm);
-                            lr[i][r] = lr[i][r] * fast_exp2(mr[i][r] - mn);   // finite reference: no NaN
-                            mr[i][r] = mn;
-                            d[r] = x - mn;
-                        }
+                        for (int i = 0; i < kPreRW; ++i) z[i] = mfma32(qf[i][ks], as_bf16x8(fl[cur][ks]), z[i]);
                     }
-                    // the reference is finite (kPreMrInit at first), so masked logits
-                    // (-inf) give 2^-inf = 0 without a test
+                }
+                const int kr = 16 * nt + lc;
+                const int32_t jk = static_cast<int32_t>(j0) + kr;   // this lane's kernel column
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) lr[i][r] += fast_exp2(d[r]);
-                } else {
-                    float acc = 0.f;
+                for (int i = 0; i < kPreRW; ++i) {
+                    const bool ok = kFull || jk < vis[i];
+                    if (kPass == 1) {
+                        // running (max, sum) with a lazy max: the reference of a head
+                        // (shared by its 16 kernel-column lanes) moves only when some
+                        // logit exceeds it by more than 2^8, so the common path is one
+                        // FMA, one exp and one add per logit and no divergence.
+                        // d = logit - reference; masked logits are -inf
+                        float d[4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc += fast_exp2(z[i][r] * zscale - mr[i][r]);
-                    acc += __shfl_xor(acc, 16, 64);
-                    acc += __shfl_xor(acc, 32, 64);
-                    if (lg == 0) rs[w + kPreWaves * i][kr] = ok ? acc * (1.0f / kGroup) : -INFINITY;
+                        for (int r = 0; r < 4; ++r)
+                            d[r] = ok ? fmaf(z[i][r], zscale, -mr[i][r]) : -INFINITY;
+                        if (__builtin_amdgcn_ballot_w64(d[0] > 8.f || d[1] > 8.f || d[2] > 8.f || d[3] > 8.f) != 0) {
+                            // raise the references to the max over the head's 16 columns
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const float x = ok ? z[i][r] * zscale : -INFINITY;
+                                const float cm = max16(x);
+                                const float mn = fmaxf(mr[i][r], cm);
+                                lr[i][r] = lr[i][r] * fast_exp2(mr[i][r] - mn);   // finite reference: no NaN
+                                mr[i][r] = mn;
+                                d[r] = x - mn;
+                            }
+                        }
+                        // the reference is finite (kPreMrInit at first), so masked logits
+                        // (-inf) give 2^-inf = 0 without a test
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) lr[i][r] += fast_exp2(d[r]);
+                    } else {
+                        float acc = 0.f;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc += fast_exp2(z[i][r] * zscale - mr[i][r]);
+                        acc = add_xor32(add_xor16(acc));
+                        if (lg == 0) rs[w + kPreWaves * i][kr] = ok ? acc * (1.0f / kGroup) : -INFINITY;
+                    }
                 }
             }
         }
@@ -1088,7 +1094,11 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
                 if (b0 + kPreThreads <= bhi) __syncthreads();   // ranges read before they are replaced
             }
         }
-    }
+    };
+    int64_t j0 = 0;
+    int stg = 0;
+    for (; j0 + kPreTileK <= vmin; j0 += kPreTileK, stg ^= 1) tile(j0, stg, std::true_type{});
+    for (; j0 < vmax; j0 += kPreTileK, stg ^= 1) tile(j0, stg, std::false_type{});
     if (kPass == 2 && pend) atomicMax(pend, pend_key);
     if (kPass == 1) {
         // fold the 16 kernel columns: lanes with equal lg hold the same heads
