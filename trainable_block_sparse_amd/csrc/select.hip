@@ -797,14 +797,16 @@ constexpr int kPreThreads = kPreWaves * 64;
 constexpr int kPreLoads = kPreTileK * 16 / kPreThreads;   // 16-byte loads per thread, tile and part
 constexpr float kPreMrInit = -1e30f;                  // pass 1 reference before any visible logit
 
-// fp32 compressed keys -> the bf16 pair the scoring products use: hi = x rounded
-// to bf16, lo = (x - hi) rounded to bf16, so that hi . q + lo . q carries x to
-// about 16 significant bits.  Written once per call as [part][KV head][ld][d]
+// fp32 compressed keys -> the bf16 pair the scoring products use, for x = the
+// key times zs = score_scale log2 e (one fp32 rounding): hi = x rounded to
+// bf16, lo = (x - hi) rounded to bf16, so that hi . q + lo . q carries x to
+// about 16 significant bits and the products give the logit in log2 units.  Written once per call as [part][KV head][ld][d]
 // (part 0 hi, 1 lo) for kernels 0 .. nk - 1 (those the call's rows see), instead
 // of by every thread block that stages a tile.  Thread -> one 8-value chunk.
 __global__ __launch_bounds__(256) void ck_split_hilo(const PrefillSeqs seqs, const float* __restrict__ ck,
                                                      const int64_t* __restrict__ ck_off_all, int hkv,
-                                                     int p, int s, int64_t ld, bf16_t* __restrict__ hl_all) {
+                                                     int p, int s, int64_t ld, float zs,
+                                                     bf16_t* __restrict__ hl_all) {
     const int g = blockIdx.y, si = blockIdx.z;
     const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     const int64_t* ck_off = ck_off_all + seqs.seq[si];
@@ -817,7 +819,7 @@ __global__ __launch_bounds__(256) void ck_split_hilo(const PrefillSeqs seqs, con
     const float* src = ck + (ck_off[0] * hkv + static_cast<int64_t>(g) * ccap + r) * kHeadDim + 8 * c;
     const float4 a = *reinterpret_cast<const float4*>(src);
     const float4 b = *reinterpret_cast<const float4*>(src + 4);
-    const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    const float x[8] = {a.x * zs, a.y * zs, a.z * zs, a.w * zs, b.x * zs, b.y * zs, b.z * zs, b.w * zs};
     float hi[8], lo[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -903,12 +905,17 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
             for (int64_t jb = t; jb < nblk_max; jb += kPreThreads) kb[jb] = 0u;
         }
     }
-    // pass 1 state: running (max, sum) for heads 4 lg + r; pass 2: LSE2 of those heads
-    float mr[kPreRW][4], lr[kPreRW][4];
+    // pass 1 state: running (max, sum) for heads 4 lg + r; pass 2: LSE2 of those
+    // heads.  The reference is held negated, nm = -reference, as the 4-vector
+    // that seeds a column tile's products: with fp32 keys (stored pre-scaled by
+    // score_scale log2 e) the products then end at the exponent itself.
+    f32x4_t nm[kPreRW];
+    float lr[kPreRW][4];
 #pragma unroll
-    for (int i = 0; i < kPreRW; ++i)
+    for (int i = 0; i < kPreRW; ++i) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) { mr[i][r] = kPreMrInit; lr[i][r] = 0.f; }
+        for (int r = 0; r < 4; ++r) { nm[i][r] = -kPreMrInit; lr[i][r] = 0.f; }
+    }
     if (kPass == 2) {
 #pragma unroll
         for (int i = 0; i < kPreRW; ++i) {
@@ -916,7 +923,7 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
             const int rr = row < rows ? row : rows - 1;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                mr[i][r] = lse[static_cast<size_t>(rr) * hq + g * kGroup + 4 * lg + r] * kLog2e;
+                nm[i][r] = -(lse[static_cast<size_t>(rr) * hq + g * kGroup + 4 * lg + r] * kLog2e);
         }
     }
 
@@ -949,8 +956,7 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
     for (int i = 0; i < kPreRW; ++i) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) asm volatile("" :: "v"(qf[i][ks]));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) asm volatile("" :: "v"(mr[i][r]));
+        asm volatile("" :: "v"(nm[i]));
     }
     // pass 2: a tile's block-max update (at most one per thread with the usual
     // sizes) is issued after the next tile's loads, so that the wait for those
@@ -961,8 +967,10 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
     // one 64-kernel tile; kFull (full_tag): every kernel of the tile is visible
     // to every row of the group (all tiles but the last few), so the visibility
     // mask drops out of the column loop
-    auto tile = [&](const int64_t j0, const int stg, auto full_tag) {
+    // kFirst (pass 1, tile 0, masked): the products start from zero
+    auto tile = [&](const int64_t j0, const int stg, auto full_tag, auto first_tag) {
         constexpr bool kFull = decltype(full_tag)::value;
+        constexpr bool kFirst = decltype(first_tag)::value;
         // tile j0 landed (with the previous tile's deferred updates, both issued
         // a tile ago) and every wave is done with the previous tile, whose stage
         // now takes the next one
@@ -1010,9 +1018,12 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
             for (int nt = 0; nt < 4; ++nt) {
                 const int cur = 0;
                 frags(nt, cur);
+                // bf16 keys: raw logits; fp32 keys: the scaled logits minus the
+                // reference (the products start from nm), except in pass 1's first
+                // tile, whose reference is still the -1e30 placeholder
                 f32x4_t z[kPreRW];
 #pragma unroll
-                for (int i = 0; i < kPreRW; ++i) z[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                for (int i = 0; i < kPreRW; ++i) z[i] = (kCkBf16 || kFirst) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : nm[i];
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -1036,16 +1047,21 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
                         float d[4];
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
-                            d[r] = ok ? fmaf(z[i][r], zscale, -mr[i][r]) : -INFINITY;
+                            d[r] = !ok ? -INFINITY : kCkBf16 ? fmaf(z[i][r], zscale, nm[i][r])
+                                                       : kFirst ? z[i][r] + nm[i][r] : z[i][r];
                         if (__builtin_amdgcn_ballot_w64(d[0] > 8.f || d[1] > 8.f || d[2] > 8.f || d[3] > 8.f) != 0) {
                             // raise the references to the max over the head's 16 columns
+                            // (x: the scaled logit; fp32 keys after the first tile:
+                            // the products minus the old reference's seed)
 #pragma unroll
                             for (int r = 0; r < 4; ++r) {
-                                const float x = ok ? z[i][r] * zscale : -INFINITY;
+                                const float x = !ok ? -INFINITY : kCkBf16 ? z[i][r] * zscale
+                                                                : kFirst ? z[i][r] : z[i][r] - nm[i][r];
                                 const float cm = max16(x);
-                                const float mn = fmaxf(mr[i][r], cm);
-                                lr[i][r] = lr[i][r] * fast_exp2(mr[i][r] - mn);   // finite reference: no NaN
-                                mr[i][r] = mn;
+                                const float mo = -nm[i][r];
+                                const float mn = fmaxf(mo, cm);
+                                lr[i][r] = lr[i][r] * fast_exp2(mo - mn);   // finite reference: no NaN
+                                nm[i][r] = -mn;
                                 d[r] = x - mn;
                             }
                         }
@@ -1056,7 +1072,7 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
                     } else {
                         float acc = 0.f;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) acc += fast_exp2(z[i][r] * zscale - mr[i][r]);
+                        for (int r = 0; r < 4; ++r) acc += fast_exp2(kCkBf16 ? fmaf(z[i][r], zscale, nm[i][r]) : z[i][r]);
                         acc = add_xor32(add_xor16(acc));
                         if (lg == 0) rs[w + kPreWaves * i][kr] = ok ? acc * (1.0f / kGroup) : -INFINITY;
                     }
@@ -1097,8 +1113,13 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
     };
     int64_t j0 = 0;
     int stg = 0;
-    for (; j0 + kPreTileK <= vmin; j0 += kPreTileK, stg ^= 1) tile(j0, stg, std::true_type{});
-    for (; j0 < vmax; j0 += kPreTileK, stg ^= 1) tile(j0, stg, std::false_type{});
+    if (kPass == 1 && vmax > 0) {
+        tile(j0, stg, std::false_type{}, std::true_type{});
+        j0 += kPreTileK;
+        stg ^= 1;
+    }
+    for (; j0 + kPreTileK <= vmin; j0 += kPreTileK, stg ^= 1) tile(j0, stg, std::true_type{}, std::false_type{});
+    for (; j0 < vmax; j0 += kPreTileK, stg ^= 1) tile(j0, stg, std::false_type{}, std::false_type{});
     if (kPass == 2 && pend) atomicMax(pend, pend_key);
     if (kPass == 1) {
         // fold the 16 kernel columns: lanes with equal lg hold the same heads
@@ -1107,10 +1128,11 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
             const int row = r0 + w + kPreWaves * i;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                float mx = mr[i][r];
+                const float mo = -nm[i][r];
+                float mx = mo;
 #pragma unroll
                 for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-                float sm = lr[i][r] * fast_exp2(mr[i][r] - mx);   // lanes still at kPreMrInit hold 0
+                float sm = lr[i][r] * fast_exp2(mo - mx);   // lanes still at kPreMrInit hold 0
 #pragma unroll
                 for (int o = 1; o < 16; o <<= 1) sm += __shfl_xor(sm, o, 64);
                 if (lc == 0 && row < rows)
@@ -1327,7 +1349,8 @@ static void split_hilo(const Shape& sh, const PrefillSeqs& seqs, const void* ck,
     if (ld <= 0) return;
     const dim3 grid(static_cast<unsigned>((ld * 16 + 255) / 256), sh.hkv, seqs.n);
     launch_timed(INFV2_KERNEL_SELECT_PREFILL, ck_split_hilo, grid, dim3(256), 0, st, seqs,
-                 static_cast<const float*>(ck), ck_off, sh.hkv, p, s, ld, hl);
+                 static_cast<const float*>(ck), ck_off, sh.hkv, p, s, ld,
+                 sh.score_scale * 1.4426950408889634f, hl);
 }
 
 // rows [r0, r0 + nr) of a one-sequence launch whose first row sits at q_start
