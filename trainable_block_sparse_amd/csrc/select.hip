@@ -968,7 +968,11 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
     // to every row of the group (all tiles but the last few), so the visibility
     // mask drops out of the column loop
     // kFirst (pass 1, tile 0, masked): the products start from zero
-    auto tile = [&](const int64_t j0, const int stg, auto full_tag, auto first_tag) {
+    // Pass 2 passes the stage as a compile-time constant, so that its LDS
+    // fragment addresses are lane offsets plus immediates (in pass 1 the second
+    // copy of the tile code costs more registers than it saves instructions).
+    auto tile = [&](const int64_t j0, auto stg_v, auto full_tag, auto first_tag) {
+        const int stg = static_cast<int>(stg_v);
         constexpr bool kFull = decltype(full_tag)::value;
         constexpr bool kFirst = decltype(first_tag)::value;
         // tile j0 landed (with the previous tile's deferred updates, both issued
@@ -1112,14 +1116,24 @@ __global__ __launch_bounds__(kPreThreads, 4) void sel_pre_mfma(
         }
     };
     int64_t j0 = 0;
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
     int stg = 0;
     if (kPass == 1 && vmax > 0) {
-        tile(j0, stg, std::false_type{}, std::true_type{});
+        tile(j0, S0{}, std::false_type{}, std::true_type{});
         j0 += kPreTileK;
-        stg ^= 1;
+        stg = 1;
     }
-    for (; j0 + kPreTileK <= vmin; j0 += kPreTileK, stg ^= 1) tile(j0, stg, std::true_type{}, std::false_type{});
-    for (; j0 < vmax; j0 += kPreTileK, stg ^= 1) tile(j0, stg, std::false_type{}, std::false_type{});
+    for (; j0 + kPreTileK <= vmin; j0 += kPreTileK, stg ^= 1) {
+        if (kPass == 1) tile(j0, stg, std::true_type{}, std::false_type{});
+        else if (stg) tile(j0, S1{}, std::true_type{}, std::false_type{});
+        else tile(j0, S0{}, std::true_type{}, std::false_type{});
+    }
+    for (; j0 < vmax; j0 += kPreTileK, stg ^= 1) {
+        if (kPass == 1) tile(j0, stg, std::false_type{}, std::false_type{});
+        else if (stg) tile(j0, S1{}, std::false_type{}, std::false_type{});
+        else tile(j0, S0{}, std::false_type{}, std::false_type{});
+    }
     if (kPass == 2 && pend) atomicMax(pend, pend_key);
     if (kPass == 1) {
         // fold the 16 kernel columns: lanes with equal lg hold the same heads
