@@ -34,7 +34,7 @@ namespace infv2 {
 constexpr int kPRows = 16;       // query rows per thread block
 constexpr int kPWaves = 16;      // one query row per wave, four waves per SIMD
 constexpr int kPRowsW = 16 / kPWaves;                // query rows per wave
-constexpr int kKBatch = 1;       // K-steps whose fragments are read from LDS at once
+constexpr int kKBatch = 2;       // K-steps whose fragments are read from LDS at once
 constexpr int kVBatch = 2;       // V^T d-tiles whose fragments are read from LDS at once
 constexpr int kTileLoads = 16 / kPWaves;             // 1 KB global->LDS loads per wave per tile
 constexpr int kPThreads = kPWaves * 64;
