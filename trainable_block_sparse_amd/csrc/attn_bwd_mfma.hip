@@ -25,8 +25,8 @@
 //   dV^T += dO^T . P,  dK^T += Q^T . dA 16 MFMA
 // The Q^T and dO^T operands (heads along the contraction) come from the same
 // LDS tiles through transpose reads (ds_read_b64_tr_b16).  The pairs' Q, dO,
-// lse and D go through a four-slot LDS ring with direct global->LDS loads,
-// three pairs in flight.
+// lse and D go through a three-slot LDS ring with direct global->LDS loads,
+// two pairs in flight (three thread blocks per CU).
 // A block whose list is longer than kSeg rows is split into segments whose
 // fp32 partials are summed in segment order by bwd_col_finish, so results do
 // not depend on scheduling.
@@ -40,7 +40,7 @@ constexpr int kRWaves = kUWaves;       // row pass: one row per wave
 constexpr int kRThreads = kUThreads;
 constexpr int kCThreads = 256;         // column pass: 4 waves x 16 keys
 constexpr int kRSlots = 4;             // row pass: two LDS stages of two blocks (32 KB each)
-constexpr int kSeg = 2048;             // rows per column segment
+constexpr int kSeg = 512;              // rows per column segment
 constexpr int kXcdsB = 8;
 constexpr float kSlackB = 8.f;         // log2 units, as in the forward
 
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(1024) void bwd_items_kernel(const int32_t* __restri
 }
 
 typedef bf16_t RowTiles[4][kGroup * kHeadDim];   // Q_A, Q_B, dO_A, dO_B (4 KB each)
-constexpr int kCStages = 4;                       // LDS ring of the column pass: 3 pairs in flight
+constexpr int kCStages = 3;                       // LDS ring of the column pass: 2 pairs in flight
 constexpr int kCLoads = 5;                        // global->LDS loads per wave and pair
 
 // Direct global->LDS load of 4 B per lane (lane i writes bytes 4 i .. 4 i + 3
@@ -310,13 +310,12 @@ __device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
 // further pairs' loads outstanding; loads complete in order), then a barrier
 // makes every wave's share visible and frees the slot read one pair earlier
 __device__ __forceinline__ void ring_wait(int later) {
-    static_assert(kCStages == 4 && kCLoads == 5, "vmcnt immediates below");
-    if (later >= 2) asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
-    else if (later == 1) asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" ::: "memory");
+    static_assert(kCStages == 3 && kCLoads == 5, "vmcnt immediates below");
+    if (later >= 1) asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
+__global__ __launch_bounds__(kCThreads, 3) void bwd_col_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout, int rows, int64_t q_start,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const int64_t* __restrict__ kv_off,
     const int32_t* __restrict__ col_start, const int32_t* __restrict__ list, int64_t list_ld,
@@ -373,9 +372,11 @@ __global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
     __syncthreads();                         // row ids in LDS
 
     // stage slot t of each tile: head h = t / 16 holds chunk (t % 16) ^ h there
+    // (row bases are wave-uniform: SGPR addresses with a fixed lane offset)
     const int sh_h = t >> 4, sh_c = (t & 15) ^ (t >> 4);
-    auto tile_src = [&](const bf16_t* base, int r) {
-        return base + (static_cast<size_t>(r) * hq + static_cast<size_t>(g) * kGroup + sh_h) * kHeadDim + 8 * sh_c;
+    const uint32_t tile_off = static_cast<uint32_t>(((g * kGroup + sh_h) * kHeadDim + 8 * sh_c) * 2);
+    auto row_base = [&](const bf16_t* base, int r) {
+        return base + static_cast<size_t>(r) * hq * kHeadDim;
     };
     // lse / D slot of this wave: lane l loads quantity l / 16 (lse A, lse B, D A,
     // D B) of head l % 16
@@ -386,12 +387,12 @@ __global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
     // them against the reads.
     auto issue = [&](int p) {
         const int s = p % kCStages;
-        const int ra = seg_rows[2 * p];
-        const int rb = (2 * p + 1 < n) ? seg_rows[2 * p + 1] : ra;
-        dma16(tile_src(q, ra), lds_offset(&ring[s][0][w * 512]));
-        dma16(tile_src(q, rb), lds_offset(&ring[s][1][w * 512]));
-        dma16(tile_src(dout, ra), lds_offset(&ring[s][2][w * 512]));
-        dma16(tile_src(dout, rb), lds_offset(&ring[s][3][w * 512]));
+        const int ra = __builtin_amdgcn_readfirstlane(seg_rows[2 * p]);
+        const int rb = __builtin_amdgcn_readfirstlane((2 * p + 1 < n) ? seg_rows[2 * p + 1] : ra);
+        dma16s(row_base(q, ra), tile_off, lds_offset(&ring[s][0][w * 512]));
+        dma16s(row_base(q, rb), tile_off, lds_offset(&ring[s][1][w * 512]));
+        dma16s(row_base(dout, ra), tile_off, lds_offset(&ring[s][2][w * 512]));
+        dma16s(row_base(dout, rb), tile_off, lds_offset(&ring[s][3][w * 512]));
         dma4(ld_src + static_cast<size_t>(ld_b ? rb : ra) * hq, lds_offset(&lsd[s][w][0]));
     };
     // Transposed operands (d along M, (row, head) along K) come straight from
@@ -404,14 +405,6 @@ __global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
     auto compute = [&](int p) {
         const int sl = p % kCStages;
         const RowTiles& rt = ring[sl];
-        // A fragments of tile x (Q_A, Q_B, dO_A, dO_B), K-step ks: lane holds
-        // X[head lc][d = 32 ks + 8 lg ..] (chunks XOR-swizzled by head)
-        bf16x8_t fr[4][4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                fr[x][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&rt[x][lc * kHeadDim + 8 * ((4 * ks + lg) ^ lc)]));
         const int ra = seg_rows[2 * p], rb = seg_rows[2 * p + 1];
         const bool has_b = 2 * p + 1 < n;
         // lse of rows A, B and D of rows A, B, heads 4 lg .. 4 lg + 3
@@ -422,12 +415,19 @@ __global__ __launch_bounds__(kCThreads, 2) void bwd_col_mfma(
         f32x4_t s[2], dp[2];
 #pragma unroll
         for (int x = 0; x < 2; ++x) { s[x] = f32x4_t{0.f, 0.f, 0.f, 0.f}; dp[x] = s[x]; }
+        // A fragments of tile x (Q_A, Q_B, dO_A, dO_B), one K-step at a time
+        // (three waves per SIMD need the registers): lane holds
+        // X[head lc][d = 32 ks + 8 lg ..] (chunks XOR-swizzled by head)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
+            bf16x8_t fr[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                fr[x] = as_bf16x8(*reinterpret_cast<const uint4*>(&rt[x][lc * kHeadDim + 8 * ((4 * ks + lg) ^ lc)]));
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
-                s[x] = mfma32(fr[x][ks], kf[ks], s[x]);
-                dp[x] = mfma32(fr[2 + x][ks], vf[ks], dp[x]);
+                s[x] = mfma32(fr[x], kf[ks], s[x]);
+                dp[x] = mfma32(fr[2 + x], vf[ks], dp[x]);
             }
         }
         // lane holds S[head 4 lg + r][key 16 w + lc] of rows A (x = 0) and B (x = 1)

@@ -230,6 +230,12 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
     asm volatile("global_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
                  : "memory");
 }
+// The same with a wave-uniform base address (held in SGPRs) and a 32-bit byte
+// offset per lane: no 64-bit address arithmetic or registers per load.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t byte_off, uint32_t lds) {
+    asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(byte_off), "s"(base),
+                 "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
 // wait for every outstanding global access of this wave, then a block barrier
 __device__ __forceinline__ void dma_wait_barrier() {
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
