@@ -39,7 +39,8 @@ constexpr int kChunkA = 64;      // kernels per block in sel_dec_logits
 constexpr int kLogitsNtMaxBlocks = 1024;   // nontemporal key loads up to this many logits blocks
 constexpr int kLogWaves = 2;     // waves per 64-kernel chunk in sel_dec_logits_mfma (4 was no faster)
 constexpr int kLogTiles = 4 / kLogWaves;   // 16-kernel tiles per wave
-constexpr int kChunkB = 256;     // kernels per block in sel_dec_scores
+constexpr int kChunkB = 256;     // kernels per block in sel_dec_scores (512 in large grids)
+constexpr int kScoresTwoMinBlocks = 512;   // grids above this take 512-kernel blocks
 constexpr int kRowsPre = 4;      // query rows per block in the prefill passes
 constexpr int kTilePre = 64;     // kernels per LDS tile in the prefill passes
 
@@ -489,7 +490,10 @@ __device__ __forceinline__ float fold_partials(const float2* __restrict__ pp, in
 }
 
 // lse_in: a per-(sequence, KV head, head) normaliser to use instead of the one
-// folded from `partial` (the coarse-kernel approximation), or NULL
+// folded from `partial` (the coarse-kernel approximation), or NULL.
+// kJ kernels per thread: 256 kJ kernels per block (kJ = 2 for large grids:
+// half the blocks, so half the re-reads of the partials).
+template <int kJ>
 __global__ __launch_bounds__(256) void sel_dec_scores(
     const int64_t* __restrict__ kv_off, const int64_t* __restrict__ lens, int lens_end,
     const int64_t* __restrict__ ck_off, int hkv, int m, int p, int s, int64_t nc_max,
@@ -497,23 +501,25 @@ __global__ __launch_bounds__(256) void sel_dec_scores(
     const float2* __restrict__ partial, const float* __restrict__ lse_in,
     uint32_t* __restrict__ keys) {
     __shared__ float ls[kGroup];
-    __shared__ float rs[kChunkB];
+    constexpr int kCh = 256 * kJ;                 // kernels per block
+    __shared__ float rs[kCh];
     const int b = blockIdx.z, g = blockIdx.y, ch = blockIdx.x, t = threadIdx.x;
     const int64_t o0 = kv_off[b], o1 = kv_off[b + 1], lv = lens[b];
     const int64_t c0 = ck_off[b], c1 = ck_off[b + 1];
     const size_t bg = static_cast<size_t>(b) * hkv + g;
     uint32_t* kb = keys + bg * kld;
-    const int64_t j0 = static_cast<int64_t>(ch) * kChunkB;
-    const int64_t j = j0 + t;
+    const int64_t j0 = static_cast<int64_t>(ch) * kCh;
 
     // this thread's 16 logits and the (max, sum-exp) partials are independent
     // loads: issue them together (one memory round trip)
-    float zz[kGroup];
-    {
+    float zz[kJ][kGroup];
+#pragma unroll
+    for (int x = 0; x < kJ; ++x) {
         // clamped to the row, not to nvis: the address does not wait for the length
+        const int64_t j = j0 + t + 256 * x;
         const float* z = logits + bg * kGroup * nc_ld + (j < nc_ld ? j : nc_ld - 1);
 #pragma unroll
-        for (int h = 0; h < kGroup; ++h) zz[h] = z[h * nc_ld];
+        for (int h = 0; h < kGroup; ++h) zz[x][h] = z[h * nc_ld];
     }
     // per-head LogSumExp from the partials of pass 1 (16 threads per head)
     if (lse_in) {
@@ -528,16 +534,20 @@ __global__ __launch_bounds__(256) void sel_dec_scores(
     nvis = nvis < ccap ? nvis : ccap;
     nvis = nvis < nc_max ? nvis : nc_max;
     __syncthreads();
-    float R = -INFINITY;
-    if (j < nvis) {
-        float acc = 0.f;
 #pragma unroll
-        for (int h = 0; h < kGroup; ++h) acc += fast_exp2((zz[h] - ls[h]) * kLog2eF);
-        R = acc * (1.0f / kGroup);
+    for (int x = 0; x < kJ; ++x) {
+        const int64_t j = j0 + t + 256 * x;
+        float R = -INFINITY;
+        if (j < nvis) {
+            float acc = 0.f;
+#pragma unroll
+            for (int h = 0; h < kGroup; ++h) acc += fast_exp2((zz[x][h] - ls[h]) * kLog2eF);
+            R = acc * (1.0f / kGroup);
+        }
+        rs[t + 256 * x] = R;
     }
-    rs[t] = R;
     __syncthreads();
-    const int64_t jhi = (j0 + kChunkB < nvis ? j0 + kChunkB : nvis) - 1;
+    const int64_t jhi = (j0 + kCh < nvis ? j0 + kCh : nvis) - 1;
     if (j0 <= jhi) {
         const int64_t blo = (j0 * s) / m, bhi = (jhi * s + p - 1) / m;
         for (int64_t blk = blo + t; blk <= bhi; blk += 256) {
@@ -1323,9 +1333,17 @@ static void dec_launch(const Shape& sh, const void* q, const void* ck, const int
             lse_c);
     }
     {
-        launch_timed(INFV2_KERNEL_SELECT_SCORES, sel_dec_scores, gb, dim3(256), 0, st, kv_off,
-                     lens, lens_end, ck_off, sh.hkv, sh.m, sh.p, sh.s, ncm, w.nc_ld, w.nchunk_a,
-                     w.keys_ld, logits, partial, lse_c, keys);
+        // large grids: 512 kernels per block
+        const bool two = static_cast<int64_t>(gb.x) * gb.y * gb.z > kScoresTwoMinBlocks;
+        const dim3 gs(two ? (gb.x + 1) / 2 : gb.x, sh.hkv, batch);
+        if (two)
+            launch_timed(INFV2_KERNEL_SELECT_SCORES, sel_dec_scores<2>, gs, dim3(256), 0, st, kv_off,
+                         lens, lens_end, ck_off, sh.hkv, sh.m, sh.p, sh.s, ncm, w.nc_ld, w.nchunk_a,
+                         w.keys_ld, logits, partial, lse_c, keys);
+        else
+            launch_timed(INFV2_KERNEL_SELECT_SCORES, sel_dec_scores<1>, gs, dim3(256), 0, st, kv_off,
+                         lens, lens_end, ck_off, sh.hkv, sh.m, sh.p, sh.s, ncm, w.nc_ld, w.nchunk_a,
+                         w.keys_ld, logits, partial, lse_c, keys);
     }
     if (skip_topk) return;
     KernelTimer kt(INFV2_KERNEL_SELECT_TOPK, st);
