@@ -39,8 +39,8 @@ constexpr int kChunkA = 64;      // kernels per block in sel_dec_logits
 constexpr int kLogitsNtMaxBlocks = 1024;   // nontemporal key loads up to this many logits blocks
 constexpr int kLogWaves = 2;     // waves per 64-kernel chunk in sel_dec_logits_mfma (4 was no faster)
 constexpr int kLogTiles = 4 / kLogWaves;   // 16-kernel tiles per wave
-constexpr int kChunkB = 256;     // kernels per block in sel_dec_scores (512 in large grids)
-constexpr int kScoresTwoMinBlocks = 512;   // grids above this take 512-kernel blocks
+constexpr int kChunkB = 256;     // kernels per block in sel_dec_scores (1024 in large grids)
+constexpr int kScoresTwoMinBlocks = 512;   // grids above this take 1024-kernel blocks
 constexpr int kRowsPre = 4;      // query rows per block in the prefill passes
 constexpr int kTilePre = 64;     // kernels per LDS tile in the prefill passes
 
@@ -491,8 +491,8 @@ __device__ __forceinline__ float fold_partials(const float2* __restrict__ pp, in
 
 // lse_in: a per-(sequence, KV head, head) normaliser to use instead of the one
 // folded from `partial` (the coarse-kernel approximation), or NULL.
-// kJ kernels per thread: 256 kJ kernels per block (kJ = 2 for large grids:
-// half the blocks, so half the re-reads of the partials).
+// kJ kernels per thread: 256 kJ kernels per block (kJ = 4 for large grids:
+// a quarter of the blocks, so a quarter of the re-reads of the partials).
 template <int kJ>
 __global__ __launch_bounds__(256) void sel_dec_scores(
     const int64_t* __restrict__ kv_off, const int64_t* __restrict__ lens, int lens_end,
@@ -1333,11 +1333,11 @@ static void dec_launch(const Shape& sh, const void* q, const void* ck, const int
             lse_c);
     }
     {
-        // large grids: 512 kernels per block
+        // large grids: 1024 kernels per block
         const bool two = static_cast<int64_t>(gb.x) * gb.y * gb.z > kScoresTwoMinBlocks;
-        const dim3 gs(two ? (gb.x + 1) / 2 : gb.x, sh.hkv, batch);
+        const dim3 gs(two ? (gb.x + 3) / 4 : gb.x, sh.hkv, batch);
         if (two)
-            launch_timed(INFV2_KERNEL_SELECT_SCORES, sel_dec_scores<2>, gs, dim3(256), 0, st, kv_off,
+            launch_timed(INFV2_KERNEL_SELECT_SCORES, sel_dec_scores<4>, gs, dim3(256), 0, st, kv_off,
                          lens, lens_end, ck_off, sh.hkv, sh.m, sh.p, sh.s, ncm, w.nc_ld, w.nchunk_a,
                          w.keys_ld, logits, partial, lse_c, keys);
         else
