@@ -10,16 +10,18 @@
 //                   bf16 queries), stores the logits (fp32 scratch, 16 x n_c
 //                   floats per KV head: an eighth of a fp32 compressed-key
 //                   re-read) and a partial (max, sum-exp) per head.
-//   sel_dec_scores  grid (256-kernel chunk, KV head, sequence).  Each block folds
-//                   the partials into the per-head LogSumExp, forms the group
-//                   score R_j = mean_h exp(z_hj - LSE_h) and the block max by
+//   sel_dec_scores  grid (kernel chunk, KV head, sequence): 256 kernels per
+//                   block, 1024 in large grids.  Each block folds the partials
+//                   into the per-head LogSumExp, forms the group score
+//                   R_j = mean_h exp(z_hj - LSE_h) and the block max by
 //                   atomicMax on sortable keys.
 //   sel_dec_topk    one block per (sequence, KV head).
 // Cross-block results are handed over at kernel boundaries only: a device-scope
 // fence inside a kernel costs a write-back and invalidation of the whole L2 of
 // the XCD on gfx950, once per block.
 // Prefill (rows of one sequence, causal visibility per row):
-//   ck_split_hilo   fp32 compressed keys -> hi / lo bf16 rows, once per call.
+//   ck_split_hilo   fp32 compressed keys, times score_scale log2 e -> hi / lo
+//                   bf16 rows, once per call.
 //   sel_pre_mfma<1> 16 rows per block on the matrix cores: per-head LogSumExp.
 //   sel_pre_mfma<2> the same logits again: group score, block max.
 //   (sel_pre_lse / sel_pre_scores: the vector-ALU versions for fp32 queries)
