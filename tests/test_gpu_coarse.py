@@ -124,7 +124,7 @@ def test_coarse_decode_fp32():
     _run_decode(wl, 96, label="coarse decode fp32 96")
 
 
-@pytest.mark.parametrize("cfg,coarse", [(1, 128), (2, 128), (2, 256)])
+@pytest.mark.parametrize("cfg,coarse", [(1, 128), (2, 128), (2, 256), (4, 128)])
 def test_coarse_decode_configs(cfg, coarse):
     _run_decode(make_config(cfg), coarse, label=f"config {cfg} coarse {coarse}")
 
