@@ -610,6 +610,73 @@ def test_varlen_prefill_equals_per_sequence_calls():
         r0 = r1
 
 
+def test_varlen_prefill_more_sequences_than_one_launch_takes():
+    """70 short sequences in one varlen call: more than one launch holds (64
+    sequences per launch), so both the selection (workspace for all rows) and
+    the attention run in two launches.  Selections and outputs equal the
+    single-sequence calls bit for bit, and the oracle on sampled rows."""
+    import trainable_block_sparse_amd as tbs
+    from synth import f32_to_bf16_bits
+    h = _harness()
+    rng = np.random.default_rng(131)
+    nseq = 70
+    lens = rng.integers(40, 400, size=nseq, endpoint=True)
+    wl = _small(lens=lens.tolist(), topk=4, local=1, seed=131, n_planted=1)
+    _say(f"varlen prefill: {nseq} sequences of 40-400 tokens, the last rows of each")
+    dev = h.DeviceWorkload(wl)
+    dev.compress()
+    rows = np.array([int(rng.integers(1, n, endpoint=True)) for n in lens], dtype=np.int32)
+    starts = (lens - rows).astype(np.int64)
+    T = int(rows.sum())
+    qf = rng.standard_normal((T, wl.num_q_heads, wl.head_dim), dtype=np.float32)
+    q = h.to_device(f32_to_bf16_bits(qf))
+    cfg, hkv, k = dev.cfg, wl.num_kv_heads, wl.topk
+    max_len = int(lens.max())
+    ws_all = dev.ws(tbs.OP_SELECT_PREFILL, T, nseq, max_len)
+    ws_a = torch.zeros(max(256, tbs.infv2_workspace_bytes(cfg, tbs.OP_ATTN_PREFILL, int(rows.max()), 1,
+                                                         max_len)), dtype=torch.uint8, device="cuda")
+    idx_v = torch.empty((T, hkv, k), dtype=torch.int32, device="cuda")
+    out_v = torch.empty_like(q)
+    tbs.infv2_select_blocks_varlen(cfg, q, rows, starts, dev.ck, dev.ck_offsets, dev.kv_offsets,
+                                   idx_v, None, ws_all)
+    tbs.infv2_sparse_attn_prefill_varlen(cfg, q, rows, starts, dev.k, dev.v, dev.kv_offsets, idx_v,
+                                         out_v, ws_a)
+    torch.cuda.synchronize()
+    ws_s = dev.ws(tbs.OP_SELECT_PREFILL, int(rows.max()), 1, max_len)
+    prm = params_of(wl)
+    qrows_all = h.from_device(q, "bf16")
+    r0 = 0
+    checked = 0
+    for b in range(nseq):
+        r1 = r0 + int(rows[b])
+        idx_s = torch.empty((int(rows[b]), hkv, k), dtype=torch.int32, device="cuda")
+        out_s = torch.empty((int(rows[b]), wl.num_q_heads, wl.head_dim), dtype=q.dtype, device="cuda")
+        nb = int(starts[b]) + int(rows[b])
+        tbs.infv2_select_blocks(cfg, tbs.INFV2_MODE_PREFILL, q[r0:r1], int(rows[b]), int(starts[b]),
+                                dev.ck, dev.ck_offsets[b:], dev.kv_offsets[b:], None, 1, nb, idx_s,
+                                None, ws_s)
+        tbs.infv2_sparse_attn_prefill(cfg, q[r0:r1], int(rows[b]), int(starts[b]), dev.k, dev.v,
+                                      dev.kv_offsets[b:], idx_s, out_s, ws_a)
+        torch.cuda.synchronize()
+        assert torch.equal(idx_v[r0:r1], idx_s), f"seq {b}: selection"
+        assert torch.equal(out_v[r0:r1], out_s), f"seq {b}: output"
+        if b % 9 == 0 or b >= 63:           # the oracle on the last row of some sequences
+            K = wl.k_f64(b)
+            ck = dev.ck_host()[b]
+            loc = int(rows[b]) - 1
+            i = int(starts[b]) + loc
+            gi = idx_v[r0:r1].cpu().numpy().astype(np.int64)
+            for g in range(hkv):
+                rs = ref.select_row(qrows_all[r0 + loc, 16 * g:16 * g + 16], ck[g], i, prm)
+                assert not accept_selection(gi[loc, g], rs).startswith("fail"), (b, loc, g)
+            want = ref.attend_with_selection(qrows_all[r0 + loc:r0 + loc + 1], K, wl.v_f64(b), [i],
+                                             gi[loc:loc + 1], prm)
+            assert_close(h.from_device(out_v[r0 + loc:r0 + loc + 1], "bf16"), want, "bf16", f"varlen seq {b}")
+            checked += 1
+        r0 = r1
+    assert checked >= 10
+
+
 @pytest.mark.parametrize("io,ck_dtype,keys", [("bf16", "fp32", "random"), ("bf16", "bf16", "random"),
                                               ("fp32", "fp32", "random"), ("bf16", "fp32", "levels"),
                                               ("bf16", "fp32", "equal"), ("bf16", "fp32", "batch16"),
