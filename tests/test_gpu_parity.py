@@ -122,6 +122,16 @@ def test_decode_ragged_small_batch():
     _run_decode(wl, label="decode ragged bf16")
 
 
+@pytest.mark.parametrize("io,nseq,lo,hi", [("bf16", 96, 1, 3000), ("fp32", 4, 10000, 30000)])
+def test_decode_many_sequences_and_long_fp32(io, nseq, lo, hi):
+    """A batch of 96 ragged bf16 sequences (grid depth in the batch, short caches
+    next to empty-ish ones) and fp32 inputs at 10K-30K tokens (the vector-ALU
+    scoring pass over thousands of kernels)."""
+    lens = np.random.default_rng(151 + nseq).integers(lo, hi, size=nseq, endpoint=True).tolist()
+    wl = _small(lens=lens, io=io, topk=16, local=2, seed=151 + nseq, n_planted=4)
+    _run_decode(wl, label=f"decode {io} {nseq} sequences of {lo}-{hi}")
+
+
 def test_decode_fp32_ragged_and_bf16_ck():
     wl = _small(lens=[700, 1024, 2049], io="fp32", topk=6, local=1, seed=22)
     _run_decode(wl, label="decode fp32")
