@@ -137,6 +137,12 @@ def test_backward_dense_rows_and_large_topk():
     _check_full(wl, [(0, 900)], "bwd bf16 dense")
 
 
+def test_backward_topk128_union_at_capacity():
+    # 16 rows x 128 selections: the most the row pass's row-group union takes
+    wl = _small(io="bf16", L=9000, topk=128, local=4, seed=45)
+    _check_full(wl, [(8832, 8992)], "bwd bf16 top-k 128")
+
+
 def test_backward_rows_without_visible_tokens():
     """Rows whose selection is all padding have zero dq and add nothing to dk / dv."""
     h = _h()

@@ -296,6 +296,15 @@ def test_large_topk():
     _run_prefill(wl, 4000, positions=pos, label="prefill top-k 160")
 
 
+def test_prefill_topk128_union_at_capacity():
+    """Top-k 128 in bf16 prefill: 16 rows x 128 selections, the most the
+    matrix-core kernel's row-group union takes (2048 entries)."""
+    wl = _small(mode="prefill", lens=[12000], topk=128, local=4, seed=83, n_planted=6)
+    rng = np.random.default_rng(83)
+    pos = sorted(set(rng.integers(8192, 12000, 40).tolist()) | set(range(12000 - 32, 12000)))
+    _run_prefill(wl, 4000, positions=pos, label="prefill top-k 128")
+
+
 def test_decode_batch_with_an_empty_sequence():
     """An empty cache (length 0) in a packed batch: no blocks (all ids -1), a zero
     output row, and the other sequences unaffected."""
