@@ -23,8 +23,8 @@
 // the old reference (p <= 256, exact in fp32 and bf16), which skips the
 // cross-lane max and the rescale on almost every block.  Row sums stay per lane
 // until the end.  Keys after the row (t > i) are masked in the row's own block.
-// Thread blocks are placed so that each XCD (own L2) serves consecutive row
-// groups of one KV head.
+// Thread blocks are placed so that each XCD (own L2) serves row groups of one
+// KV head, the later (larger) ones first.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "prefill_tiles.hpp"
@@ -52,15 +52,30 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
     float scale_log2) {
     __shared__ __attribute__((aligned(16))) StageTiles kst[2], vst[2];   // two stages
     __shared__ UnionSmem sm;
-    // XCD-aware placement: thread block b runs on XCD b % 8; give each XCD a
-    // contiguous range of (KV head, row group) work items
-    const int nwg = static_cast<int>(gridDim.x);
-    const int xcd = static_cast<int>(blockIdx.x) % kXcds, kx = static_cast<int>(blockIdx.x) / kXcds;
-    const int qx = nwg / kXcds, rx = nwg % kXcds;
-    const int lid = xcd * qx + (xcd < rx ? xcd : rx) + kx;
-    // work item -> (KV head, sequence, its row group)
+    // XCD-aware placement: thread block b runs on XCD b % 8 and the blocks of
+    // one XCD start in the order of b.  When the KV heads divide the XCDs, each
+    // head gets 8 / hkv XCDs of its own (its K / V prefix in their L2), they take
+    // its row groups in turn, and each XCD runs its share from the last row
+    // group down: later rows see more blocks, so the largest unions start first
+    // and the small ones fill in behind them (a per-XCD tail of +2 % in a host
+    // model of config 3's unions, against +11 % for contiguous ranges in row
+    // order).  Otherwise each XCD gets a contiguous range of work items.
     const int nrg = seqs.grp_end[seqs.n - 1];
-    const int g = lid / nrg, grp = lid % nrg;
+    const int xcd = static_cast<int>(blockIdx.x) % kXcds, kx = static_cast<int>(blockIdx.x) / kXcds;
+    int g, grp;
+    if (kXcds % hkv == 0) {
+        const int xh = kXcds / hkv;                        // XCDs per KV head
+        g = xcd / xh;
+        const int rank = kx * xh + xcd % xh;
+        if (rank >= nrg) return;                           // grid padding (whole block)
+        grp = nrg - 1 - rank;
+    } else {
+        const int nwg = static_cast<int>(gridDim.x);
+        const int qx = nwg / kXcds, rx = nwg % kXcds;
+        const int lid = xcd * qx + (xcd < rx ? xcd : rx) + kx;
+        g = lid / nrg;
+        grp = lid % nrg;
+    }
     int si = 0;
     while (si + 1 < seqs.n && grp >= seqs.grp_end[si]) ++si;
     const int r0 = (grp - (si > 0 ? seqs.grp_end[si - 1] : 0)) * kPRows;
@@ -297,6 +312,16 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_prefill_mfma(
     }
 }
 
+// blocks of the launch: 8 per (8 / hkv) row groups when the KV heads divide the
+// XCDs (the kernel maps them head by head), else one per (KV head, row group)
+static unsigned prefill_grid(int nrg, int hkv) {
+    if (kXcds % hkv == 0) {
+        const int xh = kXcds / hkv;
+        return static_cast<unsigned>(kXcds) * static_cast<unsigned>((nrg + xh - 1) / xh);
+    }
+    return static_cast<unsigned>(nrg) * static_cast<unsigned>(hkv);
+}
+
 bool attn_prefill_mfma_ok(const Shape& sh) {
     return sh.io_bf16 && sh.m == kPB && kPRows * sh.topk <= kUnionCap;
 }
@@ -311,7 +336,7 @@ hipError_t launch_attn_prefill_mfma_seqs(const Shape& sh, const PrefillSeqs& seq
     if (nrg < 1) return hipSuccess;
     const float scale_log2 = sh.attn_scale * 1.4426950408889634f;
     launch_timed(INFV2_KERNEL_ATTN_PREFILL, attn_prefill_mfma,
-                 dim3(static_cast<unsigned>(nrg) * sh.hkv), dim3(kPThreads), 0, st, seqs,
+                 dim3(prefill_grid(nrg, sh.hkv)), dim3(kPThreads), 0, st, seqs,
         static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
         static_cast<const bf16_t*>(v), kv_off, idx, static_cast<bf16_t*>(out), sh.hq, sh.hkv,
         sh.topk, scale_log2);
