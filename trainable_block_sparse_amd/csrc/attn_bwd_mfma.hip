@@ -4,8 +4,9 @@
 // blocks; the selection is held fixed.  The arithmetic is the one stated in
 // attn_bwd.hip; here it runs on 16x16x32 bf16 MFMA with fp32 accumulation.
 //
-// Row pass (bwd_row_mfma): like the forward prefill kernel, a thread block owns
-// 16 consecutive rows of one KV head (one row per wave) and streams the union
+// Row pass (bwd_row_mfma): like the forward prefill kernel (and placed like it),
+// a thread block owns 16 consecutive rows of one KV head (one row per wave) and
+// streams the union
 // of their selected blocks through LDS (K and V as stored; the K^T operand comes
 // from the K tile by transpose reads), two blocks per barrier interval with the
 // next interval's loads in flight.  Per (row, block):
@@ -90,8 +91,26 @@ __global__ __launch_bounds__(kRThreads, 1) void bwd_row_mfma(
     float scale) {
     __shared__ __attribute__((aligned(16))) BlockTile kst[kRSlots], vst[kRSlots];   // stage x: slots 2 x, 2 x + 1
     __shared__ UnionSmem sm;
-    const int lid = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
-    const int g = lid / nrg, r0 = (lid % nrg) * kURows;
+    // placement as in the forward: each KV head's XCDs take its row groups in
+    // turn, from the last (largest union) down; one call spans the whole
+    // sequence, so contiguous ranges in row order would leave the XCD with the
+    // last rows several times the work of the one with the first
+    int g, grp;
+    {
+        const int xcd = static_cast<int>(blockIdx.x) % kXcdsB, kx = static_cast<int>(blockIdx.x) / kXcdsB;
+        if (kXcdsB % hkv == 0) {
+            const int xh = kXcdsB / hkv;
+            g = xcd / xh;
+            const int rank = kx * xh + xcd % xh;
+            if (rank >= nrg) return;                       // grid padding (whole block)
+            grp = nrg - 1 - rank;
+        } else {
+            const int lid = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+            g = lid / nrg;
+            grp = lid % nrg;
+        }
+    }
+    const int r0 = grp * kURows;
     const int t = threadIdx.x;
     const int w = t >> 6, l = t & 63, lg = l >> 4, lc = l & 15;
     const int64_t cap = kv_off[1] - kv_off[0];
@@ -542,8 +561,11 @@ hipError_t launch_attn_prefill_bwd_mfma(const Shape& sh, const BwdWs& w, const v
     hipError_t e = hipSuccess;
     {
         const int nrg = (rows + kURows - 1) / kURows;
+        const unsigned grid_r = kXcdsB % sh.hkv == 0
+            ? static_cast<unsigned>(kXcdsB) * static_cast<unsigned>((nrg + kXcdsB / sh.hkv - 1) / (kXcdsB / sh.hkv))
+            : static_cast<unsigned>(nrg) * static_cast<unsigned>(sh.hkv);
         launch_timed(INFV2_KERNEL_BWD_ROW, bwd_row_mfma,
-                     dim3(static_cast<unsigned>(nrg) * sh.hkv), dim3(kRThreads), 0, st,
+                     dim3(grid_r), dim3(kRThreads), 0, st,
             static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(out),
             static_cast<const bf16_t*>(dout), rows, q_start, static_cast<const bf16_t*>(k),
             static_cast<const bf16_t*>(v), kv_off, idx, static_cast<bf16_t*>(dq), lse2, delta,
