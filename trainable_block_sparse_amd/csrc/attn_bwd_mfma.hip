@@ -345,8 +345,13 @@ __global__ __launch_bounds__(kCThreads, 3) void bwd_col_mfma(
     __shared__ __attribute__((aligned(16))) float lsd[kCStages][kCThreads / 64][64];  // per wave
     __shared__ __attribute__((aligned(16))) int32_t seg_rows[kSeg + 2];  // the segment's row ids
     const int ncol = hkv * nblk;
-    const int item = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
-    if (item >= item_start[ncol]) return;
+    // items in block order, dealt round the XCDs: the blocks resident at any
+    // time work on neighbouring columns of one head, whose row lists overlap
+    // (the local window, popular blocks), so the Q and dO rows they gather are
+    // shared in the last-level cache; giving each XCD a contiguous range spreads
+    // them over the whole sequence instead (measured 18 % slower)
+    const int item = static_cast<int>(blockIdx.x);
+    if (item >= item_start[ncol]) return;      // the grid is sized for the most items there can be
     // column of this item: last c with item_start[c] <= item
     int lo = 0, hi = ncol - 1;
     while (lo < hi) {
