@@ -531,23 +531,34 @@ __global__ __launch_bounds__(256) void bwd_col_finish(
     if (n <= 1) return;
     const int64_t cap = kv_off[1] - kv_off[0];
     const size_t hoff = (kv_off[0] * hkv + static_cast<int64_t>(g) * cap) * kHeadDim;
-    // thread t: 32 consecutive values of the [2][64][128] partial
-    for (int e = t * 4; e < 2 * kPB * kHeadDim; e += 256 * 4) {
-        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int x = 0; x < n; ++x) {
-            const float4 p = *reinterpret_cast<const float4*>(partial + static_cast<size_t>(i0 + x) * 2 * kPB * kHeadDim + e);
-            s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
-        }
-        const int which = e / (kPB * kHeadDim), rem = e % (kPB * kHeadDim);
-        const int64_t key = static_cast<int64_t>(j) * kPB + rem / kHeadDim;
-        if (key >= lim) continue;
-        const float f = which == 0 ? scale : 1.f;
-        uint2 pk;
-        pk.x = pack_rne(s.x * f, s.y * f);
-        pk.y = pack_rne(s.z * f, s.w * f);
-        bf16_t* dst = (which == 0 ? dk : dv) + hoff + key * kHeadDim + rem % kHeadDim;
-        *reinterpret_cast<uint2*>(dst) = pk;
+    // thread: 4 consecutive values of the [2][64][128] partial (block y takes
+    // 1024 of them); four segments' loads in flight at a time, summed in
+    // segment order
+    constexpr size_t kStride = 2 * kPB * kHeadDim;
+    const int e = (static_cast<int>(blockIdx.y) * 256 + t) * 4;
+    const float* src = partial + static_cast<size_t>(i0) * kStride + e;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    int x = 0;
+    for (; x + 4 <= n; x += 4) {
+        float4 p[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) p[u] = *reinterpret_cast<const float4*>(src + static_cast<size_t>(x + u) * kStride);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) { s.x += p[u].x; s.y += p[u].y; s.z += p[u].z; s.w += p[u].w; }
     }
+    for (; x < n; ++x) {
+        const float4 p = *reinterpret_cast<const float4*>(src + static_cast<size_t>(x) * kStride);
+        s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+    }
+    const int which = e / (kPB * kHeadDim), rem = e % (kPB * kHeadDim);
+    const int64_t key = static_cast<int64_t>(j) * kPB + rem / kHeadDim;
+    if (key >= lim) return;
+    const float f = which == 0 ? scale : 1.f;
+    uint2 pk;
+    pk.x = pack_rne(s.x * f, s.y * f);
+    pk.y = pack_rne(s.z * f, s.w * f);
+    bf16_t* dst = (which == 0 ? dk : dv) + hoff + key * kHeadDim + rem % kHeadDim;
+    *reinterpret_cast<uint2*>(dst) = pk;
 }
 
 hipError_t launch_attn_prefill_bwd_mfma(const Shape& sh, const BwdWs& w, const void* q, int rows,
@@ -588,7 +599,8 @@ hipError_t launch_attn_prefill_bwd_mfma(const Shape& sh, const BwdWs& w, const v
         static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), kv_off, cstart, list,
         w.list_ld, item_start, lse2, delta, static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv),
         partial, sh.hq, sh.hkv, w.nblk, scale_log2, sh.attn_scale);
-    bwd_col_finish<<<dim3(static_cast<unsigned>(ncol)), 256, 0, st>>>(
+    static_assert(2 * kPB * kHeadDim % 1024 == 0, "finish grid");
+    bwd_col_finish<<<dim3(static_cast<unsigned>(ncol), 2 * kPB * kHeadDim / 1024), 256, 0, st>>>(
         item_start, partial, n, kv_off, static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), sh.hkv,
         w.nblk, sh.attn_scale);
     return hipGetLastError();
