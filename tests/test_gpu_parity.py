@@ -552,6 +552,89 @@ def test_selection_with_massive_ties():
     _run_prefill(wl, 1500, label="prefill all-equal scores")
 
 
+def _isolated_high(n_high, seed):
+    """Keys constant inside each 64-token block: one level of a direction for
+    every block but n_high isolated ones per KV head at twice that level.  The
+    blocks whose overlapping kernels see only the common level all score exactly
+    alike (hundreds of them); the high blocks and their neighbours differ."""
+    rng = np.random.default_rng(seed)
+
+    def keys(b, shape):
+        hkv, n, d = shape
+        u = rng.standard_normal(d)
+        u /= np.linalg.norm(u)
+        nb = -(-n // 64)
+        lvl = np.ones((hkv, nb))
+        for g in range(hkv):
+            lvl[g, rng.choice(np.arange(8, nb - 16, 4), size=n_high, replace=False)] = 2.0
+        return np.repeat(lvl, 64, axis=1)[:, :n, None] * 0.5 * u[None, None, :]
+    return keys
+
+
+def _ties_with_keys_above(wl, ck, rows):
+    """The oracle's view: at each (row, KV head) more than 256 candidates share
+    the score of the k'-th largest, and some score above it."""
+    prm = params_of(wl)
+    q = wl.q_f64()
+    for i in rows:
+        for g in range(wl.num_kv_heads):
+            qi = q[0 if wl.mode == "decode" else i, 16 * g:16 * g + 16]
+            rs = ref.select_row(qi, ck[g], i, prm)
+            sc = rs.S[~rs.forced]
+            thr = np.sort(sc)[::-1][rs.kprime - 1]
+            assert (sc == thr).sum() > 256 and (sc > thr).sum() > 0, (i, g)
+
+
+def _fused_step_equals(dev, wl, idx, out):
+    """infv2_decode_step on the cache of a _run_decode (compressed keys complete:
+    the step rebuilds the newest kernel's key with the same bits) gives the same
+    selection and output as the separate calls."""
+    import trainable_block_sparse_amd as tbs
+    h = _harness()
+    B = wl.batch
+    ws = torch.zeros(tbs.infv2_workspace_bytes(dev.cfg, tbs.OP_DECODE_STEP, B, B, dev.max_len),
+                     dtype=torch.uint8, device="cuda")
+    idx_s = dev.guarded((B, wl.num_kv_heads, wl.topk), torch.int32)
+    out_s = dev.guarded(tuple(dev.q.shape), dev.q.dtype)
+    lens = torch.tensor(wl.lens.astype(np.int64), device="cuda")
+    tbs.infv2_decode_step(dev.cfg, dev.q, dev.k, dev.v, dev.kv_offsets, lens, dev.ck_offsets, dev.ck,
+                          B, dev.max_len, idx_s, out_s, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx_s.cpu().numpy().astype(np.int64), idx), "decode step: selection"
+    assert np.array_equal(h.from_device(out_s, wl.io_dtype), out), "decode step: output"
+    _say(f"decode step equal; {dev.check_canaries()} guarded buffers untouched")
+
+
+def test_decode_beyond_2048_blocks():
+    """A 200K-token cache (3125 blocks: 13 block keys per top-k thread, the
+    16-key register instantiation and two bitmap words per lane in the fused
+    step) at k = 64, against the oracle, and the fused step against the
+    separate calls."""
+    wl = _small(lens=[200000], topk=64, local=4, seed=63, n_planted=6)
+    dev, idx, out = _run_decode(wl, label="decode 200K")
+    _fused_step_equals(dev, wl, idx, out)
+
+
+def test_selection_ties_at_threshold_with_keys_above():
+    """More than 256 candidates share the score at the top-k threshold (more
+    than the rank step takes, so the narrowing ends on a single key value) and
+    a few candidates score above it: the selection keeps those and the lowest
+    blocks of the tied run, in the decode selection, the fused decode step (its
+    own top-k) and the prefill selection."""
+    wl = _with_keys(_small(lens=[40000], topk=40, local=2, seed=61), _isolated_high(6, 61))
+    K = wl.k_f64(0)
+    _ties_with_keys_above(wl, ref.compress_keys(K, wl.kernel_size, wl.kernel_stride, "fp32"),
+                          [K.shape[1] - 1])
+    dev, idx, out = _run_decode(wl, label="decode: ties at the threshold, keys above")
+    _fused_step_equals(dev, wl, idx, out)
+    wp = _with_keys(_small(mode="prefill", lens=[24000], topk=40, local=2, seed=62), _isolated_high(6, 62))
+    Kp = wp.k_f64(0)
+    _ties_with_keys_above(wp, ref.compress_keys(Kp, wp.kernel_size, wp.kernel_stride, "fp32"),
+                          [23999, 20000])
+    _run_prefill(wp, 4000, positions=[0, 4095, 20000, 23000, 23999],
+                 label="prefill: ties at the threshold, keys above")
+
+
 def test_varlen_prefill_equals_per_sequence_calls():
     """Serving-style prefill: three sequences, each with a chunk of rows starting
     mid-sequence, in one varlen call.  Selections and outputs equal the

@@ -214,10 +214,12 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(
 // Decode step: the top-k of the (sequence, KV head) runs in every thread block
 // of its attention, before the tiles, so the step needs no separate top-k launch
 // and no round trip of the block list through memory.  The selection is the
-// one the top-k kernel makes (same code, same keys); split 0 also stores it.
-// Tiles as attn_decode_mfma.  Keys: the block-score keys of the scoring pass,
-// rows of kld entries padded to 256 kPer.
-constexpr int kFusedTopkMax = 256;       // largest top-k the fused kernel keeps in LDS
+// one the top-k kernel makes (same code, same keys); single-tile grids keep it
+// as a bitmap of the selected blocks, read by each wave for its own block
+// (cheaper than the ordered list at batch 1, dearer in the larger grids where
+// waves run several tiles); split 0 also stores the list.  Tiles as attn_decode_mfma.  Keys: the
+// block-score keys of the scoring pass, rows of kld entries padded to 256 kPer.
+constexpr int kFusedTopkMax = 256;       // largest top-k the fused kernel serves
 
 template <int kPer, bool kRun>
 __global__ __launch_bounds__(256) void attn_decode_topk_mfma(
@@ -228,8 +230,10 @@ __global__ __launch_bounds__(256) void attn_decode_topk_mfma(
     int hq, int hkv, int m, int topk, int nsplit, int tpw_arg, float scale_log2) {
     const int tpw = kRun ? tpw_arg : 1;
     static_assert(kPer % 2 == 0, "keys load in pairs");
+    constexpr int kWords = topk_bm_words(256, kPer);
     __shared__ union { TopkSmem<256> tk; DecSmem dec; } sm;
-    __shared__ int32_t sel[kFusedTopkMax];
+    __shared__ uint32_t sel_bits[kWords];     // single tiles: the selection, bit j = block j
+    __shared__ int32_t sel[kFusedTopkMax];    // runs: the selection as a list
     const int b = blockIdx.z, g = blockIdx.y, sp = blockIdx.x, t = threadIdx.x;
     const int w = t >> 6, l = t & 63, lg = l >> 4, lc = l & 15;
     const size_t bg = static_cast<size_t>(b) * hkv + g;
@@ -261,15 +265,27 @@ __global__ __launch_bounds__(256) void attn_decode_topk_mfma(
     c = c < nblk_max - 1 ? c : nblk_max - 1;
     int cnt = static_cast<int>(c + 1) - jb;
     cnt = cnt < 0 ? 0 : (cnt > kPer ? kPer : cnt);
-    block_topk_regs<256>(key, jb, cnt, static_cast<int>(c), topk, init, local, sel,
-                         static_cast<float*>(nullptr), sm.tk);
-    __syncthreads();                     // the list is complete; the top-k's LDS is free
-    if (sp == 0)
-        for (int r = t; r < topk; r += 256) idx_out[bg * topk + r] = sel[r];
     const int tpb = m >> 4;
     const int u0 = (sp * 4 + w) * tpw;   // this wave's first tile
     const int e = u0 / tpb, st0 = u0 - e * tpb;
-    const int32_t blk = (e < topk) ? sel[e] : -1;
+    int32_t blk;
+    if constexpr (!kRun) {
+        // small grids: the selection as a bitmap (no ordered output scan); each
+        // wave finds its own block in it
+        block_topk_regs<256, kPer, true>(key, jb, cnt, static_cast<int>(c), topk, init, local, nullptr,
+                                         static_cast<float*>(nullptr), sm.tk, sel_bits);
+        __syncthreads();                 // the bitmap is complete; the top-k's LDS is free
+        const BitmapLanes<kWords> bm(sel_bits);
+        if (sp == 0 && w == 0) bm.write_list(idx_out + bg * topk, topk);
+        blk = (e < topk) ? bm.nth(e) : -1;
+    } else {
+        block_topk_regs<256>(key, jb, cnt, static_cast<int>(c), topk, init, local, sel,
+                             static_cast<float*>(nullptr), sm.tk);
+        __syncthreads();                 // the list is complete; the top-k's LDS is free
+        if (sp == 0)
+            for (int r = t; r < topk; r += 256) idx_out[bg * topk + r] = sel[r];
+        blk = (e < topk) ? sel[e] : -1;
+    }
     const bf16_t* kh = k + (static_cast<size_t>(o0) * hkv + static_cast<size_t>(g) * cap) * kHeadDim + 8 * lg;
     const bf16_t* vh = v + (static_cast<size_t>(o0) * hkv + static_cast<size_t>(g) * cap) * kHeadDim + 8 * lg;
     decode_run<kRun>(sm.dec, qf, blk, st0, tpw, m, n, kh, vh, scale_log2, part_o, part_ml,

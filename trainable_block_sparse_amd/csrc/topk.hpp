@@ -54,13 +54,20 @@ __host__ __device__ constexpr int topk_kper(int per) {
     return per <= 2 ? 2 : per <= 8 ? 8 : per <= 16 ? 16 : 64;
 }
 
+// words of the selection bitmap for kThreads threads of kPer blocks
+__host__ __device__ constexpr int topk_bm_words(int threads, int per) { return (threads * per + 31) / 32; }
+
 // key[u] is the key of block jb + u for u < cnt (cnt = valid blocks of this
 // thread, 0 if none).  Must be called by all kThreads threads of the block.
-// Writes idx[k] ascending, padded with -1 (and score[k] if non-null).
-template <int kThreads, int kPer, typename Smem>
+// Writes idx[k] ascending, padded with -1 (and score[k] if non-null); with
+// kBitmap, instead sets bit j of the LDS words bits[] (cleared here) for every
+// selected block j, and the caller's barrier makes them visible (no ordered
+// output scan).
+template <int kThreads, int kPer, bool kBitmap = false, typename Smem>
 __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int cnt, int c, int k,
                                        int init, int local, int32_t* __restrict__ idx,
-                                       float* __restrict__ score, Smem& sm) {
+                                       float* __restrict__ score, Smem& sm,
+                                       uint32_t* __restrict__ bits = nullptr) {
     static_assert(kThreads % 64 == 0 && kThreads <= kTopkBins && kTopkBins % kThreads == 0,
                   "block size");
     static_assert(kPer <= 64, "at most 64 keys per thread");
@@ -69,6 +76,16 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int nb = c + 1;
     const float kNaN = __uint_as_float(0x7fc00000u);
+    static_assert(!kBitmap || (kPer <= 32 && 32 % kPer == 0), "a thread's blocks lie in one bitmap word");
+    if constexpr (kBitmap) {
+        for (int x = t; x < topk_bm_words(kThreads, kPer); x += kThreads) bits[x] = 0;
+        if (nb <= k) {                  // dense: every block
+            __syncthreads();            // orders the clearing
+            const uint32_t all = cnt > 0 ? (cnt >= 32 ? 0xffffffffu : (1u << cnt) - 1u) : 0u;
+            if (all != 0u) atomicOr(&bits[jb >> 5], all << (jb & 31));
+            return;
+        }
+    }
     if (nb <= k) {                      // dense: every block, then -1 padding
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
@@ -101,6 +118,7 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
     //       2 = single key value: the lowest `need` blocks, 3 = none.
     uint32_t lo = 0, hi = 0, need = kp;
     int mode = 3;
+    if (kBitmap && kp == 0) __syncthreads();   // orders the bitmap's clearing
     if (kp > 0) {
         // the first histogram is cleared here; the barrier after the min / max
         // orders the clearing before its increments
@@ -220,7 +238,7 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
     }
     // selection flags of this thread's blocks
     Mask smask = 0;
-    if (mode == 2) {                      // lowest `need` window blocks in block order
+    if (mode == 2) {                      // keys above the window, and its lowest `need` blocks
         uint32_t n_eq = 0;
 #pragma unroll
         for (int u = 0; u < kPer; ++u) n_eq += in_window(u) ? 1u : 0u;
@@ -228,6 +246,7 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
         uint32_t r = block_incl_scan_1b<kWaves>(n_eq, sm.scan_tmp[1], n_all) - n_eq;
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
+            if (cand(u) && key[u] > hi) smask |= Mask(1) << u;
             if (in_window(u)) {
                 if (r < need) smask |= Mask(1) << u;
                 ++r;
@@ -248,6 +267,10 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
 #pragma unroll
     for (int u = 0; u < kPer; ++u)
         if (u < cnt && !cand(u)) smask |= Mask(1) << u;     // forced
+    if constexpr (kBitmap) {
+        if (smask != 0) atomicOr(&bits[jb >> 5], static_cast<uint32_t>(smask) << (jb & 31));
+        return;
+    }
     const uint32_t n_sel = sizeof(Mask) == 8 ? __popcll(static_cast<uint64_t>(smask))
                                              : __popc(static_cast<uint32_t>(smask));
     uint32_t n_total;
@@ -269,5 +292,68 @@ __device__ inline void block_topk_regs(const uint32_t (&key)[kPer], int jb, int 
         if (score) score[r] = kNaN;
     }
 }
+
+// Wave-level reads of the selection bitmap (kWords words, bit j = block j):
+// lane l holds words [l kWpl, (l + 1) kWpl) and their inclusive set-bit count.
+template <int kWords>
+struct BitmapLanes {
+    static constexpr int kWpl = (kWords + 63) / 64;
+    uint32_t wv[kWpl];
+    uint32_t excl, incl;
+    __device__ explicit BitmapLanes(const uint32_t* bits) {
+        const int lane = threadIdx.x & 63;
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int i = 0; i < kWpl; ++i) {
+            const int x = lane * kWpl + i;
+            wv[i] = x < kWords ? bits[x] : 0u;
+            cnt += __popc(wv[i]);
+        }
+        incl = wave_incl_sum(cnt);
+        excl = incl - cnt;
+    }
+    // block of the e-th (0-based, ascending) selected slot, -1 past the last;
+    // e wave-uniform, the result in every lane.  The lane whose words hold that
+    // slot is found by a ballot; its word and the slot's rank in it are read
+    // into every lane, and lane b < 32 tests whether bit b is that set bit.
+    __device__ int32_t nth(int e) const {
+        const int lane = threadIdx.x & 63;
+        const uint32_t ue = static_cast<uint32_t>(e);
+        const uint64_t ball = __ballot(excl <= ue && ue < incl);
+        if (ball == 0) return -1;
+        const int src = static_cast<int>(__builtin_ctzll(ball));
+        uint32_t r = ue - static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(excl), src));
+        uint32_t word = 0;
+        int wi = 0;
+        bool found = false;
+#pragma unroll
+        for (int i = 0; i < kWpl; ++i) {
+            const uint32_t wvi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wv[i]), src));
+            const uint32_t p = __popc(wvi);
+            if (!found && r < p) { word = wvi; wi = i; found = true; }
+            else if (!found) r -= p;
+        }
+        const uint32_t below = lane < 32 ? (1u << lane) - 1u : 0xffffffffu;
+        const uint64_t hit = __ballot(lane < 32 && ((word >> lane) & 1u) != 0u && __popc(word & below) == r);
+        return (src * kWpl + wi) * 32 + static_cast<int>(__builtin_ctzll(hit));
+    }
+    // the selection as an ascending list of k slots, padded with -1 (one wave)
+    __device__ void write_list(int32_t* __restrict__ out, int k) const {
+        const int lane = threadIdx.x & 63;
+        uint32_t pos = excl;
+#pragma unroll
+        for (int i = 0; i < kWpl; ++i) {
+            uint32_t word = wv[i];
+            while (word != 0u) {
+                const int b = __builtin_ctz(word);
+                if (pos < static_cast<uint32_t>(k)) out[pos] = (lane * kWpl + i) * 32 + b;
+                ++pos;
+                word &= word - 1u;
+            }
+        }
+        const int total = __builtin_amdgcn_readlane(static_cast<int>(incl), 63);
+        for (int r = total + lane; r < k; r += 64) out[r] = -1;
+    }
+};
 
 }  // namespace infv2
