@@ -297,7 +297,9 @@ __global__ __launch_bounds__(256) void attn_decode_topk_mfma(
 // threads.  Thread t folds the (m, l) pairs of splits t, t + 256, ..; for the
 // outputs, thread t takes columns 4 (t % 32) .. +3 of splits t / 32, t / 32 + 8,
 // .. (the first eight of them loaded together with the pairs), and the eight
-// split groups are summed in LDS in a fixed order.
+// split groups are summed in LDS in a fixed order.  Up to 64 splits (the batch-1
+// grids) every wave folds all the pairs itself, one split per lane, and takes
+// the weights from their lanes: the final sum is then the only barrier.
 template <typename Tout>
 __global__ __launch_bounds__(256) void attn_decode_merge(const float* __restrict__ part_o,
                                                          const float2* __restrict__ part_ml,
@@ -319,6 +321,47 @@ __global__ __launch_bounds__(256) void attn_decode_merge(const float* __restrict
 #pragma unroll
     for (int i = 0; i < kPre; ++i)
         if (sg + kSg * i < nsplit) pre[i] = po[(sg + kSg * i) * stride];
+    auto add = [&](float4& acc, float w, const float4& a) {
+        acc.x = fmaf(w, a.x, acc.x); acc.y = fmaf(w, a.y, acc.y);
+        acc.z = fmaf(w, a.z, acc.z); acc.w = fmaf(w, a.w, acc.w);
+    };
+    auto finish = [&](const float4& acc, float den) {
+        part[sg][cq] = acc;
+        __syncthreads();
+        if (t < kHeadDim / 4) {
+            float4 r = part[0][t];
+#pragma unroll
+            for (int j = 1; j < kSg; ++j) {
+                const float4 a = part[j][t];
+                r.x += a.x; r.y += a.y; r.z += a.z; r.w += a.w;
+            }
+            const float inv = den > 0.f ? 1.f / den : 0.f;
+            Tout* dst = out + (static_cast<size_t>(b) * hq + static_cast<size_t>(g) * kGroup + h) * kHeadDim + 4 * t;
+            io<Tout>::store(dst + 0, r.x * inv);
+            io<Tout>::store(dst + 1, r.y * inv);
+            io<Tout>::store(dst + 2, r.z * inv);
+            io<Tout>::store(dst + 3, r.w * inv);
+        }
+    };
+    if (nsplit <= 64) {
+        // one split per lane: every wave folds all the (m, l) pairs itself with
+        // wave reductions and takes the weights of its splits from their lanes,
+        // so the only barrier is the final sum over split groups (the same
+        // arithmetic in the same order as the general path below)
+        const int lane = t & 63;
+        const float2 mlv = lane < nsplit ? part_ml[(bg * nsplit + lane) * kGroup + h] : make_float2(-INFINITY, 0.f);
+        const float gm1 = wave_max(mlv.x);
+        const float wt = (mlv.x == -INFINITY) ? 0.f : exp2f(mlv.x - gm1);
+        const float den1 = wave_sum(wt * mlv.y);
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int i = 0; i < kPre; ++i) {
+            const float wx = __shfl(wt, sg + kSg * i, 64);
+            if (sg + kSg * i < nsplit) add(acc, wx, pre[i]);
+        }
+        finish(acc, den1);
+        return;
+    }
     float2 ml[kMlPer];
 #pragma unroll
     for (int i = 0; i < kMlPer; ++i) {
@@ -345,31 +388,12 @@ __global__ __launch_bounds__(256) void attn_decode_merge(const float* __restrict
     __syncthreads();
     const float den = red[1][0] + red[1][1] + red[1][2] + red[1][3];
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    auto add = [&](float w, const float4& a) {
-        acc.x = fmaf(w, a.x, acc.x); acc.y = fmaf(w, a.y, acc.y);
-        acc.z = fmaf(w, a.z, acc.z); acc.w = fmaf(w, a.w, acc.w);
-    };
 #pragma unroll
     for (int i = 0; i < kPre; ++i)
-        if (sg + kSg * i < nsplit) add(wgt[sg + kSg * i], pre[i]);
+        if (sg + kSg * i < nsplit) add(acc, wgt[sg + kSg * i], pre[i]);
 #pragma unroll 4
-    for (int x = sg + kSg * kPre; x < nsplit; x += kSg) add(wgt[x], po[x * stride]);
-    part[sg][cq] = acc;
-    __syncthreads();
-    if (t < kHeadDim / 4) {
-        float4 r = part[0][t];
-#pragma unroll
-        for (int j = 1; j < kSg; ++j) {
-            const float4 a = part[j][t];
-            r.x += a.x; r.y += a.y; r.z += a.z; r.w += a.w;
-        }
-        const float inv = den > 0.f ? 1.f / den : 0.f;
-        Tout* dst = out + (static_cast<size_t>(b) * hq + static_cast<size_t>(g) * kGroup + h) * kHeadDim + 4 * t;
-        io<Tout>::store(dst + 0, r.x * inv);
-        io<Tout>::store(dst + 1, r.y * inv);
-        io<Tout>::store(dst + 2, r.z * inv);
-        io<Tout>::store(dst + 3, r.w * inv);
-    }
+    for (int x = sg + kSg * kPre; x < nsplit; x += kSg) add(acc, wgt[x], po[x * stride]);
+    finish(acc, den);
 }
 
 hipError_t launch_attn_decode_mfma(const Shape& sh, const void* q, const void* k, const void* v,
