@@ -109,25 +109,34 @@ def cold_replicas(step_bytes: int, floor: int = 8) -> int:
     return max(floor, -(-COLD_PASS_BYTES // max(1, step_bytes)))
 
 
-def kernel_times(tbs, torch, run, steps: int, families, ahead_ms: float = 50.0) -> dict:
+def kernel_times(tbs, torch, run, steps: int, families, ahead_ms: float = 50.0,
+                 passes: int = 2) -> dict:
     """Live per-kernel times: the library stamps every launch of one kernel
-    family with a pair of HIP events while a session is open; one eager pass of
-    `steps` steps per family, after an Infinity-Cache flush and queued behind a
-    spin kernel of `ahead_ms` so the GPU runs the pass back to back."""
+    family with a pair of HIP events while a session is open; eager passes of
+    `steps` steps per family, each after an Infinity-Cache flush and queued
+    behind a spin kernel of `ahead_ms` so the GPU runs the pass back to back.
+    Of `passes` such passes the one with the lower mean is kept (timing noise
+    only adds time; both passes start from a flushed cache)."""
     out = {}
     for fam in families:
-        torch.cuda.synchronize()
-        flush_mall(torch)
-        queue_ahead(torch, ahead_ms)
-        tbs.infv2_timing_start(fam)
-        try:
-            for t in range(steps):
-                run(t)
-        finally:
-            ms, n = tbs.infv2_timing_stop()
+        best = None
+        for _ in range(passes):
+            torch.cuda.synchronize()
+            flush_mall(torch)
+            queue_ahead(torch, ahead_ms)
+            tbs.infv2_timing_start(fam)
+            try:
+                for t in range(steps):
+                    run(t)
+            finally:
+                ms, n = tbs.infv2_timing_stop()
+            if best is None or (n and best[1] and ms / n < best[0] / best[1]):
+                best = (ms, n)
+        ms, n = best
         out[fam] = {"launches_per_step": n / steps,
                     "us_per_launch": ms * 1e3 / n if n else None,
-                    "us_per_step": ms * 1e3 / steps}
+                    "us_per_step": ms * 1e3 / steps,
+                    "passes": passes}
     return out
 
 
