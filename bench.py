@@ -676,6 +676,32 @@ def bench_prefill(args, torch, tbs, gh, ck_dtype=None) -> dict:
             evs.append((e0, e1, e2, e3))
         return evs
 
+    side = torch.cuda.Stream()
+    idx2 = torch.empty_like(idx)
+    out2 = torch.empty_like(out)
+
+    def run_two_streams():
+        """The same calls with each chunk's attention on a second stream: the
+        next chunk's compression and selection (which need neither its output
+        nor its workspace) run on the first stream meanwhile, so their thread
+        blocks fill the compute units the attention's last blocks leave idle."""
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        for q0 in range(0, L, C):
+            q1 = min(L, q0 + C)
+            lens = dev.kv_lens.new_tensor([q1])
+            begin = dev.kv_lens.new_tensor([num_kernels(q0, p, s)])
+            tbs.infv2_compress_keys(cfg, dev.k, dev.kv_offsets, lens, dev.ck_offsets, begin, 1, q1,
+                                    num_kernels(q1, p, s) - num_kernels(q0, p, s), dev.ck)
+            tbs.infv2_select_blocks(cfg, tbs.INFV2_MODE_PREFILL, dev.q[q0:q1], q1 - q0, q0, dev.ck,
+                                    dev.ck_offsets, dev.kv_offsets, None, 1, q1, idx2[q0:q1], None,
+                                    ws)
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                tbs.infv2_sparse_attn_prefill(cfg, dev.q[q0:q1], q1 - q0, q0, dev.k, dev.v,
+                                              dev.kv_offsets, idx2[q0:q1], out2[q0:q1], wsa)
+        main.wait_stream(side)
+
     run(False)
     torch.cuda.synchronize()
     reps = []
@@ -685,6 +711,19 @@ def bench_prefill(args, torch, tbs, gh, ck_dtype=None) -> dict:
         ph = np.array([[a.elapsed_time(b) for a, b in zip(x[:-1], x[1:])] for x in evs])  # ms
         reps.append(ph)
     ph = np.median(np.stack(reps), axis=0)          # [chunks][3]
+    run_two_streams()
+    torch.cuda.synchronize()
+    two, one = [], []
+    for _ in range(max(1, args.prefill_reps)):
+        e0 = T.event()
+        run(False)
+        e1 = T.event()
+        run_two_streams()
+        e2 = T.event()
+        torch.cuda.synchronize()
+        one.append(e0.elapsed_time(e1))
+        two.append(e1.elapsed_time(e2))
+    two_ok = bool(torch.equal(idx, idx2) and torch.equal(out, out2))
     gi = idx.cpu().numpy()
     pos = np.arange(L)
     tok = attended_tokens(gi, pos, np.full(L, L), wl.block_size)       # [L][Hkv]
@@ -706,6 +745,8 @@ def bench_prefill(args, torch, tbs, gh, ck_dtype=None) -> dict:
         "kv_reuse_per_loaded_block": float(pairs.sum() / union.sum()),
         "attn_ms": attn_ms, "select_ms": sel_ms, "compress_ms": float(ph[:, 0].sum()),
         "total_ms": total_ms, "tflops_attn": useful / (attn_ms * 1e-3) / 1e12,
+        "total_ms_endpoints": float(np.median(one)), "total_ms_two_streams": float(np.median(two)),
+        "two_streams_equal": two_ok,
         "tflops_path": useful / (total_ms * 1e-3) / 1e12,
         "score_gemm_flops_per_pass": score_flops_pass,
         "last_chunk_attn_ms": float(ph[-1, 2]),
@@ -1172,7 +1213,9 @@ def main() -> int:
     log(f"decode 128K: {main_res['ms_per_step'] * 1e3:.1f} us/step, per call {main_res['per_call_us']}")
     pre = None if args.no_prefill else bench_prefill(args, torch, tbs, gh)
     if pre:
-        log(f"prefill 32K: attn {pre['attn_ms']:.2f} ms, total {pre['total_ms']:.2f} ms, "
+        log(f"prefill 32K: attn {pre['attn_ms']:.2f} ms, total {pre['total_ms']:.2f} ms "
+            f"({pre['total_ms_endpoints']:.2f} ms between two events; two streams "
+            f"{pre['total_ms_two_streams']:.2f} ms, equal: {pre['two_streams_equal']}), "
             f"{pre['tflops_attn']:.1f} TFLOPS")
     bat = None if args.no_batched else bench_batched(args, torch, tbs, gh)
     if bat:
