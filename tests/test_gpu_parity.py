@@ -635,6 +635,48 @@ def test_selection_ties_at_threshold_with_keys_above():
                  label="prefill: ties at the threshold, keys above")
 
 
+def test_prefill_chunks_on_two_streams():
+    """Concurrent calls on two streams with their own workspaces, as the header
+    allows: each chunk's attention on a second stream while the next chunk's
+    compression and selection run on the first.  Same compressed keys,
+    selections and outputs, bit for bit, as the calls made one after another."""
+    import trainable_block_sparse_amd as tbs
+    h = _harness()
+    wl = _small(mode="prefill", lens=[12000], topk=16, local=2, seed=91)
+    L, C = 12000, 2000
+    _say("prefill chunks on two streams")
+    a = h.DeviceWorkload(wl)
+    idx_a, _, out_a = a.prefill(C)
+    b = h.DeviceWorkload(wl)
+    p, s = wl.kernel_size, wl.kernel_stride
+    idx_b = b.guarded((L, wl.num_kv_heads, b.cfg.topk), torch.int32)
+    out_b = b.guarded(tuple(b.q.shape), b.q.dtype)
+    ws = b.ws(tbs.OP_SELECT_PREFILL, C, 1, L)
+    wsa = b.ws(tbs.OP_ATTN_PREFILL, C, 1, L)
+    starts = list(range(0, L, C))
+    lens = [torch.tensor([min(L, q0 + C)], dtype=torch.int64, device="cuda") for q0 in starts]
+    begins = [torch.tensor([h.num_kernels(q0, p, s)], dtype=torch.int64, device="cuda") for q0 in starts]
+    torch.cuda.synchronize()
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    side.wait_stream(main)
+    for c, q0 in enumerate(starts):
+        q1 = min(L, q0 + C)
+        tbs.infv2_compress_keys(b.cfg, b.k, b.kv_offsets, lens[c], b.ck_offsets, begins[c], 1, q1,
+                                h.num_kernels(q1, p, s) - h.num_kernels(q0, p, s), b.ck)
+        tbs.infv2_select_blocks(b.cfg, tbs.INFV2_MODE_PREFILL, b.q[q0:q1], q1 - q0, q0, b.ck,
+                                b.ck_offsets, b.kv_offsets, None, 1, q1, idx_b[q0:q1], None, ws)
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            tbs.infv2_sparse_attn_prefill(b.cfg, b.q[q0:q1], q1 - q0, q0, b.k, b.v, b.kv_offsets,
+                                          idx_b[q0:q1], out_b[q0:q1], wsa)
+    main.wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(a.ck, b.ck), "compressed keys"
+    assert torch.equal(idx_a, idx_b), "selection"
+    assert torch.equal(out_a, out_b), "output"
+    _say(f"two streams equal; {b.check_canaries()} guarded buffers untouched")
+
+
 def test_varlen_prefill_equals_per_sequence_calls():
     """Serving-style prefill: three sequences, each with a chunk of rows starting
     mid-sequence, in one varlen call.  Selections and outputs equal the
