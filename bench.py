@@ -500,23 +500,28 @@ def bench_decode(cfg_index: int, args, torch, tbs, gh, replicas: int = 0, ck_dty
 def bench_decode_loop(args, torch, tbs, gh) -> dict:
     """Decode loop at 128K: each step appends one token per sequence to its cache
     (infv2_append_kv: K/V rows and the compressed key the token completes), then
-    selects and attends.  The caches have room for the appended tokens; lengths
-    advance on every step, graph replays included."""
+    selects and attends; and the same loop as one infv2_decode_step_append call
+    per token (the append folded into the step's kernels).  The caches have room
+    for every appended token; lengths advance on every step, graph replays
+    included."""
     from synth import make_config, extra_decode_queries
     wl = make_config(2)
     dev = gh.DeviceWorkload(wl, args.ck_dtype)
     cfg = dev.cfg
     B, hkv, d = wl.batch, wl.num_kv_heads, wl.head_dim
-    n0 = int(wl.lens[0])
-    step_bytes = sum(decode_bytes(wl, 2 if args.ck_dtype == "bf16" else 4, [n0]).values())
+    n_end = int(wl.lens[0])
+    step_bytes = sum(decode_bytes(wl, 2 if args.ck_dtype == "bf16" else 4, [n_end]).values())
     R = args.replicas if args.replicas > 0 else cold_replicas(step_bytes)
     W, K = args.warmup, args.steps
-    room = W + 4 * K + 64                         # every append of every timing pass fits
-    cap = n0 + room
-    # caches of capacity n0 + room holding the n0-token prefix
+    room = W + 12 * K + 64                        # every append of every timing pass fits
+    # caches of capacity n_end (128K) holding an n0-token prefix: the loop ends
+    # at most at 128K, so it runs the same kernel instantiations as the step
+    # measured on the full 128K cache (a larger capacity would give more than
+    # 2048 blocks, and the top-k 16 keys per thread instead of 8)
+    cap, n0 = n_end, n_end - room
     def padded(t):
         x = torch.zeros((hkv, cap, d), dtype=t.dtype, device="cuda")
-        x[:, :n0] = t.view(hkv, n0, d)
+        x[:, :n0] = t.view(hkv, n_end, d)[:, :n0]
         return x.view(-1)
     Ks = [padded(dev.k) for _ in range(R)]
     Vs = [padded(dev.v) for _ in range(R)]
@@ -572,10 +577,45 @@ def bench_decode_loop(args, torch, tbs, gh) -> dict:
     torch.cuda.synchronize()
     graph_ms = g0.elapsed_time(g1) / K
     kt = kernel_times(tbs, torch, lambda t: step(order[t % K]), K, ("append",))
+    # the same loop with the append folded into the step
+    ws_step = dev.ws(tbs.OP_DECODE_STEP, B, B, cap)
+
+    def step_fused(r):
+        tbs.infv2_decode_step_append(cfg, qs[r], kn[r], vn[r], Ks[r], Vs[r], kv_off, lens[r], ck_off,
+                                     CKs[r], B, cap, idx, out, ws_step)
+
+    def step_two(r):
+        tbs.infv2_append_kv(cfg, kn[r], vn[r], Ks[r], Vs[r], kv_off, lens[r], ck_off, CKs[r], B)
+        tbs.infv2_decode_step(cfg, qs[r], Ks[r], Vs[r], kv_off, lens[r], ck_off, CKs[r], B, cap, idx,
+                              out, ws_step)
+
+    def graph_time(fn):
+        gx = torch.cuda.CUDAGraph()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(gx, stream=side):
+                for r in order:
+                    fn(r)
+        torch.cuda.current_stream().wait_stream(side)
+        gx.replay()
+        torch.cuda.synchronize()
+        flush_mall(torch)
+        a0 = T.event()
+        gx.replay()
+        a1 = T.event()
+        torch.cuda.synchronize()
+        return a0.elapsed_time(a1) / K
+
+    two_ms = graph_time(step_two)
+    fused_ms = graph_time(step_fused)
     final_len = int(lens[0].item())
+    assert final_len < cap, "the caches ran out of room for the appended tokens"
+    assert final_len - n0 <= room
     return {"workload": "decode_loop_bf16_128k", "batch": B, "start_len": n0, "final_len_replica0": final_len,
             "ms_per_step_eager": eager_ms, "ms_per_step_graph": graph_ms, "replicas": R,
             "tok_per_s": B / (graph_ms * 1e-3), "append_us_per_launch": kt["append"]["us_per_launch"],
+            "ms_per_step_graph_append_then_step": two_ms,
+            "ms_per_step_graph_step_append": fused_ms, "tok_per_s_step_append": B / (fused_ms * 1e-3),
             "note": "graph of the timed steps, replayed after a cache flush; lengths advance on "
                     "every replay"}
 
@@ -1149,7 +1189,8 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"also run 8 device-to-device copies of {CALIBRATION_MIB} MiB (reference "
                          "kernel of known size for scaling the FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--only", choices=["decode", "prefill", "batched", "backward", "coarse", "varlen"],
+    ap.add_argument("--only", choices=["decode", "prefill", "batched", "backward", "coarse", "varlen",
+                                       "loop"],
                     default=None,
                     help="run one workload only and print its record (for profiling)")
     ap.add_argument("--summarize-rocprof", nargs="+", metavar=("KIND", "CSV"), default=None,
@@ -1201,6 +1242,8 @@ def main() -> int:
             rec = bench_coarse(args, torch, tbs, gh)
         elif args.only == "varlen":
             rec = bench_varlen_prefill(args, torch, tbs, gh)
+        elif args.only == "loop":
+            rec = bench_decode_loop(args, torch, tbs, gh)
         elif args.only == "backward":
             from synth import make_config
             rec = bench_backward(args, torch, tbs, gh, {"_wl": make_config(3)})
@@ -1238,7 +1281,8 @@ def main() -> int:
             + ", ".join(f"{c}: {p2[f'coarse_{c}']['select_ms']:.2f} ms" for c in (64, 128, 256)))
     loop = None if args.no_loop else bench_decode_loop(args, torch, tbs, gh)
     if loop:
-        log(f"decode loop 128K (append + select + attend): {loop['ms_per_step_graph'] * 1e3:.1f} us/step")
+        log(f"decode loop 128K (append + select + attend): {loop['ms_per_step_graph'] * 1e3:.1f} us/step; "
+            f"one decode_step_append per token: {loop['ms_per_step_graph_step_append'] * 1e3:.1f} us/step")
     # the same decode workloads with bf16 compressed keys (the documented option)
     alt = {}
     out_pre_bf16 = None

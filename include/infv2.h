@@ -288,6 +288,30 @@ int32_t infv2_decode_step(const infv2_config* cfg, const void* q, const void* k,
                           int32_t* block_idx, void* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * infv2_decode_step_append -- the serving loop's step: infv2_append_kv (the new
+ * token of every sequence enters the cache, "Semantic kernels": it completes
+ * kernel (n - p) / s when s divides n - p) followed by infv2_decode_step, with
+ * the same results bit for bit (caches, compressed keys, kv_lens, block_idx,
+ * out), in the decode step's launches: with bf16 inputs the first kernel also
+ * writes the new K/V rows and the last one advances kv_lens (one launch fewer
+ * than the two calls).  Other inputs run the two calls.
+ *
+ *   q            device, io_dtype [batch][Hq][d], the new tokens' queries
+ *   k_new, v_new device, io_dtype [batch][Hkv][d], the new tokens' keys / values
+ *   k, v, kv_offsets, kv_lens, ck_offsets, ck, batch   as for infv2_append_kv
+ *                (caches, compressed keys and kv_lens updated in place; a full
+ *                sequence is left as it is and decodes over its cache)
+ *   max_len      >= every sequence's length after the append
+ *   block_idx, out, ws, ws_bytes   as for infv2_decode_step (op = DECODE_STEP)
+ * Concurrent calls on one cache race; calls ordered on one stream are safe.
+ */
+int32_t infv2_decode_step_append(const infv2_config* cfg, const void* q, const void* k_new,
+                                 const void* v_new, void* k, void* v, const int64_t* kv_offsets,
+                                 int64_t* kv_lens, const int64_t* ck_offsets, void* ck,
+                                 int32_t batch, int64_t max_len, int32_t* block_idx, void* out,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/*
  * infv2_sparse_attn_prefill -- step 2 for a chunk of consecutive query rows
  * of one sequence ("Design principles summary": every query token selects its
  * own blocks; rows are causal, t <= i).

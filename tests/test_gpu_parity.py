@@ -889,6 +889,80 @@ def test_decode_step_equals_separate_calls(io, ck_dtype, keys):
     _say(f"decode step: 41 steps equal, {a.check_canaries()} guarded buffers untouched")
 
 
+@pytest.mark.parametrize("io,ck_dtype,keys", [("bf16", "fp32", "random"), ("bf16", "bf16", "random"),
+                                              ("bf16", "fp32", "batch16"), ("fp32", "fp32", "random")])
+def test_decode_step_append_equals_append_then_step(io, ck_dtype, keys):
+    """infv2_decode_step_append (the new token's K/V written into the caches by
+    the step's first kernel, the lengths advanced by its last) equals
+    infv2_append_kv followed by infv2_decode_step bit for bit, over 41 steps
+    that complete a kernel every 16 tokens: selections and outputs every step;
+    caches, compressed keys and lengths at the end.  The cache rows past the
+    start are cleared first, so a row the step fails to write shows; the
+    shortest sequences reach their capacity and take no-op appends.  fp32
+    inputs take the two-call path."""
+    import trainable_block_sparse_amd as tbs
+    from synth import extra_decode_queries
+    h = _harness()
+    if keys == "batch16":
+        lens = np.random.default_rng(183).integers(20000, 40000, size=16, endpoint=True).tolist()
+        wl = _small(lens=lens, io=io, topk=64, local=4, seed=183)
+    else:
+        wl = _small(lens=[3001, 700, 4500, 33], io=io, topk=8, local=2, seed=181)
+    _say(f"decode step with append vs append + step io={io} ck={ck_dtype} keys={keys}")
+    a = h.DeviceWorkload(wl, ck_dtype)
+    b = h.DeviceWorkload(wl, ck_dtype)
+    B, hkv, d, k = wl.batch, wl.num_kv_heads, wl.head_dim, wl.topk
+    cap = wl.lens.astype(np.int64)
+    off = np.concatenate([[0], np.cumsum(cap)])
+    start = np.maximum(cap - 40, 1)
+    k_full = a.k.clone().reshape(-1, d)
+    v_full = a.v.clone().reshape(-1, d)
+
+    def rows_of(bi, g, lo, hi):
+        base = int(off[bi]) * hkv + g * int(cap[bi])
+        return slice(base + lo, base + hi)
+    for dev in (a, b):
+        kk, vv = dev.k.view(-1, d), dev.v.view(-1, d)
+        for bi in range(B):
+            for g in range(hkv):
+                kk[rows_of(bi, g, int(start[bi]), int(cap[bi]))] = 0
+                vv[rows_of(bi, g, int(start[bi]), int(cap[bi]))] = 0
+        dev.kv_lens.copy_(torch.tensor(start, device="cuda"))
+        dev.compress(kv_lens=dev.kv_lens)
+    qs = h.to_device(extra_decode_queries(wl, 41))
+    ws_a = torch.zeros(tbs.infv2_workspace_bytes(a.cfg, tbs.OP_DECODE_STEP, B, B, a.max_len),
+                       dtype=torch.uint8, device="cuda")
+    ws_b = torch.zeros_like(ws_a)
+    for step in range(41):
+        pos = np.minimum(start + step, cap - 1)          # the row appended (ignored when full)
+        idx_rows = [rows_of(bi, g, int(pos[bi]), int(pos[bi]) + 1) for bi in range(B) for g in range(hkv)]
+        k_new = torch.cat([k_full[r] for r in idx_rows]).reshape(B, hkv, d).contiguous()
+        v_new = torch.cat([v_full[r] for r in idx_rows]).reshape(B, hkv, d).contiguous()
+        idx_a = a.guarded((B, hkv, k), torch.int32)
+        out_a = a.guarded(tuple(qs[step].shape), qs[step].dtype)
+        tbs.infv2_decode_step_append(a.cfg, qs[step], k_new, v_new, a.k, a.v, a.kv_offsets, a.kv_lens,
+                                     a.ck_offsets, a.ck, B, a.max_len, idx_a, out_a, ws_a)
+        tbs.infv2_append_kv(b.cfg, k_new, v_new, b.k, b.v, b.kv_offsets, b.kv_lens, b.ck_offsets, b.ck, B)
+        idx_b = torch.empty((B, hkv, k), dtype=torch.int32, device="cuda")
+        out_b = torch.empty_like(qs[step])
+        tbs.infv2_decode_step(b.cfg, qs[step], b.k, b.v, b.kv_offsets, b.kv_lens, b.ck_offsets, b.ck, B,
+                              b.max_len, idx_b, out_b, ws_b)
+        torch.cuda.synchronize()
+        assert torch.equal(idx_a, idx_b), f"step {step}: selection differs"
+        assert torch.equal(out_a, out_b), f"step {step}: output differs"
+    assert torch.equal(a.kv_lens, b.kv_lens), "lengths"
+    assert torch.equal(a.kv_lens.cpu(), torch.tensor(np.minimum(start + 41, cap))), "lengths advanced"
+    assert torch.equal(a.k, b.k) and torch.equal(a.v, b.v), "caches"
+    assert torch.equal(a.k.reshape(-1, d), k_full) and torch.equal(a.v.reshape(-1, d), v_full), \
+        "caches refilled with the appended rows"
+    assert torch.equal(a.ck, b.ck), "compressed keys"
+    cks = a.ck_host()
+    for sq in range(B):
+        assert np.array_equal(cks[sq], ref.compress_keys(wl.k_f64(sq), wl.kernel_size, wl.kernel_stride,
+                                                         ck_dtype)), f"seq {sq}"
+    _say(f"decode step with append: 41 steps equal, {a.check_canaries()} guarded buffers untouched")
+
+
 def test_decode_equals_last_prefill_row():
     h = _harness()
     wl = _small(mode="prefill", lens=[1500], topk=8, local=2, seed=34)

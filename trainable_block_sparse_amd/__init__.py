@@ -101,6 +101,8 @@ def load_library(path: str = LIB_PATH):
         "infv2_sparse_attn_decode": (i32, [cfgp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, sz, vp]),
         "infv2_sparse_attn_decode_noalloc": (i32, [cfgp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp]),
         "infv2_decode_step": (i32, [cfgp, vp, vp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, sz, vp]),
+        "infv2_decode_step_append": (i32, [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, vp, vp,
+                                           vp, sz, vp]),
         "infv2_sparse_attn_prefill": (i32, [cfgp, vp, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp]),
         "infv2_sparse_attn_prefill_bwd": (i32, [cfgp, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp,
                                                 vp, vp, sz, vp]),
@@ -120,7 +122,7 @@ def load_library(path: str = LIB_PATH):
 
 EXPORTED = ("infv2_compress_keys", "infv2_append_kv", "infv2_select_blocks",
             "infv2_select_blocks_coarse", "infv2_sparse_attn_decode", "infv2_sparse_attn_decode_noalloc", "infv2_decode_step",
-            "infv2_sparse_attn_prefill", "infv2_select_blocks_varlen",
+            "infv2_decode_step_append", "infv2_sparse_attn_prefill", "infv2_select_blocks_varlen",
             "infv2_sparse_attn_prefill_varlen", "infv2_sparse_attn_prefill_bwd", "infv2_workspace_bytes", "infv2_num_kernels",
             "infv2_status_str", "infv2_abi_version", "infv2_timing_start", "infv2_timing_stop")
 
@@ -278,6 +280,16 @@ def infv2_decode_step(cfg: Config, q, k, v, kv_offsets, kv_lens, ck_offsets, ck,
         ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(kv_offsets), _ptr(kv_lens), _ptr(ck_offsets),
         _ptr(ck), batch, max_len, _ptr(block_idx), _ptr(out), _ptr(ws), nbytes, _stream(stream)),
         "infv2_decode_step")
+
+
+def infv2_decode_step_append(cfg: Config, q, k_new, v_new, k, v, kv_offsets, kv_lens, ck_offsets, ck,
+                             batch: int, max_len: int, block_idx, out, ws, stream=None) -> None:
+    c = cfg.to_c()
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load_library().infv2_decode_step_append(
+        ctypes.byref(c), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k), _ptr(v), _ptr(kv_offsets),
+        _ptr(kv_lens), _ptr(ck_offsets), _ptr(ck), batch, max_len, _ptr(block_idx), _ptr(out), _ptr(ws),
+        nbytes, _stream(stream)), "infv2_decode_step_append")
 
 
 def infv2_sparse_attn_decode_noalloc(cfg: Config, q, k, v, kv_offsets, kv_lens, batch: int,

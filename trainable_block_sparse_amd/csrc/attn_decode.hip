@@ -304,7 +304,8 @@ template <typename Tout>
 __global__ __launch_bounds__(256) void attn_decode_merge(const float* __restrict__ part_o,
                                                          const float2* __restrict__ part_ml,
                                                          Tout* __restrict__ out, int hq, int hkv,
-                                                         int nsplit) {
+                                                         int nsplit, int64_t* __restrict__ lens_adv,
+                                                         const int64_t* __restrict__ kv_off) {
     constexpr int kSg = 8;                 // split groups
     constexpr int kPre = 8;                // splits per thread loaded with the (m, l) pairs
     constexpr int kMlPer = kDecodeMaxSplit / 256;
@@ -313,6 +314,12 @@ __global__ __launch_bounds__(256) void attn_decode_merge(const float* __restrict
     __shared__ float4 part[kSg][kHeadDim / 4];
     const int h = blockIdx.x, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
     const int sg = t >> 5, cq = t & 31, wv = t >> 6;
+    // a step that appended its token: the sequence's length moves on by one here,
+    // in the step's last kernel, which no longer reads it
+    if (lens_adv && h == 0 && g == 0 && t == 0) {
+        const int64_t lv = lens_adv[b];
+        if (lv < kv_off[b + 1] - kv_off[b]) lens_adv[b] = lv + 1;
+    }
     const size_t bg = static_cast<size_t>(b) * hkv + g;
     const size_t stride = static_cast<size_t>(kGroup) * kHeadDim / 4;     // float4 per split
     const float4* po = reinterpret_cast<const float4*>(part_o) +
@@ -403,7 +410,7 @@ hipError_t launch_attn_decode_mfma(const Shape& sh, const void* q, const void* k
     dim3 grid(nsplit, sh.hkv, batch);
     const float scale_log2 = sh.attn_scale * 1.4426950408889634f;
     const int64_t* lens = kv_lens ? kv_lens : kv_off + 1;
-    const int lens_end = kv_lens ? 0 : 1;
+    const int lens_end = kv_lens ? (sh.lens_plus_one ? 2 : 0) : 1;
     if (tpw > 1)
         launch_timed(INFV2_KERNEL_ATTN_DECODE, attn_decode_mfma<true>, grid, dim3(256), 0, st,
             static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
@@ -429,7 +436,7 @@ hipError_t launch_attn_decode_topk(const Shape& sh, const void* q, const void* k
     dim3 grid(nsplit, sh.hkv, batch);
     const float scale_log2 = sh.attn_scale * 1.4426950408889634f;
     const int64_t* lens = kv_lens ? kv_lens : kv_off + 1;
-    const int lens_end = kv_lens ? 0 : 1;
+    const int lens_end = kv_lens ? (sh.lens_plus_one ? 2 : 0) : 1;
     const int per = topk_per(nblk_max, 256);
 #define INFV2_L(P, R) launch_timed(INFV2_KERNEL_ATTN_DECODE, attn_decode_topk_mfma<P, R>, grid, dim3(256), 0, st, \
         static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), \
@@ -447,14 +454,15 @@ hipError_t launch_attn_decode_topk(const Shape& sh, const void* q, const void* k
 }
 
 hipError_t launch_attn_decode_merge(const Shape& sh, const float* part_o, const float2* part_ml,
-                                    void* out, int batch, int nsplit, hipStream_t st) {
+                                    void* out, int batch, int nsplit, hipStream_t st,
+                                    int64_t* lens_adv, const int64_t* kv_off) {
     dim3 grid(kGroup, sh.hkv, batch);
     if (sh.io_bf16)
         launch_timed(INFV2_KERNEL_ATTN_MERGE, attn_decode_merge<bf16_t>, grid, dim3(256), 0, st,
-                     part_o, part_ml, static_cast<bf16_t*>(out), sh.hq, sh.hkv, nsplit);
+                     part_o, part_ml, static_cast<bf16_t*>(out), sh.hq, sh.hkv, nsplit, lens_adv, kv_off);
     else
         launch_timed(INFV2_KERNEL_ATTN_MERGE, attn_decode_merge<float>, grid, dim3(256), 0, st,
-                     part_o, part_ml, static_cast<float*>(out), sh.hq, sh.hkv, nsplit);
+                     part_o, part_ml, static_cast<float*>(out), sh.hq, sh.hkv, nsplit, lens_adv, kv_off);
     return hipGetLastError();
 }
 

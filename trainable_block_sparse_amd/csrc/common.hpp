@@ -205,10 +205,11 @@ __device__ __forceinline__ uint4 ldg16_nt(const void* p) {
 // Valid length of sequence b from its offsets and the caller's lengths.  The
 // launchers pass `lens` = kv_lens, or kv_offsets + 1 with lens_end = 1 when
 // kv_lens is NULL, so the length is loaded unconditionally, together with the
-// offsets (one memory round trip instead of two).
+// offsets (one memory round trip instead of two).  lens_end = 2: a decode step
+// that appends the new token first, so the length is kv_lens[b] + 1.
 __device__ __forceinline__ int64_t seq_len(int64_t o0, int64_t o1, int64_t lv, int lens_end) {
     const int64_t cap = o1 - o0;
-    const int64_t n = lens_end ? cap : lv;
+    const int64_t n = lens_end == 1 ? cap : lv + (lens_end >> 1);
     return n < cap ? n : cap;
 }
 

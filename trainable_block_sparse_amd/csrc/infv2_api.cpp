@@ -295,6 +295,52 @@ int32_t infv2_decode_step(const infv2_config* c, const void* q, const void* k, c
                                                out, ws_attn, s));
 }
 
+int32_t infv2_decode_step_append(const infv2_config* c, const void* q, const void* k_new,
+                                 const void* v_new, void* k, void* v, const int64_t* kv_offsets,
+                                 int64_t* kv_lens, const int64_t* ck_offsets, void* ck,
+                                 int32_t batch, int64_t max_len, int32_t* block_idx, void* out,
+                                 void* ws, size_t ws_bytes, void* stream) {
+    int32_t st = check_config(c);
+    if (st != INFV2_OK) return st;
+    if (!q || !k_new || !v_new || !k || !v || !kv_offsets || !kv_lens || !ck_offsets || !ck ||
+        !block_idx || !out)
+        return INFV2_ERR_NULL;
+    if (batch < 1) return INFV2_ERR_SHAPE;
+    if ((st = check_len(c, max_len)) != INFV2_OK) return st;
+    const size_t need = ws_bytes_for(c, INFV2_OP_DECODE_STEP, batch, batch, max_len);
+    if (!ws || ws_bytes < need) return INFV2_ERR_WORKSPACE;
+    Shape sh = make_shape(c);
+    const infv2::SelectDecodeWs sw = infv2::select_decode_ws(sh, batch, max_len);
+    if (!sh.io_bf16 || !infv2::attn_decode_topk_ok(sh, sw.nblk_max)) {
+        // the two calls it stands for
+        if ((st = infv2_append_kv(c, k_new, v_new, k, v, kv_offsets, kv_lens, ck_offsets, ck, batch,
+                                  stream)) != INFV2_OK)
+            return st;
+        return infv2_decode_step(c, q, k, v, kv_offsets, kv_lens, ck_offsets, ck, batch, max_len,
+                                 block_idx, out, ws, ws_bytes, stream);
+    }
+    // the step's kernels see kv_lens[b] + 1; the logits kernel writes the new
+    // token into the caches (and builds the kernel it completes from it), the
+    // merge kernel stores the new lengths
+    sh.lens_plus_one = 1;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws_attn = static_cast<char*>(ws) + infv2::align256(sw.total);
+    const infv2::AttnDecodeWs aw = infv2::attn_decode_ws(sh, batch);
+    const infv2::DecAppend app{k_new, v_new, k, v};
+    hipError_t e = infv2::launch_select_decode(sh, q, ck, ck_offsets, kv_offsets, kv_lens, batch,
+                                               max_len, block_idx, nullptr, ws, nullptr, s, k, true,
+                                               &app);
+    if (e != hipSuccess) return INFV2_ERR_DEVICE;
+    const uint32_t* keys = reinterpret_cast<const uint32_t*>(static_cast<char*>(ws) + sw.keys);
+    float* po = reinterpret_cast<float*>(ws_attn + aw.part_o);
+    float2* pml = reinterpret_cast<float2*>(ws_attn + aw.part_ml);
+    e = infv2::launch_attn_decode_topk(sh, q, k, v, kv_offsets, kv_lens, batch, keys, sw.keys_ld,
+                                       sw.nblk_max, block_idx, po, pml, aw.nsplit_m, aw.tpw, s);
+    if (e != hipSuccess) return status_of(e);
+    return status_of(infv2::launch_attn_decode_merge(sh, po, pml, out, batch, aw.nsplit_m, s, kv_lens,
+                                                     kv_offsets));
+}
+
 int32_t infv2_sparse_attn_prefill(const infv2_config* c, const void* q, int32_t rows,
                                   int64_t q_start, const void* k, const void* v,
                                   const int64_t* kv_offsets, const int32_t* block_idx, void* out,

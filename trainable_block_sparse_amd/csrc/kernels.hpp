@@ -51,6 +51,20 @@ struct Shape {
     int hq, hkv, d, m, p, s, topk, init, local;
     int io_bf16, ck_bf16;
     float score_scale, attn_scale;
+    // decode step with the cache append folded in: every kernel of the step
+    // takes a sequence's length as kv_lens[b] + 1 (capped at its capacity),
+    // and the last kernel stores that length
+    int lens_plus_one = 0;
+};
+
+// the new token of each sequence for a decode step that also appends it:
+// k_new / v_new [batch][Hkv][d] (bf16), written into the caches k / v at
+// position kv_lens[b] when it is below the capacity
+struct DecAppend {
+    const void* k_new;
+    const void* v_new;
+    void* k;
+    void* v;
 };
 
 // workspace carving (all offsets 256-byte aligned)
@@ -131,7 +145,7 @@ hipError_t launch_select_decode(const Shape& sh, const void* q, const void* ck,
                                 const int64_t* kv_lens, int batch, int64_t max_len,
                                 int32_t* idx, float* score, void* ws, const CoarseSel* cs,
                                 hipStream_t st, const void* fuse_k = nullptr,
-                                bool skip_topk = false);
+                                bool skip_topk = false, const DecAppend* app = nullptr);
 
 hipError_t launch_select_prefill(const Shape& sh, const void* q, int rows, int64_t q_start,
                                  const void* ck, const int64_t* ck_off, int64_t max_len,
@@ -158,8 +172,11 @@ hipError_t launch_attn_decode_mfma(const Shape& sh, const void* q, const void* k
                                    const int64_t* kv_off, const int64_t* kv_lens, int batch,
                                    const int32_t* idx, float* part_o, float2* part_ml, int nsplit,
                                    int tpw, hipStream_t st);
+// lens_adv != nullptr: also advance lens_adv[b] by one where it is below the
+// capacity (the step's append; no other kernel of the step is running then)
 hipError_t launch_attn_decode_merge(const Shape& sh, const float* part_o, const float2* part_ml,
-                                    void* out, int batch, int nsplit, hipStream_t st);
+                                    void* out, int batch, int nsplit, hipStream_t st,
+                                    int64_t* lens_adv = nullptr, const int64_t* kv_off = nullptr);
 // Decode attention that first makes the top-k selection from the block-score
 // keys (rows of kld, one per (sequence, KV head)) in every thread block, with
 // the matrix-core path's splits (nsplit, tpw); split 0 stores the selection in

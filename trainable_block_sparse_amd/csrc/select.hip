@@ -205,7 +205,8 @@ __global__ __launch_bounds__(256) void sel_dec_logits(
 template <bool kCkBf16, int kThreads>
 __device__ __forceinline__ void new_compressed_key(const bf16_t* __restrict__ src, int p,
                                                    double (*fpart)[kHeadDim], float* fkey,
-                                                   void* __restrict__ ck_w, size_t dst) {
+                                                   void* __restrict__ ck_w, size_t dst,
+                                                   const bf16_t* __restrict__ newest) {
     constexpr int kParts = kThreads / 16;            // row groups
     const int t = threadIdx.x, oc = t & 15, rg = t >> 4;
     double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
@@ -214,7 +215,10 @@ __device__ __forceinline__ void new_compressed_key(const bf16_t* __restrict__ sr
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int r = r0 + kParts * u;
-            x[u] = r < p ? ldg16(src + static_cast<size_t>(r) * kHeadDim + 8 * oc) : make_uint4(0u, 0u, 0u, 0u);
+            // the last row is the newest token, read from the step's input when
+            // it is being appended in the same launch
+            const bf16_t* row = (newest && r == p - 1) ? newest : src + static_cast<size_t>(r) * kHeadDim;
+            x[u] = r < p ? ldg16(row + 8 * oc) : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -320,7 +324,9 @@ __global__ __launch_bounds__(kLogWaves * 64) void sel_dec_logits_mfma(
     const int64_t* __restrict__ kv_off, const int64_t* __restrict__ lens, int lens_end, int hq,
     int hkv, int p, int s, float score_scale, int64_t nc_max, int64_t nc_ld, int nchunk,
     int64_t nblk_max, int64_t kld, float* __restrict__ logits, float2* __restrict__ partial,
-    uint32_t* __restrict__ keys, const bf16_t* __restrict__ kcache, void* __restrict__ ck_w) {
+    uint32_t* __restrict__ keys, const bf16_t* __restrict__ kcache, void* __restrict__ ck_w,
+    const bf16_t* __restrict__ knew, const bf16_t* __restrict__ vnew, bf16_t* __restrict__ kapp,
+    bf16_t* __restrict__ vapp) {
     __shared__ float2 xm[kLogWaves][kGroup];   // each wave's (max, sum) per head
     constexpr int kFuseParts = kLogWaves * 64 / 16;     // row groups of the fused key sum
     __shared__ double fpart[kFuse ? kFuseParts : 1][kHeadDim];
@@ -369,6 +375,17 @@ __global__ __launch_bounds__(kLogWaves * 64) void sel_dec_logits_mfma(
             for (int x = 0; x < kU; ++x) raw[m2][x] = make_uint4(0u, 0u, 0u, 0u);
         }
     }
+    // appending step (lens_end = 2, lv = the length before the step): the new
+    // token enters the caches at position lv when there is room; the block of
+    // chunk 0 writes it, and the compression below takes that row from the input
+    const bool app = kFuse && knew != nullptr && lv < o1 - o0;
+    if (app && ch == 0 && t < 32) {
+        const size_t sx = (static_cast<size_t>(b) * hkv + g) * kHeadDim + 8 * (t & 15);
+        const size_t dx = (static_cast<size_t>(o0) * hkv + static_cast<size_t>(g) * (o1 - o0) +
+                           static_cast<size_t>(lv)) * kHeadDim + 8 * (t & 15);
+        if (t < 16) *reinterpret_cast<uint4*>(kapp + dx) = *reinterpret_cast<const uint4*>(knew + sx);
+        else *reinterpret_cast<uint4*>(vapp + dx) = *reinterpret_cast<const uint4*>(vnew + sx);
+    }
     // fused compression: the kernel j_new = nvis - 1 completed by token n - 1
     const int64_t j_new = nvis - 1;
     const bool fuse = kFuse && n >= p && (n - p) % s == 0 && j_new < ccap && j_new >= j0 &&
@@ -377,7 +394,9 @@ __global__ __launch_bounds__(kLogWaves * 64) void sel_dec_logits_mfma(
         const bf16_t* src = kcache + (static_cast<size_t>(o0) * hkv + static_cast<size_t>(g) * (o1 - o0) +
                                       static_cast<size_t>(j_new) * s) * kHeadDim;
         new_compressed_key<kCkBf16, kLogWaves * 64>(src, p, fpart, fkey, ck_w,
-                                                    static_cast<size_t>(cbase + j_new) * kHeadDim);
+                                                    static_cast<size_t>(cbase + j_new) * kHeadDim,
+                                                    app ? knew + (static_cast<size_t>(b) * hkv + g) * kHeadDim
+                                                        : nullptr);
         // the lanes holding row j_new take it from LDS instead of the stale load
 #pragma unroll
         for (int m2 = 0; m2 < kLogTiles; ++m2) {
@@ -1276,11 +1295,16 @@ template <typename Tq, typename Tck>
 static void dec_launch(const Shape& sh, const void* q, const void* ck, const int64_t* ck_off,
                        const int64_t* kv_off, const int64_t* kv_lens, int batch, int64_t max_len,
                        const SelectDecodeWs& w, char* ws, int32_t* idx, float* score,
-                       const CoarseSel* cs, const void* fuse_k, bool skip_topk, hipStream_t st) {
+                       const CoarseSel* cs, const void* fuse_k, bool skip_topk, hipStream_t st,
+                       const DecAppend* app) {
     dim3 ga(w.nchunk_a, sh.hkv, batch), gb(w.nchunk_b, sh.hkv, batch);
     const int64_t ncm = w.nc_max > 0 ? w.nc_max : 1;
     const int64_t* lens = kv_lens ? kv_lens : kv_off + 1;
-    const int lens_end = kv_lens ? 0 : 1;
+    const int lens_end = kv_lens ? (sh.lens_plus_one ? 2 : 0) : 1;
+    const bf16_t* knew = app ? static_cast<const bf16_t*>(app->k_new) : nullptr;
+    const bf16_t* vnew = app ? static_cast<const bf16_t*>(app->v_new) : nullptr;
+    bf16_t* kapp = app ? static_cast<bf16_t*>(app->k) : nullptr;
+    bf16_t* vapp = app ? static_cast<bf16_t*>(app->v) : nullptr;
     float* logits = reinterpret_cast<float*>(ws + w.logits);
     float2* partial = reinterpret_cast<float2*>(ws + w.partial);
     uint32_t* keys = reinterpret_cast<uint32_t*>(ws + w.keys);
@@ -1302,7 +1326,9 @@ static void dec_launch(const Shape& sh, const void* q, const void* ck, const int
                          dim3(kLogWaves * 64), 0, st,
                 static_cast<const bf16_t*>(q), cs->ckc, cs->ckc_off, kv_off, lens, lens_end, sh.hq,
                 sh.hkv, c, c, sh.score_scale, ncm_c, ld_c, nch_c, w.nblk_max, w.keys_ld, logits_c,
-                partial_c, keys, static_cast<const bf16_t*>(nullptr), static_cast<void*>(nullptr));
+                partial_c, keys, static_cast<const bf16_t*>(nullptr), static_cast<void*>(nullptr),
+                static_cast<const bf16_t*>(nullptr), static_cast<const bf16_t*>(nullptr),
+                static_cast<bf16_t*>(nullptr), static_cast<bf16_t*>(nullptr));
         else
             launch_timed(INFV2_KERNEL_SELECT_LOGITS, sel_dec_logits<Tq, Tck>, gc, dim3(256), 0, st,
                 static_cast<const Tq*>(q), static_cast<const Tck*>(cs->ckc), cs->ckc_off, kv_off,
@@ -1317,7 +1343,8 @@ static void dec_launch(const Shape& sh, const void* q, const void* ck, const int
                     ga, dim3(kLogWaves * 64), 0, st, \
                     static_cast<const bf16_t*>(q), ck, ck_off, kv_off, lens, lens_end, sh.hq, sh.hkv, \
                     sh.p, sh.s, sh.score_scale, ncm, w.nc_ld, w.nchunk_a, w.nblk_max, w.keys_ld, logits, \
-                    partial, keys, static_cast<const bf16_t*>(fuse_k), const_cast<void*>(ck))
+                    partial, keys, static_cast<const bf16_t*>(fuse_k), const_cast<void*>(ck), \
+                    knew, vnew, kapp, vapp)
             if (fuse_k) { if (nt) INFV2_L(true, true); else INFV2_L(true, false); }
             else { if (nt) INFV2_L(false, true); else INFV2_L(false, false); }
 #undef INFV2_L
@@ -1357,7 +1384,8 @@ hipError_t launch_select_decode(const Shape& sh, const void* q, const void* ck,
                                 const int64_t* ck_off, const int64_t* kv_off,
                                 const int64_t* kv_lens, int batch, int64_t max_len,
                                 int32_t* idx, float* score, void* ws, const CoarseSel* cs,
-                                hipStream_t st, const void* fuse_k, bool skip_topk) {
+                                hipStream_t st, const void* fuse_k, bool skip_topk,
+                                const DecAppend* app) {
     const SelectDecodeWs w = select_decode_ws(sh, batch, max_len);
     if (!score && !fuse_k && !skip_topk && max_len <= static_cast<int64_t>(sh.topk) * sh.m) {   // every row dense
         launch_dense_ids(sh, 1, batch, 0, kv_off, kv_lens, w.nblk_max, idx, st);
@@ -1365,11 +1393,11 @@ hipError_t launch_select_decode(const Shape& sh, const void* q, const void* ck,
     }
     char* base = static_cast<char*>(ws);
     if (sh.io_bf16) {
-        if (sh.ck_bf16) dec_launch<bf16_t, bf16_t>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, fuse_k, skip_topk, st);
-        else dec_launch<bf16_t, float>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, fuse_k, skip_topk, st);
+        if (sh.ck_bf16) dec_launch<bf16_t, bf16_t>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, fuse_k, skip_topk, st, app);
+        else dec_launch<bf16_t, float>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, fuse_k, skip_topk, st, app);
     } else {
-        if (sh.ck_bf16) dec_launch<float, bf16_t>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, nullptr, skip_topk, st);
-        else dec_launch<float, float>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, nullptr, skip_topk, st);
+        if (sh.ck_bf16) dec_launch<float, bf16_t>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, nullptr, skip_topk, st, nullptr);
+        else dec_launch<float, float>(sh, q, ck, ck_off, kv_off, kv_lens, batch, max_len, w, base, idx, score, cs, nullptr, skip_topk, st, nullptr);
     }
     return hipGetLastError();
 }
