@@ -23,6 +23,9 @@
 // most four steps; typical inputs need one).  The ascending output needs one
 // block scan because ownership is contiguous.  Barriers: one for the min / max,
 // two per narrowing step, three for the rank step, one for the output scan.
+// A caller that only needs to find given slots of the selection can take it
+// as a bitmap instead (kBitmap: bit j = block j, set with one LDS atomic OR per
+// thread, no output scan), read with wave-level popcounts (BitmapLanes).
 #pragma once
 
 #include <type_traits>
