@@ -963,6 +963,64 @@ def test_decode_step_append_equals_append_then_step(io, ck_dtype, keys):
     _say(f"decode step with append: 41 steps equal, {a.check_canaries()} guarded buffers untouched")
 
 
+def test_decode_step_append_graph_replays():
+    """A captured graph of three appending decode steps, replayed three times
+    with eager work and synchronisations in between (lengths, caches and
+    compressed keys advance on every replay), equals nine eager steps on a twin
+    cache: each replay's last selection and output, and the final state."""
+    import trainable_block_sparse_amd as tbs
+    from synth import extra_decode_queries
+    h = _harness()
+    wl = _small(lens=[9000, 20000], topk=16, local=4, seed=187)
+    _say("graph replays of the appending decode step")
+    a = h.DeviceWorkload(wl)
+    b = h.DeviceWorkload(wl)
+    B, hkv, d, k = wl.batch, wl.num_kv_heads, wl.head_dim, wl.topk
+    start = wl.lens.astype(np.int64) - 20                 # room for nine appends
+    for dev in (a, b):
+        dev.kv_lens.copy_(torch.tensor(start, device="cuda"))
+        dev.compress(kv_lens=dev.kv_lens)
+    qs = h.to_device(extra_decode_queries(wl, 3))
+    rng = np.random.default_rng(187)
+    kv_new = [torch.tensor(rng.standard_normal((B, hkv, d)), dtype=torch.float32, device="cuda").to(torch.bfloat16)
+              for _ in range(6)]
+    ws_a = torch.zeros(tbs.infv2_workspace_bytes(a.cfg, tbs.OP_DECODE_STEP, B, B, a.max_len),
+                       dtype=torch.uint8, device="cuda")
+    ws_b = torch.zeros_like(ws_a)
+    idx_a = torch.empty((B, hkv, k), dtype=torch.int32, device="cuda")
+    out_a = torch.empty_like(qs[0])
+
+    def step(dev, i, ws, idx, out):
+        tbs.infv2_decode_step_append(dev.cfg, qs[i], kv_new[2 * i], kv_new[2 * i + 1], dev.k, dev.v,
+                                     dev.kv_offsets, dev.kv_lens, dev.ck_offsets, dev.ck, B, dev.max_len,
+                                     idx, out, ws)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for i in range(3):
+                step(a, i, ws_a, idx_a, out_a)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(a.kv_lens.cpu(), torch.tensor(start)), "capture ran the steps"
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        _ = (a.q.float() * 2).sum().item()             # eager work between replays
+        for i in range(3):
+            idx_b = torch.empty((B, hkv, k), dtype=torch.int32, device="cuda")
+            out_b = torch.empty_like(qs[0])
+            step(b, i, ws_b, idx_b, out_b)
+        torch.cuda.synchronize()
+        assert torch.equal(idx_a, idx_b), f"replay {rep}: selection"
+        assert torch.equal(out_a, out_b), f"replay {rep}: output"
+        assert torch.equal(a.kv_lens, b.kv_lens), f"replay {rep}: lengths"
+    assert torch.equal(a.kv_lens.cpu(), torch.tensor(start + 9))
+    assert torch.equal(a.k, b.k) and torch.equal(a.v, b.v) and torch.equal(a.ck, b.ck)
+
+
 def test_decode_equals_last_prefill_row():
     h = _harness()
     wl = _small(mode="prefill", lens=[1500], topk=8, local=2, seed=34)
