@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define INFV2_ABI_VERSION 8
+#define INFV2_ABI_VERSION 9   /* 9: infv2_decode_step_append */
 
 typedef enum infv2_status {
     INFV2_OK = 0,
